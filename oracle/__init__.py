@@ -1,0 +1,28 @@
+"""Plain, slow float64 CPU oracle for the chunked test-time-training memory.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute anything in this package: only ``tests/``, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` use it.  It
+shares no code with the HIP library (no kernels, headers, helpers, constants or
+pre/post-processing) and it never imports that library.
+
+What it computes, in the pages' own order (a per-token loop, float64):
+
+* ``linear_forward`` -- the linear memory ``z = M q`` trained by gradient steps
+  on ``l = 1/2 ||M k - v||^2`` with gradients taken at the chunk-start state,
+  Titans momentum and forgetting.  Pinned by the pages' worked examples and by
+  closed forms (delta rule, linear attention, batch gradient descent, one-step
+  loss contraction, decay unrolling, constant-gate momentum expansion).
+* ``mlp_forward`` -- the same schedule for a 2-layer MLP memory
+  ``f(u) = u + SiLU(u W1) W2`` with gradients by explicit backprop.  Pinned by
+  torch.autograd (a library routine), finite differences, and by agreement of
+  an autograd-driven generic loop whose linear instance is pinned by the
+  worked examples.
+
+Every function here is pinned by tests in ``tests/test_oracle_*.py``; none is
+"parity unpinned".
+"""
+
+from .memory import linear_forward, mlp_forward, silu, silu_grad, mlp_chunk_grads
+
+__all__ = ["linear_forward", "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]

@@ -1,0 +1,185 @@
+"""Per-token float64 loops for the chunked TTT / Titans memory (test infrastructure only).
+
+Notation (column vectors): the linear memory is a matrix ``M`` of shape
+``[dv, dk]`` read as ``z = M q``; ``M[i, j]`` carries key coordinate ``j`` into
+value coordinate ``i``.  Gates per token: ``theta`` (inner learning rate),
+``eta`` (momentum decay), ``alpha`` (forgetting).  All arrays may carry any
+number of leading batch dimensions (batch, head, ...); the loops below run over
+tokens only and treat every leading index independently, as independent
+sequences do on the pages.
+
+Sources (page title, then section / equation):
+
+* "Continual Learning: From Attention to Neural Memory", sections 3.2-3.3: the
+  loss ``1/2 ||k W - v||^2`` and its gradient as an outer product of key and
+  error (row-vector form there; ``W`` there is ``M`` transposed here).
+* same page, section 4.2: a TTT step ``W_t = W_{t-1} - lr * grad``, the read
+  ``z_t = f(q_t; W_t)`` after the write, one same-shaped gradient per tensor.
+* same page, section 4.7: mini-batch TTT -- gradients of a chunk share the
+  chunk-start state; a token's read still sees only its own prefix of writes.
+* same page, section 5.2 and "论文速览 | Titans" sections 3.4 and 3.7: momentum
+  ``S_t = eta_t S_{t-1} - theta_t grad`` and forgetting
+  ``M_t = (1 - alpha_t) M_{t-1} + S_t``, the gradient evaluated at the old
+  memory.
+* "论文速览 | Titans" section 4.2: the chunk-start reference state
+  ``t' = t - mod(t, b)``, read here as "the state after the last token of the
+  previous chunk" (0-based tokens), which is what the worked examples require.
+* "5.1.1 · TTT layers 与 fast weights" section 1.1, eq. (6): mini-batch GD as the
+  third choice of descent direction, gradients relative to the end of the
+  previous mini-batch.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["linear_forward", "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]
+
+
+def _f64(x):
+    return None if x is None else np.asarray(x, dtype=np.float64)
+
+
+def _matvec(A, x):
+    """``A @ x`` for stacks: A [..., m, n], x [..., n] -> [..., m]."""
+    return np.matmul(A, x[..., :, None])[..., :, 0]
+
+
+def _outer(a, b):
+    """Outer product for stacks: a [..., m], b [..., n] -> [..., m, n]."""
+    return a[..., :, None] * b[..., None, :]
+
+
+def linear_forward(q, k, v, theta, eta, alpha, M0=None, S0=None, b=1, grad="l2"):
+    """Linear memory, chunk-start gradients, per-token momentum and forgetting.
+
+    Arguments: ``q, k`` ``[..., T, dk]``; ``v`` ``[..., T, dv]``; ``theta, eta,
+    alpha`` ``[..., T]``; ``M0, S0`` ``[..., dv, dk]`` or None for zeros;
+    ``b`` the chunk (mini-batch) size, ``b >= 1``; the last chunk may be short.
+
+    ``grad="l2"`` uses the gradient of ``1/2 ||M k - v||^2`` at the chunk-start
+    memory, ``(M_c k - v) k^T`` ("Continual Learning..." section 3.3).
+    ``grad="neg_vk"`` replaces it by ``-v k^T``, which turns the update into
+    the additive write of unnormalised linear attention ("Continual
+    Learning..." section 3.1; "论文速览 | Titans" section 2.3); it exists only
+    so that tests can pin the schedule against closed forms.
+
+    Returns ``z [..., T, dv], M_T [..., dv, dk], S_T [..., dv, dk]`` (float64).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    theta, eta, alpha = _f64(theta), _f64(eta), _f64(alpha)
+    if b < 1:
+        raise ValueError("chunk size b must be >= 1")
+    if grad not in ("l2", "neg_vk"):
+        raise ValueError("grad must be 'l2' or 'neg_vk'")
+    lead, T, dk = q.shape[:-2], q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    M = np.zeros(lead + (dv, dk)) if M0 is None else np.array(np.broadcast_to(_f64(M0), lead + (dv, dk)))
+    S = np.zeros(lead + (dv, dk)) if S0 is None else np.array(np.broadcast_to(_f64(S0), lead + (dv, dk)))
+    z = np.zeros(lead + (T, dv))
+
+    for c0 in range(0, T, b):
+        # Chunk-start memory: the state after every write of the previous chunks.
+        M_c = M.copy()
+        for t in range(c0, min(c0 + b, T)):
+            k_t, v_t = k[..., t, :], v[..., t, :]
+            if grad == "l2":
+                err = _matvec(M_c, k_t) - v_t          # prediction minus target
+                G = _outer(err, k_t)                   # d/dM of 1/2||M k - v||^2
+            else:
+                G = -_outer(v_t, k_t)
+            th = theta[..., t][..., None, None]
+            et = eta[..., t][..., None, None]
+            al = alpha[..., t][..., None, None]
+            S = et * S - th * G                        # momentum ("surprise")
+            M = (1.0 - al) * M + S                     # forget, then add momentum
+            z[..., t, :] = _matvec(M, q[..., t, :])    # read after this token's write
+    return z, M, S
+
+
+def silu(x):
+    """SiLU(x) = x * sigmoid(x)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def silu_grad(x):
+    """d/dx SiLU(x) = s (1 + x (1 - s)) with s = sigmoid(x)."""
+    x = np.asarray(x, dtype=np.float64)
+    s = 1.0 / (1.0 + np.exp(-x))
+    return s * (1.0 + x * (1.0 - s))
+
+
+def _mlp_apply(u, W1, W2):
+    """Deep memory read, row-vector form: ``f(u) = u + SiLU(u W1) W2``."""
+    h = np.matmul(u[..., None, :], W1)[..., 0, :]
+    return u + np.matmul(silu(h)[..., None, :], W2)[..., 0, :]
+
+
+def mlp_chunk_grads(k, v, W1, W2, loss_on="full"):
+    """Gradients of ``1/2 ||f(k) - v||^2`` w.r.t. ``W1 [.., dk, hid]`` and ``W2 [.., hid, dv]``.
+
+    Explicit backprop through ``f(u) = u + SiLU(u W1) W2`` (row vectors), for one
+    key/value pair per leading index (``k [..., dk]``, ``v [..., dv]``).  With
+    ``loss_on="mlp"`` the residual ``u`` is left out of the loss target (the
+    other reading of the deep-memory description); the read is unchanged.
+
+    Chain rule, step by step: ``h = k W1``; ``a = SiLU(h)``; ``r = k + a W2 - v``;
+    ``dL/dW2 = a^T r``; ``dL/da = r W2^T``; ``dL/dh = dL/da * SiLU'(h)``;
+    ``dL/dW1 = k^T dL/dh``.
+    """
+    h = np.matmul(k[..., None, :], W1)[..., 0, :]
+    a = silu(h)
+    y = np.matmul(a[..., None, :], W2)[..., 0, :]
+    if loss_on == "full":
+        r = k + y - v
+    elif loss_on == "mlp":
+        r = y - v
+    else:
+        raise ValueError("loss_on must be 'full' or 'mlp'")
+    dW2 = _outer(a, r)
+    da = np.matmul(r[..., None, :], np.swapaxes(W2, -1, -2))[..., 0, :]
+    dh = da * silu_grad(h)
+    dW1 = _outer(k, dh)
+    return dW1, dW2
+
+
+def mlp_forward(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0=None, S2_0=None, b=1, loss_on="full"):
+    """Deep (2-layer MLP) memory with the same chunked schedule as ``linear_forward``.
+
+    ``f(u) = u + SiLU(u W1) W2`` in row-vector form ("论文速览 | Titans" section
+    3.9: a memory of at least two layers; "Nested Learning ... part 11/14"
+    eq. (89): a residual MLP block without biases).  Both tensors get their own
+    momentum and use the same per-token ``theta, eta, alpha`` ("Continual
+    Learning..." section 4.2: one same-shaped gradient per tensor; section 5.1:
+    the update history has the same structure as the weights).
+
+    Shapes: ``q, k, v [..., T, d]``; ``W1_0, S1_0 [..., d, hid]``;
+    ``W2_0, S2_0 [..., hid, d]``.  Returns ``z, W1_T, W2_T, S1_T, S2_T``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    theta, eta, alpha = _f64(theta), _f64(eta), _f64(alpha)
+    if b < 1:
+        raise ValueError("chunk size b must be >= 1")
+    lead, T, d = q.shape[:-2], q.shape[-2], q.shape[-1]
+    W1_0, W2_0 = _f64(W1_0), _f64(W2_0)
+    hid = W1_0.shape[-1]
+    W1 = np.array(np.broadcast_to(W1_0, lead + (d, hid)))
+    W2 = np.array(np.broadcast_to(W2_0, lead + (hid, d)))
+    S1 = np.zeros_like(W1) if S1_0 is None else np.array(np.broadcast_to(_f64(S1_0), W1.shape))
+    S2 = np.zeros_like(W2) if S2_0 is None else np.array(np.broadcast_to(_f64(S2_0), W2.shape))
+    z = np.zeros(lead + (T, d))
+
+    for c0 in range(0, T, b):
+        W1_c, W2_c = W1.copy(), W2.copy()          # chunk-start weights
+        for t in range(c0, min(c0 + b, T)):
+            G1, G2 = mlp_chunk_grads(k[..., t, :], v[..., t, :], W1_c, W2_c, loss_on)
+            th = theta[..., t][..., None, None]
+            et = eta[..., t][..., None, None]
+            al = alpha[..., t][..., None, None]
+            S1 = et * S1 - th * G1
+            S2 = et * S2 - th * G2
+            W1 = (1.0 - al) * W1 + S1
+            W2 = (1.0 - al) * W2 + S2
+            z[..., t, :] = _mlp_apply(q[..., t, :], W1, W2)
+    return z, W1, W2, S1, S2
