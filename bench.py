@@ -1,0 +1,196 @@
+"""Throughput of the chunked TTT / Titans linear-memory forward on one MI355X.
+
+A step is one forward pass of the whole memory layer -- every (batch, head)
+sequence, every chunk -- over one batch of synthetic inputs that are already
+resident in HBM: the Titans linear-memory workload, B=4 H=16 T=8192 d=128 b=64,
+bf16 q/k/v, float32 gates, state and z.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from test_neural_memory_amd import memory as tm  # noqa: E402
+from test_neural_memory_amd.workloads import WORKLOADS, make_inputs, to_numpy64  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w, in_bytes=2, z_bytes=4, reads_state=False):
+    """Bytes and flops the method itself must move / do for one forward.
+
+    Per (batch, head, token): read q, k, v (d elements each) and three gates,
+    write z (d floats); per chunk the dual form does 2 b d^2 flops for each of
+    K M0^T, Q M0^T, Q S0^T, dM, dS and 2 b^2 d for each of Q K^T and P E, i.e.
+    10 d^2 + 4 b d flops per head-token.  Per (batch, head): write M_T, S_T
+    (and read M0, S0 when given).
+    """
+    ht = w.B * w.H * w.T
+    per_tok = 3 * w.d * in_bytes + 3 * 4 + w.d * z_bytes
+    state = w.B * w.H * w.d * w.d * 4 * (4 if reads_state else 2)
+    flops = ht * (10 * w.d * w.d + 4 * w.b * w.d)
+    return ht * per_tok + state, flops, per_tok
+
+
+def _oracle_worker(args):
+    # Runs in a separate process: one BLAS thread, the oracle as it stands.
+    q, k, v, th, et, al, b = args
+    from threadpoolctl import threadpool_limits
+    from oracle import linear_forward
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        linear_forward(q, k, v, th, et, al, None, None, b=b)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, inp, heads):
+    """Time the float64 oracle on ``heads`` (batch, head) pairs with full T, in a process pool."""
+    import multiprocessing as mp
+    ncores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    g = {k: to_numpy64(v) for k, v in inp.items() if k in ("q", "k", "v", "theta", "eta", "alpha")}
+    B, H = w.B, w.H
+    pairs = [(i // H, i % H) for i in range(B * H)][:heads]
+    groups = [pairs[i::ncores] for i in range(ncores)]
+    jobs = []
+    for grp in groups:
+        if not grp:
+            continue
+        bi = np.array([p[0] for p in grp])
+        hi = np.array([p[1] for p in grp])
+        jobs.append(tuple(g[x][bi, hi] for x in ("q", "k", "v", "theta", "eta", "alpha")) + (w.b,))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(len(jobs)) as pool:
+        per_job = pool.map(_oracle_worker, jobs)
+    wall = time.perf_counter() - t0
+    head_tokens = len(pairs) * w.T
+    return {
+        "value": head_tokens / H / wall,   # tokens/s, each token covering all H heads
+        "unit": "tokens/s",
+        "cores": len(jobs),
+        "kind": "oracle",
+        "sample": f"{len(pairs)} of {B * H} (batch, head) sequences, full T={w.T}, all d={w.d} rows; "
+                  f"float64 per-token NumPy loop, {len(jobs)} processes x 1 thread; "
+                  f"wall {wall:.2f} s, busiest process {max(per_job):.2f} s; "
+                  f"tokens/s = sampled head-tokens / H / wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) sequences in the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the memory forward needs no "
+              "collective and this build runs on a single MI355X; shard (batch, head) pairs across "
+              "processes to use more GPUs.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        sys.exit(2)
+
+    w = WORKLOADS[args.workload]
+    log(f"workload {w}")
+    inp = make_inputs(w)
+    dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    B, H, T, d = w.B, w.H, w.T, w.d
+    z = torch.empty(B, H, T, d, dtype=torch.float32, device="cuda")
+    MT = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    ST = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    call = lambda: tm.forward(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"],  # noqa: E731
+                              dev.get("M0"), dev.get("S0"), b=w.b, out=(z, MT, ST))
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, one kernel launch each, on torch's current stream
+    # (the stream the library launches on), bracketed by HIP events.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        call()
+        ends[i].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
+    avg_launch_ms = float(np.mean(launch_ms))
+
+    nbytes, flops, per_tok = algorithmic_work(w, reads_state=dev.get("M0") is not None)
+    achieved_gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    tokens_per_s = B * T / (ms_per_step * 1e-3)
+    log(f"avg launch {avg_launch_ms * 1e3:.1f} us, min {min(launch_ms) * 1e3:.1f} us, "
+        f"max {max(launch_ms) * 1e3:.1f} us; wall/step {t_wall / args.steps * 1e3:.3f} ms")
+    log(f"algorithmic bytes/launch {nbytes / 1e6:.1f} MB -> {achieved_gbs:.0f} GB/s; "
+        f"flops/launch {flops / 1e9:.1f} GFLOP -> {flops / (avg_launch_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+
+    # Sampled parity check of the timed outputs against the oracle.
+    from oracle import linear_forward
+    rows = np.r_[0:4, d - 4:d]
+    g = {k: to_numpy64(v[0, 0]) for k, v in inp.items() if v is not None}
+    zo, Mo, So = linear_forward(g["q"], g["k"], g["v"][:, rows], g["theta"], g["eta"], g["alpha"], None, None, b=w.b)
+    zg = z[0, 0][:, rows].double().cpu().numpy()
+    rms = float(np.sqrt(np.mean(zo ** 2)))
+    parity = float(np.max(np.abs(zg - zo)) / rms)
+    log(f"sampled parity (sequence 0, rows {list(rows)}): max|dz|/rms = {parity:.3e}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp, args.cpu_heads)
+        log(f"cpu baseline: {cpu}")
+
+    result = {
+        "metric": "memory-layer tokens/s at H=16,d=128,b=64",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "b": w.b,
+                   "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "state": "f32", "z": "f32",
+                   "head_tokens_per_s": B * H * T / (ms_per_step * 1e-3)},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "mfma_frac": flops / (avg_launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+        "parity_sample_max_rel_err": parity,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,10 @@
+"""MI355X-native chunked test-time-training memory (TTT / Titans neural memory).
+
+The compute lives in ``libttt_mem.so`` (HIP for gfx950, C ABI in
+``include/ttt_mem.h``); this package holds its build script, a thin torch
+binding and the seeded synthetic workloads used by the tests and the bench.
+"""
+
+from .memory import forward, ttt_mem_forward_bf16, ttt_mem_forward_f32
+
+__all__ = ["forward", "ttt_mem_forward_bf16", "ttt_mem_forward_f32"]

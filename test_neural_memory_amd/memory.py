@@ -1,0 +1,84 @@
+"""Thin torch binding of libttt_mem: argument marshalling only.
+
+Every function here validates tensor placement and layout, allocates the
+outputs with torch (device memory), and calls the C ABI of the same name on
+torch's current HIP stream.  All arithmetic happens in the HIP kernels.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _as_dev(t, name, dtype, shape, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.contiguous()
+
+
+def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be HIP device tensors (torch 'cuda' device)")
+    q = _as_dev(q, "q", in_dtype, (B, H, T, d), dev)
+    k = _as_dev(k, "k", in_dtype, (B, H, T, d), dev)
+    v = _as_dev(v, "v", in_dtype, (B, H, T, d), dev)
+    theta = _as_dev(theta, "theta", torch.float32, (B, H, T), dev)
+    eta = _as_dev(eta, "eta", torch.float32, (B, H, T), dev)
+    alpha = _as_dev(alpha, "alpha", torch.float32, (B, H, T), dev)
+    M0 = _as_dev(M0, "M0", torch.float32, (B, H, d, d), dev)
+    S0 = _as_dev(S0, "S0", torch.float32, (B, H, d, d), dev)
+    if out is None:
+        z = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+        M_T = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+        S_T = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    else:
+        z, M_T, S_T = out
+        for t, nm, shp in ((z, "z", (B, H, T, d)), (M_T, "M_T", (B, H, d, d)), (S_T, "S_T", (B, H, d, d))):
+            if t is not None and (not t.is_contiguous() or t.dtype != torch.float32
+                                  or tuple(t.shape) != shp or t.device != dev):
+                raise ValueError(f"out tensor {nm} must be contiguous float32 {shp} on {dev}")
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        status = getattr(lib, name)(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(M0), _ptr(S0),
+            _ptr(z), _ptr(M_T), _ptr(S_T), B, H, T, d, int(b), stream)
+    _lib.check(name, status)
+    return z, M_T, S_T
+
+
+def ttt_mem_forward_f32(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
+    """float32 linear memory; returns ``(z, M_T, S_T)`` (see include/ttt_mem.h)."""
+    return _forward("ttt_mem_forward_f32", torch.float32, q, k, v, theta, eta, alpha, M0, S0, b, out)
+
+
+def ttt_mem_forward_bf16(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
+    """bf16-input linear memory (float32 state and z); returns ``(z, M_T, S_T)``."""
+    return _forward("ttt_mem_forward_bf16", torch.bfloat16, q, k, v, theta, eta, alpha, M0, S0, b, out)
+
+
+def forward(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
+    """Dispatch on the input dtype (float32 or bfloat16)."""
+    if q.dtype == torch.float32:
+        return ttt_mem_forward_f32(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
+    if q.dtype == torch.bfloat16:
+        return ttt_mem_forward_bf16(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
+    raise TypeError(f"unsupported input dtype {q.dtype}")

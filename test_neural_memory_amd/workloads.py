@@ -1,0 +1,148 @@
+"""Seeded synthetic workloads for the memory kernels (inputs only).
+
+This module draws inputs; it holds none of the memory's arithmetic.  Both the
+HIP path (tests, bench) and the float64 oracle consume exactly these arrays:
+bf16 inputs are rounded once here (round-to-nearest-even, via torch) and the
+oracle reads the rounded values upcast to float64.
+
+The five workloads (shapes, value distributions, chunk sizes):
+
+1. tiny linear memory, float32: B=1 H=1 T=64 d=16 b=8; q, k, v ~ N(0,1) with
+   q and k L2-normalised per token; theta ~ U[0.01, 0.1], eta ~ U[0.8, 0.95],
+   alpha ~ U[0, 0.05]; M0 = S0 = 0.
+2. TTT-Linear-style: B=8 H=12 T=2048 d=64 b=16, bf16 q, k, v as above;
+   theta = 0.05, eta = 0, alpha = 0; M0 ~ N(0, 0.02^2) drawn per head and
+   shared by the batch; S0 = 0.
+3. Titans linear memory: B=4 H=16 T=8192 d=128 b=64, bf16 q, k, v as above;
+   theta = 0.1 sigmoid(N(0,1)), eta = sigmoid(N(2, 0.5)), alpha =
+   0.05 sigmoid(N(-1,1)) per token (second argument of N is the variance);
+   M0 = S0 = 0.
+4. long-context carry: B=1 H=32 T=131072 d=128 b=64, distributions of 3.
+5. deep (2-layer MLP) memory: B=4 H=8 T=4096 d=64 hidden=256 b=16, bf16 q, k,
+   v as above; theta = 0.02, eta = 0.9, alpha = 0.01; W1 ~ N(0, 1/64),
+   W2 ~ N(0, 1/256) per head shared by the batch; momenta 0.
+
+Seeds: ``numpy.random.default_rng(1000 + id)``; draw order q, k, v, theta,
+eta, alpha, then initial states.  Any size can be overridden (for parity cases
+small enough for the oracle) while keeping the distributions.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "to_numpy64"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    id: int
+    name: str
+    B: int
+    H: int
+    T: int
+    d: int
+    b: int
+    dtype: str            # "f32" or "bf16" (q, k, v)
+    gates: str            # "uniform", "const" or "titans"
+    theta: float = 0.0
+    eta: float = 0.0
+    alpha: float = 0.0
+    m0_std: float = 0.0   # per-head N(0, m0_std^2) initial memory, 0 = zeros
+    hidden: int = 0       # > 0: deep (MLP) memory
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    1: Workload(1, "tiny-linear-f32", 1, 1, 64, 16, 8, "f32", "uniform"),
+    2: Workload(2, "ttt-linear-style", 8, 12, 2048, 64, 16, "bf16", "const", theta=0.05, eta=0.0, alpha=0.0,
+                m0_std=0.02),
+    3: Workload(3, "titans-linear", 4, 16, 8192, 128, 64, "bf16", "titans"),
+    4: Workload(4, "long-context-carry", 1, 32, 131072, 128, 64, "bf16", "titans"),
+    5: Workload(5, "deep-mlp-memory", 4, 8, 4096, 64, 16, "bf16", "const", theta=0.02, eta=0.9, alpha=0.01,
+                hidden=256),
+}
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _unit_rows(x):
+    # L2-normalise each token vector (input featurisation, not the memory).
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (x / np.maximum(n, 1e-30)).astype(np.float32)
+
+
+def _normal(rng, shape, chunk=1 << 26):
+    """float32 N(0,1) draws, generated in slices to bound host memory."""
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(-1)
+    for s in range(0, flat.size, chunk):
+        flat[s:s + chunk] = rng.standard_normal(min(chunk, flat.size - s), dtype=np.float32)
+    return out
+
+
+def make_inputs(w: Workload, seed: int | None = None) -> dict:
+    """Draw one workload's inputs as CPU torch tensors.
+
+    Returns a dict with ``q, k, v`` ([B,H,T,d], float32 or bfloat16), ``theta,
+    eta, alpha`` ([B,H,T] float32) and ``M0, S0`` ([B,H,d,d] float32 or None)
+    -- for the deep memory ``W1`` ([B,H,d,hid]), ``W2`` ([B,H,hid,d]) and
+    ``S1, S2`` (None) instead of ``M0, S0``.
+    """
+    rng = np.random.default_rng(1000 + w.id if seed is None else seed)
+    B, H, T, d = w.B, w.H, w.T, w.d
+    shape = (B, H, T, d)
+    q = _unit_rows(_normal(rng, shape))
+    k = _unit_rows(_normal(rng, shape))
+    v = _normal(rng, shape)
+    gshape = (B, H, T)
+    if w.gates == "uniform":
+        theta = rng.uniform(0.01, 0.1, gshape)
+        eta = rng.uniform(0.8, 0.95, gshape)
+        alpha = rng.uniform(0.0, 0.05, gshape)
+    elif w.gates == "const":
+        theta = np.full(gshape, w.theta)
+        eta = np.full(gshape, w.eta)
+        alpha = np.full(gshape, w.alpha)
+    elif w.gates == "titans":
+        theta = 0.1 * _sigmoid(rng.standard_normal(gshape))
+        eta = _sigmoid(rng.normal(2.0, np.sqrt(0.5), gshape))
+        alpha = 0.05 * _sigmoid(rng.normal(-1.0, 1.0, gshape))
+    else:
+        raise ValueError(w.gates)
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    out = {
+        "q": torch.from_numpy(q).to(tdt),
+        "k": torch.from_numpy(k).to(tdt),
+        "v": torch.from_numpy(v).to(tdt),
+        "theta": torch.from_numpy(theta.astype(np.float32)),
+        "eta": torch.from_numpy(eta.astype(np.float32)),
+        "alpha": torch.from_numpy(alpha.astype(np.float32)),
+    }
+    if w.hidden:
+        W1 = rng.standard_normal((H, d, w.hidden)) / np.sqrt(d)
+        W2 = rng.standard_normal((H, w.hidden, d)) / np.sqrt(w.hidden)
+        out["W1"] = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(W1, (B, H, d, w.hidden)), dtype=np.float32))
+        out["W2"] = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(W2, (B, H, w.hidden, d)), dtype=np.float32))
+        out["S1"] = None
+        out["S2"] = None
+    else:
+        if w.m0_std > 0:
+            M0 = rng.standard_normal((H, d, d)) * w.m0_std
+            out["M0"] = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(M0, (B, H, d, d)), dtype=np.float32))
+        else:
+            out["M0"] = None
+        out["S0"] = None
+    return out
+
+
+def to_numpy64(t):
+    """A CPU tensor (any float dtype) as a float64 numpy array; None stays None."""
+    return None if t is None else t.detach().to("cpu", torch.float64).numpy()

@@ -1,0 +1,55 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel launched)."""
+
+import ctypes
+
+import pytest
+
+from test_neural_memory_amd import _lib
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _lib.header_symbols()
+    assert {"ttt_mem_forward_f32", "ttt_mem_forward_bf16", "ttt_mem_status_string",
+            "ttt_mem_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.ttt_mem_abi_version() == (1 << 16)
+    assert lib.ttt_mem_status_string(0) == b"ok"
+    for s in (-1, -2, -3, 12345):
+        assert lib.ttt_mem_status_string(s)
+
+
+def _call(lib, name, ptrs=None, B=1, H=1, T=8, d=16, b=4):
+    p = [None] * 11 if ptrs is None else ptrs
+    return getattr(lib, name)(*p, B, H, T, d, b, None)
+
+
+@pytest.mark.parametrize("name", ["ttt_mem_forward_f32", "ttt_mem_forward_bf16"])
+def test_rejections_happen_before_any_launch(lib, name):
+    # NULL required pointers, bad sizes: every one returns before touching HIP.
+    assert _call(lib, name) == -1                    # NULL q, k, v, ...
+    assert _call(lib, name, d=48) == -2              # unsupported head dim
+    assert _call(lib, name, b=0) == -1
+    assert _call(lib, name, b=65) == -2
+    assert _call(lib, name, T=-1) == -1
+    assert _call(lib, name, B=-2) == -1
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(11)]
+    fake[0] = ctypes.c_void_p(0x1002)               # misaligned q
+    assert _call(lib, name, ptrs=fake) == -1
+    fake = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(11)]
+    fake[8] = fake[0]                                # z aliases q
+    assert _call(lib, name, ptrs=fake) == -1
+
+
+@pytest.mark.parametrize("name", ["ttt_mem_forward_f32", "ttt_mem_forward_bf16"])
+def test_empty_batch_returns_ok_without_pointers(lib, name):
+    assert _call(lib, name, B=0) == 0
+    assert _call(lib, name, H=0) == 0

@@ -1,0 +1,237 @@
+"""GPU parity of the HIP linear-memory path against the float64 oracle.
+
+Every comparison is element by element on the same seeded inputs, measured as
+max|gpu - oracle| / rms(oracle) per output (z, M_T, S_T): <= 1e-4 for the
+float32 path and <= 2e-2 for the bf16-input / float32-accumulate path.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from tests._parity import TOL, rel_err, run_gpu, run_oracle, select, to_dev
+from test_neural_memory_amd import memory as tm
+from test_neural_memory_amd._lib import TTTError
+from test_neural_memory_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check_all(inp, b, tol, heads=None, rows=None):
+    z, M, S = run_gpu(inp, b)
+    zo, Mo, So = run_oracle(inp, b, heads, rows)
+    d = inp["q"].shape[-1]
+    if heads is None:
+        B, H = inp["q"].shape[:2]
+        heads = [(i, j) for i in range(B) for j in range(H)]
+    rows = np.arange(d) if rows is None else np.asarray(rows)
+    errs = (rel_err(select(z, heads, rows), zo),
+            rel_err(select(M, heads, rows, state=True), Mo),
+            rel_err(select(S, heads, rows, state=True), So))
+    _say(f"  errors z={errs[0]:.3e} M_T={errs[1]:.3e} S_T={errs[2]:.3e} (tol {tol})")
+    assert max(errs) <= tol, errs
+    return errs
+
+
+def test_tiny_f32_workload_full():
+    w = WORKLOADS[1]
+    _say(f"case {w.name}")
+    _check_all(make_inputs(w), w.b, TOL["f32"])
+
+
+SMALL = [
+    # (label, workload id, overrides) -- several tiles and a ragged final chunk
+    ("ttt-linear-small", 2, dict(B=2, H=3, T=2048 - 5)),
+    ("titans-small", 3, dict(B=1, H=3, T=1000)),
+    ("titans-small-d64", 3, dict(B=2, H=2, T=777, d=64)),
+    ("long-carry-small", 4, dict(H=2, T=4096 + 33)),
+]
+
+
+@pytest.mark.parametrize("label,wid,kw", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_workloads(label, wid, kw, dtype):
+    w = WORKLOADS[wid].replace(dtype=dtype, **kw)
+    _say(f"case {label} {dtype} {w}")
+    _check_all(make_inputs(w), w.b, TOL[dtype])
+
+
+FULL = [
+    (2, [(0, 0), (3, 7), (7, 11)], None),
+    (3, [(0, 0), (1, 9), (3, 15)], list(range(0, 8)) + list(range(60, 68)) + list(range(120, 128))),
+    (4, [(0, 0), (0, 31)], list(range(0, 4)) + list(range(64, 68)) + list(range(124, 128))),
+]
+
+
+@pytest.mark.parametrize("wid,heads,rows", FULL, ids=[f"workload{f[0]}" for f in FULL])
+def test_full_size_sampled(wid, heads, rows):
+    # Full shapes in the bench's launch configuration; the oracle checks sampled
+    # (batch, head) pairs and value rows (rows are independent problems).
+    w = WORKLOADS[wid]
+    _say(f"case full {w.name}")
+    inp = make_inputs(w)
+    _check_all(inp, w.b, TOL[w.dtype], heads=heads, rows=rows)
+
+
+EDGE = [
+    ("b1", dict(B=1, H=2, T=40, d=32, b=1)),
+    ("b5-ragged", dict(B=1, H=3, T=53, d=64, b=5)),
+    ("b17", dict(B=2, H=1, T=100, d=32, b=17)),
+    ("b33", dict(B=1, H=2, T=200, d=128, b=33)),
+    ("b64-short", dict(B=1, H=1, T=20, d=128, b=64)),
+    ("T1", dict(B=3, H=1, T=1, d=64, b=16)),
+    ("d16", dict(B=2, H=3, T=90, d=16, b=16)),
+    ("odd-bh", dict(B=3, H=5, T=70, d=32, b=8)),
+    ("many-heads", dict(B=8, H=16, T=130, d=64, b=16)),
+]
+
+
+@pytest.mark.parametrize("label,kw", EDGE, ids=[e[0] for e in EDGE])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_shapes(label, kw, dtype):
+    w = WORKLOADS[3].replace(dtype=dtype, **kw)
+    _say(f"case edge {label} {dtype}")
+    inp = make_inputs(w, seed=7)
+    inp["S0"] = torch.randn(w.B, w.H, w.d, w.d) * 0.05
+    inp["M0"] = torch.randn(w.B, w.H, w.d, w.d) * 0.1
+    _check_all(inp, w.b, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_degenerate_gates(dtype):
+    # eta = 0 and alpha = 1 exactly on some tokens, theta = 0 on others.
+    w = WORKLOADS[3].replace(B=1, H=2, T=300, d=64, b=64, dtype=dtype)
+    inp = make_inputs(w, seed=11)
+    inp["eta"][:, :, ::7] = 0.0
+    inp["alpha"][:, :, 5::31] = 1.0
+    inp["theta"][:, :, 3::11] = 0.0
+    inp["M0"] = torch.randn(1, 2, 64, 64) * 0.1
+    _say(f"case degenerate gates {dtype}")
+    _check_all(inp, w.b, TOL[dtype])
+
+
+def test_zero_momentum_everywhere():
+    w = WORKLOADS[2].replace(B=1, H=2, T=500)
+    _say("case eta=alpha=0 (mini-batch delta rule)")
+    _check_all(make_inputs(w), w.b, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_empty_sequence_copies_state(dtype):
+    M0 = torch.randn(2, 3, 32, 32, device="cuda")
+    S0 = torch.randn(2, 3, 32, 32, device="cuda")
+    e = torch.empty(2, 3, 0, 32, device="cuda", dtype=dtype)
+    g = torch.empty(2, 3, 0, device="cuda")
+    z, M, S = tm.forward(e, e, e, g, g, g, M0, S0, b=8)
+    torch.cuda.synchronize()
+    assert z.shape == (2, 3, 0, 32)
+    assert torch.equal(M, M0) and torch.equal(S, S0)
+    z, M, S = tm.forward(e, e, e, g, g, g, None, None, b=8)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(M) == 0 and torch.count_nonzero(S) == 0
+
+
+def test_empty_batch_is_a_noop():
+    e = torch.empty(0, 4, 16, 32, device="cuda", dtype=torch.bfloat16)
+    g = torch.empty(0, 4, 16, device="cuda")
+    z, M, S = tm.forward(e, e, e, g, g, g, b=8)
+    torch.cuda.synchronize()
+    assert z.numel() == 0
+
+
+def _dev_inputs(seed=3, **kw):
+    w = WORKLOADS[3].replace(**kw)
+    inp = make_inputs(w, seed=seed)
+    inp["M0"] = torch.randn(w.B, w.H, w.d, w.d) * 0.1
+    inp["S0"] = torch.randn(w.B, w.H, w.d, w.d) * 0.02
+    return w, to_dev(inp)
+
+
+def test_null_states_equal_zero_states():
+    w, x = _dev_inputs(B=2, H=2, T=150, d=64, b=64)
+    zeros = torch.zeros_like(x["M0"])
+    a = tm.forward(x["q"], x["k"], x["v"], x["theta"], x["eta"], x["alpha"], None, None, b=w.b)
+    c = tm.forward(x["q"], x["k"], x["v"], x["theta"], x["eta"], x["alpha"], zeros, zeros, b=w.b)
+    torch.cuda.synchronize()
+    for p_, q_ in zip(a, c):
+        assert torch.equal(p_, q_)
+
+
+def test_in_place_carry_and_no_state_out():
+    w, x = _dev_inputs(B=2, H=2, T=150, d=128, b=64)
+    ref = tm.forward(x["q"], x["k"], x["v"], x["theta"], x["eta"], x["alpha"], x["M0"], x["S0"], b=w.b)
+    M, S = x["M0"].clone(), x["S0"].clone()
+    z = torch.empty_like(ref[0])
+    tm.forward(x["q"], x["k"], x["v"], x["theta"], x["eta"], x["alpha"], M, S, b=w.b, out=(z, M, S))
+    z2 = torch.empty_like(ref[0])
+    tm.forward(x["q"], x["k"], x["v"], x["theta"], x["eta"], x["alpha"], x["M0"], x["S0"], b=w.b,
+               out=(z2, None, None))
+    torch.cuda.synchronize()
+    assert torch.equal(z, ref[0]) and torch.equal(M, ref[1]) and torch.equal(S, ref[2])
+    assert torch.equal(z2, ref[0])
+
+
+@pytest.mark.parametrize("b,split", [(64, 128), (16, 48), (5, 35)])
+def test_resume_at_chunk_boundary_is_bit_identical(b, split):
+    w, x = _dev_inputs(B=1, H=3, T=300, d=64, b=b)
+    full = tm.forward(x["q"], x["k"], x["v"], x["theta"], x["eta"], x["alpha"], x["M0"], x["S0"], b=b)
+    sl1 = {k: (v[:, :, :split] if k in ("q", "k", "v", "theta", "eta", "alpha") else v) for k, v in x.items()}
+    sl2 = {k: (v[:, :, split:].contiguous() if k in ("q", "k", "v", "theta", "eta", "alpha") else v)
+           for k, v in x.items()}
+    a = tm.forward(sl1["q"].contiguous(), sl1["k"].contiguous(), sl1["v"].contiguous(), sl1["theta"].contiguous(),
+                   sl1["eta"].contiguous(), sl1["alpha"].contiguous(), x["M0"], x["S0"], b=b)
+    c = tm.forward(sl2["q"], sl2["k"], sl2["v"], sl2["theta"], sl2["eta"], sl2["alpha"], a[1], a[2], b=b)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([a[0], c[0]], dim=2), full[0])
+    assert torch.equal(c[1], full[1]) and torch.equal(c[2], full[2])
+
+
+def test_run_to_run_determinism():
+    w, x = _dev_inputs(B=4, H=16, T=1024, d=128, b=64)
+    outs = [tm.forward(x["q"], x["k"], x["v"], x["theta"], x["eta"], x["alpha"], x["M0"], x["S0"], b=64)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for p_, q_ in zip(o, outs[0]):
+            assert torch.equal(p_, q_)
+
+
+def test_argument_errors_are_reported():
+    w, x = _dev_inputs(B=1, H=1, T=64, d=64, b=16)
+    args = (x["q"], x["k"], x["v"], x["theta"], x["eta"], x["alpha"])
+    with pytest.raises(TTTError) as e:
+        tm.forward(*args, b=0)
+    assert e.value.status == -1
+    with pytest.raises(TTTError) as e:
+        tm.forward(*args, b=65)
+    assert e.value.status == -2
+    q48 = torch.zeros(1, 1, 64, 48, device="cuda", dtype=torch.bfloat16)
+    g = x["theta"]
+    with pytest.raises(TTTError) as e:
+        tm.forward(q48, q48, q48, g, g, g, b=16)
+    assert e.value.status == -2
+    # misaligned q (offset by one element inside a larger buffer)
+    buf = torch.zeros(1 * 1 * 64 * 64 + 1, device="cuda", dtype=torch.bfloat16)
+    qm = buf[1:].view(1, 1, 64, 64)
+    with pytest.raises(TTTError) as e:
+        tm.forward(qm, x["k"], x["v"], g, x["eta"], x["alpha"], b=16)
+    assert e.value.status == -1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shapes(seed):
+    rng = np.random.default_rng(100 + seed)
+    d = int(rng.choice([16, 32, 64, 128]))
+    b = int(rng.choice([1, 3, 8, 16, 24, 33, 64]))
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 6))
+    T = int(rng.integers(1, 200))
+    dtype = ["bf16", "f32"][seed % 2]
+    w = WORKLOADS[3].replace(B=B, H=H, T=T, d=d, b=b, dtype=dtype)
+    _say(f"case random {w}")
+    inp = make_inputs(w, seed=seed)
+    inp["M0"] = torch.randn(B, H, d, d) * 0.1
+    _check_all(inp, b, TOL[dtype])
