@@ -1,55 +1,61 @@
 // Chunked TTT / Titans linear memory forward for gfx950 (MI355X), and its C ABI.
 //
-// One workgroup owns RB = 16*NW consecutive rows of one (batch, head) memory
-// and walks that sequence chunk by chunk; each wave keeps a 16-row slice of M
-// and of the momentum S in MFMA accumulator registers for the whole sequence,
-// so the state never leaves the chip between chunks.  Rows of a linear memory
-// evolve independently (row i only meets value coordinate i), so row blocks
-// of one head need no communication.
+// What one workgroup does.  It owns RB = 16*NS consecutive rows of the memory
+// of one (batch, head) sequence and walks that sequence chunk by chunk.  Rows
+// of a linear memory evolve independently (row i only ever meets value
+// coordinate i), so the row blocks of one sequence never communicate.  The
+// workgroup has two kinds of waves:
 //
-// Per chunk of n <= b tokens (padded to NP rows, NP a multiple of 16/32):
-//   1. the chunk's q, k (and a transposed copy of k), the workgroup's columns
-//      of v and the gates are staged in LDS;
-//   2. one wave runs the gate scans across its 64 lanes (lane = token):
-//      A_i = prod_{l<=i} a_l (a = 1 - alpha), E_i = prod_{l<=i} eta_l,
-//      c_i = a_i c_{i-1} + E_i, the chunk-end weights w^M, w^S, and the
-//      helpers of the lower-triangular decay matrix gamma (below);
-//   3. all waves form P = -(tril(Q K^T) .* theta_j gamma_ij) on MFMA;
-//   4. each wave, on MFMA:  E = K M0^T - V              (residuals at chunk start)
-//                           Z^T = A.(M0 Q^T) + c.(S0 Q^T) + E^T P^T
-//                           M  <- A_n M0 + c_n S0 + (K^T (w^M . E))^T
-//                           S  <- E_n S0 + (K^T (w^S . E))^T
-//      with w^M_j = -theta_j gamma_{n-1,j} and w^S_j = -theta_j prod_{l>j} eta_l.
-//      On the bf16-input path the matrix units take fp16 operands (same
-//      rate as bf16 on gfx950, 3 more mantissa bits): bf16 q and k convert
-//      to fp16 exactly in the fp16 normal range, and M0, S0, E and P are
-//      rounded to fp16 once per chunk.  Operands must stay below 65504 in
-//      magnitude; accumulation and the carried state are float32.
+//   * NS state waves.  Each keeps a 16-row slice of M and of the momentum S in
+//     MFMA accumulator registers for the whole sequence (the state never
+//     leaves the chip between chunks) and, per chunk, runs the dual form:
+//        E   = K M0^T - V                          (residuals at chunk start)
+//        Z^T = A.(M0 Q^T) + c.(S0 Q^T) + E^T P^T   (reads of every token)
+//        M   <- A_n M0 + c_n S0 + (K^T (w^M . E))^T
+//        S   <- E_n S0 + (K^T (w^S . E))^T
+//   * two producer waves, one chunk ahead of the state waves.  They prefetch
+//     the next chunks' q, k, v and gates from HBM into registers, stage them
+//     in double-buffered LDS (q and k as MFMA operands, k also transposed, -v
+//     in float32), scan the gates, and build the intra-chunk weight matrix
+//        P = -(tril(Q K^T) .* theta_j gamma_ij)
+//     together with the chunk-end weights w^M, w^S.
 //
-// These are the per-token recurrences S_t = eta_t S_{t-1} - theta_t grad,
-// M_t = (1 - alpha_t) M_{t-1} + S_t, z_t = M_t q_t ("论文速览 | Titans",
-// sections 3.4, 3.7) with every gradient of a chunk taken at the chunk-start
-// memory (same page, section 4.2; "5.1.1 · TTT layers 与 fast weights",
-// section 1.1, eq. (6)), unrolled over the chunk.  With alpha = eta = 0 this
-// is the dual form of that page, eqs. (7)-(9); decay unrolling follows
-// "论文速览 | Titans" sections 4.3-4.5.  Unlike a ratio of cumulative products
-// (beta_t / beta_i there), every weight here is built from products and sums
-// only, so gates equal to zero (eta = 0, alpha = 1) are exact.
+// Per token this is S_t = eta_t S_{t-1} - theta_t grad, M_t = (1 - alpha_t)
+// M_{t-1} + S_t, z_t = M_t q_t ("论文速览 | Titans", sections 3.4 and 3.7), with
+// every gradient of a chunk taken at the chunk-start memory (same page,
+// section 4.2; "5.1.1 · TTT layers 与 fast weights", section 1.1, eq. (6)),
+// unrolled over the chunk.  With alpha = eta = 0 it is the dual form of that
+// page's eqs. (7)-(9); decay and momentum unrolling follow "论文速览 | Titans"
+// sections 4.3-4.5.
 //
-// The decay matrix: gamma_ij = sum_{m=j..i} (prod_{l=m+1..i} a_l)(prod_{l=j+1..m} eta_l)
-// for j <= i.  Per column j the pair (gamma_ij, p_ij = prod_{l=j+1..i} eta_l)
-// follows the 2x2 linear map T_i = [[a_i, eta_i], [0, eta_i]] in i.  Diagonal
-// 16x16 blocks run that recurrence directly (lane = column); a block below the
-// diagonal uses the product of the T's from the end of the column's block to
-// row i (a segmented lane scan plus at most two block products), applied to
-// the column's state at the end of its own block.
+// Gate algebra (a = 1 - alpha; within a chunk, tokens i = 0..n-1):
+//   A_i = prod_{l<=i} a_l,  E_i = prod_{l<=i} eta_l,  c_i = a_i c_{i-1} + E_i,
+//   gamma_ij = sum_{m=j..i} (prod_{l=m+1..i} a_l)(prod_{l=j+1..m} eta_l),
+//   w^M_j = -theta_j gamma_{n-1,j},  w^S_j = -theta_j prod_{l=j+1..n-1} eta_l.
+// All of them are entries of products of the 2x2 maps T_l = [[a_l, eta_l],
+// [0, eta_l]]:  T_i...T_0 = [[A_i, c_i], [0, E_i]], and column j of gamma
+// follows (gamma_ij, p_ij) = T_i...T_{j+1} (1, 1).  One DPP scan of these
+// maps across the 64 lanes (lane = token) gives A, c, E and, after its first
+// four steps, the maps from each 16-token block start; 16x16 blocks on the
+// diagonal of gamma run the column recurrence directly and blocks below it
+// apply block maps to the column states at the end of their own block.  Only
+// products and sums appear -- no ratio of cumulative products (the pages'
+// beta_t / beta_i) -- so gates equal to 0 (eta = 0, alpha = 1) are exact.
 //
-// MFMA operand layout trick: an accumulator tile holds, in lane (n, g), rows
-// 4g..4g+3 of column n.  Storing M transposed (tiles of M^T) puts in each lane
-// four consecutive columns of one row of M, which is exactly a k-slot group of
-// an MFMA A or B operand when the contraction runs over those columns.  So M,
-// S and E feed the next products straight from registers; the operands read
-// from LDS are stored with the matching permutation of the contraction index.
+// MFMA operand layout.  An accumulator tile holds, in lane (n, g), rows
+// 4g..4g+3 of column n.  Keeping M transposed (tiles of M^T) therefore puts in
+// each lane four consecutive columns of one row of M: exactly a k-slot group
+// of an MFMA A or B operand when the contraction runs over those columns.  So
+// M, S and E feed the next products straight from registers, and operands
+// staged in LDS are stored with the matching permutation of the contraction
+// index.
+//
+// Precision.  The float32 path uses float32 MFMA (v_mfma_f32_16x16x4_f32).
+// The bf16-input path uses fp16 operands (v_mfma_f32_16x16x32_f16, same rate
+// as bf16 on gfx950, 3 more mantissa bits): bf16 q and k convert to fp16
+// exactly in the fp16 normal range, and M0, S0, E, P and the chunk weights are
+// rounded to fp16 once per chunk where they enter a product; accumulation and
+// the carried state are float32.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -64,8 +70,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kProducers = 2;
+constexpr int kLdsBytes = 160 * 1024;
 
 __host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
+__host__ __device__ constexpr int cdiv(int x, int m) { return (x + m - 1) / m; }
 
 // ---------------------------------------------------------------------------
 // MFMA operand traits.  A "k-group" is the contraction length of one operand
@@ -98,11 +107,8 @@ struct Op<float> {
     __device__ static frag lds(const float* row, int s, int g) {
         return *reinterpret_cast<const f32x4*>(row + 16 * s + 4 * g);
     }
-    // Store four consecutive contraction indices x..x+3 (x % 4 == 0).
-    __device__ static void put4(float* row, int x, f32x4 v) {
-        *reinterpret_cast<f32x4*>(row + perm(x)) = v;
-    }
-    __device__ static float to_f32(float x) { return x; }
+    // Store contraction indices x..x+3 (x % 4 == 0).
+    __device__ static void put4(float* row, int x, f32x4 v) { *reinterpret_cast<f32x4*>(row + perm(x)) = v; }
 };
 
 template <>
@@ -141,8 +147,40 @@ template <typename T> struct GlobalOf;
 template <> struct GlobalOf<float> { using type = float; };
 template <> struct GlobalOf<_Float16> { using type = uint16_t; };
 
-__device__ inline float g2f(float x) { return x; }
-__device__ inline float g2f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+// Element e of a 16-byte global load, as float.
+__device__ inline float elem(const uint4& r, int e, float) {
+    const uint32_t w = (&r.x)[e];
+    return __uint_as_float(w);
+}
+__device__ inline float elem(const uint4& r, int e, uint16_t) {
+    const uint32_t w = (&r.x)[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+// DPP move with an identity for lanes that have no source (gfx9 controls).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or(float identity, float src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, identity),
+                                                                 __builtin_bit_cast(int, src), CTRL, ROW_MASK,
+                                                                 0xf, false));
+}
+// One inclusive-scan step over 2x2 upper-triangular maps [[X, Y], [0, W]]:
+// mine <- mine * earlier (the earlier map is applied first).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ void tri_step(float& X, float& Y, float& W) {
+    const float xs = dpp_or<CTRL, ROW_MASK>(1.f, X);
+    const float ys = dpp_or<CTRL, ROW_MASK>(0.f, Y);
+    const float ws = dpp_or<CTRL, ROW_MASK>(1.f, W);
+    Y = X * ys + Y * ws;
+    X = X * xs;
+    W = W * ws;
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+__device__ __forceinline__ float readlane(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
 
 struct Params {
     const void* q;
@@ -161,44 +199,344 @@ struct Params {
     int b;
 };
 
-template <typename T, int D, int NW, int NP>
-__global__ __launch_bounds__(kWave * NW) void linear_memory_fwd(const Params p) {
+// Compile-time geometry of one kernel instance.
+template <typename T, int D, int NS, int NP>
+struct Geo {
     using O = Op<T>;
     using G = typename GlobalOf<T>::type;
-    constexpr int RB = 16 * NW;          // rows of M per workgroup
-    constexpr int NRB = D / RB;          // workgroups per (batch, head)
-    constexpr int NC = D / 16;           // 16-column tiles of M
-    constexpr int NT = NP / 16;          // 16-token tiles of a chunk
-    constexpr int KG = O::KG;
-    constexpr int NKC = (D + KG - 1) / KG;     // k-groups over the key dimension
-    constexpr int NKT = NP / KG;               // k-groups over the chunk's tokens
-    constexpr int EPAD = 16 / sizeof(T);       // 16-byte row padding
-    constexpr int LQ = round_up(D, KG) + EPAD; // row stride of sQ, sK
-    constexpr int LKT = NP + EPAD;             // row stride of sKT
-    constexpr int LP = NP + EPAD;              // row stride of sP
-    constexpr int LV = NP + 4;                 // row stride of sVT (float)
-    constexpr int VEC = 16 / sizeof(G);        // elements per 16-byte global load
-    constexpr int NTHR = kWave * NW;
+    static constexpr int RB = 16 * NS;               // rows of M per workgroup
+    static constexpr int NRB = D / RB;               // workgroups per sequence
+    static constexpr int NC = D / 16;                // 16-column tiles of M
+    static constexpr int NT = NP / 16;               // 16-token tiles of a chunk
+    static constexpr int KG = O::KG;
+    static constexpr int NKC = cdiv(D, KG);          // k-groups over the key dimension
+    static constexpr int NKT = NP / KG;              // k-groups over the chunk's tokens
+    static constexpr int EPAD = 16 / sizeof(T);      // 16-byte row padding
+    static constexpr int LQ = round_up(D, KG) + EPAD;
+    static constexpr int LKT = NP + EPAD;
+    static constexpr int LP = NP + EPAD;
+    static constexpr int LV = NP + 4;
+    static constexpr int CB = 16 / sizeof(G);        // elements per 16-byte global load
+    static constexpr int NQB = (NP / 4) * (D / CB);  // 4-token x CB-column blocks of q and k
+    static constexpr int NVB = (NP / 4) * (RB / CB); // 4-token x CB-row blocks of v
+    static constexpr int QBL = cdiv(NQB, kProducers * kWave);
+    static constexpr int VBL = cdiv(NVB, kWave);
+    static constexpr int NWAVE = NS + kProducers;
+    // LDS bytes of one chunk buffer and of the single-buffered gate helpers.
+    static constexpr int BUF_BYTES = (2 * NP * LQ + D * LKT + NP * LP + 2 * NP) * (int)sizeof(T) +
+                                     (RB * LV + 2 * NP + 4) * 4;
+    static constexpr int HELP_BYTES = (2 * NP + 2 * NT * 256 + NT * NP * 3 + 2 * NP) * 4;
+    static constexpr int NBUF = (2 * BUF_BYTES + HELP_BYTES <= kLdsBytes) ? 2 : 1;
     static_assert(NP % KG == 0, "chunk padding must fill whole k-groups");
     static_assert(D % RB == 0, "row blocks must tile d");
+    static_assert(NBUF * BUF_BYTES + HELP_BYTES <= kLdsBytes, "LDS budget");
+};
 
-    __shared__ __attribute__((aligned(16))) T sQ[NP * LQ];
-    __shared__ __attribute__((aligned(16))) T sK[NP * LQ];
-    __shared__ __attribute__((aligned(16))) T sKT[D * LKT];
-    __shared__ __attribute__((aligned(16))) T sP[NP * LP];
-    __shared__ __attribute__((aligned(16))) float sVT[RB * LV];
-    __shared__ __attribute__((aligned(16))) float sGamD[NT * 256];
-    __shared__ __attribute__((aligned(16))) float sPhi[NT * NP * 2];
-    __shared__ __attribute__((aligned(16))) float sTh[NP], sEg[NP], sAg[NP];
-    __shared__ __attribute__((aligned(16))) float sAv[NP], sCv[NP], sWM[NP], sWS[NP];
-    __shared__ __attribute__((aligned(16))) float sGend[NP], sPend[NP];
-    __shared__ float sScal[4];
+template <typename T, int D, int NS, int NP>
+struct Smem {
+    using Gm = Geo<T, D, NS, NP>;
+    struct Buf {
+        T q[NP * Gm::LQ];        // q rows, key dim permuted
+        T k[NP * Gm::LQ];        // k rows, key dim permuted
+        T kt[D * Gm::LKT];       // k^T rows, token dim permuted
+        T p[NP * Gm::LP];        // -P rows, token dim permuted
+        T wm[NP];                // w^M, token dim permuted
+        T ws[NP];                // w^S, token dim permuted
+        float vn[Gm::RB * Gm::LV];  // -v^T for the workgroup's rows
+        float av[NP];            // A_i
+        float cv[NP];            // c_i
+        float scal[4];           // A_n, c_n, E_n
+    };
+    Buf buf[Gm::NBUF];
+    float ga[NP], ge[NP];        // a, eta of the chunk being prepared
+    float gamd[Gm::NT * 256];    // theta_j gamma_ij on diagonal blocks [blk][i][j]
+    float gampd[Gm::NT * 256];   // theta_j p_ij on diagonal blocks
+    float phi[Gm::NT * NP * 3];  // maps from the end of block q to row i [q][i][X,Y,W]
+    float gend[NP], pend[NP];    // theta_j (gamma, p) at the end of column j's block
+};
+
+// Producer-side registers: the next chunk's inputs in flight from HBM.
+template <typename Gm>
+struct Prefetch {
+    uint4 q[Gm::QBL][4];
+    uint4 k[Gm::QBL][4];
+    uint4 v[Gm::VBL][4];
+    float th, et, al;
+};
+
+template <typename T, int D, int NS, int NP>
+struct Kernel {
+    using Gm = Geo<T, D, NS, NP>;
+    using O = Op<T>;
+    using G = typename Gm::G;
+    using F = typename O::frag;
+    using S = Smem<T, D, NS, NP>;
+    using Buf = typename S::Buf;
+    static constexpr int NT = Gm::NT, NC = Gm::NC, KG = Gm::KG, NKC = Gm::NKC, NKT = Gm::NKT;
+    static constexpr int LQ = Gm::LQ, LKT = Gm::LKT, LP = Gm::LP, LV = Gm::LV, CB = Gm::CB, RB = Gm::RB;
+
+    // ---- producers: issue global loads of chunk c into registers ----------
+    __device__ static void issue(Prefetch<Gm>& pf, const Params& p, const G* gq, const G* gk, const G* gv,
+                                 size_t seq_tok, int row_wg, int c, int ptid, int pw, int lane) {
+        const int c0 = c * p.b;
+        const int n = min(p.b, p.T - c0);
+#pragma unroll
+        for (int kk = 0; kk < Gm::QBL; ++kk) {
+            const int u = ptid + kProducers * kWave * kk;
+            const int t4 = u / (D / CB), cb = u % (D / CB);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * t4 + r;
+                if (u < Gm::NQB && t < n) {
+                    const size_t off = (seq_tok + c0 + t) * D + cb * CB;
+                    pf.q[kk][r] = *reinterpret_cast<const uint4*>(gq + off);
+                    pf.k[kk][r] = *reinterpret_cast<const uint4*>(gk + off);
+                } else {
+                    pf.q[kk][r] = uint4{0u, 0u, 0u, 0u};
+                    pf.k[kk][r] = uint4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+        if (pw == 1) {
+#pragma unroll
+            for (int kk = 0; kk < Gm::VBL; ++kk) {
+                const int u = lane + kWave * kk;
+                const int t4 = u / (RB / CB), rb = u % (RB / CB);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * t4 + r;
+                    if (u < Gm::NVB && t < n)
+                        pf.v[kk][r] = *reinterpret_cast<const uint4*>(gv + (seq_tok + c0 + t) * D + row_wg + rb * CB);
+                    else
+                        pf.v[kk][r] = uint4{0u, 0u, 0u, 0u};
+                }
+            }
+        } else {
+            const bool ok = lane < n;
+            const size_t gi = seq_tok + c0 + lane;
+            pf.th = ok ? p.theta[gi] : 0.f;   // padding tokens write nothing
+            pf.et = ok ? p.eta[gi] : 1.f;     // and leave products unchanged
+            pf.al = ok ? p.alpha[gi] : 0.f;
+        }
+    }
+
+    // ---- producers: registers -> LDS chunk buffer --------------------------
+    __device__ static void stage(const Prefetch<Gm>& pf, Buf& B, int ptid, int pw, int lane) {
+        const G tag{};
+#pragma unroll
+        for (int kk = 0; kk < Gm::QBL; ++kk) {
+            const int u = ptid + kProducers * kWave * kk;
+            if (u < Gm::NQB) {
+                const int t4 = u / (D / CB), cb = u % (D / CB);
+                float kv[4][CB];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * t4 + r;
+#pragma unroll
+                    for (int e = 0; e < CB; e += 4) {
+                        O::put4(B.q + t * LQ, cb * CB + e,
+                                f32x4{elem(pf.q[kk][r], e, tag), elem(pf.q[kk][r], e + 1, tag),
+                                      elem(pf.q[kk][r], e + 2, tag), elem(pf.q[kk][r], e + 3, tag)});
+                    }
+#pragma unroll
+                    for (int e = 0; e < CB; ++e) kv[r][e] = elem(pf.k[kk][r], e, tag);
+#pragma unroll
+                    for (int e = 0; e < CB; e += 4)
+                        O::put4(B.k + t * LQ, cb * CB + e, f32x4{kv[r][e], kv[r][e + 1], kv[r][e + 2], kv[r][e + 3]});
+                }
+#pragma unroll
+                for (int e = 0; e < CB; ++e)
+                    O::put4(B.kt + (cb * CB + e) * LKT, 4 * t4, f32x4{kv[0][e], kv[1][e], kv[2][e], kv[3][e]});
+            }
+        }
+        if (pw == 1) {
+#pragma unroll
+            for (int kk = 0; kk < Gm::VBL; ++kk) {
+                const int u = lane + kWave * kk;
+                if (u < Gm::NVB) {
+                    const int t4 = u / (RB / CB), rb = u % (RB / CB);
+#pragma unroll
+                    for (int e = 0; e < CB; ++e)
+                        *reinterpret_cast<f32x4*>(B.vn + (rb * CB + e) * LV + 4 * t4) =
+                            -f32x4{elem(pf.v[kk][0], e, tag), elem(pf.v[kk][1], e, tag),
+                                   elem(pf.v[kk][2], e, tag), elem(pf.v[kk][3], e, tag)};
+                }
+            }
+        }
+    }
+
+    // ---- producer wave 0: gate scans and decay-matrix helpers --------------
+    __device__ static void gates(const Prefetch<Gm>& pf, S& sm, Buf& B, int n, int lane) {
+        const int l = lane;
+        const float th = pf.th, et = pf.et, a = 1.f - pf.al;
+        if (l < NP) { sm.ga[l] = a; sm.ge[l] = et; }
+        // Inclusive prefix of T_l within 16-lane rows: Psi_l = T_l ... T_{16*(l/16)}.
+        float X = a, Y = et, W = et;
+        tri_step<kRowShr1>(X, Y, W);
+        tri_step<kRowShr2>(X, Y, W);
+        tri_step<kRowShr4>(X, Y, W);
+        tri_step<kRowShr8>(X, Y, W);
+        const float px = X, py = Y, pwv = W;
+        // Extend to the whole wave: T_l ... T_0 = [[A_l, c_l], [0, E_l]].
+        tri_step<kRowBcast15, 0xa>(X, Y, W);
+        tri_step<kRowBcast31, 0xc>(X, Y, W);
+        if (l < NP) { B.av[l] = X; B.cv[l] = Y; }
+        if (l == n - 1) { B.scal[0] = X; B.scal[1] = Y; B.scal[2] = W; }
+        // Maps from the end of block q to row l, for every block q below l's block.
+        float BX[NT], BY[NT], BW[NT];
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            BX[q] = readlane(px, 16 * q + 15);
+            BY[q] = readlane(py, 16 * q + 15);
+            BW[q] = readlane(pwv, 16 * q + 15);
+        }
+        if (l < NP) {
+            const int pb = l >> 4;
+            float cx = px, cy = py, cw = pwv;
+#pragma unroll
+            for (int q = NT - 2; q >= 0; --q) {
+                if (q < pb) {
+                    float* dst = sm.phi + (q * NP + l) * 3;
+                    dst[0] = cx; dst[1] = cy; dst[2] = cw;
+                    const float ny = cx * BY[q] + cy * BW[q];
+                    cx *= BX[q];
+                    cw *= BW[q];
+                    cy = ny;
+                }
+            }
+        }
+        // Diagonal 16x16 blocks: lane = (block, column j), rows run in order.
+        const int qb = l >> 4, jj = l & 15;
+        if (qb < NT) {
+            float pp = 0.f, gg = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int i = 16 * qb + s;
+                const float ai = sm.ga[i], ei = sm.ge[i];
+                if (s == jj) { pp = 1.f; gg = 1.f; }
+                else if (s > jj) { pp = ei * pp; gg = ai * gg + pp; }
+                sm.gamd[(qb * 16 + s) * 16 + jj] = th * gg;
+                sm.gampd[(qb * 16 + s) * 16 + jj] = th * pp;
+            }
+            sm.gend[l] = th * gg;
+            sm.pend[l] = th * pp;
+        }
+    }
+
+    // ---- producers: P tiles and the chunk-end weights ----------------------
+    __device__ static void ptiles(S& sm, Buf& B, int n, int pw, int lr, int lg) {
+        const int ilast = n - 1;
+        for (int u = pw; u < NT * NT; u += kProducers) {
+            const int pb = u / NT, qb = u % NT;
+            const int i = 16 * pb + lr;
+            const int jb = 16 * qb + 4 * lg;
+            if (pb < qb) {
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                O::put4(B.p + i * LP, jb, zero);
+                if (i == ilast) { O::put4(B.wm, jb, zero); O::put4(B.ws, jb, zero); }
+                continue;
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKC; ++s)
+                acc = O::mma(acc, O::lds(B.k + (16 * qb + lr) * LQ, s, lg), O::lds(B.q + i * LQ, s, lg));
+            // acc[e] = q_i . k_j for j = jb + e
+            f32x4 L, LPe;
+            if (pb == qb) {
+                L = *reinterpret_cast<const f32x4*>(sm.gamd + (qb * 16 + lr) * 16 + 4 * lg);
+                LPe = *reinterpret_cast<const f32x4*>(sm.gampd + (qb * 16 + lr) * 16 + 4 * lg);
+            } else {
+                const float* ph = sm.phi + (qb * NP + i) * 3;
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(sm.gend + jb);
+                const f32x4 pv = *reinterpret_cast<const f32x4*>(sm.pend + jb);
+                L = ph[0] * gv + ph[1] * pv;
+                LPe = ph[2] * pv;
+            }
+            O::put4(B.p + i * LP, jb, -(acc * L));
+            if (i == ilast) { O::put4(B.wm, jb, -L); O::put4(B.ws, jb, -LPe); }
+        }
+    }
+
+    // ---- state waves ------------------------------------------------------
+    // Phase 1: residuals E, reads z; returns E as MFMA fragments.
+    __device__ static void phase1(const f32x4* Macc, const f32x4* Sacc, const Buf& B, F* EB, float* z,
+                                  size_t zrow0, int n, int w, int lr, int lg) {
+        F MB[NKC], SB[NKC];
+#pragma unroll
+        for (int s = 0; s < NKC; ++s) {
+            MB[s] = O::template from_acc<NC>(Macc, s);
+            SB[s] = O::template from_acc<NC>(Sacc, s);
+        }
+        f32x4 E[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            E[tt] = *reinterpret_cast<const f32x4*>(B.vn + (16 * w + lr) * LV + 16 * tt + 4 * lg);
+#pragma unroll
+            for (int s = 0; s < NKC; ++s) E[tt] = O::mma(E[tt], O::lds(B.k + (16 * tt + lr) * LQ, s, lg), MB[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < NKT; ++s) EB[s] = O::template from_acc<NT>(E, s);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 za = {0.f, 0.f, 0.f, 0.f}, zc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKC; ++s) {
+                const F bq = O::lds(B.q + (16 * tt + lr) * LQ, s, lg);
+                za = O::mma(za, MB[s], bq);
+                zc = O::mma(zc, SB[s], bq);
+            }
+            const int t = 16 * tt + lr;
+            f32x4 zt = B.av[t] * za + B.cv[t] * zc;
+#pragma unroll
+            for (int s = 0; s < NKT; ++s)
+                if (KG * s <= 16 * tt + 15) zt = O::mma(zt, EB[s], O::lds(B.p + t * LP, s, lg));
+            if (t < n) *reinterpret_cast<f32x4*>(z + zrow0 + static_cast<size_t>(t) * D) = zt;
+        }
+    }
+
+    // Phase 2: state update from the residual fragments.
+    __device__ static void phase2(f32x4* Macc, f32x4* Sacc, const Buf& B, const F* EB, int lr, int lg) {
+        F WMB[NKT], WSB[NKT];
+#pragma unroll
+        for (int s = 0; s < NKT; ++s) {
+            WMB[s] = EB[s] * O::lds(B.wm, s, lg);
+            WSB[s] = EB[s] * O::lds(B.ws, s, lg);
+        }
+        const float An = B.scal[0], Cn = B.scal[1], En = B.scal[2];
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+            Macc[ct] = An * Macc[ct] + Cn * Sacc[ct];
+            Sacc[ct] = En * Sacc[ct];
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) {
+                const F a = O::lds(B.kt + (16 * ct + lr) * LKT, s, lg);
+                Macc[ct] = O::mma(Macc[ct], a, WMB[s]);
+                Sacc[ct] = O::mma(Sacc[ct], a, WSB[s]);
+            }
+        }
+    }
+};
+
+template <typename T, int D, int NS, int NP>
+__global__ __launch_bounds__(kWave * (NS + kProducers)) void linear_memory_fwd(const Params p) {
+    using Gm = Geo<T, D, NS, NP>;
+    using K = Kernel<T, D, NS, NP>;
+    using G = typename Gm::G;
+    using F = typename Op<T>::frag;
+    constexpr int NBUF = Gm::NBUF;
+    constexpr int NC = Gm::NC;
+    constexpr int RB = Gm::RB;
+
+    __shared__ __attribute__((aligned(16))) typename K::S sm;
 
     const int tid = threadIdx.x;
     const int w = tid / kWave;
     const int lane = tid % kWave;
     const int lr = lane & 15;   // MFMA row/column index within a 16-tile
     const int lg = lane >> 4;   // MFMA k-slot group
+    const bool is_state = w < NS;
+    const int pw = w - NS;      // producer index (0, 1) for producer waves
+    const int ptid = tid - NS * kWave;
 
     // Workgroup -> (sequence, row block).  When the count allows, the row
     // blocks of one sequence get workgroup ids that are congruent mod 8, so
@@ -206,319 +544,125 @@ __global__ __launch_bounds__(kWave * NW) void linear_memory_fwd(const Params p) 
     const int nwg = gridDim.x;
     int lin = blockIdx.x;
     if ((p.BH % 8) == 0) lin = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
-    const int bh = lin / NRB;
-    const int rb = lin % NRB;
+    const int bh = lin / Gm::NRB;
+    const int rb = lin % Gm::NRB;
     const int seqlen = p.T;
     const int b = p.b;
-    const int row_wg = rb * RB;          // first row of M in this workgroup
-    const int row_w = row_wg + 16 * w;   // first row of this wave's slice
+    const int row_wg = rb * RB;
+    const int row_w = row_wg + 16 * w;
+    const int nch = (seqlen + b - 1) / b;
+    const size_t seq_tok = static_cast<size_t>(bh) * seqlen;
+    const G* __restrict__ gq = static_cast<const G*>(p.q);
+    const G* __restrict__ gk = static_cast<const G*>(p.k);
+    const G* __restrict__ gv = static_cast<const G*>(p.v);
 
     // Zero the staging tiles once: padding columns (d < 32 on the fp16 path) stay 0.
-    for (int i = tid; i < NP * LQ; i += NTHR) { sQ[i] = T(0.f); sK[i] = T(0.f); }
-    for (int i = tid; i < D * LKT; i += NTHR) sKT[i] = T(0.f);
-    for (int i = tid; i < NP * LP; i += NTHR) sP[i] = T(0.f);
+    {
+        uint32_t* words = reinterpret_cast<uint32_t*>(&sm);
+        for (int i = tid; i < static_cast<int>(sizeof(sm) / 4); i += kWave * Gm::NWAVE) words[i] = 0u;
+    }
 
     // State slice: lane (lr, lg) of tile ct holds M[row_w + lr][16ct + 4lg + i].
     f32x4 Macc[NC], Sacc[NC];
     const size_t state_off = static_cast<size_t>(bh) * D * D + static_cast<size_t>(row_w + lr) * D;
-#pragma unroll
-    for (int ct = 0; ct < NC; ++ct) {
-        const int col = 16 * ct + 4 * lg;
-        Macc[ct] = p.M0 ? *reinterpret_cast<const f32x4*>(p.M0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-        Sacc[ct] = p.S0 ? *reinterpret_cast<const f32x4*>(p.S0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const G* __restrict__ gq = static_cast<const G*>(p.q);
-    const G* __restrict__ gk = static_cast<const G*>(p.k);
-    const G* __restrict__ gv = static_cast<const G*>(p.v);
-    const size_t seq_tok = static_cast<size_t>(bh) * seqlen;   // first token row of this sequence
-
-    for (int c0 = 0; c0 < seqlen; c0 += b) {
-        const int n = min(b, seqlen - c0);
-        __syncthreads();   // the previous chunk is done with every LDS buffer
-
-        // ---- 1. stage the chunk in LDS ------------------------------------
-        for (int u = tid; u < NP * (D / VEC); u += NTHR) {
-            const int t = u / (D / VEC);
-            const int c = (u % (D / VEC)) * VEC;
-            float qv[VEC], kv[VEC];
-            if (t < n) {
-                const size_t off = (seq_tok + c0 + t) * D + c;
-                const uint4 rq = *reinterpret_cast<const uint4*>(gq + off);
-                const uint4 rk = *reinterpret_cast<const uint4*>(gk + off);
-                const G* eq = reinterpret_cast<const G*>(&rq);
-                const G* ek = reinterpret_cast<const G*>(&rk);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) { qv[e] = g2f(eq[e]); kv[e] = g2f(ek[e]); }
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) { qv[e] = 0.f; kv[e] = 0.f; }
-            }
-#pragma unroll
-            for (int e = 0; e < VEC; e += 4) {
-                O::put4(sQ + t * LQ, c + e, f32x4{qv[e], qv[e + 1], qv[e + 2], qv[e + 3]});
-                O::put4(sK + t * LQ, c + e, f32x4{kv[e], kv[e + 1], kv[e + 2], kv[e + 3]});
-            }
-            const int pt = O::perm(t);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) sKT[(c + e) * LKT + pt] = T(kv[e]);
-        }
-        for (int u = tid; u < NP * (RB / VEC); u += NTHR) {
-            const int t = u / (RB / VEC);
-            const int r = (u % (RB / VEC)) * VEC;
-            float vv[VEC];
-            if (t < n) {
-                const uint4 rv = *reinterpret_cast<const uint4*>(gv + (seq_tok + c0 + t) * D + row_wg + r);
-                const G* ev = reinterpret_cast<const G*>(&rv);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) vv[e] = g2f(ev[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) vv[e] = 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) sVT[(r + e) * LV + t] = vv[e];
-        }
-        if (tid < NP) {
-            const bool ok = tid < n;
-            const size_t gi = seq_tok + c0 + tid;
-            sTh[tid] = ok ? p.theta[gi] : 0.f;          // padded tokens write nothing
-            sEg[tid] = ok ? p.eta[gi] : 1.f;            // and leave products unchanged
-            sAg[tid] = ok ? 1.f - p.alpha[gi] : 1.f;
-        }
-        __syncthreads();
-
-        // ---- 2. gate scans (wave 0, lane = token) --------------------------
-        if (w == 0) {
-            const int l = lane;
-            const float th = l < NP ? sTh[l] : 0.f;
-            const float et = l < NP ? sEg[l] : 1.f;
-            const float a = l < NP ? sAg[l] : 1.f;
-            // E_i: inclusive prefix product of eta.
-            float E = et;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const float y = __shfl_up(E, o);
-                if (l >= o) E *= y;
-            }
-            // (A_i, c_i): prefix composition of the affine maps x -> a_i x + E_i.
-            float m = a, cc = E;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const float mp = __shfl_up(m, o);
-                const float cp = __shfl_up(cc, o);
-                if (l >= o) { cc = m * cp + cc; m = m * mp; }
-            }
-            // Exclusive suffix products of a and eta (padding lanes hold 1).
-            float sa = a, se = et;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const float ya = __shfl_down(sa, o);
-                const float ye = __shfl_down(se, o);
-                if (l + o < kWave) { sa *= ya; se *= ye; }
-            }
-            float SA = __shfl_down(sa, 1);
-            float SE = __shfl_down(se, 1);
-            if (l == kWave - 1) { SA = 1.f; SE = 1.f; }
-            // gamma_{n-1,j} = SA_j + eta_{j+1} gamma_{n-1,j+1}, zero past the last token:
-            // suffix composition of x -> mu_j x + nu_j.
-            const float et_next = __shfl_down(et, 1);
-            float mu = (l < n - 1) ? et_next : 0.f;
-            float nu = (l < n) ? SA : 0.f;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const float mq = __shfl_down(mu, o);
-                const float nq = __shfl_down(nu, o);
-                if (l + o < kWave) { nu = mu * nq + nu; mu = mu * mq; }
-            }
-            if (l < NP) {
-                sAv[l] = m;
-                sCv[l] = cc;
-                sWM[l] = -th * nu;
-                sWS[l] = -th * SE;
-            }
-            if (l == n - 1) { sScal[0] = m; sScal[1] = cc; sScal[2] = E; }
-
-            // Diagonal 16x16 blocks of theta_j gamma_ij: lane = (block, column).
-            const int qb = l >> 4, jj = l & 15;
-            if (qb < NT) {
-                const int j = 16 * qb + jj;
-                const float thj = sTh[j];
-                float pp = 0.f, gg = 0.f;
-#pragma unroll
-                for (int s = 0; s < 16; ++s) {
-                    const int i = 16 * qb + s;
-                    const float ai = sAg[i], ei = sEg[i];
-                    if (s == jj) { pp = 1.f; gg = 1.f; }
-                    else if (s > jj) { pp = ei * pp; gg = ai * gg + pp; }
-                    sGamD[(qb * 16 + s) * 16 + jj] = thj * gg;
-                }
-                sGend[j] = thj * gg;
-                sPend[j] = thj * pp;
-            }
-
-            // Transfer maps for rows below a block: Psi_i = T_i ... T_{16*blk(i)}
-            // as (X, Y, W) = [[X, Y], [0, W]], then products with whole blocks.
-            float X = a, Y = et, W = et;
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-                const float xp = __shfl_up(X, o), yp = __shfl_up(Y, o), wp = __shfl_up(W, o);
-                if ((l & 15) >= o) { Y = X * yp + Y * wp; X = X * xp; W = W * wp; }
-            }
-            float BX[NT], BY[NT], BW[NT];
-#pragma unroll
-            for (int q = 0; q < NT; ++q) {
-                BX[q] = __shfl(X, 16 * q + 15);
-                BY[q] = __shfl(Y, 16 * q + 15);
-                BW[q] = __shfl(W, 16 * q + 15);
-            }
-            if (l < NP) {
-                const int pb = l >> 4;
-                float cx = X, cy = Y, cw = W;
-#pragma unroll
-                for (int q = NT - 2; q >= 0; --q) {
-                    if (q < pb) {
-                        sPhi[(q * NP + l) * 2 + 0] = cx;
-                        sPhi[(q * NP + l) * 2 + 1] = cy;
-                        // extend the map over block q for the next block up
-                        const float ny = cx * BY[q] + cy * BW[q];
-                        cx = cx * BX[q];
-                        cw = cw * BW[q];
-                        cy = ny;
-                    }
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- 3. P = -(tril(Q K^T) .* theta_j gamma_ij), stored as B operand rows
-        for (int u = w; u < NT * NT; u += NW) {
-            const int pb = u / NT, qb = u % NT;
-            const int i = 16 * pb + lr;
-            if (pb < qb) {
-                O::put4(sP + i * LP, 16 * qb + 4 * lg, f32x4{0.f, 0.f, 0.f, 0.f});
-                continue;
-            }
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < NKC; ++s)
-                acc = O::mma(acc, O::lds(sK + (16 * qb + lr) * LQ, s, lg), O::lds(sQ + i * LQ, s, lg));
-            // acc[e] = q_i . k_j for j = 16qb + 4lg + e
-            f32x4 L;
-            if (pb == qb) {
-                L = *reinterpret_cast<const f32x4*>(sGamD + (qb * 16 + lr) * 16 + 4 * lg);
-            } else {
-                const float x = sPhi[(qb * NP + i) * 2 + 0];
-                const float y = sPhi[(qb * NP + i) * 2 + 1];
-                const f32x4 gv = *reinterpret_cast<const f32x4*>(sGend + 16 * qb + 4 * lg);
-                const f32x4 pv = *reinterpret_cast<const f32x4*>(sPend + 16 * qb + 4 * lg);
-                L = x * gv + y * pv;
-            }
-            O::put4(sP + i * LP, 16 * qb + 4 * lg, -(acc * L));
-        }
-        __syncthreads();
-
-        // ---- 4. residuals, read-out and state update (per wave) ------------
-        using F = typename O::frag;
-        F MB[NKC], SB[NKC];
-#pragma unroll
-        for (int s = 0; s < NKC; ++s) {
-            MB[s] = O::template from_acc<NC>(Macc, s);
-            SB[s] = O::template from_acc<NC>(Sacc, s);
-        }
-        // E = K M0^T - V; lane (lr, lg) of tile tt holds E[16tt + 4lg + e][row_w + lr].
-        f32x4 Eacc[NT];
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            Eacc[tt] = -*reinterpret_cast<const f32x4*>(sVT + (16 * w + lr) * LV + 16 * tt + 4 * lg);
-#pragma unroll
-            for (int s = 0; s < NKC; ++s)
-                Eacc[tt] = O::mma(Eacc[tt], O::lds(sK + (16 * tt + lr) * LQ, s, lg), MB[s]);
-        }
-        // Z^T = A.(M0 Q^T) + c.(S0 Q^T) + E^T P^T; lane (lr, lg) of tile tt holds
-        // z[token 16tt + lr][row_w + 4lg + e].
-        F EB[NKT];
-#pragma unroll
-        for (int s = 0; s < NKT; ++s) EB[s] = O::template from_acc<NT>(Eacc, s);
-        const size_t zrow0 = (seq_tok + c0) * D + row_w + 4 * lg;
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 za = {0.f, 0.f, 0.f, 0.f}, zc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < NKC; ++s) {
-                const F bq = O::lds(sQ + (16 * tt + lr) * LQ, s, lg);
-                za = O::mma(za, MB[s], bq);
-                zc = O::mma(zc, SB[s], bq);
-            }
-            const int t = 16 * tt + lr;
-            f32x4 zt = sAv[t] * za + sCv[t] * zc;
-#pragma unroll
-            for (int s = 0; s < NKT; ++s)
-                if (KG * s <= 16 * tt + 15) zt = O::mma(zt, EB[s], O::lds(sP + t * LP, s, lg));
-            if (t < n) *reinterpret_cast<f32x4*>(p.z + zrow0 + static_cast<size_t>(t) * D) = zt;
-        }
-        // M <- A_n M0 + c_n S0 + (K^T (w^M . E))^T,  S <- E_n S0 + (K^T (w^S . E))^T
-        f32x4 EM[NT], ES[NT];
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            EM[tt] = Eacc[tt] * *reinterpret_cast<const f32x4*>(sWM + 16 * tt + 4 * lg);
-            ES[tt] = Eacc[tt] * *reinterpret_cast<const f32x4*>(sWS + 16 * tt + 4 * lg);
-        }
-        F WMB[NKT], WSB[NKT];
-#pragma unroll
-        for (int s = 0; s < NKT; ++s) {
-            WMB[s] = O::template from_acc<NT>(EM, s);
-            WSB[s] = O::template from_acc<NT>(ES, s);
-        }
-        const float An = sScal[0], Cn = sScal[1], En = sScal[2];
+    if (is_state) {
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
-            Macc[ct] = An * Macc[ct] + Cn * Sacc[ct];
-            Sacc[ct] = En * Sacc[ct];
-#pragma unroll
-            for (int s = 0; s < NKT; ++s) {
-                const F a = O::lds(sKT + (16 * ct + lr) * LKT, s, lg);
-                Macc[ct] = O::mma(Macc[ct], a, WMB[s]);
-                Sacc[ct] = O::mma(Sacc[ct], a, WSB[s]);
+            const int col = 16 * ct + 4 * lg;
+            Macc[ct] = p.M0 ? *reinterpret_cast<const f32x4*>(p.M0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+            Sacc[ct] = p.S0 ? *reinterpret_cast<const f32x4*>(p.S0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __syncthreads();
+
+    Prefetch<Gm> pf;
+    F EB[Gm::NKT];
+    auto chunk_n = [&](int c) { return min(b, seqlen - c * b); };
+
+    if constexpr (NBUF == 2) {
+        if (nch > 0 && !is_state) {
+            K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, 0, ptid, pw, lane);
+            K::stage(pf, sm.buf[0], ptid, pw, lane);
+            if (pw == 0) K::gates(pf, sm, sm.buf[0], chunk_n(0), lane);
+            if (nch > 1) K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, 1, ptid, pw, lane);
+        }
+        __syncthreads();
+        if (nch > 0 && !is_state) K::ptiles(sm, sm.buf[0], chunk_n(0), pw, lr, lg);
+        __syncthreads();
+        for (int c = 0; c < nch; ++c) {
+            const int bf = c & 1;
+            if (is_state) {
+                K::phase1(Macc, Sacc, sm.buf[bf], EB, p.z, (seq_tok + static_cast<size_t>(c) * b) * D + row_w + 4 * lg,
+                          chunk_n(c), w, lr, lg);
+            } else if (c + 1 < nch) {
+                K::stage(pf, sm.buf[bf ^ 1], ptid, pw, lane);
+                if (pw == 0) K::gates(pf, sm, sm.buf[bf ^ 1], chunk_n(c + 1), lane);
+                if (c + 2 < nch) K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, c + 2, ptid, pw, lane);
             }
+            __syncthreads();
+            if (is_state) {
+                K::phase2(Macc, Sacc, sm.buf[bf], EB, lr, lg);
+            } else if (c + 1 < nch) {
+                K::ptiles(sm, sm.buf[bf ^ 1], chunk_n(c + 1), pw, lr, lg);
+            }
+            __syncthreads();
+        }
+    } else {
+        for (int c = 0; c < nch; ++c) {
+            if (!is_state) {
+                K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, c, ptid, pw, lane);
+                K::stage(pf, sm.buf[0], ptid, pw, lane);
+                if (pw == 0) K::gates(pf, sm, sm.buf[0], chunk_n(c), lane);
+            }
+            __syncthreads();
+            if (!is_state) K::ptiles(sm, sm.buf[0], chunk_n(c), pw, lr, lg);
+            __syncthreads();
+            if (is_state) {
+                K::phase1(Macc, Sacc, sm.buf[0], EB, p.z, (seq_tok + static_cast<size_t>(c) * b) * D + row_w + 4 * lg,
+                          chunk_n(c), w, lr, lg);
+                K::phase2(Macc, Sacc, sm.buf[0], EB, lr, lg);
+            }
+            __syncthreads();
         }
     }
 
+    if (is_state) {
 #pragma unroll
-    for (int ct = 0; ct < NC; ++ct) {
-        const int col = 16 * ct + 4 * lg;
-        if (p.MT) *reinterpret_cast<f32x4*>(p.MT + state_off + col) = Macc[ct];
-        if (p.ST) *reinterpret_cast<f32x4*>(p.ST + state_off + col) = Sacc[ct];
+        for (int ct = 0; ct < NC; ++ct) {
+            const int col = 16 * ct + 4 * lg;
+            if (p.MT) *reinterpret_cast<f32x4*>(p.MT + state_off + col) = Macc[ct];
+            if (p.ST) *reinterpret_cast<f32x4*>(p.ST + state_off + col) = Sacc[ct];
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Host side: validation, instance selection, launch.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int NP>
+template <typename T, int D, int NS, int NP>
 hipError_t launch(const Params& p, hipStream_t stream) {
-    constexpr int RB = 16 * NW;
-    const long long nwg = static_cast<long long>(p.BH) * (D / RB);
-    hipLaunchKernelGGL((linear_memory_fwd<T, D, NW, NP>), dim3(static_cast<unsigned>(nwg)),
-                       dim3(kWave * NW), 0, stream, p);
+    using Gm = Geo<T, D, NS, NP>;
+    const long long nwg = static_cast<long long>(p.BH) * Gm::NRB;
+    hipLaunchKernelGGL((linear_memory_fwd<T, D, NS, NP>), dim3(static_cast<unsigned>(nwg)),
+                       dim3(kWave * Gm::NWAVE), 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NS>
 hipError_t launch_np(const Params& p, int np, hipStream_t stream) {
     if constexpr (Op<T>::KG == 32) {
-        return np <= 32 ? launch<T, D, NW, 32>(p, stream) : launch<T, D, NW, 64>(p, stream);
+        return np <= 32 ? launch<T, D, NS, 32>(p, stream) : launch<T, D, NS, 64>(p, stream);
     } else {
-        if (np <= 16) return launch<T, D, NW, 16>(p, stream);
-        if (np <= 32) return launch<T, D, NW, 32>(p, stream);
-        return launch<T, D, NW, 64>(p, stream);
+        if (np <= 16) return launch<T, D, NS, 16>(p, stream);
+        if (np <= 32) return launch<T, D, NS, 32>(p, stream);
+        return launch<T, D, NS, 64>(p, stream);
     }
 }
 
 template <typename T, int D>
-hipError_t launch_nw(const Params& p, int np, hipStream_t stream) {
+hipError_t launch_ns(const Params& p, int np, hipStream_t stream) {
     if constexpr (D >= 32) {
-        // Two waves per workgroup when that still leaves >= 256 workgroups.
+        // Two state waves (32 rows) per workgroup when that still leaves >= 256 workgroups.
         const long long row_tiles = static_cast<long long>(p.BH) * (D / 16);
         if (row_tiles >= 512) return launch_np<T, D, 2>(p, np, stream);
     }
@@ -529,10 +673,10 @@ template <typename T>
 hipError_t dispatch(const Params& p, int d, hipStream_t stream) {
     const int np = round_up(p.b, 16);
     switch (d) {
-        case 16: return launch_nw<T, 16>(p, np, stream);
-        case 32: return launch_nw<T, 32>(p, np, stream);
-        case 64: return launch_nw<T, 64>(p, np, stream);
-        default: return launch_nw<T, 128>(p, np, stream);
+        case 16: return launch_ns<T, 16>(p, np, stream);
+        case 32: return launch_ns<T, 32>(p, np, stream);
+        case 64: return launch_ns<T, 64>(p, np, stream);
+        default: return launch_ns<T, 128>(p, np, stream);
     }
 }
 
