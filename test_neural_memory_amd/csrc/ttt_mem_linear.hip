@@ -4,7 +4,8 @@
 // of one (batch, head) sequence and walks that sequence chunk by chunk.  Rows
 // of a linear memory evolve independently (row i only ever meets value
 // coordinate i), so the row blocks of one sequence never communicate.  The
-// workgroup has two kinds of waves:
+// workgroup has two kinds of waves, each running its own loop (the loops
+// execute the same barriers):
 //
 //   * NS state waves.  Each keeps a 16-row slice of M and of the momentum S in
 //     MFMA accumulator registers for the whole sequence (the state never
@@ -15,9 +16,8 @@
 //        S   <- E_n S0 + (K^T (w^S . E))^T
 //   * two producer waves, one chunk ahead of the state waves.  They prefetch
 //     the next chunks' q, k, v and gates from HBM into registers, stage them
-//     in double-buffered LDS (q and k as MFMA operands, k also transposed, -v
-//     in float32), scan the gates, and build the intra-chunk weight matrix
-//        P = -(tril(Q K^T) .* theta_j gamma_ij)
+//     in double-buffered LDS as MFMA operands, scan the gates, and build the
+//     intra-chunk weight matrix P = -(tril(Q K^T) .* theta_j gamma_ij)
 //     together with the chunk-end weights w^M, w^S.
 //
 // Per token this is S_t = eta_t S_{t-1} - theta_t grad, M_t = (1 - alpha_t)
@@ -44,11 +44,16 @@
 //
 // MFMA operand layout.  An accumulator tile holds, in lane (n, g), rows
 // 4g..4g+3 of column n.  Keeping M transposed (tiles of M^T) therefore puts in
-// each lane four consecutive columns of one row of M: exactly a k-slot group
-// of an MFMA A or B operand when the contraction runs over those columns.  So
-// M, S and E feed the next products straight from registers, and operands
-// staged in LDS are stored with the matching permutation of the contraction
-// index.
+// each lane four consecutive columns of one row of M -- a k-slot group of an
+// MFMA operand when the contraction runs over those columns -- so M, S and E
+// feed the next products straight from registers.  On the fp16 path a
+// 32-wide k-group holds two 16-row tiles; tile 2s+h, row m stands for index
+// 32s + 8(m/4) + 4h + m%4, so that lane group g of a fragment carries the
+// eight consecutive indices 32s + 8g .. 32s + 8g + 7, and LDS operands are
+// plain row-major tiles (XOR-swizzled in 16-byte chunks to avoid LDS bank
+// conflicts).  Operands that are needed transposed (k for the state update,
+// v for the residuals) are read with the gfx950 LDS transpose load
+// (ds_read_b64_tr_b16), so no transposed copy is staged.
 //
 // Precision.  The float32 path uses float32 MFMA (v_mfma_f32_16x16x4_f32).
 // The bf16-input path uses fp16 operands (v_mfma_f32_16x16x32_f16, same rate
@@ -68,6 +73,8 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kProducers = 2;
@@ -75,17 +82,40 @@ constexpr int kLdsBytes = 160 * 1024;
 
 __host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 __host__ __device__ constexpr int cdiv(int x, int m) { return (x + m - 1) / m; }
+__host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// 16-byte chunk swizzle of a row-major fp16 tile with NCH chunks per row:
+// conflict-free for 16 lanes reading one chunk of 16 interleaved tile rows and
+// for the transpose loads of the state update.
+template <int NCH>
+__device__ __forceinline__ int swz(int t) {
+    if constexpr (NCH >= 16) {
+        return ((t & 3) << 2) | ((t >> 3) & 3);
+    } else if constexpr (NCH == 8) {
+        return ((t >> 1) & 1) | (((t >> 3) & 1) << 1) | ((((t >> 1) ^ (t >> 4)) & 1) << 2);
+    } else if constexpr (NCH == 4) {
+        return (t >> 3) & 3;
+    } else {
+        return 0;
+    }
+}
+
+// LDS transpose load of four 16-bit elements (gfx950).  Within each group of
+// 16 lanes, lane i receives element i%4 of the chunk read by lane 4j + i/4 in
+// slot j.
+__device__ __forceinline__ i16x4 ds_read_tr16(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(p)));
+}
 
 // ---------------------------------------------------------------------------
 // MFMA operand traits.  A "k-group" is the contraction length of one operand
 // fragment: 16 for float32 (four v_mfma_f32_16x16x4_f32, one slot each) and 32
-// for fp16 (one v_mfma_f32_16x16x32_f16, eight slots).  In both, lane group g
-// of a fragment for k-group s carries contraction indices
-//   f32 : slot i      -> 16s + 4g + i
-//   fp16: slot i < 4  -> 32s + 4g + i,   slot 4 + i -> 32s + 16 + 4g + i
-// which is the accumulator's own row order, so accumulator tiles convert to
-// fragments lane-locally.  LDS operands are stored permuted along the
-// contraction index so that a lane's slots are 16 contiguous bytes.
+// for fp16 (one v_mfma_f32_16x16x32_f16, eight slots).  tmap(tile, m) is the
+// index (token or key column) that row m of a 16-row tile stands for; lane
+// group g of the fragment for k-group s carries the indices tmap(tile, 4g+i)
+// of the k-group's tiles in slot order, which is the accumulator's own row
+// order, so accumulator tiles convert to fragments lane-locally.
 // ---------------------------------------------------------------------------
 template <typename T>
 struct Op;
@@ -93,8 +123,9 @@ struct Op;
 template <>
 struct Op<float> {
     static constexpr int KG = 16;
+    static constexpr bool kF16 = false;
     using frag = f32x4;
-    __device__ static int perm(int x) { return x; }
+    __device__ static int tmap(int tile, int m) { return 16 * tile + m; }
     __device__ static f32x4 mma(f32x4 acc, const frag& a, const frag& b) {
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
@@ -104,20 +135,15 @@ struct Op<float> {
     }
     template <int NTILES>
     __device__ static frag from_acc(const f32x4* tiles, int s) { return tiles[s]; }
-    __device__ static frag lds(const float* row, int s, int g) {
-        return *reinterpret_cast<const f32x4*>(row + 16 * s + 4 * g);
-    }
-    // Store contraction indices x..x+3 (x % 4 == 0).
-    __device__ static void put4(float* row, int x, f32x4 v) { *reinterpret_cast<f32x4*>(row + perm(x)) = v; }
 };
 
 template <>
 struct Op<_Float16> {
     static constexpr int KG = 32;
+    static constexpr bool kF16 = true;
     using frag = f16x8;
-    // x = 32s + 16h + 4g + i  ->  32s + 8g + 4h + i
-    __device__ static int perm(int x) {
-        return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
+    __device__ static int tmap(int tile, int m) {
+        return 32 * (tile >> 1) + 8 * (m >> 2) + 4 * (tile & 1) + (m & 3);
     }
     __device__ static f32x4 mma(f32x4 acc, const frag& a, const frag& b) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
@@ -131,14 +157,6 @@ struct Op<_Float16> {
         f[4] = (_Float16)hi[0]; f[5] = (_Float16)hi[1]; f[6] = (_Float16)hi[2]; f[7] = (_Float16)hi[3];
         return f;
     }
-    __device__ static frag lds(const _Float16* row, int s, int g) {
-        return *reinterpret_cast<const f16x8*>(row + 32 * s + 8 * g);
-    }
-    __device__ static void put4(_Float16* row, int x, f32x4 v) {
-        f16x4 h;
-        h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
-        *reinterpret_cast<f16x4*>(row + perm(x)) = h;
-    }
 };
 
 // Global-memory element types: float for the f32 path, raw bf16 bits for the
@@ -147,15 +165,8 @@ template <typename T> struct GlobalOf;
 template <> struct GlobalOf<float> { using type = float; };
 template <> struct GlobalOf<_Float16> { using type = uint16_t; };
 
-// Element e of a 16-byte global load, as float.
-__device__ inline float elem(const uint4& r, int e, float) {
-    const uint32_t w = (&r.x)[e];
-    return __uint_as_float(w);
-}
-__device__ inline float elem(const uint4& r, int e, uint16_t) {
-    const uint32_t w = (&r.x)[e >> 1];
-    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-}
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // DPP move with an identity for lanes that have no source (gfx9 controls).
 template <int CTRL, int ROW_MASK>
@@ -204,64 +215,64 @@ template <typename T, int D, int NS, int NP>
 struct Geo {
     using O = Op<T>;
     using G = typename GlobalOf<T>::type;
-    static constexpr int RB = 16 * NS;               // rows of M per workgroup
-    static constexpr int NRB = D / RB;               // workgroups per sequence
-    static constexpr int NC = D / 16;                // 16-column tiles of M
-    static constexpr int NT = NP / 16;               // 16-token tiles of a chunk
+    static constexpr bool F16 = O::kF16;
     static constexpr int KG = O::KG;
-    static constexpr int NKC = cdiv(D, KG);          // k-groups over the key dimension
-    static constexpr int NKT = NP / KG;              // k-groups over the chunk's tokens
-    static constexpr int EPAD = 16 / sizeof(T);      // 16-byte row padding
-    static constexpr int LQ = round_up(D, KG) + EPAD;
-    static constexpr int LKT = NP + EPAD;
-    static constexpr int LP = NP + EPAD;
-    static constexpr int LV = NP + 4;
-    static constexpr int CB = 16 / sizeof(G);        // elements per 16-byte global load
-    static constexpr int NQB = (NP / 4) * (D / CB);  // 4-token x CB-column blocks of q and k
-    static constexpr int NVB = (NP / 4) * (RB / CB); // 4-token x CB-row blocks of v
-    static constexpr int QBL = cdiv(NQB, kProducers * kWave);
-    static constexpr int VBL = cdiv(NVB, kWave);
+    static constexpr int DS = F16 ? cmax(D, 32) : D;  // stored key width (fp16: >= one k-group)
+    static constexpr int RB = 16 * NS;                // rows of M per workgroup
+    static constexpr int NRB = D / RB;                // workgroups per sequence
+    static constexpr int NC = DS / 16;                // 16-column tiles of M (incl. padding)
+    static constexpr int NT = NP / 16;                // 16-token tiles of a chunk
+    static constexpr int NKC = DS / KG;               // k-groups over the key dimension
+    static constexpr int NKT = NP / KG;               // k-groups over the chunk's tokens
+    // LDS row strides in elements.  fp16: unpadded, 16-byte-chunk swizzled;
+    // float32: padded by 16 bytes.
+    static constexpr int LQ = F16 ? DS : DS + 4;
+    static constexpr int LP = F16 ? NP : NP + 4;
+    static constexpr int LKT = NP + 4;                // float32 only: k^T rows
+    static constexpr int LV = F16 ? RB : NP + 4;      // fp16: raw bf16 v rows; float32: -v^T rows
+    static constexpr int NCHQ = DS * 2 / 16;          // fp16 16-byte chunks per q/k row
+    static constexpr int NCHP = NP * 2 / 16;          // fp16 16-byte chunks per P row
+    static constexpr int CB = 16 / sizeof(G);         // elements per 16-byte global load
+    static constexpr int NQU = NP * (D / CB);         // 16-byte units of q (and of k) per chunk
+    static constexpr int NVU = NP * (RB / CB);        // 16-byte units of v per chunk
+    static constexpr int QUL = cdiv(NQU, kProducers * kWave);
+    static constexpr int VUL = cdiv(NVU, kWave);
     static constexpr int NWAVE = NS + kProducers;
-    // LDS bytes of one chunk buffer and of the single-buffered gate helpers.
-    static constexpr int BUF_BYTES = (2 * NP * LQ + D * LKT + NP * LP + 2 * NP) * (int)sizeof(T) +
-                                     (RB * LV + 2 * NP + 4) * 4;
+    static constexpr int BUF_BYTES = (2 * NP * LQ + NP * LP + 2 * NP) * (int)sizeof(T) +
+                                     (F16 ? NP * LV * 2 : (DS * LKT + RB * LV) * 4) + (2 * NP + 4) * 4;
     static constexpr int HELP_BYTES = (2 * NP + 2 * NT * 256 + NT * NP * 3 + 2 * NP) * 4;
-    static constexpr int NBUF = (2 * BUF_BYTES + HELP_BYTES <= kLdsBytes) ? 2 : 1;
+    static constexpr int NBUF = (2 * BUF_BYTES + HELP_BYTES + 1024 <= kLdsBytes) ? 2 : 1;
     static_assert(NP % KG == 0, "chunk padding must fill whole k-groups");
     static_assert(D % RB == 0, "row blocks must tile d");
-    static_assert(NBUF * BUF_BYTES + HELP_BYTES <= kLdsBytes, "LDS budget");
+    static_assert(NBUF * BUF_BYTES + HELP_BYTES + 1024 <= kLdsBytes, "LDS budget");
 };
 
 template <typename T, int D, int NS, int NP>
 struct Smem {
     using Gm = Geo<T, D, NS, NP>;
+    static constexpr bool F16 = Gm::F16;
     struct Buf {
-        T q[NP * Gm::LQ];        // q rows, key dim permuted
-        T k[NP * Gm::LQ];        // k rows, key dim permuted
-        T kt[D * Gm::LKT];       // k^T rows, token dim permuted
-        T p[NP * Gm::LP];        // -P rows, token dim permuted
-        T wm[NP];                // w^M, token dim permuted
-        T ws[NP];                // w^S, token dim permuted
-        float vn[Gm::RB * Gm::LV];  // -v^T for the workgroup's rows
-        float av[NP];            // A_i
-        float cv[NP];            // c_i
-        float scal[4];           // A_n, c_n, E_n
+        alignas(16) T q[NP * Gm::LQ];                  // q rows (fp16: swizzled chunks)
+        alignas(16) T k[NP * Gm::LQ];                  // k rows
+        alignas(16) T p[NP * Gm::LP];                  // -P rows, token dim in fragment order
+        alignas(16) T wm[NP];                          // w^M (fragment order = token order)
+        alignas(16) T ws[NP];                          // w^S
+        // fp16: raw bf16 v rows [token][row]; float32: k^T rows and -v^T rows.
+        alignas(16) uint16_t vb[F16 ? NP * Gm::LV : 1];
+        alignas(16) float kt[F16 ? 1 : D * Gm::LKT];
+        alignas(16) float vn[F16 ? 1 : Gm::RB * Gm::LV];
+        alignas(16) float av[NP];                      // A_i
+        alignas(16) float cv[NP];                      // c_i
+        alignas(16) float scal[4];                     // A_n, c_n, E_n
     };
     Buf buf[Gm::NBUF];
-    float ga[NP], ge[NP];        // a, eta of the chunk being prepared
-    float gamd[Gm::NT * 256];    // theta_j gamma_ij on diagonal blocks [blk][i][j]
-    float gampd[Gm::NT * 256];   // theta_j p_ij on diagonal blocks
-    float phi[Gm::NT * NP * 3];  // maps from the end of block q to row i [q][i][X,Y,W]
-    float gend[NP], pend[NP];    // theta_j (gamma, p) at the end of column j's block
-};
-
-// Producer-side registers: the next chunk's inputs in flight from HBM.
-template <typename Gm>
-struct Prefetch {
-    uint4 q[Gm::QBL][4];
-    uint4 k[Gm::QBL][4];
-    uint4 v[Gm::VBL][4];
-    float th, et, al;
+    alignas(16) float ga[NP];              // a of the chunk being prepared
+    alignas(16) float ge[NP];              // eta of the chunk being prepared
+    alignas(16) float gamd[Gm::NT * 256];  // theta_j gamma_ij on diagonal 16-blocks [blk][i][j]
+    alignas(16) float gampd[Gm::NT * 256]; // theta_j p_ij on diagonal 16-blocks
+    alignas(16) float phi[Gm::NT * NP * 3];  // maps from the end of block q to row i [q][i][X,Y,W]
+    alignas(16) float gend[NP];            // theta_j gamma at the end of column j's block
+    alignas(16) float pend[NP];            // theta_j p at the end of column j's block
 };
 
 template <typename T, int D, int NS, int NP>
@@ -272,44 +283,90 @@ struct Kernel {
     using F = typename O::frag;
     using S = Smem<T, D, NS, NP>;
     using Buf = typename S::Buf;
-    static constexpr int NT = Gm::NT, NC = Gm::NC, KG = Gm::KG, NKC = Gm::NKC, NKT = Gm::NKT;
-    static constexpr int LQ = Gm::LQ, LKT = Gm::LKT, LP = Gm::LP, LV = Gm::LV, CB = Gm::CB, RB = Gm::RB;
+    static constexpr bool F16 = Gm::F16;
+    static constexpr int NT = Gm::NT, NC = Gm::NC, KG = Gm::KG, NKC = Gm::NKC, NKT = Gm::NKT, DS = Gm::DS;
+    static constexpr int LQ = Gm::LQ, LP = Gm::LP, LKT = Gm::LKT, LV = Gm::LV, CB = Gm::CB, RB = Gm::RB;
+    static constexpr int NCHQ = Gm::NCHQ, NCHP = Gm::NCHP;
+    static constexpr int TPB = KG / 16;   // 16-token tiles per k-group
 
-    // ---- producers: issue global loads of chunk c into registers ----------
-    __device__ static void issue(Prefetch<Gm>& pf, const Params& p, const G* gq, const G* gk, const G* gv,
+    // ---- LDS operand access -------------------------------------------------
+    // Fragment of k-group s from row t of a q/k tile, lane group g.
+    __device__ static F frag_q(const T* base, int t, int s, int g) {
+        if constexpr (F16) {
+            const int ch = (4 * s + g) ^ swz<NCHQ>(t);
+            return *reinterpret_cast<const f16x8*>(base + t * LQ + 8 * ch);
+        } else {
+            return *reinterpret_cast<const f32x4*>(base + t * LQ + 16 * s + 4 * g);
+        }
+    }
+    __device__ static F frag_p(const T* base, int t, int s, int g) {
+        if constexpr (F16) {
+            const int ch = (4 * s + g) ^ swz<NCHP>(t);
+            return *reinterpret_cast<const f16x8*>(base + t * LP + 8 * ch);
+        } else {
+            return *reinterpret_cast<const f32x4*>(base + t * LP + 16 * s + 4 * g);
+        }
+    }
+    // Store indices x..x+3 (x % 4 == 0) of row t of a P tile.
+    __device__ static void put_p(T* base, int t, int x, f32x4 v) {
+        if constexpr (F16) {
+            const int ch = (x >> 3) ^ swz<NCHP>(t);
+            f16x4 h;
+            h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
+            *reinterpret_cast<f16x4*>(base + t * LP + 8 * ch + (x & 4)) = h;
+        } else {
+            *reinterpret_cast<f32x4*>(base + t * LP + x) = v;
+        }
+    }
+    __device__ static void put_w(T* w, int x, f32x4 v) {
+        if constexpr (F16) {
+            f16x4 h;
+            h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
+            *reinterpret_cast<f16x4*>(w + x) = h;
+        } else {
+            *reinterpret_cast<f32x4*>(w + x) = v;
+        }
+    }
+    __device__ static F frag_w(const T* w, int s, int g) {
+        if constexpr (F16) return *reinterpret_cast<const f16x8*>(w + 32 * s + 8 * g);
+        else return *reinterpret_cast<const f32x4*>(w + 16 * s + 4 * g);
+    }
+
+    // ---- producers ------------------------------------------------------------
+    struct Prefetch {
+        uint4 q[Gm::QUL];
+        uint4 k[Gm::QUL];
+        uint4 v[Gm::VUL];
+        float th, et, al;
+    };
+
+    // Issue the global loads of chunk c into registers.
+    __device__ static void issue(Prefetch& pf, const Params& p, const G* gq, const G* gk, const G* gv,
                                  size_t seq_tok, int row_wg, int c, int ptid, int pw, int lane) {
         const int c0 = c * p.b;
         const int n = min(p.b, p.T - c0);
 #pragma unroll
-        for (int kk = 0; kk < Gm::QBL; ++kk) {
+        for (int kk = 0; kk < Gm::QUL; ++kk) {
             const int u = ptid + kProducers * kWave * kk;
-            const int t4 = u / (D / CB), cb = u % (D / CB);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * t4 + r;
-                if (u < Gm::NQB && t < n) {
-                    const size_t off = (seq_tok + c0 + t) * D + cb * CB;
-                    pf.q[kk][r] = *reinterpret_cast<const uint4*>(gq + off);
-                    pf.k[kk][r] = *reinterpret_cast<const uint4*>(gk + off);
-                } else {
-                    pf.q[kk][r] = uint4{0u, 0u, 0u, 0u};
-                    pf.k[kk][r] = uint4{0u, 0u, 0u, 0u};
-                }
+            const int t = u / (D / CB), cb = u % (D / CB);
+            if (u < Gm::NQU && t < n) {
+                const size_t off = (seq_tok + c0 + t) * D + cb * CB;
+                pf.q[kk] = *reinterpret_cast<const uint4*>(gq + off);
+                pf.k[kk] = *reinterpret_cast<const uint4*>(gk + off);
+            } else {
+                pf.q[kk] = uint4{0u, 0u, 0u, 0u};
+                pf.k[kk] = uint4{0u, 0u, 0u, 0u};
             }
         }
         if (pw == 1) {
 #pragma unroll
-            for (int kk = 0; kk < Gm::VBL; ++kk) {
+            for (int kk = 0; kk < Gm::VUL; ++kk) {
                 const int u = lane + kWave * kk;
-                const int t4 = u / (RB / CB), rb = u % (RB / CB);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * t4 + r;
-                    if (u < Gm::NVB && t < n)
-                        pf.v[kk][r] = *reinterpret_cast<const uint4*>(gv + (seq_tok + c0 + t) * D + row_wg + rb * CB);
-                    else
-                        pf.v[kk][r] = uint4{0u, 0u, 0u, 0u};
-                }
+                const int t = u / (RB / CB), rb = u % (RB / CB);
+                if (u < Gm::NVU && t < n)
+                    pf.v[kk] = *reinterpret_cast<const uint4*>(gv + (seq_tok + c0 + t) * D + row_wg + rb * CB);
+                else
+                    pf.v[kk] = uint4{0u, 0u, 0u, 0u};
             }
         } else {
             const bool ok = lane < n;
@@ -320,53 +377,57 @@ struct Kernel {
         }
     }
 
-    // ---- producers: registers -> LDS chunk buffer --------------------------
-    __device__ static void stage(const Prefetch<Gm>& pf, Buf& B, int ptid, int pw, int lane) {
-        const G tag{};
+    // Registers -> LDS chunk buffer.
+    __device__ static void stage(const Prefetch& pf, Buf& B, int ptid, int pw, int lane) {
 #pragma unroll
-        for (int kk = 0; kk < Gm::QBL; ++kk) {
+        for (int kk = 0; kk < Gm::QUL; ++kk) {
             const int u = ptid + kProducers * kWave * kk;
-            if (u < Gm::NQB) {
-                const int t4 = u / (D / CB), cb = u % (D / CB);
-                float kv[4][CB];
+            if (u < Gm::NQU) {
+                const int t = u / (D / CB), cb = u % (D / CB);
+                if constexpr (F16) {
+                    const int ch = cb ^ swz<NCHQ>(t);
+                    const uint4 rq = pf.q[kk], rk = pf.k[kk];
+                    f16x8 hq, hk;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * t4 + r;
-#pragma unroll
-                    for (int e = 0; e < CB; e += 4) {
-                        O::put4(B.q + t * LQ, cb * CB + e,
-                                f32x4{elem(pf.q[kk][r], e, tag), elem(pf.q[kk][r], e + 1, tag),
-                                      elem(pf.q[kk][r], e + 2, tag), elem(pf.q[kk][r], e + 3, tag)});
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t wq = (&rq.x)[e], wk = (&rk.x)[e];
+                        hq[2 * e] = (_Float16)bf16lo(wq);
+                        hq[2 * e + 1] = (_Float16)bf16hi(wq);
+                        hk[2 * e] = (_Float16)bf16lo(wk);
+                        hk[2 * e + 1] = (_Float16)bf16hi(wk);
                     }
+                    *reinterpret_cast<f16x8*>(B.q + t * LQ + 8 * ch) = hq;
+                    *reinterpret_cast<f16x8*>(B.k + t * LQ + 8 * ch) = hk;
+                } else {
+                    const int c = cb * CB;
+                    *reinterpret_cast<uint4*>(B.q + t * LQ + c) = pf.q[kk];
+                    *reinterpret_cast<uint4*>(B.k + t * LQ + c) = pf.k[kk];
+                    const uint4 rk = pf.k[kk];
 #pragma unroll
-                    for (int e = 0; e < CB; ++e) kv[r][e] = elem(pf.k[kk][r], e, tag);
-#pragma unroll
-                    for (int e = 0; e < CB; e += 4)
-                        O::put4(B.k + t * LQ, cb * CB + e, f32x4{kv[r][e], kv[r][e + 1], kv[r][e + 2], kv[r][e + 3]});
+                    for (int e = 0; e < 4; ++e) B.kt[(c + e) * LKT + t] = __uint_as_float((&rk.x)[e]);
                 }
-#pragma unroll
-                for (int e = 0; e < CB; ++e)
-                    O::put4(B.kt + (cb * CB + e) * LKT, 4 * t4, f32x4{kv[0][e], kv[1][e], kv[2][e], kv[3][e]});
             }
         }
         if (pw == 1) {
 #pragma unroll
-            for (int kk = 0; kk < Gm::VBL; ++kk) {
+            for (int kk = 0; kk < Gm::VUL; ++kk) {
                 const int u = lane + kWave * kk;
-                if (u < Gm::NVB) {
-                    const int t4 = u / (RB / CB), rb = u % (RB / CB);
+                if (u < Gm::NVU) {
+                    const int t = u / (RB / CB), rb = u % (RB / CB);
+                    if constexpr (F16) {
+                        *reinterpret_cast<uint4*>(B.vb + t * LV + rb * CB) = pf.v[kk];
+                    } else {
+                        const uint4 rv = pf.v[kk];
 #pragma unroll
-                    for (int e = 0; e < CB; ++e)
-                        *reinterpret_cast<f32x4*>(B.vn + (rb * CB + e) * LV + 4 * t4) =
-                            -f32x4{elem(pf.v[kk][0], e, tag), elem(pf.v[kk][1], e, tag),
-                                   elem(pf.v[kk][2], e, tag), elem(pf.v[kk][3], e, tag)};
+                        for (int e = 0; e < 4; ++e) B.vn[(rb * CB + e) * LV + t] = -__uint_as_float((&rv.x)[e]);
+                    }
                 }
             }
         }
     }
 
-    // ---- producer wave 0: gate scans and decay-matrix helpers --------------
-    __device__ static void gates(const Prefetch<Gm>& pf, S& sm, Buf& B, int n, int lane) {
+    // Producer wave 0: gate scans and decay-matrix helpers.
+    __device__ static void gates(const Prefetch& pf, S& sm, Buf& B, int n, int lane) {
         const int l = lane;
         const float th = pf.th, et = pf.et, a = 1.f - pf.al;
         if (l < NP) { sm.ga[l] = a; sm.ge[l] = et; }
@@ -423,42 +484,88 @@ struct Kernel {
         }
     }
 
-    // ---- producers: P tiles and the chunk-end weights ----------------------
+    // Producers: P tiles and the chunk-end weights.  Tile (pb, qb) holds rows
+    // i = tmap(pb, .) and columns j = tmap(qb, .); it is nonzero only when the
+    // k-group of pb is not before that of qb.  Producer pw takes the row tiles
+    // pb = pw, pw + 2, ...
     __device__ static void ptiles(S& sm, Buf& B, int n, int pw, int lr, int lg) {
         const int ilast = n - 1;
-        for (int u = pw; u < NT * NT; u += kProducers) {
-            const int pb = u / NT, qb = u % NT;
-            const int i = 16 * pb + lr;
-            const int jb = 16 * qb + 4 * lg;
-            if (pb < qb) {
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                O::put4(B.p + i * LP, jb, zero);
-                if (i == ilast) { O::put4(B.wm, jb, zero); O::put4(B.ws, jb, zero); }
-                continue;
-            }
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int pb = pw; pb < NT; pb += kProducers) {
+            const int i = O::tmap(pb, lr);
+            F qf[NKC];
 #pragma unroll
-            for (int s = 0; s < NKC; ++s)
-                acc = O::mma(acc, O::lds(B.k + (16 * qb + lr) * LQ, s, lg), O::lds(B.q + i * LQ, s, lg));
-            // acc[e] = q_i . k_j for j = jb + e
-            f32x4 L, LPe;
-            if (pb == qb) {
-                L = *reinterpret_cast<const f32x4*>(sm.gamd + (qb * 16 + lr) * 16 + 4 * lg);
-                LPe = *reinterpret_cast<const f32x4*>(sm.gampd + (qb * 16 + lr) * 16 + 4 * lg);
-            } else {
-                const float* ph = sm.phi + (qb * NP + i) * 3;
-                const f32x4 gv = *reinterpret_cast<const f32x4*>(sm.gend + jb);
-                const f32x4 pv = *reinterpret_cast<const f32x4*>(sm.pend + jb);
-                L = ph[0] * gv + ph[1] * pv;
-                LPe = ph[2] * pv;
+            for (int s = 0; s < NKC; ++s) qf[s] = frag_q(B.q, i, s, lg);
+            const int bi = i >> 4;
+            for (int qb = 0; qb < NT; ++qb) {
+                const int jb = O::tmap(qb, 4 * lg);   // j = jb + e, e = 0..3, one 16-block
+                if (qb / TPB > pb / TPB) {
+                    // Columns never read for these rows; only the chunk-end row's weights.
+                    if (i == ilast) {
+                        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                        put_w(B.wm, jb, zero);
+                        put_w(B.ws, jb, zero);
+                    }
+                    continue;
+                }
+                const int kr = O::tmap(qb, lr);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < NKC; ++s) acc = O::mma(acc, frag_q(B.k, kr, s, lg), qf[s]);
+                // acc[e] = q_i . k_{jb+e}
+                const int bj = jb >> 4;
+                f32x4 L, LPe;
+                if (bi == bj) {
+                    L = *reinterpret_cast<const f32x4*>(sm.gamd + (bi * 16 + (i & 15)) * 16 + (jb & 15));
+                    LPe = *reinterpret_cast<const f32x4*>(sm.gampd + (bi * 16 + (i & 15)) * 16 + (jb & 15));
+                } else if (bi > bj) {
+                    const float* ph = sm.phi + (bj * NP + i) * 3;
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(sm.gend + jb);
+                    const f32x4 pv = *reinterpret_cast<const f32x4*>(sm.pend + jb);
+                    L = ph[0] * gv + ph[1] * pv;
+                    LPe = ph[2] * pv;
+                } else {
+                    L = f32x4{0.f, 0.f, 0.f, 0.f};
+                    LPe = L;
+                }
+                put_p(B.p, i, jb, -(acc * L));
+                if (i == ilast) { put_w(B.wm, jb, -L); put_w(B.ws, jb, -LPe); }
             }
-            O::put4(B.p + i * LP, jb, -(acc * L));
-            if (i == ilast) { O::put4(B.wm, jb, -L); O::put4(B.ws, jb, -LPe); }
         }
     }
 
     // ---- state waves ------------------------------------------------------
-    // Phase 1: residuals E, reads z; returns E as MFMA fragments.
+    // -V for accumulator tile tt: lane (lr, lg) gets -v[tmap(tt, 4lg + e)][row lr of the wave].
+    __device__ static f32x4 neg_v(const Buf& B, int tt, int w, int lr, int lg) {
+        if constexpr (F16) {
+            const int t = O::tmap(tt, 4 * lg + (lr >> 2));
+            const i16x4 r = ds_read_tr16(B.vb + t * LV + 16 * w + 4 * (lr & 3));
+            const u32x2 u = __builtin_bit_cast(u32x2, r);
+            return f32x4{-bf16lo(u[0]), -bf16hi(u[0]), -bf16lo(u[1]), -bf16hi(u[1])};
+        } else {
+            return *reinterpret_cast<const f32x4*>(B.vn + (16 * w + lr) * LV + 16 * tt + 4 * lg);
+        }
+    }
+    // A operand of the state update for column tile ct, token k-group s:
+    // lane (m = lr, lg) holds k[tokens of the k-group's slots][column tmap(ct, lr)].
+    __device__ static F kt_frag(const Buf& B, int ct, int s, int lr, int lg) {
+        if constexpr (F16) {
+            const int col = 32 * (ct >> 1) + 8 * (lr & 3) + 4 * (ct & 1);
+            const int ch = col >> 3;
+            const int t0 = 32 * s + 8 * lg + (lr >> 2);
+            const int t1 = t0 + 4;
+            const i16x4 lo = ds_read_tr16(B.k + t0 * LQ + 8 * (ch ^ swz<NCHQ>(t0)) + (col & 4));
+            const i16x4 hi = ds_read_tr16(B.k + t1 * LQ + 8 * (ch ^ swz<NCHQ>(t1)) + (col & 4));
+            F f;
+            const f16x4 l4 = __builtin_bit_cast(f16x4, lo), h4 = __builtin_bit_cast(f16x4, hi);
+            f[0] = l4[0]; f[1] = l4[1]; f[2] = l4[2]; f[3] = l4[3];
+            f[4] = h4[0]; f[5] = h4[1]; f[6] = h4[2]; f[7] = h4[3];
+            return f;
+        } else {
+            return *reinterpret_cast<const f32x4*>(B.kt + (16 * ct + lr) * LKT + 16 * s + 4 * lg);
+        }
+    }
+
+    // Phase 1: residuals E and the reads z; returns E as MFMA fragments.
     __device__ static void phase1(const f32x4* Macc, const f32x4* Sacc, const Buf& B, F* EB, float* z,
                                   size_t zrow0, int n, int w, int lr, int lg) {
         F MB[NKC], SB[NKC];
@@ -470,26 +577,27 @@ struct Kernel {
         f32x4 E[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-            E[tt] = *reinterpret_cast<const f32x4*>(B.vn + (16 * w + lr) * LV + 16 * tt + 4 * lg);
+            E[tt] = neg_v(B, tt, w, lr, lg);
+            const int t = O::tmap(tt, lr);
 #pragma unroll
-            for (int s = 0; s < NKC; ++s) E[tt] = O::mma(E[tt], O::lds(B.k + (16 * tt + lr) * LQ, s, lg), MB[s]);
+            for (int s = 0; s < NKC; ++s) E[tt] = O::mma(E[tt], frag_q(B.k, t, s, lg), MB[s]);
         }
 #pragma unroll
         for (int s = 0; s < NKT; ++s) EB[s] = O::template from_acc<NT>(E, s);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
+            const int t = O::tmap(tt, lr);
             f32x4 za = {0.f, 0.f, 0.f, 0.f}, zc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < NKC; ++s) {
-                const F bq = O::lds(B.q + (16 * tt + lr) * LQ, s, lg);
+                const F bq = frag_q(B.q, t, s, lg);
                 za = O::mma(za, MB[s], bq);
                 zc = O::mma(zc, SB[s], bq);
             }
-            const int t = 16 * tt + lr;
             f32x4 zt = B.av[t] * za + B.cv[t] * zc;
 #pragma unroll
             for (int s = 0; s < NKT; ++s)
-                if (KG * s <= 16 * tt + 15) zt = O::mma(zt, EB[s], O::lds(B.p + t * LP, s, lg));
+                if (s <= tt / TPB) zt = O::mma(zt, EB[s], frag_p(B.p, t, s, lg));
             if (t < n) *reinterpret_cast<f32x4*>(z + zrow0 + static_cast<size_t>(t) * D) = zt;
         }
     }
@@ -499,8 +607,8 @@ struct Kernel {
         F WMB[NKT], WSB[NKT];
 #pragma unroll
         for (int s = 0; s < NKT; ++s) {
-            WMB[s] = EB[s] * O::lds(B.wm, s, lg);
-            WSB[s] = EB[s] * O::lds(B.ws, s, lg);
+            WMB[s] = EB[s] * frag_w(B.wm, s, lg);
+            WSB[s] = EB[s] * frag_w(B.ws, s, lg);
         }
         const float An = B.scal[0], Cn = B.scal[1], En = B.scal[2];
 #pragma unroll
@@ -509,7 +617,7 @@ struct Kernel {
             Sacc[ct] = En * Sacc[ct];
 #pragma unroll
             for (int s = 0; s < NKT; ++s) {
-                const F a = O::lds(B.kt + (16 * ct + lr) * LKT, s, lg);
+                const F a = kt_frag(B, ct, s, lr, lg);
                 Macc[ct] = O::mma(Macc[ct], a, WMB[s]);
                 Sacc[ct] = O::mma(Sacc[ct], a, WSB[s]);
             }
@@ -521,8 +629,9 @@ template <typename T, int D, int NS, int NP>
 __global__ __launch_bounds__(kWave * (NS + kProducers)) void linear_memory_fwd(const Params p) {
     using Gm = Geo<T, D, NS, NP>;
     using K = Kernel<T, D, NS, NP>;
+    using O = Op<T>;
     using G = typename Gm::G;
-    using F = typename Op<T>::frag;
+    using F = typename O::frag;
     constexpr int NBUF = Gm::NBUF;
     constexpr int NC = Gm::NC;
     constexpr int RB = Gm::RB;
@@ -534,9 +643,6 @@ __global__ __launch_bounds__(kWave * (NS + kProducers)) void linear_memory_fwd(c
     const int lane = tid % kWave;
     const int lr = lane & 15;   // MFMA row/column index within a 16-tile
     const int lg = lane >> 4;   // MFMA k-slot group
-    const bool is_state = w < NS;
-    const int pw = w - NS;      // producer index (0, 1) for producer waves
-    const int ptid = tid - NS * kWave;
 
     // Workgroup -> (sequence, row block).  When the count allows, the row
     // blocks of one sequence get workgroup ids that are congruent mod 8, so
@@ -549,89 +655,99 @@ __global__ __launch_bounds__(kWave * (NS + kProducers)) void linear_memory_fwd(c
     const int seqlen = p.T;
     const int b = p.b;
     const int row_wg = rb * RB;
-    const int row_w = row_wg + 16 * w;
     const int nch = (seqlen + b - 1) / b;
     const size_t seq_tok = static_cast<size_t>(bh) * seqlen;
-    const G* __restrict__ gq = static_cast<const G*>(p.q);
-    const G* __restrict__ gk = static_cast<const G*>(p.k);
-    const G* __restrict__ gv = static_cast<const G*>(p.v);
+    auto chunk_n = [&](int c) { return min(b, seqlen - c * b); };
 
-    // Zero the staging tiles once: padding columns (d < 32 on the fp16 path) stay 0.
+    // Zero all staging memory once: padded rows and columns stay 0.
     {
         uint32_t* words = reinterpret_cast<uint32_t*>(&sm);
         for (int i = tid; i < static_cast<int>(sizeof(sm) / 4); i += kWave * Gm::NWAVE) words[i] = 0u;
     }
-
-    // State slice: lane (lr, lg) of tile ct holds M[row_w + lr][16ct + 4lg + i].
-    f32x4 Macc[NC], Sacc[NC];
-    const size_t state_off = static_cast<size_t>(bh) * D * D + static_cast<size_t>(row_w + lr) * D;
-    if (is_state) {
-#pragma unroll
-        for (int ct = 0; ct < NC; ++ct) {
-            const int col = 16 * ct + 4 * lg;
-            Macc[ct] = p.M0 ? *reinterpret_cast<const f32x4*>(p.M0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-            Sacc[ct] = p.S0 ? *reinterpret_cast<const f32x4*>(p.S0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
     __syncthreads();
 
-    Prefetch<Gm> pf;
-    F EB[Gm::NKT];
-    auto chunk_n = [&](int c) { return min(b, seqlen - c * b); };
-
-    if constexpr (NBUF == 2) {
-        if (nch > 0 && !is_state) {
-            K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, 0, ptid, pw, lane);
-            K::stage(pf, sm.buf[0], ptid, pw, lane);
-            if (pw == 0) K::gates(pf, sm, sm.buf[0], chunk_n(0), lane);
-            if (nch > 1) K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, 1, ptid, pw, lane);
+    if (w < NS) {
+        // ===================== state wave =====================
+        const int row_w = row_wg + 16 * w;
+        // Tile ct, lane (lr, lg): M[row_w + lr][tmap(ct, 4lg + e)], e = 0..3.
+        f32x4 Macc[NC], Sacc[NC];
+        const size_t state_off = static_cast<size_t>(bh) * D * D + static_cast<size_t>(row_w + lr) * D;
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+            const int col = O::tmap(ct, 4 * lg);
+            const bool ok = col < D;
+            Macc[ct] = (p.M0 && ok) ? *reinterpret_cast<const f32x4*>(p.M0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+            Sacc[ct] = (p.S0 && ok) ? *reinterpret_cast<const f32x4*>(p.S0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        __syncthreads();
-        if (nch > 0 && !is_state) K::ptiles(sm, sm.buf[0], chunk_n(0), pw, lr, lg);
-        __syncthreads();
-        for (int c = 0; c < nch; ++c) {
-            const int bf = c & 1;
-            if (is_state) {
-                K::phase1(Macc, Sacc, sm.buf[bf], EB, p.z, (seq_tok + static_cast<size_t>(c) * b) * D + row_w + 4 * lg,
-                          chunk_n(c), w, lr, lg);
-            } else if (c + 1 < nch) {
-                K::stage(pf, sm.buf[bf ^ 1], ptid, pw, lane);
-                if (pw == 0) K::gates(pf, sm, sm.buf[bf ^ 1], chunk_n(c + 1), lane);
-                if (c + 2 < nch) K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, c + 2, ptid, pw, lane);
-            }
-            __syncthreads();
-            if (is_state) {
+        F EB[Gm::NKT];
+        if constexpr (NBUF == 2) {
+            __syncthreads();   // chunk 0 staged
+            __syncthreads();   // chunk 0 P tiles
+            for (int c = 0; c < nch; ++c) {
+                const int bf = c & 1;
+                const size_t zrow0 = (seq_tok + static_cast<size_t>(c) * b) * D + row_w + 4 * lg;
+                K::phase1(Macc, Sacc, sm.buf[bf], EB, p.z, zrow0, chunk_n(c), w, lr, lg);
+                __syncthreads();
                 K::phase2(Macc, Sacc, sm.buf[bf], EB, lr, lg);
-            } else if (c + 1 < nch) {
-                K::ptiles(sm, sm.buf[bf ^ 1], chunk_n(c + 1), pw, lr, lg);
+                __syncthreads();
             }
-            __syncthreads();
+        } else {
+            for (int c = 0; c < nch; ++c) {
+                __syncthreads();   // chunk c staged
+                __syncthreads();   // chunk c P tiles
+                const size_t zrow0 = (seq_tok + static_cast<size_t>(c) * b) * D + row_w + 4 * lg;
+                K::phase1(Macc, Sacc, sm.buf[0], EB, p.z, zrow0, chunk_n(c), w, lr, lg);
+                K::phase2(Macc, Sacc, sm.buf[0], EB, lr, lg);
+                __syncthreads();   // chunk c consumed
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+            const int col = O::tmap(ct, 4 * lg);
+            if (col < D) {
+                if (p.MT) *reinterpret_cast<f32x4*>(p.MT + state_off + col) = Macc[ct];
+                if (p.ST) *reinterpret_cast<f32x4*>(p.ST + state_off + col) = Sacc[ct];
+            }
         }
     } else {
-        for (int c = 0; c < nch; ++c) {
-            if (!is_state) {
+        // ===================== producer wave =====================
+        const int pw = w - NS;
+        const int ptid = tid - NS * kWave;
+        const G* __restrict__ gq = static_cast<const G*>(p.q);
+        const G* __restrict__ gk = static_cast<const G*>(p.k);
+        const G* __restrict__ gv = static_cast<const G*>(p.v);
+        typename K::Prefetch pf;
+        if constexpr (NBUF == 2) {
+            if (nch > 0) {
+                K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, 0, ptid, pw, lane);
+                K::stage(pf, sm.buf[0], ptid, pw, lane);
+                if (pw == 0) K::gates(pf, sm, sm.buf[0], chunk_n(0), lane);
+                if (nch > 1) K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, 1, ptid, pw, lane);
+            }
+            __syncthreads();
+            if (nch > 0) K::ptiles(sm, sm.buf[0], chunk_n(0), pw, lr, lg);
+            __syncthreads();
+            for (int c = 0; c < nch; ++c) {
+                const int nb = (c & 1) ^ 1;
+                if (c + 1 < nch) {
+                    K::stage(pf, sm.buf[nb], ptid, pw, lane);
+                    if (pw == 0) K::gates(pf, sm, sm.buf[nb], chunk_n(c + 1), lane);
+                    if (c + 2 < nch) K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, c + 2, ptid, pw, lane);
+                }
+                __syncthreads();
+                if (c + 1 < nch) K::ptiles(sm, sm.buf[nb], chunk_n(c + 1), pw, lr, lg);
+                __syncthreads();
+            }
+        } else {
+            for (int c = 0; c < nch; ++c) {
                 K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, c, ptid, pw, lane);
                 K::stage(pf, sm.buf[0], ptid, pw, lane);
                 if (pw == 0) K::gates(pf, sm, sm.buf[0], chunk_n(c), lane);
+                __syncthreads();
+                K::ptiles(sm, sm.buf[0], chunk_n(c), pw, lr, lg);
+                __syncthreads();
+                __syncthreads();
             }
-            __syncthreads();
-            if (!is_state) K::ptiles(sm, sm.buf[0], chunk_n(c), pw, lr, lg);
-            __syncthreads();
-            if (is_state) {
-                K::phase1(Macc, Sacc, sm.buf[0], EB, p.z, (seq_tok + static_cast<size_t>(c) * b) * D + row_w + 4 * lg,
-                          chunk_n(c), w, lr, lg);
-                K::phase2(Macc, Sacc, sm.buf[0], EB, lr, lg);
-            }
-            __syncthreads();
-        }
-    }
-
-    if (is_state) {
-#pragma unroll
-        for (int ct = 0; ct < NC; ++ct) {
-            const int col = 16 * ct + 4 * lg;
-            if (p.MT) *reinterpret_cast<f32x4*>(p.MT + state_off + col) = Macc[ct];
-            if (p.ST) *reinterpret_cast<f32x4*>(p.ST + state_off + col) = Sacc[ct];
         }
     }
 }
