@@ -14,11 +14,19 @@
 //        Z^T = A.(M0 Q^T) + c.(S0 Q^T) + E^T P^T   (reads of every token)
 //        M   <- A_n M0 + c_n S0 + (K^T (w^M . E))^T
 //        S   <- E_n S0 + (K^T (w^S . E))^T
-//   * two producer waves, one chunk ahead of the state waves.  They prefetch
-//     the next chunks' q, k, v and gates from HBM into registers, stage them
-//     in double-buffered LDS as MFMA operands, scan the gates, and build the
-//     intra-chunk weight matrix P = -(tril(Q K^T) .* theta_j gamma_ij)
-//     together with the chunk-end weights w^M, w^S.
+//   * producer waves (two, or four with the column split below), one chunk
+//     ahead of the state waves.  They prefetch the next chunks' q, k, v and
+//     gates from HBM into registers, stage them in double-buffered LDS as
+//     MFMA operands, scan the gates (one wave) and run the decay matrix's
+//     diagonal blocks (another), then build the intra-chunk weight matrix
+//     P = -(tril(Q K^T) .* theta_j gamma_ij) and the chunk-end weights w^M, w^S.
+//
+// Column split (fp16 path, d >= 64): each 16-row tile is held by two state
+// waves, one per half of the key columns of M and S.  Per chunk each of them
+// reads out half of the chunk's tokens over all columns, using the partner's
+// fp16 fragments of M0 and S0 from LDS, and updates only its own columns,
+// using the partner's residual tiles from LDS.  With two waves per SIMD the
+// long latency chains of the state and producer work hide each other.
 //
 // Per token this is S_t = eta_t S_{t-1} - theta_t grad, M_t = (1 - alpha_t)
 // M_{t-1} + S_t, z_t = M_t q_t ("论文速览 | Titans", sections 3.4 and 3.7), with
@@ -75,9 +83,17 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to two fp16, round to nearest even (one v_cvt_pk_f16_f32).
+__device__ __forceinline__ f16x2 cvt2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, f16x2); }
+__device__ __forceinline__ f16x4 cvt4(f32x4 v) {
+    const f16x2 lo = cvt2(v[0], v[1]), hi = cvt2(v[2], v[3]);
+    return f16x4{lo[0], lo[1], hi[0], hi[1]};
+}
 
 constexpr int kWave = 64;
-constexpr int kProducers = 2;
 constexpr int kLdsBytes = 160 * 1024;
 
 __host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -152,10 +168,8 @@ struct Op<_Float16> {
     __device__ static frag from_acc(const f32x4* tiles, int s) {
         const f32x4 lo = tiles[2 * s];
         const f32x4 hi = (2 * s + 1 < NTILES) ? tiles[2 * s + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
-        frag f;
-        f[0] = (_Float16)lo[0]; f[1] = (_Float16)lo[1]; f[2] = (_Float16)lo[2]; f[3] = (_Float16)lo[3];
-        f[4] = (_Float16)hi[0]; f[5] = (_Float16)hi[1]; f[6] = (_Float16)hi[2]; f[7] = (_Float16)hi[3];
-        return f;
+        const f16x4 a = cvt4(lo), b = cvt4(hi);
+        return frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
 };
 
@@ -188,6 +202,28 @@ __device__ __forceinline__ void tri_step(float& X, float& Y, float& W) {
 }
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+// row_newbcast:N -- every lane of a 16-lane row receives lane N of that row.
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf,
+                                                                 0xf, false));
+}
+
+// Raw buffer descriptor over nbytes at ptr: accesses at or past nbytes read 0
+// and are not written, which bounds ragged chunks without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* ptr, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ptr), (short)0, static_cast<int>(nbytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
 
 __device__ __forceinline__ float readlane(float x, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
@@ -210,8 +246,9 @@ struct Params {
     int b;
 };
 
-// Compile-time geometry of one kernel instance.
-template <typename T, int D, int NS, int NP>
+// Compile-time geometry of one kernel instance: NS 16-row tiles per
+// workgroup, each split over CS state waves by key columns.
+template <typename T, int D, int NS, int CS, int NP>
 struct Geo {
     using O = Op<T>;
     using G = typename GlobalOf<T>::type;
@@ -224,6 +261,13 @@ struct Geo {
     static constexpr int NT = NP / 16;                // 16-token tiles of a chunk
     static constexpr int NKC = DS / KG;               // k-groups over the key dimension
     static constexpr int NKT = NP / KG;               // k-groups over the chunk's tokens
+    static constexpr int TPB = KG / 16;               // 16-tiles per k-group
+    static constexpr int NCW = NC / CS;               // column tiles of one state wave
+    static constexpr int NKCW = NKC / CS;             // column k-groups of one state wave
+    static constexpr int NTW = NT / CS;               // token tiles read out by one state wave
+    static constexpr int NPW = CS == 2 ? 4 : 2;       // producer waves
+    static constexpr int NSW = NS * CS;               // state waves
+    static constexpr int NWAVE = NSW + NPW;
     // LDS row strides in elements.  fp16: unpadded, 16-byte-chunk swizzled;
     // float32: padded by 16 bytes.
     static constexpr int LQ = F16 ? DS : DS + 4;
@@ -235,59 +279,63 @@ struct Geo {
     static constexpr int CB = 16 / sizeof(G);         // elements per 16-byte global load
     static constexpr int NQU = NP * (D / CB);         // 16-byte units of q (and of k) per chunk
     static constexpr int NVU = NP * (RB / CB);        // 16-byte units of v per chunk
-    static constexpr int QUL = cdiv(NQU, kProducers * kWave);
+    static constexpr int QUL = cdiv(NQU, NPW * kWave);
     static constexpr int VUL = cdiv(NVU, kWave);
-    static constexpr int NWAVE = NS + kProducers;
     static constexpr int BUF_BYTES = (2 * NP * LQ + NP * LP + 2 * NP) * (int)sizeof(T) +
                                      (F16 ? NP * LV * 2 : (DS * LKT + RB * LV) * 4) + (2 * NP + 4) * 4;
-    static constexpr int HELP_BYTES = (2 * NP + 2 * NT * 256 + NT * NP * 3 + 2 * NP) * 4;
+    static constexpr int XCH_BYTES = CS > 1 ? NS * (2 * NKC * kWave * 16 + NT * kWave * 8) : 0;
+    static constexpr int HELP_BYTES = (2 * NT * 256 + NT * NP * 3 + 2 * NP) * 4 + XCH_BYTES;
     static constexpr int NBUF = (2 * BUF_BYTES + HELP_BYTES + 1024 <= kLdsBytes) ? 2 : 1;
     static_assert(NP % KG == 0, "chunk padding must fill whole k-groups");
     static_assert(D % RB == 0, "row blocks must tile d");
+    static_assert(CS == 1 || (F16 && NKC % CS == 0 && NT % CS == 0), "column split needs whole k-groups");
     static_assert(NBUF * BUF_BYTES + HELP_BYTES + 1024 <= kLdsBytes, "LDS budget");
 };
 
-template <typename T, int D, int NS, int NP>
+template <typename T, int D, int NS, int CS, int NP>
 struct Smem {
-    using Gm = Geo<T, D, NS, NP>;
+    using Gm = Geo<T, D, NS, CS, NP>;
     static constexpr bool F16 = Gm::F16;
     struct Buf {
-        alignas(16) T q[NP * Gm::LQ];                  // q rows (fp16: swizzled chunks)
-        alignas(16) T k[NP * Gm::LQ];                  // k rows
-        alignas(16) T p[NP * Gm::LP];                  // -P rows, token dim in fragment order
-        alignas(16) T wm[NP];                          // w^M (fragment order = token order)
-        alignas(16) T ws[NP];                          // w^S
+        alignas(16) T q[NP * Gm::LQ];      // q rows (fp16: swizzled chunks)
+        alignas(16) T k[NP * Gm::LQ];      // k rows
+        alignas(16) T p[NP * Gm::LP];      // -P rows, token dim in fragment order
+        alignas(16) T wm[NP];              // w^M (fragment order = token order)
+        alignas(16) T ws[NP];              // w^S
         // fp16: raw bf16 v rows [token][row]; float32: k^T rows and -v^T rows.
         alignas(16) uint16_t vb[F16 ? NP * Gm::LV : 1];
         alignas(16) float kt[F16 ? 1 : D * Gm::LKT];
         alignas(16) float vn[F16 ? 1 : Gm::RB * Gm::LV];
-        alignas(16) float av[NP];                      // A_i
-        alignas(16) float cv[NP];                      // c_i
-        alignas(16) float scal[4];                     // A_n, c_n, E_n
+        alignas(16) float av[NP];          // A_i
+        alignas(16) float cv[NP];          // c_i
+        alignas(16) float scal[4];         // A_n, c_n, E_n
     };
     Buf buf[Gm::NBUF];
-    alignas(16) float ga[NP];              // a of the chunk being prepared
-    alignas(16) float ge[NP];              // eta of the chunk being prepared
-    alignas(16) float gamd[Gm::NT * 256];  // theta_j gamma_ij on diagonal 16-blocks [blk][i][j]
-    alignas(16) float gampd[Gm::NT * 256]; // theta_j p_ij on diagonal 16-blocks
+    alignas(16) float gamd[Gm::NT * 256];    // theta_j gamma_ij on diagonal 16-blocks [blk][i][j]
+    alignas(16) float gampd[Gm::NT * 256];   // theta_j p_ij on diagonal 16-blocks
     alignas(16) float phi[Gm::NT * NP * 3];  // maps from the end of block q to row i [q][i][X,Y,W]
-    alignas(16) float gend[NP];            // theta_j gamma at the end of column j's block
-    alignas(16) float pend[NP];            // theta_j p at the end of column j's block
+    alignas(16) float gend[NP];              // theta_j gamma at the end of column j's block
+    alignas(16) float pend[NP];              // theta_j p at the end of column j's block
+    // Column-split exchange between the state waves of one row tile: fp16
+    // fragments of M0, S0 per key k-group, and fp16 residual tiles per token tile.
+    alignas(16) f16x8 xm[CS > 1 ? NS * Gm::NKC * kWave : 1];
+    alignas(16) f16x8 xs[CS > 1 ? NS * Gm::NKC * kWave : 1];
+    alignas(16) f16x4 xe[CS > 1 ? NS * Gm::NT * kWave : 1];
 };
 
-template <typename T, int D, int NS, int NP>
+template <typename T, int D, int NS, int CS, int NP>
 struct Kernel {
-    using Gm = Geo<T, D, NS, NP>;
+    using Gm = Geo<T, D, NS, CS, NP>;
     using O = Op<T>;
     using G = typename Gm::G;
     using F = typename O::frag;
-    using S = Smem<T, D, NS, NP>;
+    using S = Smem<T, D, NS, CS, NP>;
     using Buf = typename S::Buf;
     static constexpr bool F16 = Gm::F16;
     static constexpr int NT = Gm::NT, NC = Gm::NC, KG = Gm::KG, NKC = Gm::NKC, NKT = Gm::NKT, DS = Gm::DS;
     static constexpr int LQ = Gm::LQ, LP = Gm::LP, LKT = Gm::LKT, LV = Gm::LV, CB = Gm::CB, RB = Gm::RB;
-    static constexpr int NCHQ = Gm::NCHQ, NCHP = Gm::NCHP;
-    static constexpr int TPB = KG / 16;   // 16-token tiles per k-group
+    static constexpr int NCHQ = Gm::NCHQ, NCHP = Gm::NCHP, TPB = Gm::TPB, NPW = Gm::NPW;
+    static constexpr int NCW = Gm::NCW, NKCW = Gm::NKCW, NTW = Gm::NTW;
 
     // ---- LDS operand access -------------------------------------------------
     // Fragment of k-group s from row t of a q/k tile, lane group g.
@@ -311,20 +359,9 @@ struct Kernel {
     __device__ static void put_p(T* base, int t, int x, f32x4 v) {
         if constexpr (F16) {
             const int ch = (x >> 3) ^ swz<NCHP>(t);
-            f16x4 h;
-            h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
-            *reinterpret_cast<f16x4*>(base + t * LP + 8 * ch + (x & 4)) = h;
+            *reinterpret_cast<f16x4*>(base + t * LP + 8 * ch + (x & 4)) = cvt4(v);
         } else {
             *reinterpret_cast<f32x4*>(base + t * LP + x) = v;
-        }
-    }
-    __device__ static void put_w(T* w, int x, f32x4 v) {
-        if constexpr (F16) {
-            f16x4 h;
-            h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
-            *reinterpret_cast<f16x4*>(w + x) = h;
-        } else {
-            *reinterpret_cast<f32x4*>(w + x) = v;
         }
     }
     __device__ static F frag_w(const T* w, int s, int g) {
@@ -333,56 +370,76 @@ struct Kernel {
     }
 
     // ---- producers ------------------------------------------------------------
+    // Each producer wave PW owns a fixed share of the chunk's 16-byte q/k
+    // units (the two gate waves take smaller shares), v rows (one wave), gate
+    // work and P tiles, all known at compile time.
+    static constexpr int WU = cdiv(Gm::NQU, kWave);   // q (or k) units per chunk in 64-lane rounds
+    template <int PW>
+    struct Share {
+        // rounds [first, first + count) of the q/k units
+        static constexpr int w0 = NPW == 4 ? WU / 8 : WU / 2;
+        static constexpr int w1 = NPW == 4 ? WU / 8 : WU - w0;
+        static constexpr int w2 = NPW == 4 ? (3 * WU) / 8 : 0;
+        static constexpr int first = PW == 0 ? 0 : PW == 1 ? w0 : PW == 2 ? w0 + w1 : w0 + w1 + w2;
+        static constexpr int count = PW == 0 ? w0 : PW == 1 ? w1 : PW == 2 ? w2 : WU - w0 - w1 - w2;
+        static constexpr bool has_v = PW == (NPW == 4 ? 2 : 1);
+    };
+    static constexpr int QUMAX = cmax(cmax(Share<0>::count, Share<1>::count),
+                                      cmax(Share<2>::count, Share<3>::count));
     struct Prefetch {
-        uint4 q[Gm::QUL];
-        uint4 k[Gm::QUL];
+        uint4 q[QUMAX > 0 ? QUMAX : 1];
+        uint4 k[QUMAX > 0 ? QUMAX : 1];
         uint4 v[Gm::VUL];
         float th, et, al;
     };
 
-    // Issue the global loads of chunk c into registers.
+    // Issue the global loads of chunk c into registers; nothing here waits for
+    // them.  Rows past the chunk's n tokens read as zeros through the bounds.
+    template <int PW>
     __device__ static void issue(Prefetch& pf, const Params& p, const G* gq, const G* gk, const G* gv,
-                                 size_t seq_tok, int row_wg, int c, int ptid, int pw, int lane) {
+                                 size_t seq_tok, int row_wg, int c, int lane) {
+        using Sh = Share<PW>;
         const int c0 = c * p.b;
         const int n = min(p.b, p.T - c0);
+        const size_t chunk_off = (seq_tok + c0) * D;
+        const uint32_t nbytes = static_cast<uint32_t>(n) * D * sizeof(G);
+        const auto rq = make_rsrc(gq + chunk_off, nbytes);
+        const auto rk = make_rsrc(gk + chunk_off, nbytes);
 #pragma unroll
-        for (int kk = 0; kk < Gm::QUL; ++kk) {
-            const int u = ptid + kProducers * kWave * kk;
+        for (int kk = 0; kk < Sh::count; ++kk) {
+            const int u = (Sh::first + kk) * kWave + lane;
             const int t = u / (D / CB), cb = u % (D / CB);
-            if (u < Gm::NQU && t < n) {
-                const size_t off = (seq_tok + c0 + t) * D + cb * CB;
-                pf.q[kk] = *reinterpret_cast<const uint4*>(gq + off);
-                pf.k[kk] = *reinterpret_cast<const uint4*>(gk + off);
-            } else {
-                pf.q[kk] = uint4{0u, 0u, 0u, 0u};
-                pf.k[kk] = uint4{0u, 0u, 0u, 0u};
-            }
+            const uint32_t off = (static_cast<uint32_t>(t) * D + cb * CB) * sizeof(G);
+            pf.q[kk] = buf_load16(rq, off);
+            pf.k[kk] = buf_load16(rk, off);
         }
-        if (pw == 1) {
+        if constexpr (Sh::has_v) {
+            const auto rv = make_rsrc(gv + chunk_off, nbytes);
 #pragma unroll
             for (int kk = 0; kk < Gm::VUL; ++kk) {
                 const int u = lane + kWave * kk;
                 const int t = u / (RB / CB), rb = u % (RB / CB);
-                if (u < Gm::NVU && t < n)
-                    pf.v[kk] = *reinterpret_cast<const uint4*>(gv + (seq_tok + c0 + t) * D + row_wg + rb * CB);
-                else
-                    pf.v[kk] = uint4{0u, 0u, 0u, 0u};
+                pf.v[kk] = buf_load16(rv, (static_cast<uint32_t>(t) * D + row_wg + rb * CB) * sizeof(G));
             }
-        } else {
-            const bool ok = lane < n;
-            const size_t gi = seq_tok + c0 + lane;
-            pf.th = ok ? p.theta[gi] : 0.f;   // padding tokens write nothing
-            pf.et = ok ? p.eta[gi] : 1.f;     // and leave products unchanged
-            pf.al = ok ? p.alpha[gi] : 0.f;
+        }
+        if constexpr (PW < 2) {
+            // Padding tokens read theta = alpha = eta = 0; the gate work maps eta to 1.
+            const uint32_t gbytes = static_cast<uint32_t>(n) * 4;
+            const size_t gi = seq_tok + c0;
+            pf.th = buf_load4(make_rsrc(p.theta + gi, gbytes), lane * 4);
+            pf.al = buf_load4(make_rsrc(p.alpha + gi, gbytes), lane * 4);
+            pf.et = buf_load4(make_rsrc(p.eta + gi, gbytes), lane * 4);
         }
     }
 
     // Registers -> LDS chunk buffer.
-    __device__ static void stage(const Prefetch& pf, Buf& B, int ptid, int pw, int lane) {
+    template <int PW>
+    __device__ static void stage(const Prefetch& pf, Buf& B, int lane) {
+        using Sh = Share<PW>;
 #pragma unroll
-        for (int kk = 0; kk < Gm::QUL; ++kk) {
-            const int u = ptid + kProducers * kWave * kk;
-            if (u < Gm::NQU) {
+        for (int kk = 0; kk < Sh::count; ++kk) {
+            const int u = (Sh::first + kk) * kWave + lane;
+            if ((Gm::NQU % kWave) == 0 || u < Gm::NQU) {
                 const int t = u / (D / CB), cb = u % (D / CB);
                 if constexpr (F16) {
                     const int ch = cb ^ swz<NCHQ>(t);
@@ -391,10 +448,11 @@ struct Kernel {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const uint32_t wq = (&rq.x)[e], wk = (&rk.x)[e];
-                        hq[2 * e] = (_Float16)bf16lo(wq);
-                        hq[2 * e + 1] = (_Float16)bf16hi(wq);
-                        hk[2 * e] = (_Float16)bf16lo(wk);
-                        hk[2 * e + 1] = (_Float16)bf16hi(wk);
+                        const f16x2 a = cvt2(bf16lo(wq), bf16hi(wq)), b = cvt2(bf16lo(wk), bf16hi(wk));
+                        hq[2 * e] = a[0];
+                        hq[2 * e + 1] = a[1];
+                        hk[2 * e] = b[0];
+                        hk[2 * e + 1] = b[1];
                     }
                     *reinterpret_cast<f16x8*>(B.q + t * LQ + 8 * ch) = hq;
                     *reinterpret_cast<f16x8*>(B.k + t * LQ + 8 * ch) = hk;
@@ -408,11 +466,11 @@ struct Kernel {
                 }
             }
         }
-        if (pw == 1) {
+        if constexpr (Share<PW>::has_v) {
 #pragma unroll
             for (int kk = 0; kk < Gm::VUL; ++kk) {
                 const int u = lane + kWave * kk;
-                if (u < Gm::NVU) {
+                if ((Gm::NVU % kWave) == 0 || u < Gm::NVU) {
                     const int t = u / (RB / CB), rb = u % (RB / CB);
                     if constexpr (F16) {
                         *reinterpret_cast<uint4*>(B.vb + t * LV + rb * CB) = pf.v[kk];
@@ -426,11 +484,10 @@ struct Kernel {
         }
     }
 
-    // Producer wave 0: gate scans and decay-matrix helpers.
-    __device__ static void gates(const Prefetch& pf, S& sm, Buf& B, int n, int lane) {
+    // Producer wave 0: gate scan (A, c, E) and the block maps of the decay matrix.
+    __device__ static void gate_scan(const Prefetch& pf, S& sm, Buf& B, int n, int lane) {
         const int l = lane;
-        const float th = pf.th, et = pf.et, a = 1.f - pf.al;
-        if (l < NP) { sm.ga[l] = a; sm.ge[l] = et; }
+        const float et = l < n ? pf.et : 1.f, a = 1.f - pf.al;
         // Inclusive prefix of T_l within 16-lane rows: Psi_l = T_l ... T_{16*(l/16)}.
         float X = a, Y = et, W = et;
         tri_step<kRowShr1>(X, Y, W);
@@ -466,83 +523,113 @@ struct Kernel {
                 }
             }
         }
-        // Diagonal 16x16 blocks: lane = (block, column j), rows run in order.
+    }
+
+    // Producer wave 1: diagonal 16x16 blocks of the decay matrix.  Lane =
+    // (block, column j); row i = 16*block + s takes a_i, eta_i from lane s of
+    // the same 16-lane row.
+    template <int S_>
+    __device__ static void diag_step(float a, float et, float th, int jj, float& pp, float& gg, float* gd,
+                                     float* gpd) {
+        const float ai = row_bcast<S_>(a), ei = row_bcast<S_>(et);
+        if (S_ == jj) { pp = 1.f; gg = 1.f; }
+        else if (S_ > jj) { pp = ei * pp; gg = ai * gg + pp; }
+        gd[S_ * 16] = th * gg;
+        gpd[S_ * 16] = th * pp;
+    }
+    __device__ static void gate_diag(const Prefetch& pf, S& sm, int n, int lane) {
+        const int l = lane;
+        const float th = pf.th, et = l < n ? pf.et : 1.f, a = 1.f - pf.al;
         const int qb = l >> 4, jj = l & 15;
+        float pp = 0.f, gg = 0.f;
+        float* gd = sm.gamd + qb * 256 + jj;
+        float* gpd = sm.gampd + qb * 256 + jj;
         if (qb < NT) {
-            float pp = 0.f, gg = 0.f;
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const int i = 16 * qb + s;
-                const float ai = sm.ga[i], ei = sm.ge[i];
-                if (s == jj) { pp = 1.f; gg = 1.f; }
-                else if (s > jj) { pp = ei * pp; gg = ai * gg + pp; }
-                sm.gamd[(qb * 16 + s) * 16 + jj] = th * gg;
-                sm.gampd[(qb * 16 + s) * 16 + jj] = th * pp;
-            }
+            diag_step<0>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<1>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<2>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<3>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<4>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<5>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<6>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<7>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<8>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<9>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<10>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<11>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<12>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<13>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<14>(a, et, th, jj, pp, gg, gd, gpd);
+            diag_step<15>(a, et, th, jj, pp, gg, gd, gpd);
             sm.gend[l] = th * gg;
             sm.pend[l] = th * pp;
         }
     }
 
-    // Producers: P tiles and the chunk-end weights.  Tile (pb, qb) holds rows
-    // i = tmap(pb, .) and columns j = tmap(qb, .); it is nonzero only when the
-    // k-group of pb is not before that of qb.  Producer pw takes the row tiles
-    // pb = pw, pw + 2, ...
-    __device__ static void ptiles(S& sm, Buf& B, int n, int pw, int lr, int lg) {
-        const int ilast = n - 1;
-        for (int pb = pw; pb < NT; pb += kProducers) {
-            const int i = O::tmap(pb, lr);
-            F qf[NKC];
+    // theta_j gamma_ij and theta_j p_ij for 4 consecutive j = jb..jb+3 (one 16-block).
+    __device__ static void decay4(const S& sm, int i, int jb, f32x4& L, f32x4& LPe) {
+        const int bi = i >> 4, bj = jb >> 4;
+        const f32x4 ld = *reinterpret_cast<const f32x4*>(sm.gamd + (bi * 16 + (i & 15)) * 16 + (jb & 15));
+        const f32x4 lpd = *reinterpret_cast<const f32x4*>(sm.gampd + (bi * 16 + (i & 15)) * 16 + (jb & 15));
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(sm.gend + jb);
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(sm.pend + jb);
+        const float* ph = sm.phi + (bj * NP + i) * 3;   // in bounds for every bj < NT
+        const float x = ph[0], y = ph[1], wv = ph[2];
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 lo = x * gv + y * pv, lpo = wv * pv;
+        L = bi == bj ? ld : (bi > bj ? lo : zero);
+        LPe = bi == bj ? lpd : (bi > bj ? lpo : zero);
+    }
+
+    // Producers: P tiles.  Tile (pb, qb) holds rows i = tmap(pb, .) and
+    // columns j = tmap(qb, .); only tiles whose column k-group is not after the
+    // row's k-group are ever read.  They are dealt round-robin to the producers.
+    template <int PW>
+    __device__ static void ptiles(const S& sm, Buf& B, int lr, int lg) {
+        int v = 0;
 #pragma unroll
-            for (int s = 0; s < NKC; ++s) qf[s] = frag_q(B.q, i, s, lg);
-            const int bi = i >> 4;
+        for (int pb = 0; pb < NT; ++pb) {
+#pragma unroll
             for (int qb = 0; qb < NT; ++qb) {
-                const int jb = O::tmap(qb, 4 * lg);   // j = jb + e, e = 0..3, one 16-block
-                if (qb / TPB > pb / TPB) {
-                    // Columns never read for these rows; only the chunk-end row's weights.
-                    if (i == ilast) {
-                        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                        put_w(B.wm, jb, zero);
-                        put_w(B.ws, jb, zero);
-                    }
-                    continue;
-                }
+                if (qb / TPB > pb / TPB) continue;
+                if ((v++ % NPW) != PW) continue;
+                const int i = O::tmap(pb, lr);
                 const int kr = O::tmap(qb, lr);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < NKC; ++s) acc = O::mma(acc, frag_q(B.k, kr, s, lg), qf[s]);
-                // acc[e] = q_i . k_{jb+e}
-                const int bj = jb >> 4;
+                for (int s = 0; s < NKC; ++s) acc = O::mma(acc, frag_q(B.k, kr, s, lg), frag_q(B.q, i, s, lg));
+                const int jb = O::tmap(qb, 4 * lg);   // acc[e] = q_i . k_{jb+e}
                 f32x4 L, LPe;
-                if (bi == bj) {
-                    L = *reinterpret_cast<const f32x4*>(sm.gamd + (bi * 16 + (i & 15)) * 16 + (jb & 15));
-                    LPe = *reinterpret_cast<const f32x4*>(sm.gampd + (bi * 16 + (i & 15)) * 16 + (jb & 15));
-                } else if (bi > bj) {
-                    const float* ph = sm.phi + (bj * NP + i) * 3;
-                    const f32x4 gv = *reinterpret_cast<const f32x4*>(sm.gend + jb);
-                    const f32x4 pv = *reinterpret_cast<const f32x4*>(sm.pend + jb);
-                    L = ph[0] * gv + ph[1] * pv;
-                    LPe = ph[2] * pv;
-                } else {
-                    L = f32x4{0.f, 0.f, 0.f, 0.f};
-                    LPe = L;
-                }
+                decay4(sm, i, jb, L, LPe);
                 put_p(B.p, i, jb, -(acc * L));
-                if (i == ilast) { put_w(B.wm, jb, -L); put_w(B.ws, jb, -LPe); }
+            }
+        }
+    }
+    // Chunk-end weights w^M_j = -theta_j gamma_{n-1,j}, w^S_j = -theta_j p_{n-1,j}; lane = 4 tokens.
+    __device__ static void wrow(const S& sm, Buf& B, int n, int lane) {
+        if (lane < NP / 4) {
+            f32x4 L, LPe;
+            decay4(sm, n - 1, 4 * lane, L, LPe);
+            if constexpr (F16) {
+                *reinterpret_cast<f16x4*>(B.wm + 4 * lane) = cvt4(-L);
+                *reinterpret_cast<f16x4*>(B.ws + 4 * lane) = cvt4(-LPe);
+            } else {
+                *reinterpret_cast<f32x4*>(B.wm + 4 * lane) = -L;
+                *reinterpret_cast<f32x4*>(B.ws + 4 * lane) = -LPe;
             }
         }
     }
 
     // ---- state waves ------------------------------------------------------
-    // -V for accumulator tile tt: lane (lr, lg) gets -v[tmap(tt, 4lg + e)][row lr of the wave].
-    __device__ static f32x4 neg_v(const Buf& B, int tt, int w, int lr, int lg) {
+    // -V for token tile tt: lane (lr, lg) gets -v[tmap(tt, 4lg + e)][row r0 + lr].
+    __device__ static f32x4 neg_v(const Buf& B, int tt, int r0, int lr, int lg) {
         if constexpr (F16) {
             const int t = O::tmap(tt, 4 * lg + (lr >> 2));
-            const i16x4 r = ds_read_tr16(B.vb + t * LV + 16 * w + 4 * (lr & 3));
+            const i16x4 r = ds_read_tr16(B.vb + t * LV + r0 + 4 * (lr & 3));
             const u32x2 u = __builtin_bit_cast(u32x2, r);
             return f32x4{-bf16lo(u[0]), -bf16hi(u[0]), -bf16lo(u[1]), -bf16hi(u[1])};
         } else {
-            return *reinterpret_cast<const f32x4*>(B.vn + (16 * w + lr) * LV + 16 * tt + 4 * lg);
+            return *reinterpret_cast<const f32x4*>(B.vn + (r0 + lr) * LV + 16 * tt + 4 * lg);
         }
     }
     // A operand of the state update for column tile ct, token k-group s:
@@ -555,86 +642,200 @@ struct Kernel {
             const int t1 = t0 + 4;
             const i16x4 lo = ds_read_tr16(B.k + t0 * LQ + 8 * (ch ^ swz<NCHQ>(t0)) + (col & 4));
             const i16x4 hi = ds_read_tr16(B.k + t1 * LQ + 8 * (ch ^ swz<NCHQ>(t1)) + (col & 4));
-            F f;
             const f16x4 l4 = __builtin_bit_cast(f16x4, lo), h4 = __builtin_bit_cast(f16x4, hi);
-            f[0] = l4[0]; f[1] = l4[1]; f[2] = l4[2]; f[3] = l4[3];
-            f[4] = h4[0]; f[5] = h4[1]; f[6] = h4[2]; f[7] = h4[3];
-            return f;
+            return F{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
         } else {
             return *reinterpret_cast<const f32x4*>(B.kt + (16 * ct + lr) * LKT + 16 * s + 4 * lg);
         }
     }
 
-    // Phase 1: residuals E and the reads z; returns E as MFMA fragments.
-    __device__ static void phase1(const f32x4* Macc, const f32x4* Sacc, const Buf& B, F* EB, float* z,
-                                  size_t zrow0, int n, int w, int lr, int lg) {
-        F MB[NKC], SB[NKC];
+    // State wave (rho, chi): rows r0..r0+15 of the workgroup block, column
+    // tiles chi*NCW.., token tiles chi*NTW.. .  MB/SB hold fp16 fragments of
+    // M0, S0 for every key k-group (own ones from registers, the partner's
+    // from the exchange).
+    struct StateCtx {
+        int rho, chi, r0, lr, lg;
+    };
+
+    // Phase A: residuals E and readouts (A.M0 q + c.S0 q) of the own token
+    // tiles.  MB/SB hold the fp16 fragments of M0, S0 for the own key
+    // k-groups; MP/SP receive the partner's from the exchange.
+    __device__ static void phaseA(const StateCtx& x, const Buf& B, S& sm, const F* MB, const F* SB, f32x4* E,
+                                  f32x4* Zp) {
+        F MP[NKCW], SP[NKCW];
+        const int pchi = x.chi ^ 1;
+        if constexpr (CS > 1) {
 #pragma unroll
-        for (int s = 0; s < NKC; ++s) {
-            MB[s] = O::template from_acc<NC>(Macc, s);
-            SB[s] = O::template from_acc<NC>(Sacc, s);
+            for (int sw = 0; sw < NKCW; ++sw) {
+                const int s = pchi * NKCW + sw;
+                MP[sw] = sm.xm[(x.rho * NKC + s) * kWave + x.lr + 16 * x.lg];
+                SP[sw] = sm.xs[(x.rho * NKC + s) * kWave + x.lr + 16 * x.lg];
+            }
         }
-        f32x4 E[NT];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            E[tt] = neg_v(B, tt, w, lr, lg);
-            const int t = O::tmap(tt, lr);
-#pragma unroll
-            for (int s = 0; s < NKC; ++s) E[tt] = O::mma(E[tt], frag_q(B.k, t, s, lg), MB[s]);
-        }
-#pragma unroll
-        for (int s = 0; s < NKT; ++s) EB[s] = O::template from_acc<NT>(E, s);
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            const int t = O::tmap(tt, lr);
+        for (int tw = 0; tw < NTW; ++tw) {
+            const int tt = x.chi * NTW + tw;
+            const int t = O::tmap(tt, x.lr);
+            E[tw] = neg_v(B, tt, x.r0, x.lr, x.lg);
             f32x4 za = {0.f, 0.f, 0.f, 0.f}, zc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < NKC; ++s) {
-                const F bq = frag_q(B.q, t, s, lg);
-                za = O::mma(za, MB[s], bq);
-                zc = O::mma(zc, SB[s], bq);
+            for (int sw = 0; sw < NKCW; ++sw) {
+                const int s = x.chi * NKCW + sw;   // own key k-group
+                E[tw] = O::mma(E[tw], frag_q(B.k, t, s, x.lg), MB[sw]);
+                const F bq = frag_q(B.q, t, s, x.lg);
+                za = O::mma(za, MB[sw], bq);
+                zc = O::mma(zc, SB[sw], bq);
             }
-            f32x4 zt = B.av[t] * za + B.cv[t] * zc;
+            if constexpr (CS > 1) {
 #pragma unroll
-            for (int s = 0; s < NKT; ++s)
-                if (s <= tt / TPB) zt = O::mma(zt, EB[s], frag_p(B.p, t, s, lg));
-            if (t < n) *reinterpret_cast<f32x4*>(z + zrow0 + static_cast<size_t>(t) * D) = zt;
+                for (int sw = 0; sw < NKCW; ++sw) {
+                    const int s = pchi * NKCW + sw;   // partner's key k-group
+                    E[tw] = O::mma(E[tw], frag_q(B.k, t, s, x.lg), MP[sw]);
+                    const F bq = frag_q(B.q, t, s, x.lg);
+                    za = O::mma(za, MP[sw], bq);
+                    zc = O::mma(zc, SP[sw], bq);
+                }
+            }
+            Zp[tw] = B.av[t] * za + B.cv[t] * zc;
+        }
+        if constexpr (CS > 1) {
+#pragma unroll
+            for (int tw = 0; tw < NTW; ++tw) {
+                const int tt = x.chi * NTW + tw;
+                sm.xe[(x.rho * NT + tt) * kWave + x.lr + 16 * x.lg] = cvt4(E[tw]);
+            }
         }
     }
 
-    // Phase 2: state update from the residual fragments.
-    __device__ static void phase2(f32x4* Macc, f32x4* Sacc, const Buf& B, const F* EB, int lr, int lg) {
+    // Phase B: intra-chunk term and store of z for the own token tiles, then
+    // the update of the own columns of M and S.
+    __device__ static void phaseB(const StateCtx& x, const Buf& B, S& sm, f32x4* Macc, f32x4* Sacc, F* MB, F* SB,
+                                  const f32x4* E, f32x4* Zp, __amdgpu_buffer_rsrc_t rz, uint32_t zcol) {
+        // (MB, SB: the own key k-groups, refreshed from the updated state at the end.)
+        F EB[NKT];
+        if constexpr (CS > 1) {
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) {
+                const f16x4 lo = sm.xe[(x.rho * NT + 2 * s) * kWave + x.lr + 16 * x.lg];
+                const f16x4 hi = sm.xe[(x.rho * NT + 2 * s + 1) * kWave + x.lr + 16 * x.lg];
+                EB[s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) EB[s] = O::template from_acc<NT>(E, s);
+        }
+#pragma unroll
+        for (int tw = 0; tw < NTW; ++tw) {
+            const int tt = x.chi * NTW + tw;
+            const int t = O::tmap(tt, x.lr);
+#pragma unroll
+            for (int s = 0; s < NKT; ++s)
+                if (s <= tt / TPB) Zp[tw] = O::mma(Zp[tw], EB[s], frag_p(B.p, t, s, x.lg));
+            buf_store16(Zp[tw], rz, (static_cast<uint32_t>(t) * D + zcol) * 4);   // rows >= n dropped
+        }
         F WMB[NKT], WSB[NKT];
 #pragma unroll
         for (int s = 0; s < NKT; ++s) {
-            WMB[s] = EB[s] * frag_w(B.wm, s, lg);
-            WSB[s] = EB[s] * frag_w(B.ws, s, lg);
+            WMB[s] = EB[s] * frag_w(B.wm, s, x.lg);
+            WSB[s] = EB[s] * frag_w(B.ws, s, x.lg);
         }
         const float An = B.scal[0], Cn = B.scal[1], En = B.scal[2];
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct) {
-            Macc[ct] = An * Macc[ct] + Cn * Sacc[ct];
-            Sacc[ct] = En * Sacc[ct];
+        for (int cw = 0; cw < NCW; ++cw) {
+            const int ct = x.chi * NCW + cw;
+            Macc[cw] = An * Macc[cw] + Cn * Sacc[cw];
+            Sacc[cw] = En * Sacc[cw];
 #pragma unroll
             for (int s = 0; s < NKT; ++s) {
-                const F a = kt_frag(B, ct, s, lr, lg);
-                Macc[ct] = O::mma(Macc[ct], a, WMB[s]);
-                Sacc[ct] = O::mma(Sacc[ct], a, WSB[s]);
+                const F a = kt_frag(B, ct, s, x.lr, x.lg);
+                Macc[cw] = O::mma(Macc[cw], a, WMB[s]);
+                Sacc[cw] = O::mma(Sacc[cw], a, WSB[s]);
+            }
+        }
+        own_frags(x, sm, Macc, Sacc, MB, SB);
+    }
+
+    // fp16 fragments of the own columns of M, S (and their copy for the partner).
+    __device__ static void own_frags(const StateCtx& x, S& sm, const f32x4* Macc, const f32x4* Sacc, F* MB, F* SB) {
+#pragma unroll
+        for (int sw = 0; sw < NKCW; ++sw) {
+            MB[sw] = O::template from_acc<NCW>(Macc, sw);
+            SB[sw] = O::template from_acc<NCW>(Sacc, sw);
+            if constexpr (CS > 1) {
+                const int s = x.chi * NKCW + sw;
+                sm.xm[(x.rho * NKC + s) * kWave + x.lr + 16 * x.lg] = MB[sw];
+                sm.xs[(x.rho * NKC + s) * kWave + x.lr + 16 * x.lg] = SB[sw];
             }
         }
     }
 };
 
-template <typename T, int D, int NS, int NP>
-__global__ __launch_bounds__(kWave * (NS + kProducers)) void linear_memory_fwd(const Params p) {
-    using Gm = Geo<T, D, NS, NP>;
-    using K = Kernel<T, D, NS, NP>;
+// One producer wave's loop (role PW): the same barriers as the state waves.
+template <typename T, int D, int NS, int CS, int NP, int PW>
+__device__ __forceinline__ void producer_loop_impl(const Params& p, typename Kernel<T, D, NS, CS, NP>::S& sm,
+                                                   size_t seq_tok, int row_wg, int nch, int lane) {
+    using Gm = Geo<T, D, NS, CS, NP>;
+    using K = Kernel<T, D, NS, CS, NP>;
+    using G = typename Gm::G;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int b = p.b;
+    auto chunk_n = [&](int c) { return min(b, p.T - c * b); };
+    const G* __restrict__ gq = static_cast<const G*>(p.q);
+    const G* __restrict__ gk = static_cast<const G*>(p.k);
+    const G* __restrict__ gv = static_cast<const G*>(p.v);
+    typename K::Prefetch pf;
+    auto prepare = [&](int c, typename K::Buf& B) {   // stage chunk c (held in pf), gates
+        K::template stage<PW>(pf, B, lane);
+        if constexpr (PW == 0) K::gate_scan(pf, sm, B, chunk_n(c), lane);
+        if constexpr (PW == 1) K::gate_diag(pf, sm, chunk_n(c), lane);
+    };
+    auto finish = [&](int c, typename K::Buf& B) {    // P tiles and chunk-end weights
+        K::template ptiles<PW>(sm, B, lr, lg);
+        if constexpr (PW == Gm::NPW - 1) K::wrow(sm, B, chunk_n(c), lane);
+    };
+    auto issue = [&](int c) { K::template issue<PW>(pf, p, gq, gk, gv, seq_tok, row_wg, c, lane); };
+    if constexpr (Gm::NBUF == 2) {
+        if (nch > 0) {
+            issue(0);
+            prepare(0, sm.buf[0]);
+            if (nch > 1) issue(1);
+        }
+        __syncthreads();
+        if (nch > 0) finish(0, sm.buf[0]);
+        __syncthreads();
+        for (int c = 0; c < nch; ++c) {
+            const int nb = (c & 1) ^ 1;
+            if (c + 1 < nch) {
+                prepare(c + 1, sm.buf[nb]);
+                if (c + 2 < nch) issue(c + 2);
+            }
+            __syncthreads();
+            if (c + 1 < nch) finish(c + 1, sm.buf[nb]);
+            __syncthreads();
+        }
+    } else {
+        for (int c = 0; c < nch; ++c) {
+            issue(c);
+            prepare(c, sm.buf[0]);
+            __syncthreads();
+            finish(c, sm.buf[0]);
+            __syncthreads();
+            __syncthreads();
+            __syncthreads();
+        }
+    }
+}
+
+template <typename T, int D, int NS, int CS, int NP>
+__global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 4 : 2))) void linear_memory_fwd(const Params p) {
+    using Gm = Geo<T, D, NS, CS, NP>;
+    using K = Kernel<T, D, NS, CS, NP>;
     using O = Op<T>;
     using G = typename Gm::G;
     using F = typename O::frag;
     constexpr int NBUF = Gm::NBUF;
-    constexpr int NC = Gm::NC;
     constexpr int RB = Gm::RB;
+    constexpr int NSW = Gm::NSW;
 
     __shared__ __attribute__((aligned(16))) typename K::S sm;
 
@@ -666,88 +867,69 @@ __global__ __launch_bounds__(kWave * (NS + kProducers)) void linear_memory_fwd(c
     }
     __syncthreads();
 
-    if (w < NS) {
+    if (w < NSW) {
         // ===================== state wave =====================
-        const int row_w = row_wg + 16 * w;
-        // Tile ct, lane (lr, lg): M[row_w + lr][tmap(ct, 4lg + e)], e = 0..3.
-        f32x4 Macc[NC], Sacc[NC];
-        const size_t state_off = static_cast<size_t>(bh) * D * D + static_cast<size_t>(row_w + lr) * D;
+        typename K::StateCtx x;
+        x.rho = w / CS;
+        x.chi = w % CS;
+        x.r0 = 16 * x.rho;           // first row within the workgroup block
+        x.lr = lr;
+        x.lg = lg;
+        const int row = row_wg + x.r0;
+        // Own column tile cw, lane (lr, lg): M[row + lr][tmap(chi*NCW + cw, 4lg + e)], e = 0..3.
+        f32x4 Macc[Gm::NCW], Sacc[Gm::NCW];
+        const size_t state_off = static_cast<size_t>(bh) * D * D + static_cast<size_t>(row + lr) * D;
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct) {
-            const int col = O::tmap(ct, 4 * lg);
+        for (int cw = 0; cw < Gm::NCW; ++cw) {
+            const int col = O::tmap(x.chi * Gm::NCW + cw, 4 * lg);
             const bool ok = col < D;
-            Macc[ct] = (p.M0 && ok) ? *reinterpret_cast<const f32x4*>(p.M0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-            Sacc[ct] = (p.S0 && ok) ? *reinterpret_cast<const f32x4*>(p.S0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+            Macc[cw] = (p.M0 && ok) ? *reinterpret_cast<const f32x4*>(p.M0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+            Sacc[cw] = (p.S0 && ok) ? *reinterpret_cast<const f32x4*>(p.S0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        F EB[Gm::NKT];
+        F MB[Gm::NKCW], SB[Gm::NKCW];
+        f32x4 E[Gm::NTW], Zp[Gm::NTW];
+        K::own_frags(x, sm, Macc, Sacc, MB, SB);
+        const uint32_t zcol = row + 4 * lg;
         if constexpr (NBUF == 2) {
             __syncthreads();   // chunk 0 staged
             __syncthreads();   // chunk 0 P tiles
             for (int c = 0; c < nch; ++c) {
                 const int bf = c & 1;
-                const size_t zrow0 = (seq_tok + static_cast<size_t>(c) * b) * D + row_w + 4 * lg;
-                K::phase1(Macc, Sacc, sm.buf[bf], EB, p.z, zrow0, chunk_n(c), w, lr, lg);
+                const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
+                                          static_cast<uint32_t>(chunk_n(c)) * D * 4);
+                K::phaseA(x, sm.buf[bf], sm, MB, SB, E, Zp);
                 __syncthreads();
-                K::phase2(Macc, Sacc, sm.buf[bf], EB, lr, lg);
+                K::phaseB(x, sm.buf[bf], sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
                 __syncthreads();
             }
         } else {
             for (int c = 0; c < nch; ++c) {
                 __syncthreads();   // chunk c staged
                 __syncthreads();   // chunk c P tiles
-                const size_t zrow0 = (seq_tok + static_cast<size_t>(c) * b) * D + row_w + 4 * lg;
-                K::phase1(Macc, Sacc, sm.buf[0], EB, p.z, zrow0, chunk_n(c), w, lr, lg);
-                K::phase2(Macc, Sacc, sm.buf[0], EB, lr, lg);
+                const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
+                                          static_cast<uint32_t>(chunk_n(c)) * D * 4);
+                K::phaseA(x, sm.buf[0], sm, MB, SB, E, Zp);
+                __syncthreads();
+                K::phaseB(x, sm.buf[0], sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
                 __syncthreads();   // chunk c consumed
             }
         }
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct) {
-            const int col = O::tmap(ct, 4 * lg);
+        for (int cw = 0; cw < Gm::NCW; ++cw) {
+            const int col = O::tmap(x.chi * Gm::NCW + cw, 4 * lg);
             if (col < D) {
-                if (p.MT) *reinterpret_cast<f32x4*>(p.MT + state_off + col) = Macc[ct];
-                if (p.ST) *reinterpret_cast<f32x4*>(p.ST + state_off + col) = Sacc[ct];
+                if (p.MT) *reinterpret_cast<f32x4*>(p.MT + state_off + col) = Macc[cw];
+                if (p.ST) *reinterpret_cast<f32x4*>(p.ST + state_off + col) = Sacc[cw];
             }
         }
     } else {
         // ===================== producer wave =====================
-        const int pw = w - NS;
-        const int ptid = tid - NS * kWave;
-        const G* __restrict__ gq = static_cast<const G*>(p.q);
-        const G* __restrict__ gk = static_cast<const G*>(p.k);
-        const G* __restrict__ gv = static_cast<const G*>(p.v);
-        typename K::Prefetch pf;
-        if constexpr (NBUF == 2) {
-            if (nch > 0) {
-                K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, 0, ptid, pw, lane);
-                K::stage(pf, sm.buf[0], ptid, pw, lane);
-                if (pw == 0) K::gates(pf, sm, sm.buf[0], chunk_n(0), lane);
-                if (nch > 1) K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, 1, ptid, pw, lane);
-            }
-            __syncthreads();
-            if (nch > 0) K::ptiles(sm, sm.buf[0], chunk_n(0), pw, lr, lg);
-            __syncthreads();
-            for (int c = 0; c < nch; ++c) {
-                const int nb = (c & 1) ^ 1;
-                if (c + 1 < nch) {
-                    K::stage(pf, sm.buf[nb], ptid, pw, lane);
-                    if (pw == 0) K::gates(pf, sm, sm.buf[nb], chunk_n(c + 1), lane);
-                    if (c + 2 < nch) K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, c + 2, ptid, pw, lane);
-                }
-                __syncthreads();
-                if (c + 1 < nch) K::ptiles(sm, sm.buf[nb], chunk_n(c + 1), pw, lr, lg);
-                __syncthreads();
-            }
-        } else {
-            for (int c = 0; c < nch; ++c) {
-                K::issue(pf, p, gq, gk, gv, seq_tok, row_wg, c, ptid, pw, lane);
-                K::stage(pf, sm.buf[0], ptid, pw, lane);
-                if (pw == 0) K::gates(pf, sm, sm.buf[0], chunk_n(c), lane);
-                __syncthreads();
-                K::ptiles(sm, sm.buf[0], chunk_n(c), pw, lr, lg);
-                __syncthreads();
-                __syncthreads();
-            }
+        const int pw = w - NSW;
+        if (pw == 0) producer_loop_impl<T, D, NS, CS, NP, 0>(p, sm, seq_tok, row_wg, nch, lane);
+        else if (pw == 1) producer_loop_impl<T, D, NS, CS, NP, 1>(p, sm, seq_tok, row_wg, nch, lane);
+        else if constexpr (Gm::NPW == 4) {
+            if (pw == 2) producer_loop_impl<T, D, NS, CS, NP, 2>(p, sm, seq_tok, row_wg, nch, lane);
+            else producer_loop_impl<T, D, NS, CS, NP, 3>(p, sm, seq_tok, row_wg, nch, lane);
         }
     }
 }
@@ -755,11 +937,11 @@ __global__ __launch_bounds__(kWave * (NS + kProducers)) void linear_memory_fwd(c
 // ---------------------------------------------------------------------------
 // Host side: validation, instance selection, launch.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NS, int NP>
+template <typename T, int D, int NS, int CS, int NP>
 hipError_t launch(const Params& p, hipStream_t stream) {
-    using Gm = Geo<T, D, NS, NP>;
+    using Gm = Geo<T, D, NS, CS, NP>;
     const long long nwg = static_cast<long long>(p.BH) * Gm::NRB;
-    hipLaunchKernelGGL((linear_memory_fwd<T, D, NS, NP>), dim3(static_cast<unsigned>(nwg)),
+    hipLaunchKernelGGL((linear_memory_fwd<T, D, NS, CS, NP>), dim3(static_cast<unsigned>(nwg)),
                        dim3(kWave * Gm::NWAVE), 0, stream, p);
     return hipGetLastError();
 }
@@ -767,18 +949,21 @@ hipError_t launch(const Params& p, hipStream_t stream) {
 template <typename T, int D, int NS>
 hipError_t launch_np(const Params& p, int np, hipStream_t stream) {
     if constexpr (Op<T>::KG == 32) {
-        return np <= 32 ? launch<T, D, NS, 32>(p, stream) : launch<T, D, NS, 64>(p, stream);
+        // fp16: split the columns over two state waves when every half keeps
+        // whole k-groups (d >= 64).
+        constexpr int CS = D >= 64 ? 2 : 1;
+        return np <= 32 ? launch<T, D, NS, CS, 32>(p, stream) : launch<T, D, NS, CS, 64>(p, stream);
     } else {
-        if (np <= 16) return launch<T, D, NS, 16>(p, stream);
-        if (np <= 32) return launch<T, D, NS, 32>(p, stream);
-        return launch<T, D, NS, 64>(p, stream);
+        if (np <= 16) return launch<T, D, NS, 1, 16>(p, stream);
+        if (np <= 32) return launch<T, D, NS, 1, 32>(p, stream);
+        return launch<T, D, NS, 1, 64>(p, stream);
     }
 }
 
 template <typename T, int D>
 hipError_t launch_ns(const Params& p, int np, hipStream_t stream) {
     if constexpr (D >= 32) {
-        // Two state waves (32 rows) per workgroup when that still leaves >= 256 workgroups.
+        // Two 16-row tiles per workgroup when that still leaves >= 256 workgroups.
         const long long row_tiles = static_cast<long long>(p.BH) * (D / 16);
         if (row_tiles >= 512) return launch_np<T, D, 2>(p, np, stream);
     }
