@@ -94,6 +94,8 @@ __device__ __forceinline__ f16x4 cvt4(f32x4 v) {
 }
 
 constexpr int kWave = 64;
+constexpr int kGR = 20;             // row stride of a diagonal decay block (floats)
+constexpr int kGB = 16 * kGR + 16;  // block stride (floats)
 constexpr int kLdsBytes = 160 * 1024;
 
 __host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -284,7 +286,7 @@ struct Geo {
     static constexpr int BUF_BYTES = (2 * NP * LQ + NP * LP + 2 * NP) * (int)sizeof(T) +
                                      (F16 ? NP * LV * 2 : (DS * LKT + RB * LV) * 4) + (2 * NP + 4) * 4;
     static constexpr int XCH_BYTES = CS > 1 ? NS * (2 * NKC * kWave * 16 + NT * kWave * 8) : 0;
-    static constexpr int HELP_BYTES = (2 * NT * 256 + NT * NP * 3 + 2 * NP) * 4 + XCH_BYTES;
+    static constexpr int HELP_BYTES = (2 * NT * kGB + NT * NP * 3 + 2 * NP) * 4 + XCH_BYTES;
     static constexpr int NBUF = (2 * BUF_BYTES + HELP_BYTES + 1024 <= kLdsBytes) ? 2 : 1;
     static_assert(NP % KG == 0, "chunk padding must fill whole k-groups");
     static_assert(D % RB == 0, "row blocks must tile d");
@@ -311,8 +313,10 @@ struct Smem {
         alignas(16) float scal[4];         // A_n, c_n, E_n
     };
     Buf buf[Gm::NBUF];
-    alignas(16) float gamd[Gm::NT * 256];    // theta_j gamma_ij on diagonal 16-blocks [blk][i][j]
-    alignas(16) float gampd[Gm::NT * 256];   // theta_j p_ij on diagonal 16-blocks
+    // theta_j gamma_ij and theta_j p_ij on the diagonal 16-blocks, [blk][i][j]
+    // with padded rows (kGR floats) and blocks (kGB floats): bank-conflict free.
+    alignas(16) float gamd[Gm::NT * kGB];
+    alignas(16) float gampd[Gm::NT * kGB];
     alignas(16) float phi[Gm::NT * NP * 3];  // maps from the end of block q to row i [q][i][X,Y,W]
     alignas(16) float gend[NP];              // theta_j gamma at the end of column j's block
     alignas(16) float pend[NP];              // theta_j p at the end of column j's block
@@ -379,11 +383,15 @@ struct Kernel {
         // rounds [first, first + count) of the q/k units
         static constexpr int w0 = NPW == 4 ? WU / 8 : WU / 2;
         static constexpr int w1 = NPW == 4 ? WU / 8 : WU - w0;
-        static constexpr int w2 = NPW == 4 ? (3 * WU) / 8 : 0;
+        static constexpr int w2 = NPW == 4 ? WU / 4 : 0;
         static constexpr int first = PW == 0 ? 0 : PW == 1 ? w0 : PW == 2 ? w0 + w1 : w0 + w1 + w2;
         static constexpr int count = PW == 0 ? w0 : PW == 1 ? w1 : PW == 2 ? w2 : WU - w0 - w1 - w2;
         static constexpr bool has_v = PW == (NPW == 4 ? 2 : 1);
     };
+    // Tile-block pairs are dealt round-robin; the chunk-end weight row goes to
+    // the first producer that gets fewer pairs than the others (else the last).
+    static constexpr int NPAIR = (NT / TPB) * (NT / TPB + 1) / 2;
+    static constexpr int kWrowWave = (NPAIR % NPW) == 0 ? NPW - 1 : NPAIR % NPW;
     static constexpr int QUMAX = cmax(cmax(Share<0>::count, Share<1>::count),
                                       cmax(Share<2>::count, Share<3>::count));
     struct Prefetch {
@@ -527,40 +535,41 @@ struct Kernel {
 
     // Producer wave 1: diagonal 16x16 blocks of the decay matrix.  Lane =
     // (block, column j); row i = 16*block + s takes a_i, eta_i from lane s of
-    // the same 16-lane row.
-    template <int S_>
-    __device__ static void diag_step(float a, float et, float th, int jj, float& pp, float& gg, float* gd,
-                                     float* gpd) {
-        const float ai = row_bcast<S_>(a), ei = row_bcast<S_>(et);
-        if (S_ == jj) { pp = 1.f; gg = 1.f; }
-        else if (S_ > jj) { pp = ei * pp; gg = ai * gg + pp; }
-        gd[S_ * 16] = th * gg;
-        gpd[S_ * 16] = th * pp;
-    }
+    // the same 16-lane row.  The column state starts at (gamma, p) = (1, 1) on
+    // its own row: p <- eta_i p + [i == j], gamma <- a_i gamma + p, which is
+    // zero above the diagonal.
     __device__ static void gate_diag(const Prefetch& pf, S& sm, int n, int lane) {
         const int l = lane;
         const float th = pf.th, et = l < n ? pf.et : 1.f, a = 1.f - pf.al;
         const int qb = l >> 4, jj = l & 15;
-        float pp = 0.f, gg = 0.f;
-        float* gd = sm.gamd + qb * 256 + jj;
-        float* gpd = sm.gampd + qb * 256 + jj;
+        float ai[16], ei[16];
+        ai[0] = row_bcast<0>(a); ei[0] = row_bcast<0>(et);
+        ai[1] = row_bcast<1>(a); ei[1] = row_bcast<1>(et);
+        ai[2] = row_bcast<2>(a); ei[2] = row_bcast<2>(et);
+        ai[3] = row_bcast<3>(a); ei[3] = row_bcast<3>(et);
+        ai[4] = row_bcast<4>(a); ei[4] = row_bcast<4>(et);
+        ai[5] = row_bcast<5>(a); ei[5] = row_bcast<5>(et);
+        ai[6] = row_bcast<6>(a); ei[6] = row_bcast<6>(et);
+        ai[7] = row_bcast<7>(a); ei[7] = row_bcast<7>(et);
+        ai[8] = row_bcast<8>(a); ei[8] = row_bcast<8>(et);
+        ai[9] = row_bcast<9>(a); ei[9] = row_bcast<9>(et);
+        ai[10] = row_bcast<10>(a); ei[10] = row_bcast<10>(et);
+        ai[11] = row_bcast<11>(a); ei[11] = row_bcast<11>(et);
+        ai[12] = row_bcast<12>(a); ei[12] = row_bcast<12>(et);
+        ai[13] = row_bcast<13>(a); ei[13] = row_bcast<13>(et);
+        ai[14] = row_bcast<14>(a); ei[14] = row_bcast<14>(et);
+        ai[15] = row_bcast<15>(a); ei[15] = row_bcast<15>(et);
         if (qb < NT) {
-            diag_step<0>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<1>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<2>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<3>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<4>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<5>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<6>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<7>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<8>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<9>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<10>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<11>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<12>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<13>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<14>(a, et, th, jj, pp, gg, gd, gpd);
-            diag_step<15>(a, et, th, jj, pp, gg, gd, gpd);
+            float* gd = sm.gamd + qb * kGB + jj;
+            float* gpd = sm.gampd + qb * kGB + jj;
+            float pp = 0.f, gg = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                pp = ei[s] * pp + (s == jj ? 1.f : 0.f);
+                gg = ai[s] * gg + pp;
+                gd[s * kGR] = th * gg;
+                gpd[s * kGR] = th * pp;
+            }
             sm.gend[l] = th * gg;
             sm.pend[l] = th * pp;
         }
@@ -569,8 +578,8 @@ struct Kernel {
     // theta_j gamma_ij and theta_j p_ij for 4 consecutive j = jb..jb+3 (one 16-block).
     __device__ static void decay4(const S& sm, int i, int jb, f32x4& L, f32x4& LPe) {
         const int bi = i >> 4, bj = jb >> 4;
-        const f32x4 ld = *reinterpret_cast<const f32x4*>(sm.gamd + (bi * 16 + (i & 15)) * 16 + (jb & 15));
-        const f32x4 lpd = *reinterpret_cast<const f32x4*>(sm.gampd + (bi * 16 + (i & 15)) * 16 + (jb & 15));
+        const f32x4 ld = *reinterpret_cast<const f32x4*>(sm.gamd + bi * kGB + (i & 15) * kGR + (jb & 15));
+        const f32x4 lpd = *reinterpret_cast<const f32x4*>(sm.gampd + bi * kGB + (i & 15) * kGR + (jb & 15));
         const f32x4 gv = *reinterpret_cast<const f32x4*>(sm.gend + jb);
         const f32x4 pv = *reinterpret_cast<const f32x4*>(sm.pend + jb);
         const float* ph = sm.phi + (bj * NP + i) * 3;   // in bounds for every bj < NT
@@ -583,25 +592,42 @@ struct Kernel {
 
     // Producers: P tiles.  Tile (pb, qb) holds rows i = tmap(pb, .) and
     // columns j = tmap(qb, .); only tiles whose column k-group is not after the
-    // row's k-group are ever read.  They are dealt round-robin to the producers.
+    // row's k-group are ever read.  Producer PW takes the tiles of row block
+    // and column block (rbk, cbk) = kTiles[PW] (blocks of TPB tiles), so the q
+    // and k fragments of a block are read once for all its tiles.
     template <int PW>
     __device__ static void ptiles(const S& sm, Buf& B, int lr, int lg) {
-        int v = 0;
+        constexpr int NB = NT / TPB;   // k-groups (tile blocks) per chunk
+        // Lower-triangular (rbk, cbk) block pairs in order, dealt to producers.
 #pragma unroll
-        for (int pb = 0; pb < NT; ++pb) {
+        for (int rbk = 0; rbk < NB; ++rbk) {
 #pragma unroll
-            for (int qb = 0; qb < NT; ++qb) {
-                if (qb / TPB > pb / TPB) continue;
-                if ((v++ % NPW) != PW) continue;
-                const int i = O::tmap(pb, lr);
-                const int kr = O::tmap(qb, lr);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int cbk = 0; cbk <= rbk; ++cbk) {
+                const int pair = rbk * (rbk + 1) / 2 + cbk;
+                if (pair % NPW != PW) continue;
+                F qf[TPB][NKC], kf[TPB][NKC];
 #pragma unroll
-                for (int s = 0; s < NKC; ++s) acc = O::mma(acc, frag_q(B.k, kr, s, lg), frag_q(B.q, i, s, lg));
-                const int jb = O::tmap(qb, 4 * lg);   // acc[e] = q_i . k_{jb+e}
-                f32x4 L, LPe;
-                decay4(sm, i, jb, L, LPe);
-                put_p(B.p, i, jb, -(acc * L));
+                for (int h = 0; h < TPB; ++h)
+#pragma unroll
+                    for (int s = 0; s < NKC; ++s) {
+                        qf[h][s] = frag_q(B.q, O::tmap(rbk * TPB + h, lr), s, lg);
+                        kf[h][s] = frag_q(B.k, O::tmap(cbk * TPB + h, lr), s, lg);
+                    }
+#pragma unroll
+                for (int hp = 0; hp < TPB; ++hp) {
+#pragma unroll
+                    for (int hq = 0; hq < TPB; ++hq) {
+                        const int pb = rbk * TPB + hp, qb = cbk * TPB + hq;
+                        const int i = O::tmap(pb, lr);
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < NKC; ++s) acc = O::mma(acc, kf[hq][s], qf[hp][s]);
+                        const int jb = O::tmap(qb, 4 * lg);   // acc[e] = q_i . k_{jb+e}
+                        f32x4 L, LPe;
+                        decay4(sm, i, jb, L, LPe);
+                        put_p(B.p, i, jb, -(acc * L));
+                    }
+                }
             }
         }
     }
@@ -791,7 +817,7 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
     };
     auto finish = [&](int c, typename K::Buf& B) {    // P tiles and chunk-end weights
         K::template ptiles<PW>(sm, B, lr, lg);
-        if constexpr (PW == Gm::NPW - 1) K::wrow(sm, B, chunk_n(c), lane);
+        if constexpr (PW == K::kWrowWave) K::wrow(sm, B, chunk_n(c), lane);
     };
     auto issue = [&](int c) { K::template issue<PW>(pf, p, gq, gk, gv, seq_tok, row_wg, c, lane); };
     if constexpr (Gm::NBUF == 2) {
