@@ -94,25 +94,45 @@ __device__ __forceinline__ f16x4 cvt4(f32x4 v) {
 }
 
 constexpr int kWave = 64;
-constexpr int kGR = 20;             // row stride of a diagonal decay block (floats)
-constexpr int kGB = 16 * kGR + 16;  // block stride (floats)
+constexpr int kGR = 16;             // row stride of a diagonal decay block (floats)
+constexpr int kGB = 16 * kGR + 4;   // block stride (floats): offsets blocks by one 16-byte slot
 constexpr int kLdsBytes = 160 * 1024;
 
 __host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 __host__ __device__ constexpr int cdiv(int x, int m) { return (x + m - 1) / m; }
 __host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// 16-byte chunk swizzle of a row-major fp16 tile with NCH chunks per row:
-// conflict-free for 16 lanes reading one chunk of 16 interleaved tile rows and
-// for the transpose loads of the state update.
+// LDS service on gfx950 (measured with the bank-conflict counter): 64 banks
+// of 4 bytes.  A ds_read_b128 is served in four passes of 16 lanes -- lanes
+// 0-31 split by the parity of lane bits 2, 3 and 4, and the same for lanes
+// 32-63 -- and a pass is conflict-free when its 16 addresses hit distinct
+// 16-byte slots of a 256-byte line.  A ds_write_b128 is served eight
+// consecutive lanes at a time against 128 bytes.  The swizzles below permute
+// the 16-byte chunks of each row of a row-major fp16 tile (NCH chunks per row)
+// so that every MFMA fragment read of interleaved tile rows and every tile
+// write is conflict-free.
+//
+// q and k tiles (also read by the transpose loads of the state update, which
+// use half of each 16-byte slot and so run at half rate whatever the layout).
 template <int NCH>
-__device__ __forceinline__ int swz(int t) {
+__device__ __forceinline__ int swz_qk(int t) {
     if constexpr (NCH >= 16) {
-        return ((t & 3) << 2) | ((t >> 3) & 3);
+        return ((t & 3) << 1) | (t & 8);
     } else if constexpr (NCH == 8) {
-        return ((t >> 1) & 1) | (((t >> 3) & 1) << 1) | ((((t >> 1) ^ (t >> 4)) & 1) << 2);
+        return (t & 2) | ((t >> 1) & 4);
     } else if constexpr (NCH == 4) {
-        return (t >> 3) & 3;
+        return (t >> 2) & 2;
+    } else {
+        return 0;
+    }
+}
+// Intra-chunk weight tile P (rows of NP fp16).
+template <int NCH>
+__device__ __forceinline__ int swz_p(int t) {
+    if constexpr (NCH == 8) {
+        return (t & 3) | ((t >> 1) & 4);
+    } else if constexpr (NCH == 4) {
+        return ((t >> 1) & 1) | ((t >> 2) & 2);
     } else {
         return 0;
     }
@@ -345,7 +365,7 @@ struct Kernel {
     // Fragment of k-group s from row t of a q/k tile, lane group g.
     __device__ static F frag_q(const T* base, int t, int s, int g) {
         if constexpr (F16) {
-            const int ch = (4 * s + g) ^ swz<NCHQ>(t);
+            const int ch = (4 * s + g) ^ swz_qk<NCHQ>(t);
             return *reinterpret_cast<const f16x8*>(base + t * LQ + 8 * ch);
         } else {
             return *reinterpret_cast<const f32x4*>(base + t * LQ + 16 * s + 4 * g);
@@ -353,20 +373,21 @@ struct Kernel {
     }
     __device__ static F frag_p(const T* base, int t, int s, int g) {
         if constexpr (F16) {
-            const int ch = (4 * s + g) ^ swz<NCHP>(t);
+            const int ch = (4 * s + g) ^ swz_p<NCHP>(t);
             return *reinterpret_cast<const f16x8*>(base + t * LP + 8 * ch);
         } else {
             return *reinterpret_cast<const f32x4*>(base + t * LP + 16 * s + 4 * g);
         }
     }
-    // Store indices x..x+3 (x % 4 == 0) of row t of a P tile.
+    // Store indices x..x+3 (x % 4 == 0) of row t of a P tile (float32 path).
     __device__ static void put_p(T* base, int t, int x, f32x4 v) {
-        if constexpr (F16) {
-            const int ch = (x >> 3) ^ swz<NCHP>(t);
-            *reinterpret_cast<f16x4*>(base + t * LP + 8 * ch + (x & 4)) = cvt4(v);
-        } else {
-            *reinterpret_cast<f32x4*>(base + t * LP + x) = v;
-        }
+        *reinterpret_cast<f32x4*>(base + t * LP + x) = v;
+    }
+    // fp16 path: store indices x..x+7 (x % 8 == 0) of row t, one 16-byte chunk.
+    __device__ static void put_p8(T* base, int t, int x, f32x4 lo, f32x4 hi) {
+        const int ch = (x >> 3) ^ swz_p<NCHP>(t);
+        const f16x4 l = cvt4(lo), h = cvt4(hi);
+        *reinterpret_cast<f16x8*>(base + t * LP + 8 * ch) = f16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
     }
     __device__ static F frag_w(const T* w, int s, int g) {
         if constexpr (F16) return *reinterpret_cast<const f16x8*>(w + 32 * s + 8 * g);
@@ -450,7 +471,7 @@ struct Kernel {
             if ((Gm::NQU % kWave) == 0 || u < Gm::NQU) {
                 const int t = u / (D / CB), cb = u % (D / CB);
                 if constexpr (F16) {
-                    const int ch = cb ^ swz<NCHQ>(t);
+                    const int ch = cb ^ swz_qk<NCHQ>(t);
                     const uint4 rq = pf.q[kk], rk = pf.k[kk];
                     f16x8 hq, hk;
 #pragma unroll
@@ -615,18 +636,23 @@ struct Kernel {
                     }
 #pragma unroll
                 for (int hp = 0; hp < TPB; ++hp) {
+                    const int pb = rbk * TPB + hp;
+                    const int i = O::tmap(pb, lr);
+                    f32x4 pv[TPB];
 #pragma unroll
                     for (int hq = 0; hq < TPB; ++hq) {
-                        const int pb = rbk * TPB + hp, qb = cbk * TPB + hq;
-                        const int i = O::tmap(pb, lr);
+                        const int qb = cbk * TPB + hq;
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int s = 0; s < NKC; ++s) acc = O::mma(acc, kf[hq][s], qf[hp][s]);
                         const int jb = O::tmap(qb, 4 * lg);   // acc[e] = q_i . k_{jb+e}
                         f32x4 L, LPe;
                         decay4(sm, i, jb, L, LPe);
-                        put_p(B.p, i, jb, -(acc * L));
+                        pv[hq] = -(acc * L);
                     }
+                    // The TPB column tiles of a block hold consecutive token columns.
+                    if constexpr (F16) put_p8(B.p, i, O::tmap(cbk * TPB, 4 * lg), pv[0], pv[1]);
+                    else put_p(B.p, i, O::tmap(cbk * TPB, 4 * lg), pv[0]);
                 }
             }
         }
@@ -666,8 +692,8 @@ struct Kernel {
             const int ch = col >> 3;
             const int t0 = 32 * s + 8 * lg + (lr >> 2);
             const int t1 = t0 + 4;
-            const i16x4 lo = ds_read_tr16(B.k + t0 * LQ + 8 * (ch ^ swz<NCHQ>(t0)) + (col & 4));
-            const i16x4 hi = ds_read_tr16(B.k + t1 * LQ + 8 * (ch ^ swz<NCHQ>(t1)) + (col & 4));
+            const i16x4 lo = ds_read_tr16(B.k + t0 * LQ + 8 * (ch ^ swz_qk<NCHQ>(t0)) + (col & 4));
+            const i16x4 hi = ds_read_tr16(B.k + t1 * LQ + 8 * (ch ^ swz_qk<NCHQ>(t1)) + (col & 4));
             const f16x4 l4 = __builtin_bit_cast(f16x4, lo), h4 = __builtin_bit_cast(f16x4, hi);
             return F{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
         } else {
