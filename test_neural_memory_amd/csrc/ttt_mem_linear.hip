@@ -596,19 +596,34 @@ struct Kernel {
         }
     }
 
-    // theta_j gamma_ij and theta_j p_ij for 4 consecutive j = jb..jb+3 (one 16-block).
+    // theta_j gamma_ij (and, with PE, theta_j p_ij) for 4 consecutive j =
+    // jb..jb+3 of one 16-block.  Every candidate is loaded (all addresses are
+    // in bounds) and the result selected without branches: lanes of one wave
+    // mix diagonal, below-diagonal and above-diagonal blocks, and branches
+    // around the loads would serialise their LDS latencies.
+    template <bool PE>
     __device__ static void decay4(const S& sm, int i, int jb, f32x4& L, f32x4& LPe) {
         const int bi = i >> 4, bj = jb >> 4;
-        const f32x4 ld = *reinterpret_cast<const f32x4*>(sm.gamd + bi * kGB + (i & 15) * kGR + (jb & 15));
-        const f32x4 lpd = *reinterpret_cast<const f32x4*>(sm.gampd + bi * kGB + (i & 15) * kGR + (jb & 15));
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(sm.gend + jb);
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(sm.pend + jb);
+        f32x4 ld = *reinterpret_cast<const f32x4*>(sm.gamd + bi * kGB + (i & 15) * kGR + (jb & 15));
+        f32x4 gv = *reinterpret_cast<const f32x4*>(sm.gend + jb);
         const float* ph = sm.phi + (bj * NP + i) * 3;   // in bounds for every bj < NT
-        const float x = ph[0], y = ph[1], wv = ph[2];
+        float x = ph[0], y = ph[1];
+        f32x4 lpd, pv;
+        float wv;
+        pv = *reinterpret_cast<const f32x4*>(sm.pend + jb);
+        if constexpr (PE) {
+            lpd = *reinterpret_cast<const f32x4*>(sm.gampd + bi * kGB + (i & 15) * kGR + (jb & 15));
+            wv = ph[2];
+            asm volatile("" : "+v"(lpd), "+v"(wv));
+        }
+        asm volatile("" : "+v"(ld), "+v"(gv), "+v"(pv), "+v"(x), "+v"(y));
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 lo = x * gv + y * pv, lpo = wv * pv;
+        const f32x4 lo = x * gv + y * pv;
         L = bi == bj ? ld : (bi > bj ? lo : zero);
-        LPe = bi == bj ? lpd : (bi > bj ? lpo : zero);
+        if constexpr (PE) {
+            const f32x4 lpo = wv * pv;
+            LPe = bi == bj ? lpd : (bi > bj ? lpo : zero);
+        }
     }
 
     // Producers: P tiles.  Tile (pb, qb) holds rows i = tmap(pb, .) and
@@ -647,7 +662,7 @@ struct Kernel {
                         for (int s = 0; s < NKC; ++s) acc = O::mma(acc, kf[hq][s], qf[hp][s]);
                         const int jb = O::tmap(qb, 4 * lg);   // acc[e] = q_i . k_{jb+e}
                         f32x4 L, LPe;
-                        decay4(sm, i, jb, L, LPe);
+                        decay4<false>(sm, i, jb, L, LPe);
                         pv[hq] = -(acc * L);
                     }
                     // The TPB column tiles of a block hold consecutive token columns.
@@ -661,7 +676,7 @@ struct Kernel {
     __device__ static void wrow(const S& sm, Buf& B, int n, int lane) {
         if (lane < NP / 4) {
             f32x4 L, LPe;
-            decay4(sm, n - 1, 4 * lane, L, LPe);
+            decay4<true>(sm, n - 1, 4 * lane, L, LPe);
             if constexpr (F16) {
                 *reinterpret_cast<f16x4*>(B.wm + 4 * lane) = cvt4(-L);
                 *reinterpret_cast<f16x4*>(B.ws + 4 * lane) = cvt4(-LPe);
@@ -835,8 +850,7 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
     const G* __restrict__ gq = static_cast<const G*>(p.q);
     const G* __restrict__ gk = static_cast<const G*>(p.k);
     const G* __restrict__ gv = static_cast<const G*>(p.v);
-    typename K::Prefetch pf;
-    auto prepare = [&](int c, typename K::Buf& B) {   // stage chunk c (held in pf), gates
+    auto prepare = [&](int c, typename K::Buf& B, const typename K::Prefetch& pf) {   // stage chunk c, gates
         K::template stage<PW>(pf, B, lane);
         if constexpr (PW == 0) K::gate_scan(pf, sm, B, chunk_n(c), lane);
         if constexpr (PW == 1) K::gate_diag(pf, sm, chunk_n(c), lane);
@@ -845,30 +859,43 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
         K::template ptiles<PW>(sm, B, lr, lg);
         if constexpr (PW == K::kWrowWave) K::wrow(sm, B, chunk_n(c), lane);
     };
-    auto issue = [&](int c) { K::template issue<PW>(pf, p, gq, gk, gv, seq_tok, row_wg, c, lane); };
+    auto issue = [&](int c, typename K::Prefetch& pf) {
+        K::template issue<PW>(pf, p, gq, gk, gv, seq_tok, row_wg, c, lane);
+    };
     if constexpr (Gm::NBUF == 2) {
+        // Two register sets of prefetched chunks: the loads of chunk c + 3 are
+        // issued while chunk c + 1 is staged, two chunk periods before use.
+        typename K::Prefetch pf0, pf1;
+        if (nch > 0) issue(0, pf0);
+        if (nch > 1) issue(1, pf1);
         if (nch > 0) {
-            issue(0);
-            prepare(0, sm.buf[0]);
-            if (nch > 1) issue(1);
+            prepare(0, sm.buf[0], pf0);
+            if (nch > 2) issue(2, pf0);
         }
         __syncthreads();
         if (nch > 0) finish(0, sm.buf[0]);
         __syncthreads();
-        for (int c = 0; c < nch; ++c) {
+        // Step c stages chunk c + 1 (held in pf) into buffer (c + 1) & 1 while
+        // the state waves consume chunk c, then builds its P tiles.
+        auto step = [&](int c, typename K::Prefetch& pf) {
             const int nb = (c & 1) ^ 1;
             if (c + 1 < nch) {
-                prepare(c + 1, sm.buf[nb]);
-                if (c + 2 < nch) issue(c + 2);
+                prepare(c + 1, sm.buf[nb], pf);
+                if (c + 3 < nch) issue(c + 3, pf);
             }
             __syncthreads();
             if (c + 1 < nch) finish(c + 1, sm.buf[nb]);
             __syncthreads();
+        };
+        for (int c = 0; c < nch; c += 2) {
+            step(c, pf1);
+            if (c + 1 < nch) step(c + 1, pf0);
         }
     } else {
+        typename K::Prefetch pf;
         for (int c = 0; c < nch; ++c) {
-            issue(c);
-            prepare(c, sm.buf[0]);
+            issue(c, pf);
+            prepare(c, sm.buf[0], pf);
             __syncthreads();
             finish(c, sm.buf[0]);
             __syncthreads();
