@@ -877,19 +877,18 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
         __syncthreads();
         // Step c stages chunk c + 1 (held in pf) into buffer (c + 1) & 1 while
         // the state waves consume chunk c, then builds its P tiles.
-        auto step = [&](int c, typename K::Prefetch& pf) {
-            const int nb = (c & 1) ^ 1;
+        auto step = [&](int c, typename K::Prefetch& pf, typename K::Buf& B) {
             if (c + 1 < nch) {
-                prepare(c + 1, sm.buf[nb], pf);
+                prepare(c + 1, B, pf);
                 if (c + 3 < nch) issue(c + 3, pf);
             }
             __syncthreads();
-            if (c + 1 < nch) finish(c + 1, sm.buf[nb]);
+            if (c + 1 < nch) finish(c + 1, B);
             __syncthreads();
         };
         for (int c = 0; c < nch; c += 2) {
-            step(c, pf1);
-            if (c + 1 < nch) step(c + 1, pf0);
+            step(c, pf1, sm.buf[1]);
+            if (c + 1 < nch) step(c + 1, pf0, sm.buf[0]);
         }
     } else {
         typename K::Prefetch pf;
@@ -972,14 +971,19 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 4 : 2))) void linear_
         if constexpr (NBUF == 2) {
             __syncthreads();   // chunk 0 staged
             __syncthreads();   // chunk 0 P tiles
-            for (int c = 0; c < nch; ++c) {
-                const int bf = c & 1;
+            // Chunk c reads buffer c & 1; the loop is unrolled by two so that
+            // every LDS address is a compile-time offset from lane constants.
+            auto chunk = [&](int c, const typename K::Buf& B) {
                 const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
                                           static_cast<uint32_t>(chunk_n(c)) * D * 4);
-                K::phaseA(x, sm.buf[bf], sm, MB, SB, E, Zp);
+                K::phaseA(x, B, sm, MB, SB, E, Zp);
                 __syncthreads();
-                K::phaseB(x, sm.buf[bf], sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
+                K::phaseB(x, B, sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
                 __syncthreads();
+            };
+            for (int c = 0; c < nch; c += 2) {
+                chunk(c, sm.buf[0]);
+                if (c + 1 < nch) chunk(c + 1, sm.buf[1]);
             }
         } else {
             for (int c = 0; c < nch; ++c) {
