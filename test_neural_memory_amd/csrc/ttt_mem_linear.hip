@@ -423,13 +423,16 @@ struct Kernel {
     };
 
     // Issue the global loads of chunk c into registers; nothing here waits for
-    // them.  Rows past the chunk's n tokens read as zeros through the bounds.
+    // them.  Rows past the chunk's n tokens read as zeros through the bounds,
+    // and a chunk past the end of the sequence has n = 0: its loads touch no
+    // memory.  Issuing unconditionally keeps the number of loads in flight the
+    // same on every path, so waits on an older prefetch set stay partial.
     template <int PW>
     __device__ static void issue(Prefetch& pf, const Params& p, const G* gq, const G* gk, const G* gv,
                                  size_t seq_tok, int row_wg, int c, int lane) {
         using Sh = Share<PW>;
         const int c0 = c * p.b;
-        const int n = min(p.b, p.T - c0);
+        const int n = max(0, min(p.b, p.T - c0));
         const size_t chunk_off = (seq_tok + c0) * D;
         const uint32_t nbytes = static_cast<uint32_t>(n) * D * sizeof(G);
         const auto rq = make_rsrc(gq + chunk_off, nbytes);
@@ -866,22 +869,18 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
         // Two register sets of prefetched chunks: the loads of chunk c + 3 are
         // issued while chunk c + 1 is staged, two chunk periods before use.
         typename K::Prefetch pf0, pf1;
-        if (nch > 0) issue(0, pf0);
-        if (nch > 1) issue(1, pf1);
-        if (nch > 0) {
-            prepare(0, sm.buf[0], pf0);
-            if (nch > 2) issue(2, pf0);
-        }
+        issue(0, pf0);
+        issue(1, pf1);
+        if (nch > 0) prepare(0, sm.buf[0], pf0);
+        issue(2, pf0);
         __syncthreads();
         if (nch > 0) finish(0, sm.buf[0]);
         __syncthreads();
         // Step c stages chunk c + 1 (held in pf) into buffer (c + 1) & 1 while
         // the state waves consume chunk c, then builds its P tiles.
         auto step = [&](int c, typename K::Prefetch& pf, typename K::Buf& B) {
-            if (c + 1 < nch) {
-                prepare(c + 1, B, pf);
-                if (c + 3 < nch) issue(c + 3, pf);
-            }
+            if (c + 1 < nch) prepare(c + 1, B, pf);
+            issue(c + 3, pf);
             __syncthreads();
             if (c + 1 < nch) finish(c + 1, B);
             __syncthreads();
