@@ -93,6 +93,36 @@ int ttt_mem_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          float* z, float* M_T, float* S_T,
                          int B, int H, int T, int d, int b, void* stream);
 
+/*
+ * Deep (two-layer MLP) memory, bfloat16 q, k, v; float32 gates, weights,
+ * momenta and z.  The memory is f(u) = u + SiLU(u W1) W2 in row-vector form
+ * (W1: d x hidden, W2: hidden x d, no biases), written by gradient steps on
+ * 1/2 ||f(k_t) - v_t||^2 taken by explicit backprop at the chunk-start
+ * weights; each tensor has its own momentum (S1, S2) and both use the token's
+ * theta, eta, alpha with the same recurrences as the linear memory
+ * ("论文速览 | Titans", sections 3.4, 3.7, 3.9 and 4.2; "Continual Learning:
+ * From Attention to Neural Memory", sections 4.2 and 5.1-5.2).  The read is
+ * z_t = f(q_t) with the weights after token t's own write.
+ *
+ *   Layouts: q, k, v, z [B, H, T, d] as above; W1_0, S1_0, W1_T, S1_T
+ *   [B, H, d, hidden] and W2_0, S2_0, W2_T, S2_T [B, H, hidden, d], float32
+ *   row-major (W1[i*hidden + j] maps input coordinate i to hidden unit j).
+ *   W1_0 and W2_0 are required; S1_0, S2_0 may be NULL (zeros); any output
+ *   weight may be NULL (not written) or the same pointer as its own initial
+ *   tensor (in-place carry).  Pointers to the weights must be 4-byte aligned;
+ *   q, k, v, z 16-byte aligned.
+ *   Sizes: d = 64 and hidden = 256, 1 <= b <= 16 (other sizes return
+ *   TTT_ERR_UNSUPPORTED).  Matrix products use fp16 operands with float32
+ *   accumulation (same precondition as ttt_mem_forward_bf16); SiLU uses the
+ *   hardware exp2 and reciprocal.
+ */
+int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const float* theta, const float* eta, const float* alpha,
+                             const float* W1_0, const float* W2_0,
+                             const float* S1_0, const float* S2_0,
+                             float* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T,
+                             int B, int H, int T, int d, int hidden, int b, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* ttt_mem_status_string(int status);
 

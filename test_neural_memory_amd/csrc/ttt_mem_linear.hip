@@ -75,23 +75,10 @@
 #include <stdint.h>
 
 #include "ttt_mem.h"
+#include "gfx950.h"
 
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// Two floats to two fp16, round to nearest even (one v_cvt_pk_f16_f32).
-__device__ __forceinline__ f16x2 cvt2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, f16x2); }
-__device__ __forceinline__ f16x4 cvt4(f32x4 v) {
-    const f16x2 lo = cvt2(v[0], v[1]), hi = cvt2(v[2], v[3]);
-    return f16x4{lo[0], lo[1], hi[0], hi[1]};
-}
 
 constexpr int kWave = 64;
 constexpr int kGR = 16;             // row stride of a diagonal decay block (floats)
@@ -138,13 +125,6 @@ __device__ __forceinline__ int swz_p(int t) {
     }
 }
 
-// LDS transpose load of four 16-bit elements (gfx950).  Within each group of
-// 16 lanes, lane i receives element i%4 of the chunk read by lane 4j + i/4 in
-// slot j.
-__device__ __forceinline__ i16x4 ds_read_tr16(const void* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(p)));
-}
 
 // ---------------------------------------------------------------------------
 // MFMA operand traits.  A "k-group" is the contraction length of one operand
@@ -201,29 +181,7 @@ template <typename T> struct GlobalOf;
 template <> struct GlobalOf<float> { using type = float; };
 template <> struct GlobalOf<_Float16> { using type = uint16_t; };
 
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// DPP move with an identity for lanes that have no source (gfx9 controls).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_or(float identity, float src) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, identity),
-                                                                 __builtin_bit_cast(int, src), CTRL, ROW_MASK,
-                                                                 0xf, false));
-}
-// One inclusive-scan step over 2x2 upper-triangular maps [[X, Y], [0, W]]:
-// mine <- mine * earlier (the earlier map is applied first).
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ void tri_step(float& X, float& Y, float& W) {
-    const float xs = dpp_or<CTRL, ROW_MASK>(1.f, X);
-    const float ys = dpp_or<CTRL, ROW_MASK>(0.f, Y);
-    const float ws = dpp_or<CTRL, ROW_MASK>(1.f, W);
-    Y = X * ys + Y * ws;
-    X = X * xs;
-    W = W * ws;
-}
-constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 // row_newbcast:N -- every lane of a 16-lane row receives lane N of that row.
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
@@ -231,25 +189,7 @@ __device__ __forceinline__ float row_bcast(float x) {
                                                                  0xf, false));
 }
 
-// Raw buffer descriptor over nbytes at ptr: accesses at or past nbytes read 0
-// and are not written, which bounds ragged chunks without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* ptr, uint32_t nbytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ptr), (short)0, static_cast<int>(nbytes), 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ __forceinline__ void buf_store16(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
-}
 
-__device__ __forceinline__ float readlane(float x, int lane) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
-}
 
 struct Params {
     const void* q;
@@ -1063,13 +1003,6 @@ hipError_t dispatch(const Params& p, int d, hipStream_t stream) {
     }
 }
 
-bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-    if (!a || !b) return false;
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    return x < y + nb && y < x + na;
-}
 
 template <typename T>
 int forward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,

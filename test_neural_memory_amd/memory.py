@@ -82,3 +82,49 @@ def forward(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
     if q.dtype == torch.bfloat16:
         return ttt_mem_forward_bf16(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
     raise TypeError(f"unsupported input dtype {q.dtype}")
+
+
+def ttt_mem_mlp_forward_bf16(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0=None, S2_0=None, *, b, out=None):
+    """bf16-input deep (2-layer MLP) memory; returns ``(z, W1_T, W2_T, S1_T, S2_T)``.
+
+    ``W1_0, S1_0`` are ``[B, H, d, hidden]`` and ``W2_0, S2_0`` ``[B, H, hidden, d]``
+    float32; ``out`` may pass preallocated ``(z, W1_T, W2_T, S1_T, S2_T)``.
+    """
+    name = "ttt_mem_mlp_forward_bf16"
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be HIP device tensors (torch 'cuda' device)")
+    if W1_0 is None or W2_0 is None:
+        raise ValueError("W1_0 and W2_0 are required")
+    hid = W1_0.shape[-1]
+    q = _as_dev(q, "q", torch.bfloat16, (B, H, T, d), dev)
+    k = _as_dev(k, "k", torch.bfloat16, (B, H, T, d), dev)
+    v = _as_dev(v, "v", torch.bfloat16, (B, H, T, d), dev)
+    theta = _as_dev(theta, "theta", torch.float32, (B, H, T), dev)
+    eta = _as_dev(eta, "eta", torch.float32, (B, H, T), dev)
+    alpha = _as_dev(alpha, "alpha", torch.float32, (B, H, T), dev)
+    W1_0 = _as_dev(W1_0, "W1_0", torch.float32, (B, H, d, hid), dev)
+    W2_0 = _as_dev(W2_0, "W2_0", torch.float32, (B, H, hid, d), dev)
+    S1_0 = _as_dev(S1_0, "S1_0", torch.float32, (B, H, d, hid), dev)
+    S2_0 = _as_dev(S2_0, "S2_0", torch.float32, (B, H, hid, d), dev)
+    shapes = ((B, H, T, d), (B, H, d, hid), (B, H, hid, d), (B, H, d, hid), (B, H, hid, d))
+    if out is None:
+        out = tuple(torch.empty(s, dtype=torch.float32, device=dev) for s in shapes)
+    else:
+        for t, nm, shp in zip(out, ("z", "W1_T", "W2_T", "S1_T", "S2_T"), shapes):
+            if t is not None and (not t.is_contiguous() or t.dtype != torch.float32
+                                  or tuple(t.shape) != shp or t.device != dev):
+                raise ValueError(f"out tensor {nm} must be contiguous float32 {shp} on {dev}")
+    z, W1_T, W2_T, S1_T, S2_T = out
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        status = lib.ttt_mem_mlp_forward_bf16(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(W1_0), _ptr(W2_0),
+            _ptr(S1_0), _ptr(S2_0), _ptr(z), _ptr(W1_T), _ptr(W2_T), _ptr(S1_T), _ptr(S2_T),
+            B, H, T, d, int(hid), int(b), stream)
+    _lib.check(name, status)
+    return z, W1_T, W2_T, S1_T, S2_T
