@@ -1,11 +1,13 @@
-"""Throughput of the chunked TTT / Titans linear-memory forward on one MI355X.
+"""Throughput of the chunked TTT / Titans memory forward on one MI355X.
 
 A step is one forward pass of the whole memory layer -- every (batch, head)
 sequence, every chunk -- over one batch of synthetic inputs that are already
-resident in HBM: the Titans linear-memory workload, B=4 H=16 T=8192 d=128 b=64,
-bf16 q/k/v, float32 gates, state and z.  Prints ONE JSON line.
+resident in HBM.  By default: the Titans linear-memory workload, B=4 H=16
+T=8192 d=128 b=64, bf16 q/k/v, float32 gates, state and z.  ``--workload 5``
+times the deep (2-layer MLP) memory workload, B=4 H=8 T=4096 d=64 hidden=256
+b=16.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {2,3,4,5}] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -50,6 +52,24 @@ def algorithmic_work(w, in_bytes=2, z_bytes=4, reads_state=False):
     return ht * per_tok + state, flops, per_tok
 
 
+def algorithmic_work_mlp(w, in_bytes=2, z_bytes=4):
+    """Bytes and flops of one deep-memory forward (f(u) = u + SiLU(u W1) W2, hidden h).
+
+    Per (batch, head, token), per chunk of b tokens in the dual form: 2dh flops
+    for each of K W1, Ak W2, R W2^T, Q W1, Q S1, Aq W2, Aq S2 and for each of the
+    four weight/momentum carries (22 dh = 88 d^2 at h = 4d), plus 2bd or 2bh
+    for each of Q K^T, (L.QK^T) dH, Aq Ak^T and (L.G) R (4b(d + h) = 20bd).
+    Bytes: q, k, v, three gates and z per token; the four weight tensors read
+    and written once per (batch, head).
+    """
+    ht = w.B * w.H * w.T
+    d, h = w.d, w.hidden
+    per_tok = 3 * d * in_bytes + 3 * 4 + d * z_bytes
+    state = w.B * w.H * 8 * d * h * 4
+    flops = ht * (22 * d * h + 4 * w.b * (d + h))
+    return ht * per_tok + state, flops, per_tok
+
+
 def measured_traffic(w):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter summary.
 
@@ -74,12 +94,15 @@ def measured_traffic(w):
 
 def _oracle_worker(args):
     # Runs in a separate process: one BLAS thread, the oracle as it stands.
-    q, k, v, th, et, al, b = args
+    q, k, v, th, et, al, b, W1, W2 = args
     from threadpoolctl import threadpool_limits
-    from oracle import linear_forward
+    from oracle import linear_forward, mlp_forward
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        linear_forward(q, k, v, th, et, al, None, None, b=b)
+        if W1 is None:
+            linear_forward(q, k, v, th, et, al, None, None, b=b)
+        else:
+            mlp_forward(q, k, v, th, et, al, W1, W2, None, None, b=b)
         return time.perf_counter() - t0
 
 
@@ -87,7 +110,7 @@ def cpu_baseline(w, inp, heads):
     """Time the float64 oracle on ``heads`` (batch, head) pairs with full T, in a process pool."""
     import multiprocessing as mp
     ncores = max(1, min(len(os.sched_getaffinity(0)), 16))
-    g = {k: to_numpy64(v) for k, v in inp.items() if k in ("q", "k", "v", "theta", "eta", "alpha")}
+    g = {k: to_numpy64(v) for k, v in inp.items() if k in ("q", "k", "v", "theta", "eta", "alpha", "W1", "W2")}
     B, H = w.B, w.H
     pairs = [(i // H, i % H) for i in range(B * H)][:heads]
     groups = [pairs[i::ncores] for i in range(ncores)]
@@ -97,7 +120,8 @@ def cpu_baseline(w, inp, heads):
             continue
         bi = np.array([p[0] for p in grp])
         hi = np.array([p[1] for p in grp])
-        jobs.append(tuple(g[x][bi, hi] for x in ("q", "k", "v", "theta", "eta", "alpha")) + (w.b,))
+        jobs.append(tuple(g[x][bi, hi] for x in ("q", "k", "v", "theta", "eta", "alpha")) + (w.b,)
+                    + ((g["W1"][bi, hi], g["W2"][bi, hi]) if w.hidden else (None, None)))
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(len(jobs)) as pool:
@@ -109,7 +133,8 @@ def cpu_baseline(w, inp, heads):
         "unit": "tokens/s",
         "cores": len(jobs),
         "kind": "oracle",
-        "sample": f"{len(pairs)} of {B * H} (batch, head) sequences, full T={w.T}, all d={w.d} rows; "
+        "sample": f"{len(pairs)} of {B * H} (batch, head) sequences, full T={w.T}"
+                  f"{'' if w.hidden else f', all d={w.d} rows'}; "
                   f"float64 per-token NumPy loop, {len(jobs)} processes x 1 thread; "
                   f"wall {wall:.2f} s, busiest process {max(per_job):.2f} s; "
                   f"tokens/s = sampled head-tokens / H / wall",
@@ -121,9 +146,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) sequences in the oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="(batch, head) sequences in the oracle sample (0: 64 for the linear memory, "
+                         "16 for the deep memory)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed region, run 3 plain device copies of MIB MiB (float32 read once, "
                          "written once) so that hardware byte counters can be scaled against known traffic")
@@ -139,15 +166,22 @@ def main():
         sys.exit(2)
 
     w = WORKLOADS[args.workload]
+    deep = w.hidden > 0
     log(f"workload {w}")
     inp = make_inputs(w)
     dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     B, H, T, d = w.B, w.H, w.T, w.d
     z = torch.empty(B, H, T, d, dtype=torch.float32, device="cuda")
-    MT = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
-    ST = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
-    call = lambda: tm.forward(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"],  # noqa: E731
-                              dev.get("M0"), dev.get("S0"), b=w.b, out=(z, MT, ST))
+    if deep:
+        outs = (z,) + tuple(torch.empty_like(dev[k]) for k in ("W1", "W2", "W1", "W2"))
+        call = lambda: tm.ttt_mem_mlp_forward_bf16(  # noqa: E731
+            dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"], dev["W1"], dev["W2"],
+            b=w.b, out=outs)
+    else:
+        MT = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+        ST = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+        call = lambda: tm.forward(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"],  # noqa: E731
+                                  dev.get("M0"), dev.get("S0"), b=w.b, out=(z, MT, ST))
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -179,32 +213,62 @@ def main():
     ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
     avg_launch_ms = float(np.mean(launch_ms))
 
-    nbytes, flops, per_tok = algorithmic_work(w, reads_state=dev.get("M0") is not None)
-    traffic = measured_traffic(w)
+    if deep:
+        nbytes, flops, per_tok = algorithmic_work_mlp(w)
+        traffic = None
+    else:
+        nbytes, flops, per_tok = algorithmic_work(w, reads_state=dev.get("M0") is not None)
+        traffic = measured_traffic(w)
     achieved_gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    achieved_tflops = flops / (avg_launch_ms * 1e-3) / 1e12
     tokens_per_s = B * T / (ms_per_step * 1e-3)
     log(f"avg launch {avg_launch_ms * 1e3:.1f} us, min {min(launch_ms) * 1e3:.1f} us, "
         f"max {max(launch_ms) * 1e3:.1f} us; wall/step {t_wall / args.steps * 1e3:.3f} ms")
     log(f"algorithmic bytes/launch {nbytes / 1e6:.1f} MB -> {achieved_gbs:.0f} GB/s; "
-        f"flops/launch {flops / 1e9:.1f} GFLOP -> {flops / (avg_launch_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+        f"flops/launch {flops / 1e9:.1f} GFLOP -> {achieved_tflops:.1f} TFLOP/s")
 
     # Sampled parity check of the timed outputs against the oracle.
-    from oracle import linear_forward
-    rows = np.r_[0:4, d - 4:d]
+    from oracle import linear_forward, mlp_forward
     g = {k: to_numpy64(v[0, 0]) for k, v in inp.items() if v is not None}
-    zo, Mo, So = linear_forward(g["q"], g["k"], g["v"][:, rows], g["theta"], g["eta"], g["alpha"], None, None, b=w.b)
-    zg = z[0, 0][:, rows].double().cpu().numpy()
+    if deep:
+        zo = mlp_forward(g["q"], g["k"], g["v"], g["theta"], g["eta"], g["alpha"], g["W1"], g["W2"], b=w.b)[0]
+        zg = z[0, 0].double().cpu().numpy()
+        what = "sequence 0, all columns"
+    else:
+        rows = np.r_[0:4, d - 4:d]
+        M0 = g["M0"][rows] if "M0" in g else None
+        zo = linear_forward(g["q"], g["k"], g["v"][:, rows], g["theta"], g["eta"], g["alpha"], M0, None, b=w.b)[0]
+        zg = z[0, 0][:, rows].double().cpu().numpy()
+        what = f"sequence 0, rows {list(rows)}"
     rms = float(np.sqrt(np.mean(zo ** 2)))
     parity = float(np.max(np.abs(zg - zo)) / rms)
-    log(f"sampled parity (sequence 0, rows {list(rows)}): max|dz|/rms = {parity:.3e}")
+    log(f"sampled parity ({what}): max|dz|/rms = {parity:.3e}")
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp, args.cpu_heads)
+        heads = args.cpu_heads or (16 if deep else 64)
+        cpu = cpu_baseline(w, inp, heads)
         log(f"cpu baseline: {cpu}")
 
+    if deep:
+        metric = "deep-memory tokens/s at H=8,d=64,hidden=256,b=16"
+        roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                    "hbm_frac": achieved_gbs / HBM_PEAK_GBS}
+        cfg = {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "hidden": w.hidden, "b": w.b,
+               "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "weights": "f32", "z": "f32",
+               "head_tokens_per_s": B * H * T / (ms_per_step * 1e-3)}
+    else:
+        metric = "memory-layer tokens/s at H=16,d=128,b=64"
+        roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved_gbs / HBM_PEAK_GBS,
+                    "traffic": traffic, "traffic_unit": "bytes/launch", "algorithmic_bytes": nbytes,
+                    "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS}
+        cfg = {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "b": w.b,
+               "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "state": "f32", "z": "f32",
+               "head_tokens_per_s": B * H * T / (ms_per_step * 1e-3)}
     result = {
-        "metric": "memory-layer tokens/s at H=16,d=128,b=64",
+        "metric": metric,
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -216,13 +280,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "b": w.b,
-                   "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "state": "f32", "z": "f32",
-                   "head_tokens_per_s": B * H * T / (ms_per_step * 1e-3)},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic, "traffic_unit": "bytes/launch", "algorithmic_bytes": nbytes,
-                     "mfma_frac": flops / (avg_launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "config": cfg,
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "parity_sample_max_rel_err": parity,
     }
