@@ -227,7 +227,7 @@ struct Geo {
     static constexpr int NCW = NC / CS;               // column tiles of one state wave
     static constexpr int NKCW = NKC / CS;             // column k-groups of one state wave
     static constexpr int NTW = NT / CS;               // token tiles read out by one state wave
-    static constexpr int NPW = CS == 2 ? 4 : 2;       // producer waves
+    static constexpr int NPW = CS == 2 ? 8 : 2;       // producer waves
     static constexpr int NSW = NS * CS;               // state waves
     static constexpr int NWAVE = NSW + NPW;
     // LDS row strides in elements.  fp16: unpadded, 16-byte-chunk swizzled;
@@ -339,22 +339,36 @@ struct Kernel {
     // units (the two gate waves take smaller shares), v rows (one wave), gate
     // work and P tiles, all known at compile time.
     static constexpr int WU = cdiv(Gm::NQU, kWave);   // q (or k) units per chunk in 64-lane rounds
+    // q/k rounds of producer PW.  With eight producers the gate waves 0 and 1
+    // take WU/16 rounds each and waves 2..7 split the rest evenly; with two,
+    // the rounds are halved.
+    static constexpr int rounds(int pw) {
+        if (NPW == 8) {
+            const int g = WU / 16;
+            if (pw < 2) return g;
+            const int rest = WU - 2 * g;
+            return rest / 6 + (pw - 2 < rest % 6 ? 1 : 0);
+        }
+        return pw == 0 ? WU / 2 : WU - WU / 2;
+    }
+    static constexpr int first_round(int pw) { return pw == 0 ? 0 : first_round(pw - 1) + rounds(pw - 1); }
     template <int PW>
     struct Share {
-        // rounds [first, first + count) of the q/k units
-        static constexpr int w0 = NPW == 4 ? WU / 8 : WU / 2;
-        static constexpr int w1 = NPW == 4 ? WU / 8 : WU - w0;
-        static constexpr int w2 = NPW == 4 ? WU / 4 : 0;
-        static constexpr int first = PW == 0 ? 0 : PW == 1 ? w0 : PW == 2 ? w0 + w1 : w0 + w1 + w2;
-        static constexpr int count = PW == 0 ? w0 : PW == 1 ? w1 : PW == 2 ? w2 : WU - w0 - w1 - w2;
-        static constexpr bool has_v = PW == (NPW == 4 ? 2 : 1);
+        static constexpr int first = first_round(PW);
+        static constexpr int count = rounds(PW);
+        static constexpr bool has_v = PW == NPW - 1;
     };
-    // Tile-block pairs are dealt round-robin; the chunk-end weight row goes to
-    // the first producer that gets fewer pairs than the others (else the last).
+    // P tiles: with eight producers, the row tiles of each lower-triangular
+    // tile-block pair (one row tile against the pair's column block) are dealt
+    // to waves 2..7 and the chunk-end weights go to wave 0; otherwise whole
+    // pairs are dealt round-robin and the weights go to the last wave.
     static constexpr int NPAIR = (NT / TPB) * (NT / TPB + 1) / 2;
-    static constexpr int kWrowWave = (NPAIR % NPW) == 0 ? NPW - 1 : NPAIR % NPW;
-    static constexpr int QUMAX = cmax(cmax(Share<0>::count, Share<1>::count),
-                                      cmax(Share<2>::count, Share<3>::count));
+    static constexpr int kWrowWave = NPW == 8 ? 0 : ((NPAIR % NPW) == 0 ? NPW - 1 : NPAIR % NPW);
+    static constexpr int unit_owner(int pair, int hp) {
+        return NPW == 8 ? 2 + (pair * TPB + hp) % (NPW - 2) : pair % NPW;
+    }
+    static constexpr int qumax(int pw) { return pw == NPW ? 0 : cmax(rounds(pw), qumax(pw + 1)); }
+    static constexpr int QUMAX = qumax(0);
     struct Prefetch {
         uint4 q[QUMAX > 0 ? QUMAX : 1];
         uint4 k[QUMAX > 0 ? QUMAX : 1];
@@ -577,32 +591,37 @@ struct Kernel {
     template <int PW>
     __device__ static void ptiles(const S& sm, Buf& B, int lr, int lg) {
         constexpr int NB = NT / TPB;   // k-groups (tile blocks) per chunk
-        // Lower-triangular (rbk, cbk) block pairs in order, dealt to producers.
+        // Lower-triangular (rbk, cbk) block pairs in order; row tile hp of a
+        // pair belongs to producer unit_owner(pair, hp).
 #pragma unroll
         for (int rbk = 0; rbk < NB; ++rbk) {
 #pragma unroll
             for (int cbk = 0; cbk <= rbk; ++cbk) {
                 const int pair = rbk * (rbk + 1) / 2 + cbk;
-                if (pair % NPW != PW) continue;
-                F qf[TPB][NKC], kf[TPB][NKC];
+                bool any = false;
+#pragma unroll
+                for (int hp = 0; hp < TPB; ++hp) any = any || unit_owner(pair, hp) == PW;
+                if (!any) continue;
+                F kf[TPB][NKC];
 #pragma unroll
                 for (int h = 0; h < TPB; ++h)
 #pragma unroll
-                    for (int s = 0; s < NKC; ++s) {
-                        qf[h][s] = frag_q(B.q, O::tmap(rbk * TPB + h, lr), s, lg);
-                        kf[h][s] = frag_q(B.k, O::tmap(cbk * TPB + h, lr), s, lg);
-                    }
+                    for (int s = 0; s < NKC; ++s) kf[h][s] = frag_q(B.k, O::tmap(cbk * TPB + h, lr), s, lg);
 #pragma unroll
                 for (int hp = 0; hp < TPB; ++hp) {
+                    if (unit_owner(pair, hp) != PW) continue;
                     const int pb = rbk * TPB + hp;
                     const int i = O::tmap(pb, lr);
+                    F qf[NKC];
+#pragma unroll
+                    for (int s = 0; s < NKC; ++s) qf[s] = frag_q(B.q, i, s, lg);
                     f32x4 pv[TPB];
 #pragma unroll
                     for (int hq = 0; hq < TPB; ++hq) {
                         const int qb = cbk * TPB + hq;
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int s = 0; s < NKC; ++s) acc = O::mma(acc, kf[hq][s], qf[hp][s]);
+                        for (int s = 0; s < NKC; ++s) acc = O::mma(acc, kf[hq][s], qf[s]);
                         const int jb = O::tmap(qb, 4 * lg);   // acc[e] = q_i . k_{jb+e}
                         f32x4 L, LPe;
                         decay4<false>(sm, i, jb, L, LPe);
@@ -844,7 +863,7 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
 }
 
 template <typename T, int D, int NS, int CS, int NP>
-__global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 4 : 2))) void linear_memory_fwd(const Params p) {
+__global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_memory_fwd(const Params p) {
     using Gm = Geo<T, D, NS, CS, NP>;
     using K = Kernel<T, D, NS, CS, NP>;
     using O = Op<T>;
@@ -949,9 +968,15 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 4 : 2))) void linear_
         const int pw = w - NSW;
         if (pw == 0) producer_loop_impl<T, D, NS, CS, NP, 0>(p, sm, seq_tok, row_wg, nch, lane);
         else if (pw == 1) producer_loop_impl<T, D, NS, CS, NP, 1>(p, sm, seq_tok, row_wg, nch, lane);
-        else if constexpr (Gm::NPW == 4) {
-            if (pw == 2) producer_loop_impl<T, D, NS, CS, NP, 2>(p, sm, seq_tok, row_wg, nch, lane);
-            else producer_loop_impl<T, D, NS, CS, NP, 3>(p, sm, seq_tok, row_wg, nch, lane);
+        else if constexpr (Gm::NPW == 8) {
+            switch (pw) {
+                case 2: producer_loop_impl<T, D, NS, CS, NP, 2>(p, sm, seq_tok, row_wg, nch, lane); break;
+                case 3: producer_loop_impl<T, D, NS, CS, NP, 3>(p, sm, seq_tok, row_wg, nch, lane); break;
+                case 4: producer_loop_impl<T, D, NS, CS, NP, 4>(p, sm, seq_tok, row_wg, nch, lane); break;
+                case 5: producer_loop_impl<T, D, NS, CS, NP, 5>(p, sm, seq_tok, row_wg, nch, lane); break;
+                case 6: producer_loop_impl<T, D, NS, CS, NP, 6>(p, sm, seq_tok, row_wg, nch, lane); break;
+                default: producer_loop_impl<T, D, NS, CS, NP, 7>(p, sm, seq_tok, row_wg, nch, lane); break;
+            }
         }
     }
 }
