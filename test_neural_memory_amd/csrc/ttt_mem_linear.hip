@@ -244,9 +244,10 @@ struct Geo {
     static constexpr int QUL = cdiv(NQU, NPW * kWave);
     static constexpr int VUL = cdiv(NVU, kWave);
     static constexpr int BUF_BYTES = (2 * NP * LQ + NP * LP + 2 * NP) * (int)sizeof(T) +
-                                     (F16 ? NP * LV * 2 : (DS * LKT + RB * LV) * 4) + (2 * NP + 4) * 4;
+                                     (F16 ? NP * LV * 2 : (DS * LKT + RB * LV) * 4);
     static constexpr int XCH_BYTES = CS > 1 ? NS * (2 * NKC * kWave * 16 + NT * kWave * 8) : 0;
-    static constexpr int HELP_BYTES = (2 * NT * kGB + NT * NP * 3 + 2 * NP) * 4 + XCH_BYTES;
+    static constexpr int GATE_BYTES = 2 * (2 * NT * kGB + NT * NP * 3 + 2 * NP) * 4 + 4 * (2 * NP + 4) * 4;
+    static constexpr int HELP_BYTES = GATE_BYTES + XCH_BYTES;
     static constexpr int NBUF = (2 * BUF_BYTES + HELP_BYTES + 1024 <= kLdsBytes) ? 2 : 1;
     static_assert(NP % KG == 0, "chunk padding must fill whole k-groups");
     static_assert(D % RB == 0, "row blocks must tile d");
@@ -268,18 +269,27 @@ struct Smem {
         alignas(16) uint16_t vb[F16 ? NP * Gm::LV : 1];
         alignas(16) float kt[F16 ? 1 : D * Gm::LKT];
         alignas(16) float vn[F16 ? 1 : Gm::RB * Gm::LV];
-        alignas(16) float av[NP];          // A_i
-        alignas(16) float cv[NP];          // c_i
-        alignas(16) float scal[4];         // A_n, c_n, E_n
     };
     Buf buf[Gm::NBUF];
-    // theta_j gamma_ij and theta_j p_ij on the diagonal 16-blocks, [blk][i][j]
-    // with padded rows (kGR floats) and blocks (kGB floats): bank-conflict free.
-    alignas(16) float gamd[Gm::NT * kGB];
-    alignas(16) float gampd[Gm::NT * kGB];
-    alignas(16) float phi[Gm::NT * NP * 3];  // maps from the end of block q to row i [q][i][X,Y,W]
-    alignas(16) float gend[NP];              // theta_j gamma at the end of column j's block
-    alignas(16) float pend[NP];              // theta_j p at the end of column j's block
+    // Decay-matrix quantities of one chunk (producers only), double-buffered
+    // by chunk parity: the gate waves run two chunks ahead of the state waves.
+    struct GateSlot {
+        // theta_j gamma_ij and theta_j p_ij on the diagonal 16-blocks, [blk][i][j]
+        // with padded rows (kGR floats) and blocks (kGB floats): bank-conflict free.
+        alignas(16) float gamd[Gm::NT * kGB];
+        alignas(16) float gampd[Gm::NT * kGB];
+        alignas(16) float phi[Gm::NT * NP * 3];  // maps from the end of block q to row i [q][i][X,Y,W]
+        alignas(16) float gend[NP];              // theta_j gamma at the end of column j's block
+        alignas(16) float pend[NP];              // theta_j p at the end of column j's block
+    };
+    GateSlot gs[2];
+    // Gate quantities the state waves read, a ring over four chunks.
+    struct ReadGates {
+        alignas(16) float av[NP];    // A_i
+        alignas(16) float cv[NP];    // c_i
+        alignas(16) float scal[4];   // A_n, c_n, E_n
+    };
+    ReadGates rg[4];
     // Column-split exchange between the state waves of one row tile: fp16
     // fragments of M0, S0 per key k-group, and fp16 residual tiles per token tile.
     alignas(16) f16x8 xm[CS > 1 ? NS * Gm::NKC * kWave : 1];
@@ -295,6 +305,8 @@ struct Kernel {
     using F = typename O::frag;
     using S = Smem<T, D, NS, CS, NP>;
     using Buf = typename S::Buf;
+    using GateSlot = typename S::GateSlot;
+    using ReadGates = typename S::ReadGates;
     static constexpr bool F16 = Gm::F16;
     static constexpr int NT = Gm::NT, NC = Gm::NC, KG = Gm::KG, NKC = Gm::NKC, NKT = Gm::NKT, DS = Gm::DS;
     static constexpr int LQ = Gm::LQ, LP = Gm::LP, LKT = Gm::LKT, LV = Gm::LV, CB = Gm::CB, RB = Gm::RB;
@@ -471,7 +483,7 @@ struct Kernel {
     }
 
     // Producer wave 0: gate scan (A, c, E) and the block maps of the decay matrix.
-    __device__ static void gate_scan(const Prefetch& pf, S& sm, Buf& B, int n, int lane) {
+    __device__ static void gate_scan(const Prefetch& pf, GateSlot& gs, ReadGates& rg, int n, int lane) {
         const int l = lane;
         const float et = l < n ? pf.et : 1.f, a = 1.f - pf.al;
         // Inclusive prefix of T_l within 16-lane rows: Psi_l = T_l ... T_{16*(l/16)}.
@@ -484,8 +496,8 @@ struct Kernel {
         // Extend to the whole wave: T_l ... T_0 = [[A_l, c_l], [0, E_l]].
         tri_step<kRowBcast15, 0xa>(X, Y, W);
         tri_step<kRowBcast31, 0xc>(X, Y, W);
-        if (l < NP) { B.av[l] = X; B.cv[l] = Y; }
-        if (l == n - 1) { B.scal[0] = X; B.scal[1] = Y; B.scal[2] = W; }
+        if (l < NP) { rg.av[l] = X; rg.cv[l] = Y; }
+        if (l == n - 1) { rg.scal[0] = X; rg.scal[1] = Y; rg.scal[2] = W; }
         // Maps from the end of block q to row l, for every block q below l's block.
         float BX[NT], BY[NT], BW[NT];
 #pragma unroll
@@ -500,7 +512,7 @@ struct Kernel {
 #pragma unroll
             for (int q = NT - 2; q >= 0; --q) {
                 if (q < pb) {
-                    float* dst = sm.phi + (q * NP + l) * 3;
+                    float* dst = gs.phi + (q * NP + l) * 3;
                     dst[0] = cx; dst[1] = cy; dst[2] = cw;
                     const float ny = cx * BY[q] + cy * BW[q];
                     cx *= BX[q];
@@ -516,7 +528,7 @@ struct Kernel {
     // the same 16-lane row.  The column state starts at (gamma, p) = (1, 1) on
     // its own row: p <- eta_i p + [i == j], gamma <- a_i gamma + p, which is
     // zero above the diagonal.
-    __device__ static void gate_diag(const Prefetch& pf, S& sm, int n, int lane) {
+    __device__ static void gate_diag(const Prefetch& pf, GateSlot& gs, int n, int lane) {
         const int l = lane;
         const float th = pf.th, et = l < n ? pf.et : 1.f, a = 1.f - pf.al;
         const int qb = l >> 4, jj = l & 15;
@@ -538,8 +550,8 @@ struct Kernel {
         ai[14] = row_bcast<14>(a); ei[14] = row_bcast<14>(et);
         ai[15] = row_bcast<15>(a); ei[15] = row_bcast<15>(et);
         if (qb < NT) {
-            float* gd = sm.gamd + qb * kGB + jj;
-            float* gpd = sm.gampd + qb * kGB + jj;
+            float* gd = gs.gamd + qb * kGB + jj;
+            float* gpd = gs.gampd + qb * kGB + jj;
             float pp = 0.f, gg = 0.f;
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
@@ -548,8 +560,8 @@ struct Kernel {
                 gd[s * kGR] = th * gg;
                 gpd[s * kGR] = th * pp;
             }
-            sm.gend[l] = th * gg;
-            sm.pend[l] = th * pp;
+            gs.gend[l] = th * gg;
+            gs.pend[l] = th * pp;
         }
     }
 
@@ -559,7 +571,7 @@ struct Kernel {
     // mix diagonal, below-diagonal and above-diagonal blocks, and branches
     // around the loads would serialise their LDS latencies.
     template <bool PE>
-    __device__ static void decay4(const S& sm, int i, int jb, f32x4& L, f32x4& LPe) {
+    __device__ static void decay4(const GateSlot& sm, int i, int jb, f32x4& L, f32x4& LPe) {
         const int bi = i >> 4, bj = jb >> 4;
         f32x4 ld = *reinterpret_cast<const f32x4*>(sm.gamd + bi * kGB + (i & 15) * kGR + (jb & 15));
         f32x4 gv = *reinterpret_cast<const f32x4*>(sm.gend + jb);
@@ -589,7 +601,7 @@ struct Kernel {
     // and column block (rbk, cbk) = kTiles[PW] (blocks of TPB tiles), so the q
     // and k fragments of a block are read once for all its tiles.
     template <int PW>
-    __device__ static void ptiles(const S& sm, Buf& B, int lr, int lg) {
+    __device__ static void ptiles(const GateSlot& sm, Buf& B, int lr, int lg) {
         constexpr int NB = NT / TPB;   // k-groups (tile blocks) per chunk
         // Lower-triangular (rbk, cbk) block pairs in order; row tile hp of a
         // pair belongs to producer unit_owner(pair, hp).
@@ -635,7 +647,7 @@ struct Kernel {
         }
     }
     // Chunk-end weights w^M_j = -theta_j gamma_{n-1,j}, w^S_j = -theta_j p_{n-1,j}; lane = 4 tokens.
-    __device__ static void wrow(const S& sm, Buf& B, int n, int lane) {
+    __device__ static void wrow(const GateSlot& sm, Buf& B, int n, int lane) {
         if (lane < NP / 4) {
             f32x4 L, LPe;
             decay4<true>(sm, n - 1, 4 * lane, L, LPe);
@@ -689,7 +701,8 @@ struct Kernel {
     // Phase A: residuals E and readouts (A.M0 q + c.S0 q) of the own token
     // tiles.  MB/SB hold the fp16 fragments of M0, S0 for the own key
     // k-groups; MP/SP receive the partner's from the exchange.
-    __device__ static void phaseA(const StateCtx& x, const Buf& B, S& sm, const F* MB, const F* SB, f32x4* E,
+    __device__ static void phaseA(const StateCtx& x, const Buf& B, const ReadGates& rg, S& sm, const F* MB,
+                                  const F* SB, f32x4* E,
                                   f32x4* Zp) {
         F MP[NKCW], SP[NKCW];
         const int pchi = x.chi ^ 1;
@@ -725,7 +738,7 @@ struct Kernel {
                     zc = O::mma(zc, SP[sw], bq);
                 }
             }
-            Zp[tw] = B.av[t] * za + B.cv[t] * zc;
+            Zp[tw] = rg.av[t] * za + rg.cv[t] * zc;
         }
         if constexpr (CS > 1) {
 #pragma unroll
@@ -738,7 +751,8 @@ struct Kernel {
 
     // Phase B: intra-chunk term and store of z for the own token tiles, then
     // the update of the own columns of M and S.
-    __device__ static void phaseB(const StateCtx& x, const Buf& B, S& sm, f32x4* Macc, f32x4* Sacc, F* MB, F* SB,
+    __device__ static void phaseB(const StateCtx& x, const Buf& B, const ReadGates& rg, S& sm, f32x4* Macc,
+                                  f32x4* Sacc, F* MB, F* SB,
                                   const f32x4* E, f32x4* Zp, __amdgpu_buffer_rsrc_t rz, uint32_t zcol) {
         // (MB, SB: the own key k-groups, refreshed from the updated state at the end.)
         F EB[NKT];
@@ -768,7 +782,7 @@ struct Kernel {
             WMB[s] = EB[s] * frag_w(B.wm, s, x.lg);
             WSB[s] = EB[s] * frag_w(B.ws, s, x.lg);
         }
-        const float An = B.scal[0], Cn = B.scal[1], En = B.scal[2];
+        const float An = rg.scal[0], Cn = rg.scal[1], En = rg.scal[2];
 #pragma unroll
         for (int cw = 0; cw < NCW; ++cw) {
             const int ct = x.chi * NCW + cw;
@@ -812,47 +826,59 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
     const G* __restrict__ gq = static_cast<const G*>(p.q);
     const G* __restrict__ gk = static_cast<const G*>(p.k);
     const G* __restrict__ gv = static_cast<const G*>(p.v);
-    auto prepare = [&](int c, typename K::Buf& B, const typename K::Prefetch& pf) {   // stage chunk c, gates
+    auto prepare = [&](typename K::Buf& B, const typename K::Prefetch& pf) {   // stage a chunk
         K::template stage<PW>(pf, B, lane);
-        if constexpr (PW == 0) K::gate_scan(pf, sm, B, chunk_n(c), lane);
-        if constexpr (PW == 1) K::gate_diag(pf, sm, chunk_n(c), lane);
     };
-    auto finish = [&](int c, typename K::Buf& B) {    // P tiles and chunk-end weights
-        K::template ptiles<PW>(sm, B, lr, lg);
-        if constexpr (PW == K::kWrowWave) K::wrow(sm, B, chunk_n(c), lane);
+    auto gates = [&](int c, const typename K::Prefetch& pf) {   // gate quantities of chunk c
+        if constexpr (PW == 0) K::gate_scan(pf, sm.gs[c & 1], sm.rg[c & 3], chunk_n(c), lane);
+        if constexpr (PW == 1) K::gate_diag(pf, sm.gs[c & 1], chunk_n(c), lane);
+    };
+    auto finish = [&](int c, typename K::Buf& B) {    // P tiles and chunk-end weights of chunk c
+        K::template ptiles<PW>(sm.gs[c & 1], B, lr, lg);
+        if constexpr (PW == K::kWrowWave) K::wrow(sm.gs[c & 1], B, chunk_n(c), lane);
     };
     auto issue = [&](int c, typename K::Prefetch& pf) {
         K::template issue<PW>(pf, p, gq, gk, gv, seq_tok, row_wg, c, lane);
     };
     if constexpr (Gm::NBUF == 2) {
-        // Two register sets of prefetched chunks: the loads of chunk c + 3 are
-        // issued while chunk c + 1 is staged, two chunk periods before use.
+        // Two register sets of prefetched chunks (even and odd chunks): the
+        // loads of chunk c + 3 are issued while chunk c + 1 is staged, two
+        // chunk periods before use.  The gate quantities run one chunk further
+        // ahead, in the second phase, so that the serial gate work never sits
+        // between the staging of a chunk and its P tiles.
         typename K::Prefetch pf0, pf1;
         issue(0, pf0);
         issue(1, pf1);
-        if (nch > 0) prepare(0, sm.buf[0], pf0);
+        if (nch > 0) {
+            prepare(sm.buf[0], pf0);
+            gates(0, pf0);
+        }
         issue(2, pf0);
         __syncthreads();
         if (nch > 0) finish(0, sm.buf[0]);
+        if (nch > 1) gates(1, pf1);
         __syncthreads();
-        // Step c stages chunk c + 1 (held in pf) into buffer (c + 1) & 1 while
-        // the state waves consume chunk c, then builds its P tiles.
-        auto step = [&](int c, typename K::Prefetch& pf, typename K::Buf& B) {
-            if (c + 1 < nch) prepare(c + 1, B, pf);
-            issue(c + 3, pf);
+        // Step c (the state waves consume chunk c): stage chunk c + 1 from cur
+        // into B, then build its P tiles and the gate quantities of chunk
+        // c + 2 (held in nxt).
+        auto step = [&](int c, typename K::Prefetch& cur, const typename K::Prefetch& nxt, typename K::Buf& B) {
+            if (c + 1 < nch) prepare(B, cur);
+            issue(c + 3, cur);
             __syncthreads();
             if (c + 1 < nch) finish(c + 1, B);
+            if (c + 2 < nch) gates(c + 2, nxt);
             __syncthreads();
         };
         for (int c = 0; c < nch; c += 2) {
-            step(c, pf1, sm.buf[1]);
-            if (c + 1 < nch) step(c + 1, pf0, sm.buf[0]);
+            step(c, pf1, pf0, sm.buf[1]);
+            if (c + 1 < nch) step(c + 1, pf0, pf1, sm.buf[0]);
         }
     } else {
         typename K::Prefetch pf;
         for (int c = 0; c < nch; ++c) {
             issue(c, pf);
-            prepare(c, sm.buf[0], pf);
+            prepare(sm.buf[0], pf);
+            gates(c, pf);
             __syncthreads();
             finish(c, sm.buf[0]);
             __syncthreads();
@@ -934,9 +960,10 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
             auto chunk = [&](int c, const typename K::Buf& B) {
                 const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
                                           static_cast<uint32_t>(chunk_n(c)) * D * 4);
-                K::phaseA(x, B, sm, MB, SB, E, Zp);
+                const typename K::ReadGates& rg = sm.rg[c & 3];
+                K::phaseA(x, B, rg, sm, MB, SB, E, Zp);
                 __syncthreads();
-                K::phaseB(x, B, sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
+                K::phaseB(x, B, rg, sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
                 __syncthreads();
             };
             for (int c = 0; c < nch; c += 2) {
@@ -949,9 +976,9 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
                 __syncthreads();   // chunk c P tiles
                 const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
                                           static_cast<uint32_t>(chunk_n(c)) * D * 4);
-                K::phaseA(x, sm.buf[0], sm, MB, SB, E, Zp);
+                K::phaseA(x, sm.buf[0], sm.rg[c & 3], sm, MB, SB, E, Zp);
                 __syncthreads();
-                K::phaseB(x, sm.buf[0], sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
+                K::phaseB(x, sm.buf[0], sm.rg[c & 3], sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
                 __syncthreads();   // chunk c consumed
             }
         }
