@@ -36,6 +36,29 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const void* p) {
         (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(p)));
 }
 
+// LDS by 32-bit byte address.  lds_addr gives the address of a pointer into
+// __shared__ memory; opaque() hides a value from the optimizer so that a base
+// address computed once stays in one register and every access adds a
+// compile-time offset (folded into the instruction's 16-bit offset field).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+template <typename V>
+__device__ __forceinline__ V lds_load(uint32_t a) {
+    return *(const __attribute__((address_space(3))) V*)(static_cast<uintptr_t>(a));
+}
+template <typename V>
+__device__ __forceinline__ void lds_store(uint32_t a, V v) {
+    *(__attribute__((address_space(3))) V*)(static_cast<uintptr_t>(a)) = v;
+}
+__device__ __forceinline__ i16x4 ds_read_tr16_at(uint32_t a) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(static_cast<uintptr_t>(a)));
+}
+
 // Raw buffer descriptor over nbytes at ptr: accesses at or past nbytes read 0
 // and are not written, which bounds ragged chunks without branches.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* ptr, uint32_t nbytes) {

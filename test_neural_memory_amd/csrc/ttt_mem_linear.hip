@@ -126,6 +126,15 @@ __device__ __forceinline__ int swz_p(int t) {
 }
 
 
+// Dense decay matrix rows (NP floats = NP/4 16-byte chunks): the read of a
+// P-tile lane (row i = tmap(pb, lr), four columns from tmap(qb, 4 lg)) and
+// the build's row-block writes are conflict-free for 16-chunk rows.
+template <int NP>
+__device__ __forceinline__ int gam_swz(int i) {
+    const int sw = (i & 0xb) | ((((i >> 1) ^ (i >> 2)) & 1) << 2);
+    return sw & (NP / 4 - 1);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA operand traits.  A "k-group" is the contraction length of one operand
 // fragment: 16 for float32 (four v_mfma_f32_16x16x4_f32, one slot each) and 32
@@ -249,6 +258,9 @@ struct Geo {
     static constexpr int GATE_BYTES = 2 * (2 * NT * kGB + NT * NP * 3 + 2 * NP) * 4 + 4 * (2 * NP + 4) * 4;
     static constexpr int HELP_BYTES = GATE_BYTES + XCH_BYTES;
     static constexpr int NBUF = (2 * BUF_BYTES + HELP_BYTES + 1024 <= kLdsBytes) ? 2 : 1;
+    // The dense decay matrix theta_j gamma_ij of one chunk, when it fits.
+    static constexpr int GAM_BYTES = NP * NP * 4;
+    static constexpr bool USE_GAM = NBUF * BUF_BYTES + HELP_BYTES + GAM_BYTES + 1024 <= kLdsBytes;
     static_assert(NP % KG == 0, "chunk padding must fill whole k-groups");
     static_assert(D % RB == 0, "row blocks must tile d");
     static_assert(CS == 1 || (F16 && NKC % CS == 0 && NT % CS == 0), "column split needs whole k-groups");
@@ -290,6 +302,10 @@ struct Smem {
         alignas(16) float scal[4];   // A_n, c_n, E_n
     };
     ReadGates rg[4];
+    // Dense decay matrix of the chunk whose P tiles are being built: row i
+    // (token) holds theta_j gamma_ij for every j, 16-byte chunks XOR-swizzled
+    // by gam_swz(i); blocks above the diagonal stay zero.
+    alignas(16) float gam[Gm::USE_GAM ? NP * NP : 4];
     // Column-split exchange between the state waves of one row tile: fp16
     // fragments of M0, S0 per key k-group, and fp16 residual tiles per token tile.
     alignas(16) f16x8 xm[CS > 1 ? NS * Gm::NKC * kWave : 1];
@@ -352,23 +368,28 @@ struct Kernel {
     // work and P tiles, all known at compile time.
     static constexpr int WU = cdiv(Gm::NQU, kWave);   // q (or k) units per chunk in 64-lane rounds
     // q/k rounds of producer PW.  With eight producers the gate waves 0 and 1
-    // take WU/16 rounds each and waves 2..7 split the rest evenly; with two,
-    // the rounds are halved.
+    // stage nothing (they build the decay matrix and the chunk-end weights
+    // meanwhile) and waves 2..7 split the rounds, the larger shares first;
+    // with two, the rounds are halved.
     static constexpr int rounds(int pw) {
-        if (NPW == 8) {
-            const int g = WU / 16;
-            if (pw < 2) return g;
-            const int rest = WU - 2 * g;
-            return rest / 6 + (pw - 2 < rest % 6 ? 1 : 0);
-        }
+        if (NPW == 8) return pw < 2 ? 0 : WU / 6 + (pw - 2 < WU % 6 ? 1 : 0);
         return pw == 0 ? WU / 2 : WU - WU / 2;
     }
     static constexpr int first_round(int pw) { return pw == 0 ? 0 : first_round(pw - 1) + rounds(pw - 1); }
+    // v rows: with eight producers split between waves 6 and 7 (which take
+    // the smaller q/k shares); with two, on wave 1.
+    static constexpr int vrounds(int pw) {
+        if (NPW == 8) return pw == 6 ? Gm::VUL / 2 : pw == 7 ? Gm::VUL - Gm::VUL / 2 : 0;
+        return pw == NPW - 1 ? Gm::VUL : 0;
+    }
+    static constexpr int vfirst_of(int pw) { return pw == 0 ? 0 : vfirst_of(pw - 1) + vrounds(pw - 1); }
     template <int PW>
     struct Share {
         static constexpr int first = first_round(PW);
         static constexpr int count = rounds(PW);
-        static constexpr bool has_v = PW == NPW - 1;
+        static constexpr int vfirst = vfirst_of(PW);
+        static constexpr int vcount = vrounds(PW);
+        static constexpr bool has_v = vcount > 0;
     };
     // P tiles: with eight producers, the row tiles of each lower-triangular
     // tile-block pair (one row tile against the pair's column block) are dealt
@@ -376,6 +397,10 @@ struct Kernel {
     // pairs are dealt round-robin and the weights go to the last wave.
     static constexpr int NPAIR = (NT / TPB) * (NT / TPB + 1) / 2;
     static constexpr int kWrowWave = NPW == 8 ? 0 : ((NPAIR % NPW) == 0 ? NPW - 1 : NPAIR % NPW);
+    // Decay-matrix blocks of the two gate waves: the blocks below the
+    // diagonal alternate, the diagonal copies go to wave 1 (wave 0 also
+    // builds the chunk-end weights).
+    static constexpr int gam_owner(int bi, int bj, int idx) { return bi == bj ? 1 : (idx & 1); }
     static constexpr int unit_owner(int pair, int hp) {
         return NPW == 8 ? 2 + (pair * TPB + hp) % (NPW - 2) : pair % NPW;
     }
@@ -414,8 +439,8 @@ struct Kernel {
         if constexpr (Sh::has_v) {
             const auto rv = make_rsrc(gv + chunk_off, nbytes);
 #pragma unroll
-            for (int kk = 0; kk < Gm::VUL; ++kk) {
-                const int u = lane + kWave * kk;
+            for (int kk = 0; kk < Sh::vcount; ++kk) {
+                const int u = lane + kWave * (Sh::vfirst + kk);
                 const int t = u / (RB / CB), rb = u % (RB / CB);
                 pf.v[kk] = buf_load16(rv, (static_cast<uint32_t>(t) * D + row_wg + rb * CB) * sizeof(G));
             }
@@ -464,10 +489,10 @@ struct Kernel {
                 }
             }
         }
-        if constexpr (Share<PW>::has_v) {
+        if constexpr (Sh::has_v) {
 #pragma unroll
-            for (int kk = 0; kk < Gm::VUL; ++kk) {
-                const int u = lane + kWave * kk;
+            for (int kk = 0; kk < Sh::vcount; ++kk) {
+                const int u = lane + kWave * (Sh::vfirst + kk);
                 if ((Gm::NVU % kWave) == 0 || u < Gm::NVU) {
                     const int t = u / (RB / CB), rb = u % (RB / CB);
                     if constexpr (F16) {
@@ -595,13 +620,44 @@ struct Kernel {
         }
     }
 
+    // Dense decay matrix from the gate data of one chunk, split over the two
+    // gate waves by gam_owner (16x16 blocks on and below the diagonal).
+    // Lane (r, c4) writes row 16 bi + r, columns 16 bj + 4 c4 .. + 3: on the
+    // diagonal the block recurrence's values, below it the map from the end
+    // of block bj to row i applied to the column states at that block end.
+    template <int HALF>
+    __device__ static void gamma_build(const GateSlot& gs, float* gam, int lane) {
+        const int r = lane & 15, c4 = lane >> 4;
+        int idx = 0;
+#pragma unroll
+        for (int bi = 0; bi < NT; ++bi) {
+#pragma unroll
+            for (int bj = 0; bj < bi; ++bj, ++idx) {
+                if (gam_owner(bi, bj, idx) != HALF) continue;
+                const int i = 16 * bi + r, j = 16 * bj + 4 * c4;
+                const float* ph = gs.phi + (bj * NP + i) * 3;
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(gs.gend + j);
+                const f32x4 pv = *reinterpret_cast<const f32x4*>(gs.pend + j);
+                const f32x4 g = ph[0] * gv + ph[1] * pv;
+                *reinterpret_cast<f32x4*>(gam + i * NP + 4 * ((j >> 2) ^ gam_swz<NP>(i))) = g;
+            }
+        }
+#pragma unroll
+        for (int bi = 0; bi < NT; ++bi) {
+            if (gam_owner(bi, bi, 0) != HALF) continue;
+            const int i = 16 * bi + r, j = 16 * bi + 4 * c4;
+            const f32x4 g = *reinterpret_cast<const f32x4*>(gs.gamd + bi * kGB + r * kGR + 4 * c4);
+            *reinterpret_cast<f32x4*>(gam + i * NP + 4 * ((j >> 2) ^ gam_swz<NP>(i))) = g;
+        }
+    }
+
     // Producers: P tiles.  Tile (pb, qb) holds rows i = tmap(pb, .) and
     // columns j = tmap(qb, .); only tiles whose column k-group is not after the
     // row's k-group are ever read.  Producer PW takes the tiles of row block
     // and column block (rbk, cbk) = kTiles[PW] (blocks of TPB tiles), so the q
     // and k fragments of a block are read once for all its tiles.
     template <int PW>
-    __device__ static void ptiles(const GateSlot& sm, Buf& B, int lr, int lg) {
+    __device__ static void ptiles(const GateSlot& sm, const float* gam, Buf& B, int lr, int lg) {
         constexpr int NB = NT / TPB;   // k-groups (tile blocks) per chunk
         // Lower-triangular (rbk, cbk) block pairs in order; row tile hp of a
         // pair belongs to producer unit_owner(pair, hp).
@@ -636,7 +692,11 @@ struct Kernel {
                         for (int s = 0; s < NKC; ++s) acc = O::mma(acc, kf[hq][s], qf[s]);
                         const int jb = O::tmap(qb, 4 * lg);   // acc[e] = q_i . k_{jb+e}
                         f32x4 L, LPe;
-                        decay4<false>(sm, i, jb, L, LPe);
+                        if constexpr (Gm::USE_GAM) {
+                            L = *reinterpret_cast<const f32x4*>(gam + i * NP + 4 * ((jb >> 2) ^ gam_swz<NP>(i)));
+                        } else {
+                            decay4<false>(sm, i, jb, L, LPe);
+                        }
                         pv[hq] = -(acc * L);
                     }
                     // The TPB column tiles of a block hold consecutive token columns.
@@ -798,6 +858,210 @@ struct Kernel {
         own_frags(x, sm, Macc, Sacc, MB, SB);
     }
 
+    // ---- column-split state waves (fp16): software-pipelined phases --------
+    // Every LDS operand stream of a state wave has one per-lane base address,
+    // computed once (buffer 0, the wave's first own token tile) and hidden
+    // from the optimizer; each access adds a compile-time offset for the
+    // buffer, the token tile, the k-group or the array.  The phases issue the
+    // loads of the next k-group (column tile) before the products of the
+    // current one, so LDS latency overlaps the matrix cores instead of
+    // sitting between each load and its product.
+    struct Lanes {
+        uint32_t qk[NKC];              // q fragments, k-groups in processing order (own first)
+        uint32_t kt[cmax(NCW / 2, 1)]; // transposed k reads, per pair of own column tiles
+        uint32_t v;                    // transposed v reads
+        uint32_t p[NKT];               // P fragments per token k-group
+        uint32_t w;                    // w^M fragments (w^S at a fixed offset)
+        uint32_t xp, xo;               // partner's / own M0 fragments in the exchange (S0 at a fixed offset)
+        uint32_t xe, xeo;              // residual tiles: all of the row tile / own
+        uint32_t g;                    // A_i of the wave's first token in gate slot 0 (c_i at a fixed offset)
+    };
+    static constexpr int rowoff(int tw) { return 32 * (tw >> 1) + 4 * (tw & 1); }
+    static constexpr uint32_t kBufB = sizeof(Buf);
+    static constexpr uint32_t kOffQ = offsetof(Buf, q), kOffK = offsetof(Buf, k), kOffP = offsetof(Buf, p);
+    static constexpr uint32_t kOffWM = offsetof(Buf, wm), kOffWS = offsetof(Buf, ws), kOffV = offsetof(Buf, vb);
+    static constexpr uint32_t kOffXS = offsetof(S, xs) - offsetof(S, xm);
+    static constexpr uint32_t kGateB = sizeof(ReadGates);
+    static constexpr uint32_t kOffCV = offsetof(ReadGates, cv) - offsetof(ReadGates, av);
+
+    __device__ static Lanes lanes(const StateCtx& x, S& sm) {
+        static_assert(F16 && CS == 2 && NTW <= 2 && NCW % 2 == 0 && NCHQ >= 8, "pipelined phases: fp16 column split");
+        static_assert(kBufB + kOffK + 2 * 4 * LQ < 65536 && kBufB + 8 + 2 * (32 * (NKT - 1) + 4) * LQ < 65536,
+                      "LDS offsets must fit 16 bits");
+        static_assert(kBufB + kOffWS - kOffWM + 64 * NKT < 65536 && kBufB + 8 * LP < 65536, "LDS offsets");
+        Lanes a;
+        const int pchi = x.chi ^ 1;
+        const int t = O::tmap(x.chi * NTW, x.lr);   // token of the wave's first own tile, row lr
+        const uint32_t b0 = lds_addr(&sm.buf[0]);
+#pragma unroll
+        for (int j = 0; j < NKC; ++j) {
+            const int s = j < NKCW ? x.chi * NKCW + j : pchi * NKCW + (j - NKCW);
+            a.qk[j] = opaque(b0 + 2 * (t * LQ + 8 * ((4 * s + x.lg) ^ swz_qk<NCHQ>(t))));
+        }
+        const int tk = 8 * x.lg + (x.lr >> 2);
+#pragma unroll
+        for (int h = 0; h < NCW / 2; ++h) {
+            const int ch = 4 * ((x.chi * NCW) / 2 + h) + (x.lr & 3);
+            a.kt[h] = opaque(b0 + kOffK + 2 * (tk * LQ + 8 * (ch ^ swz_qk<NCHQ>(tk))));
+        }
+        const int tv = O::tmap(x.chi * NTW, 4 * x.lg + (x.lr >> 2));
+        a.v = opaque(b0 + kOffV + 2 * (tv * LV + x.r0 + 4 * (x.lr & 3)));
+#pragma unroll
+        for (int s2 = 0; s2 < NKT; ++s2)
+            a.p[s2] = opaque(b0 + kOffP + 2 * (t * LP + 8 * ((4 * s2 + x.lg) ^ swz_p<NCHP>(t))));
+        a.w = opaque(b0 + kOffWM + 16 * x.lg);
+        a.xp = opaque(lds_addr(&sm.xm[(x.rho * NKC + pchi * NKCW) * kWave + x.lr + 16 * x.lg]));
+        a.xo = opaque(lds_addr(&sm.xm[(x.rho * NKC + x.chi * NKCW) * kWave + x.lr + 16 * x.lg]));
+        a.xe = opaque(lds_addr(&sm.xe[x.rho * NT * kWave + x.lr + 16 * x.lg]));
+        a.xeo = opaque(lds_addr(&sm.xe[(x.rho * NT + x.chi * NTW) * kWave + x.lr + 16 * x.lg]));
+        a.g = opaque(lds_addr(&sm.rg[0].av[t]));
+        return a;
+    }
+
+    // Phase A (pipelined): E = K M0^T - V and Z = A.(M0 Q^T) + c.(S0 Q^T) for
+    // the own token tiles over all key k-groups (own fragments from registers,
+    // the partner's from the exchange); the residual tiles go to the exchange.
+    template <int BI>
+    __device__ static void phaseA2(const Lanes& a, uint32_t gs, const F* MB, const F* SB, f32x4* E, f32x4* Zp) {
+        constexpr uint32_t BO = BI * kBufB;
+        F kf[2][NTW], qf[2][NTW], MP[NKCW], SP[NKCW];
+        i16x4 vr[NTW];
+        float av[NTW], cv[NTW];
+        auto load = [&](int j, int slot) {
+#pragma unroll
+            for (int tw = 0; tw < NTW; ++tw) {
+                kf[slot][tw] = lds_load<F>(a.qk[j] + BO + kOffK + 2 * rowoff(tw) * LQ);
+                qf[slot][tw] = lds_load<F>(a.qk[j] + BO + kOffQ + 2 * rowoff(tw) * LQ);
+            }
+        };
+#pragma unroll
+        for (int tw = 0; tw < NTW; ++tw) vr[tw] = ds_read_tr16_at(a.v + BO + 2 * rowoff(tw) * LV);
+        load(0, 0);
+#pragma unroll
+        for (int sw = 0; sw < NKCW; ++sw) {
+            MP[sw] = lds_load<F>(a.xp + 16 * kWave * sw);
+            SP[sw] = lds_load<F>(a.xp + kOffXS + 16 * kWave * sw);
+        }
+#pragma unroll
+        for (int tw = 0; tw < NTW; ++tw) {
+            av[tw] = lds_load<float>(gs + 4 * rowoff(tw));
+            cv[tw] = lds_load<float>(gs + kOffCV + 4 * rowoff(tw));
+        }
+        f32x4 za[NTW], zc[NTW];
+#pragma unroll
+        for (int j = 0; j < NKC; ++j) {
+            if (j + 1 < NKC) load(j + 1, (j + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j == 0) {
+#pragma unroll
+                for (int tw = 0; tw < NTW; ++tw) {
+                    const u32x2 u = __builtin_bit_cast(u32x2, vr[tw]);
+                    E[tw] = f32x4{-bf16lo(u[0]), -bf16hi(u[0]), -bf16lo(u[1]), -bf16hi(u[1])};
+                    za[tw] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    zc[tw] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            const F& Mj = j < NKCW ? MB[j] : MP[j - NKCW];
+            const F& Sj = j < NKCW ? SB[j] : SP[j - NKCW];
+#pragma unroll
+            for (int tw = 0; tw < NTW; ++tw) {
+                E[tw] = O::mma(E[tw], kf[j & 1][tw], Mj);
+                za[tw] = O::mma(za[tw], Mj, qf[j & 1][tw]);
+                zc[tw] = O::mma(zc[tw], Sj, qf[j & 1][tw]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int tw = 0; tw < NTW; ++tw) {
+            Zp[tw] = av[tw] * za[tw] + cv[tw] * zc[tw];
+            lds_store<f16x4>(a.xeo + 8 * kWave * tw, cvt4(E[tw]));
+        }
+    }
+
+    // Phase B (pipelined): decay of the state, the intra-chunk term and the
+    // store of z for the own token tiles, then the update of the own columns
+    // with the transposed k reads of the next column tile in flight.  The
+    // intra-chunk products run over every token k-group: the blocks of P
+    // above its diagonal are never written and stay zero.
+    template <int BI>
+    __device__ static void phaseB2(const Lanes& a, uint32_t gsc, f32x4* Macc, f32x4* Sacc, F* MB, F* SB, f32x4* Zp,
+                                   __amdgpu_buffer_rsrc_t rz, uint32_t zoff) {
+        constexpr uint32_t BO = BI * kBufB;
+        const f32x4 sc = lds_load<f32x4>(gsc);   // A_n, c_n, E_n (the same address in every lane)
+        f16x4 eb[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) eb[tt] = lds_load<f16x4>(a.xe + 8 * kWave * tt);
+        F pfr[NTW][NKT];
+#pragma unroll
+        for (int tw = 0; tw < NTW; ++tw)
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) pfr[tw][s] = lds_load<F>(a.p[s] + BO + 2 * rowoff(tw) * LP);
+        F wmf[NKT], wsf[NKT];
+#pragma unroll
+        for (int s = 0; s < NKT; ++s) {
+            wmf[s] = lds_load<F>(a.w + BO + 64 * s);
+            wsf[s] = lds_load<F>(a.w + BO + (kOffWS - kOffWM) + 64 * s);
+        }
+        F ktf[2][NKT];
+        auto load_kt = [&](int cw, int slot) {
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) {
+                const uint32_t b = a.kt[cw >> 1] + BO + 8 * (cw & 1) + 2 * 32 * s * LQ;
+                const i16x4 lo = ds_read_tr16_at(b);
+                const i16x4 hi = ds_read_tr16_at(b + 2 * 4 * LQ);
+                const f16x4 l4 = __builtin_bit_cast(f16x4, lo), h4 = __builtin_bit_cast(f16x4, hi);
+                ktf[slot][s] = F{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+            }
+        };
+        load_kt(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // State decay (the loads above are in flight).
+        const float An = sc[0], Cn = sc[1], En = sc[2];
+#pragma unroll
+        for (int cw = 0; cw < NCW; ++cw) {
+            Macc[cw] = An * Macc[cw] + Cn * Sacc[cw];
+            Sacc[cw] = En * Sacc[cw];
+        }
+        F EB[NKT];
+#pragma unroll
+        for (int s = 0; s < NKT; ++s) {
+            const f16x4 lo = eb[2 * s], hi = eb[2 * s + 1];
+            EB[s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int tw = 0; tw < NTW; ++tw) {
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) Zp[tw] = O::mma(Zp[tw], EB[s], pfr[tw][s]);
+        }
+        F WMB[NKT], WSB[NKT];
+#pragma unroll
+        for (int s = 0; s < NKT; ++s) {
+            WMB[s] = EB[s] * wmf[s];
+            WSB[s] = EB[s] * wsf[s];
+        }
+#pragma unroll
+        for (int tw = 0; tw < NTW; ++tw) buf_store16(Zp[tw], rz, zoff + 4 * rowoff(tw) * D);   // rows >= n dropped
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cw = 0; cw < NCW; ++cw) {
+            if (cw + 1 < NCW) load_kt(cw + 1, (cw + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) {
+                Macc[cw] = O::mma(Macc[cw], ktf[cw & 1][s], WMB[s]);
+                Sacc[cw] = O::mma(Sacc[cw], ktf[cw & 1][s], WSB[s]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int sw = 0; sw < NKCW; ++sw) {
+            MB[sw] = O::template from_acc<NCW>(Macc, sw);
+            SB[sw] = O::template from_acc<NCW>(Sacc, sw);
+            lds_store<F>(a.xo + 16 * kWave * sw, MB[sw]);
+            lds_store<F>(a.xo + kOffXS + 16 * kWave * sw, SB[sw]);
+        }
+    }
+
     // fp16 fragments of the own columns of M, S (and their copy for the partner).
     __device__ static void own_frags(const StateCtx& x, S& sm, const f32x4* Macc, const f32x4* Sacc, F* MB, F* SB) {
 #pragma unroll
@@ -821,6 +1085,9 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
     using K = Kernel<T, D, NS, CS, NP>;
     using G = typename Gm::G;
     const int lr = lane & 15, lg = lane >> 4;
+    // Issue priority: the serial gate work first, then the state waves, then
+    // the P tiles and staging (the state waves' priority is set in the kernel).
+    __builtin_amdgcn_s_setprio(PW < 2 ? 3 : 1);
     const int b = p.b;
     auto chunk_n = [&](int c) { return min(b, p.T - c * b); };
     const G* __restrict__ gq = static_cast<const G*>(p.q);
@@ -833,9 +1100,18 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
         if constexpr (PW == 0) K::gate_scan(pf, sm.gs[c & 1], sm.rg[c & 3], chunk_n(c), lane);
         if constexpr (PW == 1) K::gate_diag(pf, sm.gs[c & 1], chunk_n(c), lane);
     };
-    auto finish = [&](int c, typename K::Buf& B) {    // P tiles and chunk-end weights of chunk c
-        K::template ptiles<PW>(sm.gs[c & 1], B, lr, lg);
-        if constexpr (PW == K::kWrowWave) K::wrow(sm.gs[c & 1], B, chunk_n(c), lane);
+    // Decay matrix and chunk-end weights of chunk c (from its gate data),
+    // one phase before its P tiles.
+    auto build = [&](int c, typename K::Buf& B) {
+        if constexpr (Gm::USE_GAM) {
+            if constexpr (PW == 0) K::template gamma_build<0>(sm.gs[c & 1], sm.gam, lane);
+            if constexpr (PW == 1) K::template gamma_build<1>(sm.gs[c & 1], sm.gam, lane);
+            if constexpr (PW == K::kWrowWave) K::wrow(sm.gs[c & 1], B, chunk_n(c), lane);
+        }
+    };
+    auto finish = [&](int c, typename K::Buf& B) {    // P tiles of chunk c
+        K::template ptiles<PW>(sm.gs[c & 1], sm.gam, B, lr, lg);
+        if constexpr (!Gm::USE_GAM && PW == K::kWrowWave) K::wrow(sm.gs[c & 1], B, chunk_n(c), lane);
     };
     auto issue = [&](int c, typename K::Prefetch& pf) {
         K::template issue<PW>(pf, p, gq, gk, gv, seq_tok, row_wg, c, lane);
@@ -855,14 +1131,19 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
         }
         issue(2, pf0);
         __syncthreads();
-        if (nch > 0) finish(0, sm.buf[0]);
+        if (nch > 0) build(0, sm.buf[0]);
         if (nch > 1) gates(1, pf1);
         __syncthreads();
+        if (nch > 0) finish(0, sm.buf[0]);
+        __syncthreads();
         // Step c (the state waves consume chunk c): stage chunk c + 1 from cur
-        // into B, then build its P tiles and the gate quantities of chunk
-        // c + 2 (held in nxt).
+        // into B and build its decay matrix, then its P tiles and the gate
+        // quantities of chunk c + 2 (held in nxt).
         auto step = [&](int c, typename K::Prefetch& cur, const typename K::Prefetch& nxt, typename K::Buf& B) {
-            if (c + 1 < nch) prepare(B, cur);
+            if (c + 1 < nch) {
+                prepare(B, cur);
+                build(c + 1, B);
+            }
             issue(c + 3, cur);
             __syncthreads();
             if (c + 1 < nch) finish(c + 1, B);
@@ -879,6 +1160,8 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
             issue(c, pf);
             prepare(sm.buf[0], pf);
             gates(c, pf);
+            __syncthreads();
+            build(c, sm.buf[0]);
             __syncthreads();
             finish(c, sm.buf[0]);
             __syncthreads();
@@ -932,6 +1215,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
     if (w < NSW) {
         // ===================== state wave =====================
         typename K::StateCtx x;
+        __builtin_amdgcn_s_setprio(2);
         x.rho = w / CS;
         x.chi = w % CS;
         x.r0 = 16 * x.rho;           // first row within the workgroup block
@@ -952,8 +1236,38 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
         f32x4 E[Gm::NTW], Zp[Gm::NTW];
         K::own_frags(x, sm, Macc, Sacc, MB, SB);
         const uint32_t zcol = row + 4 * lg;
-        if constexpr (NBUF == 2) {
+        if constexpr (NBUF == 2 && Gm::F16 && CS == 2) {
             __syncthreads();   // chunk 0 staged
+            __syncthreads();   // chunk 0 decay matrix
+            __syncthreads();   // chunk 0 P tiles
+            const typename K::Lanes a = K::lanes(x, sm);
+            const uint32_t zoff = opaque((O::tmap(x.chi * Gm::NTW, lr) * D + zcol) * 4);
+            // Chunk c reads buffer c & 1 and gate slot c & 3.
+            for (int c = 0; c < nch; c += 2) {
+                {
+                    const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
+                                              static_cast<uint32_t>(chunk_n(c)) * D * 4);
+                    const uint32_t gs = a.g + static_cast<uint32_t>(c & 3) * K::kGateB;
+                    K::template phaseA2<0>(a, gs, MB, SB, E, Zp);
+                    __syncthreads();
+                    const uint32_t gsc = lds_addr(&sm.rg[c & 3].scal[0]);
+                    K::template phaseB2<0>(a, gsc, Macc, Sacc, MB, SB, Zp, rz, zoff);
+                    __syncthreads();
+                }
+                if (c + 1 < nch) {
+                    const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c + 1) * b) * D,
+                                              static_cast<uint32_t>(chunk_n(c + 1)) * D * 4);
+                    const uint32_t gs = a.g + static_cast<uint32_t>((c + 1) & 3) * K::kGateB;
+                    K::template phaseA2<1>(a, gs, MB, SB, E, Zp);
+                    __syncthreads();
+                    const uint32_t gsc = lds_addr(&sm.rg[(c + 1) & 3].scal[0]);
+                    K::template phaseB2<1>(a, gsc, Macc, Sacc, MB, SB, Zp, rz, zoff);
+                    __syncthreads();
+                }
+            }
+        } else if constexpr (NBUF == 2) {
+            __syncthreads();   // chunk 0 staged
+            __syncthreads();   // chunk 0 decay matrix
             __syncthreads();   // chunk 0 P tiles
             // Chunk c reads buffer c & 1; the loop is unrolled by two so that
             // every LDS address is a compile-time offset from lane constants.
@@ -973,6 +1287,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
         } else {
             for (int c = 0; c < nch; ++c) {
                 __syncthreads();   // chunk c staged
+                __syncthreads();   // chunk c decay matrix
                 __syncthreads();   // chunk c P tiles
                 const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
                                           static_cast<uint32_t>(chunk_n(c)) * D * 4);
