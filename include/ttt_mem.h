@@ -123,6 +123,34 @@ int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_
                              float* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T,
                              int B, int H, int T, int d, int hidden, int b, void* stream);
 
+/*
+ * Linear memory, token by token (the primal form), for generation: every
+ * token's gradient is taken at the memory the previous token left (chunks of
+ * one token; "5.1.1 · TTT layers 与 fast weights", section 1.1, the
+ * primal/dual comparison after eq. (9): prefill in the dual form, decode in
+ * the primal form).  The result equals ttt_mem_forward_* with b = 1; the
+ * intended use is T = 1 per call with the state carried in place
+ * (M_T == M0, S_T == S0) from one generated token to the next
+ * ("Continual Learning: From Attention to Neural Memory", section 4.3, the
+ * note on streaming inference).  All arithmetic is float32; the bf16 entry
+ * point widens q, k, v exactly.  Layouts, NULL states, aliasing and error
+ * behaviour as above; alignment: M0, S0, M_T, S_T 16 bytes, q and k 16 bytes
+ * (float32) or 8 bytes (bf16), v, z and the gates their element size.
+ * Sizes: d in {16, 32, 64, 128}.  The state is read once and written once
+ * per call; tokens are processed in order inside the call.
+ */
+int ttt_mem_decode_f32(const float* q, const float* k, const float* v,
+                       const float* theta, const float* eta, const float* alpha,
+                       const float* M0, const float* S0,
+                       float* z, float* M_T, float* S_T,
+                       int B, int H, int T, int d, void* stream);
+
+int ttt_mem_decode_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const float* theta, const float* eta, const float* alpha,
+                        const float* M0, const float* S0,
+                        float* z, float* M_T, float* S_T,
+                        int B, int H, int T, int d, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* ttt_mem_status_string(int status);
 

@@ -30,7 +30,7 @@ def _as_dev(t, name, dtype, shape, device):
     return t.contiguous()
 
 
-def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out):
+def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=True):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
     B, H, T, d = q.shape
@@ -58,9 +58,10 @@ def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out):
     lib = _lib.load()
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
+        sizes = (B, H, T, d, int(b)) if with_b else (B, H, T, d)
         status = getattr(lib, name)(
             _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(M0), _ptr(S0),
-            _ptr(z), _ptr(M_T), _ptr(S_T), B, H, T, d, int(b), stream)
+            _ptr(z), _ptr(M_T), _ptr(S_T), *sizes, stream)
     _lib.check(name, status)
     return z, M_T, S_T
 
@@ -81,6 +82,28 @@ def forward(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
         return ttt_mem_forward_f32(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
     if q.dtype == torch.bfloat16:
         return ttt_mem_forward_bf16(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
+    raise TypeError(f"unsupported input dtype {q.dtype}")
+
+
+def ttt_mem_decode_f32(q, k, v, theta, eta, alpha, M0=None, S0=None, *, out=None):
+    """float32 token-by-token (primal) linear memory; returns ``(z, M_T, S_T)``.
+
+    Pass ``out=(z, M0, S0)`` to carry the state in place between calls.
+    """
+    return _forward("ttt_mem_decode_f32", torch.float32, q, k, v, theta, eta, alpha, M0, S0, 1, out, with_b=False)
+
+
+def ttt_mem_decode_bf16(q, k, v, theta, eta, alpha, M0=None, S0=None, *, out=None):
+    """bf16-input token-by-token (primal) linear memory (float32 arithmetic, state and z)."""
+    return _forward("ttt_mem_decode_bf16", torch.bfloat16, q, k, v, theta, eta, alpha, M0, S0, 1, out, with_b=False)
+
+
+def decode(q, k, v, theta, eta, alpha, M0=None, S0=None, *, out=None):
+    """Dispatch the token-by-token form on the input dtype (float32 or bfloat16)."""
+    if q.dtype == torch.float32:
+        return ttt_mem_decode_f32(q, k, v, theta, eta, alpha, M0, S0, out=out)
+    if q.dtype == torch.bfloat16:
+        return ttt_mem_decode_bf16(q, k, v, theta, eta, alpha, M0, S0, out=out)
     raise TypeError(f"unsupported input dtype {q.dtype}")
 
 
