@@ -5,9 +5,12 @@ sequence, every chunk -- over one batch of synthetic inputs that are already
 resident in HBM.  By default: the Titans linear-memory workload, B=4 H=16
 T=8192 d=128 b=64, bf16 q/k/v, float32 gates, state and z.  ``--workload 5``
 times the deep (2-layer MLP) memory workload, B=4 H=8 T=4096 d=64 hidden=256
-b=16.  Prints ONE JSON line.
+b=16.  ``--decode`` times token-by-token generation on the Titans shapes
+instead: a step is one call of the primal form for one token of every
+(batch, head) sequence (B=4 H=16 d=128), with the state carried in place from
+step to step.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {2,3,4,5}] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {2,3,4,5} | --decode] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -70,7 +73,18 @@ def algorithmic_work_mlp(w, in_bytes=2, z_bytes=4):
     return ht * per_tok + state, flops, per_tok
 
 
-def measured_traffic(w):
+def algorithmic_work_decode(w, in_bytes=2, z_bytes=4):
+    """Bytes and flops of one token-by-token step for every (batch, head).
+
+    Per (batch, head): read and write M and S (4 d^2 floats), read q, k, v and
+    three gates, write z.  Flops: M k, the S and M updates and M q, 2 d^2 each.
+    """
+    bh = w.B * w.H
+    per_seq = 16 * w.d * w.d + 3 * w.d * in_bytes + 3 * 4 + w.d * z_bytes
+    return bh * per_seq, bh * 8 * w.d * w.d, per_seq
+
+
+def measured_traffic(w, kind="forward"):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter summary.
 
     The summary records the sha256 of the kernel source it was measured on; if
@@ -80,8 +94,12 @@ def measured_traffic(w):
     import hashlib
     if w.id != 3:
         return None
-    path = os.path.join(ROOT, "profiles", "linear_memory_fwd_titans_d128_b64_traffic.json")
-    src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear.hip")
+    if kind == "decode":
+        path = os.path.join(ROOT, "profiles", "linear_memory_decode_titans_d128_traffic.json")
+        src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_decode.hip")
+    else:
+        path = os.path.join(ROOT, "profiles", "linear_memory_fwd_titans_d128_b64_traffic.json")
+        src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear.hip")
     try:
         rec = json.load(open(path))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -104,6 +122,125 @@ def _oracle_worker(args):
         else:
             mlp_forward(q, k, v, th, et, al, W1, W2, None, None, b=b)
         return time.perf_counter() - t0
+
+
+def cpu_baseline_decode(w, inp, tokens):
+    """Time the float64 oracle with b = 1 (the token-by-token form) on every
+    (batch, head) sequence for ``tokens`` tokens, in a process pool."""
+    import multiprocessing as mp
+    ncores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    g = {k: to_numpy64(v) for k, v in inp.items() if k in ("q", "k", "v", "theta", "eta", "alpha")}
+    B, H = w.B, w.H
+    pairs = [(i // H, i % H) for i in range(B * H)]
+    groups = [pairs[i::ncores] for i in range(ncores)]
+    jobs = []
+    for grp in groups:
+        if not grp:
+            continue
+        bi = np.array([p[0] for p in grp])
+        hi = np.array([p[1] for p in grp])
+        jobs.append(tuple(g[x][bi, hi][..., :tokens, :] if g[x].ndim == 4 else g[x][bi, hi][..., :tokens]
+                          for x in ("q", "k", "v", "theta", "eta", "alpha")) + (1, None, None))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(len(jobs)) as pool:
+        per_job = pool.map(_oracle_worker, jobs)
+    wall = time.perf_counter() - t0
+    return {
+        "value": B * tokens / wall,   # tokens/s, each token covering all H heads
+        "unit": "tokens/s",
+        "cores": len(jobs),
+        "kind": "oracle",
+        "sample": f"all {B * H} (batch, head) sequences, {tokens} tokens each, b=1 (token by token); "
+                  f"float64 per-token NumPy loop, {len(jobs)} processes x 1 thread; wall {wall:.2f} s, "
+                  f"busiest process {max(per_job):.2f} s; tokens/s = B * tokens / wall",
+    }
+
+
+def decode_main(args):
+    """Token-by-token generation on the Titans shapes (one token per step, state carried in place)."""
+    steps_total = 1 + args.warmup + args.steps   # token 0: parity step; then warmup; then timed
+    w = WORKLOADS[3].replace(T=steps_total)
+    log(f"decode workload: {w} (one token per step, {steps_total} steps)")
+    inp = make_inputs(w)
+    B, H, d = w.B, w.H, w.d
+    rng = np.random.default_rng(2003)
+    M0 = torch.from_numpy((rng.standard_normal((B, H, d, d)) * 0.05).astype(np.float32))
+    S0 = torch.from_numpy((rng.standard_normal((B, H, d, d)) * 0.005).astype(np.float32))
+    dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    # One [B, H, 1, d] slice per token, contiguous, prepared before timing.
+    toks = []
+    for t in range(steps_total):
+        toks.append(tuple(dev[x][:, :, t:t + 1, :].contiguous() if dev[x].dim() == 4
+                          else dev[x][:, :, t:t + 1].contiguous() for x in ("q", "k", "v", "theta", "eta", "alpha")))
+    M = M0.cuda()
+    S = S0.cuda()
+    z = torch.empty(B, H, 1, d, dtype=torch.float32, device="cuda")
+
+    # Parity of one step from the initial state, every row of sequence 0.
+    from oracle import linear_forward
+    tm.decode(*toks[0], M, S, out=(z, M, S))
+    torch.cuda.synchronize()
+    g = [to_numpy64(x[0, 0].cpu()) for x in toks[0]]
+    zo, Mo, So = linear_forward(*g, to_numpy64(M0[0, 0]), to_numpy64(S0[0, 0]), b=1)
+    errs = [float(np.max(np.abs(to_numpy64(x[0, 0].cpu()) - r)) / np.sqrt(np.mean(r ** 2)))
+            for x, r in ((z[:, :, 0], zo[0]), (M, Mo), (S, So))]
+    parity = max(errs)
+    log(f"parity of step 0 (sequence 0, all rows): z {errs[0]:.3e}, M {errs[1]:.3e}, S {errs[2]:.3e}")
+
+    for t in range(1, 1 + args.warmup):
+        tm.decode(*toks[t], M, S, out=(z, M, S))
+    torch.cuda.synchronize()
+    # Eager steps are bound by host submission (microsecond kernels); a
+    # generation loop replays captured steps.  The K timed steps are captured
+    # once into a HIP graph (kernel launches only) and replayed.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            tm.decode(*toks[1 + args.warmup + i], M, S, out=(z, M, S))
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    avg_launch_ms = ms_per_step
+    nbytes, flops, per_seq = algorithmic_work_decode(w)
+    achieved_gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    log(f"graph of {args.steps} steps: {ms_per_step * 1e3:.2f} us per step; wall/step {t_wall / args.steps * 1e3:.4f} ms")
+    log(f"algorithmic bytes/step {nbytes / 1e6:.2f} MB -> {achieved_gbs:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        wc = WORKLOADS[3].replace(T=4096)   # a longer token stream of the same recipe for the host sample
+        cpu = cpu_baseline_decode(wc, make_inputs(wc), wc.T)
+        log(f"cpu baseline: {cpu}")
+    result = {
+        "metric": "decode tokens/s at B=4,H=16,d=128 (one token per step, state carried)",
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "titans-linear-decode", "B": B, "H": H, "d": d, "tokens_per_step": 1,
+                   "inputs": "bf16 q,k,v; f32 gates", "arithmetic": "f32", "state": "f32 in place",
+                   "z": "f32", "head_tokens_per_s": B * H / (ms_per_step * 1e-3)},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w, "decode"),
+                     "traffic_unit": "bytes/launch", "algorithmic_bytes": nbytes},
+        "cpu_baseline": cpu,
+        "parity_sample_max_rel_err": parity,
+    }
+    print(json.dumps(result), flush=True)
 
 
 def cpu_baseline(w, inp, heads):
@@ -147,6 +284,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--decode", action="store_true",
+                    help="time token-by-token generation (primal form) on the Titans shapes instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="(batch, head) sequences in the oracle sample (0: 64 for the linear memory, "
@@ -165,6 +304,18 @@ def main():
         print("bench.py needs a HIP GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x elementwise copy of {n * 4} bytes read + {n * 4} bytes written")
+        del src, dst
+    if args.decode:
+        decode_main(args)
+        return
     w = WORKLOADS[args.workload]
     deep = w.hidden > 0
     log(f"workload {w}")
@@ -182,16 +333,6 @@ def main():
         ST = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
         call = lambda: tm.forward(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"],  # noqa: E731
                                   dev.get("M0"), dev.get("S0"), b=w.b, out=(z, MT, ST))
-
-    if args.copy_calibration:
-        n = args.copy_calibration * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        log(f"copy calibration: 3 x elementwise copy of {n * 4} bytes read + {n * 4} bytes written")
-        del src, dst
 
     for _ in range(args.warmup):
         call()

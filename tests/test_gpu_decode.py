@@ -161,9 +161,38 @@ def test_decode_argument_errors():
     assert e.value.status == -2
     w = WORKLOADS[3].replace(B=1, H=1, T=4, dtype="f32", d=16)
     inp = to_dev(make_inputs(w))
-    z = inp["q"].clone()
     with pytest.raises(TTTError) as e:   # z aliasing q
         tm.decode(inp["q"], inp["k"], inp["v"], inp["theta"], inp["eta"], inp["alpha"],
                   out=(inp["q"], None, None))
     assert e.value.status == -1
-    del z
+
+
+def test_decode_graph_replays_match_eager():
+    # The bench times decode steps replayed from a HIP graph (state carried in
+    # place).  Each replay continues the state; every replay must equal the
+    # same steps run eagerly, with eager work and synchronisation in between.
+    w = WORKLOADS[3].replace(B=1, H=4, T=3)
+    inp = to_dev(_with_state(make_inputs(w)))
+    toks = [tuple(inp[x][:, :, t:t + 1, :].contiguous() if inp[x].dim() == 4 else inp[x][:, :, t:t + 1].contiguous()
+                  for x in ("q", "k", "v", "theta", "eta", "alpha")) for t in range(w.T)]
+    M, S = inp["M0"].clone(), inp["S0"].clone()
+    z = torch.empty(w.B, w.H, 1, w.d, dtype=torch.float32, device="cuda")
+    tm.decode(*toks[0], M.clone(), S.clone())   # load the library before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(w.T):
+            tm.decode(*toks[t], M, S, out=(z, M, S))
+    # Capture launches nothing: reset the carried state before the first replay.
+    M.copy_(inp["M0"])
+    S.copy_(inp["S0"])
+    Me, Se = inp["M0"].clone(), inp["S0"].clone()
+    ze = torch.empty_like(z)
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for t in range(w.T):
+            tm.decode(*toks[t], Me, Se, out=(ze, Me, Se))
+        torch.cuda.synchronize()
+        _say(f"  replay {rep}: max|dz| {float((z - ze).abs().max()):.3e}")
+        assert torch.equal(z, ze) and torch.equal(M, Me) and torch.equal(S, Se)
