@@ -131,7 +131,7 @@ int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_
  * the primal form).  The result equals ttt_mem_forward_* with b = 1; the
  * intended use is T = 1 per call with the state carried in place
  * (M_T == M0, S_T == S0) from one generated token to the next
- * ("Continual Learning: From Attention to Neural Memory", section 4.3, the
+ * ("Continual Learning: From Attention to Neural Memory", section 4.8, the
  * note on streaming inference).  All arithmetic is float32; the bf16 entry
  * point widens q, k, v exactly.  Layouts, NULL states, aliasing and error
  * behaviour as above; alignment: M0, S0, M_T, S_T 16 bytes, q and k 16 bytes

@@ -6,7 +6,7 @@
 // gradient is taken at the memory its predecessor left, i.e. chunks of one
 // token ("5.1.1 · TTT layers 与 fast weights", section 1.1, the primal/dual
 // comparison after eq. (9)), with the state carried from call to call
-// ("Continual Learning: From Attention to Neural Memory", section 4.3, the
+// ("Continual Learning: From Attention to Neural Memory", section 4.8, the
 // note on streaming inference).  Per token t and memory row i:
 //
 //   e_i   = M[i,:] . k_t - v_t[i]
