@@ -922,7 +922,8 @@ struct Kernel {
     // the own token tiles over all key k-groups (own fragments from registers,
     // the partner's from the exchange); the residual tiles go to the exchange.
     template <int BI>
-    __device__ static void phaseA2(const Lanes& a, uint32_t gs, const F* MB, const F* SB, f32x4* E, f32x4* Zp) {
+    __device__ static void phaseA2(const Lanes& a, uint32_t gs, uint32_t gsc, const F* MB, const F* SB, f32x4* E,
+                                   f32x4* Zp, f32x4* Macc, f32x4* Sacc) {
         constexpr uint32_t BO = BI * kBufB;
         F kf[2][NTW], qf[2][NTW], MP[NKCW], SP[NKCW];
         i16x4 vr[NTW];
@@ -976,18 +977,25 @@ struct Kernel {
             Zp[tw] = av[tw] * za[tw] + cv[tw] * zc[tw];
             lds_store<f16x4>(a.xeo + 8 * kWave * tw, cvt4(E[tw]));
         }
+        // Decay of the own state for the carry (M0, S0 entered the products
+        // above through their fp16 fragments; this phase has slack).
+        const f32x4 sc = lds_load<f32x4>(gsc);   // A_n, c_n, E_n (the same address in every lane)
+#pragma unroll
+        for (int cw = 0; cw < NCW; ++cw) {
+            Macc[cw] = sc[0] * Macc[cw] + sc[1] * Sacc[cw];
+            Sacc[cw] = sc[2] * Sacc[cw];
+        }
     }
 
-    // Phase B (pipelined): decay of the state, the intra-chunk term and the
-    // store of z for the own token tiles, then the update of the own columns
+    // Phase B (pipelined): the intra-chunk term and the store of z for the own
+    // token tiles, then the update of the own (already decayed) columns
     // with the transposed k reads of the next column tile in flight.  The
     // intra-chunk products run over every token k-group: the blocks of P
     // above its diagonal are never written and stay zero.
     template <int BI>
-    __device__ static void phaseB2(const Lanes& a, uint32_t gsc, f32x4* Macc, f32x4* Sacc, F* MB, F* SB, f32x4* Zp,
+    __device__ static void phaseB2(const Lanes& a, f32x4* Macc, f32x4* Sacc, F* MB, F* SB, f32x4* Zp,
                                    __amdgpu_buffer_rsrc_t rz, uint32_t zoff) {
         constexpr uint32_t BO = BI * kBufB;
-        const f32x4 sc = lds_load<f32x4>(gsc);   // A_n, c_n, E_n (the same address in every lane)
         f16x4 eb[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) eb[tt] = lds_load<f16x4>(a.xe + 8 * kWave * tt);
@@ -1015,13 +1023,6 @@ struct Kernel {
         };
         load_kt(0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // State decay (the loads above are in flight).
-        const float An = sc[0], Cn = sc[1], En = sc[2];
-#pragma unroll
-        for (int cw = 0; cw < NCW; ++cw) {
-            Macc[cw] = An * Macc[cw] + Cn * Sacc[cw];
-            Sacc[cw] = En * Sacc[cw];
-        }
         F EB[NKT];
 #pragma unroll
         for (int s = 0; s < NKT; ++s) {
@@ -1248,20 +1249,20 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
                     const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
                                               static_cast<uint32_t>(chunk_n(c)) * D * 4);
                     const uint32_t gs = a.g + static_cast<uint32_t>(c & 3) * K::kGateB;
-                    K::template phaseA2<0>(a, gs, MB, SB, E, Zp);
-                    __syncthreads();
                     const uint32_t gsc = lds_addr(&sm.rg[c & 3].scal[0]);
-                    K::template phaseB2<0>(a, gsc, Macc, Sacc, MB, SB, Zp, rz, zoff);
+                    K::template phaseA2<0>(a, gs, gsc, MB, SB, E, Zp, Macc, Sacc);
+                    __syncthreads();
+                    K::template phaseB2<0>(a, Macc, Sacc, MB, SB, Zp, rz, zoff);
                     __syncthreads();
                 }
                 if (c + 1 < nch) {
                     const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c + 1) * b) * D,
                                               static_cast<uint32_t>(chunk_n(c + 1)) * D * 4);
                     const uint32_t gs = a.g + static_cast<uint32_t>((c + 1) & 3) * K::kGateB;
-                    K::template phaseA2<1>(a, gs, MB, SB, E, Zp);
-                    __syncthreads();
                     const uint32_t gsc = lds_addr(&sm.rg[(c + 1) & 3].scal[0]);
-                    K::template phaseB2<1>(a, gsc, Macc, Sacc, MB, SB, Zp, rz, zoff);
+                    K::template phaseA2<1>(a, gs, gsc, MB, SB, E, Zp, Macc, Sacc);
+                    __syncthreads();
+                    K::template phaseB2<1>(a, Macc, Sacc, MB, SB, Zp, rz, zoff);
                     __syncthreads();
                 }
             }
