@@ -159,7 +159,7 @@ def cpu_baseline_decode(w, inp, tokens):
 
 def decode_main(args):
     """Token-by-token generation on the Titans shapes (one token per step, state carried in place)."""
-    steps_total = 1 + args.warmup + args.steps   # token 0: parity step; then warmup; then timed
+    steps_total = 1 + args.steps   # token 0: parity step; then the K captured steps
     w = WORKLOADS[3].replace(T=steps_total)
     log(f"decode workload: {w} (one token per step, {steps_total} steps)")
     inp = make_inputs(w)
@@ -188,16 +188,17 @@ def decode_main(args):
     parity = max(errs)
     log(f"parity of step 0 (sequence 0, all rows): z {errs[0]:.3e}, M {errs[1]:.3e}, S {errs[2]:.3e}")
 
-    for t in range(1, 1 + args.warmup):
-        tm.decode(*toks[t], M, S, out=(z, M, S))
-    torch.cuda.synchronize()
     # Eager steps are bound by host submission (microsecond kernels); a
-    # generation loop replays captured steps.  The K timed steps are captured
-    # once into a HIP graph (kernel launches only) and replayed.
+    # generation loop replays captured steps.  The K steps are captured once
+    # into a HIP graph (kernel launches only); the warmup replays it until W
+    # untimed steps have run, then one replay is timed.
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for i in range(args.steps):
-            tm.decode(*toks[1 + args.warmup + i], M, S, out=(z, M, S))
+            tm.decode(*toks[1 + i], M, S, out=(z, M, S))
+    torch.cuda.synchronize()
+    for _ in range((args.warmup + args.steps - 1) // args.steps):
+        graph.replay()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -282,7 +283,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU's clocks ramp up over the first ~20 ms of back-to-back launches
+    # (a launch of the Titans workload falls from ~290 us to ~220 us); the
+    # default warmup runs past that ramp.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--decode", action="store_true",
                     help="time token-by-token generation (primal form) on the Titans shapes instead")
