@@ -8,9 +8,12 @@ times the deep (2-layer MLP) memory workload, B=4 H=8 T=4096 d=64 hidden=256
 b=16.  ``--decode`` times token-by-token generation on the Titans shapes
 instead: a step is one call of the primal form for one token of every
 (batch, head) sequence (B=4 H=16 d=128), with the state carried in place from
-step to step.  Prints ONE JSON line.
+step to step.  ``--varlen`` times packed variable-length documents with the
+Titans recipe (32768 tokens per head in documents of seeded lengths, each
+from its own state).  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {2,3,4,5} | --decode] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {2,3,4,5} | --decode | --varlen]
+                    [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -244,6 +247,125 @@ def decode_main(args):
     print(json.dumps(result), flush=True)
 
 
+def varlen_lengths(total, seed=3001, mean=1024):
+    """Seeded document lengths for a packed batch: lognormal (sigma 1) around `mean`,
+    clipped to [1, 8192], the last one trimmed so that they sum to `total`."""
+    rng = np.random.default_rng(seed)
+    out, acc = [], 0
+    while acc < total:
+        n = int(np.clip(rng.lognormal(np.log(mean) - 0.5, 1.0), 1, 8192))
+        n = min(n, total - acc)
+        out.append(n)
+        acc += n
+    return out
+
+
+def varlen_main(args):
+    """Packed variable-length documents with the Titans recipe: H=16, d=128, b=64,
+    B*T = 32768 tokens per head split into documents of seeded lengths."""
+    wv = WORKLOADS[3].replace(B=1, T=4 * 8192)
+    lengths = varlen_lengths(wv.T)
+    N, H, T, d = len(lengths), wv.H, wv.T, wv.d
+    log(f"varlen workload: {N} documents, lengths min {min(lengths)} median {int(np.median(lengths))} "
+        f"max {max(lengths)}, {T} tokens per head, H={H} d={d} b={wv.b}")
+    inp = make_inputs(wv)
+    dev = {k: v[0].cuda() for k, v in inp.items() if v is not None}
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    z = torch.empty(H, T, d, dtype=torch.float32, device="cuda")
+    MT = torch.empty(N, H, d, d, dtype=torch.float32, device="cuda")
+    ST = torch.empty_like(MT)
+    call = lambda: tm.forward_varlen(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"],  # noqa: E731
+                                     cu, b=wv.b, out=(z, MT, ST))
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        starts[i].record()
+        call()
+        ends[i].record()
+    torch.cuda.synchronize()
+    launch_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
+    avg_launch_ms = float(np.mean(launch_ms))
+    per_tok = 3 * d * 2 + 3 * 4 + d * 4
+    nbytes = H * T * per_tok + N * H * d * d * 4 * 2
+    achieved_gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    log(f"avg launch {avg_launch_ms * 1e3:.1f} us, min {min(launch_ms) * 1e3:.1f} us; "
+        f"algorithmic bytes/launch {nbytes / 1e6:.1f} MB -> {achieved_gbs:.0f} GB/s")
+    # Parity: the first two documents of head 0, every row.
+    from oracle import linear_forward
+    g = {k: to_numpy64(v[0, 0]) for k, v in inp.items() if v is not None}
+    errs = []
+    for s_ in range(min(2, N)):
+        t0, t1 = int(sum(lengths[:s_])), int(sum(lengths[:s_ + 1]))
+        zo = linear_forward(g["q"][t0:t1], g["k"][t0:t1], g["v"][t0:t1], g["theta"][t0:t1], g["eta"][t0:t1],
+                            g["alpha"][t0:t1], None, None, b=wv.b)[0]
+        errs.append(float(np.max(np.abs(z[0, t0:t1].double().cpu().numpy() - zo)) / np.sqrt(np.mean(zo ** 2))))
+    parity = max(errs)
+    log(f"sampled parity (documents 0-1, head 0): max|dz|/rms = {parity:.3e}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_varlen(inp, lengths, H, wv.b)
+        log(f"cpu baseline: {cpu}")
+    result = {
+        "metric": "packed-document tokens/s at H=16,d=128,b=64 (variable-length documents)",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "titans-linear-varlen", "documents": N, "tokens_per_head": T, "H": H, "d": d,
+                   "b": wv.b, "lengths": "lognormal(sigma 1) around 1024, clipped to [1, 8192], seed 3001",
+                   "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "state": "f32", "z": "f32"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None, "traffic_unit": "bytes/launch",
+                     "algorithmic_bytes": nbytes},
+        "cpu_baseline": cpu,
+        "parity_sample_max_rel_err": parity,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_varlen(inp, lengths, H, b, docs=12):
+    """Time the float64 oracle on the first `docs` documents of every head, in a process pool."""
+    import multiprocessing as mp
+    ncores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    g = {k: to_numpy64(v[0]) for k, v in inp.items() if k in ("q", "k", "v", "theta", "eta", "alpha")}
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    pairs = [(s_, h) for s_ in range(min(docs, len(lengths))) for h in range(H)]
+    jobs = [[] for _ in range(ncores)]
+    for i, (s_, h) in enumerate(pairs):
+        t0, t1 = cu[s_], cu[s_ + 1]
+        jobs[i % ncores].append(tuple(g[x][h:h + 1, t0:t1] for x in ("q", "k", "v", "theta", "eta", "alpha")))
+    work = []
+    for grp in jobs:
+        for item in grp:
+            work.append(item + (b, None, None))
+    ctx = mp.get_context("fork")
+    t0w = time.perf_counter()
+    with ctx.Pool(ncores) as pool:
+        per_job = pool.map(_oracle_worker, work)
+    wall = time.perf_counter() - t0w
+    tokens = int(cu[min(docs, len(lengths))])
+    return {
+        "value": tokens / wall,   # tokens/s, each token covering all H heads
+        "unit": "tokens/s",
+        "cores": ncores,
+        "kind": "oracle",
+        "sample": f"first {min(docs, len(lengths))} of {len(lengths)} documents ({tokens} tokens) on all {H} heads; "
+                  f"float64 per-token NumPy loop, {ncores} processes x 1 thread; wall {wall:.2f} s, "
+                  f"busiest task {max(per_job):.2f} s; tokens/s = sampled tokens / wall",
+    }
+
+
 def cpu_baseline(w, inp, heads):
     """Time the float64 oracle on ``heads`` (batch, head) pairs with full T, in a process pool."""
     import multiprocessing as mp
@@ -290,6 +412,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--decode", action="store_true",
                     help="time token-by-token generation (primal form) on the Titans shapes instead")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time packed variable-length documents with the Titans recipe instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="(batch, head) sequences in the oracle sample (0: 64 for the linear memory, "
@@ -319,6 +443,9 @@ def main():
         del src, dst
     if args.decode:
         decode_main(args)
+        return
+    if args.varlen:
+        varlen_main(args)
         return
     w = WORKLOADS[args.workload]
     deep = w.hidden > 0

@@ -124,6 +124,42 @@ int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_
                              int B, int H, int T, int d, int hidden, int b, void* stream);
 
 /*
+ * Linear memory over packed variable-length documents: every document starts
+ * from its own initial state, so nothing of one document leaks into the next
+ * through the fast weights ("5.1.1 · TTT layers 与 fast weights", section 1.2,
+ * the notes on packed documents: the state reset follows the document
+ * boundaries, momentum included; "Continual Learning: From Attention to
+ * Neural Memory", sections 4.6 and 4.8: every independent sequence begins
+ * from its own starting point, the memory is reset per sequence).  Each
+ * document is chunked
+ * on its own (its first chunk starts at its first token) and computed exactly
+ * as ttt_mem_forward_* computes one sequence.
+ *
+ *   cu_seqlens: DEVICE int32 [N + 1], non-decreasing, cu_seqlens[0] = 0,
+ *     cu_seqlens[N] <= T; document s is tokens cu_seqlens[s] ..
+ *     cu_seqlens[s+1]-1.  (The host cannot read it; the kernel clamps every
+ *     offset into [0, T], so a malformed table gives wrong results, never an
+ *     access outside the arrays.)  An empty document copies its initial state.
+ *   Layouts: q, k, v, z [H, T, d]; theta, eta, alpha [H, T]; M0, S0, M_T, S_T
+ *     [N, H, d, d] (document-major).  Tokens outside every document are not
+ *     read and their z is not written.
+ *   Everything else (NULL states, aliasing, alignment, d, b, precision) as
+ *   for ttt_mem_forward_f32 / ttt_mem_forward_bf16; cu_seqlens must not
+ *   overlap z, M_T or S_T.
+ */
+int ttt_mem_forward_varlen_f32(const float* q, const float* k, const float* v,
+                               const float* theta, const float* eta, const float* alpha,
+                               const float* M0, const float* S0,
+                               float* z, float* M_T, float* S_T,
+                               const int* cu_seqlens, int N, int H, int T, int d, int b, void* stream);
+
+int ttt_mem_forward_varlen_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const float* theta, const float* eta, const float* alpha,
+                                const float* M0, const float* S0,
+                                float* z, float* M_T, float* S_T,
+                                const int* cu_seqlens, int N, int H, int T, int d, int b, void* stream);
+
+/*
  * Linear memory, token by token (the primal form), for generation: every
  * token's gradient is taken at the memory the previous token left (chunks of
  * one token; "5.1.1 · TTT layers 与 fast weights", section 1.1, the

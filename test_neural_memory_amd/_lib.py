@@ -24,6 +24,8 @@ _SIGNATURES = {
     "ttt_mem_forward_f32": (_I, [_P] * 11 + [_I] * 5 + [_P]),
     "ttt_mem_forward_bf16": (_I, [_P] * 11 + [_I] * 5 + [_P]),
     "ttt_mem_mlp_forward_bf16": (_I, [_P] * 15 + [_I] * 6 + [_P]),
+    "ttt_mem_forward_varlen_f32": (_I, [_P] * 12 + [_I] * 5 + [_P]),
+    "ttt_mem_forward_varlen_bf16": (_I, [_P] * 12 + [_I] * 5 + [_P]),
     "ttt_mem_decode_f32": (_I, [_P] * 11 + [_I] * 4 + [_P]),
     "ttt_mem_decode_bf16": (_I, [_P] * 11 + [_I] * 4 + [_P]),
     "ttt_mem_status_string": (ctypes.c_char_p, [_I]),

@@ -215,6 +215,11 @@ struct Params {
     int BH;
     int T;
     int b;
+    // Packed variable-length documents (NULL: dense [B, H, T, d]): document s
+    // of head h is tokens cu[s] .. cu[s+1]-1 of head h's [T, d] rows, and
+    // its state is slot s * H + h.
+    const int* cu;
+    int H;
 };
 
 // Compile-time geometry of one kernel instance: NS 16-row tiles per
@@ -420,10 +425,10 @@ struct Kernel {
     // same on every path, so waits on an older prefetch set stay partial.
     template <int PW>
     __device__ static void issue(Prefetch& pf, const Params& p, const G* gq, const G* gk, const G* gv,
-                                 size_t seq_tok, int row_wg, int c, int lane) {
+                                 size_t seq_tok, int seqlen, int row_wg, int c, int lane) {
         using Sh = Share<PW>;
         const int c0 = c * p.b;
-        const int n = max(0, min(p.b, p.T - c0));
+        const int n = max(0, min(p.b, seqlen - c0));
         const size_t chunk_off = (seq_tok + c0) * D;
         const uint32_t nbytes = static_cast<uint32_t>(n) * D * sizeof(G);
         const auto rq = make_rsrc(gq + chunk_off, nbytes);
@@ -1081,7 +1086,7 @@ struct Kernel {
 // One producer wave's loop (role PW): the same barriers as the state waves.
 template <typename T, int D, int NS, int CS, int NP, int PW>
 __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Kernel<T, D, NS, CS, NP>::S& sm,
-                                                   size_t seq_tok, int row_wg, int nch, int lane) {
+                                                   size_t seq_tok, int seqlen, int row_wg, int nch, int lane) {
     using Gm = Geo<T, D, NS, CS, NP>;
     using K = Kernel<T, D, NS, CS, NP>;
     using G = typename Gm::G;
@@ -1090,7 +1095,7 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
     // the P tiles and staging (the state waves' priority is set in the kernel).
     __builtin_amdgcn_s_setprio(PW < 2 ? 3 : 1);
     const int b = p.b;
-    auto chunk_n = [&](int c) { return min(b, p.T - c * b); };
+    auto chunk_n = [&](int c) { return min(b, seqlen - c * b); };
     const G* __restrict__ gq = static_cast<const G*>(p.q);
     const G* __restrict__ gk = static_cast<const G*>(p.k);
     const G* __restrict__ gv = static_cast<const G*>(p.v);
@@ -1115,7 +1120,7 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
         if constexpr (!Gm::USE_GAM && PW == K::kWrowWave) K::wrow(sm.gs[c & 1], B, chunk_n(c), lane);
     };
     auto issue = [&](int c, typename K::Prefetch& pf) {
-        K::template issue<PW>(pf, p, gq, gk, gv, seq_tok, row_wg, c, lane);
+        K::template issue<PW>(pf, p, gq, gk, gv, seq_tok, seqlen, row_wg, c, lane);
     };
     if constexpr (Gm::NBUF == 2) {
         // Two register sets of prefetched chunks (even and odd chunks): the
@@ -1199,11 +1204,19 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
     if ((p.BH % 8) == 0) lin = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
     const int bh = lin / Gm::NRB;
     const int rb = lin % Gm::NRB;
-    const int seqlen = p.T;
+    int seqlen = p.T;
+    size_t seq_tok = static_cast<size_t>(bh) * p.T;
+    if (p.cu) {
+        // Offsets clamped into [0, T]: a malformed table cannot send any
+        // access outside the packed arrays.
+        const int s = bh / p.H, h = bh % p.H;
+        const int t0 = min(max(p.cu[s], 0), p.T);
+        seqlen = min(max(p.cu[s + 1], t0), p.T) - t0;
+        seq_tok = static_cast<size_t>(h) * p.T + t0;
+    }
     const int b = p.b;
     const int row_wg = rb * RB;
     const int nch = (seqlen + b - 1) / b;
-    const size_t seq_tok = static_cast<size_t>(bh) * seqlen;
     auto chunk_n = [&](int c) { return min(b, seqlen - c * b); };
 
     // Zero all staging memory once: padded rows and columns stay 0.
@@ -1309,16 +1322,16 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
     } else {
         // ===================== producer wave =====================
         const int pw = w - NSW;
-        if (pw == 0) producer_loop_impl<T, D, NS, CS, NP, 0>(p, sm, seq_tok, row_wg, nch, lane);
-        else if (pw == 1) producer_loop_impl<T, D, NS, CS, NP, 1>(p, sm, seq_tok, row_wg, nch, lane);
+        if (pw == 0) producer_loop_impl<T, D, NS, CS, NP, 0>(p, sm, seq_tok, seqlen, row_wg, nch, lane);
+        else if (pw == 1) producer_loop_impl<T, D, NS, CS, NP, 1>(p, sm, seq_tok, seqlen, row_wg, nch, lane);
         else if constexpr (Gm::NPW == 8) {
             switch (pw) {
-                case 2: producer_loop_impl<T, D, NS, CS, NP, 2>(p, sm, seq_tok, row_wg, nch, lane); break;
-                case 3: producer_loop_impl<T, D, NS, CS, NP, 3>(p, sm, seq_tok, row_wg, nch, lane); break;
-                case 4: producer_loop_impl<T, D, NS, CS, NP, 4>(p, sm, seq_tok, row_wg, nch, lane); break;
-                case 5: producer_loop_impl<T, D, NS, CS, NP, 5>(p, sm, seq_tok, row_wg, nch, lane); break;
-                case 6: producer_loop_impl<T, D, NS, CS, NP, 6>(p, sm, seq_tok, row_wg, nch, lane); break;
-                default: producer_loop_impl<T, D, NS, CS, NP, 7>(p, sm, seq_tok, row_wg, nch, lane); break;
+                case 2: producer_loop_impl<T, D, NS, CS, NP, 2>(p, sm, seq_tok, seqlen, row_wg, nch, lane); break;
+                case 3: producer_loop_impl<T, D, NS, CS, NP, 3>(p, sm, seq_tok, seqlen, row_wg, nch, lane); break;
+                case 4: producer_loop_impl<T, D, NS, CS, NP, 4>(p, sm, seq_tok, seqlen, row_wg, nch, lane); break;
+                case 5: producer_loop_impl<T, D, NS, CS, NP, 5>(p, sm, seq_tok, seqlen, row_wg, nch, lane); break;
+                case 6: producer_loop_impl<T, D, NS, CS, NP, 6>(p, sm, seq_tok, seqlen, row_wg, nch, lane); break;
+                default: producer_loop_impl<T, D, NS, CS, NP, 7>(p, sm, seq_tok, seqlen, row_wg, nch, lane); break;
             }
         }
     }
@@ -1413,7 +1426,58 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
         return TTT_ERR_INVALID_ARG;
     if (M_T && S_T && overlaps(M_T, st_bytes, S_T, st_bytes)) return TTT_ERR_INVALID_ARG;
 
-    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b};
+    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, nullptr, H};
+    const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+// Packed variable-length documents: q, k, v, z [H, T, d] and gates [H, T]
+// with document s of head h at tokens cu[s] .. cu[s+1]-1; states [N, H, d, d].
+template <typename T>
+int forward_varlen_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
+                        const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
+                        const int* cu, int N, int H, int Tlen, int d, int b, void* stream) {
+    using G = typename GlobalOf<T>::type;
+    if (N < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
+    if (b < 1) return TTT_ERR_INVALID_ARG;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
+    if (b > 64) return TTT_ERR_UNSUPPORTED;
+    const long long BH = static_cast<long long>(N) * H;
+    if (BH == 0) return TTT_OK;
+    if (!cu || !aligned(cu, 4)) return TTT_ERR_INVALID_ARG;
+    if (BH * (d / 16) > 0x7fffffffLL) return TTT_ERR_UNSUPPORTED;
+    if (static_cast<long long>(H) * Tlen > 0x7fffffffLL) return TTT_ERR_UNSUPPORTED;
+    const size_t tok = static_cast<size_t>(H) * static_cast<size_t>(Tlen);
+    const size_t in_bytes = tok * d * sizeof(G);
+    const size_t z_bytes = tok * d * sizeof(float);
+    const size_t st_bytes = static_cast<size_t>(BH) * d * d * sizeof(float);
+    const size_t cu_bytes = (static_cast<size_t>(N) + 1) * sizeof(int);
+    if (Tlen > 0) {
+        if (!q || !k || !v || !theta || !eta || !alpha || !z) return TTT_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(z, 16)) return TTT_ERR_INVALID_ARG;
+        if (!aligned(theta, 4) || !aligned(eta, 4) || !aligned(alpha, 4)) return TTT_ERR_INVALID_ARG;
+        const void* ins[] = {q, k, v};
+        for (const void* in : ins)
+            if (overlaps(z, z_bytes, in, in_bytes)) return TTT_ERR_INVALID_ARG;
+        const void* gates[] = {theta, eta, alpha};
+        for (const void* g : gates)
+            if (overlaps(z, z_bytes, g, tok * sizeof(float))) return TTT_ERR_INVALID_ARG;
+        if (overlaps(z, z_bytes, M0, st_bytes) || overlaps(z, z_bytes, S0, st_bytes) ||
+            overlaps(z, z_bytes, M_T, st_bytes) || overlaps(z, z_bytes, S_T, st_bytes) ||
+            overlaps(z, z_bytes, cu, cu_bytes))
+            return TTT_ERR_INVALID_ARG;
+    }
+    const void* states[] = {M0, S0, M_T, S_T};
+    for (const void* st : states)
+        if (st && !aligned(st, 16)) return TTT_ERR_INVALID_ARG;
+    if (M_T && M_T != M0 && (overlaps(M_T, st_bytes, M0, st_bytes) || overlaps(M_T, st_bytes, S0, st_bytes)))
+        return TTT_ERR_INVALID_ARG;
+    if (S_T && S_T != S0 && (overlaps(S_T, st_bytes, S0, st_bytes) || overlaps(S_T, st_bytes, M0, st_bytes)))
+        return TTT_ERR_INVALID_ARG;
+    if (M_T && S_T && overlaps(M_T, st_bytes, S_T, st_bytes)) return TTT_ERR_INVALID_ARG;
+    if (overlaps(M_T, st_bytes, cu, cu_bytes) || overlaps(S_T, st_bytes, cu, cu_bytes)) return TTT_ERR_INVALID_ARG;
+
+    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1432,6 +1496,21 @@ int ttt_mem_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
                          float* M_T, float* S_T, int B, int H, int T, int d, int b, void* stream) {
     return forward_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, B, H, T, d, b, stream);
+}
+
+int ttt_mem_forward_varlen_f32(const float* q, const float* k, const float* v, const float* theta, const float* eta,
+                               const float* alpha, const float* M0, const float* S0, float* z, float* M_T,
+                               float* S_T, const int* cu_seqlens, int N, int H, int T, int d, int b, void* stream) {
+    return forward_varlen_impl<float>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, cu_seqlens, N, H, T, d, b,
+                                      stream);
+}
+
+int ttt_mem_forward_varlen_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                                const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
+                                float* M_T, float* S_T, const int* cu_seqlens, int N, int H, int T, int d, int b,
+                                void* stream) {
+    return forward_varlen_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, cu_seqlens, N, H, T, d, b,
+                                         stream);
 }
 
 const char* ttt_mem_status_string(int status) {

@@ -85,6 +85,56 @@ def forward(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
     raise TypeError(f"unsupported input dtype {q.dtype}")
 
 
+def forward_varlen(q, k, v, theta, eta, alpha, cu_seqlens, M0=None, S0=None, *, b, out=None):
+    """Linear memory over packed variable-length documents; returns ``(z, M_T, S_T)``.
+
+    ``q, k, v`` are ``[H, T, d]`` (float32 or bfloat16), the gates ``[H, T]``,
+    ``cu_seqlens`` an int32 device tensor ``[N + 1]`` of document offsets, and
+    the states ``[N, H, d, d]``: each document starts from its own state.
+    """
+    if q.dim() != 3:
+        raise ValueError("q must be [H, T, d]")
+    H, T, d = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be HIP device tensors (torch 'cuda' device)")
+    if q.dtype == torch.float32:
+        name = "ttt_mem_forward_varlen_f32"
+    elif q.dtype == torch.bfloat16:
+        name = "ttt_mem_forward_varlen_bf16"
+    else:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    cu = _as_dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    q = _as_dev(q, "q", q.dtype, (H, T, d), dev)
+    k = _as_dev(k, "k", q.dtype, (H, T, d), dev)
+    v = _as_dev(v, "v", q.dtype, (H, T, d), dev)
+    theta = _as_dev(theta, "theta", torch.float32, (H, T), dev)
+    eta = _as_dev(eta, "eta", torch.float32, (H, T), dev)
+    alpha = _as_dev(alpha, "alpha", torch.float32, (H, T), dev)
+    M0 = _as_dev(M0, "M0", torch.float32, (N, H, d, d), dev)
+    S0 = _as_dev(S0, "S0", torch.float32, (N, H, d, d), dev)
+    shapes = ((H, T, d), (N, H, d, d), (N, H, d, d))
+    if out is None:
+        out = tuple(torch.empty(s_, dtype=torch.float32, device=dev) for s_ in shapes)
+    else:
+        for t, nm, shp in zip(out, ("z", "M_T", "S_T"), shapes):
+            if t is not None and (not t.is_contiguous() or t.dtype != torch.float32
+                                  or tuple(t.shape) != shp or t.device != dev):
+                raise ValueError(f"out tensor {nm} must be contiguous float32 {shp} on {dev}")
+    z, M_T, S_T = out
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        status = getattr(lib, name)(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(M0), _ptr(S0),
+            _ptr(z), _ptr(M_T), _ptr(S_T), _ptr(cu), N, H, T, d, int(b), stream)
+    _lib.check(name, status)
+    return z, M_T, S_T
+
+
 def ttt_mem_decode_f32(q, k, v, theta, eta, alpha, M0=None, S0=None, *, out=None):
     """float32 token-by-token (primal) linear memory; returns ``(z, M_T, S_T)``.
 
