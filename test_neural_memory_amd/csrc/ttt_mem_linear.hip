@@ -191,11 +191,11 @@ template <> struct GlobalOf<float> { using type = float; };
 template <> struct GlobalOf<_Float16> { using type = uint16_t; };
 
 
-// row_newbcast:N -- every lane of a 16-lane row receives lane N of that row.
+// row_newbcast:N -- every lane of a 16-lane row receives lane N of that row
+// (every lane has a source, so the instruction needs no old value).
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf,
-                                                                 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
 }
 
 
@@ -557,7 +557,7 @@ struct Kernel {
     // (block, column j); row i = 16*block + s takes a_i, eta_i from lane s of
     // the same 16-lane row.  The column state starts at (gamma, p) = (1, 1) on
     // its own row: p <- eta_i p + [i == j], gamma <- a_i gamma + p, which is
-    // zero above the diagonal.
+    // zero above the diagonal (scaled by theta_j, below).
     __device__ static void gate_diag(const Prefetch& pf, GateSlot& gs, int n, int lane) {
         const int l = lane;
         const float th = pf.th, et = l < n ? pf.et : 1.f, a = 1.f - pf.al;
@@ -582,16 +582,18 @@ struct Kernel {
         if (qb < NT) {
             float* gd = gs.gamd + qb * kGB + jj;
             float* gpd = gs.gampd + qb * kGB + jj;
+            // The recurrences are linear, so starting column j at theta_j
+            // instead of 1 yields theta_j gamma_ij and theta_j p_ij directly.
             float pp = 0.f, gg = 0.f;
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
-                pp = ei[s] * pp + (s == jj ? 1.f : 0.f);
+                pp = s == jj ? th : ei[s] * pp;
                 gg = ai[s] * gg + pp;
-                gd[s * kGR] = th * gg;
-                gpd[s * kGR] = th * pp;
+                gd[s * kGR] = gg;
+                gpd[s * kGR] = pp;
             }
-            gs.gend[l] = th * gg;
-            gs.pend[l] = th * pp;
+            gs.gend[l] = gg;
+            gs.pend[l] = pp;
         }
     }
 
