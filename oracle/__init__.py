@@ -13,6 +13,11 @@ What it computes, in the pages' own order (a per-token loop, float64):
   Titans momentum and forgetting.  Pinned by the pages' worked examples and by
   closed forms (delta rule, linear attention, batch gradient descent, one-step
   loss contraction, decay unrolling, constant-gate momentum expansion).
+* ``linear_backward`` -- the outer gradient of ``linear_forward`` with respect
+  to every input and the initial state, by reverse mode through the same
+  per-token loop.  Pinned by central finite differences of the pinned forward,
+  the pages' scalar outer-gradient examples, and the closed-form gradients of
+  weighted linear attention.
 * ``mlp_forward`` -- the same schedule for a 2-layer MLP memory
   ``f(u) = u + SiLU(u W1) W2`` with gradients by explicit backprop.  Pinned by
   torch.autograd (a library routine), finite differences, and by agreement of
@@ -23,6 +28,6 @@ Every function here is pinned by tests in ``tests/test_oracle_*.py``; none is
 "parity unpinned".
 """
 
-from .memory import linear_forward, mlp_forward, silu, silu_grad, mlp_chunk_grads
+from .memory import linear_forward, linear_backward, mlp_forward, silu, silu_grad, mlp_chunk_grads
 
-__all__ = ["linear_forward", "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]
+__all__ = ["linear_forward", "linear_backward", "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]

@@ -33,7 +33,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["linear_forward", "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]
+__all__ = ["linear_forward", "linear_backward", "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]
 
 
 def _f64(x):
@@ -95,6 +95,91 @@ def linear_forward(q, k, v, theta, eta, alpha, M0=None, S0=None, b=1, grad="l2")
             M = (1.0 - al) * M + S                     # forget, then add momentum
             z[..., t, :] = _matvec(M, q[..., t, :])    # read after this token's write
     return z, M, S
+
+
+def linear_backward(q, k, v, theta, eta, alpha, dz, dM_T=None, dS_T=None, M0=None, S0=None, b=1):
+    """Reverse-mode gradient of ``linear_forward`` (``grad="l2"``), token by token.
+
+    The outer loss is any function of the outputs; ``dz [..., T, dv]``,
+    ``dM_T, dS_T [..., dv, dk]`` (None for zero) are its derivatives with respect
+    to ``z``, ``M_T`` and ``S_T``.  Returns the derivatives with respect to every
+    input: ``dq, dk, dv, dtheta, deta, dalpha, dM0, dS0``.
+
+    The inner update is ordinary arithmetic, so its outer gradient is the chain
+    rule applied backward through the sequence of state transitions ("Continual
+    Learning: From Attention to Neural Memory", section 4.5: backpropagation
+    through time over the unrolled writes, no gradient path detached;
+    "5.1.1 · TTT layers 与 fast weights", section 1.1, eqs. (15)-(16): the
+    outer gradient of a key runs through the inner gradient it produced).
+    Each gradient of a chunk was taken at the chunk-start memory, so that
+    memory collects the key/value paths of the whole chunk before the walk
+    moves on to the previous chunk.
+
+    The forward states are recomputed and kept for every token (plain and
+    memory-hungry: small inputs only).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    theta, eta, alpha, dz = _f64(theta), _f64(eta), _f64(alpha), _f64(dz)
+    if b < 1:
+        raise ValueError("chunk size b must be >= 1")
+    lead, T, dk_ = q.shape[:-2], q.shape[-2], q.shape[-1]
+    dv_ = v.shape[-1]
+    shape = lead + (dv_, dk_)
+    M = np.zeros(shape) if M0 is None else np.array(np.broadcast_to(_f64(M0), shape))
+    S = np.zeros(shape) if S0 is None else np.array(np.broadcast_to(_f64(S0), shape))
+
+    # Forward, keeping what the reverse walk needs: the state before and after
+    # each token, and each chunk's start memory and residuals.
+    M_prev, S_prev, M_new = [], [], []
+    M_start, err = [], []
+    for c0 in range(0, T, b):
+        M_c = M.copy()
+        for t in range(c0, min(c0 + b, T)):
+            e = _matvec(M_c, k[..., t, :]) - v[..., t, :]
+            th = theta[..., t][..., None, None]
+            et = eta[..., t][..., None, None]
+            al = alpha[..., t][..., None, None]
+            M_prev.append(M)
+            S_prev.append(S)
+            M_start.append(M_c)
+            err.append(e)
+            S = et * S - th * _outer(e, k[..., t, :])
+            M = (1.0 - al) * M + S
+            M_new.append(M)
+
+    gq, gk, gv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    gth, get, gal = np.zeros_like(theta), np.zeros_like(eta), np.zeros_like(alpha)
+    gM = np.zeros(shape) if dM_T is None else np.array(np.broadcast_to(_f64(dM_T), shape))
+    gS = np.zeros(shape) if dS_T is None else np.array(np.broadcast_to(_f64(dS_T), shape))
+    starts = list(range(0, T, b))
+    for c0 in reversed(starts):
+        gMc = np.zeros(shape)                  # collects every path through M_c
+        for t in reversed(range(c0, min(c0 + b, T))):
+            q_t, k_t, dz_t = q[..., t, :], k[..., t, :], dz[..., t, :]
+            e, M_c = err[t], M_start[t]
+            th = theta[..., t][..., None, None]
+            et = eta[..., t][..., None, None]
+            al = alpha[..., t][..., None, None]
+            # z_t = M_t q_t
+            gM = gM + _outer(dz_t, q_t)
+            gq[..., t, :] = _matvec(np.swapaxes(M_new[t], -1, -2), dz_t)
+            # M_t = (1 - alpha_t) M_{t-1} + S_t
+            gS = gS + gM
+            gal[..., t] = -np.sum(gM * M_prev[t], axis=(-1, -2))
+            gM = (1.0 - al) * gM
+            # S_t = eta_t S_{t-1} - theta_t e_t k_t^T
+            G = _outer(e, k_t)
+            get[..., t] = np.sum(gS * S_prev[t], axis=(-1, -2))
+            gth[..., t] = -np.sum(gS * G, axis=(-1, -2))
+            gG = -th * gS
+            gS = et * gS
+            # G = e k^T with e = M_c k - v
+            ge = _matvec(gG, k_t)
+            gk[..., t, :] = _matvec(np.swapaxes(gG, -1, -2), e) + _matvec(np.swapaxes(M_c, -1, -2), ge)
+            gv[..., t, :] = -ge
+            gMc = gMc + _outer(ge, k_t)
+        gM = gM + gMc                          # M_c is the state entering the chunk
+    return gq, gk, gv, gth, get, gal, gM, gS
 
 
 def silu(x):
