@@ -26,7 +26,7 @@ def _run_case(inp):
     return linear_forward(
         _arr(inp["q"]), _arr(inp["k"]), _arr(inp["v"]),
         _arr(inp["theta"]), _arr(inp["eta"]), _arr(inp["alpha"]),
-        _arr(inp["M0"]), _arr(inp["S0"]), b=inp["b"], grad=inp["grad"])
+        _arr(inp["M0"]), _arr(inp["S0"]), b=inp["b"], grad=inp.get("grad", "l2"))
 
 
 def _golden_cases():
