@@ -54,6 +54,7 @@
 #ifndef TTT_MEM_H
 #define TTT_MEM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -187,13 +188,87 @@ int ttt_mem_decode_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         float* z, float* M_T, float* S_T,
                         int B, int H, int T, int d, void* stream);
 
+/*
+ * Training forward and backward pass of the linear memory.
+ *
+ * The outer loss of a model that contains the memory trains q, k, v, the gates
+ * and the initial state through the inner updates: every write is ordinary
+ * arithmetic, so its outer gradient is the chain rule applied backward through
+ * the unrolled state transitions, with no gradient path detached
+ * ("Continual Learning: From Attention to Neural Memory", section 4.5;
+ * "5.1.1 · TTT layers 与 fast weights", section 1.2, eqs. (15)-(16): the
+ * outer gradient of a key runs through the inner gradient it produced).
+ * The backward walks the chunks in reverse order, as the forward walks them
+ * forward; inside a chunk it uses the same matrix (dual) form
+ * ("论文速览 | Titans", section 4.7: chunks pass the memory state, and the
+ * backward differentiates the inner update).
+ *
+ * ttt_mem_forward_ckpt_*: the forward above, plus the state entering every
+ * chunk, which the backward differentiates from:
+ *     ckpt [B, H, NC, 2, d, d] float32, NC = ceil(T / b);
+ *     ckpt[b, h, c, 0] = M and ckpt[b, h, c, 1] = S before chunk c
+ *     (c = 0: M0 and S0, zeros for NULL).
+ * Its size in bytes is ttt_mem_ckpt_bytes(B, H, T, d, b).  ckpt is required
+ * (non-NULL, 16-byte aligned) and must not overlap any other argument.
+ *
+ * ttt_mem_backward_*: given the derivatives of the outer loss with respect
+ * to the forward's outputs,
+ *     dz [B, H, T, d] float32, dM_T, dS_T [B, H, d, d] float32 (NULL: zero),
+ * and the same q, k, v, theta, eta, alpha, B, H, T, d, b as the forward that
+ * wrote ckpt, writes the derivatives with respect to its inputs:
+ *     dq, dk, dv                 [B, H, T, d] float32 (both entry points),
+ *     dtheta, deta, dalpha       [B, H, T]    float32,
+ *     dM0, dS0                   [B, H, d, d] float32 (NULL: not written).
+ * work is a caller-owned float32 scratch buffer of ttt_mem_ckpt_bytes(B, H,
+ * T, d, b) bytes (the derivatives with respect to the state leaving every
+ * chunk); its contents on entry do not matter and on return are unspecified.
+ * The bf16 entry point takes q, k, v in bf16 and computes its matrix products
+ * with fp16 operands and float32 accumulation, as the bf16 forward does; the
+ * float32 one uses float32 products.
+ * Argument rules as for the forward: sizes, alignment (16 bytes for every
+ * array except the gate arrays and their gradients, 4 bytes), no overlap
+ * between any output and any other argument (dM0 may not alias dM_T).
+ * Two kernels run in order on `stream`: a reverse walk over the chunks per
+ * row block of the state, then one workgroup per (batch, head, chunk).
+ */
+int ttt_mem_forward_ckpt_f32(const float* q, const float* k, const float* v,
+                             const float* theta, const float* eta, const float* alpha,
+                             const float* M0, const float* S0,
+                             float* z, float* M_T, float* S_T, float* ckpt,
+                             int B, int H, int T, int d, int b, void* stream);
+
+int ttt_mem_forward_ckpt_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const float* theta, const float* eta, const float* alpha,
+                              const float* M0, const float* S0,
+                              float* z, float* M_T, float* S_T, float* ckpt,
+                              int B, int H, int T, int d, int b, void* stream);
+
+/* Bytes of ckpt (and of the backward's work buffer); 0 for negative sizes. */
+size_t ttt_mem_ckpt_bytes(int B, int H, int T, int d, int b);
+
+int ttt_mem_backward_f32(const float* q, const float* k, const float* v,
+                         const float* theta, const float* eta, const float* alpha,
+                         const float* ckpt, const float* dz, const float* dM_T, const float* dS_T,
+                         float* dq, float* dk, float* dv,
+                         float* dtheta, float* deta, float* dalpha,
+                         float* dM0, float* dS0, float* work,
+                         int B, int H, int T, int d, int b, void* stream);
+
+int ttt_mem_backward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const float* theta, const float* eta, const float* alpha,
+                          const float* ckpt, const float* dz, const float* dM_T, const float* dS_T,
+                          float* dq, float* dk, float* dv,
+                          float* dtheta, float* deta, float* dalpha,
+                          float* dM0, float* dS0, float* work,
+                          int B, int H, int T, int d, int b, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* ttt_mem_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int ttt_mem_abi_version(void);
 
-#define TTT_MEM_ABI_VERSION ((1 << 16) | 0)
+#define TTT_MEM_ABI_VERSION ((1 << 16) | 1)
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,11 @@ _SIGNATURES = {
     "ttt_mem_forward_varlen_bf16": (_I, [_P] * 12 + [_I] * 5 + [_P]),
     "ttt_mem_decode_f32": (_I, [_P] * 11 + [_I] * 4 + [_P]),
     "ttt_mem_decode_bf16": (_I, [_P] * 11 + [_I] * 4 + [_P]),
+    "ttt_mem_forward_ckpt_f32": (_I, [_P] * 12 + [_I] * 5 + [_P]),
+    "ttt_mem_forward_ckpt_bf16": (_I, [_P] * 12 + [_I] * 5 + [_P]),
+    "ttt_mem_ckpt_bytes": (ctypes.c_size_t, [_I] * 5),
+    "ttt_mem_backward_f32": (_I, [_P] * 19 + [_I] * 5 + [_P]),
+    "ttt_mem_backward_bf16": (_I, [_P] * 19 + [_I] * 5 + [_P]),
     "ttt_mem_status_string": (ctypes.c_char_p, [_I]),
     "ttt_mem_abi_version": (_I, []),
 }

@@ -100,6 +100,61 @@ __device__ __forceinline__ void tri_step(float& X, float& Y, float& W) {
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
+// ---------------------------------------------------------------------------
+// MFMA operand traits.  A "k-group" is the contraction length of one operand
+// fragment: 16 for float32 (four v_mfma_f32_16x16x4_f32, one slot each) and 32
+// for fp16 (one v_mfma_f32_16x16x32_f16, eight slots).  tmap(tile, m) is the
+// index (token or key column) that row m of a 16-row tile stands for; lane
+// group g of the fragment for k-group s carries the indices tmap(tile, 4g+i)
+// of the k-group's tiles in slot order, which is the accumulator's own row
+// order, so accumulator tiles convert to fragments lane-locally.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Op;
+
+template <>
+struct Op<float> {
+    static constexpr int KG = 16;
+    static constexpr bool kF16 = false;
+    using frag = f32x4;
+    __device__ static int tmap(int tile, int m) { return 16 * tile + m; }
+    __device__ static f32x4 mma(f32x4 acc, const frag& a, const frag& b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+        return acc;
+    }
+    template <int NTILES>
+    __device__ static frag from_acc(const f32x4* tiles, int s) { return tiles[s]; }
+};
+
+template <>
+struct Op<_Float16> {
+    static constexpr int KG = 32;
+    static constexpr bool kF16 = true;
+    using frag = f16x8;
+    __device__ static int tmap(int tile, int m) {
+        return 32 * (tile >> 1) + 8 * (m >> 2) + 4 * (tile & 1) + (m & 3);
+    }
+    __device__ static f32x4 mma(f32x4 acc, const frag& a, const frag& b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    }
+    template <int NTILES>
+    __device__ static frag from_acc(const f32x4* tiles, int s) {
+        const f32x4 lo = tiles[2 * s];
+        const f32x4 hi = (2 * s + 1 < NTILES) ? tiles[2 * s + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f16x4 a = cvt4(lo), b = cvt4(hi);
+        return frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+};
+
+// Global-memory element types: float for the f32 path, raw bf16 bits for the
+// bf16-input path (whose matrix operands are fp16).
+template <typename T> struct GlobalOf;
+template <> struct GlobalOf<float> { using type = float; };
+template <> struct GlobalOf<_Float16> { using type = uint16_t; };
+
 // Host-side pointer checks.
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
@@ -107,6 +162,14 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     if (!a || !b) return false;
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
     return x < y + nb && y < x + na;
+}
+
+// Bytes of the chunk-start state checkpoints of a dense [B, H, T] problem:
+// [B*H][ceil(T/b)][M | S][d][d] float32 (0 for sizes no entry point accepts).
+size_t ckpt_bytes(int B, int H, int T, int d, int b) {
+    if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1) return 0;
+    const size_t nch = (static_cast<size_t>(T) + b - 1) / b;
+    return static_cast<size_t>(B) * H * nch * 2 * d * d * sizeof(float);
 }
 
 }  // namespace

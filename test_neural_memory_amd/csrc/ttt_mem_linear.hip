@@ -135,60 +135,7 @@ __device__ __forceinline__ int gam_swz(int i) {
     return sw & (NP / 4 - 1);
 }
 
-// ---------------------------------------------------------------------------
-// MFMA operand traits.  A "k-group" is the contraction length of one operand
-// fragment: 16 for float32 (four v_mfma_f32_16x16x4_f32, one slot each) and 32
-// for fp16 (one v_mfma_f32_16x16x32_f16, eight slots).  tmap(tile, m) is the
-// index (token or key column) that row m of a 16-row tile stands for; lane
-// group g of the fragment for k-group s carries the indices tmap(tile, 4g+i)
-// of the k-group's tiles in slot order, which is the accumulator's own row
-// order, so accumulator tiles convert to fragments lane-locally.
-// ---------------------------------------------------------------------------
-template <typename T>
-struct Op;
 
-template <>
-struct Op<float> {
-    static constexpr int KG = 16;
-    static constexpr bool kF16 = false;
-    using frag = f32x4;
-    __device__ static int tmap(int tile, int m) { return 16 * tile + m; }
-    __device__ static f32x4 mma(f32x4 acc, const frag& a, const frag& b) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
-        return acc;
-    }
-    template <int NTILES>
-    __device__ static frag from_acc(const f32x4* tiles, int s) { return tiles[s]; }
-};
-
-template <>
-struct Op<_Float16> {
-    static constexpr int KG = 32;
-    static constexpr bool kF16 = true;
-    using frag = f16x8;
-    __device__ static int tmap(int tile, int m) {
-        return 32 * (tile >> 1) + 8 * (m >> 2) + 4 * (tile & 1) + (m & 3);
-    }
-    __device__ static f32x4 mma(f32x4 acc, const frag& a, const frag& b) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-    }
-    template <int NTILES>
-    __device__ static frag from_acc(const f32x4* tiles, int s) {
-        const f32x4 lo = tiles[2 * s];
-        const f32x4 hi = (2 * s + 1 < NTILES) ? tiles[2 * s + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f16x4 a = cvt4(lo), b = cvt4(hi);
-        return frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    }
-};
-
-// Global-memory element types: float for the f32 path, raw bf16 bits for the
-// bf16-input path (whose matrix operands are fp16).
-template <typename T> struct GlobalOf;
-template <> struct GlobalOf<float> { using type = float; };
-template <> struct GlobalOf<_Float16> { using type = uint16_t; };
 
 
 // row_newbcast:N -- every lane of a 16-lane row receives lane N of that row
@@ -220,6 +167,9 @@ struct Params {
     // its state is slot s * H + h.
     const int* cu;
     int H;
+    // Chunk-start states for the backward pass (NULL: not written), dense
+    // sequences only: [B*H][ceil(T/b)][M | S][d][d] float32.
+    float* ckpt;
 };
 
 // Compile-time geometry of one kernel instance: NS 16-row tiles per
@@ -1248,6 +1198,22 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
             Macc[cw] = (p.M0 && ok) ? *reinterpret_cast<const f32x4*>(p.M0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
             Sacc[cw] = (p.S0 && ok) ? *reinterpret_cast<const f32x4*>(p.S0 + state_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // Checkpoint of the state entering chunk c (what the backward pass
+        // differentiates from), in the layout of M_T / S_T.
+        auto save = [&](int c) {
+            if (p.ckpt) {
+                float* base = p.ckpt + (static_cast<size_t>(bh) * nch + c) * (2 * D * D) +
+                              static_cast<size_t>(row + lr) * D;
+#pragma unroll
+                for (int cw = 0; cw < Gm::NCW; ++cw) {
+                    const int col = O::tmap(x.chi * Gm::NCW + cw, 4 * lg);
+                    if (col < D) {
+                        *reinterpret_cast<f32x4*>(base + col) = Macc[cw];
+                        *reinterpret_cast<f32x4*>(base + D * D + col) = Sacc[cw];
+                    }
+                }
+            }
+        };
         F MB[Gm::NKCW], SB[Gm::NKCW];
         f32x4 E[Gm::NTW], Zp[Gm::NTW];
         K::own_frags(x, sm, Macc, Sacc, MB, SB);
@@ -1265,6 +1231,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
                                               static_cast<uint32_t>(chunk_n(c)) * D * 4);
                     const uint32_t gs = a.g + static_cast<uint32_t>(c & 3) * K::kGateB;
                     const uint32_t gsc = lds_addr(&sm.rg[c & 3].scal[0]);
+                    save(c);
                     K::template phaseA2<0>(a, gs, gsc, MB, SB, E, Zp, Macc, Sacc);
                     __syncthreads();
                     K::template phaseB2<0>(a, Macc, Sacc, MB, SB, Zp, rz, zoff);
@@ -1275,6 +1242,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
                                               static_cast<uint32_t>(chunk_n(c + 1)) * D * 4);
                     const uint32_t gs = a.g + static_cast<uint32_t>((c + 1) & 3) * K::kGateB;
                     const uint32_t gsc = lds_addr(&sm.rg[(c + 1) & 3].scal[0]);
+                    save(c + 1);
                     K::template phaseA2<1>(a, gs, gsc, MB, SB, E, Zp, Macc, Sacc);
                     __syncthreads();
                     K::template phaseB2<1>(a, Macc, Sacc, MB, SB, Zp, rz, zoff);
@@ -1291,6 +1259,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
                 const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
                                           static_cast<uint32_t>(chunk_n(c)) * D * 4);
                 const typename K::ReadGates& rg = sm.rg[c & 3];
+                save(c);
                 K::phaseA(x, B, rg, sm, MB, SB, E, Zp);
                 __syncthreads();
                 K::phaseB(x, B, rg, sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
@@ -1307,6 +1276,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
                 __syncthreads();   // chunk c P tiles
                 const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
                                           static_cast<uint32_t>(chunk_n(c)) * D * 4);
+                save(c);
                 K::phaseA(x, sm.buf[0], sm.rg[c & 3], sm, MB, SB, E, Zp);
                 __syncthreads();
                 K::phaseB(x, sm.buf[0], sm.rg[c & 3], sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
@@ -1390,7 +1360,7 @@ hipError_t dispatch(const Params& p, int d, hipStream_t stream) {
 template <typename T>
 int forward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
                  const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
-                 int B, int H, int Tlen, int d, int b, void* stream) {
+                 float* ckpt, int B, int H, int Tlen, int d, int b, void* stream) {
     using G = typename GlobalOf<T>::type;
     if (B < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
     if (b < 1) return TTT_ERR_INVALID_ARG;
@@ -1427,8 +1397,22 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
     if (S_T && S_T != S0 && (overlaps(S_T, st_bytes, S0, st_bytes) || overlaps(S_T, st_bytes, M0, st_bytes)))
         return TTT_ERR_INVALID_ARG;
     if (M_T && S_T && overlaps(M_T, st_bytes, S_T, st_bytes)) return TTT_ERR_INVALID_ARG;
+    if (ckpt) {
+        // Written while the inputs are read and the outputs written: no overlap with any of them.
+        const size_t ck_bytes = ckpt_bytes(B, H, Tlen, d, b);
+        if (!aligned(ckpt, 16)) return TTT_ERR_INVALID_ARG;
+        const void* ins[] = {q, k, v};
+        for (const void* in : ins)
+            if (overlaps(ckpt, ck_bytes, in, in_bytes)) return TTT_ERR_INVALID_ARG;
+        const void* gates[] = {theta, eta, alpha};
+        for (const void* g : gates)
+            if (overlaps(ckpt, ck_bytes, g, tok * sizeof(float))) return TTT_ERR_INVALID_ARG;
+        for (const void* s : states)
+            if (overlaps(ckpt, ck_bytes, s, st_bytes)) return TTT_ERR_INVALID_ARG;
+        if (overlaps(ckpt, ck_bytes, z, z_bytes)) return TTT_ERR_INVALID_ARG;
+    }
 
-    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, nullptr, H};
+    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, nullptr, H, ckpt};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1479,7 +1463,7 @@ int forward_varlen_impl(const void* q, const void* k, const void* v, const float
     if (M_T && S_T && overlaps(M_T, st_bytes, S_T, st_bytes)) return TTT_ERR_INVALID_ARG;
     if (overlaps(M_T, st_bytes, cu, cu_bytes) || overlaps(S_T, st_bytes, cu, cu_bytes)) return TTT_ERR_INVALID_ARG;
 
-    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H};
+    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H, nullptr};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1491,13 +1475,13 @@ extern "C" {
 int ttt_mem_forward_f32(const float* q, const float* k, const float* v, const float* theta, const float* eta,
                         const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
                         int B, int H, int T, int d, int b, void* stream) {
-    return forward_impl<float>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, B, H, T, d, b, stream);
+    return forward_impl<float>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, nullptr, B, H, T, d, b, stream);
 }
 
 int ttt_mem_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
                          const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
                          float* M_T, float* S_T, int B, int H, int T, int d, int b, void* stream) {
-    return forward_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, B, H, T, d, b, stream);
+    return forward_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, nullptr, B, H, T, d, b, stream);
 }
 
 int ttt_mem_forward_varlen_f32(const float* q, const float* k, const float* v, const float* theta, const float* eta,
@@ -1514,6 +1498,22 @@ int ttt_mem_forward_varlen_bf16(const uint16_t* q, const uint16_t* k, const uint
     return forward_varlen_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, cu_seqlens, N, H, T, d, b,
                                          stream);
 }
+
+int ttt_mem_forward_ckpt_f32(const float* q, const float* k, const float* v, const float* theta, const float* eta,
+                             const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
+                             float* ckpt, int B, int H, int T, int d, int b, void* stream) {
+    if (!ckpt) return TTT_ERR_INVALID_ARG;
+    return forward_impl<float>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, ckpt, B, H, T, d, b, stream);
+}
+
+int ttt_mem_forward_ckpt_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                              const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
+                              float* M_T, float* S_T, float* ckpt, int B, int H, int T, int d, int b, void* stream) {
+    if (!ckpt) return TTT_ERR_INVALID_ARG;
+    return forward_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, ckpt, B, H, T, d, b, stream);
+}
+
+size_t ttt_mem_ckpt_bytes(int B, int H, int T, int d, int b) { return ckpt_bytes(B, H, T, d, b); }
 
 const char* ttt_mem_status_string(int status) {
     switch (status) {

@@ -1,0 +1,1118 @@
+// Backward pass of the chunked TTT / Titans linear memory for gfx950 (MI355X),
+// and its C ABI.
+//
+// The outer gradient of the memory is the chain rule run backward through the
+// unrolled writes ("Continual Learning: From Attention to Neural Memory",
+// section 4.5; "5.1.1 · TTT layers 与 fast weights", section 1.2, eqs. (15)-(16)).
+// Chunk by chunk the forward is an affine map of the state, so the backward
+// is its transpose, walked from the last chunk to the first ("论文速览 |
+// Titans", section 4.7).
+//
+// One chunk, tokens i = 0..n-1, start state (M0, S0), gates as in the forward
+// (a = 1 - alpha):
+//   A_i = prod_{l<=i} a_l,  E_i = prod_{l<=i} eta_l,  c_i = a_i c_{i-1} + E_i,
+//   gamma_ij (j <= i): gamma_jj = 1, gamma_ij = a_i gamma_{i-1,j} + p_ij,
+//                      p_jj = 1,     p_ij = eta_i p_{i-1,j},
+//   L_ij = theta_j gamma_ij,  w^M_j = L_{n-1,j},  w^S_j = theta_j p_{n-1,j},
+//   E  = K M0^T - V                              (residuals, row j = e_j)
+//   Z  = diag(A) Q M0^T + diag(c) Q S0^T - P E,  P = (Q K^T) .* L (lower, diagonal included)
+//   M' = A_{n-1} M0 + c_{n-1} S0 - E^T diag(w^M) K
+//   S' = E_{n-1} S0 - E^T diag(w^S) K.
+// Given dZ, dM', dS' (the derivatives of the outer loss):
+//   dE  = -P^T dZ - diag(w^M) K dM'^T - diag(w^S) K dS'^T,   dV = -dE
+//   dM0 = A_{n-1} dM' + dZ^T diag(A) Q + dE^T K
+//   dS0 = c_{n-1} dM' + E_{n-1} dS' + dZ^T diag(c) Q
+//   D   = dZ E^T,   DL = D .* L
+//   dQ  = diag(A) dZ M0 + diag(c) dZ S0 - DL K
+//   dK  = -DL^T Q + dE M0 - diag(w^M) E dM' - diag(w^S) E dS'
+// and the gates through the scalar cotangents
+//   dA_i = q_i . (M0^T dz_i),  dc_i = q_i . (S0^T dz_i)  (plus <dM',M0>, <dM',S0> at i = n-1),
+//   dE_{n-1} = <dS',S0>,  dL_ij = -(q_i . k_j) D_ij (plus -e_j^T dM' k_j on row n-1),
+//   dw^S_j = -e_j^T dS' k_j,
+// run backward through the products and the column recurrences of gamma
+// (division-free, so gates equal to 0 are exact).
+//
+// The (dM, dS) carry needs only q, k, dz and the gates; everything else of a
+// chunk needs the chunk's own start state and end cotangent.  Hence two
+// kernels:
+//   * carry: one workgroup per (sequence, block of 16*NS rows of the state),
+//     reverse walk over the chunks with dM, dS in MFMA accumulators (rows of
+//     the memory never meet, as in the forward); writes dV and the cotangent
+//     leaving every chunk to a work buffer.  Producer waves stage the next
+//     chunks and build P, one and two chunks ahead.
+//   * grads: one workgroup per (sequence, chunk), fully parallel; reads the
+//     chunk-start state saved by the forward and the cotangent from the work
+//     buffer; computes dQ, dK and the gate gradients with the whole feature
+//     dimension on chip.
+//
+// Precision: as the forward.  The float32 path uses float32 MFMA; the bf16
+// path uses fp16 operands (bf16 inputs convert exactly in the fp16 normal
+// range; states, cotangents and P are rounded to fp16 where they enter a
+// product) with float32 accumulation, float32 carried cotangents and float32
+// gate arithmetic.
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ttt_mem.h"
+#include "gfx950.h"
+
+namespace {
+
+constexpr int kW = 64;
+constexpr int kLdsMax = 160 * 1024;
+
+__host__ __device__ constexpr int bmax(int a, int b) { return a > b ? a : b; }
+
+// Earlier LDS accesses of this wave have completed (same-wave hand-over of
+// LDS data between lanes).
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Fragment loads for the MFMA operand traits Op<T> (k-groups of KG, KS slots
+// per lane: lane (lr, lg) holds k-slots KS*lg .. KS*lg + KS - 1).
+template <typename T>
+struct Fr {
+    using O = Op<T>;
+    using F = typename O::frag;
+    static constexpr int KG = O::KG;
+    static constexpr int KS = KG / 4;
+
+    // Row-major LDS tile X (LD elements per row): lane (lr, lg) gets
+    // X[row][k0 + KS*lg + s], s < KS (one 16-byte read).
+    __device__ static F rm(const T* X, int LD, int row, int k0, int lg) {
+        return *reinterpret_cast<const F*>(X + row * LD + k0 + KS * lg);
+    }
+    // Transposed read: lane (lr, lg) gets X[k0 + KS*lg + s][c0 + lr].
+    __device__ static F cm(const T* X, int LD, int k0, int c0, int lr, int lg) {
+        if constexpr (O::kF16) {
+            return tr(X, LD, k0 + 8 * lg + (lr >> 2), c0 + 4 * (lr & 3));
+        } else {
+            const T* p = X + (k0 + 4 * lg) * LD + c0 + lr;
+            return F{p[0], p[LD], p[2 * LD], p[3 * LD]};
+        }
+    }
+    // Transposed read whose rows stand for the tmap order of column tile ct:
+    // lane (lr, lg) gets X[k0 + KS*lg + s][tmap(ct, lr)].
+    __device__ static F cm_t(const T* X, int LD, int k0, int ct, int lr, int lg) {
+        if constexpr (O::kF16) {
+            return tr(X, LD, k0 + 8 * lg + (lr >> 2), 32 * (ct >> 1) + 8 * (lr & 3) + 4 * (ct & 1));
+        } else {
+            return cm(X, LD, k0, 16 * ct, lr, lg);
+        }
+    }
+    // Two LDS transpose loads: within each 16-lane group, lane i receives
+    // column (its reader's base + i % 4) of rows row0 + 0..3 and row0 + 4..7.
+    __device__ static F tr(const T* X, int LD, int row0, int col) {
+        const i16x4 lo = ds_read_tr16(X + row0 * LD + col);
+        const i16x4 hi = ds_read_tr16(X + (row0 + 4) * LD + col);
+        const f16x4 a = __builtin_bit_cast(f16x4, lo), b = __builtin_bit_cast(f16x4, hi);
+        return F{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+    // KS float32 values -> fragment (fp16: round to nearest even).
+    __device__ static F from_f32(const float* x) {
+        if constexpr (O::kF16) {
+            const f16x4 a = cvt4(f32x4{x[0], x[1], x[2], x[3]}), b = cvt4(f32x4{x[4], x[5], x[6], x[7]});
+            return F{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        } else {
+            return F{x[0], x[1], x[2], x[3]};
+        }
+    }
+    // Fragment times KS per-slot float32 factors.
+    __device__ static F scale(const F& f, const float* w) {
+        F r;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) r[s] = static_cast<T>(static_cast<float>(f[s]) * w[s]);
+        return r;
+    }
+};
+
+// Four float32 values -> four elements of T at an LDS address (8 or 16 bytes).
+template <typename T>
+__device__ __forceinline__ void st4(T* dst, f32x4 v) {
+    if constexpr (Op<T>::kF16) {
+        *reinterpret_cast<f16x4*>(dst) = cvt4(v);
+    } else {
+        *reinterpret_cast<f32x4*>(dst) = v;
+    }
+}
+template <typename T>
+__device__ __forceinline__ f32x4 ld4(const T* src) {
+    if constexpr (Op<T>::kF16) {
+        const f16x4 h = *reinterpret_cast<const f16x4*>(src);
+        return f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
+                     static_cast<float>(h[3])};
+    } else {
+        return *reinterpret_cast<const f32x4*>(src);
+    }
+}
+
+// One 16-byte unit of a global input row (8 bf16 or 4 float32) -> LDS as T
+// (zeros when !ok).
+template <typename T>
+__device__ __forceinline__ void stage_unit(T* dst, const typename GlobalOf<T>::type* src, bool ok) {
+    const uint4 u = ok ? *reinterpret_cast<const uint4*>(src) : uint4{0u, 0u, 0u, 0u};
+    if constexpr (Op<T>::kF16) {
+        const f16x4 a = cvt4(f32x4{bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y)});
+        const f16x4 b = cvt4(f32x4{bf16lo(u.z), bf16hi(u.z), bf16lo(u.w), bf16hi(u.w)});
+        *reinterpret_cast<f16x8*>(dst) = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+        *reinterpret_cast<uint4*>(dst) = u;
+    }
+}
+
+// Four input elements (bf16 or float32) of a global row as float32.
+template <typename T>
+__device__ __forceinline__ f32x4 gload4(const typename GlobalOf<T>::type* src) {
+    if constexpr (Op<T>::kF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(src);
+        return f32x4{bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y)};
+    } else {
+        return *reinterpret_cast<const f32x4*>(src);
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < kW; m <<= 1) x += __shfl_xor(x, m, kW);
+    return x;
+}
+
+// Chunk gates of one wave (lane = token l of a chunk padded to NP tokens with
+// theta = 0, eta = a = 1): prefix products A_l, E_l and c_l.
+template <int NP>
+__device__ __forceinline__ void gate_prefix(float my_a, float my_et, int l, float& A, float& E, float& c) {
+    A = 1.f;
+    E = 1.f;
+    c = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const float ai = readlane(my_a, i), ei = readlane(my_et, i);
+        if (i <= l) {
+            A *= ai;
+            E *= ei;
+            c = ai * c + E;
+        }
+    }
+}
+
+// ===========================================================================
+// Carry kernel: reverse walk over the chunks, (dM, dS) per row block.
+// ===========================================================================
+struct CarryParams {
+    const void* q;
+    const void* k;
+    const float* dz;
+    const float* theta;
+    const float* eta;
+    const float* alpha;
+    const float* dMT;   // NULL: zero
+    const float* dST;
+    float* work;        // [BH][nch][dM | dS][D][D]: cotangent leaving each chunk
+    float* dv;          // [BH][T][D]
+    float* dM0;         // NULL: not written
+    float* dS0;
+    int BH;
+    int T;
+    int b;
+    int nch;
+};
+
+template <typename T, int D, int NS, int NP>
+struct CarryGeo {
+    using O = Op<T>;
+    static constexpr int KG = O::KG;
+    static constexpr int DS = bmax(D, KG);      // stored feature width (fp16: >= one k-group)
+    static constexpr int RB = 16 * NS;          // rows of the state per workgroup
+    static constexpr int NRB = D / RB;
+    static constexpr int NT = NP / 16;
+    static constexpr int NKD = DS / KG;
+    static constexpr int NKT = NP / KG;
+    static constexpr int NCT = DS / 16;         // 16-column tiles of the state
+    static constexpr int PAD = 16 / (int)sizeof(T);
+    static constexpr int LQ = DS + PAD;
+    static constexpr int LZ = RB + PAD;
+    static constexpr int LP = NP + PAD;
+    static constexpr int LF = NP + 4;
+    static constexpr int QSLOT = (2 * NP * LQ + NP * LZ) * (int)sizeof(T) + 3 * NP * 4;
+    static constexpr int PSLOT = NP * LP * (int)sizeof(T) + 4 * NP * 4 + 16;
+    static constexpr int LS = NP * LF * 4;
+    // Three staging slots (state waves, P builder and loader each on their
+    // own chunk, one barrier per chunk) when they fit; else one slot and a
+    // serial schedule.
+    static constexpr int NQ = (3 * QSLOT + 2 * PSLOT + LS + 1024 <= kLdsMax) ? 3 : 1;
+    static constexpr int NPR = NQ == 3 ? 2 : 1;
+    static constexpr int NWAVE = NS + 2;
+    static_assert(NQ * QSLOT + NPR * PSLOT + LS + 1024 <= kLdsMax, "LDS budget");
+    static_assert(D % RB == 0 && NP % KG == 0, "tiling");
+};
+
+template <typename T, int D, int NS, int NP>
+struct CarrySmem {
+    using Gm = CarryGeo<T, D, NS, NP>;
+    struct QSlot {
+        alignas(16) T q[NP * Gm::LQ];
+        alignas(16) T k[NP * Gm::LQ];
+        alignas(16) T dz[NP * Gm::LZ];     // dz columns of the workgroup's rows
+        alignas(16) float th[NP];
+        alignas(16) float et[NP];
+        alignas(16) float av[NP];
+    };
+    struct PSlot {
+        alignas(16) T pt[NP * Gm::LP];     // P^T: row t holds P[i][t] over i
+        alignas(16) float A[NP];
+        alignas(16) float c[NP];
+        alignas(16) float wm[NP];
+        alignas(16) float ws[NP];
+        alignas(16) float scal[4];         // A_{n-1}, c_{n-1}, E_{n-1}
+    };
+    QSlot qs[Gm::NQ];
+    PSlot ps[Gm::NPR];
+    alignas(16) float ls[NP * Gm::LF];     // L_ij = theta_j gamma_ij (builder only)
+};
+
+template <typename T, int D, int NS, int NP>
+struct Carry {
+    using Gm = CarryGeo<T, D, NS, NP>;
+    using O = Op<T>;
+    using R = Fr<T>;
+    using F = typename O::frag;
+    using G = typename GlobalOf<T>::type;
+    using Sm = CarrySmem<T, D, NS, NP>;
+    static constexpr int KG = Gm::KG, KS = R::KS, LQ = Gm::LQ, LZ = Gm::LZ, LP = Gm::LP, LF = Gm::LF;
+
+    // Stage chunk c: q, k rows (all features), dz columns row0..row0+RB-1, raw gates.
+    __device__ static void load(const CarryParams& p, typename Sm::QSlot& s, size_t tok0, int n, int row0,
+                                int lane) {
+        constexpr int CB = 16 / (int)sizeof(G);       // elements per 16-byte unit
+        constexpr int UR = Gm::DS / CB;              // units per row
+        const G* q = static_cast<const G*>(p.q);
+        const G* k = static_cast<const G*>(p.k);
+        for (int u = lane; u < NP * UR; u += kW) {
+            const int t = u / UR, col = (u % UR) * CB;
+            const bool ok = t < n && col < D;
+            const size_t g = (tok0 + t) * D + col;
+            stage_unit<T>(s.q + t * LQ + col, q + (ok ? g : 0), ok);
+            stage_unit<T>(s.k + t * LQ + col, k + (ok ? g : 0), ok);
+        }
+        constexpr int UZ = Gm::RB / 4;
+        for (int u = lane; u < NP * UZ; u += kW) {
+            const int t = u / UZ, col = (u % UZ) * 4;
+            const f32x4 v = t < n ? *reinterpret_cast<const f32x4*>(p.dz + (tok0 + t) * D + row0 + col)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+            st4<T>(s.dz + t * LZ + col, v);
+        }
+        for (int l = lane; l < NP; l += kW) {
+            const bool ok = l < n;
+            s.th[l] = ok ? p.theta[tok0 + l] : 0.f;
+            s.et[l] = ok ? p.eta[tok0 + l] : 1.f;
+            s.av[l] = ok ? 1.f - p.alpha[tok0 + l] : 1.f;
+        }
+    }
+
+    // Gates, decay matrix and P^T of one staged chunk.
+    __device__ static void build(const typename Sm::QSlot& s, typename Sm::PSlot& ps, float* ls, int n, int lane) {
+        const int lr = lane & 15, lg = lane >> 4;
+        const float my_th = s.th[lane % NP], my_et = s.et[lane % NP], my_a = s.av[lane % NP];
+        float A, E, c;
+        gate_prefix<NP>(my_a, my_et, lane, A, E, c);
+        if (lane < NP) {
+            ps.A[lane] = A;
+            ps.c[lane] = c;
+        }
+        const float An = readlane(A, n - 1), cn = readlane(c, n - 1), En = readlane(E, n - 1);
+        if (lane == 0) {
+            ps.scal[0] = An;
+            ps.scal[1] = cn;
+            ps.scal[2] = En;
+        }
+        // Column j = lane of gamma and p.
+        float g = 0.f, pp = 0.f, wm = 0.f, ws = 0.f;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const float ai = readlane(my_a, i), ei = readlane(my_et, i);
+            if (i == lane) {
+                pp = 1.f;
+                g = 1.f;
+            } else if (i > lane) {
+                pp = ei * pp;
+                g = ai * g + pp;
+            }
+            if (lane < NP) ls[i * LF + lane] = my_th * g;
+            if (i == n - 1) {
+                wm = my_th * g;
+                ws = my_th * pp;
+            }
+        }
+        if (lane < NP) {
+            ps.wm[lane] = wm;
+            ps.ws[lane] = ws;
+        }
+        wave_lds_fence();
+        // P^T tiles: G[i][t] = q_i . k_t on the lower tiles, times L_it.
+#pragma unroll
+        for (int it = 0; it < Gm::NT; ++it) {
+#pragma unroll
+            for (int tt = 0; tt < Gm::NT; ++tt) {
+                const int t = 16 * tt + lr;
+                T* dst = ps.pt + t * LP + 16 * it + 4 * lg;
+                if (tt > it) {
+                    st4<T>(dst, f32x4{0.f, 0.f, 0.f, 0.f});
+                    continue;
+                }
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < Gm::NKD; ++kk)
+                    acc = O::mma(acc, R::rm(s.q, LQ, 16 * it + lr, kk * KG, lg), R::rm(s.k, LQ, t, kk * KG, lg));
+                f32x4 pv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * it + 4 * lg + e;
+                    pv[e] = t <= i ? acc[e] * ls[i * LF + t] : 0.f;
+                }
+                st4<T>(dst, pv);
+            }
+        }
+    }
+};
+
+template <typename T, int D, int NS, int NP>
+__global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_memory_bwd_carry(const CarryParams p) {
+    using Gm = CarryGeo<T, D, NS, NP>;
+    using C = Carry<T, D, NS, NP>;
+    using O = Op<T>;
+    using R = Fr<T>;
+    using F = typename O::frag;
+    constexpr int KG = Gm::KG, KS = R::KS, NT = Gm::NT, NKD = Gm::NKD, NKT = Gm::NKT, NCT = Gm::NCT;
+
+    __shared__ __attribute__((aligned(16))) typename C::Sm sm;
+
+    const int w = threadIdx.x / kW;
+    const int lane = threadIdx.x % kW;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nwg = gridDim.x;
+    int lin = blockIdx.x;
+    if ((p.BH % 8) == 0) lin = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;   // row blocks of a sequence on one XCD
+    const int bh = lin / Gm::NRB;
+    const int rb = lin % Gm::NRB;
+    const int row_wg = rb * Gm::RB;
+    const int nch = p.nch;
+    const size_t seq_tok = static_cast<size_t>(bh) * p.T;
+    auto chunk_of = [&](int u) { return nch - 1 - u; };
+    auto chunk_n = [&](int c) { return min(p.b, p.T - c * p.b); };
+
+    const bool is_state = w < NS;
+    const bool is_loader = w == NS;
+    const bool is_builder = w == NS + 1;
+
+    auto do_load = [&](int u) {
+        const int c = chunk_of(u);
+        C::load(p, sm.qs[u % Gm::NQ], seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane);
+    };
+    auto do_build = [&](int u) {
+        const int c = chunk_of(u);
+        C::build(sm.qs[u % Gm::NQ], sm.ps[u % Gm::NPR], sm.ls, chunk_n(c), lane);
+    };
+
+    // State wave: rows r0 .. r0+15 of dM, dS as accumulator tiles of dM^T
+    // (tile jt, row m -> column tmap(jt, m) of dM; lane column -> row r0 + lr).
+    f32x4 dM[NCT], dS[NCT];
+    const int r0l = 16 * w;
+    const int r0 = row_wg + r0l;
+    const size_t st_off = static_cast<size_t>(bh) * D * D + static_cast<size_t>(r0 + lr) * D;
+    if (is_state) {
+#pragma unroll
+        for (int jt = 0; jt < NCT; ++jt) {
+            const int col = O::tmap(jt, 4 * lg);
+            const bool ok = col < D;
+            dM[jt] = (p.dMT && ok) ? *reinterpret_cast<const f32x4*>(p.dMT + st_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+            dS[jt] = (p.dST && ok) ? *reinterpret_cast<const f32x4*>(p.dST + st_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    auto do_state = [&](int u) {
+        const int c = chunk_of(u);
+        const int n = chunk_n(c);
+        const size_t tok0 = seq_tok + static_cast<size_t>(c) * p.b;
+        const typename C::Sm::QSlot& s = sm.qs[u % Gm::NQ];
+        const typename C::Sm::PSlot& ps = sm.ps[u % Gm::NPR];
+        // Cotangent of the state leaving chunk c.
+        {
+            float* base = p.work + (static_cast<size_t>(bh) * nch + c) * (2 * D * D) + static_cast<size_t>(r0 + lr) * D;
+#pragma unroll
+            for (int jt = 0; jt < NCT; ++jt) {
+                const int col = O::tmap(jt, 4 * lg);
+                if (col < D) {
+                    *reinterpret_cast<f32x4*>(base + col) = dM[jt];
+                    *reinterpret_cast<f32x4*>(base + D * D + col) = dS[jt];
+                }
+            }
+        }
+        F MB[NKD], SB[NKD], ZC[NKT];
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) {
+            MB[kk] = O::template from_acc<NCT>(dM, kk);
+            SB[kk] = O::template from_acc<NCT>(dS, kk);
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKT; ++kk) ZC[kk] = R::cm(s.dz, Gm::LZ, kk * KG, r0l, lr, lg);
+        // dE (tokens x own rows): -w^M K dM^T - w^S K dS^T - P^T dZ.
+        f32x4 dE[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int trow = O::tmap(tt, lr);
+            f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = x1, x3 = x1;
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) {
+                const F kf = R::rm(s.k, Gm::LQ, trow, kk * KG, lg);
+                x1 = O::mma(x1, kf, MB[kk]);
+                x2 = O::mma(x2, kf, SB[kk]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKT; ++kk) x3 = O::mma(x3, R::rm(ps.pt, Gm::LP, trow, kk * KG, lg), ZC[kk]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = O::tmap(tt, 4 * lg + e);
+                dE[tt][e] = -(ps.wm[t] * x1[e] + ps.ws[t] * x2[e] + x3[e]);
+                if (t < n) p.dv[(tok0 + t) * D + r0 + lr] = -dE[tt][e];
+            }
+        }
+        // Carry: dM <- A dM + Q^T diag(A) dZ + K^T dE, dS <- c dM + E dS + Q^T diag(c) dZ.
+        F DE[NKT], ZA[NKT], ZK[NKT];
+#pragma unroll
+        for (int kk = 0; kk < NKT; ++kk) {
+            DE[kk] = O::template from_acc<NT>(dE, kk);
+            float av[KS], cv[KS];
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) {
+                av[s2] = ps.A[kk * KG + KS * lg + s2];
+                cv[s2] = ps.c[kk * KG + KS * lg + s2];
+            }
+            ZA[kk] = R::scale(ZC[kk], av);
+            ZK[kk] = R::scale(ZC[kk], cv);
+        }
+        const float An = ps.scal[0], cn = ps.scal[1], En = ps.scal[2];
+#pragma unroll
+        for (int jt = 0; jt < NCT; ++jt) {
+            f32x4 nM = An * dM[jt];
+            f32x4 nS = cn * dM[jt] + En * dS[jt];
+#pragma unroll
+            for (int kk = 0; kk < NKT; ++kk) {
+                const F qf = R::cm_t(s.q, Gm::LQ, kk * KG, jt, lr, lg);
+                const F kf = R::cm_t(s.k, Gm::LQ, kk * KG, jt, lr, lg);
+                nM = O::mma(nM, qf, ZA[kk]);
+                nM = O::mma(nM, kf, DE[kk]);
+                nS = O::mma(nS, qf, ZK[kk]);
+            }
+            dM[jt] = nM;
+            dS[jt] = nS;
+        }
+    };
+
+    if constexpr (Gm::NQ == 3) {
+        if (is_loader && nch > 0) do_load(0);
+        __syncthreads();
+        if (is_builder && nch > 0) do_build(0);
+        if (is_loader && nch > 1) do_load(1);
+        __syncthreads();
+        for (int u = 0; u < nch; ++u) {
+            if (is_state) do_state(u);
+            else if (is_builder) {
+                if (u + 1 < nch) do_build(u + 1);
+            } else if (u + 2 < nch) {
+                do_load(u + 2);
+            }
+            __syncthreads();
+        }
+    } else {
+        for (int u = 0; u < nch; ++u) {
+            if (is_loader) do_load(u);
+            __syncthreads();
+            if (is_builder) do_build(u);
+            __syncthreads();
+            if (is_state) do_state(u);
+            __syncthreads();
+        }
+    }
+
+    if (is_state) {
+#pragma unroll
+        for (int jt = 0; jt < NCT; ++jt) {
+            const int col = O::tmap(jt, 4 * lg);
+            if (col < D) {
+                if (p.dM0) *reinterpret_cast<f32x4*>(p.dM0 + st_off + col) = dM[jt];
+                if (p.dS0) *reinterpret_cast<f32x4*>(p.dS0 + st_off + col) = dS[jt];
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// Gradient kernel: one workgroup per (sequence, chunk).
+// ===========================================================================
+struct GradParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* theta;
+    const float* eta;
+    const float* alpha;
+    const float* ckpt;   // [BH][nch][M | S][D][D]: state entering each chunk
+    const float* work;   // [BH][nch][dM | dS][D][D]: cotangent leaving each chunk
+    const float* dz;
+    const float* dv;
+    float* dq;
+    float* dk;
+    float* dth;
+    float* deta;
+    float* dal;
+    int BH;
+    int T;
+    int b;
+    int nch;
+};
+
+template <typename T, int D, int NP>
+struct GradGeo {
+    using O = Op<T>;
+    static constexpr int KG = O::KG;
+    static constexpr int KS = KG / 4;
+    static constexpr int DS = bmax(D, KG);
+    static constexpr int NF = D / 16;           // feature tiles, one wave each
+    static constexpr int NWAVE = 1 + NF;        // plus the gate wave
+    static constexpr int NT = NP / 16;
+    static constexpr int NKD = DS / KG;
+    static constexpr int NKT = NP / KG;
+    static constexpr int PAD = 16 / (int)sizeof(T);
+    static constexpr int LQ = DS + PAD;
+    static constexpr int LPT = NP + PAD;
+    static constexpr int LF = NP + 4;
+    static constexpr int TILE = NP * LQ * (int)sizeof(T);
+    static constexpr int BASE = 3 * TILE + NP * LPT * (int)sizeof(T) + 2 * NP * LF * 4 + 8 * NP * 4;
+    // Per-wave partial sums (four token vectors and three dots) reuse the
+    // residual tile once it is consumed; the gate wave adds them in wave order.
+    static constexpr int PART = 4 * NP + 4;
+    static_assert(NF * PART * 4 <= TILE, "partials fit the residual tile");
+    // dz and -dv staged as operands too when they fit (else read from HBM / L2).
+    static constexpr bool DZ_LDS = BASE + 2 * TILE + 1024 <= kLdsMax;
+    static_assert(BASE + 1024 <= kLdsMax, "LDS budget");
+    static_assert(NP % KG == 0, "tiling");
+};
+
+template <typename T, int D, int NP>
+struct GradSmem {
+    using Gm = GradGeo<T, D, NP>;
+    alignas(16) T q[NP * Gm::LQ];
+    alignas(16) T k[NP * Gm::LQ];
+    alignas(16) T ec[NP * Gm::LQ];               // residuals E at the chunk-start state
+    alignas(16) T dz[Gm::DZ_LDS ? NP * Gm::LQ : 8];
+    alignas(16) T de[Gm::DZ_LDS ? NP * Gm::LQ : 8];
+    alignas(16) T dlt[NP * Gm::LPT];             // -(D .* L)^T
+    alignas(16) float lm[NP * Gm::LF];           // L_ij; then the eta contributions
+    alignas(16) float dl[NP * Gm::LF];           // dL_ij; then the a contributions
+    alignas(16) float th[NP];
+    alignas(16) float et[NP];
+    alignas(16) float av[NP];
+    alignas(16) float A[NP];
+    alignas(16) float Ev[NP];
+    alignas(16) float c[NP];
+    alignas(16) float wm[NP];
+    alignas(16) float ws[NP];
+};
+
+template <typename T, int D, int NP>
+__global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory_bwd_grads(const GradParams p) {
+    using Gm = GradGeo<T, D, NP>;
+    using O = Op<T>;
+    using R = Fr<T>;
+    using F = typename O::frag;
+    using G = typename GlobalOf<T>::type;
+    constexpr int KG = Gm::KG, KS = Gm::KS, NT = Gm::NT, NKD = Gm::NKD, NKT = Gm::NKT;
+    constexpr int LQ = Gm::LQ, LPT = Gm::LPT, LF = Gm::LF;
+
+    __shared__ __attribute__((aligned(16))) GradSmem<T, D, NP> sm;
+
+    const int tid = threadIdx.x;
+    const int w = tid / kW;
+    const int lane = tid % kW;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int bh = blockIdx.x / p.nch;
+    const int c = blockIdx.x % p.nch;
+    const int n = min(p.b, p.T - c * p.b);
+    const size_t tok0 = static_cast<size_t>(bh) * p.T + static_cast<size_t>(c) * p.b;
+    const float* Mc = p.ckpt + (static_cast<size_t>(bh) * p.nch + c) * (2 * D * D);
+    const float* Sc = Mc + D * D;
+    const float* dMe = p.work + (static_cast<size_t>(bh) * p.nch + c) * (2 * D * D);
+    const float* dSe = dMe + D * D;
+
+    // ---- stage q, k (and dz, -dv), raw gates; clear the accumulators ----
+    {
+        constexpr int CB = 16 / (int)sizeof(G);
+        constexpr int UR = Gm::DS / CB;
+        const G* q = static_cast<const G*>(p.q);
+        const G* k = static_cast<const G*>(p.k);
+        for (int u = tid; u < NP * UR; u += kW * Gm::NWAVE) {
+            const int t = u / UR, col = (u % UR) * CB;
+            const bool ok = t < n && col < D;
+            const size_t g = (tok0 + t) * D + col;
+            stage_unit<T>(sm.q + t * LQ + col, q + (ok ? g : 0), ok);
+            stage_unit<T>(sm.k + t * LQ + col, k + (ok ? g : 0), ok);
+            if constexpr (Gm::DS > D) stage_unit<T>(sm.ec + t * LQ + col, q, false);
+        }
+        if constexpr (Gm::DZ_LDS) {
+            constexpr int U4 = Gm::DS / 4;
+            for (int u = tid; u < NP * U4; u += kW * Gm::NWAVE) {
+                const int t = u / U4, col = (u % U4) * 4;
+                const bool ok = t < n && col < D;
+                const f32x4 z4 = ok ? *reinterpret_cast<const f32x4*>(p.dz + (tok0 + t) * D + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+                const f32x4 v4 = ok ? *reinterpret_cast<const f32x4*>(p.dv + (tok0 + t) * D + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+                st4<T>(sm.dz + t * LQ + col, z4);
+                st4<T>(sm.de + t * LQ + col, -v4);
+            }
+        }
+        for (int l = tid; l < NP; l += kW * Gm::NWAVE) {
+            const bool ok = l < n;
+            sm.th[l] = ok ? p.theta[tok0 + l] : 0.f;
+            sm.et[l] = ok ? p.eta[tok0 + l] : 1.f;
+            sm.av[l] = ok ? 1.f - p.alpha[tok0 + l] : 1.f;
+        }
+    }
+    // Partial sums of feature wave f: [dA | dc | dw^M | dw^S][NP], then the three dots.
+    float* const part = reinterpret_cast<float*>(sm.ec);
+    __syncthreads();
+
+    // Row-major operand fragment of dz or -dv (token row t, k-group at k0).
+    auto zfrag = [&](const T* lds, const float* glob, float sign, int t, int k0) -> F {
+        if constexpr (Gm::DZ_LDS) {
+            return R::rm(lds, LQ, t, k0, lg);
+        } else {
+            float x[KS];
+            const int col = k0 + KS * lg;
+            const bool ok = t < n && col < D;
+#pragma unroll
+            for (int s = 0; s < KS; s += 4) {
+                const f32x4 v4 = ok ? *reinterpret_cast<const f32x4*>(glob + (tok0 + t) * D + col + s) : f32x4{0.f, 0.f, 0.f, 0.f};
+                x[s] = sign * v4[0];
+                x[s + 1] = sign * v4[1];
+                x[s + 2] = sign * v4[2];
+                x[s + 3] = sign * v4[3];
+            }
+            return R::from_f32(x);
+        }
+    };
+
+    if (w == 0) {
+        // ===================== gate wave =====================
+        const int l = lane;
+        const float my_th = sm.th[l % NP], my_et = sm.et[l % NP], my_a = sm.av[l % NP];
+        float A, E, cc;
+        gate_prefix<NP>(my_a, my_et, l, A, E, cc);
+        if (l < NP) {
+            sm.A[l] = A;
+            sm.Ev[l] = E;
+            sm.c[l] = cc;
+        }
+        float gam[NP], pm[NP];
+        float g = 0.f, pp = 0.f, wm = 0.f, ws = 0.f;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const float ai = readlane(my_a, i), ei = readlane(my_et, i);
+            if (i == l) {
+                pp = 1.f;
+                g = 1.f;
+            } else if (i > l) {
+                pp = ei * pp;
+                g = ai * g + pp;
+            }
+            gam[i] = g;
+            pm[i] = pp;
+            if (l < NP) sm.lm[i * LF + l] = my_th * g;
+            if (i == n - 1) {
+                wm = my_th * g;
+                ws = my_th * pp;
+            }
+        }
+        if (l < NP) {
+            sm.wm[l] = wm;
+            sm.ws[l] = ws;
+        }
+        __syncthreads();   // (1) gates and residual tiles ready
+
+        // Lower tiles of G = Q K^T and D = dZ E^T: dL = -G .* D, -(D .* L)^T.
+#pragma unroll
+        for (int it = 0; it < NT; ++it) {
+#pragma unroll
+            for (int jt = 0; jt < NT; ++jt) {
+                const int j = 16 * jt + lr;
+                T* dst = sm.dlt + j * LPT + 16 * it + 4 * lg;
+                if (jt > it) {
+                    st4<T>(dst, f32x4{0.f, 0.f, 0.f, 0.f});
+                    continue;
+                }
+                f32x4 gacc = {0.f, 0.f, 0.f, 0.f}, dacc = gacc;
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) {
+                    gacc = O::mma(gacc, R::rm(sm.q, LQ, 16 * it + lr, kk * KG, lg), R::rm(sm.k, LQ, j, kk * KG, lg));
+                    dacc = O::mma(dacc, zfrag(sm.dz, p.dz, 1.f, 16 * it + lr, kk * KG), R::rm(sm.ec, LQ, j, kk * KG, lg));
+                }
+                f32x4 nd;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * it + 4 * lg + e;
+                    const bool ok = j <= i;
+                    nd[e] = ok ? -dacc[e] * sm.lm[i * LF + j] : 0.f;
+                    sm.dl[i * LF + j] = ok ? -gacc[e] * dacc[e] : 0.f;
+                }
+                st4<T>(dst, nd);
+            }
+        }
+        __syncthreads();   // (2) dL, -(D .* L)^T complete
+        __syncthreads();   // (3) partial sums of the feature waves written
+        // Scalar cotangents: partial sums added in wave order (deterministic).
+        float dA_l = 0.f, dc_l = 0.f, dwm_j = 0.f, dws_j = 0.f, dot0 = 0.f, dot1 = 0.f, dEn = 0.f;
+#pragma unroll
+        for (int f = 0; f < Gm::NF; ++f) {
+            const float* pf = part + f * Gm::PART;
+            dA_l += pf[l % NP];
+            dc_l += pf[NP + l % NP];
+            dwm_j += pf[2 * NP + l % NP];
+            dws_j += pf[3 * NP + l % NP];
+            dot0 += pf[4 * NP];
+            dot1 += pf[4 * NP + 1];
+            dEn += pf[4 * NP + 2];
+        }
+
+        // Reverse through the column recurrences of gamma and p (lane = column j).
+        float gg = 0.f, gp = 0.f, dth = 0.f;
+#pragma unroll
+        for (int i = NP - 1; i >= 0; --i) {
+            const bool act = i >= l && i < n;
+            float dli = act ? sm.dl[i * LF + l] : 0.f;
+            const bool last = act && i == n - 1;
+            if (last) dli += dwm_j;
+            gg += my_th * dli;
+            dth += dli * gam[i];
+            if (last) {
+                gp += my_th * dws_j;
+                dth += dws_j * pm[i];
+            }
+            float ca = 0.f, ce = 0.f;
+            if (i > 0 && i > l) {
+                ca = gg * gam[i > 0 ? i - 1 : 0];
+                gp += gg;
+                ce = gp * pm[i > 0 ? i - 1 : 0];
+                gg *= readlane(my_a, i);
+                gp *= readlane(my_et, i);
+            }
+            if (l < NP) {
+                sm.dl[i * LF + l] = ca;
+                sm.lm[i * LF + l] = ce;
+            }
+        }
+        wave_lds_fence();
+        // Row sums (lane = row i) and the prefix-product part.
+        float sa = 0.f, se = 0.f;
+        if (l < NP) {
+#pragma unroll
+            for (int j = 0; j < NP; j += 4) {
+                const f32x4 va = *reinterpret_cast<const f32x4*>(sm.dl + l * LF + j);
+                const f32x4 ve = *reinterpret_cast<const f32x4*>(sm.lm + l * LF + j);
+                sa += (va[0] + va[1]) + (va[2] + va[3]);
+                se += (ve[0] + ve[1]) + (ve[2] + ve[3]);
+            }
+        }
+        const float my_dA = dA_l + (l == n - 1 ? dot0 : 0.f);
+        const float my_dc = dc_l + (l == n - 1 ? dot1 : 0.f);
+        float rA = 0.f, rc = 0.f, gA = 0.f, gc = 0.f;
+#pragma unroll
+        for (int i = NP - 1; i >= 0; --i) {
+            const float an = i + 1 < NP ? readlane(my_a, i + 1) : 0.f;
+            rA = an * rA + readlane(my_dA, i);
+            rc = an * rc + readlane(my_dc, i);
+            if (i == l) {
+                gA = rA;
+                gc = rc;
+            }
+        }
+        float rE = 0.f, gE = 0.f;
+#pragma unroll
+        for (int i = NP - 1; i >= 0; --i) {
+            const float en = i + 1 < NP ? readlane(my_et, i + 1) : 0.f;
+            rE = en * rE + readlane(gc, i) + (i == n - 1 ? dEn : 0.f);
+            if (i == l) gE = rE;
+        }
+        if (l < n) {
+            const float A_prev = l > 0 ? sm.A[l - 1] : 1.f;
+            const float c_prev = l > 0 ? sm.c[l - 1] : 0.f;
+            const float E_prev = l > 0 ? sm.Ev[l - 1] : 1.f;
+            const float da = sa + gA * A_prev + gc * c_prev;
+            const float de = se + gE * E_prev;
+            p.dth[tok0 + l] = dth;
+            p.deta[tok0 + l] = de;
+            p.dal[tok0 + l] = -da;
+        }
+    } else {
+        // ===================== feature wave =====================
+        const int f0 = 16 * (w - 1);   // rows (phase 1) / features (phases 2, 3) f0 .. f0+15
+        // Residual rows of E^T: E^T[r][t] = M0[r][:] . k_t - v_t[r], r = f0 + (acc row).
+        {
+            F am[NKD];
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) {
+                float x[KS];
+                const int col = kk * KG + KS * lg;
+#pragma unroll
+                for (int s = 0; s < KS; s += 4) {
+                    const f32x4 v4 = col + s < D ? *reinterpret_cast<const f32x4*>(Mc + (f0 + lr) * D + col + s)
+                                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+                    x[s] = v4[0];
+                    x[s + 1] = v4[1];
+                    x[s + 2] = v4[2];
+                    x[s + 3] = v4[3];
+                }
+                am[kk] = R::from_f32(x);
+            }
+            const G* vg = static_cast<const G*>(p.v);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = 16 * tt + lr;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) acc = O::mma(acc, am[kk], R::rm(sm.k, LQ, t, kk * KG, lg));
+                const f32x4 vv = t < n ? gload4<T>(vg + (tok0 + t) * D + f0 + 4 * lg) : f32x4{0.f, 0.f, 0.f, 0.f};
+                st4<T>(sm.ec + t * LQ + f0 + 4 * lg, acc - vv);
+            }
+        }
+        // Columns f0 .. f0+15 of M0, S0, dM', dS' as operand fragments whose
+        // rows are those columns (k = row of the state), and their dots.
+        F mcf[NKD], scf[NKD], dmf[NKD], dsf[NKD];
+        float d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) {
+            float xm[KS], xs[KS], xdm[KS], xds[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int r = kk * KG + KS * lg + s;
+                const bool ok = r < D;
+                const size_t o = static_cast<size_t>(ok ? r : 0) * D + f0 + lr;
+                xm[s] = ok ? Mc[o] : 0.f;
+                xs[s] = ok ? Sc[o] : 0.f;
+                xdm[s] = ok ? dMe[o] : 0.f;
+                xds[s] = ok ? dSe[o] : 0.f;
+                d1 += xdm[s] * xm[s];
+                d2 += xdm[s] * xs[s];
+                d3 += xds[s] * xs[s];
+            }
+            mcf[kk] = R::from_f32(xm);
+            scf[kk] = R::from_f32(xs);
+            dmf[kk] = R::from_f32(xdm);
+            dsf[kk] = R::from_f32(xds);
+        }
+        d1 = wave_sum(d1);
+        d2 = wave_sum(d2);
+        d3 = wave_sum(d3);
+        __syncthreads();   // (1)
+
+        // Products with features f0.. as rows and tokens as columns: lane
+        // (lr, lg) holds features f0 + 4lg + e of token t = 16tt + lr.
+        f32x4 dQ[NT], dK[NT];
+        float pa[NT], pc[NT], pwm[NT], pws[NT];
+        auto red = [&](float x) {
+            x += __shfl_xor(x, 16, kW);
+            x += __shfl_xor(x, 32, kW);
+            return x;
+        };
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int t = 16 * tt + lr;
+            f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = X, H = X, U = X, W = X;
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) {
+                const F zf = zfrag(sm.dz, p.dz, 1.f, t, kk * KG);
+                const F ef = zfrag(sm.de, p.dv, -1.f, t, kk * KG);
+                const F cf = R::rm(sm.ec, LQ, t, kk * KG, lg);
+                X = O::mma(X, mcf[kk], zf);
+                Y = O::mma(Y, scf[kk], zf);
+                H = O::mma(H, mcf[kk], ef);
+                U = O::mma(U, dmf[kk], cf);
+                W = O::mma(W, dsf[kk], cf);
+            }
+            const f32x4 qv = ld4<T>(sm.q + t * LQ + f0 + 4 * lg);
+            const f32x4 kv = ld4<T>(sm.k + t * LQ + f0 + 4 * lg);
+            pa[tt] = red((qv[0] * X[0] + qv[1] * X[1]) + (qv[2] * X[2] + qv[3] * X[3]));
+            pc[tt] = red((qv[0] * Y[0] + qv[1] * Y[1]) + (qv[2] * Y[2] + qv[3] * Y[3]));
+            pwm[tt] = -red((kv[0] * U[0] + kv[1] * U[1]) + (kv[2] * U[2] + kv[3] * U[3]));
+            pws[tt] = -red((kv[0] * W[0] + kv[1] * W[1]) + (kv[2] * W[2] + kv[3] * W[3]));
+            const float At = sm.A[t], ct = sm.c[t], wmt = sm.wm[t], wst = sm.ws[t];
+            dQ[tt] = At * X + ct * Y;
+            dK[tt] = H - wmt * U - wst * W;
+        }
+        __syncthreads();   // (2) residual tile consumed
+        {
+            float* pf = part + (w - 1) * Gm::PART;
+            if (lg == 0) {
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    const int t = 16 * tt + lr;
+                    pf[t] = pa[tt];
+                    pf[NP + t] = pc[tt];
+                    pf[2 * NP + t] = pwm[tt];
+                    pf[3 * NP + t] = pws[tt];
+                }
+            }
+            if (lane == 0) {
+                pf[4 * NP] = d1;
+                pf[4 * NP + 1] = d2;
+                pf[4 * NP + 2] = d3;
+            }
+        }
+        __syncthreads();   // (3)
+
+        // dQ -= (DL K)^T, dK -= (DL^T Q)^T  (dlt holds -DL^T).
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+            for (int kk = 0; kk < NKT; ++kk) {
+                dQ[tt] = O::mma(dQ[tt], R::cm(sm.k, LQ, kk * KG, f0, lr, lg), R::cm(sm.dlt, LPT, kk * KG, 16 * tt, lr, lg));
+                dK[tt] = O::mma(dK[tt], R::cm(sm.q, LQ, kk * KG, f0, lr, lg), R::rm(sm.dlt, LPT, 16 * tt + lr, kk * KG, lg));
+            }
+            const int t = 16 * tt + lr;
+            if (t < n) {
+                *reinterpret_cast<f32x4*>(p.dq + (tok0 + t) * D + f0 + 4 * lg) = dQ[tt];
+                *reinterpret_cast<f32x4*>(p.dk + (tok0 + t) * D + f0 + 4 * lg) = dK[tt];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NS, int NP>
+hipError_t launch_carry(const CarryParams& cp, hipStream_t s) {
+    using Gm = CarryGeo<T, D, NS, NP>;
+    const long long nwg = static_cast<long long>(cp.BH) * Gm::NRB;
+    hipLaunchKernelGGL((linear_memory_bwd_carry<T, D, NS, NP>), dim3(static_cast<unsigned>(nwg)),
+                       dim3(kW * Gm::NWAVE), 0, s, cp);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int NP>
+hipError_t launch_grads(const GradParams& gp, hipStream_t s) {
+    using Gm = GradGeo<T, D, NP>;
+    const long long nwg = static_cast<long long>(gp.BH) * gp.nch;
+    if (nwg == 0) return hipSuccess;
+    hipLaunchKernelGGL((linear_memory_bwd_grads<T, D, NP>), dim3(static_cast<unsigned>(nwg)),
+                       dim3(kW * Gm::NWAVE), 0, s, gp);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int NP>
+hipError_t launch_bwd(const CarryParams& cp, const GradParams& gp, hipStream_t s) {
+    constexpr int NS = D >= 32 ? 2 : 1;
+    hipError_t err = launch_carry<T, D, NS, NP>(cp, s);
+    if (err != hipSuccess) return err;
+    return launch_grads<T, D, NP>(gp, s);
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_np(const CarryParams& cp, const GradParams& gp, int b, hipStream_t s) {
+    if constexpr (Op<T>::KG == 32) {
+        return b <= 32 ? launch_bwd<T, D, 32>(cp, gp, s) : launch_bwd<T, D, 64>(cp, gp, s);
+    } else {
+        if (b <= 16) return launch_bwd<T, D, 16>(cp, gp, s);
+        if (b <= 32) return launch_bwd<T, D, 32>(cp, gp, s);
+        return launch_bwd<T, D, 64>(cp, gp, s);
+    }
+}
+
+struct Span {
+    const void* p;
+    size_t n;
+};
+
+template <typename T>
+int backward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
+                  const float* alpha, const float* ckpt, const float* dz, const float* dMT, const float* dST,
+                  float* dq, float* dk, float* dv, float* dth, float* deta, float* dal, float* dM0, float* dS0,
+                  float* work, int B, int H, int Tlen, int d, int b, void* stream) {
+    using G = typename GlobalOf<T>::type;
+    if (B < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
+    if (b < 1) return TTT_ERR_INVALID_ARG;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
+    if (b > 64) return TTT_ERR_UNSUPPORTED;
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0) return TTT_OK;
+    const long long nch = (static_cast<long long>(Tlen) + b - 1) / b;
+    if (BH * static_cast<long long>(Tlen) > 0x7fffffffLL || BH * nch > 0x7fffffffLL || BH * (d / 16) > 0x7fffffffLL)
+        return TTT_ERR_UNSUPPORTED;
+    const size_t tok = static_cast<size_t>(BH) * static_cast<size_t>(Tlen);
+    const size_t in_b = tok * d * sizeof(G), f_b = tok * d * 4, g_b = tok * 4;
+    const size_t st_b = static_cast<size_t>(BH) * d * d * 4;
+    const size_t ck_b = ckpt_bytes(B, H, Tlen, d, b);
+    if (Tlen > 0) {
+        const void* req[] = {q, k, v, theta, eta, alpha, ckpt, dz, dq, dk, dv, dth, deta, dal, work};
+        for (const void* r : req)
+            if (!r) return TTT_ERR_INVALID_ARG;
+        const void* a16[] = {q, k, v, ckpt, dz, dq, dk, dv, work};
+        for (const void* r : a16)
+            if (!aligned(r, 16)) return TTT_ERR_INVALID_ARG;
+        const void* a4[] = {theta, eta, alpha, dth, deta, dal};
+        for (const void* r : a4)
+            if (!aligned(r, 4)) return TTT_ERR_INVALID_ARG;
+    }
+    const void* st[] = {dMT, dST, dM0, dS0};
+    for (const void* r : st)
+        if (r && !aligned(r, 16)) return TTT_ERR_INVALID_ARG;
+    // No output may overlap any input or another output.
+    const Span ins[] = {{q, in_b}, {k, in_b}, {v, in_b}, {theta, g_b}, {eta, g_b}, {alpha, g_b},
+                        {ckpt, ck_b}, {dz, f_b}, {dMT, st_b}, {dST, st_b}};
+    const Span outs[] = {{dq, f_b}, {dk, f_b}, {dv, f_b}, {dth, g_b}, {deta, g_b}, {dal, g_b},
+                         {dM0, st_b}, {dS0, st_b}, {work, ck_b}};
+    const int n_outs = static_cast<int>(sizeof(outs) / sizeof(outs[0]));
+    for (int i = 0; i < n_outs; ++i) {
+        if (outs[i].n == 0) continue;
+        for (const Span& in : ins)
+            if (in.n && overlaps(outs[i].p, outs[i].n, in.p, in.n)) return TTT_ERR_INVALID_ARG;
+        for (int j = i + 1; j < n_outs; ++j)
+            if (outs[j].n && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return TTT_ERR_INVALID_ARG;
+    }
+
+    const CarryParams cp{q, k, dz, theta, eta, alpha, dMT, dST, work, dv, dM0, dS0,
+                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch)};
+    const GradParams gp{q, k, v, theta, eta, alpha, ckpt, work, dz, dv, dq, dk, dth, deta, dal,
+                        static_cast<int>(BH), Tlen, b, static_cast<int>(nch)};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    switch (d) {
+        case 16: err = launch_bwd_np<T, 16>(cp, gp, b, s); break;
+        case 32: err = launch_bwd_np<T, 32>(cp, gp, b, s); break;
+        case 64: err = launch_bwd_np<T, 64>(cp, gp, b, s); break;
+        default: err = launch_bwd_np<T, 128>(cp, gp, b, s); break;
+    }
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_mem_backward_f32(const float* q, const float* k, const float* v, const float* theta, const float* eta,
+                         const float* alpha, const float* ckpt, const float* dz, const float* dM_T,
+                         const float* dS_T, float* dq, float* dk, float* dv, float* dtheta, float* deta,
+                         float* dalpha, float* dM0, float* dS0, float* work, int B, int H, int T, int d, int b,
+                         void* stream) {
+    return backward_impl<float>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta, dalpha,
+                                dM0, dS0, work, B, H, T, d, b, stream);
+}
+
+int ttt_mem_backward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                          const float* eta, const float* alpha, const float* ckpt, const float* dz,
+                          const float* dM_T, const float* dS_T, float* dq, float* dk, float* dv, float* dtheta,
+                          float* deta, float* dalpha, float* dM0, float* dS0, float* work, int B, int H, int T,
+                          int d, int b, void* stream) {
+    return backward_impl<_Float16>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta,
+                                   dalpha, dM0, dS0, work, B, H, T, d, b, stream);
+}
+
+}  // extern "C"

@@ -30,7 +30,7 @@ def _as_dev(t, name, dtype, shape, device):
     return t.contiguous()
 
 
-def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=True):
+def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=True, extra=None):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
     B, H, T, d = q.shape
@@ -59,9 +59,11 @@ def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         sizes = (B, H, T, d, int(b)) if with_b else (B, H, T, d)
-        status = getattr(lib, name)(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(M0), _ptr(S0),
-            _ptr(z), _ptr(M_T), _ptr(S_T), *sizes, stream)
+        ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(M0), _ptr(S0),
+                _ptr(z), _ptr(M_T), _ptr(S_T)]
+        if extra is not None:
+            ptrs.append(_ptr(extra))
+        status = getattr(lib, name)(*ptrs, *sizes, stream)
     _lib.check(name, status)
     return z, M_T, S_T
 
@@ -83,6 +85,131 @@ def forward(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
     if q.dtype == torch.bfloat16:
         return ttt_mem_forward_bf16(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
     raise TypeError(f"unsupported input dtype {q.dtype}")
+
+
+def _nch(T, b):
+    return (T + b - 1) // b
+
+
+def forward_train(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None, ckpt=None):
+    """Forward that also saves the state entering every chunk for ``backward``.
+
+    Returns ``(z, M_T, S_T, ckpt)`` with ``ckpt [B, H, ceil(T/b), 2, d, d]``
+    float32 (``ckpt[..., c, 0]`` = M and ``[..., c, 1]`` = S before chunk c).
+    """
+    if q.dtype == torch.float32:
+        name = "ttt_mem_forward_ckpt_f32"
+    elif q.dtype == torch.bfloat16:
+        name = "ttt_mem_forward_ckpt_bf16"
+    else:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    shape = (B, H, _nch(T, int(b)), 2, d, d)
+    if ckpt is None:
+        ckpt = torch.empty(shape, dtype=torch.float32, device=q.device)
+    elif (not ckpt.is_contiguous() or ckpt.dtype != torch.float32 or tuple(ckpt.shape) != shape
+          or ckpt.device != q.device):
+        raise ValueError(f"ckpt must be contiguous float32 {shape} on {q.device}")
+    z, M_T, S_T = _forward(name, q.dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, extra=ckpt)
+    return z, M_T, S_T, ckpt
+
+
+def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, work=None, out=None,
+             want_state_grads=True):
+    """Gradients of the linear memory from ``forward_train``'s checkpoints.
+
+    ``dz [B, H, T, d]``, ``dM_T, dS_T [B, H, d, d]`` (float32; None = zero) are
+    the derivatives of the outer loss with respect to ``z, M_T, S_T``.
+    Returns ``(dq, dk, dv, dtheta, deta, dalpha, dM0, dS0)``, all float32
+    (``dM0, dS0`` are None when ``want_state_grads`` is False).  ``work`` may
+    pass a float32 scratch tensor shaped like ``ckpt``; ``out`` preallocated
+    outputs in the same order.
+    """
+    if q.dtype == torch.float32:
+        name = "ttt_mem_backward_f32"
+    elif q.dtype == torch.bfloat16:
+        name = "ttt_mem_backward_bf16"
+    else:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be HIP device tensors (torch 'cuda' device)")
+    b = int(b)
+    in_dtype = q.dtype
+    q = _as_dev(q, "q", in_dtype, (B, H, T, d), dev)
+    k = _as_dev(k, "k", in_dtype, (B, H, T, d), dev)
+    v = _as_dev(v, "v", in_dtype, (B, H, T, d), dev)
+    theta = _as_dev(theta, "theta", torch.float32, (B, H, T), dev)
+    eta = _as_dev(eta, "eta", torch.float32, (B, H, T), dev)
+    alpha = _as_dev(alpha, "alpha", torch.float32, (B, H, T), dev)
+    ck_shape = (B, H, _nch(T, b), 2, d, d)
+    ckpt = _as_dev(ckpt, "ckpt", torch.float32, ck_shape, dev)
+    dz = _as_dev(dz, "dz", torch.float32, (B, H, T, d), dev)
+    dM_T = _as_dev(dM_T, "dM_T", torch.float32, (B, H, d, d), dev)
+    dS_T = _as_dev(dS_T, "dS_T", torch.float32, (B, H, d, d), dev)
+    if work is None:
+        work = torch.empty(ck_shape, dtype=torch.float32, device=dev)
+    else:
+        work = _as_dev(work, "work", torch.float32, ck_shape, dev)
+    shapes = [(B, H, T, d)] * 3 + [(B, H, T)] * 3 + [(B, H, d, d)] * 2
+    if out is None:
+        out = [torch.empty(s_, dtype=torch.float32, device=dev) for s_ in shapes]
+        if not want_state_grads:
+            out[6] = out[7] = None
+    else:
+        out = list(out)
+        for i, (t, shp) in enumerate(zip(out, shapes)):
+            if t is not None and (not t.is_contiguous() or t.dtype != torch.float32
+                                  or tuple(t.shape) != shp or t.device != dev):
+                raise ValueError(f"out tensor {i} must be contiguous float32 {shp} on {dev}")
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        status = getattr(lib, name)(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(ckpt), _ptr(dz),
+            _ptr(dM_T), _ptr(dS_T), *[_ptr(t) for t in out], _ptr(work), B, H, T, d, b, stream)
+    _lib.check(name, status)
+    return tuple(out)
+
+
+class LinearMemoryFunction(torch.autograd.Function):
+    """``(z, M_T, S_T) = memory(q, k, v, theta, eta, alpha, M0, S0)`` with a HIP backward.
+
+    Forward saves the chunk-start states; backward calls ``backward``.  Gradients
+    of bf16 inputs are returned in bf16 (computed in float32).
+    """
+
+    @staticmethod
+    def forward(ctx, q, k, v, theta, eta, alpha, M0, S0, b):
+        z, M_T, S_T, ckpt = forward_train(q, k, v, theta, eta, alpha, M0, S0, b=b)
+        ctx.save_for_backward(q, k, v, theta, eta, alpha, ckpt)
+        ctx.b = b
+        ctx.has_state = (M0 is not None, S0 is not None)
+        return z, M_T, S_T
+
+    @staticmethod
+    def backward(ctx, dz, dM_T, dS_T):
+        q, k, v, theta, eta, alpha, ckpt = ctx.saved_tensors
+        B, H, T, d = q.shape
+        if dz is None:
+            dz = torch.zeros((B, H, T, d), dtype=torch.float32, device=q.device)
+        g = backward(q, k, v, theta, eta, alpha, ckpt, dz.float().contiguous(),
+                     None if dM_T is None else dM_T.float().contiguous(),
+                     None if dS_T is None else dS_T.float().contiguous(), b=ctx.b)
+        dq, dk, dv = (x.to(q.dtype) for x in g[:3])
+        dM0 = g[6] if ctx.has_state[0] else None
+        dS0 = g[7] if ctx.has_state[1] else None
+        return dq, dk, dv, g[3], g[4], g[5], dM0, dS0, None
+
+
+def linear_memory(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b):
+    """Differentiable linear memory: ``(z, M_T, S_T)``, gradients through the HIP backward."""
+    return LinearMemoryFunction.apply(q, k, v, theta, eta, alpha, M0, S0, b)
 
 
 def forward_varlen(q, k, v, theta, eta, alpha, cu_seqlens, M0=None, S0=None, *, b, out=None):

@@ -34,7 +34,7 @@ import dataclasses
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "to_numpy64"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_cotangents", "to_numpy64"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -140,6 +140,29 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         else:
             out["M0"] = None
         out["S0"] = None
+    return out
+
+
+def make_cotangents(w: Workload, seed: int | None = None, states: bool = True, chunks=None) -> dict:
+    """Draw derivatives of an outer loss with respect to the memory's outputs.
+
+    ``dz`` [B,H,T,d] ~ N(0,1) float32; with ``states``, ``dM_T, dS_T``
+    [B,H,d,d] ~ N(0,1) float32 (else None).  ``chunks=(c0, c1)`` keeps dz only
+    on the tokens of chunks c0 .. c1-1 (chunk size w.b) and zeroes the rest.
+    Seed: ``numpy.random.default_rng(2000 + id)``.
+    """
+    rng = np.random.default_rng(2000 + w.id if seed is None else seed)
+    B, H, T, d = w.B, w.H, w.T, w.d
+    dz = _normal(rng, (B, H, T, d)).astype(np.float32)
+    if chunks is not None:
+        c0, c1 = chunks
+        keep = np.zeros(T, dtype=bool)
+        keep[c0 * w.b:min(c1 * w.b, T)] = True
+        dz[:, :, ~keep, :] = 0.0
+    out = {"dz": torch.from_numpy(dz), "dM_T": None, "dS_T": None}
+    if states:
+        out["dM_T"] = torch.from_numpy(rng.standard_normal((B, H, d, d)).astype(np.float32))
+        out["dS_T"] = torch.from_numpy(rng.standard_normal((B, H, d, d)).astype(np.float32))
     return out
 
 

@@ -21,7 +21,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ttt_mem_abi_version() == (1 << 16)
+    assert lib.ttt_mem_abi_version() == (1 << 16) | 1
     assert lib.ttt_mem_status_string(0) == b"ok"
     for s in (-1, -2, -3, 12345):
         assert lib.ttt_mem_status_string(s)
@@ -53,3 +53,27 @@ def test_rejections_happen_before_any_launch(lib, name):
 def test_empty_batch_returns_ok_without_pointers(lib, name):
     assert _call(lib, name, B=0) == 0
     assert _call(lib, name, H=0) == 0
+
+
+def test_ckpt_bytes(lib):
+    # [B, H, ceil(T/b), M | S, d, d] float32.
+    assert lib.ttt_mem_ckpt_bytes(2, 3, 130, 64, 64) == 2 * 3 * 3 * 2 * 64 * 64 * 4
+    assert lib.ttt_mem_ckpt_bytes(1, 1, 0, 16, 8) == 0
+    assert lib.ttt_mem_ckpt_bytes(-1, 1, 8, 16, 8) == 0
+
+
+@pytest.mark.parametrize("name", ["ttt_mem_forward_ckpt_f32", "ttt_mem_forward_ckpt_bf16"])
+def test_training_forward_requires_ckpt(lib, name):
+    assert getattr(lib, name)(*([None] * 12), 1, 1, 8, 16, 4, None) == -1
+
+
+@pytest.mark.parametrize("name", ["ttt_mem_backward_f32", "ttt_mem_backward_bf16"])
+def test_backward_rejections_happen_before_any_launch(lib, name):
+    def call(B=1, H=1, T=8, d=16, b=4):
+        return getattr(lib, name)(*([None] * 19), B, H, T, d, b, None)
+    assert call() == -1                      # NULL required pointers
+    assert call(d=48) == -2                  # unsupported head dim
+    assert call(b=0) == -1
+    assert call(b=65) == -2
+    assert call(T=-1) == -1
+    assert call(B=0) == 0                    # nothing to do: no pointer is touched

@@ -1,0 +1,207 @@
+"""GPU parity of the linear memory's training forward and backward pass.
+
+The oracle is ``linear_backward`` (float64 reverse mode through the per-token
+loop, pinned by finite differences and the pages' outer-gradient examples).
+Bounds as for the forward, per output: max|gpu - oracle| / rms(oracle) <= 1e-4
+on the float32 path and <= 2e-2 on the bf16-input path (fp16 MFMA operands,
+float32 accumulation).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import linear_backward, linear_forward
+from tests._parity import TOL, rel_err, to_dev
+from test_neural_memory_amd import memory as tm
+from test_neural_memory_amd._lib import TTTError
+from test_neural_memory_amd.workloads import WORKLOADS, make_cotangents, make_inputs, to_numpy64
+
+pytestmark = pytest.mark.gpu
+NAMES = ("dq", "dk", "dv", "dtheta", "deta", "dalpha", "dM0", "dS0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _with_state(inp, seed=31, scale=0.05):
+    B, H, T, d = inp["q"].shape
+    rng = np.random.default_rng(seed)
+    inp = dict(inp)
+    inp["M0"] = torch.from_numpy((rng.standard_normal((B, H, d, d)) * scale).astype(np.float32))
+    inp["S0"] = torch.from_numpy((rng.standard_normal((B, H, d, d)) * scale * 0.1).astype(np.float32))
+    return inp
+
+
+def _gpu(inp, cot, b):
+    dev = to_dev(inp)
+    cd = to_dev(cot)
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    z, M, S, ckpt = tm.forward_train(*args, dev.get("M0"), dev.get("S0"), b=b)
+    g = tm.backward(*args, ckpt, cd["dz"], cd.get("dM_T"), cd.get("dS_T"), b=b)
+    torch.cuda.synchronize()
+    return (z, M, S, ckpt), g
+
+
+def _oracle(inp, cot, b):
+    n = {k: to_numpy64(v) for k, v in inp.items()}
+    c = {k: to_numpy64(v) for k, v in cot.items()}
+    return linear_backward(n["q"], n["k"], n["v"], n["theta"], n["eta"], n["alpha"], c["dz"], c.get("dM_T"),
+                           c.get("dS_T"), n.get("M0"), n.get("S0"), b=b)
+
+
+def _check(inp, cot, b, tol):
+    _, g = _gpu(inp, cot, b)
+    ref = _oracle(inp, cot, b)
+    errs = {nm: rel_err(to_numpy64(x.cpu()), r) for nm, x, r in zip(NAMES, g, ref)}
+    _say("  errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" (tol {tol})")
+    assert max(errs.values()) <= tol, errs
+
+
+CASES = [
+    # (label, workload id, overrides, b): several chunks, ragged tails, every head size
+    ("tiny-d16-b8", 1, dict(), 8),
+    ("d16-b8-ragged", 1, dict(B=1, H=2, T=45), 8),
+    ("ttt-d64-b16", 2, dict(B=1, H=2, T=70), 16),
+    ("d32-b32", 3, dict(B=1, H=2, T=77, d=32), 32),
+    ("titans-d128-b64", 3, dict(B=1, H=2, T=150), 64),
+    ("titans-d64-b64", 3, dict(B=1, H=2, T=130, d=64), 64),
+    ("titans-d128-b16", 3, dict(B=1, H=1, T=50), 16),
+]
+
+
+@pytest.mark.parametrize("label,wid,kw,b", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_parity(label, wid, kw, b, dtype):
+    w = WORKLOADS[wid].replace(dtype=dtype, **kw)
+    _say(f"case {label} {dtype} {w} b={b}")
+    inp = _with_state(make_inputs(w)) if wid != 2 else make_inputs(w)
+    _check(inp, make_cotangents(w), b, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_one_token_chunks(dtype):
+    w = WORKLOADS[3].replace(B=1, H=1, T=20, d=32, dtype=dtype)
+    _say(f"case b=1 {dtype}")
+    _check(_with_state(make_inputs(w)), make_cotangents(w), 1, TOL[dtype])
+
+
+def test_backward_zero_states_and_no_state_cotangents():
+    w = WORKLOADS[3].replace(B=1, H=2, T=100)
+    _say("case zero states, dM_T = dS_T = None")
+    _check(make_inputs(w), make_cotangents(w, states=False), 64, TOL["bf16"])
+
+
+@pytest.mark.parametrize("gates", ["eta0", "alpha1", "theta0"])
+def test_backward_degenerate_gates(gates):
+    w = WORKLOADS[3].replace(B=1, H=1, T=90, d=64, dtype="f32")
+    inp = _with_state(make_inputs(w))
+    if gates == "eta0":
+        inp["eta"].zero_()
+    elif gates == "alpha1":
+        inp["alpha"][..., 37] = 1.0
+    else:
+        inp["theta"].zero_()
+    _say(f"case degenerate {gates}")
+    _check(inp, make_cotangents(w), 32, TOL["f32"])
+
+
+def test_empty_sequence_passes_state_cotangents_through():
+    w = WORKLOADS[3].replace(B=1, H=2, T=0, dtype="f32")
+    inp = to_dev(make_inputs(w))
+    cot = to_dev(make_cotangents(w))
+    args = (inp["q"], inp["k"], inp["v"], inp["theta"], inp["eta"], inp["alpha"])
+    ckpt = torch.empty(1, 2, 0, 2, w.d, w.d, device="cuda")
+    g = tm.backward(*args, ckpt, cot["dz"], cot["dM_T"], cot["dS_T"], b=64)
+    torch.cuda.synchronize()
+    assert torch.equal(g[6], cot["dM_T"]) and torch.equal(g[7], cot["dS_T"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_checkpoints_are_the_chunk_start_states(dtype):
+    # ckpt[c] is what the plain forward leaves after c chunks, bit for bit, and
+    # the training forward's outputs equal the plain forward's.
+    w = WORKLOADS[3].replace(B=1, H=2, T=200, d=64, dtype=dtype)
+    inp = to_dev(_with_state(make_inputs(w)))
+    args = (inp["q"], inp["k"], inp["v"], inp["theta"], inp["eta"], inp["alpha"])
+    b = 64
+    z, M, S, ckpt = tm.forward_train(*args, inp["M0"], inp["S0"], b=b)
+    z0, M0, S0 = tm.forward(*args, inp["M0"], inp["S0"], b=b)
+    torch.cuda.synchronize()
+    assert torch.equal(z, z0) and torch.equal(M, M0) and torch.equal(S, S0)
+    assert torch.equal(ckpt[:, :, 0, 0], inp["M0"]) and torch.equal(ckpt[:, :, 0, 1], inp["S0"])
+    for c in range(1, ckpt.shape[2]):
+        pre = [a[:, :, :c * b].contiguous() for a in args]
+        _, Mc, Sc = tm.forward(*pre, inp["M0"], inp["S0"], b=b)
+        torch.cuda.synchronize()
+        assert torch.equal(ckpt[:, :, c, 0], Mc) and torch.equal(ckpt[:, :, c, 1], Sc), c
+
+
+def test_autograd_function_matches_direct_call():
+    w = WORKLOADS[3].replace(B=1, H=2, T=100, d=64, dtype="f32")
+    inp = to_dev(_with_state(make_inputs(w)))
+    cot = to_dev(make_cotangents(w))
+    leaves = {k: v.clone().requires_grad_(True) for k, v in inp.items()}
+    z, M, S = tm.linear_memory(leaves["q"], leaves["k"], leaves["v"], leaves["theta"], leaves["eta"], leaves["alpha"],
+                        leaves["M0"], leaves["S0"], b=32)
+    loss = (z * cot["dz"]).sum() + (M * cot["dM_T"]).sum() + (S * cot["dS_T"]).sum()
+    loss.backward()
+    args = (inp["q"], inp["k"], inp["v"], inp["theta"], inp["eta"], inp["alpha"])
+    _, _, _, ckpt = tm.forward_train(*args, inp["M0"], inp["S0"], b=32)
+    g = tm.backward(*args, ckpt, cot["dz"], cot["dM_T"], cot["dS_T"], b=32)
+    torch.cuda.synchronize()
+    for nm, key, ref in zip(NAMES, ("q", "k", "v", "theta", "eta", "alpha", "M0", "S0"), g):
+        assert torch.equal(leaves[key].grad, ref), nm
+
+
+def test_full_size_titans_window():
+    # The full-size Titans workload (B=4, H=16, T=8192, d=128, b=64) in the
+    # bench's launch configuration, with the outer loss on chunks 60-61 only
+    # and no state cotangent: nothing flows into those chunks from later, so
+    # their gradients are the oracle's on that 2-chunk window started from the
+    # oracle's own state after 60 chunks.  Tokens after the window get exactly
+    # zero gradient, dq is zero wherever dz is, and the cotangent leaving chunk
+    # 59 (the work buffer) is the window's dM0, dS0.
+    w = WORKLOADS[3]
+    c0, c1 = 60, 62
+    inp = make_inputs(w)
+    cot = make_cotangents(w, states=False, chunks=(c0, c1))
+    dev = to_dev(inp)
+    cd = to_dev(cot)
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    _say("case full size: training forward")
+    z, M, S, ckpt = tm.forward_train(*args, b=w.b)
+    work = torch.empty_like(ckpt)
+    _say("case full size: backward")
+    g = tm.backward(*args, ckpt, cd["dz"], b=w.b, work=work)
+    torch.cuda.synchronize()
+    t0, t1 = c0 * w.b, c1 * w.b
+    for x in g[:6]:
+        assert not torch.any(x[:, :, t1:]), "gradient after the window"
+    assert not torch.any(g[0][:, :, :t0])
+    for (bi, hi) in ((0, 0), (3, 15)):
+        n = {k: to_numpy64(v[bi, hi]) for k, v in inp.items() if v is not None}
+        _, Ms, Ss = linear_forward(n["q"][:t0], n["k"][:t0], n["v"][:t0], n["theta"][:t0], n["eta"][:t0],
+                                   n["alpha"][:t0], None, None, b=w.b)
+        sl = slice(t0, t1)
+        ref = linear_backward(n["q"][sl], n["k"][sl], n["v"][sl], n["theta"][sl], n["eta"][sl], n["alpha"][sl],
+                              to_numpy64(cot["dz"][bi, hi, sl]), None, None, Ms, Ss, b=w.b)
+        got = [to_numpy64(x[bi, hi, sl].cpu()) for x in g[:6]]
+        got += [to_numpy64(work[bi, hi, c0 - 1, 0].cpu()), to_numpy64(work[bi, hi, c0 - 1, 1].cpu())]
+        errs = {nm: rel_err(x, r) for nm, x, r in zip(NAMES, got, ref)}
+        _say(f"  ({bi},{hi}) errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        assert max(errs.values()) <= TOL["bf16"], errs
+
+
+def test_backward_argument_errors():
+    w = WORKLOADS[3].replace(B=1, H=1, T=10, d=16, dtype="f32")
+    inp = to_dev(make_inputs(w))
+    cot = to_dev(make_cotangents(w))
+    args = (inp["q"], inp["k"], inp["v"], inp["theta"], inp["eta"], inp["alpha"])
+    _, _, _, ckpt = tm.forward_train(*args, b=4)
+    with pytest.raises(TTTError) as e:
+        tm.backward(*args, ckpt, cot["dz"], b=4, out=[inp["q"]] + [None] * 7)   # dq aliasing q
+    assert e.value.status == -1
+    with pytest.raises(ValueError):
+        tm.backward(*args, ckpt, cot["dz"], b=8)   # checkpoints of another chunk size
