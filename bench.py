@@ -10,9 +10,12 @@ instead: a step is one call of the primal form for one token of every
 (batch, head) sequence (B=4 H=16 d=128), with the state carried in place from
 step to step.  ``--varlen`` times packed variable-length documents with the
 Titans recipe (32768 tokens per head in documents of seeded lengths, each
-from its own state).  Prints ONE JSON line.
+from its own state).  ``--backward`` times one training step of the Titans
+linear memory: the forward that saves the chunk-start states plus the
+backward pass (gradients for q, k, v, the three gates and the initial state),
+with a seeded synthetic outer-loss derivative dz.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {2,3,4,5} | --decode | --varlen]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {2,3,4,5} | --decode | --varlen | --backward]
                     [--no-cpu-baseline]
 """
 
@@ -32,7 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from test_neural_memory_amd import memory as tm  # noqa: E402
-from test_neural_memory_amd.workloads import WORKLOADS, make_inputs, to_numpy64  # noqa: E402
+from test_neural_memory_amd.workloads import WORKLOADS, make_cotangents, make_inputs, to_numpy64  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
@@ -247,6 +250,169 @@ def decode_main(args):
     print(json.dumps(result), flush=True)
 
 
+def algorithmic_work_backward(w, in_bytes=2):
+    """Bytes and flops the method must move / do for one backward pass.
+
+    Per (batch, head, token): read q, k, v, three gates and dz; write dq, dk,
+    dv (float32) and three gate gradients.  Per (batch, head): write dM0, dS0
+    (no state cotangent is given).  Flops, per head-token in the dual form:
+    the carry's dE and state updates (5 products of 2 b d^2 per chunk: K dM^T,
+    K dS^T, Q^T (A.dZ), Q^T (c.dZ), K^T dE) and the chunk gradients (6: K M0^T,
+    dZ M0, dZ S0, dE M0, E dM, E dS) are 22 d^2; the intra-chunk products
+    (P^T dZ, Q K^T twice, dZ E^T, DL K, DL^T Q) add 12 b d.  The checkpointed
+    states the implementation writes and reads are not counted.
+    """
+    ht = w.B * w.H * w.T
+    per_tok = 3 * w.d * in_bytes + 3 * 4 + w.d * 4 + 3 * w.d * 4 + 3 * 4
+    state = w.B * w.H * w.d * w.d * 4 * 2
+    flops = ht * (22 * w.d * w.d + 12 * w.b * w.d)
+    return ht * per_tok + state, flops, per_tok
+
+
+def _oracle_train_worker(args):
+    # One BLAS thread; the oracle's forward and backward, one sequence at a time.
+    seqs, b = args
+    from threadpoolctl import threadpool_limits
+    from oracle import linear_backward, linear_forward
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for q, k, v, th, et, al, dz in seqs:
+            linear_forward(q, k, v, th, et, al, None, None, b=b)
+            linear_backward(q, k, v, th, et, al, dz, None, None, None, None, b=b)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline_backward(w, inp, cot, pairs=64, tokens=2048):
+    """Time the float64 oracle (forward, then backward) on `pairs` (batch, head)
+    sequences cut to their first `tokens` tokens, in a process pool."""
+    import multiprocessing as mp
+    ncores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    g = {k: to_numpy64(v) for k, v in inp.items() if k in ("q", "k", "v", "theta", "eta", "alpha")}
+    dz = to_numpy64(cot["dz"])
+    B, H = w.B, w.H
+    sel = [(i // H, i % H) for i in range(B * H)][:pairs]
+    jobs = [([], w.b) for _ in range(ncores)]
+    for i, (bi, hi) in enumerate(sel):
+        jobs[i % ncores][0].append(tuple(g[x][bi, hi, :tokens] for x in ("q", "k", "v", "theta", "eta", "alpha"))
+                                   + (dz[bi, hi, :tokens],))
+    jobs = [j for j in jobs if j[0]]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(len(jobs)) as pool:
+        per_job = pool.map(_oracle_train_worker, jobs)
+    wall = time.perf_counter() - t0
+    head_tokens = len(sel) * tokens
+    return {
+        "value": head_tokens / H / wall,   # training tokens/s, each token covering all H heads
+        "unit": "tokens/s",
+        "cores": len(jobs),
+        "kind": "oracle",
+        "sample": f"{len(sel)} of {B * H} (batch, head) sequences, first {tokens} of T={w.T} tokens, all "
+                  f"d={w.d} rows; float64 per-token NumPy forward then reverse-mode backward, "
+                  f"{len(jobs)} processes x 1 thread; wall {wall:.2f} s, busiest process {max(per_job):.2f} s; "
+                  f"tokens/s = sampled head-tokens / H / wall",
+    }
+
+
+def backward_main(args):
+    """One training step of the Titans linear memory: forward with checkpoints + backward."""
+    w = WORKLOADS[3]
+    B, H, T, d = w.B, w.H, w.T, w.d
+    log(f"training step workload {w}")
+    inp = make_inputs(w)
+    cot = make_cotangents(w, states=False)
+    dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    dz = cot["dz"].cuda()
+    args_ = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    z = torch.empty(B, H, T, d, dtype=torch.float32, device="cuda")
+    MT = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    ST = torch.empty_like(MT)
+    nch = (T + w.b - 1) // w.b
+    ckpt = torch.empty(B, H, nch, 2, d, d, dtype=torch.float32, device="cuda")
+    work = torch.empty_like(ckpt)
+    outs = [torch.empty(B, H, T, d, dtype=torch.float32, device="cuda") for _ in range(3)] + \
+           [torch.empty(B, H, T, dtype=torch.float32, device="cuda") for _ in range(3)] + \
+           [torch.empty(B, H, d, d, dtype=torch.float32, device="cuda") for _ in range(2)]
+    fwd = lambda: tm.forward_train(*args_, b=w.b, out=(z, MT, ST), ckpt=ckpt)  # noqa: E731
+    bwd = lambda: tm.backward(*args_, ckpt, dz, b=w.b, work=work, out=outs)  # noqa: E731
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    # Timed region: K training steps on torch's current stream (the stream
+    # the library launches on), events around the forward and the backward.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        fwd()
+        ev[i][1].record()
+        bwd()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    nbytes, flops, _ = algorithmic_work_backward(w)
+    fbytes, _, _ = algorithmic_work(w)
+    achieved_gbs = nbytes / (bwd_ms * 1e-3) / 1e9
+    achieved_tflops = flops / (bwd_ms * 1e-3) / 1e12
+    ck_bytes = ckpt.numel() * 4
+    log(f"forward with checkpoints {fwd_ms * 1e3:.1f} us (algorithmic {fbytes / (fwd_ms * 1e-3) / 1e9:.0f} GB/s "
+        f"+ {ck_bytes / 1e9:.2f} GB of checkpoints), backward {bwd_ms * 1e3:.1f} us; wall/step "
+        f"{t_wall / args.steps * 1e3:.3f} ms")
+    log(f"backward algorithmic bytes {nbytes / 1e9:.3f} GB -> {achieved_gbs:.0f} GB/s; flops {flops / 1e9:.1f} "
+        f"GFLOP -> {achieved_tflops:.1f} TFLOP/s")
+
+    # Sampled parity: the last two chunks of sequences (0, 0) and (B-1, H-1).
+    # No loss reaches past them, so their gradients are the oracle's on that
+    # window started from the oracle's own state after the chunks before it.
+    from oracle import linear_backward, linear_forward
+    t0 = (nch - 2) * w.b
+    errs = []
+    for (bi, hi) in ((0, 0), (B - 1, H - 1)):
+        g = {k: to_numpy64(v[bi, hi]) for k, v in inp.items() if v is not None}
+        _, Ms, Ss = linear_forward(g["q"][:t0], g["k"][:t0], g["v"][:t0], g["theta"][:t0], g["eta"][:t0],
+                                   g["alpha"][:t0], None, None, b=w.b)
+        ref = linear_backward(g["q"][t0:], g["k"][t0:], g["v"][t0:], g["theta"][t0:], g["eta"][t0:],
+                              g["alpha"][t0:], to_numpy64(cot["dz"][bi, hi, t0:]), None, None, Ms, Ss, b=w.b)
+        for x, r in zip(outs[:6], ref[:6]):
+            xg = x[bi, hi, t0:].double().cpu().numpy()
+            errs.append(float(np.max(np.abs(xg - r)) / np.sqrt(np.mean(r ** 2))))
+    parity = max(errs)
+    log(f"sampled parity (last two chunks of two sequences, every gradient): max|d|/rms = {parity:.3e}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_backward(w, inp, cot)
+        log(f"cpu baseline: {cpu}")
+    result = {
+        "metric": "training tokens/s (forward + backward) at H=16,d=128,b=64",
+        "value": B * T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "titans-linear-train", "B": B, "H": H, "T": T, "d": d, "b": w.b,
+                   "inputs": "bf16 q,k,v; f32 gates; f32 dz (seeded N(0,1))", "accumulate": "f32",
+                   "gradients": "f32", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
+                   "checkpoint_bytes": ck_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None, "traffic_unit": "bytes/launch",
+                     "algorithmic_bytes": nbytes, "kernel": "backward pass (carry walk + chunk gradients)",
+                     "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+        "parity_sample_max_rel_err": parity,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def varlen_lengths(total, seed=3001, mean=1024):
     """Seeded document lengths for a packed batch: lognormal (sigma 1) around `mean`,
     clipped to [1, 8192], the last one trimmed so that they sum to `total`."""
@@ -414,6 +580,8 @@ def main():
                     help="time token-by-token generation (primal form) on the Titans shapes instead")
     ap.add_argument("--varlen", action="store_true",
                     help="time packed variable-length documents with the Titans recipe instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="time one training step (forward with checkpoints + backward) on the Titans workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="(batch, head) sequences in the oracle sample (0: 64 for the linear memory, "
@@ -446,6 +614,9 @@ def main():
         return
     if args.varlen:
         varlen_main(args)
+        return
+    if args.backward:
+        backward_main(args)
         return
     w = WORKLOADS[args.workload]
     deep = w.hidden > 0

@@ -161,6 +161,18 @@ __device__ __forceinline__ void stage_unit(T* dst, const typename GlobalOf<T>::t
     }
 }
 
+// One 16-byte unit already in registers -> LDS as T.
+template <typename T>
+__device__ __forceinline__ void put_unit(T* dst, uint4 u) {
+    if constexpr (Op<T>::kF16) {
+        const f16x4 a = cvt4(f32x4{bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y)});
+        const f16x4 b = cvt4(f32x4{bf16lo(u.z), bf16hi(u.z), bf16lo(u.w), bf16hi(u.w)});
+        *reinterpret_cast<f16x8*>(dst) = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+        *reinterpret_cast<uint4*>(dst) = u;
+    }
+}
+
 // Four input elements (bf16 or float32) of a global row as float32.
 template <typename T>
 __device__ __forceinline__ f32x4 gload4(const typename GlobalOf<T>::type* src) {
@@ -178,22 +190,42 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// Chunk gates of one wave (lane = token l of a chunk padded to NP tokens with
-// theta = 0, eta = a = 1): prefix products A_l, E_l and c_l.
+// Inclusive scan across the wave (lane order) of the maps [[X, Y], [0, W]]:
+// lane l ends with T_l ... T_0 (T_0 applied first).
+__device__ __forceinline__ void map_scan(float& X, float& Y, float& W) {
+    tri_step<kRowShr1>(X, Y, W);
+    tri_step<kRowShr2>(X, Y, W);
+    tri_step<kRowShr4>(X, Y, W);
+    tri_step<kRowShr8>(X, Y, W);
+    tri_step<kRowBcast15, 0xa>(X, Y, W);
+    tri_step<kRowBcast31, 0xc>(X, Y, W);
+}
+
+// Chunk gates of one wave (lane = token l of a chunk padded with theta = 0,
+// eta = a = 1): T_l = [[a_l, eta_l], [0, eta_l]] composes to
+// T_l ... T_0 = [[A_l, c_l], [0, E_l]].
+__device__ __forceinline__ void gate_prefix(float my_a, float my_et, float& A, float& E, float& c) {
+    float X = my_a, Y = my_et, W = my_et;
+    map_scan(X, Y, W);
+    A = X;
+    c = Y;
+    E = W;
+}
+
+// Reverse linear recurrence r_i = u_i + f_i r_{i+1} over i = NP-1 .. 0
+// (lane i holds u_i and f_i; f_i multiplies the later value): the lanes are
+// reversed, scanned as maps [[f, u], [0, 1]] and reversed back.
 template <int NP>
-__device__ __forceinline__ void gate_prefix(float my_a, float my_et, int l, float& A, float& E, float& c) {
-    A = 1.f;
-    E = 1.f;
-    c = 0.f;
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        const float ai = readlane(my_a, i), ei = readlane(my_et, i);
-        if (i <= l) {
-            A *= ai;
-            E *= ei;
-            c = ai * c + E;
-        }
+__device__ __forceinline__ float reverse_recurrence(float u, float f, int lane) {
+    const int src = NP - 1 - lane;
+    const int from = src >= 0 ? src : lane;
+    float X = __shfl(f, from, kW), Y = __shfl(u, from, kW), W = 1.f;
+    if (src < 0) {
+        X = 1.f;
+        Y = 0.f;
     }
+    map_scan(X, Y, W);
+    return __shfl(Y, src >= 0 ? src : lane, kW);
 }
 
 // ===========================================================================
@@ -242,7 +274,7 @@ struct CarryGeo {
     // serial schedule.
     static constexpr int NQ = (3 * QSLOT + 2 * PSLOT + LS + 1024 <= kLdsMax) ? 3 : 1;
     static constexpr int NPR = NQ == 3 ? 2 : 1;
-    static constexpr int NWAVE = NS + 2;
+    static constexpr int NWAVE = NS + 3;            // state waves, two loaders, one builder
     static_assert(NQ * QSLOT + NPR * PSLOT + LS + 1024 <= kLdsMax, "LDS budget");
     static_assert(D % RB == 0 && NP % KG == 0, "tiling");
 };
@@ -281,11 +313,79 @@ struct Carry {
     using Sm = CarrySmem<T, D, NS, NP>;
     static constexpr int KG = Gm::KG, KS = R::KS, LQ = Gm::LQ, LZ = Gm::LZ, LP = Gm::LP, LF = Gm::LF;
 
-    // Stage chunk c: q, k rows (all features), dz columns row0..row0+RB-1, raw gates.
-    __device__ static void load(const CarryParams& p, typename Sm::QSlot& s, size_t tok0, int n, int row0,
-                                int lane) {
-        constexpr int CB = 16 / (int)sizeof(G);       // elements per 16-byte unit
-        constexpr int UR = Gm::DS / CB;              // units per row
+    // Loader: a chunk's q, k rows (all features), dz columns row0..row0+RB-1
+    // and gates are fetched into registers one step ahead (issue) and written
+    // to a staging slot the next step (commit), so HBM latency overlaps a
+    // whole chunk step.
+    static constexpr int CB = 16 / (int)sizeof(G);   // elements per 16-byte unit
+    static constexpr int UR = Gm::DS / CB;           // q / k units per row
+    static constexpr int NLW = 2;                    // loader waves
+    static constexpr int NQU = (NP * UR + NLW * kW - 1) / (NLW * kW);
+    static constexpr int UZ = Gm::RB / 4;            // dz units (4 floats) per row
+    static constexpr int NZU = (NP * UZ + NLW * kW - 1) / (NLW * kW);
+    struct Regs {
+        uint4 q[NQU], k[NQU];
+        f32x4 z[NZU];
+        float th, et, al;
+    };
+    // Loader wave lw (0 or 1) handles units lw*kW + lane + i*NLW*kW; wave 0 also the gates.
+    __device__ static void issue(const CarryParams& p, Regs& r, size_t tok0, int n, int row0, int lane, int lw) {
+        const G* q = static_cast<const G*>(p.q);
+        const G* k = static_cast<const G*>(p.k);
+#pragma unroll
+        for (int i = 0; i < NQU; ++i) {
+            const int u = lane + (lw + i * NLW) * kW;
+            const int t = u / UR, col = (u % UR) * CB;
+            const bool ok = u < NP * UR && t < n && col < D;
+            const size_t g = ok ? (tok0 + t) * D + col : 0;   // clamped: every load is in bounds
+            const uint4 a = *reinterpret_cast<const uint4*>(q + g);
+            const uint4 b = *reinterpret_cast<const uint4*>(k + g);
+            r.q[i] = ok ? a : uint4{0u, 0u, 0u, 0u};
+            r.k[i] = ok ? b : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < NZU; ++i) {
+            const int u = lane + (lw + i * NLW) * kW;
+            const int t = u / UZ, col = (u % UZ) * 4;
+            const bool ok = u < NP * UZ && t < n;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(p.dz + (ok ? (tok0 + t) * D + row0 + col : 0));
+            r.z[i] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const bool ok = lane < n;
+        const size_t gi = ok ? tok0 + lane : 0;
+        const float th = p.theta[gi], et = p.eta[gi], al = p.alpha[gi];
+        r.th = ok ? th : 0.f;
+        r.et = ok ? et : 1.f;
+        r.al = ok ? al : 0.f;
+    }
+    __device__ static void commit(const Regs& r, typename Sm::QSlot& s, int lane, int lw) {
+#pragma unroll
+        for (int i = 0; i < NQU; ++i) {
+            const int u = lane + (lw + i * NLW) * kW;
+            if (u < NP * UR) {
+                const int t = u / UR, col = (u % UR) * CB;
+                put_unit<T>(s.q + t * LQ + col, r.q[i]);
+                put_unit<T>(s.k + t * LQ + col, r.k[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NZU; ++i) {
+            const int u = lane + (lw + i * NLW) * kW;
+            if (u < NP * UZ) {
+                const int t = u / UZ, col = (u % UZ) * 4;
+                st4<T>(s.dz + t * LZ + col, r.z[i]);
+            }
+        }
+        if (lw == 0 && lane < NP) {
+            s.th[lane] = r.th;
+            s.et[lane] = r.et;
+            s.av[lane] = 1.f - r.al;
+        }
+    }
+
+    // Serial schedule (one slot): load and stage directly.
+    __device__ static void load_direct(const CarryParams& p, typename Sm::QSlot& s, size_t tok0, int n, int row0,
+                                       int lane) {
         const G* q = static_cast<const G*>(p.q);
         const G* k = static_cast<const G*>(p.k);
         for (int u = lane; u < NP * UR; u += kW) {
@@ -295,7 +395,6 @@ struct Carry {
             stage_unit<T>(s.q + t * LQ + col, q + (ok ? g : 0), ok);
             stage_unit<T>(s.k + t * LQ + col, k + (ok ? g : 0), ok);
         }
-        constexpr int UZ = Gm::RB / 4;
         for (int u = lane; u < NP * UZ; u += kW) {
             const int t = u / UZ, col = (u % UZ) * 4;
             const f32x4 v = t < n ? *reinterpret_cast<const f32x4*>(p.dz + (tok0 + t) * D + row0 + col)
@@ -315,7 +414,7 @@ struct Carry {
         const int lr = lane & 15, lg = lane >> 4;
         const float my_th = s.th[lane % NP], my_et = s.et[lane % NP], my_a = s.av[lane % NP];
         float A, E, c;
-        gate_prefix<NP>(my_a, my_et, lane, A, E, c);
+        gate_prefix(my_a, my_et, A, E, c);
         if (lane < NP) {
             ps.A[lane] = A;
             ps.c[lane] = c;
@@ -402,13 +501,16 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
     auto chunk_n = [&](int c) { return min(p.b, p.T - c * p.b); };
 
     const bool is_state = w < NS;
-    const bool is_loader = w == NS;
-    const bool is_builder = w == NS + 1;
+    const bool is_loader = w == NS || w == NS + 1;
+    const bool is_builder = w == NS + 2;
+    const int lw = w - NS;   // loader index
 
-    auto do_load = [&](int u) {
+    typename C::Regs lr_regs;
+    auto do_issue = [&](int u) {
         const int c = chunk_of(u);
-        C::load(p, sm.qs[u % Gm::NQ], seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane);
+        C::issue(p, lr_regs, seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane, lw);
     };
+    auto do_commit = [&](int u) { C::commit(lr_regs, sm.qs[u % Gm::NQ], lane, lw); };
     auto do_build = [&](int u) {
         const int c = chunk_of(u);
         C::build(sm.qs[u % Gm::NQ], sm.ps[u % Gm::NPR], sm.ls, chunk_n(c), lane);
@@ -420,7 +522,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
     const int r0l = 16 * w;
     const int r0 = row_wg + r0l;
     const size_t st_off = static_cast<size_t>(bh) * D * D + static_cast<size_t>(r0 + lr) * D;
-    if (is_state) {
+    auto state_init = [&]() {
 #pragma unroll
         for (int jt = 0; jt < NCT; ++jt) {
             const int col = O::tmap(jt, 4 * lg);
@@ -428,7 +530,17 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
             dM[jt] = (p.dMT && ok) ? *reinterpret_cast<const f32x4*>(p.dMT + st_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
             dS[jt] = (p.dST && ok) ? *reinterpret_cast<const f32x4*>(p.dST + st_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    }
+    };
+    auto state_final = [&]() {
+#pragma unroll
+        for (int jt = 0; jt < NCT; ++jt) {
+            const int col = O::tmap(jt, 4 * lg);
+            if (col < D) {
+                if (p.dM0) *reinterpret_cast<f32x4*>(p.dM0 + st_off + col) = dM[jt];
+                if (p.dS0) *reinterpret_cast<f32x4*>(p.dS0 + st_off + col) = dS[jt];
+            }
+        }
+    };
 
     auto do_state = [&](int u) {
         const int c = chunk_of(u);
@@ -509,42 +621,59 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         }
     };
 
+    // Each role runs its own loop; the loops execute the same barriers.
     if constexpr (Gm::NQ == 3) {
-        if (is_loader && nch > 0) do_load(0);
-        __syncthreads();
-        if (is_builder && nch > 0) do_build(0);
-        if (is_loader && nch > 1) do_load(1);
-        __syncthreads();
-        for (int u = 0; u < nch; ++u) {
-            if (is_state) do_state(u);
-            else if (is_builder) {
-                if (u + 1 < nch) do_build(u + 1);
-            } else if (u + 2 < nch) {
-                do_load(u + 2);
-            }
+        // Step u: state waves on chunk u, builder on u + 1, loader commits
+        // u + 2 and fetches u + 3.
+        if (is_state) {
+            state_init();
             __syncthreads();
+            __syncthreads();
+            for (int u = 0; u < nch; ++u) {
+                do_state(u);
+                __syncthreads();
+            }
+            state_final();
+        } else if (is_builder) {
+            __syncthreads();
+            if (nch > 0) do_build(0);
+            __syncthreads();
+            for (int u = 0; u < nch; ++u) {
+                if (u + 1 < nch) do_build(u + 1);
+                __syncthreads();
+            }
+        } else {
+            if (nch > 0) {
+                do_issue(0);
+                do_commit(0);
+            }
+            if (nch > 1) do_issue(1);
+            __syncthreads();
+            if (nch > 1) do_commit(1);
+            if (nch > 2) do_issue(2);
+            __syncthreads();
+            for (int u = 0; u < nch; ++u) {
+                if (u + 2 < nch) do_commit(u + 2);
+                if (u + 3 < nch) do_issue(u + 3);
+                __syncthreads();
+            }
         }
     } else {
+        if (is_state) state_init();
         for (int u = 0; u < nch; ++u) {
-            if (is_loader) do_load(u);
+            if (w == NS) {
+                const int c = chunk_of(u);
+                C::load_direct(p, sm.qs[0], seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane);
+            }
             __syncthreads();
             if (is_builder) do_build(u);
             __syncthreads();
             if (is_state) do_state(u);
             __syncthreads();
         }
+        if (is_state) state_final();
     }
 
-    if (is_state) {
-#pragma unroll
-        for (int jt = 0; jt < NCT; ++jt) {
-            const int col = O::tmap(jt, 4 * lg);
-            if (col < D) {
-                if (p.dM0) *reinterpret_cast<f32x4*>(p.dM0 + st_off + col) = dM[jt];
-                if (p.dS0) *reinterpret_cast<f32x4*>(p.dS0 + st_off + col) = dS[jt];
-            }
-        }
-    }
 }
 
 // ===========================================================================
@@ -578,8 +707,9 @@ struct GradGeo {
     static constexpr int KG = O::KG;
     static constexpr int KS = KG / 4;
     static constexpr int DS = bmax(D, KG);
-    static constexpr int NF = D / 16;           // feature tiles, one wave each
-    static constexpr int NWAVE = 1 + NF;        // plus the gate wave
+    static constexpr int NF = D / 16;           // feature tiles
+    static constexpr int FPW = D >= 128 ? 1 : 1; // feature tiles per wave (register budget)
+    static constexpr int NWAVE = 1 + NF / FPW;  // plus the gate wave
     static constexpr int NT = NP / 16;
     static constexpr int NKD = DS / KG;
     static constexpr int NKT = NP / KG;
@@ -608,7 +738,7 @@ struct GradSmem {
     alignas(16) T dz[Gm::DZ_LDS ? NP * Gm::LQ : 8];
     alignas(16) T de[Gm::DZ_LDS ? NP * Gm::LQ : 8];
     alignas(16) T dlt[NP * Gm::LPT];             // -(D .* L)^T
-    alignas(16) float lm[NP * Gm::LF];           // L_ij; then the eta contributions
+    alignas(16) float lm[NP * Gm::LF];           // gamma_ij; then the eta contributions
     alignas(16) float dl[NP * Gm::LF];           // dL_ij; then the a contributions
     alignas(16) float th[NP];
     alignas(16) float et[NP];
@@ -651,23 +781,57 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         constexpr int UR = Gm::DS / CB;
         const G* q = static_cast<const G*>(p.q);
         const G* k = static_cast<const G*>(p.k);
-        for (int u = tid; u < NP * UR; u += kW * Gm::NWAVE) {
+        // All loads of a thread first (clamped, always in bounds), then the
+        // LDS writes: one HBM latency for the whole staging.
+        constexpr int NTH = kW * Gm::NWAVE;
+        constexpr int NQU = (NP * UR + NTH - 1) / NTH;
+        uint4 qa[NQU], ka[NQU];
+#pragma unroll
+        for (int i = 0; i < NQU; ++i) {
+            const int u = tid + i * NTH;
             const int t = u / UR, col = (u % UR) * CB;
-            const bool ok = t < n && col < D;
-            const size_t g = (tok0 + t) * D + col;
-            stage_unit<T>(sm.q + t * LQ + col, q + (ok ? g : 0), ok);
-            stage_unit<T>(sm.k + t * LQ + col, k + (ok ? g : 0), ok);
-            if constexpr (Gm::DS > D) stage_unit<T>(sm.ec + t * LQ + col, q, false);
+            const bool ok = u < NP * UR && t < n && col < D;
+            const size_t g = ok ? (tok0 + t) * D + col : 0;
+            const uint4 a = *reinterpret_cast<const uint4*>(q + g);
+            const uint4 b = *reinterpret_cast<const uint4*>(k + g);
+            qa[i] = ok ? a : uint4{0u, 0u, 0u, 0u};
+            ka[i] = ok ? b : uint4{0u, 0u, 0u, 0u};
+        }
+        constexpr int U4 = Gm::DS / 4;
+        constexpr int NZU = Gm::DZ_LDS ? (NP * U4 + NTH - 1) / NTH : 1;
+        f32x4 za[NZU], va[NZU];
+        if constexpr (Gm::DZ_LDS) {
+#pragma unroll
+            for (int i = 0; i < NZU; ++i) {
+                const int u = tid + i * NTH;
+                const int t = u / U4, col = (u % U4) * 4;
+                const bool ok = u < NP * U4 && t < n && col < D;
+                const size_t g = ok ? (tok0 + t) * D + col : 0;
+                const f32x4 z4 = *reinterpret_cast<const f32x4*>(p.dz + g);
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(p.dv + g);
+                za[i] = ok ? z4 : f32x4{0.f, 0.f, 0.f, 0.f};
+                va[i] = ok ? -v4 : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NQU; ++i) {
+            const int u = tid + i * NTH;
+            if (u < NP * UR) {
+                const int t = u / UR, col = (u % UR) * CB;
+                put_unit<T>(sm.q + t * LQ + col, qa[i]);
+                put_unit<T>(sm.k + t * LQ + col, ka[i]);
+                if constexpr (Gm::DS > D) put_unit<T>(sm.ec + t * LQ + col, uint4{0u, 0u, 0u, 0u});
+            }
         }
         if constexpr (Gm::DZ_LDS) {
-            constexpr int U4 = Gm::DS / 4;
-            for (int u = tid; u < NP * U4; u += kW * Gm::NWAVE) {
-                const int t = u / U4, col = (u % U4) * 4;
-                const bool ok = t < n && col < D;
-                const f32x4 z4 = ok ? *reinterpret_cast<const f32x4*>(p.dz + (tok0 + t) * D + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-                const f32x4 v4 = ok ? *reinterpret_cast<const f32x4*>(p.dv + (tok0 + t) * D + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-                st4<T>(sm.dz + t * LQ + col, z4);
-                st4<T>(sm.de + t * LQ + col, -v4);
+#pragma unroll
+            for (int i = 0; i < NZU; ++i) {
+                const int u = tid + i * NTH;
+                if (u < NP * U4) {
+                    const int t = u / U4, col = (u % U4) * 4;
+                    st4<T>(sm.dz + t * LQ + col, za[i]);
+                    st4<T>(sm.de + t * LQ + col, va[i]);
+                }
             }
         }
         for (int l = tid; l < NP; l += kW * Gm::NWAVE) {
@@ -706,13 +870,12 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         const int l = lane;
         const float my_th = sm.th[l % NP], my_et = sm.et[l % NP], my_a = sm.av[l % NP];
         float A, E, cc;
-        gate_prefix<NP>(my_a, my_et, l, A, E, cc);
+        gate_prefix(my_a, my_et, A, E, cc);
         if (l < NP) {
             sm.A[l] = A;
             sm.Ev[l] = E;
             sm.c[l] = cc;
         }
-        float gam[NP], pm[NP];
         float g = 0.f, pp = 0.f, wm = 0.f, ws = 0.f;
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
@@ -724,9 +887,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 pp = ei * pp;
                 g = ai * g + pp;
             }
-            gam[i] = g;
-            pm[i] = pp;
-            if (l < NP) sm.lm[i * LF + l] = my_th * g;
+            if (l < NP) sm.lm[i * LF + l] = g;
             if (i == n - 1) {
                 wm = my_th * g;
                 ws = my_th * pp;
@@ -739,9 +900,9 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         __syncthreads();   // (1) gates and residual tiles ready
 
         // Lower tiles of G = Q K^T and D = dZ E^T: dL = -G .* D, -(D .* L)^T.
-#pragma unroll
+#pragma unroll 1
         for (int it = 0; it < NT; ++it) {
-#pragma unroll
+#pragma unroll 1
             for (int jt = 0; jt < NT; ++jt) {
                 const int j = 16 * jt + lr;
                 T* dst = sm.dlt + j * LPT + 16 * it + 4 * lg;
@@ -756,11 +917,12 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                     dacc = O::mma(dacc, zfrag(sm.dz, p.dz, 1.f, 16 * it + lr, kk * KG), R::rm(sm.ec, LQ, j, kk * KG, lg));
                 }
                 f32x4 nd;
+                const float thj = sm.th[j];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 16 * it + 4 * lg + e;
                     const bool ok = j <= i;
-                    nd[e] = ok ? -dacc[e] * sm.lm[i * LF + j] : 0.f;
+                    nd[e] = ok ? -dacc[e] * (thj * sm.lm[i * LF + j]) : 0.f;
                     sm.dl[i * LF + j] = ok ? -gacc[e] * dacc[e] : 0.f;
                 }
                 st4<T>(dst, nd);
@@ -783,37 +945,52 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         }
 
         // Reverse through the column recurrences of gamma and p (lane = column j).
+        // Row i reads gamma rows i, i-1 and dL row i; the loads for the next
+        // row are issued one iteration ahead.  p comes back from gamma without
+        // a division: p_ij = gamma_ij - a_i gamma_{i-1,j} (gamma_{j-1,j} = 0).
+        const int lc = l < NP ? l : 0;
         float gg = 0.f, gp = 0.f, dth = 0.f;
+        float g_i = sm.lm[(NP - 1) * LF + lc];
+        float g_im1 = NP > 1 ? sm.lm[(NP - 2) * LF + lc] : 0.f;
+        float d_i = sm.dl[(NP - 1) * LF + lc];
 #pragma unroll
         for (int i = NP - 1; i >= 0; --i) {
+            const float g_im2 = i >= 2 ? sm.lm[(i >= 2 ? i - 2 : 0) * LF + lc] : 0.f;
+            const float d_im1 = i >= 1 ? sm.dl[(i >= 1 ? i - 1 : 0) * LF + lc] : 0.f;
             const bool act = i >= l && i < n;
-            float dli = act ? sm.dl[i * LF + l] : 0.f;
+            float dli = act ? d_i : 0.f;
             const bool last = act && i == n - 1;
             if (last) dli += dwm_j;
             gg += my_th * dli;
-            dth += dli * gam[i];
+            dth += dli * g_i;
+            const float a_i = readlane(my_a, i);
             if (last) {
                 gp += my_th * dws_j;
-                dth += dws_j * pm[i];
+                dth += dws_j * (g_i - a_i * g_im1);
             }
             float ca = 0.f, ce = 0.f;
             if (i > 0 && i > l) {
-                ca = gg * gam[i > 0 ? i - 1 : 0];
+                const float a_im1 = readlane(my_a, i > 0 ? i - 1 : 0);
+                ca = gg * g_im1;
                 gp += gg;
-                ce = gp * pm[i > 0 ? i - 1 : 0];
-                gg *= readlane(my_a, i);
+                ce = gp * (g_im1 - a_im1 * g_im2);
+                gg *= a_i;
                 gp *= readlane(my_et, i);
             }
             if (l < NP) {
                 sm.dl[i * LF + l] = ca;
                 sm.lm[i * LF + l] = ce;
             }
+            g_i = g_im1;
+            g_im1 = g_im2;
+            d_i = d_im1;
+            __builtin_amdgcn_sched_barrier(0);
         }
         wave_lds_fence();
         // Row sums (lane = row i) and the prefix-product part.
         float sa = 0.f, se = 0.f;
         if (l < NP) {
-#pragma unroll
+#pragma unroll 2
             for (int j = 0; j < NP; j += 4) {
                 const f32x4 va = *reinterpret_cast<const f32x4*>(sm.dl + l * LF + j);
                 const f32x4 ve = *reinterpret_cast<const f32x4*>(sm.lm + l * LF + j);
@@ -823,24 +1000,13 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         }
         const float my_dA = dA_l + (l == n - 1 ? dot0 : 0.f);
         const float my_dc = dc_l + (l == n - 1 ? dot1 : 0.f);
-        float rA = 0.f, rc = 0.f, gA = 0.f, gc = 0.f;
-#pragma unroll
-        for (int i = NP - 1; i >= 0; --i) {
-            const float an = i + 1 < NP ? readlane(my_a, i + 1) : 0.f;
-            rA = an * rA + readlane(my_dA, i);
-            rc = an * rc + readlane(my_dc, i);
-            if (i == l) {
-                gA = rA;
-                gc = rc;
-            }
-        }
-        float rE = 0.f, gE = 0.f;
-#pragma unroll
-        for (int i = NP - 1; i >= 0; --i) {
-            const float en = i + 1 < NP ? readlane(my_et, i + 1) : 0.f;
-            rE = en * rE + readlane(gc, i) + (i == n - 1 ? dEn : 0.f);
-            if (i == l) gE = rE;
-        }
+        // g_i = u_i + f_i g_{i+1} with f_i = a_{i+1} (A and c) or eta_{i+1} (E).
+        const float a_next = __shfl(my_a, l + 1 < kW ? l + 1 : l, kW);
+        const float e_next = __shfl(my_et, l + 1 < kW ? l + 1 : l, kW);
+        const float fa = l + 1 < NP ? a_next : 0.f, fe = l + 1 < NP ? e_next : 0.f;
+        const float gA = reverse_recurrence<NP>(my_dA, fa, l);
+        const float gc = reverse_recurrence<NP>(my_dc, fa, l);
+        const float gE = reverse_recurrence<NP>(gc + (l == n - 1 ? dEn : 0.f), fe, l);
         if (l < n) {
             const float A_prev = l > 0 ? sm.A[l - 1] : 1.f;
             const float c_prev = l > 0 ? sm.c[l - 1] : 0.f;
@@ -853,26 +1019,53 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         }
     } else {
         // ===================== feature wave =====================
-        const int f0 = 16 * (w - 1);   // rows (phase 1) / features (phases 2, 3) f0 .. f0+15
-        // Residual rows of E^T: E^T[r][t] = M0[r][:] . k_t - v_t[r], r = f0 + (acc row).
-        {
+        // Feature tiles fw*FPW .. fw*FPW + FPW - 1, 16 rows (residuals) or
+        // features (gradients) each.
+        constexpr int FPW = Gm::FPW;
+        const int fw = w - 1;
+        // Columns f0 .. f0+15 of a state as an operand whose rows are those
+        // columns (k = row of the state): raw loads, then conversion, so the
+        // next state's loads are in flight while the current one is used.
+        constexpr int NRAW = NKD * KS;
+        auto colload = [&](const float* X, int f0, float* raw) {
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) {
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) {
+                    const int r = kk * KG + KS * lg + s2;
+                    raw[kk * KS + s2] = X[static_cast<size_t>(r < D ? r : 0) * D + f0 + lr];
+                }
+            }
+        };
+        auto colcvt = [&](const float* raw, F* out) {
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) {
+                float x[KS];
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) x[s2] = kk * KG + KS * lg + s2 < D ? raw[kk * KS + s2] : 0.f;
+                out[kk] = R::from_f32(x);
+            }
+        };
+        // Residual rows of E^T: E^T[r][t] = M0[r][:] . k_t - v_t[r].
+        const G* vg = static_cast<const G*>(p.v);
+#pragma unroll
+        for (int ft = 0; ft < FPW; ++ft) {
+            const int f0 = 16 * (fw * FPW + ft);
             F am[NKD];
+            const size_t ro = static_cast<size_t>(f0 + lr) * D;
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
                 float x[KS];
                 const int col = kk * KG + KS * lg;
 #pragma unroll
-                for (int s = 0; s < KS; s += 4) {
-                    const f32x4 v4 = col + s < D ? *reinterpret_cast<const f32x4*>(Mc + (f0 + lr) * D + col + s)
-                                                 : f32x4{0.f, 0.f, 0.f, 0.f};
-                    x[s] = v4[0];
-                    x[s + 1] = v4[1];
-                    x[s + 2] = v4[2];
-                    x[s + 3] = v4[3];
+                for (int s4 = 0; s4 < KS; s4 += 4) {
+                    const bool ok = col + s4 < D;
+                    const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mc + ro + (ok ? col + s4 : 0));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[s4 + e] = ok ? m4[e] : 0.f;
                 }
                 am[kk] = R::from_f32(x);
             }
-            const G* vg = static_cast<const G*>(p.v);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 const int t = 16 * tt + lr;
@@ -883,103 +1076,131 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 st4<T>(sm.ec + t * LQ + f0 + 4 * lg, acc - vv);
             }
         }
-        // Columns f0 .. f0+15 of M0, S0, dM', dS' as operand fragments whose
-        // rows are those columns (k = row of the state), and their dots.
-        F mcf[NKD], scf[NKD], dmf[NKD], dsf[NKD];
-        float d1 = 0.f, d2 = 0.f, d3 = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) {
-            float xm[KS], xs[KS], xdm[KS], xds[KS];
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int r = kk * KG + KS * lg + s;
-                const bool ok = r < D;
-                const size_t o = static_cast<size_t>(ok ? r : 0) * D + f0 + lr;
-                xm[s] = ok ? Mc[o] : 0.f;
-                xs[s] = ok ? Sc[o] : 0.f;
-                xdm[s] = ok ? dMe[o] : 0.f;
-                xds[s] = ok ? dSe[o] : 0.f;
-                d1 += xdm[s] * xm[s];
-                d2 += xdm[s] * xs[s];
-                d3 += xds[s] * xs[s];
-            }
-            mcf[kk] = R::from_f32(xm);
-            scf[kk] = R::from_f32(xs);
-            dmf[kk] = R::from_f32(xdm);
-            dsf[kk] = R::from_f32(xds);
-        }
-        d1 = wave_sum(d1);
-        d2 = wave_sum(d2);
-        d3 = wave_sum(d3);
+        float raw[NRAW];
+        colload(Sc, 16 * fw * FPW, raw);
         __syncthreads();   // (1)
 
         // Products with features f0.. as rows and tokens as columns: lane
         // (lr, lg) holds features f0 + 4lg + e of token t = 16tt + lr.
-        f32x4 dQ[NT], dK[NT];
-        float pa[NT], pc[NT], pwm[NT], pws[NT];
         auto red = [&](float x) {
             x += __shfl_xor(x, 16, kW);
             x += __shfl_xor(x, 32, kW);
             return x;
         };
+        auto rdot = [&](const f32x4& a, const f32x4& b) { return red((a[0] * b[0] + a[1] * b[1]) + (a[2] * b[2] + a[3] * b[3])); };
+        // The three state dots over the wave's columns (every element of the
+        // d x d states once over the feature waves), from the operand
+        // fragments (the positions of two states' fragments coincide).
+        auto fdot = [&](const F* a, const F* b) {
+            float acc = 0.f;
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            const int t = 16 * tt + lr;
-            f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = X, H = X, U = X, W = X;
+            for (int kk = 0; kk < NKD; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < NKD; ++kk) {
-                const F zf = zfrag(sm.dz, p.dz, 1.f, t, kk * KG);
-                const F ef = zfrag(sm.de, p.dv, -1.f, t, kk * KG);
-                const F cf = R::rm(sm.ec, LQ, t, kk * KG, lg);
-                X = O::mma(X, mcf[kk], zf);
-                Y = O::mma(Y, scf[kk], zf);
-                H = O::mma(H, mcf[kk], ef);
-                U = O::mma(U, dmf[kk], cf);
-                W = O::mma(W, dsf[kk], cf);
+                for (int s2 = 0; s2 < KS; ++s2) acc += static_cast<float>(a[kk][s2]) * static_cast<float>(b[kk][s2]);
+            return acc;
+        };
+        float d1 = 0.f, d2 = 0.f, d3 = 0.f;
+        f32x4 dQ[FPW][NT], dK[FPW][NT];
+        float pa[FPW][NT], pc[FPW][NT], pwm[FPW][NT], pws[FPW][NT];
+#pragma unroll
+        for (int ft = 0; ft < FPW; ++ft) {
+            const int f0 = 16 * (fw * FPW + ft);
+            F fs[NKD], fo[NKD], fm[NKD];
+            colcvt(raw, fs);                       // S0
+            colload(dSe, f0, raw);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = 16 * tt + lr;
+                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) Y = O::mma(Y, fs[kk], zfrag(sm.dz, p.dz, 1.f, t, kk * KG));
+                pc[ft][tt] = rdot(ld4<T>(sm.q + t * LQ + f0 + 4 * lg), Y);
+                dQ[ft][tt] = sm.c[t] * Y;
             }
-            const f32x4 qv = ld4<T>(sm.q + t * LQ + f0 + 4 * lg);
-            const f32x4 kv = ld4<T>(sm.k + t * LQ + f0 + 4 * lg);
-            pa[tt] = red((qv[0] * X[0] + qv[1] * X[1]) + (qv[2] * X[2] + qv[3] * X[3]));
-            pc[tt] = red((qv[0] * Y[0] + qv[1] * Y[1]) + (qv[2] * Y[2] + qv[3] * Y[3]));
-            pwm[tt] = -red((kv[0] * U[0] + kv[1] * U[1]) + (kv[2] * U[2] + kv[3] * U[3]));
-            pws[tt] = -red((kv[0] * W[0] + kv[1] * W[1]) + (kv[2] * W[2] + kv[3] * W[3]));
-            const float At = sm.A[t], ct = sm.c[t], wmt = sm.wm[t], wst = sm.ws[t];
-            dQ[tt] = At * X + ct * Y;
-            dK[tt] = H - wmt * U - wst * W;
+            colcvt(raw, fo);                       // dS'
+            d3 += fdot(fo, fs);
+            colload(dMe, f0, raw);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = 16 * tt + lr;
+                f32x4 W = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) W = O::mma(W, fo[kk], R::rm(sm.ec, LQ, t, kk * KG, lg));
+                pws[ft][tt] = -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), W);
+                dK[ft][tt] = -sm.ws[t] * W;
+            }
+            colcvt(raw, fo);                       // dM'
+            d2 += fdot(fo, fs);
+            colload(Mc, f0, raw);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = 16 * tt + lr;
+                f32x4 U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) U = O::mma(U, fo[kk], R::rm(sm.ec, LQ, t, kk * KG, lg));
+                pwm[ft][tt] = -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), U);
+                dK[ft][tt] -= sm.wm[t] * U;
+            }
+            colcvt(raw, fm);                       // M0
+            d1 += fdot(fo, fm);
+            if (ft + 1 < FPW) colload(Sc, f0 + 16, raw);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = 16 * tt + lr;
+                f32x4 X = {0.f, 0.f, 0.f, 0.f}, H = X;
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) {
+                    X = O::mma(X, fm[kk], zfrag(sm.dz, p.dz, 1.f, t, kk * KG));
+                    H = O::mma(H, fm[kk], zfrag(sm.de, p.dv, -1.f, t, kk * KG));
+                }
+                pa[ft][tt] = rdot(ld4<T>(sm.q + t * LQ + f0 + 4 * lg), X);
+                dQ[ft][tt] += sm.A[t] * X;
+                dK[ft][tt] += H;
+            }
         }
+        d1 = wave_sum(d1);
+        d2 = wave_sum(d2);
+        d3 = wave_sum(d3);
         __syncthreads();   // (2) residual tile consumed
-        {
-            float* pf = part + (w - 1) * Gm::PART;
+#pragma unroll
+        for (int ft = 0; ft < FPW; ++ft) {
+            float* pf = part + (fw * FPW + ft) * Gm::PART;
             if (lg == 0) {
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
                     const int t = 16 * tt + lr;
-                    pf[t] = pa[tt];
-                    pf[NP + t] = pc[tt];
-                    pf[2 * NP + t] = pwm[tt];
-                    pf[3 * NP + t] = pws[tt];
+                    pf[t] = pa[ft][tt];
+                    pf[NP + t] = pc[ft][tt];
+                    pf[2 * NP + t] = pwm[ft][tt];
+                    pf[3 * NP + t] = pws[ft][tt];
                 }
             }
             if (lane == 0) {
-                pf[4 * NP] = d1;
-                pf[4 * NP + 1] = d2;
-                pf[4 * NP + 2] = d3;
+                pf[4 * NP] = ft == 0 ? d1 : 0.f;
+                pf[4 * NP + 1] = ft == 0 ? d2 : 0.f;
+                pf[4 * NP + 2] = ft == 0 ? d3 : 0.f;
             }
         }
         __syncthreads();   // (3)
 
         // dQ -= (DL K)^T, dK -= (DL^T Q)^T  (dlt holds -DL^T).
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
+        for (int ft = 0; ft < FPW; ++ft) {
+            const int f0 = 16 * (fw * FPW + ft);
 #pragma unroll
-            for (int kk = 0; kk < NKT; ++kk) {
-                dQ[tt] = O::mma(dQ[tt], R::cm(sm.k, LQ, kk * KG, f0, lr, lg), R::cm(sm.dlt, LPT, kk * KG, 16 * tt, lr, lg));
-                dK[tt] = O::mma(dK[tt], R::cm(sm.q, LQ, kk * KG, f0, lr, lg), R::rm(sm.dlt, LPT, 16 * tt + lr, kk * KG, lg));
-            }
-            const int t = 16 * tt + lr;
-            if (t < n) {
-                *reinterpret_cast<f32x4*>(p.dq + (tok0 + t) * D + f0 + 4 * lg) = dQ[tt];
-                *reinterpret_cast<f32x4*>(p.dk + (tok0 + t) * D + f0 + 4 * lg) = dK[tt];
+            for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+                for (int kk = 0; kk < NKT; ++kk) {
+                    dQ[ft][tt] = O::mma(dQ[ft][tt], R::cm(sm.k, LQ, kk * KG, f0, lr, lg),
+                                        R::cm(sm.dlt, LPT, kk * KG, 16 * tt, lr, lg));
+                    dK[ft][tt] = O::mma(dK[ft][tt], R::cm(sm.q, LQ, kk * KG, f0, lr, lg),
+                                        R::rm(sm.dlt, LPT, 16 * tt + lr, kk * KG, lg));
+                }
+                const int t = 16 * tt + lr;
+                if (t < n) {
+                    *reinterpret_cast<f32x4*>(p.dq + (tok0 + t) * D + f0 + 4 * lg) = dQ[ft][tt];
+                    *reinterpret_cast<f32x4*>(p.dk + (tok0 + t) * D + f0 + 4 * lg) = dK[ft][tt];
+                }
             }
         }
     }
