@@ -103,6 +103,9 @@ def measured_traffic(w, kind="forward"):
     if kind == "decode":
         path = os.path.join(ROOT, "profiles", "linear_memory_decode_titans_d128_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_decode.hip")
+    elif kind == "backward":
+        path = os.path.join(ROOT, "profiles", "linear_memory_train_titans_d128_b64_traffic.json")
+        src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear_bwd.hip")
     else:
         path = os.path.join(ROOT, "profiles", "linear_memory_fwd_titans_d128_b64_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear.hip")
@@ -404,7 +407,8 @@ def backward_main(args):
                    "gradients": "f32", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                    "checkpoint_bytes": ck_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None, "traffic_unit": "bytes/launch",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w, "backward"),
+                     "traffic_unit": "bytes/launch",
                      "algorithmic_bytes": nbytes, "kernel": "backward pass (carry walk + chunk gradients)",
                      "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,

@@ -708,7 +708,7 @@ struct GradGeo {
     static constexpr int KS = KG / 4;
     static constexpr int DS = bmax(D, KG);
     static constexpr int NF = D / 16;           // feature tiles
-    static constexpr int FPW = D >= 128 ? 1 : 1; // feature tiles per wave (register budget)
+    static constexpr int FPW = 1; // feature tiles per wave (register budget)
     static constexpr int NWAVE = 1 + NF / FPW;  // plus the gate wave
     static constexpr int NT = NP / 16;
     static constexpr int NKD = DS / KG;
@@ -984,6 +984,9 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             g_i = g_im1;
             g_im1 = g_im2;
             d_i = d_im1;
+            // Keep the running sums in registers row by row (the compiler
+            // would otherwise defer them and hold every row's dL live).
+            asm volatile("" : "+v"(dth), "+v"(gg), "+v"(gp));
             __builtin_amdgcn_sched_barrier(0);
         }
         wave_lds_fence();
