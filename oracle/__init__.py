@@ -18,6 +18,10 @@ What it computes, in the pages' own order (a per-token loop, float64):
   per-token loop.  Pinned by central finite differences of the pinned forward,
   the pages' scalar outer-gradient examples, and the closed-form gradients of
   weighted linear attention.
+* ``linear_forward_chunk_gates`` / ``linear_backward_chunk_gates`` -- the same
+  iteration with gates shared by the tokens of a chunk.  Pinned by the closed
+  form that the shared gates allow (a geometric decay sum inside a chunk) and
+  by finite differences of the chunk gates.
 * ``mlp_forward`` -- the same schedule for a 2-layer MLP memory
   ``f(u) = u + SiLU(u W1) W2`` with gradients by explicit backprop.  Pinned by
   torch.autograd (a library routine), finite differences, and by agreement of
@@ -28,6 +32,8 @@ Every function here is pinned by tests in ``tests/test_oracle_*.py``; none is
 "parity unpinned".
 """
 
-from .memory import linear_forward, linear_backward, mlp_forward, silu, silu_grad, mlp_chunk_grads
+from .memory import (linear_backward, linear_backward_chunk_gates, linear_forward, linear_forward_chunk_gates,
+                     mlp_forward, silu, silu_grad, mlp_chunk_grads)
 
-__all__ = ["linear_forward", "linear_backward", "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]
+__all__ = ["linear_forward", "linear_backward", "linear_forward_chunk_gates", "linear_backward_chunk_gates",
+           "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]

@@ -33,7 +33,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["linear_forward", "linear_backward", "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]
+__all__ = ["linear_forward", "linear_backward", "linear_forward_chunk_gates", "linear_backward_chunk_gates",
+           "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]
 
 
 def _f64(x):
@@ -180,6 +181,42 @@ def linear_backward(q, k, v, theta, eta, alpha, dz, dM_T=None, dS_T=None, M0=Non
             gMc = gMc + _outer(ge, k_t)
         gM = gM + gMc                          # M_c is the state entering the chunk
     return gq, gk, gv, gth, get, gal, gM, gS
+
+
+def _expand_chunk_gates(g, T, b):
+    """[..., NC] per-chunk values -> [..., T]: every token of chunk c takes entry c."""
+    g = _f64(g)
+    return np.repeat(g, b, axis=-1)[..., :T]
+
+
+def linear_forward_chunk_gates(q, k, v, theta, eta, alpha, M0=None, S0=None, b=1):
+    """``linear_forward`` with gates shared by the tokens of each chunk.
+
+    "论文速览 | Titans" section 4.6: a faster variant in which alpha, theta and
+    eta do not depend on the token but are shared within a chunk.  ``theta,
+    eta, alpha`` are ``[..., ceil(T/b)]``; token t of chunk c = t // b uses
+    entry c.  The iteration itself is unchanged.
+    """
+    T = np.shape(q)[-2]
+    return linear_forward(q, k, v, _expand_chunk_gates(theta, T, b), _expand_chunk_gates(eta, T, b),
+                          _expand_chunk_gates(alpha, T, b), M0, S0, b=b)
+
+
+def linear_backward_chunk_gates(q, k, v, theta, eta, alpha, dz, dM_T=None, dS_T=None, M0=None, S0=None, b=1):
+    """Gradient of ``linear_forward_chunk_gates``: a gate shared by a chunk's
+    tokens collects the sum of their per-token gradients (chain rule through
+    the broadcast)."""
+    T = np.shape(q)[-2]
+    g = linear_backward(q, k, v, _expand_chunk_gates(theta, T, b), _expand_chunk_gates(eta, T, b),
+                        _expand_chunk_gates(alpha, T, b), dz, dM_T, dS_T, M0, S0, b=b)
+    nc = (T + b - 1) // b
+
+    def per_chunk(x):
+        pad = nc * b - T
+        x = np.concatenate([x, np.zeros(x.shape[:-1] + (pad,))], axis=-1) if pad else x
+        return x.reshape(x.shape[:-1] + (nc, b)).sum(axis=-1)
+
+    return g[0], g[1], g[2], per_chunk(g[3]), per_chunk(g[4]), per_chunk(g[5]), g[6], g[7]
 
 
 def silu(x):
