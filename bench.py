@@ -13,9 +13,13 @@ Titans recipe (32768 tokens per head in documents of seeded lengths, each
 from its own state).  ``--backward`` times one training step of the Titans
 linear memory: the forward that saves the chunk-start states plus the
 backward pass (gradients for q, k, v, the three gates and the initial state),
-with a seeded synthetic outer-loss derivative dz.  Prints ONE JSON line.
+with a seeded synthetic outer-loss derivative dz.  ``--chunk-gates`` times
+the Titans forward with gates shared by each chunk's tokens (one theta, eta,
+alpha per 64-token chunk, drawn from the same distributions).  Prints ONE
+JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload {2,3,4,5} | --decode | --varlen | --backward]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload {2,3,4,5} | --decode | --varlen | --backward | --chunk-gates]
                     [--no-cpu-baseline]
 """
 
@@ -121,12 +125,15 @@ def measured_traffic(w, kind="forward"):
 
 def _oracle_worker(args):
     # Runs in a separate process: one BLAS thread, the oracle as it stands.
-    q, k, v, th, et, al, b, W1, W2 = args
+    q, k, v, th, et, al, b, W1, W2 = args[:9]
+    chunk_gates = len(args) > 9 and args[9]
     from threadpoolctl import threadpool_limits
-    from oracle import linear_forward, mlp_forward
+    from oracle import linear_forward, linear_forward_chunk_gates, mlp_forward
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        if W1 is None:
+        if chunk_gates:
+            linear_forward_chunk_gates(q, k, v, th, et, al, None, None, b=b)
+        elif W1 is None:
             linear_forward(q, k, v, th, et, al, None, None, b=b)
         else:
             mlp_forward(q, k, v, th, et, al, W1, W2, None, None, b=b)
@@ -536,7 +543,7 @@ def cpu_baseline_varlen(inp, lengths, H, b, docs=12):
     }
 
 
-def cpu_baseline(w, inp, heads):
+def cpu_baseline(w, inp, heads, chunk_gates=False):
     """Time the float64 oracle on ``heads`` (batch, head) pairs with full T, in a process pool."""
     import multiprocessing as mp
     ncores = max(1, min(len(os.sched_getaffinity(0)), 16))
@@ -551,7 +558,7 @@ def cpu_baseline(w, inp, heads):
         bi = np.array([p[0] for p in grp])
         hi = np.array([p[1] for p in grp])
         jobs.append(tuple(g[x][bi, hi] for x in ("q", "k", "v", "theta", "eta", "alpha")) + (w.b,)
-                    + ((g["W1"][bi, hi], g["W2"][bi, hi]) if w.hidden else (None, None)))
+                    + ((g["W1"][bi, hi], g["W2"][bi, hi]) if w.hidden else (None, None)) + (chunk_gates,))
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(len(jobs)) as pool:
@@ -586,6 +593,8 @@ def main():
                     help="time packed variable-length documents with the Titans recipe instead")
     ap.add_argument("--backward", action="store_true",
                     help="time one training step (forward with checkpoints + backward) on the Titans workload")
+    ap.add_argument("--chunk-gates", action="store_true",
+                    help="time the Titans forward with gates shared by each chunk's tokens instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="(batch, head) sequences in the oracle sample (0: 64 for the linear memory, "
@@ -623,9 +632,21 @@ def main():
         backward_main(args)
         return
     w = WORKLOADS[args.workload]
+    if args.chunk_gates and args.workload != 3:
+        print("--chunk-gates runs on the Titans workload (3)", file=sys.stderr)
+        sys.exit(2)
     deep = w.hidden > 0
-    log(f"workload {w}")
+    log(f"workload {w}{' with chunk-shared gates' if args.chunk_gates else ''}")
     inp = make_inputs(w)
+    if args.chunk_gates:
+        # One gate triple per (batch, head, chunk), the Titans distributions.
+        nc = (w.T + w.b - 1) // w.b
+        rng = np.random.default_rng(4003)
+        sig = lambda x: 1.0 / (1.0 + np.exp(-x))  # noqa: E731
+        gsh = (w.B, w.H, nc)
+        inp["theta"] = torch.from_numpy((0.1 * sig(rng.standard_normal(gsh))).astype(np.float32))
+        inp["eta"] = torch.from_numpy(sig(rng.normal(2.0, np.sqrt(0.5), gsh)).astype(np.float32))
+        inp["alpha"] = torch.from_numpy((0.05 * sig(rng.normal(-1.0, 1.0, gsh))).astype(np.float32))
     dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     B, H, T, d = w.B, w.H, w.T, w.d
     z = torch.empty(B, H, T, d, dtype=torch.float32, device="cuda")
@@ -637,8 +658,9 @@ def main():
     else:
         MT = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
         ST = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
-        call = lambda: tm.forward(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"],  # noqa: E731
-                                  dev.get("M0"), dev.get("S0"), b=w.b, out=(z, MT, ST))
+        fwd = tm.forward_chunk_gates if args.chunk_gates else tm.forward
+        call = lambda: fwd(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"],  # noqa: E731
+                           dev.get("M0"), dev.get("S0"), b=w.b, out=(z, MT, ST))
 
     for _ in range(args.warmup):
         call()
@@ -666,6 +688,10 @@ def main():
     else:
         nbytes, flops, per_tok = algorithmic_work(w, reads_state=dev.get("M0") is not None)
         traffic = measured_traffic(w)
+        if args.chunk_gates:
+            # Three gate floats per chunk instead of per token.
+            nbytes -= w.B * w.H * (w.T - (w.T + w.b - 1) // w.b) * 12
+            traffic = None
     achieved_gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
     achieved_tflops = flops / (avg_launch_ms * 1e-3) / 1e12
     tokens_per_s = B * T / (ms_per_step * 1e-3)
@@ -675,7 +701,7 @@ def main():
         f"flops/launch {flops / 1e9:.1f} GFLOP -> {achieved_tflops:.1f} TFLOP/s")
 
     # Sampled parity check of the timed outputs against the oracle.
-    from oracle import linear_forward, mlp_forward
+    from oracle import linear_forward, linear_forward_chunk_gates, mlp_forward
     g = {k: to_numpy64(v[0, 0]) for k, v in inp.items() if v is not None}
     if deep:
         zo = mlp_forward(g["q"], g["k"], g["v"], g["theta"], g["eta"], g["alpha"], g["W1"], g["W2"], b=w.b)[0]
@@ -684,7 +710,8 @@ def main():
     else:
         rows = np.r_[0:4, d - 4:d]
         M0 = g["M0"][rows] if "M0" in g else None
-        zo = linear_forward(g["q"], g["k"], g["v"][:, rows], g["theta"], g["eta"], g["alpha"], M0, None, b=w.b)[0]
+        lf = linear_forward_chunk_gates if args.chunk_gates else linear_forward
+        zo = lf(g["q"], g["k"], g["v"][:, rows], g["theta"], g["eta"], g["alpha"], M0, None, b=w.b)[0]
         zg = z[0, 0][:, rows].double().cpu().numpy()
         what = f"sequence 0, rows {list(rows)}"
     rms = float(np.sqrt(np.mean(zo ** 2)))
@@ -694,7 +721,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         heads = args.cpu_heads or (16 if deep else 64)
-        cpu = cpu_baseline(w, inp, heads)
+        cpu = cpu_baseline(w, inp, heads, chunk_gates=args.chunk_gates)
         log(f"cpu baseline: {cpu}")
 
     if deep:
@@ -706,13 +733,14 @@ def main():
                "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "weights": "f32", "z": "f32",
                "head_tokens_per_s": B * H * T / (ms_per_step * 1e-3)}
     else:
-        metric = "memory-layer tokens/s at H=16,d=128,b=64"
+        metric = "memory-layer tokens/s at H=16,d=128,b=64" + (" (chunk-shared gates)" if args.chunk_gates else "")
         roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved_gbs / HBM_PEAK_GBS,
                     "traffic": traffic, "traffic_unit": "bytes/launch", "algorithmic_bytes": nbytes,
                     "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS}
-        cfg = {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "b": w.b,
-               "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "state": "f32", "z": "f32",
+        cfg = {"workload": w.name + ("-chunk-gates" if args.chunk_gates else ""), "B": B, "H": H, "T": T, "d": d,
+               "b": w.b, "inputs": "bf16 q,k,v; f32 gates" + (" per chunk" if args.chunk_gates else ""),
+               "accumulate": "f32", "state": "f32", "z": "f32",
                "head_tokens_per_s": B * H * T / (ms_per_step * 1e-3)}
     result = {
         "metric": metric,

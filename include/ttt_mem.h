@@ -262,13 +262,52 @@ int ttt_mem_backward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           float* dM0, float* dS0, float* work,
                           int B, int H, int T, int d, int b, void* stream);
 
+/*
+ * Chunk-shared gates ("论文速览 | Titans", section 4.6: a faster, less
+ * expressive variant in which alpha, theta and eta do not depend on the
+ * token but are shared by the tokens of a chunk, so that inside a chunk the
+ * recurrence is linear and time-invariant).  Identical to the entry points
+ * above except that theta, eta, alpha -- and, for the backward, dtheta,
+ * deta, dalpha -- are [B, H, NC] float32 with NC = ceil(T / b): every token
+ * of chunk c uses entry c, and the gradient of entry c is the sum over the
+ * chunk's tokens.  ttt_mem_forward_cg_* takes an optional ckpt (NULL: not
+ * written) for ttt_mem_backward_cg_*.
+ */
+int ttt_mem_forward_cg_f32(const float* q, const float* k, const float* v,
+                           const float* theta, const float* eta, const float* alpha,
+                           const float* M0, const float* S0,
+                           float* z, float* M_T, float* S_T, float* ckpt,
+                           int B, int H, int T, int d, int b, void* stream);
+
+int ttt_mem_forward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const float* theta, const float* eta, const float* alpha,
+                            const float* M0, const float* S0,
+                            float* z, float* M_T, float* S_T, float* ckpt,
+                            int B, int H, int T, int d, int b, void* stream);
+
+int ttt_mem_backward_cg_f32(const float* q, const float* k, const float* v,
+                            const float* theta, const float* eta, const float* alpha,
+                            const float* ckpt, const float* dz, const float* dM_T, const float* dS_T,
+                            float* dq, float* dk, float* dv,
+                            float* dtheta, float* deta, float* dalpha,
+                            float* dM0, float* dS0, float* work,
+                            int B, int H, int T, int d, int b, void* stream);
+
+int ttt_mem_backward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const float* theta, const float* eta, const float* alpha,
+                             const float* ckpt, const float* dz, const float* dM_T, const float* dS_T,
+                             float* dq, float* dk, float* dv,
+                             float* dtheta, float* deta, float* dalpha,
+                             float* dM0, float* dS0, float* work,
+                             int B, int H, int T, int d, int b, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* ttt_mem_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int ttt_mem_abi_version(void);
 
-#define TTT_MEM_ABI_VERSION ((1 << 16) | 1)
+#define TTT_MEM_ABI_VERSION ((1 << 16) | 2)
 
 #ifdef __cplusplus
 }

@@ -170,6 +170,9 @@ struct Params {
     // Chunk-start states for the backward pass (NULL: not written), dense
     // sequences only: [B*H][ceil(T/b)][M | S][d][d] float32.
     float* ckpt;
+    // Gates shared by the tokens of a chunk (dense sequences only): theta,
+    // eta, alpha are [B*H][ceil(T/b)] and every token of chunk c uses entry c.
+    int chunk_gates;
 };
 
 // Compile-time geometry of one kernel instance: NS 16-row tiles per
@@ -402,11 +405,18 @@ struct Kernel {
         }
         if constexpr (PW < 2) {
             // Padding tokens read theta = alpha = eta = 0; the gate work maps eta to 1.
-            const uint32_t gbytes = static_cast<uint32_t>(n) * 4;
-            const size_t gi = seq_tok + c0;
-            pf.th = buf_load4(make_rsrc(p.theta + gi, gbytes), lane * 4);
-            pf.al = buf_load4(make_rsrc(p.alpha + gi, gbytes), lane * 4);
-            pf.et = buf_load4(make_rsrc(p.eta + gi, gbytes), lane * 4);
+            // Chunk-shared gates: every real token reads the chunk's entry.
+            uint32_t gbytes = static_cast<uint32_t>(n) * 4, goff = lane * 4;
+            size_t gi = seq_tok + c0;
+            if (p.chunk_gates) {
+                const int nchunks = (p.T + p.b - 1) / p.b;
+                gi = (seq_tok / p.T) * nchunks + c0 / p.b;
+                gbytes = 4;
+                goff = lane < n ? 0u : 4u;
+            }
+            pf.th = buf_load4(make_rsrc(p.theta + gi, gbytes), goff);
+            pf.al = buf_load4(make_rsrc(p.alpha + gi, gbytes), goff);
+            pf.et = buf_load4(make_rsrc(p.eta + gi, gbytes), goff);
         }
     }
 
@@ -1360,7 +1370,7 @@ hipError_t dispatch(const Params& p, int d, hipStream_t stream) {
 template <typename T>
 int forward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
                  const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
-                 float* ckpt, int B, int H, int Tlen, int d, int b, void* stream) {
+                 float* ckpt, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false) {
     using G = typename GlobalOf<T>::type;
     if (B < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
     if (b < 1) return TTT_ERR_INVALID_ARG;
@@ -1374,6 +1384,8 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
     const size_t in_bytes = tok * d * sizeof(G);
     const size_t z_bytes = tok * d * sizeof(float);
     const size_t st_bytes = static_cast<size_t>(BH) * d * d * sizeof(float);
+    // Gate entries: one per token, or one per chunk.
+    const size_t g_count = chunk_gates ? static_cast<size_t>(BH) * ((static_cast<size_t>(Tlen) + b - 1) / b) : tok;
     if (Tlen > 0) {
         if (!q || !k || !v || !theta || !eta || !alpha || !z) return TTT_ERR_INVALID_ARG;
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(z, 16)) return TTT_ERR_INVALID_ARG;
@@ -1383,7 +1395,7 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
             if (overlaps(z, z_bytes, in, in_bytes)) return TTT_ERR_INVALID_ARG;
         const void* gates[] = {theta, eta, alpha};
         for (const void* g : gates)
-            if (overlaps(z, z_bytes, g, tok * sizeof(float))) return TTT_ERR_INVALID_ARG;
+            if (overlaps(z, z_bytes, g, g_count * sizeof(float))) return TTT_ERR_INVALID_ARG;
         if (overlaps(z, z_bytes, M0, st_bytes) || overlaps(z, z_bytes, S0, st_bytes) ||
             overlaps(z, z_bytes, M_T, st_bytes) || overlaps(z, z_bytes, S_T, st_bytes))
             return TTT_ERR_INVALID_ARG;
@@ -1406,13 +1418,14 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
             if (overlaps(ckpt, ck_bytes, in, in_bytes)) return TTT_ERR_INVALID_ARG;
         const void* gates[] = {theta, eta, alpha};
         for (const void* g : gates)
-            if (overlaps(ckpt, ck_bytes, g, tok * sizeof(float))) return TTT_ERR_INVALID_ARG;
+            if (overlaps(ckpt, ck_bytes, g, g_count * sizeof(float))) return TTT_ERR_INVALID_ARG;
         for (const void* s : states)
             if (overlaps(ckpt, ck_bytes, s, st_bytes)) return TTT_ERR_INVALID_ARG;
         if (overlaps(ckpt, ck_bytes, z, z_bytes)) return TTT_ERR_INVALID_ARG;
     }
 
-    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, nullptr, H, ckpt};
+    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, nullptr, H, ckpt,
+             chunk_gates ? 1 : 0};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1463,7 +1476,7 @@ int forward_varlen_impl(const void* q, const void* k, const void* v, const float
     if (M_T && S_T && overlaps(M_T, st_bytes, S_T, st_bytes)) return TTT_ERR_INVALID_ARG;
     if (overlaps(M_T, st_bytes, cu, cu_bytes) || overlaps(S_T, st_bytes, cu, cu_bytes)) return TTT_ERR_INVALID_ARG;
 
-    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H, nullptr};
+    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H, nullptr, 0};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1514,6 +1527,19 @@ int ttt_mem_forward_ckpt_bf16(const uint16_t* q, const uint16_t* k, const uint16
 }
 
 size_t ttt_mem_ckpt_bytes(int B, int H, int T, int d, int b) { return ckpt_bytes(B, H, T, d, b); }
+
+int ttt_mem_forward_cg_f32(const float* q, const float* k, const float* v, const float* theta, const float* eta,
+                           const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
+                           float* ckpt, int B, int H, int T, int d, int b, void* stream) {
+    return forward_impl<float>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, ckpt, B, H, T, d, b, stream, true);
+}
+
+int ttt_mem_forward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                            const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
+                            float* M_T, float* S_T, float* ckpt, int B, int H, int T, int d, int b, void* stream) {
+    return forward_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, ckpt, B, H, T, d, b, stream,
+                                  true);
+}
 
 const char* ttt_mem_status_string(int status) {
     switch (status) {

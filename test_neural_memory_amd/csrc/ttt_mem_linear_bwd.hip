@@ -248,6 +248,7 @@ struct CarryParams {
     int T;
     int b;
     int nch;
+    int chunk_gates;    // gates [BH][nch] shared by the tokens of a chunk
 };
 
 template <typename T, int D, int NS, int NP>
@@ -329,7 +330,8 @@ struct Carry {
         float th, et, al;
     };
     // Loader wave lw (0 or 1) handles units lw*kW + lane + i*NLW*kW; wave 0 also the gates.
-    __device__ static void issue(const CarryParams& p, Regs& r, size_t tok0, int n, int row0, int lane, int lw) {
+    __device__ static void issue(const CarryParams& p, Regs& r, size_t tok0, int n, int row0, int lane, int lw,
+                                 size_t g0, int gs) {
         const G* q = static_cast<const G*>(p.q);
         const G* k = static_cast<const G*>(p.k);
 #pragma unroll
@@ -352,7 +354,7 @@ struct Carry {
             r.z[i] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         const bool ok = lane < n;
-        const size_t gi = ok ? tok0 + lane : 0;
+        const size_t gi = ok ? g0 + static_cast<size_t>(lane) * gs : 0;
         const float th = p.theta[gi], et = p.eta[gi], al = p.alpha[gi];
         r.th = ok ? th : 0.f;
         r.et = ok ? et : 1.f;
@@ -385,7 +387,7 @@ struct Carry {
 
     // Serial schedule (one slot): load and stage directly.
     __device__ static void load_direct(const CarryParams& p, typename Sm::QSlot& s, size_t tok0, int n, int row0,
-                                       int lane) {
+                                       int lane, size_t g0, int gs) {
         const G* q = static_cast<const G*>(p.q);
         const G* k = static_cast<const G*>(p.k);
         for (int u = lane; u < NP * UR; u += kW) {
@@ -403,9 +405,10 @@ struct Carry {
         }
         for (int l = lane; l < NP; l += kW) {
             const bool ok = l < n;
-            s.th[l] = ok ? p.theta[tok0 + l] : 0.f;
-            s.et[l] = ok ? p.eta[tok0 + l] : 1.f;
-            s.av[l] = ok ? 1.f - p.alpha[tok0 + l] : 1.f;
+            const size_t gi = g0 + static_cast<size_t>(l) * gs;
+            s.th[l] = ok ? p.theta[gi] : 0.f;
+            s.et[l] = ok ? p.eta[gi] : 1.f;
+            s.av[l] = ok ? 1.f - p.alpha[gi] : 1.f;
         }
     }
 
@@ -499,6 +502,11 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
     const size_t seq_tok = static_cast<size_t>(bh) * p.T;
     auto chunk_of = [&](int u) { return nch - 1 - u; };
     auto chunk_n = [&](int c) { return min(p.b, p.T - c * p.b); };
+    // Gate entry of token 0 of chunk c, and the step between tokens.
+    const int gstride = p.chunk_gates ? 0 : 1;
+    auto gate0 = [&](int c) {
+        return p.chunk_gates ? static_cast<size_t>(bh) * nch + c : seq_tok + static_cast<size_t>(c) * p.b;
+    };
 
     const bool is_state = w < NS;
     const bool is_loader = w == NS || w == NS + 1;
@@ -508,7 +516,8 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
     typename C::Regs lr_regs;
     auto do_issue = [&](int u) {
         const int c = chunk_of(u);
-        C::issue(p, lr_regs, seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane, lw);
+        C::issue(p, lr_regs, seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane, lw, gate0(c),
+                 gstride);
     };
     auto do_commit = [&](int u) { C::commit(lr_regs, sm.qs[u % Gm::NQ], lane, lw); };
     auto do_build = [&](int u) {
@@ -663,7 +672,8 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         for (int u = 0; u < nch; ++u) {
             if (w == NS) {
                 const int c = chunk_of(u);
-                C::load_direct(p, sm.qs[0], seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane);
+                C::load_direct(p, sm.qs[0], seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane,
+                               gate0(c), gstride);
             }
             __syncthreads();
             if (is_builder) do_build(u);
@@ -699,6 +709,7 @@ struct GradParams {
     int T;
     int b;
     int nch;
+    int chunk_gates;     // gates and their gradients [BH][nch]
 };
 
 template <typename T, int D, int NP>
@@ -836,9 +847,10 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         }
         for (int l = tid; l < NP; l += kW * Gm::NWAVE) {
             const bool ok = l < n;
-            sm.th[l] = ok ? p.theta[tok0 + l] : 0.f;
-            sm.et[l] = ok ? p.eta[tok0 + l] : 1.f;
-            sm.av[l] = ok ? 1.f - p.alpha[tok0 + l] : 1.f;
+            const size_t gi = p.chunk_gates ? static_cast<size_t>(bh) * p.nch + c : tok0 + l;
+            sm.th[l] = ok ? p.theta[gi] : 0.f;
+            sm.et[l] = ok ? p.eta[gi] : 1.f;
+            sm.av[l] = ok ? 1.f - p.alpha[gi] : 1.f;
         }
     }
     // Partial sums of feature wave f: [dA | dc | dw^M | dw^S][NP], then the three dots.
@@ -1010,12 +1022,22 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         const float gA = reverse_recurrence<NP>(my_dA, fa, l);
         const float gc = reverse_recurrence<NP>(my_dc, fa, l);
         const float gE = reverse_recurrence<NP>(gc + (l == n - 1 ? dEn : 0.f), fe, l);
-        if (l < n) {
-            const float A_prev = l > 0 ? sm.A[l - 1] : 1.f;
-            const float c_prev = l > 0 ? sm.c[l - 1] : 0.f;
-            const float E_prev = l > 0 ? sm.Ev[l - 1] : 1.f;
-            const float da = sa + gA * A_prev + gc * c_prev;
-            const float de = se + gE * E_prev;
+        const float A_prev = l > 0 ? sm.A[(l - 1) % NP] : 1.f;
+        const float c_prev = l > 0 ? sm.c[(l - 1) % NP] : 0.f;
+        const float E_prev = l > 0 ? sm.Ev[(l - 1) % NP] : 1.f;
+        const float da = sa + gA * A_prev + gc * c_prev;
+        const float de = se + gE * E_prev;
+        if (p.chunk_gates) {
+            // A gate shared by the chunk's tokens collects all of their gradients.
+            const float st = wave_sum(l < n ? dth : 0.f), se2 = wave_sum(l < n ? de : 0.f);
+            const float sa2 = wave_sum(l < n ? da : 0.f);
+            if (l == 0) {
+                const size_t gi = static_cast<size_t>(bh) * p.nch + c;
+                p.dth[gi] = st;
+                p.deta[gi] = se2;
+                p.dal[gi] = -sa2;
+            }
+        } else if (l < n) {
             p.dth[tok0 + l] = dth;
             p.deta[tok0 + l] = de;
             p.dal[tok0 + l] = -da;
@@ -1259,7 +1281,7 @@ template <typename T>
 int backward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
                   const float* alpha, const float* ckpt, const float* dz, const float* dMT, const float* dST,
                   float* dq, float* dk, float* dv, float* dth, float* deta, float* dal, float* dM0, float* dS0,
-                  float* work, int B, int H, int Tlen, int d, int b, void* stream) {
+                  float* work, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false) {
     using G = typename GlobalOf<T>::type;
     if (B < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
     if (b < 1) return TTT_ERR_INVALID_ARG;
@@ -1271,7 +1293,8 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
     if (BH * static_cast<long long>(Tlen) > 0x7fffffffLL || BH * nch > 0x7fffffffLL || BH * (d / 16) > 0x7fffffffLL)
         return TTT_ERR_UNSUPPORTED;
     const size_t tok = static_cast<size_t>(BH) * static_cast<size_t>(Tlen);
-    const size_t in_b = tok * d * sizeof(G), f_b = tok * d * 4, g_b = tok * 4;
+    const size_t in_b = tok * d * sizeof(G), f_b = tok * d * 4;
+    const size_t g_b = (chunk_gates ? static_cast<size_t>(BH) * static_cast<size_t>(nch) : tok) * 4;
     const size_t st_b = static_cast<size_t>(BH) * d * d * 4;
     const size_t ck_b = ckpt_bytes(B, H, Tlen, d, b);
     if (Tlen > 0) {
@@ -1302,10 +1325,11 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
             if (outs[j].n && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return TTT_ERR_INVALID_ARG;
     }
 
+    const int cg = chunk_gates ? 1 : 0;
     const CarryParams cp{q, k, dz, theta, eta, alpha, dMT, dST, work, dv, dM0, dS0,
-                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch)};
+                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg};
     const GradParams gp{q, k, v, theta, eta, alpha, ckpt, work, dz, dv, dq, dk, dth, deta, dal,
-                        static_cast<int>(BH), Tlen, b, static_cast<int>(nch)};
+                        static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (d) {
@@ -1337,6 +1361,24 @@ int ttt_mem_backward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           int d, int b, void* stream) {
     return backward_impl<_Float16>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta,
                                    dalpha, dM0, dS0, work, B, H, T, d, b, stream);
+}
+
+int ttt_mem_backward_cg_f32(const float* q, const float* k, const float* v, const float* theta, const float* eta,
+                            const float* alpha, const float* ckpt, const float* dz, const float* dM_T,
+                            const float* dS_T, float* dq, float* dk, float* dv, float* dtheta, float* deta,
+                            float* dalpha, float* dM0, float* dS0, float* work, int B, int H, int T, int d, int b,
+                            void* stream) {
+    return backward_impl<float>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta, dalpha,
+                                dM0, dS0, work, B, H, T, d, b, stream, true);
+}
+
+int ttt_mem_backward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                             const float* eta, const float* alpha, const float* ckpt, const float* dz,
+                             const float* dM_T, const float* dS_T, float* dq, float* dk, float* dv, float* dtheta,
+                             float* deta, float* dalpha, float* dM0, float* dS0, float* work, int B, int H, int T,
+                             int d, int b, void* stream) {
+    return backward_impl<_Float16>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta,
+                                   dalpha, dM0, dS0, work, B, H, T, d, b, stream, true);
 }
 
 }  // extern "C"

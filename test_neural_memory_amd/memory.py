@@ -30,7 +30,8 @@ def _as_dev(t, name, dtype, shape, device):
     return t.contiguous()
 
 
-def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=True, extra=None):
+def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=True, extra=None,
+             gate_len=None, pass_extra=False):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
     B, H, T, d = q.shape
@@ -40,9 +41,10 @@ def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=
     q = _as_dev(q, "q", in_dtype, (B, H, T, d), dev)
     k = _as_dev(k, "k", in_dtype, (B, H, T, d), dev)
     v = _as_dev(v, "v", in_dtype, (B, H, T, d), dev)
-    theta = _as_dev(theta, "theta", torch.float32, (B, H, T), dev)
-    eta = _as_dev(eta, "eta", torch.float32, (B, H, T), dev)
-    alpha = _as_dev(alpha, "alpha", torch.float32, (B, H, T), dev)
+    gl = T if gate_len is None else gate_len
+    theta = _as_dev(theta, "theta", torch.float32, (B, H, gl), dev)
+    eta = _as_dev(eta, "eta", torch.float32, (B, H, gl), dev)
+    alpha = _as_dev(alpha, "alpha", torch.float32, (B, H, gl), dev)
     M0 = _as_dev(M0, "M0", torch.float32, (B, H, d, d), dev)
     S0 = _as_dev(S0, "S0", torch.float32, (B, H, d, d), dev)
     if out is None:
@@ -61,7 +63,7 @@ def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=
         sizes = (B, H, T, d, int(b)) if with_b else (B, H, T, d)
         ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(M0), _ptr(S0),
                 _ptr(z), _ptr(M_T), _ptr(S_T)]
-        if extra is not None:
+        if extra is not None or pass_extra:
             ptrs.append(_ptr(extra))
         status = getattr(lib, name)(*ptrs, *sizes, stream)
     _lib.check(name, status)
@@ -116,8 +118,36 @@ def forward_train(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None, 
     return z, M_T, S_T, ckpt
 
 
+def forward_chunk_gates(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None, ckpt=None):
+    """Linear memory with gates shared by the tokens of each chunk.
+
+    ``theta, eta, alpha`` are ``[B, H, ceil(T/b)]``: every token of chunk c uses
+    entry c.  Returns ``(z, M_T, S_T)``, or ``(z, M_T, S_T, ckpt)`` when a
+    ``ckpt`` tensor (``[B, H, ceil(T/b), 2, d, d]`` float32) is given to keep
+    the chunk-start states for ``backward(..., chunk_gates=True)``.
+    """
+    if q.dtype == torch.float32:
+        name = "ttt_mem_forward_cg_f32"
+    elif q.dtype == torch.bfloat16:
+        name = "ttt_mem_forward_cg_bf16"
+    else:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    nc = _nch(T, int(b))
+    if ckpt is not None:
+        shape = (B, H, nc, 2, d, d)
+        if (not ckpt.is_contiguous() or ckpt.dtype != torch.float32 or tuple(ckpt.shape) != shape
+                or ckpt.device != q.device):
+            raise ValueError(f"ckpt must be contiguous float32 {shape} on {q.device}")
+    res = _forward(name, q.dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, extra=ckpt, gate_len=nc,
+                   pass_extra=True)
+    return res if ckpt is None else res + (ckpt,)
+
+
 def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, work=None, out=None,
-             want_state_grads=True):
+             want_state_grads=True, chunk_gates=False):
     """Gradients of the linear memory from ``forward_train``'s checkpoints.
 
     ``dz [B, H, T, d]``, ``dM_T, dS_T [B, H, d, d]`` (float32; None = zero) are
@@ -127,10 +157,11 @@ def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, w
     pass a float32 scratch tensor shaped like ``ckpt``; ``out`` preallocated
     outputs in the same order.
     """
+    suffix = "_cg" if chunk_gates else ""
     if q.dtype == torch.float32:
-        name = "ttt_mem_backward_f32"
+        name = f"ttt_mem_backward{suffix}_f32"
     elif q.dtype == torch.bfloat16:
-        name = "ttt_mem_backward_bf16"
+        name = f"ttt_mem_backward{suffix}_bf16"
     else:
         raise TypeError(f"unsupported input dtype {q.dtype}")
     if q.dim() != 4:
@@ -144,9 +175,10 @@ def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, w
     q = _as_dev(q, "q", in_dtype, (B, H, T, d), dev)
     k = _as_dev(k, "k", in_dtype, (B, H, T, d), dev)
     v = _as_dev(v, "v", in_dtype, (B, H, T, d), dev)
-    theta = _as_dev(theta, "theta", torch.float32, (B, H, T), dev)
-    eta = _as_dev(eta, "eta", torch.float32, (B, H, T), dev)
-    alpha = _as_dev(alpha, "alpha", torch.float32, (B, H, T), dev)
+    gl = _nch(T, b) if chunk_gates else T
+    theta = _as_dev(theta, "theta", torch.float32, (B, H, gl), dev)
+    eta = _as_dev(eta, "eta", torch.float32, (B, H, gl), dev)
+    alpha = _as_dev(alpha, "alpha", torch.float32, (B, H, gl), dev)
     ck_shape = (B, H, _nch(T, b), 2, d, d)
     ckpt = _as_dev(ckpt, "ckpt", torch.float32, ck_shape, dev)
     dz = _as_dev(dz, "dz", torch.float32, (B, H, T, d), dev)
@@ -156,7 +188,7 @@ def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, w
         work = torch.empty(ck_shape, dtype=torch.float32, device=dev)
     else:
         work = _as_dev(work, "work", torch.float32, ck_shape, dev)
-    shapes = [(B, H, T, d)] * 3 + [(B, H, T)] * 3 + [(B, H, d, d)] * 2
+    shapes = [(B, H, T, d)] * 3 + [(B, H, gl)] * 3 + [(B, H, d, d)] * 2
     if out is None:
         out = [torch.empty(s_, dtype=torch.float32, device=dev) for s_ in shapes]
         if not want_state_grads:

@@ -21,7 +21,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ttt_mem_abi_version() == (1 << 16) | 1
+    assert lib.ttt_mem_abi_version() == (1 << 16) | 2
     assert lib.ttt_mem_status_string(0) == b"ok"
     for s in (-1, -2, -3, 12345):
         assert lib.ttt_mem_status_string(s)
@@ -67,7 +67,8 @@ def test_training_forward_requires_ckpt(lib, name):
     assert getattr(lib, name)(*([None] * 12), 1, 1, 8, 16, 4, None) == -1
 
 
-@pytest.mark.parametrize("name", ["ttt_mem_backward_f32", "ttt_mem_backward_bf16"])
+@pytest.mark.parametrize("name", ["ttt_mem_backward_f32", "ttt_mem_backward_bf16", "ttt_mem_backward_cg_f32",
+                                  "ttt_mem_backward_cg_bf16"])
 def test_backward_rejections_happen_before_any_launch(lib, name):
     def call(B=1, H=1, T=8, d=16, b=4):
         return getattr(lib, name)(*([None] * 19), B, H, T, d, b, None)

@@ -1,0 +1,83 @@
+"""GPU parity of the linear memory with gates shared by each chunk's tokens.
+
+Bounds as for the per-token entry points: max|gpu - oracle| / rms(oracle)
+<= 1e-4 (float32) and <= 2e-2 (bf16 inputs).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import linear_backward_chunk_gates, linear_forward_chunk_gates
+from tests._parity import TOL, rel_err, to_dev
+from test_neural_memory_amd import memory as tm
+from test_neural_memory_amd.workloads import WORKLOADS, make_cotangents, make_inputs, to_numpy64
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _inputs(w, seed=41):
+    inp = make_inputs(w)
+    nc = (w.T + w.b - 1) // w.b
+    rng = np.random.default_rng(seed)
+    g = lambda lo, hi: torch.from_numpy(rng.uniform(lo, hi, (w.B, w.H, nc)).astype(np.float32))  # noqa: E731
+    inp["theta"], inp["eta"], inp["alpha"] = g(0.01, 0.1), g(0.7, 0.95), g(0.0, 0.05)
+    inp["M0"] = torch.from_numpy((rng.standard_normal((w.B, w.H, w.d, w.d)) * 0.05).astype(np.float32))
+    return inp
+
+
+def _expand(g, T, b):
+    return g.repeat_interleave(b, dim=-1)[..., :T].contiguous()
+
+
+CASES = [("d128-b64", 3, dict(B=1, H=2, T=150)), ("d64-b16", 3, dict(B=1, H=2, T=70, d=64, b=16)),
+         ("d16-b8", 1, dict(B=1, H=2, T=45))]
+
+
+@pytest.mark.parametrize("label,wid,kw", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_equals_per_token_gates_and_oracle(label, wid, kw, dtype):
+    w = WORKLOADS[wid].replace(dtype=dtype, **kw)
+    _say(f"case {label} {dtype} {w}")
+    inp = _inputs(w)
+    dev = to_dev(inp)
+    args = (dev["q"], dev["k"], dev["v"])
+    z, M, S = tm.forward_chunk_gates(*args, dev["theta"], dev["eta"], dev["alpha"], dev["M0"], b=w.b)
+    tok = [_expand(dev[x], w.T, w.b) for x in ("theta", "eta", "alpha")]
+    z2, M2, S2 = tm.forward(*args, *tok, dev["M0"], b=w.b)
+    torch.cuda.synchronize()
+    # The per-token kernel fed the same values computes the same floats.
+    assert torch.equal(z, z2) and torch.equal(M, M2) and torch.equal(S, S2)
+    n = {k: to_numpy64(v) for k, v in inp.items() if v is not None}
+    ref = linear_forward_chunk_gates(n["q"], n["k"], n["v"], n["theta"], n["eta"], n["alpha"], n["M0"], None, b=w.b)
+    errs = [rel_err(to_numpy64(x.cpu()), r) for x, r in zip((z, M, S), ref)]
+    _say(f"  errors z={errs[0]:.2e} M_T={errs[1]:.2e} S_T={errs[2]:.2e}")
+    assert max(errs) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("label,wid,kw", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_parity(label, wid, kw, dtype):
+    w = WORKLOADS[wid].replace(dtype=dtype, **kw)
+    _say(f"case {label} {dtype} {w}")
+    inp = _inputs(w)
+    cot = make_cotangents(w)
+    dev, cd = to_dev(inp), to_dev(cot)
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    nc = (w.T + w.b - 1) // w.b
+    ckpt = torch.empty(w.B, w.H, nc, 2, w.d, w.d, device="cuda")
+    tm.forward_chunk_gates(*args, dev["M0"], b=w.b, ckpt=ckpt)
+    g = tm.backward(*args, ckpt, cd["dz"], cd["dM_T"], cd["dS_T"], b=w.b, chunk_gates=True)
+    torch.cuda.synchronize()
+    n = {k: to_numpy64(v) for k, v in inp.items() if v is not None}
+    c = {k: to_numpy64(v) for k, v in cot.items()}
+    ref = linear_backward_chunk_gates(n["q"], n["k"], n["v"], n["theta"], n["eta"], n["alpha"], c["dz"], c["dM_T"],
+                                      c["dS_T"], n["M0"], None, b=w.b)
+    names = ("dq", "dk", "dv", "dtheta", "deta", "dalpha", "dM0", "dS0")
+    errs = {nm: rel_err(to_numpy64(x.cpu()), r) for nm, x, r in zip(names, g, ref)}
+    _say("  errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert max(errs.values()) <= TOL[dtype], errs
