@@ -338,7 +338,7 @@ def backward_main(args):
     MT = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
     ST = torch.empty_like(MT)
     nch = (T + w.b - 1) // w.b
-    ckpt = torch.empty(B, H, nch, 2, d, d, dtype=torch.float32, device="cuda")
+    ckpt = tm.new_ckpt(dev["q"], w.b)
     work = torch.empty_like(ckpt)
     outs = [torch.empty(B, H, T, d, dtype=torch.float32, device="cuda") for _ in range(3)] + \
            [torch.empty(B, H, T, dtype=torch.float32, device="cuda") for _ in range(3)] + \
@@ -368,7 +368,7 @@ def backward_main(args):
     fbytes, _, _ = algorithmic_work(w)
     achieved_gbs = nbytes / (bwd_ms * 1e-3) / 1e9
     achieved_tflops = flops / (bwd_ms * 1e-3) / 1e12
-    ck_bytes = ckpt.numel() * 4
+    ck_bytes = ckpt.numel() * ckpt.element_size()
     log(f"forward with checkpoints {fwd_ms * 1e3:.1f} us (algorithmic {fbytes / (fwd_ms * 1e-3) / 1e9:.0f} GB/s "
         f"+ {ck_bytes / 1e9:.2f} GB of checkpoints), backward {bwd_ms * 1e3:.1f} us; wall/step "
         f"{t_wall / args.steps * 1e3:.3f} ms")
@@ -411,7 +411,7 @@ def backward_main(args):
         "data": "synthetic",
         "config": {"workload": "titans-linear-train", "B": B, "H": H, "T": T, "d": d, "b": w.b,
                    "inputs": "bf16 q,k,v; f32 gates; f32 dz (seeded N(0,1))", "accumulate": "f32",
-                   "gradients": "f32", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
+                   "gradients": "f32", "checkpoints": "fp16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                    "checkpoint_bytes": ck_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w, "backward"),

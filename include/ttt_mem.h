@@ -205,11 +205,14 @@ int ttt_mem_decode_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *
  * ttt_mem_forward_ckpt_*: the forward above, plus the state entering every
  * chunk, which the backward differentiates from:
- *     ckpt [B, H, NC, 2, d, d] float32, NC = ceil(T / b);
+ *     ckpt [B, H, NC, 2, d, d], NC = ceil(T / b);
  *     ckpt[b, h, c, 0] = M and ckpt[b, h, c, 1] = S before chunk c
- *     (c = 0: M0 and S0, zeros for NULL).
- * Its size in bytes is ttt_mem_ckpt_bytes(B, H, T, d, b).  ckpt is required
- * (non-NULL, 16-byte aligned) and must not overlap any other argument.
+ *     (c = 0: M0 and S0, zeros for NULL),
+ * float32 for the _f32 entry points, IEEE fp16 (round to nearest even) for
+ * the _bf16 ones, whose products round the state to fp16 anyway.  Its size
+ * in bytes is ttt_mem_ckpt_bytes(B, H, T, d, b), resp. _bf16.  ckpt is
+ * required (non-NULL, 16-byte aligned) and must not overlap any other
+ * argument.
  *
  * ttt_mem_backward_*: given the derivatives of the outer loss with respect
  * to the forward's outputs,
@@ -219,9 +222,9 @@ int ttt_mem_decode_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *     dq, dk, dv                 [B, H, T, d] float32 (both entry points),
  *     dtheta, deta, dalpha       [B, H, T]    float32,
  *     dM0, dS0                   [B, H, d, d] float32 (NULL: not written).
- * work is a caller-owned float32 scratch buffer of ttt_mem_ckpt_bytes(B, H,
- * T, d, b) bytes (the derivatives with respect to the state leaving every
- * chunk); its contents on entry do not matter and on return are unspecified.
+ * work is a caller-owned scratch buffer of the checkpoints' type and size
+ * (the derivatives with respect to the state leaving every chunk); its
+ * contents on entry do not matter and on return are unspecified.
  * The bf16 entry point takes q, k, v in bf16 and computes its matrix products
  * with fp16 operands and float32 accumulation, as the bf16 forward does; the
  * float32 one uses float32 products.
@@ -240,11 +243,13 @@ int ttt_mem_forward_ckpt_f32(const float* q, const float* k, const float* v,
 int ttt_mem_forward_ckpt_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const float* theta, const float* eta, const float* alpha,
                               const float* M0, const float* S0,
-                              float* z, float* M_T, float* S_T, float* ckpt,
+                              float* z, float* M_T, float* S_T, uint16_t* ckpt,
                               int B, int H, int T, int d, int b, void* stream);
 
-/* Bytes of ckpt (and of the backward's work buffer); 0 for negative sizes. */
+/* Bytes of ckpt (and of the backward's work buffer) for the _f32 and the
+ * _bf16 entry points; 0 for negative sizes. */
 size_t ttt_mem_ckpt_bytes(int B, int H, int T, int d, int b);
+size_t ttt_mem_ckpt_bytes_bf16(int B, int H, int T, int d, int b);
 
 int ttt_mem_backward_f32(const float* q, const float* k, const float* v,
                          const float* theta, const float* eta, const float* alpha,
@@ -256,10 +261,10 @@ int ttt_mem_backward_f32(const float* q, const float* k, const float* v,
 
 int ttt_mem_backward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                           const float* theta, const float* eta, const float* alpha,
-                          const float* ckpt, const float* dz, const float* dM_T, const float* dS_T,
+                          const uint16_t* ckpt, const float* dz, const float* dM_T, const float* dS_T,
                           float* dq, float* dk, float* dv,
                           float* dtheta, float* deta, float* dalpha,
-                          float* dM0, float* dS0, float* work,
+                          float* dM0, float* dS0, uint16_t* work,
                           int B, int H, int T, int d, int b, void* stream);
 
 /*
@@ -282,7 +287,7 @@ int ttt_mem_forward_cg_f32(const float* q, const float* k, const float* v,
 int ttt_mem_forward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* theta, const float* eta, const float* alpha,
                             const float* M0, const float* S0,
-                            float* z, float* M_T, float* S_T, float* ckpt,
+                            float* z, float* M_T, float* S_T, uint16_t* ckpt,
                             int B, int H, int T, int d, int b, void* stream);
 
 int ttt_mem_backward_cg_f32(const float* q, const float* k, const float* v,
@@ -295,10 +300,10 @@ int ttt_mem_backward_cg_f32(const float* q, const float* k, const float* v,
 
 int ttt_mem_backward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const float* theta, const float* eta, const float* alpha,
-                             const float* ckpt, const float* dz, const float* dM_T, const float* dS_T,
+                             const uint16_t* ckpt, const float* dz, const float* dM_T, const float* dS_T,
                              float* dq, float* dk, float* dv,
                              float* dtheta, float* deta, float* dalpha,
-                             float* dM0, float* dS0, float* work,
+                             float* dM0, float* dS0, uint16_t* work,
                              int B, int H, int T, int d, int b, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -307,7 +312,7 @@ const char* ttt_mem_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ttt_mem_abi_version(void);
 
-#define TTT_MEM_ABI_VERSION ((1 << 16) | 2)
+#define TTT_MEM_ABI_VERSION ((1 << 16) | 3)
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,7 @@ _SIGNATURES = {
     "ttt_mem_forward_ckpt_f32": (_I, [_P] * 12 + [_I] * 5 + [_P]),
     "ttt_mem_forward_ckpt_bf16": (_I, [_P] * 12 + [_I] * 5 + [_P]),
     "ttt_mem_ckpt_bytes": (ctypes.c_size_t, [_I] * 5),
+    "ttt_mem_ckpt_bytes_bf16": (ctypes.c_size_t, [_I] * 5),
     "ttt_mem_backward_f32": (_I, [_P] * 19 + [_I] * 5 + [_P]),
     "ttt_mem_backward_bf16": (_I, [_P] * 19 + [_I] * 5 + [_P]),
     "ttt_mem_forward_cg_f32": (_I, [_P] * 12 + [_I] * 5 + [_P]),

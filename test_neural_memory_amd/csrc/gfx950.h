@@ -155,6 +155,27 @@ template <typename T> struct GlobalOf;
 template <> struct GlobalOf<float> { using type = float; };
 template <> struct GlobalOf<_Float16> { using type = uint16_t; };
 
+// Four float32 values -> four elements of T at an address (LDS or global;
+// 8 or 16 bytes), and back.
+template <typename T>
+__device__ __forceinline__ void st4(T* dst, f32x4 v) {
+    if constexpr (Op<T>::kF16) {
+        *reinterpret_cast<f16x4*>(dst) = cvt4(v);
+    } else {
+        *reinterpret_cast<f32x4*>(dst) = v;
+    }
+}
+template <typename T>
+__device__ __forceinline__ f32x4 ld4(const T* src) {
+    if constexpr (Op<T>::kF16) {
+        const f16x4 h = *reinterpret_cast<const f16x4*>(src);
+        return f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
+                     static_cast<float>(h[3])};
+    } else {
+        return *reinterpret_cast<const f32x4*>(src);
+    }
+}
+
 // Host-side pointer checks.
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
@@ -165,11 +186,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // Bytes of the chunk-start state checkpoints of a dense [B, H, T] problem:
-// [B*H][ceil(T/b)][M | S][d][d] float32 (0 for sizes no entry point accepts).
-size_t ckpt_bytes(int B, int H, int T, int d, int b) {
+// [B*H][ceil(T/b)][M | S][d][d] elements of elem bytes (0 for sizes no entry
+// point accepts).
+size_t ckpt_bytes(int B, int H, int T, int d, int b, size_t elem = sizeof(float)) {
     if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1) return 0;
     const size_t nch = (static_cast<size_t>(T) + b - 1) / b;
-    return static_cast<size_t>(B) * H * nch * 2 * d * d * sizeof(float);
+    return static_cast<size_t>(B) * H * nch * 2 * d * d * elem;
 }
 
 }  // namespace

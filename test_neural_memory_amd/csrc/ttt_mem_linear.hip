@@ -168,8 +168,10 @@ struct Params {
     const int* cu;
     int H;
     // Chunk-start states for the backward pass (NULL: not written), dense
-    // sequences only: [B*H][ceil(T/b)][M | S][d][d] float32.
-    float* ckpt;
+    // sequences only: [B*H][ceil(T/b)][M | S][d][d], float32 on the float32
+    // path and fp16 on the fp16-operand path (the precision every later use
+    // rounds them to).
+    void* ckpt;
     // Gates shared by the tokens of a chunk (dense sequences only): theta,
     // eta, alpha are [B*H][ceil(T/b)] and every token of chunk c uses entry c.
     int chunk_gates;
@@ -1212,14 +1214,14 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
         // differentiates from), in the layout of M_T / S_T.
         auto save = [&](int c) {
             if (p.ckpt) {
-                float* base = p.ckpt + (static_cast<size_t>(bh) * nch + c) * (2 * D * D) +
-                              static_cast<size_t>(row + lr) * D;
+                T* base = static_cast<T*>(p.ckpt) + (static_cast<size_t>(bh) * nch + c) * (2 * D * D) +
+                          static_cast<size_t>(row + lr) * D;
 #pragma unroll
                 for (int cw = 0; cw < Gm::NCW; ++cw) {
                     const int col = O::tmap(x.chi * Gm::NCW + cw, 4 * lg);
                     if (col < D) {
-                        *reinterpret_cast<f32x4*>(base + col) = Macc[cw];
-                        *reinterpret_cast<f32x4*>(base + D * D + col) = Sacc[cw];
+                        st4<T>(base + col, Macc[cw]);
+                        st4<T>(base + D * D + col, Sacc[cw]);
                     }
                 }
             }
@@ -1370,7 +1372,7 @@ hipError_t dispatch(const Params& p, int d, hipStream_t stream) {
 template <typename T>
 int forward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
                  const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
-                 float* ckpt, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false) {
+                 void* ckpt, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false) {
     using G = typename GlobalOf<T>::type;
     if (B < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
     if (b < 1) return TTT_ERR_INVALID_ARG;
@@ -1411,7 +1413,7 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
     if (M_T && S_T && overlaps(M_T, st_bytes, S_T, st_bytes)) return TTT_ERR_INVALID_ARG;
     if (ckpt) {
         // Written while the inputs are read and the outputs written: no overlap with any of them.
-        const size_t ck_bytes = ckpt_bytes(B, H, Tlen, d, b);
+        const size_t ck_bytes = ckpt_bytes(B, H, Tlen, d, b, sizeof(T));
         if (!aligned(ckpt, 16)) return TTT_ERR_INVALID_ARG;
         const void* ins[] = {q, k, v};
         for (const void* in : ins)
@@ -1521,12 +1523,15 @@ int ttt_mem_forward_ckpt_f32(const float* q, const float* k, const float* v, con
 
 int ttt_mem_forward_ckpt_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
                               const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
-                              float* M_T, float* S_T, float* ckpt, int B, int H, int T, int d, int b, void* stream) {
+                              float* M_T, float* S_T, uint16_t* ckpt, int B, int H, int T, int d, int b,
+                              void* stream) {
     if (!ckpt) return TTT_ERR_INVALID_ARG;
     return forward_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, ckpt, B, H, T, d, b, stream);
 }
 
-size_t ttt_mem_ckpt_bytes(int B, int H, int T, int d, int b) { return ckpt_bytes(B, H, T, d, b); }
+size_t ttt_mem_ckpt_bytes(int B, int H, int T, int d, int b) { return ckpt_bytes(B, H, T, d, b, 4); }
+
+size_t ttt_mem_ckpt_bytes_bf16(int B, int H, int T, int d, int b) { return ckpt_bytes(B, H, T, d, b, 2); }
 
 int ttt_mem_forward_cg_f32(const float* q, const float* k, const float* v, const float* theta, const float* eta,
                            const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
@@ -1536,7 +1541,8 @@ int ttt_mem_forward_cg_f32(const float* q, const float* k, const float* v, const
 
 int ttt_mem_forward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
                             const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
-                            float* M_T, float* S_T, float* ckpt, int B, int H, int T, int d, int b, void* stream) {
+                            float* M_T, float* S_T, uint16_t* ckpt, int B, int H, int T, int d, int b,
+                            void* stream) {
     return forward_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, ckpt, B, H, T, d, b, stream,
                                   true);
 }

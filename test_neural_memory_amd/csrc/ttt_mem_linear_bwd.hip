@@ -55,6 +55,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ttt_mem.h"
 #include "gfx950.h"
 
@@ -126,26 +128,6 @@ struct Fr {
         return r;
     }
 };
-
-// Four float32 values -> four elements of T at an LDS address (8 or 16 bytes).
-template <typename T>
-__device__ __forceinline__ void st4(T* dst, f32x4 v) {
-    if constexpr (Op<T>::kF16) {
-        *reinterpret_cast<f16x4*>(dst) = cvt4(v);
-    } else {
-        *reinterpret_cast<f32x4*>(dst) = v;
-    }
-}
-template <typename T>
-__device__ __forceinline__ f32x4 ld4(const T* src) {
-    if constexpr (Op<T>::kF16) {
-        const f16x4 h = *reinterpret_cast<const f16x4*>(src);
-        return f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
-                     static_cast<float>(h[3])};
-    } else {
-        return *reinterpret_cast<const f32x4*>(src);
-    }
-}
 
 // One 16-byte unit of a global input row (8 bf16 or 4 float32) -> LDS as T
 // (zeros when !ok).
@@ -240,7 +222,7 @@ struct CarryParams {
     const float* alpha;
     const float* dMT;   // NULL: zero
     const float* dST;
-    float* work;        // [BH][nch][dM | dS][D][D]: cotangent leaving each chunk
+    void* work;         // [BH][nch][dM | dS][D][D] (as the checkpoints): cotangent leaving each chunk
     float* dv;          // [BH][T][D]
     float* dM0;         // NULL: not written
     float* dS0;
@@ -559,13 +541,14 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         const typename C::Sm::PSlot& ps = sm.ps[u % Gm::NPR];
         // Cotangent of the state leaving chunk c.
         {
-            float* base = p.work + (static_cast<size_t>(bh) * nch + c) * (2 * D * D) + static_cast<size_t>(r0 + lr) * D;
+            T* base = static_cast<T*>(p.work) + (static_cast<size_t>(bh) * nch + c) * (2 * D * D) +
+                      static_cast<size_t>(r0 + lr) * D;
 #pragma unroll
             for (int jt = 0; jt < NCT; ++jt) {
                 const int col = O::tmap(jt, 4 * lg);
                 if (col < D) {
-                    *reinterpret_cast<f32x4*>(base + col) = dM[jt];
-                    *reinterpret_cast<f32x4*>(base + D * D + col) = dS[jt];
+                    st4<T>(base + col, dM[jt]);
+                    st4<T>(base + D * D + col, dS[jt]);
                 }
             }
         }
@@ -696,8 +679,8 @@ struct GradParams {
     const float* theta;
     const float* eta;
     const float* alpha;
-    const float* ckpt;   // [BH][nch][M | S][D][D]: state entering each chunk
-    const float* work;   // [BH][nch][dM | dS][D][D]: cotangent leaving each chunk
+    const void* ckpt;    // [BH][nch][M | S][D][D]: state entering each chunk (float32 or fp16)
+    const void* work;    // [BH][nch][dM | dS][D][D]: cotangent leaving each chunk (same type)
     const float* dz;
     const float* dv;
     float* dq;
@@ -781,10 +764,10 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
     const int c = blockIdx.x % p.nch;
     const int n = min(p.b, p.T - c * p.b);
     const size_t tok0 = static_cast<size_t>(bh) * p.T + static_cast<size_t>(c) * p.b;
-    const float* Mc = p.ckpt + (static_cast<size_t>(bh) * p.nch + c) * (2 * D * D);
-    const float* Sc = Mc + D * D;
-    const float* dMe = p.work + (static_cast<size_t>(bh) * p.nch + c) * (2 * D * D);
-    const float* dSe = dMe + D * D;
+    const T* Mc = static_cast<const T*>(p.ckpt) + (static_cast<size_t>(bh) * p.nch + c) * (2 * D * D);
+    const T* Sc = Mc + D * D;
+    const T* dMe = static_cast<const T*>(p.work) + (static_cast<size_t>(bh) * p.nch + c) * (2 * D * D);
+    const T* dSe = dMe + D * D;
 
     // ---- stage q, k (and dz, -dv), raw gates; clear the accumulators ----
     {
@@ -1051,24 +1034,26 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         // Columns f0 .. f0+15 of a state as an operand whose rows are those
         // columns (k = row of the state): raw loads, then conversion, so the
         // next state's loads are in flight while the current one is used.
-        constexpr int NRAW = NKD * KS;
-        auto colload = [&](const float* X, int f0, float* raw) {
+        // Raw column values, two consecutive rows per 32-bit register.
+        using R2 = typename std::conditional<Op<T>::kF16, f16x2, f32x2>::type;
+        constexpr int NRAW = NKD * KS / 2;
+        auto colload = [&](const T* X, int f0, R2* raw) {
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
 #pragma unroll
-                for (int s2 = 0; s2 < KS; ++s2) {
+                for (int s2 = 0; s2 < KS; s2 += 2) {
                     const int r = kk * KG + KS * lg + s2;
-                    raw[kk * KS + s2] = X[static_cast<size_t>(r < D ? r : 0) * D + f0 + lr];
+                    const size_t o = static_cast<size_t>(r < D ? r : 0) * D + f0 + lr;
+                    raw[(kk * KS + s2) / 2] = R2{X[o], X[o + D]};
                 }
             }
         };
-        auto colcvt = [&](const float* raw, F* out) {
+        auto colcvt = [&](const R2* raw, F* out) {
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
-                float x[KS];
 #pragma unroll
-                for (int s2 = 0; s2 < KS; ++s2) x[s2] = kk * KG + KS * lg + s2 < D ? raw[kk * KS + s2] : 0.f;
-                out[kk] = R::from_f32(x);
+                for (int s2 = 0; s2 < KS; ++s2)
+                    out[kk][s2] = kk * KG + KS * lg + s2 < D ? raw[(kk * KS + s2) / 2][s2 & 1] : static_cast<T>(0.f);
             }
         };
         // Residual rows of E^T: E^T[r][t] = M0[r][:] . k_t - v_t[r].
@@ -1080,16 +1065,11 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             const size_t ro = static_cast<size_t>(f0 + lr) * D;
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
-                float x[KS];
+                // KS consecutive elements of row f0 + lr: one 16-byte load.
                 const int col = kk * KG + KS * lg;
-#pragma unroll
-                for (int s4 = 0; s4 < KS; s4 += 4) {
-                    const bool ok = col + s4 < D;
-                    const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mc + ro + (ok ? col + s4 : 0));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[s4 + e] = ok ? m4[e] : 0.f;
-                }
-                am[kk] = R::from_f32(x);
+                const bool ok = col < D;
+                const F m = *reinterpret_cast<const F*>(Mc + ro + (ok ? col : 0));
+                am[kk] = ok ? m : F{};
             }
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -1101,7 +1081,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 st4<T>(sm.ec + t * LQ + f0 + 4 * lg, acc - vv);
             }
         }
-        float raw[NRAW];
+        R2 raw[NRAW];
         colload(Sc, 16 * fw * FPW, raw);
         __syncthreads();   // (1)
 
@@ -1132,6 +1112,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             const int f0 = 16 * (fw * FPW + ft);
             F fs[NKD], fo[NKD], fm[NKD];
             colcvt(raw, fs);                       // S0
+            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
             colload(dSe, f0, raw);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -1144,6 +1125,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             }
             colcvt(raw, fo);                       // dS'
             d3 += fdot(fo, fs);
+            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
             colload(dMe, f0, raw);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -1156,6 +1138,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             }
             colcvt(raw, fo);                       // dM'
             d2 += fdot(fo, fs);
+            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
             colload(Mc, f0, raw);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -1168,6 +1151,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             }
             colcvt(raw, fm);                       // M0
             d1 += fdot(fo, fm);
+            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
             if (ft + 1 < FPW) colload(Sc, f0 + 16, raw);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -1279,9 +1263,9 @@ struct Span {
 
 template <typename T>
 int backward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
-                  const float* alpha, const float* ckpt, const float* dz, const float* dMT, const float* dST,
+                  const float* alpha, const void* ckpt, const float* dz, const float* dMT, const float* dST,
                   float* dq, float* dk, float* dv, float* dth, float* deta, float* dal, float* dM0, float* dS0,
-                  float* work, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false) {
+                  void* work, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false) {
     using G = typename GlobalOf<T>::type;
     if (B < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
     if (b < 1) return TTT_ERR_INVALID_ARG;
@@ -1296,7 +1280,7 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
     const size_t in_b = tok * d * sizeof(G), f_b = tok * d * 4;
     const size_t g_b = (chunk_gates ? static_cast<size_t>(BH) * static_cast<size_t>(nch) : tok) * 4;
     const size_t st_b = static_cast<size_t>(BH) * d * d * 4;
-    const size_t ck_b = ckpt_bytes(B, H, Tlen, d, b);
+    const size_t ck_b = ckpt_bytes(B, H, Tlen, d, b, sizeof(T));
     if (Tlen > 0) {
         const void* req[] = {q, k, v, theta, eta, alpha, ckpt, dz, dq, dk, dv, dth, deta, dal, work};
         for (const void* r : req)
@@ -1355,9 +1339,9 @@ int ttt_mem_backward_f32(const float* q, const float* k, const float* v, const f
 }
 
 int ttt_mem_backward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
-                          const float* eta, const float* alpha, const float* ckpt, const float* dz,
+                          const float* eta, const float* alpha, const uint16_t* ckpt, const float* dz,
                           const float* dM_T, const float* dS_T, float* dq, float* dk, float* dv, float* dtheta,
-                          float* deta, float* dalpha, float* dM0, float* dS0, float* work, int B, int H, int T,
+                          float* deta, float* dalpha, float* dM0, float* dS0, uint16_t* work, int B, int H, int T,
                           int d, int b, void* stream) {
     return backward_impl<_Float16>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta,
                                    dalpha, dM0, dS0, work, B, H, T, d, b, stream);
@@ -1373,9 +1357,9 @@ int ttt_mem_backward_cg_f32(const float* q, const float* k, const float* v, cons
 }
 
 int ttt_mem_backward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
-                             const float* eta, const float* alpha, const float* ckpt, const float* dz,
+                             const float* eta, const float* alpha, const uint16_t* ckpt, const float* dz,
                              const float* dM_T, const float* dS_T, float* dq, float* dk, float* dv, float* dtheta,
-                             float* deta, float* dalpha, float* dM0, float* dS0, float* work, int B, int H, int T,
+                             float* deta, float* dalpha, float* dM0, float* dS0, uint16_t* work, int B, int H, int T,
                              int d, int b, void* stream) {
     return backward_impl<_Float16>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta,
                                    dalpha, dM0, dS0, work, B, H, T, d, b, stream, true);

@@ -93,11 +93,25 @@ def _nch(T, b):
     return (T + b - 1) // b
 
 
+def ckpt_dtype(in_dtype):
+    """Element type of the checkpoints (and of the backward's work buffer):
+    float32 for float32 inputs, fp16 for bf16 inputs (the precision every use
+    of the states rounds them to on that path)."""
+    return torch.float32 if in_dtype == torch.float32 else torch.float16
+
+
+def new_ckpt(q, b):
+    """An uninitialised checkpoint tensor for the inputs ``q [B, H, T, d]`` and chunk size b."""
+    B, H, T, d = q.shape
+    return torch.empty((B, H, _nch(T, int(b)), 2, d, d), dtype=ckpt_dtype(q.dtype), device=q.device)
+
+
 def forward_train(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None, ckpt=None):
     """Forward that also saves the state entering every chunk for ``backward``.
 
     Returns ``(z, M_T, S_T, ckpt)`` with ``ckpt [B, H, ceil(T/b), 2, d, d]``
-    float32 (``ckpt[..., c, 0]`` = M and ``[..., c, 1]`` = S before chunk c).
+    (``ckpt[..., c, 0]`` = M and ``[..., c, 1]`` = S before chunk c), float32
+    for float32 inputs and fp16 for bf16 inputs.
     """
     if q.dtype == torch.float32:
         name = "ttt_mem_forward_ckpt_f32"
@@ -109,11 +123,12 @@ def forward_train(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None, 
         raise ValueError("q must be [B, H, T, d]")
     B, H, T, d = q.shape
     shape = (B, H, _nch(T, int(b)), 2, d, d)
+    cdt = ckpt_dtype(q.dtype)
     if ckpt is None:
-        ckpt = torch.empty(shape, dtype=torch.float32, device=q.device)
-    elif (not ckpt.is_contiguous() or ckpt.dtype != torch.float32 or tuple(ckpt.shape) != shape
+        ckpt = torch.empty(shape, dtype=cdt, device=q.device)
+    elif (not ckpt.is_contiguous() or ckpt.dtype != cdt or tuple(ckpt.shape) != shape
           or ckpt.device != q.device):
-        raise ValueError(f"ckpt must be contiguous float32 {shape} on {q.device}")
+        raise ValueError(f"ckpt must be contiguous {cdt} {shape} on {q.device}")
     z, M_T, S_T = _forward(name, q.dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, extra=ckpt)
     return z, M_T, S_T, ckpt
 
@@ -138,9 +153,10 @@ def forward_chunk_gates(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=
     nc = _nch(T, int(b))
     if ckpt is not None:
         shape = (B, H, nc, 2, d, d)
-        if (not ckpt.is_contiguous() or ckpt.dtype != torch.float32 or tuple(ckpt.shape) != shape
+        cdt = ckpt_dtype(q.dtype)
+        if (not ckpt.is_contiguous() or ckpt.dtype != cdt or tuple(ckpt.shape) != shape
                 or ckpt.device != q.device):
-            raise ValueError(f"ckpt must be contiguous float32 {shape} on {q.device}")
+            raise ValueError(f"ckpt must be contiguous {cdt} {shape} on {q.device}")
     res = _forward(name, q.dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, extra=ckpt, gate_len=nc,
                    pass_extra=True)
     return res if ckpt is None else res + (ckpt,)
@@ -150,11 +166,12 @@ def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, w
              want_state_grads=True, chunk_gates=False):
     """Gradients of the linear memory from ``forward_train``'s checkpoints.
 
+    ``ckpt`` is ``forward_train``'s (float32, or fp16 for bf16 inputs).
     ``dz [B, H, T, d]``, ``dM_T, dS_T [B, H, d, d]`` (float32; None = zero) are
     the derivatives of the outer loss with respect to ``z, M_T, S_T``.
     Returns ``(dq, dk, dv, dtheta, deta, dalpha, dM0, dS0)``, all float32
     (``dM0, dS0`` are None when ``want_state_grads`` is False).  ``work`` may
-    pass a float32 scratch tensor shaped like ``ckpt``; ``out`` preallocated
+    pass a scratch tensor shaped and typed like ``ckpt``; ``out`` preallocated
     outputs in the same order.
     """
     suffix = "_cg" if chunk_gates else ""
@@ -180,14 +197,15 @@ def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, w
     eta = _as_dev(eta, "eta", torch.float32, (B, H, gl), dev)
     alpha = _as_dev(alpha, "alpha", torch.float32, (B, H, gl), dev)
     ck_shape = (B, H, _nch(T, b), 2, d, d)
-    ckpt = _as_dev(ckpt, "ckpt", torch.float32, ck_shape, dev)
+    cdt = ckpt_dtype(in_dtype)
+    ckpt = _as_dev(ckpt, "ckpt", cdt, ck_shape, dev)
     dz = _as_dev(dz, "dz", torch.float32, (B, H, T, d), dev)
     dM_T = _as_dev(dM_T, "dM_T", torch.float32, (B, H, d, d), dev)
     dS_T = _as_dev(dS_T, "dS_T", torch.float32, (B, H, d, d), dev)
     if work is None:
-        work = torch.empty(ck_shape, dtype=torch.float32, device=dev)
+        work = torch.empty(ck_shape, dtype=cdt, device=dev)
     else:
-        work = _as_dev(work, "work", torch.float32, ck_shape, dev)
+        work = _as_dev(work, "work", cdt, ck_shape, dev)
     shapes = [(B, H, T, d)] * 3 + [(B, H, gl)] * 3 + [(B, H, d, d)] * 2
     if out is None:
         out = [torch.empty(s_, dtype=torch.float32, device=dev) for s_ in shapes]

@@ -21,7 +21,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ttt_mem_abi_version() == (1 << 16) | 2
+    assert lib.ttt_mem_abi_version() == (1 << 16) | 3
     assert lib.ttt_mem_status_string(0) == b"ok"
     for s in (-1, -2, -3, 12345):
         assert lib.ttt_mem_status_string(s)
@@ -60,6 +60,7 @@ def test_ckpt_bytes(lib):
     assert lib.ttt_mem_ckpt_bytes(2, 3, 130, 64, 64) == 2 * 3 * 3 * 2 * 64 * 64 * 4
     assert lib.ttt_mem_ckpt_bytes(1, 1, 0, 16, 8) == 0
     assert lib.ttt_mem_ckpt_bytes(-1, 1, 8, 16, 8) == 0
+    assert lib.ttt_mem_ckpt_bytes_bf16(2, 3, 130, 64, 64) == 2 * 3 * 3 * 2 * 64 * 64 * 2
 
 
 @pytest.mark.parametrize("name", ["ttt_mem_forward_ckpt_f32", "ttt_mem_forward_ckpt_bf16"])

@@ -69,7 +69,7 @@ def test_backward_parity(label, wid, kw, dtype):
     dev, cd = to_dev(inp), to_dev(cot)
     args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
     nc = (w.T + w.b - 1) // w.b
-    ckpt = torch.empty(w.B, w.H, nc, 2, w.d, w.d, device="cuda")
+    ckpt = tm.new_ckpt(dev["q"], w.b)
     tm.forward_chunk_gates(*args, dev["M0"], b=w.b, ckpt=ckpt)
     g = tm.backward(*args, ckpt, cd["dz"], cd["dM_T"], cd["dS_T"], b=w.b, chunk_gates=True)
     torch.cuda.synchronize()
