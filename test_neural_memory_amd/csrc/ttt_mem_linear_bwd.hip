@@ -719,6 +719,10 @@ struct GradGeo {
     static_assert(NF * PART * 4 <= TILE, "partials fit the residual tile");
     // dz and -dv staged as operands too when they fit (else read from HBM / L2).
     static constexpr bool DZ_LDS = BASE + 2 * TILE + 1024 <= kLdsMax;
+    // The gate wave's reverse pass runs over dL alone before the feature
+    // waves' partial sums arrive (they enter as a closed-form correction)
+    // when a second copy of the gamma table fits; else it runs after them.
+    static constexpr bool SPLIT = BASE + (DZ_LDS ? 2 * TILE : 0) + NP * LF * 4 + 1024 <= kLdsMax;
     static_assert(BASE + 1024 <= kLdsMax, "LDS budget");
     static_assert(NP % KG == 0, "tiling");
 };
@@ -742,6 +746,7 @@ struct GradSmem {
     alignas(16) float c[NP];
     alignas(16) float wm[NP];
     alignas(16) float ws[NP];
+    alignas(16) float ce[Gm::SPLIT ? NP * Gm::LF : 4];   // the eta contributions (gamma kept in lm)
 };
 
 template <typename T, int D, int NP>
@@ -923,6 +928,82 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 st4<T>(dst, nd);
             }
         }
+        // Reverse through the column recurrences of gamma and p (lane = column j).
+        // Row i reads gamma rows i, i-1 and dL row i; the loads for the next
+        // row are issued one iteration ahead.  p comes back from gamma without
+        // a division: p_ij = gamma_ij - a_i gamma_{i-1,j} (gamma_{j-1,j} = 0).
+        // The contributions to a_i (into dl) and eta_i (into cedst) are summed
+        // over each row afterwards.  WITH_LAST adds the cotangents of the
+        // chunk-end weights (dwm_j, dws_j), which enter at row n - 1.
+        const int lc = l < NP ? l : 0;
+        float dth = 0.f;
+        auto reverse_pass = [&](auto with_last, float dwm_j, float dws_j, float* cedst) {
+            constexpr bool WITH_LAST = decltype(with_last)::value;
+            float gg = 0.f, gp = 0.f;
+            float g_i = sm.lm[(NP - 1) * LF + lc];
+            float g_im1 = NP > 1 ? sm.lm[(NP - 2) * LF + lc] : 0.f;
+            float d_i = sm.dl[(NP - 1) * LF + lc];
+#pragma unroll
+            for (int i = NP - 1; i >= 0; --i) {
+                const float g_im2 = i >= 2 ? sm.lm[(i >= 2 ? i - 2 : 0) * LF + lc] : 0.f;
+                const float d_im1 = i >= 1 ? sm.dl[(i >= 1 ? i - 1 : 0) * LF + lc] : 0.f;
+                const bool act = i >= l && i < n;
+                float dli = act ? d_i : 0.f;
+                const float a_i = readlane(my_a, i);
+                if constexpr (WITH_LAST) {
+                    const bool last = act && i == n - 1;
+                    if (last) dli += dwm_j;
+                    gg += my_th * dli;
+                    dth += dli * g_i;
+                    if (last) {
+                        gp += my_th * dws_j;
+                        dth += dws_j * (g_i - a_i * g_im1);
+                    }
+                } else {
+                    gg += my_th * dli;
+                    dth += dli * g_i;
+                }
+                float ca = 0.f, ce = 0.f;
+                if (i > 0 && i > l) {
+                    const float a_im1 = readlane(my_a, i > 0 ? i - 1 : 0);
+                    ca = gg * g_im1;
+                    gp += gg;
+                    ce = gp * (g_im1 - a_im1 * g_im2);
+                    gg *= a_i;
+                    gp *= readlane(my_et, i);
+                }
+                if (l < NP) {
+                    sm.dl[i * LF + l] = ca;
+                    cedst[i * LF + l] = ce;
+                }
+                g_i = g_im1;
+                g_im1 = g_im2;
+                d_i = d_im1;
+                // Keep the running sums in registers row by row (the compiler
+                // would otherwise defer them and hold every row's dL live).
+                asm volatile("" : "+v"(dth), "+v"(gg), "+v"(gp));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wave_lds_fence();
+        };
+        // Row sums (lane = row i) of the a and eta contributions.
+        float sa = 0.f, se = 0.f;
+        auto row_sums = [&](const float* cesrc) {
+            if (l < NP) {
+#pragma unroll 2
+                for (int j = 0; j < NP; j += 4) {
+                    const f32x4 va = *reinterpret_cast<const f32x4*>(sm.dl + l * LF + j);
+                    const f32x4 ve = *reinterpret_cast<const f32x4*>(cesrc + l * LF + j);
+                    sa += (va[0] + va[1]) + (va[2] + va[3]);
+                    se += (ve[0] + ve[1]) + (ve[2] + ve[3]);
+                }
+            }
+        };
+        if constexpr (Gm::SPLIT) {
+            wave_lds_fence();
+            reverse_pass(std::false_type{}, 0.f, 0.f, sm.ce);
+            row_sums(sm.ce);
+        }
         __syncthreads();   // (2) dL, -(D .* L)^T complete
         __syncthreads();   // (3) partial sums of the feature waves written
         // Scalar cotangents: partial sums added in wave order (deterministic).
@@ -938,70 +1019,63 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             dot1 += pf[4 * NP + 1];
             dEn += pf[4 * NP + 2];
         }
-
-        // Reverse through the column recurrences of gamma and p (lane = column j).
-        // Row i reads gamma rows i, i-1 and dL row i; the loads for the next
-        // row are issued one iteration ahead.  p comes back from gamma without
-        // a division: p_ij = gamma_ij - a_i gamma_{i-1,j} (gamma_{j-1,j} = 0).
-        const int lc = l < NP ? l : 0;
-        float gg = 0.f, gp = 0.f, dth = 0.f;
-        float g_i = sm.lm[(NP - 1) * LF + lc];
-        float g_im1 = NP > 1 ? sm.lm[(NP - 2) * LF + lc] : 0.f;
-        float d_i = sm.dl[(NP - 1) * LF + lc];
-#pragma unroll
-        for (int i = NP - 1; i >= 0; --i) {
-            const float g_im2 = i >= 2 ? sm.lm[(i >= 2 ? i - 2 : 0) * LF + lc] : 0.f;
-            const float d_im1 = i >= 1 ? sm.dl[(i >= 1 ? i - 1 : 0) * LF + lc] : 0.f;
-            const bool act = i >= l && i < n;
-            float dli = act ? d_i : 0.f;
-            const bool last = act && i == n - 1;
-            if (last) dli += dwm_j;
-            gg += my_th * dli;
-            dth += dli * g_i;
-            const float a_i = readlane(my_a, i);
-            if (last) {
-                gp += my_th * dws_j;
-                dth += dws_j * (g_i - a_i * g_im1);
-            }
-            float ca = 0.f, ce = 0.f;
-            if (i > 0 && i > l) {
-                const float a_im1 = readlane(my_a, i > 0 ? i - 1 : 0);
-                ca = gg * g_im1;
-                gp += gg;
-                ce = gp * (g_im1 - a_im1 * g_im2);
-                gg *= a_i;
-                gp *= readlane(my_et, i);
-            }
+        // g_i = u_i + f_i g_{i+1} with f_i = a_{i+1} (A, c and the a-suffix
+        // products) or eta_{i+1} (E and the eta-suffix products).
+        const float a_next = __shfl(my_a, l + 1 < kW ? l + 1 : l, kW);
+        const float e_next = __shfl(my_et, l + 1 < kW ? l + 1 : l, kW);
+        const float fa = l + 1 < NP ? a_next : 0.f, fe = l + 1 < NP ? e_next : 0.f;
+        if constexpr (!Gm::SPLIT) {
+            reverse_pass(std::true_type{}, dwm_j, dws_j, sm.lm);
+            row_sums(sm.lm);
+        } else {
+            // The chunk-end weights' cotangents enter the reverse pass at row
+            // n - 1 with gg = theta_j dwm_j =: u_j and gp = theta_j dws_j =: w_j.
+            // The pass is linear, so their part follows in closed form: at row i
+            // gg = u_j Ra_i and gp = w_j Re_i + u_j Qc_i, with the suffix products
+            // Ra_i = a_{i+1} .. a_{n-1}, Re_i = eta_{i+1} .. eta_{n-1} and
+            // Qc_i = Ra_i + eta_{i+1} Qc_{i+1}; summed over the columns j < i:
+            //   a part:   Ra_i (Gamma u)_{i-1}
+            //   eta part: Re_i (P w)_{i-1} + Qc_i (P u)_{i-1},
+            // with (P x)_{i-1} = (Gamma x)_{i-1} - a_{i-1} (Gamma x)_{i-2}.
+            const bool col_on = l < n;
+            const float g_last = sm.lm[(n - 1) * LF + lc];
+            const float g_prev = n >= 2 ? sm.lm[(n >= 2 ? n - 2 : 0) * LF + lc] : 0.f;
+            const float a_last = readlane(my_a, n - 1);
+            if (col_on) dth += dwm_j * g_last + dws_j * (g_last - a_last * g_prev);
+            // u and w go through the (no longer read) weight vectors.
             if (l < NP) {
-                sm.dl[i * LF + l] = ca;
-                sm.lm[i * LF + l] = ce;
+                sm.wm[l] = col_on ? my_th * dwm_j : 0.f;
+                sm.ws[l] = col_on ? my_th * dws_j : 0.f;
             }
-            g_i = g_im1;
-            g_im1 = g_im2;
-            d_i = d_im1;
-            // Keep the running sums in registers row by row (the compiler
-            // would otherwise defer them and hold every row's dL live).
-            asm volatile("" : "+v"(dth), "+v"(gg), "+v"(gp));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        wave_lds_fence();
-        // Row sums (lane = row i) and the prefix-product part.
-        float sa = 0.f, se = 0.f;
-        if (l < NP) {
-#pragma unroll 2
+            wave_lds_fence();
+            float gu = 0.f, gw = 0.f;   // (Gamma u)_r, (Gamma w)_r for r = lane
+#pragma unroll 4
             for (int j = 0; j < NP; j += 4) {
-                const f32x4 va = *reinterpret_cast<const f32x4*>(sm.dl + l * LF + j);
-                const f32x4 ve = *reinterpret_cast<const f32x4*>(sm.lm + l * LF + j);
-                sa += (va[0] + va[1]) + (va[2] + va[3]);
-                se += (ve[0] + ve[1]) + (ve[2] + ve[3]);
+                const f32x4 gr = *reinterpret_cast<const f32x4*>(sm.lm + lc * LF + j);
+                const f32x4 uu = *reinterpret_cast<const f32x4*>(sm.wm + j);
+                const f32x4 ww = *reinterpret_cast<const f32x4*>(sm.ws + j);
+                gu += (gr[0] * uu[0] + gr[1] * uu[1]) + (gr[2] * uu[2] + gr[3] * uu[3]);
+                gw += (gr[0] * ww[0] + gr[1] * ww[1]) + (gr[2] * ww[2] + gr[3] * ww[3]);
+            }
+            const float one_last = l == n - 1 ? 1.f : 0.f;
+            const float Ra = reverse_recurrence<NP>(one_last, fa, l);
+            const float Re = reverse_recurrence<NP>(one_last, fe, l);
+            const float Qc = reverse_recurrence<NP>(Ra, fe, l);
+            // Every lane takes part in the shuffles; the lanes with no row
+            // i - 1 (or i - 2) mask the value afterwards.
+            const int s1 = l >= 1 ? l - 1 : 0, s2 = l >= 2 ? l - 2 : 0;
+            const float gu1r = __shfl(gu, s1, kW), gu2r = __shfl(gu, s2, kW);
+            const float gw1r = __shfl(gw, s1, kW), gw2r = __shfl(gw, s2, kW);
+            const float a_m1 = __shfl(my_a, s1, kW);
+            const float gu1 = l >= 1 ? gu1r : 0.f, gu2 = l >= 2 ? gu2r : 0.f;
+            const float gw1 = l >= 1 ? gw1r : 0.f, gw2 = l >= 2 ? gw2r : 0.f;
+            if (l >= 1 && l < n) {
+                sa += Ra * gu1;
+                se += Re * (gw1 - a_m1 * gw2) + Qc * (gu1 - a_m1 * gu2);
             }
         }
         const float my_dA = dA_l + (l == n - 1 ? dot0 : 0.f);
         const float my_dc = dc_l + (l == n - 1 ? dot1 : 0.f);
-        // g_i = u_i + f_i g_{i+1} with f_i = a_{i+1} (A and c) or eta_{i+1} (E).
-        const float a_next = __shfl(my_a, l + 1 < kW ? l + 1 : l, kW);
-        const float e_next = __shfl(my_et, l + 1 < kW ? l + 1 : l, kW);
-        const float fa = l + 1 < NP ? a_next : 0.f, fe = l + 1 < NP ? e_next : 0.f;
         const float gA = reverse_recurrence<NP>(my_dA, fa, l);
         const float gc = reverse_recurrence<NP>(my_dc, fa, l);
         const float gE = reverse_recurrence<NP>(gc + (l == n - 1 ? dEn : 0.f), fe, l);
