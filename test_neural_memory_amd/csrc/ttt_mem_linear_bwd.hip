@@ -1109,25 +1109,59 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         // columns (k = row of the state): raw loads, then conversion, so the
         // next state's loads are in flight while the current one is used.
         // Raw column values, two consecutive rows per 32-bit register.
-        using R2 = typename std::conditional<Op<T>::kF16, f16x2, f32x2>::type;
+        // fp16: one 32-bit word per register (two adjacent columns of row
+        // r + (lr & 1)); lanes 2m and 2m + 1 then swap halves (one DPP move and
+        // one byte permute) so that each holds rows r, r + 1 of its own column.
+        // Buffer loads keep the state's base in scalar registers and the row
+        // offsets as constants; rows at or past D read 0.
+        using R2 = typename std::conditional<Op<T>::kF16, uint32_t, f32x2>::type;
         constexpr int NRAW = NKD * KS / 2;
         auto colload = [&](const T* X, int f0, R2* raw) {
+            if constexpr (Op<T>::kF16) {
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(X, D * D * sizeof(T));
+                const uint32_t vo = static_cast<uint32_t>(((KS * lg + (lr & 1)) * D + f0 + (lr & ~1)) * sizeof(T));
 #pragma unroll
-            for (int kk = 0; kk < NKD; ++kk) {
+                for (int kk = 0; kk < NKD; ++kk) {
 #pragma unroll
-                for (int s2 = 0; s2 < KS; s2 += 2) {
-                    const int r = kk * KG + KS * lg + s2;
-                    const size_t o = static_cast<size_t>(r < D ? r : 0) * D + f0 + lr;
-                    raw[(kk * KS + s2) / 2] = R2{X[o], X[o + D]};
+                    for (int s2 = 0; s2 < KS; s2 += 2)
+                        raw[(kk * KS + s2) / 2] = __builtin_bit_cast(
+                            uint32_t, buf_load4(rs, vo + static_cast<uint32_t>((kk * KG + s2) * D * sizeof(T))));
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) {
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; s2 += 2) {
+                        const int r = kk * KG + KS * lg + s2;
+                        const size_t o = static_cast<size_t>(r < D ? r : 0) * D + f0 + lr;
+                        raw[(kk * KS + s2) / 2] = R2{X[o], X[o + D]};
+                    }
                 }
             }
         };
         auto colcvt = [&](const R2* raw, F* out) {
+            if constexpr (Op<T>::kF16) {
+                // even lane: (own lo, partner lo); odd lane: (partner hi, own hi)
+                const uint32_t sel = (lr & 1) ? 0x03020706u : 0x05040100u;
 #pragma unroll
-            for (int kk = 0; kk < NKD; ++kk) {
+                for (int kk = 0; kk < NKD; ++kk) {
 #pragma unroll
-                for (int s2 = 0; s2 < KS; ++s2)
-                    out[kk][s2] = kk * KG + KS * lg + s2 < D ? raw[(kk * KS + s2) / 2][s2 & 1] : static_cast<T>(0.f);
+                    for (int s2 = 0; s2 < KS; s2 += 2) {
+                        const uint32_t wv = raw[(kk * KS + s2) / 2];
+                        const uint32_t pv = static_cast<uint32_t>(
+                            __builtin_amdgcn_mov_dpp(static_cast<int>(wv), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+                        const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(pv, wv, sel));
+                        out[kk][s2] = h[0];
+                        out[kk][s2 + 1] = h[1];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) {
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2)
+                        out[kk][s2] = kk * KG + KS * lg + s2 < D ? raw[(kk * KS + s2) / 2][s2 & 1] : static_cast<T>(0.f);
+                }
             }
         };
         // Residual rows of E^T: E^T[r][t] = M0[r][:] . k_t - v_t[r].
