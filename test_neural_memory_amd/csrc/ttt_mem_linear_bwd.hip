@@ -713,8 +713,8 @@ struct GradGeo {
     static constexpr int LF = NP + 4;
     static constexpr int TILE = NP * LQ * (int)sizeof(T);
     static constexpr int BASE = 3 * TILE + NP * LPT * (int)sizeof(T) + 2 * NP * LF * 4 + 8 * NP * 4;
-    // Per-wave partial sums (four token vectors and three dots) reuse the
-    // residual tile once it is consumed; the gate wave adds them in wave order.
+    // Per-wave partial sums (four token vectors and three dots), added by the
+    // gate wave in wave order.
     static constexpr int PART = 4 * NP + 4;
     static_assert(NF * PART * 4 <= TILE, "partials fit the residual tile");
     // dz and -dv staged as operands too when they fit (else read from HBM / L2).
@@ -723,6 +723,11 @@ struct GradGeo {
     // waves' partial sums arrive (they enter as a closed-form correction)
     // when a second copy of the gamma table fits; else it runs after them.
     static constexpr bool SPLIT = BASE + (DZ_LDS ? 2 * TILE : 0) + NP * LF * 4 + 1024 <= kLdsMax;
+    // The partial sums get a region of their own when it fits too (written as
+    // soon as they are formed, one barrier fewer); else they reuse the
+    // residual tile once it is consumed.
+    static constexpr bool PART_OWN =
+        SPLIT && BASE + (DZ_LDS ? 2 * TILE : 0) + NP * LF * 4 + NF * PART * 4 + 1024 <= kLdsMax;
     static_assert(BASE + 1024 <= kLdsMax, "LDS budget");
     static_assert(NP % KG == 0, "tiling");
 };
@@ -747,6 +752,7 @@ struct GradSmem {
     alignas(16) float wm[NP];
     alignas(16) float ws[NP];
     alignas(16) float ce[Gm::SPLIT ? NP * Gm::LF : 4];   // the eta contributions (gamma kept in lm)
+    alignas(16) float part[Gm::PART_OWN ? Gm::NF * Gm::PART : 4];
 };
 
 template <typename T, int D, int NP>
@@ -842,7 +848,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         }
     }
     // Partial sums of feature wave f: [dA | dc | dw^M | dw^S][NP], then the three dots.
-    float* const part = reinterpret_cast<float*>(sm.ec);
+    float* const part = Gm::PART_OWN ? sm.part : reinterpret_cast<float*>(sm.ec);
     __syncthreads();
 
     // Row-major operand fragment of dz or -dv (token row t, k-group at k0).
@@ -862,6 +868,37 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 x[s + 3] = sign * v4[3];
             }
             return R::from_f32(x);
+        }
+    };
+
+    // Lower tiles of G = Q K^T and D = dZ E^T: dL = -G .* D into dl and
+    // -(D .* L)^T into dlt (upper tiles zero), shared out over all waves.
+    auto tiles = [&]() {
+#pragma unroll 1
+        for (int idx = w; idx < NT * NT; idx += Gm::NWAVE) {
+            const int it = idx / NT, jt = idx % NT;
+            const int j = 16 * jt + lr;
+            T* dst = sm.dlt + j * LPT + 16 * it + 4 * lg;
+            if (jt > it) {
+                st4<T>(dst, f32x4{0.f, 0.f, 0.f, 0.f});
+                continue;
+            }
+            f32x4 gacc = {0.f, 0.f, 0.f, 0.f}, dacc = gacc;
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) {
+                gacc = O::mma(gacc, R::rm(sm.q, LQ, 16 * it + lr, kk * KG, lg), R::rm(sm.k, LQ, j, kk * KG, lg));
+                dacc = O::mma(dacc, zfrag(sm.dz, p.dz, 1.f, 16 * it + lr, kk * KG), R::rm(sm.ec, LQ, j, kk * KG, lg));
+            }
+            f32x4 nd;
+            const float thj = sm.th[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * lg + e;
+                const bool ok = j <= i;
+                nd[e] = ok ? -dacc[e] * (thj * sm.lm[i * LF + j]) : 0.f;
+                sm.dl[i * LF + j] = ok ? -gacc[e] * dacc[e] : 0.f;
+            }
+            st4<T>(dst, nd);
         }
     };
 
@@ -899,35 +936,8 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         }
         __syncthreads();   // (1) gates and residual tiles ready
 
-        // Lower tiles of G = Q K^T and D = dZ E^T: dL = -G .* D, -(D .* L)^T.
-#pragma unroll 1
-        for (int it = 0; it < NT; ++it) {
-#pragma unroll 1
-            for (int jt = 0; jt < NT; ++jt) {
-                const int j = 16 * jt + lr;
-                T* dst = sm.dlt + j * LPT + 16 * it + 4 * lg;
-                if (jt > it) {
-                    st4<T>(dst, f32x4{0.f, 0.f, 0.f, 0.f});
-                    continue;
-                }
-                f32x4 gacc = {0.f, 0.f, 0.f, 0.f}, dacc = gacc;
-#pragma unroll
-                for (int kk = 0; kk < NKD; ++kk) {
-                    gacc = O::mma(gacc, R::rm(sm.q, LQ, 16 * it + lr, kk * KG, lg), R::rm(sm.k, LQ, j, kk * KG, lg));
-                    dacc = O::mma(dacc, zfrag(sm.dz, p.dz, 1.f, 16 * it + lr, kk * KG), R::rm(sm.ec, LQ, j, kk * KG, lg));
-                }
-                f32x4 nd;
-                const float thj = sm.th[j];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * it + 4 * lg + e;
-                    const bool ok = j <= i;
-                    nd[e] = ok ? -dacc[e] * (thj * sm.lm[i * LF + j]) : 0.f;
-                    sm.dl[i * LF + j] = ok ? -gacc[e] * dacc[e] : 0.f;
-                }
-                st4<T>(dst, nd);
-            }
-        }
+        tiles();
+        __syncthreads();   // (1b) dL and -(D .* L)^T complete
         // Reverse through the column recurrences of gamma and p (lane = column j).
         // Row i reads gamma rows i, i-1 and dL row i; the loads for the next
         // row are issued one iteration ahead.  p comes back from gamma without
@@ -1004,8 +1014,8 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             reverse_pass(std::false_type{}, 0.f, 0.f, sm.ce);
             row_sums(sm.ce);
         }
-        __syncthreads();   // (2) dL, -(D .* L)^T complete
-        __syncthreads();   // (3) partial sums of the feature waves written
+        __syncthreads();   // (2) feature waves past their state products
+        if constexpr (!Gm::PART_OWN) __syncthreads();   // (3) partial sums of the feature waves written
         // Scalar cotangents: partial sums added in wave order (deterministic).
         float dA_l = 0.f, dc_l = 0.f, dwm_j = 0.f, dws_j = 0.f, dot0 = 0.f, dot1 = 0.f, dEn = 0.f;
 #pragma unroll
@@ -1192,6 +1202,8 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         R2 raw[NRAW];
         colload(Sc, 16 * fw * FPW, raw);
         __syncthreads();   // (1)
+        tiles();
+        __syncthreads();   // (1b)
 
         // Products with features f0.. as rows and tokens as columns: lane
         // (lr, lg) holds features f0 + 4lg + e of token t = 16tt + lr.
@@ -1215,6 +1227,16 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         float d1 = 0.f, d2 = 0.f, d3 = 0.f;
         f32x4 dQ[FPW][NT], dK[FPW][NT];
         float pa[FPW][NT], pc[FPW][NT], pwm[FPW][NT], pws[FPW][NT];
+        // Partial j of the tile's token t: stored at once into its own region
+        // (the four lane groups hold the same sum and store it together, no
+        // branch), else kept until the residual tile is free.
+        auto keep = [&](float (&arr)[FPW][NT], int ft, int tt, int j, float x) {
+            if constexpr (Gm::PART_OWN) {
+                part[(fw * FPW + ft) * Gm::PART + j * NP + 16 * tt + lr] = x;
+            } else {
+                arr[ft][tt] = x;
+            }
+        };
 #pragma unroll
         for (int ft = 0; ft < FPW; ++ft) {
             const int f0 = 16 * (fw * FPW + ft);
@@ -1228,7 +1250,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < NKD; ++kk) Y = O::mma(Y, fs[kk], zfrag(sm.dz, p.dz, 1.f, t, kk * KG));
-                pc[ft][tt] = rdot(ld4<T>(sm.q + t * LQ + f0 + 4 * lg), Y);
+                keep(pc, ft, tt, 1, rdot(ld4<T>(sm.q + t * LQ + f0 + 4 * lg), Y));
                 dQ[ft][tt] = sm.c[t] * Y;
             }
             colcvt(raw, fo);                       // dS'
@@ -1241,7 +1263,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 f32x4 W = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < NKD; ++kk) W = O::mma(W, fo[kk], R::rm(sm.ec, LQ, t, kk * KG, lg));
-                pws[ft][tt] = -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), W);
+                keep(pws, ft, tt, 3, -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), W));
                 dK[ft][tt] = -sm.ws[t] * W;
             }
             colcvt(raw, fo);                       // dM'
@@ -1254,7 +1276,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 f32x4 U = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < NKD; ++kk) U = O::mma(U, fo[kk], R::rm(sm.ec, LQ, t, kk * KG, lg));
-                pwm[ft][tt] = -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), U);
+                keep(pwm, ft, tt, 2, -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), U));
                 dK[ft][tt] -= sm.wm[t] * U;
             }
             colcvt(raw, fm);                       // M0
@@ -1270,7 +1292,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                     X = O::mma(X, fm[kk], zfrag(sm.dz, p.dz, 1.f, t, kk * KG));
                     H = O::mma(H, fm[kk], zfrag(sm.de, p.dv, -1.f, t, kk * KG));
                 }
-                pa[ft][tt] = rdot(ld4<T>(sm.q + t * LQ + f0 + 4 * lg), X);
+                keep(pa, ft, tt, 0, rdot(ld4<T>(sm.q + t * LQ + f0 + 4 * lg), X));
                 dQ[ft][tt] += sm.A[t] * X;
                 dK[ft][tt] += H;
             }
@@ -1278,18 +1300,20 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         d1 = wave_sum(d1);
         d2 = wave_sum(d2);
         d3 = wave_sum(d3);
-        __syncthreads();   // (2) residual tile consumed
+        if constexpr (!Gm::PART_OWN) __syncthreads();   // (2) residual tile consumed
 #pragma unroll
         for (int ft = 0; ft < FPW; ++ft) {
             float* pf = part + (fw * FPW + ft) * Gm::PART;
-            if (lg == 0) {
+            if constexpr (!Gm::PART_OWN) {
+                if (lg == 0) {
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
-                    const int t = 16 * tt + lr;
-                    pf[t] = pa[ft][tt];
-                    pf[NP + t] = pc[ft][tt];
-                    pf[2 * NP + t] = pwm[ft][tt];
-                    pf[3 * NP + t] = pws[ft][tt];
+                    for (int tt = 0; tt < NT; ++tt) {
+                        const int t = 16 * tt + lr;
+                        pf[t] = pa[ft][tt];
+                        pf[NP + t] = pc[ft][tt];
+                        pf[2 * NP + t] = pwm[ft][tt];
+                        pf[3 * NP + t] = pws[ft][tt];
+                    }
                 }
             }
             if (lane == 0) {
@@ -1298,7 +1322,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 pf[4 * NP + 2] = ft == 0 ? d3 : 0.f;
             }
         }
-        __syncthreads();   // (3)
+        __syncthreads();   // (3); with a partial region of its own, also (2)
 
         // dQ -= (DL K)^T, dK -= (DL^T Q)^T  (dlt holds -DL^T).
 #pragma unroll
