@@ -166,6 +166,54 @@ __device__ __forceinline__ f32x4 gload4(const typename GlobalOf<T>::type* src) {
     }
 }
 
+// 1.0 in lane i, 0.0 elsewhere: one select on a lane mask in scalar registers.
+__device__ __forceinline__ float unit_at(int i) {
+    float d;
+    asm("v_cndmask_b32_e64 %0, 0, 1.0, %1" : "=v"(d) : "s"(1ull << i));
+    return d;
+}
+
+// Column j = lane of the decay tables of a chunk: p_ij = eta_i p_{i-1,j} and
+// gamma_ij = a_i gamma_{i-1,j} + p_ij below the diagonal, both 1 on it and 0
+// above.  The two updates started from zero keep the zeros, and a unit added
+// at i = j starts the column (no branches).  a and eta are read per four rows
+// as LDS broadcasts; put(i, gamma_ij) stores row i; the values at row n - 1
+// are returned in g_last, p_last (a full chunk, n = NP, needs no per-row
+// selects for them).
+template <int NP, bool FULL, typename Put>
+__device__ __forceinline__ void gamma_columns_impl(const float* av, const float* et, int n, Put& put,
+                                                   float& g_last, float& p_last) {
+    float g = 0.f, pp = 0.f;
+    g_last = 0.f;
+    p_last = 0.f;
+#pragma unroll
+    for (int i0 = 0; i0 < NP; i0 += 4) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(av + i0);
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(et + i0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            pp = __builtin_fmaf(e4[e], pp, unit_at(i));
+            g = __builtin_fmaf(a4[e], g, pp);
+            put(i, g);
+            if constexpr (!FULL) {
+                g_last = i == n - 1 ? g : g_last;
+                p_last = i == n - 1 ? pp : p_last;
+            }
+        }
+    }
+    if constexpr (FULL) {
+        g_last = g;
+        p_last = pp;
+    }
+}
+template <int NP, typename Put>
+__device__ __forceinline__ void gamma_columns(const float* av, const float* et, int n, Put put, float& g_last,
+                                              float& p_last) {
+    if (n == NP) gamma_columns_impl<NP, true>(av, et, n, put, g_last, p_last);
+    else gamma_columns_impl<NP, false>(av, et, n, put, g_last, p_last);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int m = 1; m < kW; m <<= 1) x += __shfl_xor(x, m, kW);
@@ -299,7 +347,8 @@ struct Carry {
     // Loader: a chunk's q, k rows (all features), dz columns row0..row0+RB-1
     // and gates are fetched into registers one step ahead (issue) and written
     // to a staging slot the next step (commit), so HBM latency overlaps a
-    // whole chunk step.
+    // whole chunk step.  Issue only requests (clamped addresses, always in
+    // bounds); the ragged tail is zeroed at commit, when the data is there.
     static constexpr int CB = 16 / (int)sizeof(G);   // elements per 16-byte unit
     static constexpr int UR = Gm::DS / CB;           // q / k units per row
     static constexpr int NLW = 2;                    // loader waves
@@ -322,34 +371,32 @@ struct Carry {
             const int t = u / UR, col = (u % UR) * CB;
             const bool ok = u < NP * UR && t < n && col < D;
             const size_t g = ok ? (tok0 + t) * D + col : 0;   // clamped: every load is in bounds
-            const uint4 a = *reinterpret_cast<const uint4*>(q + g);
-            const uint4 b = *reinterpret_cast<const uint4*>(k + g);
-            r.q[i] = ok ? a : uint4{0u, 0u, 0u, 0u};
-            r.k[i] = ok ? b : uint4{0u, 0u, 0u, 0u};
+            r.q[i] = *reinterpret_cast<const uint4*>(q + g);
+            r.k[i] = *reinterpret_cast<const uint4*>(k + g);
         }
 #pragma unroll
         for (int i = 0; i < NZU; ++i) {
             const int u = lane + (lw + i * NLW) * kW;
             const int t = u / UZ, col = (u % UZ) * 4;
             const bool ok = u < NP * UZ && t < n;
-            const f32x4 v = *reinterpret_cast<const f32x4*>(p.dz + (ok ? (tok0 + t) * D + row0 + col : 0));
-            r.z[i] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            r.z[i] = *reinterpret_cast<const f32x4*>(p.dz + (ok ? (tok0 + t) * D + row0 + col : 0));
         }
-        const bool ok = lane < n;
-        const size_t gi = ok ? g0 + static_cast<size_t>(lane) * gs : 0;
-        const float th = p.theta[gi], et = p.eta[gi], al = p.alpha[gi];
-        r.th = ok ? th : 0.f;
-        r.et = ok ? et : 1.f;
-        r.al = ok ? al : 0.f;
+        const size_t gi = lane < n ? g0 + static_cast<size_t>(lane) * gs : 0;
+        r.th = p.theta[gi];
+        r.et = p.eta[gi];
+        r.al = p.alpha[gi];
     }
-    __device__ static void commit(const Regs& r, typename Sm::QSlot& s, int lane, int lw) {
+    // n: the chunk's token count (positions at or past it are written as zero
+    // and as the identity gates).
+    __device__ static void commit(const Regs& r, typename Sm::QSlot& s, int n, int lane, int lw) {
 #pragma unroll
         for (int i = 0; i < NQU; ++i) {
             const int u = lane + (lw + i * NLW) * kW;
             if (u < NP * UR) {
                 const int t = u / UR, col = (u % UR) * CB;
-                put_unit<T>(s.q + t * LQ + col, r.q[i]);
-                put_unit<T>(s.k + t * LQ + col, r.k[i]);
+                const bool ok = t < n && col < D;
+                put_unit<T>(s.q + t * LQ + col, ok ? r.q[i] : uint4{0u, 0u, 0u, 0u});
+                put_unit<T>(s.k + t * LQ + col, ok ? r.k[i] : uint4{0u, 0u, 0u, 0u});
             }
         }
 #pragma unroll
@@ -357,13 +404,14 @@ struct Carry {
             const int u = lane + (lw + i * NLW) * kW;
             if (u < NP * UZ) {
                 const int t = u / UZ, col = (u % UZ) * 4;
-                st4<T>(s.dz + t * LZ + col, r.z[i]);
+                st4<T>(s.dz + t * LZ + col, t < n ? r.z[i] : f32x4{0.f, 0.f, 0.f, 0.f});
             }
         }
         if (lw == 0 && lane < NP) {
-            s.th[lane] = r.th;
-            s.et[lane] = r.et;
-            s.av[lane] = 1.f - r.al;
+            const bool ok = lane < n;
+            s.th[lane] = ok ? r.th : 0.f;
+            s.et[lane] = ok ? r.et : 1.f;
+            s.av[lane] = ok ? 1.f - r.al : 1.f;
         }
     }
 
@@ -411,50 +459,46 @@ struct Carry {
             ps.scal[2] = En;
         }
         // Column j = lane of gamma and p.
-        float g = 0.f, pp = 0.f, wm = 0.f, ws = 0.f;
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const float ai = readlane(my_a, i), ei = readlane(my_et, i);
-            if (i == lane) {
-                pp = 1.f;
-                g = 1.f;
-            } else if (i > lane) {
-                pp = ei * pp;
-                g = ai * g + pp;
-            }
+        float g_last, p_last;
+        gamma_columns<NP>(s.av, s.et, n, [&](int i, float g) {
             if (lane < NP) ls[i * LF + lane] = my_th * g;
-            if (i == n - 1) {
-                wm = my_th * g;
-                ws = my_th * pp;
-            }
-        }
+        }, g_last, p_last);
         if (lane < NP) {
-            ps.wm[lane] = wm;
-            ps.ws[lane] = ws;
+            ps.wm[lane] = my_th * g_last;
+            ps.ws[lane] = my_th * p_last;
         }
         wave_lds_fence();
-        // P^T tiles: G[i][t] = q_i . k_t on the lower tiles, times L_it.
+        // P^T tiles: G[i][t] = q_i . k_t on the lower tiles, times L_it (L is
+        // zero above the diagonal); upper tiles zero.  The q fragments of a
+        // row tile are read once; each tile's k fragments and L values are
+        // read together ahead of its products.
 #pragma unroll
         for (int it = 0; it < Gm::NT; ++it) {
 #pragma unroll
-            for (int tt = 0; tt < Gm::NT; ++tt) {
+            for (int tt = it + 1; tt < Gm::NT; ++tt)
+                st4<T>(ps.pt + (16 * tt + lr) * LP + 16 * it + 4 * lg, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+#pragma unroll
+        for (int it = 0; it < Gm::NT; ++it) {
+            F qf[Gm::NKD];
+#pragma unroll
+            for (int kk = 0; kk < Gm::NKD; ++kk) qf[kk] = R::rm(s.q, LQ, 16 * it + lr, kk * KG, lg);
+#pragma unroll
+            for (int tt = 0; tt <= it; ++tt) {
                 const int t = 16 * tt + lr;
-                T* dst = ps.pt + t * LP + 16 * it + 4 * lg;
-                if (tt > it) {
-                    st4<T>(dst, f32x4{0.f, 0.f, 0.f, 0.f});
-                    continue;
-                }
+                F kf[Gm::NKD];
+                float lv[4];
+#pragma unroll
+                for (int kk = 0; kk < Gm::NKD; ++kk) kf[kk] = R::rm(s.k, LQ, t, kk * KG, lg);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lv[e] = ls[(16 * it + 4 * lg + e) * LF + t];
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < Gm::NKD; ++kk)
-                    acc = O::mma(acc, R::rm(s.q, LQ, 16 * it + lr, kk * KG, lg), R::rm(s.k, LQ, t, kk * KG, lg));
+                for (int kk = 0; kk < Gm::NKD; ++kk) acc = O::mma(acc, qf[kk], kf[kk]);
                 f32x4 pv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * it + 4 * lg + e;
-                    pv[e] = t <= i ? acc[e] * ls[i * LF + t] : 0.f;
-                }
-                st4<T>(dst, pv);
+                for (int e = 0; e < 4; ++e) pv[e] = t <= 16 * it + 4 * lg + e ? acc[e] * lv[e] : 0.f;
+                st4<T>(ps.pt + t * LP + 16 * it + 4 * lg, pv);
             }
         }
     }
@@ -501,7 +545,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         C::issue(p, lr_regs, seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane, lw, gate0(c),
                  gstride);
     };
-    auto do_commit = [&](int u) { C::commit(lr_regs, sm.qs[u % Gm::NQ], lane, lw); };
+    auto do_commit = [&](int u) { C::commit(lr_regs, sm.qs[u % Gm::NQ], chunk_n(chunk_of(u)), lane, lw); };
     auto do_build = [&](int u) {
         const int c = chunk_of(u);
         C::build(sm.qs[u % Gm::NQ], sm.ps[u % Gm::NPR], sm.ls, chunk_n(c), lane);
@@ -895,7 +939,8 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * it + 4 * lg + e;
                 const bool ok = j <= i;
-                nd[e] = ok ? -dacc[e] * (thj * sm.lm[i * LF + j]) : 0.f;
+                const float gv = sm.lm[i * LF + j];   // unconditional read: a select, not a branch
+                nd[e] = ok ? -dacc[e] * (thj * gv) : 0.f;
                 sm.dl[i * LF + j] = ok ? -gacc[e] * dacc[e] : 0.f;
             }
             st4<T>(dst, nd);
@@ -913,26 +958,13 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             sm.Ev[l] = E;
             sm.c[l] = cc;
         }
-        float g = 0.f, pp = 0.f, wm = 0.f, ws = 0.f;
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const float ai = readlane(my_a, i), ei = readlane(my_et, i);
-            if (i == l) {
-                pp = 1.f;
-                g = 1.f;
-            } else if (i > l) {
-                pp = ei * pp;
-                g = ai * g + pp;
-            }
+        float g_last, p_last;
+        gamma_columns<NP>(sm.av, sm.et, n, [&](int i, float g) {
             if (l < NP) sm.lm[i * LF + l] = g;
-            if (i == n - 1) {
-                wm = my_th * g;
-                ws = my_th * pp;
-            }
-        }
+        }, g_last, p_last);
         if (l < NP) {
-            sm.wm[l] = wm;
-            sm.ws[l] = ws;
+            sm.wm[l] = my_th * g_last;
+            sm.ws[l] = my_th * p_last;
         }
         __syncthreads();   // (1) gates and residual tiles ready
 
