@@ -606,7 +606,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the memory forward needs no "
-              "collective and this build runs on a single MI355X; shard (batch, head) pairs across "
+              "collective and this implementation runs on a single MI355X; shard (batch, head) pairs across "
               "processes to use more GPUs.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
