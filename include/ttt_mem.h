@@ -306,13 +306,69 @@ int ttt_mem_backward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_
                              float* dM0, float* dS0, uint16_t* work,
                              int B, int H, int T, int d, int b, void* stream);
 
+/*
+ * Training over packed variable-length documents: the forward that also keeps
+ * every document's chunk-start states, and the backward pass from them.  Each
+ * document is its own sequence with its own initial state (the forward's
+ * packed-document entry points above), so its gradients are exactly those of
+ * ttt_mem_backward_* on that document alone ("Continual Learning: From
+ * Attention to Neural Memory", section 4.5: the outer gradient runs back
+ * through the unrolled writes; "5.1.1 · TTT layers 与 fast weights", section
+ * 1.2, the notes on packed documents: nothing flows across a document
+ * boundary).
+ *
+ *   Checkpoints and work buffer: [H][ceil(T/b) + N][M | S][d][d], float32 on
+ *     the f32 entry points and fp16 on the bf16 ones, of
+ *     ttt_mem_ckpt_bytes_varlen / ttt_mem_ckpt_bytes_varlen_bf16 bytes, caller
+ *     owned.  Document s of head h uses the slots from h * (ceil(T/b) + N) +
+ *     (the chunks of documents 0..s-1) on; the rest are not written.
+ *   Layouts: q, k, v, dz, dq, dk, dv [H, T, d]; theta, eta, alpha and their
+ *     gradients [H, T]; M0, S0, dM_T, dS_T, dM0, dS0 [N, H, d, d]; cu_seqlens as
+ *     for ttt_mem_forward_varlen_*.  The gradients of tokens outside every
+ *     document are not written.
+ *   Everything else (NULL arguments, alignment, overlap and size checks,
+ *   precision) as for ttt_mem_forward_ckpt_* and ttt_mem_backward_*.
+ *   Chunk-shared gates are not supported here.  Returns TTT_ERR_INVALID_ARG
+ *   for a NULL ckpt or cu_seqlens.
+ */
+size_t ttt_mem_ckpt_bytes_varlen(int N, int H, int T, int d, int b);
+size_t ttt_mem_ckpt_bytes_varlen_bf16(int N, int H, int T, int d, int b);
+
+int ttt_mem_forward_varlen_ckpt_f32(const float* q, const float* k, const float* v,
+                                    const float* theta, const float* eta, const float* alpha,
+                                    const float* M0, const float* S0,
+                                    float* z, float* M_T, float* S_T, float* ckpt,
+                                    const int* cu_seqlens, int N, int H, int T, int d, int b, void* stream);
+
+int ttt_mem_forward_varlen_ckpt_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const float* theta, const float* eta, const float* alpha,
+                                     const float* M0, const float* S0,
+                                     float* z, float* M_T, float* S_T, uint16_t* ckpt,
+                                     const int* cu_seqlens, int N, int H, int T, int d, int b, void* stream);
+
+int ttt_mem_backward_varlen_f32(const float* q, const float* k, const float* v,
+                                const float* theta, const float* eta, const float* alpha,
+                                const float* ckpt, const float* dz, const float* dM_T, const float* dS_T,
+                                float* dq, float* dk, float* dv,
+                                float* dtheta, float* deta, float* dalpha,
+                                float* dM0, float* dS0, float* work,
+                                const int* cu_seqlens, int N, int H, int T, int d, int b, void* stream);
+
+int ttt_mem_backward_varlen_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const float* theta, const float* eta, const float* alpha,
+                                 const uint16_t* ckpt, const float* dz, const float* dM_T, const float* dS_T,
+                                 float* dq, float* dk, float* dv,
+                                 float* dtheta, float* deta, float* dalpha,
+                                 float* dM0, float* dS0, uint16_t* work,
+                                 const int* cu_seqlens, int N, int H, int T, int d, int b, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* ttt_mem_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int ttt_mem_abi_version(void);
 
-#define TTT_MEM_ABI_VERSION ((1 << 16) | 3)
+#define TTT_MEM_ABI_VERSION ((1 << 16) | 4)
 
 #ifdef __cplusplus
 }

@@ -5,12 +5,12 @@ The compute lives in ``libttt_mem.so`` (HIP for gfx950, C ABI in
 binding and the seeded synthetic workloads used by the tests and the bench.
 """
 
-from .memory import (LinearMemoryFunction, backward, decode, forward, forward_chunk_gates, forward_train, forward_varlen,
-                     linear_memory,
+from .memory import (LinearMemoryFunction, backward, backward_varlen, decode, forward, forward_chunk_gates,
+                     forward_train, forward_varlen, linear_memory, new_ckpt_varlen,
                      ttt_mem_decode_bf16, ttt_mem_decode_f32, ttt_mem_forward_bf16, ttt_mem_forward_f32,
                      ttt_mem_mlp_forward_bf16)
 
-__all__ = ["LinearMemoryFunction", "backward", "decode", "forward", "forward_chunk_gates", "forward_train", "forward_varlen",
-           "linear_memory",
+__all__ = ["LinearMemoryFunction", "backward", "backward_varlen", "decode", "forward", "forward_chunk_gates",
+           "forward_train", "forward_varlen", "linear_memory", "new_ckpt_varlen",
            "ttt_mem_decode_bf16", "ttt_mem_decode_f32", "ttt_mem_forward_bf16", "ttt_mem_forward_f32",
            "ttt_mem_mlp_forward_bf16"]

@@ -38,6 +38,12 @@ _SIGNATURES = {
     "ttt_mem_forward_cg_bf16": (_I, [_P] * 12 + [_I] * 5 + [_P]),
     "ttt_mem_backward_cg_f32": (_I, [_P] * 19 + [_I] * 5 + [_P]),
     "ttt_mem_backward_cg_bf16": (_I, [_P] * 19 + [_I] * 5 + [_P]),
+    "ttt_mem_ckpt_bytes_varlen": (ctypes.c_size_t, [_I] * 5),
+    "ttt_mem_ckpt_bytes_varlen_bf16": (ctypes.c_size_t, [_I] * 5),
+    "ttt_mem_forward_varlen_ckpt_f32": (_I, [_P] * 13 + [_I] * 5 + [_P]),
+    "ttt_mem_forward_varlen_ckpt_bf16": (_I, [_P] * 13 + [_I] * 5 + [_P]),
+    "ttt_mem_backward_varlen_f32": (_I, [_P] * 20 + [_I] * 5 + [_P]),
+    "ttt_mem_backward_varlen_bf16": (_I, [_P] * 20 + [_I] * 5 + [_P]),
     "ttt_mem_status_string": (ctypes.c_char_p, [_I]),
     "ttt_mem_abi_version": (_I, []),
 }

@@ -194,6 +194,39 @@ size_t ckpt_bytes(int B, int H, int T, int d, int b, size_t elem = sizeof(float)
     return static_cast<size_t>(B) * H * nch * 2 * d * d * elem;
 }
 
+// A byte range of a buffer (argument overlap checks).
+struct Span {
+    const void* p;
+    size_t n;
+};
+
+// Packed documents ([H, T] tokens, N documents): chunk slots per head.  A
+// document of length l has ceil(l / b) chunks, so the N documents of a head
+// have at most ceil(T / b) + N of them; document s of head h owns the slots
+// h * slots + (chunks of documents 0..s-1) onward.
+inline long long varlen_chunk_slots(int N, int T, int b) {
+    return (static_cast<long long>(T) + b - 1) / b + N;
+}
+size_t ckpt_bytes_varlen(int N, int H, int T, int d, int b, size_t elem = sizeof(float)) {
+    if (N < 0 || H < 0 || T < 0 || d < 1 || b < 1) return 0;
+    return static_cast<size_t>(H) * static_cast<size_t>(varlen_chunk_slots(N, T, b)) * 2 * d * d * elem;
+}
+// Length of document s, its offsets clamped into [0, T] (a malformed table
+// cannot reach outside the packed arrays).
+__device__ __forceinline__ int doc_len(const int* cu, int s, int T, int& t0) {
+    t0 = min(max(cu[s], 0), T);
+    return min(max(cu[s + 1], t0), T) - t0;
+}
+// Chunks of documents 0 .. s-1 (the first chunk slot of document s).
+__device__ __forceinline__ int doc_chunk_prefix(const int* cu, int s, int T, int b) {
+    int acc = 0;
+    for (int j = 0; j < s; ++j) {
+        int t0;
+        acc += (doc_len(cu, j, T, t0) + b - 1) / b;
+    }
+    return acc;
+}
+
 }  // namespace
 
 #endif  // TTT_MEM_GFX950_H

@@ -167,14 +167,16 @@ struct Params {
     // its state is slot s * H + h.
     const int* cu;
     int H;
-    // Chunk-start states for the backward pass (NULL: not written), dense
-    // sequences only: [B*H][ceil(T/b)][M | S][d][d], float32 on the float32
-    // path and fp16 on the fp16-operand path (the precision every later use
-    // rounds them to).
+    // Chunk-start states for the backward pass (NULL: not written):
+    // [B*H][ceil(T/b)][M | S][d][d] for dense sequences; for packed documents
+    // [H][tcmax][M | S][d][d], document s of head h from slot h * tcmax + (the
+    // chunks of documents 0..s-1).  float32 on the float32 path and fp16 on
+    // the fp16-operand path (the precision every later use rounds them to).
     void* ckpt;
     // Gates shared by the tokens of a chunk (dense sequences only): theta,
     // eta, alpha are [B*H][ceil(T/b)] and every token of chunk c uses entry c.
     int chunk_gates;
+    int tcmax;   // packed documents: chunk slots per head
 };
 
 // Compile-time geometry of one kernel instance: NS 16-row tiles per
@@ -1196,6 +1198,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
     int bh = lin / Gm::NRB;
     int rb = lin % Gm::NRB;
     int seqlen = p.T;
+    size_t ck_chunk0 = 0;   // checkpoint slot of the sequence's chunk 0
     size_t seq_tok = static_cast<size_t>(bh) * p.T;
     if (p.cu) {
         // Packed documents: units u = (rank, head) in rank order, dealt
@@ -1209,6 +1212,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
         }
         const int s = doc_of_rank(p.cu, p.BH / p.H, p.T, u / p.H, lane), h = u % p.H;
         bh = s * p.H + h;
+        if (p.ckpt) ck_chunk0 = static_cast<size_t>(h) * p.tcmax + doc_chunk_prefix(p.cu, s, p.T, p.b);
         // Offsets clamped into [0, T]: a malformed table cannot send any
         // access outside the packed arrays.
         const int t0 = min(max(p.cu[s], 0), p.T);
@@ -1219,6 +1223,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
     const int row_wg = rb * RB;
     const int nch = (seqlen + b - 1) / b;
     auto chunk_n = [&](int c) { return min(b, seqlen - c * b); };
+    if (!p.cu) ck_chunk0 = static_cast<size_t>(bh) * nch;
 
     // Zero all staging memory once: padded rows and columns stay 0.
     {
@@ -1251,7 +1256,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
         // differentiates from), in the layout of M_T / S_T.
         auto save = [&](int c) {
             if (p.ckpt) {
-                T* base = static_cast<T*>(p.ckpt) + (static_cast<size_t>(bh) * nch + c) * (2 * D * D) +
+                T* base = static_cast<T*>(p.ckpt) + (ck_chunk0 + c) * (2 * D * D) +
                           static_cast<size_t>(row + lr) * D;
 #pragma unroll
                 for (int cw = 0; cw < Gm::NCW; ++cw) {
@@ -1464,7 +1469,7 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
     }
 
     Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, nullptr, H, ckpt,
-             chunk_gates ? 1 : 0};
+             chunk_gates ? 1 : 0, 0};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1474,7 +1479,7 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
 template <typename T>
 int forward_varlen_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
                         const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
-                        const int* cu, int N, int H, int Tlen, int d, int b, void* stream) {
+                        const int* cu, int N, int H, int Tlen, int d, int b, void* stream, void* ckpt = nullptr) {
     using G = typename GlobalOf<T>::type;
     if (N < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
     if (b < 1) return TTT_ERR_INVALID_ARG;
@@ -1514,8 +1519,21 @@ int forward_varlen_impl(const void* q, const void* k, const void* v, const float
         return TTT_ERR_INVALID_ARG;
     if (M_T && S_T && overlaps(M_T, st_bytes, S_T, st_bytes)) return TTT_ERR_INVALID_ARG;
     if (overlaps(M_T, st_bytes, cu, cu_bytes) || overlaps(S_T, st_bytes, cu, cu_bytes)) return TTT_ERR_INVALID_ARG;
+    const long long tcmax = varlen_chunk_slots(N, Tlen, b);
+    if (ckpt) {
+        // [H][tcmax][M | S][d][d]; the gradient pass launches H * tcmax workgroups.
+        if (static_cast<long long>(H) * tcmax > 0x7fffffffLL) return TTT_ERR_UNSUPPORTED;
+        if (!aligned(ckpt, 16)) return TTT_ERR_INVALID_ARG;
+        const size_t ck_bytes = ckpt_bytes_varlen(N, H, Tlen, d, b, sizeof(T));
+        const Span others[] = {{q, in_bytes}, {k, in_bytes}, {v, in_bytes}, {theta, tok * 4}, {eta, tok * 4},
+                               {alpha, tok * 4}, {M0, st_bytes}, {S0, st_bytes}, {z, z_bytes}, {M_T, st_bytes},
+                               {S_T, st_bytes}, {cu, cu_bytes}};
+        for (const Span& o : others)
+            if (o.p && overlaps(ckpt, ck_bytes, o.p, o.n)) return TTT_ERR_INVALID_ARG;
+    }
 
-    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H, nullptr, 0};
+    Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H, ckpt, 0,
+             static_cast<int>(tcmax)};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1567,6 +1585,30 @@ int ttt_mem_forward_ckpt_bf16(const uint16_t* q, const uint16_t* k, const uint16
 }
 
 size_t ttt_mem_ckpt_bytes(int B, int H, int T, int d, int b) { return ckpt_bytes(B, H, T, d, b, 4); }
+
+size_t ttt_mem_ckpt_bytes_varlen(int N, int H, int T, int d, int b) { return ckpt_bytes_varlen(N, H, T, d, b, 4); }
+
+size_t ttt_mem_ckpt_bytes_varlen_bf16(int N, int H, int T, int d, int b) {
+    return ckpt_bytes_varlen(N, H, T, d, b, 2);
+}
+
+int ttt_mem_forward_varlen_ckpt_f32(const float* q, const float* k, const float* v, const float* theta,
+                                    const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
+                                    float* M_T, float* S_T, float* ckpt, const int* cu_seqlens, int N, int H, int T,
+                                    int d, int b, void* stream) {
+    if (!ckpt) return TTT_ERR_INVALID_ARG;
+    return forward_varlen_impl<float>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, cu_seqlens, N, H, T, d, b,
+                                      stream, ckpt);
+}
+
+int ttt_mem_forward_varlen_ckpt_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                                     const float* eta, const float* alpha, const float* M0, const float* S0,
+                                     float* z, float* M_T, float* S_T, uint16_t* ckpt, const int* cu_seqlens, int N,
+                                     int H, int T, int d, int b, void* stream) {
+    if (!ckpt) return TTT_ERR_INVALID_ARG;
+    return forward_varlen_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, cu_seqlens, N, H, T, d,
+                                         b, stream, ckpt);
+}
 
 size_t ttt_mem_ckpt_bytes_bf16(int B, int H, int T, int d, int b) { return ckpt_bytes(B, H, T, d, b, 2); }
 

@@ -279,6 +279,13 @@ struct CarryParams {
     int b;
     int nch;
     int chunk_gates;    // gates [BH][nch] shared by the tokens of a chunk
+    // Packed documents (NULL: dense): sequence bh is document bh / H of head
+    // bh % H at tokens cu[s] .. cu[s+1]-1 of the head's [T] rows; the work
+    // buffer is [H][tcmax][dM | dS][D][D] with the document's chunks from slot
+    // h * tcmax + (the chunks of documents 0..s-1).
+    const int* cu;
+    int H;
+    int tcmax;
 };
 
 template <typename T, int D, int NS, int NP>
@@ -524,10 +531,20 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
     const int bh = lin / Gm::NRB;
     const int rb = lin % Gm::NRB;
     const int row_wg = rb * Gm::RB;
-    const int nch = p.nch;
-    const size_t seq_tok = static_cast<size_t>(bh) * p.T;
+    int nch = p.nch, seqlen = p.T;
+    size_t seq_tok = static_cast<size_t>(bh) * p.T;
+    size_t w_chunk0 = static_cast<size_t>(bh) * p.nch;   // work-buffer slot of chunk 0
+    if (p.cu) {
+        // Packed documents: sequence bh = document s of head h (state slot s * H + h).
+        const int s = bh / p.H, h = bh % p.H;
+        int t0;
+        seqlen = doc_len(p.cu, s, p.T, t0);
+        seq_tok = static_cast<size_t>(h) * p.T + t0;
+        nch = (seqlen + p.b - 1) / p.b;
+        w_chunk0 = static_cast<size_t>(h) * p.tcmax + doc_chunk_prefix(p.cu, s, p.T, p.b);
+    }
     auto chunk_of = [&](int u) { return nch - 1 - u; };
-    auto chunk_n = [&](int c) { return min(p.b, p.T - c * p.b); };
+    auto chunk_n = [&](int c) { return min(p.b, seqlen - c * p.b); };
     // Gate entry of token 0 of chunk c, and the step between tokens.
     const int gstride = p.chunk_gates ? 0 : 1;
     auto gate0 = [&](int c) {
@@ -585,7 +602,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         const typename C::Sm::PSlot& ps = sm.ps[u % Gm::NPR];
         // Cotangent of the state leaving chunk c.
         {
-            T* base = static_cast<T*>(p.work) + (static_cast<size_t>(bh) * nch + c) * (2 * D * D) +
+            T* base = static_cast<T*>(p.work) + (w_chunk0 + c) * (2 * D * D) +
                       static_cast<size_t>(r0 + lr) * D;
 #pragma unroll
             for (int jt = 0; jt < NCT; ++jt) {
@@ -737,6 +754,11 @@ struct GradParams {
     int b;
     int nch;
     int chunk_gates;     // gates and their gradients [BH][nch]
+    // Packed documents (NULL: dense): workgroup = (head h, chunk slot) of
+    // the [H][tcmax] checkpoint and work layouts.
+    const int* cu;
+    int H;
+    int tcmax;
 };
 
 template <typename T, int D, int NP>
@@ -815,13 +837,42 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
     const int w = tid / kW;
     const int lane = tid % kW;
     const int lr = lane & 15, lg = lane >> 4;
-    const int bh = blockIdx.x / p.nch;
-    const int c = blockIdx.x % p.nch;
-    const int n = min(p.b, p.T - c * p.b);
-    const size_t tok0 = static_cast<size_t>(bh) * p.T + static_cast<size_t>(c) * p.b;
-    const T* Mc = static_cast<const T*>(p.ckpt) + (static_cast<size_t>(bh) * p.nch + c) * (2 * D * D);
+    int bh, c, n;
+    size_t tok0, slot;
+    if (p.cu) {
+        // Packed documents: workgroup = (head h, chunk slot); the slots past
+        // the head's last chunk have no work (the whole workgroup leaves).
+        const int h = blockIdx.x / p.tcmax, cidx = blockIdx.x % p.tcmax;
+        const int ndoc = p.BH / p.H;
+        int s = -1, acc = 0, t0 = 0, len = 0;
+        for (int j = 0; j < ndoc; ++j) {
+            int tj;
+            const int lj = doc_len(p.cu, j, p.T, tj);
+            const int nj = (lj + p.b - 1) / p.b;
+            if (cidx < acc + nj) {
+                s = j;
+                t0 = tj;
+                len = lj;
+                break;
+            }
+            acc += nj;
+        }
+        if (s < 0) return;
+        c = cidx - acc;
+        bh = s * p.H + h;
+        n = min(p.b, len - c * p.b);
+        tok0 = static_cast<size_t>(h) * p.T + t0 + static_cast<size_t>(c) * p.b;
+        slot = static_cast<size_t>(h) * p.tcmax + cidx;
+    } else {
+        bh = blockIdx.x / p.nch;
+        c = blockIdx.x % p.nch;
+        n = min(p.b, p.T - c * p.b);
+        tok0 = static_cast<size_t>(bh) * p.T + static_cast<size_t>(c) * p.b;
+        slot = static_cast<size_t>(bh) * p.nch + c;
+    }
+    const T* Mc = static_cast<const T*>(p.ckpt) + slot * (2 * D * D);
     const T* Sc = Mc + D * D;
-    const T* dMe = static_cast<const T*>(p.work) + (static_cast<size_t>(bh) * p.nch + c) * (2 * D * D);
+    const T* dMe = static_cast<const T*>(p.work) + slot * (2 * D * D);
     const T* dSe = dMe + D * D;
 
     // ---- stage q, k (and dz, -dv), raw gates; clear the accumulators ----
@@ -1394,7 +1445,7 @@ hipError_t launch_carry(const CarryParams& cp, hipStream_t s) {
 template <typename T, int D, int NP>
 hipError_t launch_grads(const GradParams& gp, hipStream_t s) {
     using Gm = GradGeo<T, D, NP>;
-    const long long nwg = static_cast<long long>(gp.BH) * gp.nch;
+    const long long nwg = gp.cu ? static_cast<long long>(gp.H) * gp.tcmax : static_cast<long long>(gp.BH) * gp.nch;
     if (nwg == 0) return hipSuccess;
     hipLaunchKernelGGL((linear_memory_bwd_grads<T, D, NP>), dim3(static_cast<unsigned>(nwg)),
                        dim3(kW * Gm::NWAVE), 0, s, gp);
@@ -1420,31 +1471,38 @@ hipError_t launch_bwd_np(const CarryParams& cp, const GradParams& gp, int b, hip
     }
 }
 
-struct Span {
-    const void* p;
-    size_t n;
-};
 
 template <typename T>
 int backward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
                   const float* alpha, const void* ckpt, const float* dz, const float* dMT, const float* dST,
                   float* dq, float* dk, float* dv, float* dth, float* deta, float* dal, float* dM0, float* dS0,
-                  void* work, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false) {
+                  void* work, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false,
+                  const int* cu = nullptr) {
+    // Dense: B sequences of T tokens per head.  Packed documents (cu set): B
+    // is the document count N, the token arrays are [H, T] and the states
+    // [N, H, d, d] (see the forward's packed-document entry points).
     using G = typename GlobalOf<T>::type;
     if (B < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
     if (b < 1) return TTT_ERR_INVALID_ARG;
     if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
     if (b > 64) return TTT_ERR_UNSUPPORTED;
+    const bool packed = cu != nullptr;
+    if (packed && chunk_gates) return TTT_ERR_UNSUPPORTED;
     const long long BH = static_cast<long long>(B) * H;
     if (BH == 0) return TTT_OK;
     const long long nch = (static_cast<long long>(Tlen) + b - 1) / b;
-    if (BH * static_cast<long long>(Tlen) > 0x7fffffffLL || BH * nch > 0x7fffffffLL || BH * (d / 16) > 0x7fffffffLL)
+    const long long tcmax = packed ? varlen_chunk_slots(B, Tlen, b) : 0;
+    const long long seqs = packed ? H : BH;   // rows of Tlen tokens
+    if (seqs * static_cast<long long>(Tlen) > 0x7fffffffLL || BH * nch > 0x7fffffffLL ||
+        BH * (d / 16) > 0x7fffffffLL || static_cast<long long>(H) * tcmax > 0x7fffffffLL)
         return TTT_ERR_UNSUPPORTED;
-    const size_t tok = static_cast<size_t>(BH) * static_cast<size_t>(Tlen);
+    if (packed && !aligned(cu, 4)) return TTT_ERR_INVALID_ARG;
+    const size_t tok = static_cast<size_t>(seqs) * static_cast<size_t>(Tlen);
     const size_t in_b = tok * d * sizeof(G), f_b = tok * d * 4;
     const size_t g_b = (chunk_gates ? static_cast<size_t>(BH) * static_cast<size_t>(nch) : tok) * 4;
     const size_t st_b = static_cast<size_t>(BH) * d * d * 4;
-    const size_t ck_b = ckpt_bytes(B, H, Tlen, d, b, sizeof(T));
+    const size_t ck_b = packed ? ckpt_bytes_varlen(B, H, Tlen, d, b, sizeof(T)) : ckpt_bytes(B, H, Tlen, d, b, sizeof(T));
+    const size_t cu_b = packed ? (static_cast<size_t>(B) + 1) * sizeof(int) : 0;
     if (Tlen > 0) {
         const void* req[] = {q, k, v, theta, eta, alpha, ckpt, dz, dq, dk, dv, dth, deta, dal, work};
         for (const void* r : req)
@@ -1461,7 +1519,7 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
         if (r && !aligned(r, 16)) return TTT_ERR_INVALID_ARG;
     // No output may overlap any input or another output.
     const Span ins[] = {{q, in_b}, {k, in_b}, {v, in_b}, {theta, g_b}, {eta, g_b}, {alpha, g_b},
-                        {ckpt, ck_b}, {dz, f_b}, {dMT, st_b}, {dST, st_b}};
+                        {ckpt, ck_b}, {dz, f_b}, {dMT, st_b}, {dST, st_b}, {cu, cu_b}};
     const Span outs[] = {{dq, f_b}, {dk, f_b}, {dv, f_b}, {dth, g_b}, {deta, g_b}, {dal, g_b},
                          {dM0, st_b}, {dS0, st_b}, {work, ck_b}};
     const int n_outs = static_cast<int>(sizeof(outs) / sizeof(outs[0]));
@@ -1475,9 +1533,9 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
 
     const int cg = chunk_gates ? 1 : 0;
     const CarryParams cp{q, k, dz, theta, eta, alpha, dMT, dST, work, dv, dM0, dS0,
-                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg};
+                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax)};
     const GradParams gp{q, k, v, theta, eta, alpha, ckpt, work, dz, dv, dq, dk, dth, deta, dal,
-                        static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg};
+                        static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax)};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (d) {
@@ -1527,6 +1585,26 @@ int ttt_mem_backward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_
                              int d, int b, void* stream) {
     return backward_impl<_Float16>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta,
                                    dalpha, dM0, dS0, work, B, H, T, d, b, stream, true);
+}
+
+int ttt_mem_backward_varlen_f32(const float* q, const float* k, const float* v, const float* theta,
+                                const float* eta, const float* alpha, const float* ckpt, const float* dz,
+                                const float* dM_T, const float* dS_T, float* dq, float* dk, float* dv, float* dtheta,
+                                float* deta, float* dalpha, float* dM0, float* dS0, float* work,
+                                const int* cu_seqlens, int N, int H, int T, int d, int b, void* stream) {
+    if (!cu_seqlens) return TTT_ERR_INVALID_ARG;
+    return backward_impl<float>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta, dalpha,
+                                dM0, dS0, work, N, H, T, d, b, stream, false, cu_seqlens);
+}
+
+int ttt_mem_backward_varlen_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                                 const float* eta, const float* alpha, const uint16_t* ckpt, const float* dz,
+                                 const float* dM_T, const float* dS_T, float* dq, float* dk, float* dv,
+                                 float* dtheta, float* deta, float* dalpha, float* dM0, float* dS0, uint16_t* work,
+                                 const int* cu_seqlens, int N, int H, int T, int d, int b, void* stream) {
+    if (!cu_seqlens) return TTT_ERR_INVALID_ARG;
+    return backward_impl<_Float16>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta,
+                                   dalpha, dM0, dS0, work, N, H, T, d, b, stream, false, cu_seqlens);
 }
 
 }  // extern "C"

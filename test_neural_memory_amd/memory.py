@@ -262,12 +262,26 @@ def linear_memory(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b):
     return LinearMemoryFunction.apply(q, k, v, theta, eta, alpha, M0, S0, b)
 
 
-def forward_varlen(q, k, v, theta, eta, alpha, cu_seqlens, M0=None, S0=None, *, b, out=None):
+def varlen_slots(N, T, b):
+    """Chunk slots per head of the packed-document checkpoints: ceil(T/b) + N."""
+    return _nch(T, int(b)) + N
+
+
+def new_ckpt_varlen(q, cu_seqlens, b):
+    """An uninitialised checkpoint tensor ``[H, slots, 2, d, d]`` for packed documents."""
+    H, T, d = q.shape
+    N = cu_seqlens.numel() - 1
+    return torch.empty((H, varlen_slots(N, T, b), 2, d, d), dtype=ckpt_dtype(q.dtype), device=q.device)
+
+
+def forward_varlen(q, k, v, theta, eta, alpha, cu_seqlens, M0=None, S0=None, *, b, out=None, ckpt=None):
     """Linear memory over packed variable-length documents; returns ``(z, M_T, S_T)``.
 
     ``q, k, v`` are ``[H, T, d]`` (float32 or bfloat16), the gates ``[H, T]``,
     ``cu_seqlens`` an int32 device tensor ``[N + 1]`` of document offsets, and
-    the states ``[N, H, d, d]``: each document starts from its own state.
+    the states ``[N, H, d, d]``: each document starts from its own state.  With
+    ``ckpt`` (``new_ckpt_varlen``), the chunk-start states of every document are
+    kept for ``backward_varlen`` and ``(z, M_T, S_T, ckpt)`` is returned.
     """
     if q.dim() != 3:
         raise ValueError("q must be [H, T, d]")
@@ -275,10 +289,11 @@ def forward_varlen(q, k, v, theta, eta, alpha, cu_seqlens, M0=None, S0=None, *, 
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("inputs must be HIP device tensors (torch 'cuda' device)")
+    tail = "_ckpt" if ckpt is not None else ""
     if q.dtype == torch.float32:
-        name = "ttt_mem_forward_varlen_f32"
+        name = f"ttt_mem_forward_varlen{tail}_f32"
     elif q.dtype == torch.bfloat16:
-        name = "ttt_mem_forward_varlen_bf16"
+        name = f"ttt_mem_forward_varlen{tail}_bf16"
     else:
         raise TypeError(f"unsupported input dtype {q.dtype}")
     if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
@@ -302,14 +317,77 @@ def forward_varlen(q, k, v, theta, eta, alpha, cu_seqlens, M0=None, S0=None, *, 
                                   or tuple(t.shape) != shp or t.device != dev):
                 raise ValueError(f"out tensor {nm} must be contiguous float32 {shp} on {dev}")
     z, M_T, S_T = out
+    extra = []
+    if ckpt is not None:
+        ckpt = _as_dev(ckpt, "ckpt", ckpt_dtype(q.dtype), (H, varlen_slots(N, T, b), 2, d, d), dev)
+        extra = [_ptr(ckpt)]
     lib = _lib.load()
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         status = getattr(lib, name)(
             _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(M0), _ptr(S0),
-            _ptr(z), _ptr(M_T), _ptr(S_T), _ptr(cu), N, H, T, d, int(b), stream)
+            _ptr(z), _ptr(M_T), _ptr(S_T), *extra, _ptr(cu), N, H, T, d, int(b), stream)
     _lib.check(name, status)
-    return z, M_T, S_T
+    return (z, M_T, S_T) if ckpt is None else (z, M_T, S_T, ckpt)
+
+
+def backward_varlen(q, k, v, theta, eta, alpha, cu_seqlens, ckpt, dz, dM_T=None, dS_T=None, *, b, work=None,
+                    out=None):
+    """Gradients over packed documents from ``forward_varlen(..., ckpt=...)``.
+
+    ``dz [H, T, d]``, ``dM_T, dS_T [N, H, d, d]`` (float32; None = zero).
+    Returns ``(dq, dk, dv, dtheta, deta, dalpha, dM0, dS0)``, float32, with
+    ``dq, dk, dv [H, T, d]``, the gate gradients ``[H, T]`` and ``dM0, dS0
+    [N, H, d, d]``.  Tokens outside every document are not written.
+    """
+    if q.dim() != 3:
+        raise ValueError("q must be [H, T, d]")
+    H, T, d = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be HIP device tensors (torch 'cuda' device)")
+    if q.dtype == torch.float32:
+        name = "ttt_mem_backward_varlen_f32"
+    elif q.dtype == torch.bfloat16:
+        name = "ttt_mem_backward_varlen_bf16"
+    else:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    b = int(b)
+    in_dtype = q.dtype
+    cu = _as_dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    q = _as_dev(q, "q", in_dtype, (H, T, d), dev)
+    k = _as_dev(k, "k", in_dtype, (H, T, d), dev)
+    v = _as_dev(v, "v", in_dtype, (H, T, d), dev)
+    theta = _as_dev(theta, "theta", torch.float32, (H, T), dev)
+    eta = _as_dev(eta, "eta", torch.float32, (H, T), dev)
+    alpha = _as_dev(alpha, "alpha", torch.float32, (H, T), dev)
+    ck_shape = (H, varlen_slots(N, T, b), 2, d, d)
+    cdt = ckpt_dtype(in_dtype)
+    ckpt = _as_dev(ckpt, "ckpt", cdt, ck_shape, dev)
+    dz = _as_dev(dz, "dz", torch.float32, (H, T, d), dev)
+    dM_T = _as_dev(dM_T, "dM_T", torch.float32, (N, H, d, d), dev)
+    dS_T = _as_dev(dS_T, "dS_T", torch.float32, (N, H, d, d), dev)
+    work = torch.empty(ck_shape, dtype=cdt, device=dev) if work is None else _as_dev(work, "work", cdt, ck_shape, dev)
+    shapes = [(H, T, d)] * 3 + [(H, T)] * 3 + [(N, H, d, d)] * 2
+    if out is None:
+        out = [torch.empty(s_, dtype=torch.float32, device=dev) for s_ in shapes]
+    else:
+        out = list(out)
+        for i, (t, shp) in enumerate(zip(out, shapes)):
+            if t is not None and (not t.is_contiguous() or t.dtype != torch.float32
+                                  or tuple(t.shape) != shp or t.device != dev):
+                raise ValueError(f"out tensor {i} must be contiguous float32 {shp} on {dev}")
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        status = getattr(lib, name)(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(ckpt), _ptr(dz),
+            _ptr(dM_T), _ptr(dS_T), *[_ptr(t) for t in out], _ptr(work), _ptr(cu), N, H, T, d, b, stream)
+    _lib.check(name, status)
+    return tuple(out)
 
 
 def ttt_mem_decode_f32(q, k, v, theta, eta, alpha, M0=None, S0=None, *, out=None):

@@ -21,7 +21,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ttt_mem_abi_version() == (1 << 16) | 3
+    assert lib.ttt_mem_abi_version() == (1 << 16) | 4
     assert lib.ttt_mem_status_string(0) == b"ok"
     for s in (-1, -2, -3, 12345):
         assert lib.ttt_mem_status_string(s)
@@ -79,3 +79,22 @@ def test_backward_rejections_happen_before_any_launch(lib, name):
     assert call(b=65) == -2
     assert call(T=-1) == -1
     assert call(B=0) == 0                    # nothing to do: no pointer is touched
+
+
+def test_ckpt_bytes_varlen(lib):
+    # [H, ceil(T/b) + N, M | S, d, d]: every document adds at most one partial chunk.
+    assert lib.ttt_mem_ckpt_bytes_varlen(3, 2, 100, 16, 8) == 2 * (13 + 3) * 2 * 16 * 16 * 4
+    assert lib.ttt_mem_ckpt_bytes_varlen_bf16(3, 2, 100, 16, 8) == 2 * (13 + 3) * 2 * 16 * 16 * 2
+    assert lib.ttt_mem_ckpt_bytes_varlen(-1, 2, 100, 16, 8) == 0
+
+
+@pytest.mark.parametrize("name", ["ttt_mem_forward_varlen_ckpt_f32", "ttt_mem_forward_varlen_ckpt_bf16"])
+def test_varlen_training_forward_requires_ckpt(lib, name):
+    # q k v theta eta alpha M0 S0 z M_T S_T ckpt cu; N H T d b; stream
+    assert getattr(lib, name)(*([None] * 13), 2, 1, 8, 16, 4, None) == -1
+
+
+@pytest.mark.parametrize("name", ["ttt_mem_backward_varlen_f32", "ttt_mem_backward_varlen_bf16"])
+def test_varlen_backward_requires_offsets(lib, name):
+    # 19 arrays, then cu_seqlens (NULL); N H T d b; stream
+    assert getattr(lib, name)(*([None] * 20), 2, 1, 8, 16, 4, None) == -1

@@ -1,0 +1,154 @@
+"""GPU parity of training over packed variable-length documents.
+
+Every document is its own sequence with its own initial state, so the oracle
+is ``linear_backward`` run on each (document, head) separately.  Bounds as for
+the dense backward: max|gpu - oracle| / rms(oracle) <= 1e-4 (float32) and
+<= 2e-2 (bf16 inputs), per gradient over all documents.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import linear_backward
+from tests._parity import TOL, rel_err
+from test_neural_memory_amd import memory as tm
+from test_neural_memory_amd._lib import TTTError
+from test_neural_memory_amd.workloads import WORKLOADS, make_inputs, to_numpy64
+
+pytestmark = pytest.mark.gpu
+NAMES = ("dq", "dk", "dv", "dtheta", "deta", "dalpha", "dM0", "dS0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _packed(wid, H, lengths, dtype, d=None, tail=0, seed=41):
+    """Packed inputs [H, T, d], gates [H, T], per-document states and cotangents."""
+    T = int(sum(lengths)) + tail
+    kw = dict(B=1, H=H, T=max(T, 1), dtype=dtype)
+    if d is not None:
+        kw["d"] = d
+    w = WORKLOADS[wid].replace(**kw)
+    inp = make_inputs(w)
+    g = {k: inp[k][0, :, :T].contiguous() for k in ("q", "k", "v", "theta", "eta", "alpha")}
+    N = len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    g["M0"] = torch.from_numpy((rng.standard_normal((N, H, w.d, w.d)) * 0.05).astype(np.float32))
+    g["S0"] = torch.from_numpy((rng.standard_normal((N, H, w.d, w.d)) * 0.005).astype(np.float32))
+    cot = {"dz": torch.from_numpy(rng.standard_normal((H, T, w.d)).astype(np.float32)),
+           "dM_T": torch.from_numpy((rng.standard_normal((N, H, w.d, w.d)) * 0.1).astype(np.float32)),
+           "dS_T": torch.from_numpy((rng.standard_normal((N, H, w.d, w.d)) * 0.1).astype(np.float32))}
+    return w, g, cot, torch.from_numpy(cu)
+
+
+def _gpu(g, cot, cu, b, out=None):
+    dev = {k: v.cuda() for k, v in g.items()}
+    cd = {k: v.cuda() for k, v in cot.items()}
+    cud = cu.cuda()
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    ckpt = tm.new_ckpt_varlen(dev["q"], cud, b)
+    z, M, S, ckpt = tm.forward_varlen(*args, cud, dev["M0"], dev["S0"], b=b, ckpt=ckpt)
+    grads = tm.backward_varlen(*args, cud, ckpt, cd["dz"], cd["dM_T"], cd["dS_T"], b=b, out=out)
+    torch.cuda.synchronize()
+    return grads
+
+
+def _check(g, cot, cu, b, tol):
+    grads = [to_numpy64(x.cpu()) for x in _gpu(g, cot, cu, b)]
+    n = {k: to_numpy64(v) for k, v in g.items()}
+    c = {k: to_numpy64(v) for k, v in cot.items()}
+    H = n["q"].shape[0]
+    gpu_parts = [[] for _ in NAMES]
+    ref_parts = [[] for _ in NAMES]
+    for s in range(len(cu) - 1):
+        t0, t1 = int(cu[s]), int(cu[s + 1])
+        for h in range(H):
+            sl = (h, slice(t0, t1))
+            ref = linear_backward(n["q"][sl], n["k"][sl], n["v"][sl], n["theta"][sl], n["eta"][sl],
+                                  n["alpha"][sl], c["dz"][sl], c["dM_T"][s, h], c["dS_T"][s, h],
+                                  n["M0"][s, h], n["S0"][s, h], b=b)
+            got = [grads[i][sl] for i in range(6)] + [grads[6][s, h], grads[7][s, h]]
+            for i in range(8):
+                gpu_parts[i].append(np.asarray(got[i]).reshape(-1))
+                ref_parts[i].append(np.asarray(ref[i]).reshape(-1))
+    errs = {nm: rel_err(np.concatenate(gp), np.concatenate(rp)) for nm, gp, rp in zip(NAMES, gpu_parts, ref_parts)}
+    _say("  errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" (tol {tol})")
+    assert max(errs.values()) <= tol, errs
+
+
+CASES = [
+    # (label, workload id, H, document lengths, b, d): lengths below, at and above b, empty documents
+    ("titans-mixed", 3, 2, [130, 1, 64, 0, 200, 33], 64, None),
+    ("titans-d64-b16", 3, 2, [50, 16, 7, 100], 16, 64),
+    ("ttt-b16", 2, 2, [31, 90, 16, 3], 16, None),
+    ("tiny-d16", 1, 2, [9, 1, 24, 8], 8, None),
+]
+
+
+@pytest.mark.parametrize("label,wid,H,lengths,b,d", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_backward_parity(label, wid, H, lengths, b, d, dtype):
+    w, g, cot, cu = _packed(wid, H, lengths, dtype, d=d)
+    _say(f"case {label} {dtype} H={H} lengths={lengths} b={b} d={w.d}")
+    _check(g, cot, cu, b, TOL[dtype])
+
+
+def test_varlen_backward_equals_dense_bitwise():
+    # N equal-length documents packed == the dense training step with B = N, bit for bit.
+    w = WORKLOADS[3].replace(B=3, H=2, T=150)
+    inp = make_inputs(w)
+    rng = np.random.default_rng(7)
+    dense = {k: v.cuda() for k, v in inp.items() if v is not None}
+    dz = torch.from_numpy(rng.standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)).cuda()
+    dMT = torch.from_numpy((rng.standard_normal((w.B, w.H, w.d, w.d)) * 0.1).astype(np.float32)).cuda()
+    dST = torch.from_numpy((rng.standard_normal((w.B, w.H, w.d, w.d)) * 0.1).astype(np.float32)).cuda()
+    args = (dense["q"], dense["k"], dense["v"], dense["theta"], dense["eta"], dense["alpha"])
+    _, _, _, ckpt = tm.forward_train(*args, b=64)
+    gd = tm.backward(*args, ckpt, dz, dMT, dST, b=64)
+    pack = {k: v.transpose(0, 1).reshape(w.H, w.B * w.T, *v.shape[3:]).contiguous() for k, v in dense.items()}
+    dzp = dz.transpose(0, 1).reshape(w.H, w.B * w.T, w.d).contiguous()
+    cu = torch.arange(0, (w.B + 1) * w.T, w.T, dtype=torch.int32, device="cuda")
+    pargs = (pack["q"], pack["k"], pack["v"], pack["theta"], pack["eta"], pack["alpha"])
+    ckp = tm.new_ckpt_varlen(pack["q"], cu, 64)
+    tm.forward_varlen(*pargs, cu, b=64, ckpt=ckp)
+    gp = tm.backward_varlen(*pargs, cu, ckp, dzp, dMT, dST, b=64)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.equal(gp[i].reshape(w.H, w.B, w.T, w.d).transpose(0, 1), gd[i]), NAMES[i]
+    for i in range(3, 6):
+        assert torch.equal(gp[i].reshape(w.H, w.B, w.T).transpose(0, 1), gd[i]), NAMES[i]
+    assert torch.equal(gp[6], gd[6]) and torch.equal(gp[7], gd[7])
+
+
+def test_varlen_backward_unused_tail_and_empty_docs():
+    # Gradients of tokens outside every document are not written; an empty
+    # document passes its state cotangents straight through.
+    w, g, cot, cu = _packed(3, 2, [0, 40, 0], "f32", tail=9)
+    H, T, d = g["q"].shape
+    out = [torch.full((H, T, d), float("nan"), device="cuda") for _ in range(3)] + \
+          [torch.full((H, T), float("nan"), device="cuda") for _ in range(3)] + \
+          [torch.empty(3, H, d, d, device="cuda") for _ in range(2)]
+    _gpu(g, cot, cu, 64, out=out)
+    for t in out[:3]:
+        assert torch.isnan(t[:, 40:]).all() and not torch.isnan(t[:, :40]).any()
+    for t in out[3:6]:
+        assert torch.isnan(t[:, 40:]).all() and not torch.isnan(t[:, :40]).any()
+    for s in (0, 2):
+        assert torch.equal(out[6][s].cpu(), cot["dM_T"][s])
+        assert torch.equal(out[7][s].cpu(), cot["dS_T"][s])
+    _check(g, cot, cu, 64, TOL["f32"])
+
+
+def test_varlen_backward_argument_errors():
+    w, g, cot, cu = _packed(3, 1, [10, 6], "f32")
+    dev = {k: v.cuda() for k, v in g.items()}
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    ck = tm.new_ckpt_varlen(dev["q"], cu, 16)
+    with pytest.raises(ValueError):   # wrong checkpoint shape
+        tm.backward_varlen(*args, cu.cuda(), ck[:, :1], cot["dz"].cuda(), b=16)
+    with pytest.raises(TTTError) as e:
+        tm.backward_varlen(*args, cu.cuda(), tm.new_ckpt_varlen(dev["q"], cu, 65), cot["dz"].cuda(), b=65)
+    assert e.value.status == -2
