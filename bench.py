@@ -10,7 +10,8 @@ instead: a step is one call of the primal form for one token of every
 (batch, head) sequence (B=4 H=16 d=128), with the state carried in place from
 step to step.  ``--varlen`` times packed variable-length documents with the
 Titans recipe (32768 tokens per head in documents of seeded lengths, each
-from its own state).  ``--backward`` times one training step of the Titans
+from its own state); with ``--backward`` as well, one training step over
+those documents.  ``--backward`` times one training step of the Titans
 linear memory: the forward that saves the chunk-start states plus the
 backward pass (gradients for q, k, v, the three gates and the initial state),
 with a seeded synthetic outer-loss derivative dz.  ``--chunk-gates`` times
@@ -19,7 +20,7 @@ alpha per 64-token chunk, drawn from the same distributions).  Prints ONE
 JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload {2,3,4,5} | --decode | --varlen | --backward | --chunk-gates]
+                    [--workload {2,3,4,5} | --decode | --varlen [--backward] | --backward | --chunk-gates]
                     [--no-cpu-baseline]
 """
 
@@ -511,6 +512,133 @@ def varlen_main(args):
     print(json.dumps(result), flush=True)
 
 
+def varlen_train_main(args):
+    """One training step over packed documents with the Titans recipe (the
+    ``--varlen`` workload): the forward that keeps every document's chunk-start
+    states, then the backward pass over the same documents."""
+    wv = WORKLOADS[3].replace(B=1, T=4 * 8192)
+    lengths = varlen_lengths(wv.T)
+    N, H, T, d, b = len(lengths), wv.H, wv.T, wv.d, wv.b
+    log(f"varlen training workload: {N} documents, lengths min {min(lengths)} median {int(np.median(lengths))} "
+        f"max {max(lengths)}, {T} tokens per head, H={H} d={d} b={b}")
+    inp = make_inputs(wv)
+    dev = {k: v[0].cuda() for k, v in inp.items() if v is not None}
+    dz_h = make_cotangents(wv, states=False)["dz"][0]
+    dz = dz_h.cuda()
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    args_ = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    z = torch.empty(H, T, d, dtype=torch.float32, device="cuda")
+    MT = torch.empty(N, H, d, d, dtype=torch.float32, device="cuda")
+    ST = torch.empty_like(MT)
+    ckpt = tm.new_ckpt_varlen(dev["q"], cu, b)
+    work = torch.empty_like(ckpt)
+    outs = [torch.empty(H, T, d, dtype=torch.float32, device="cuda") for _ in range(3)] + \
+           [torch.empty(H, T, dtype=torch.float32, device="cuda") for _ in range(3)] + \
+           [torch.empty(N, H, d, d, dtype=torch.float32, device="cuda") for _ in range(2)]
+    fwd = lambda: tm.forward_varlen(*args_, cu, b=b, out=(z, MT, ST), ckpt=ckpt)  # noqa: E731
+    bwd = lambda: tm.backward_varlen(*args_, cu, ckpt, dz, b=b, work=work, out=outs)  # noqa: E731
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        fwd()
+        ev[i][1].record()
+        bwd()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    # Algorithmic bytes of the backward, as for the dense step: inputs and dz
+    # read once, every token gradient written once, dM0 and dS0 per document.
+    per_tok = 3 * d * 2 + 3 * 4 + d * 4 + 3 * d * 4 + 3 * 4
+    nbytes = H * T * per_tok + N * H * d * d * 4 * 2
+    achieved_gbs = nbytes / (bwd_ms * 1e-3) / 1e9
+    log(f"forward with checkpoints {fwd_ms * 1e3:.1f} us, backward {bwd_ms * 1e3:.1f} us; backward algorithmic "
+        f"bytes {nbytes / 1e9:.3f} GB -> {achieved_gbs:.0f} GB/s")
+    # Parity: documents 0 and 1 on heads 0 and H-1, every gradient, against the
+    # oracle's backward of each document from a zero state.
+    from oracle import linear_backward
+    errs = []
+    for h in (0, H - 1):
+        g = {k: to_numpy64(v[0, h]) for k, v in inp.items() if v is not None}
+        dzn = to_numpy64(dz_h[h])
+        for s_ in range(min(2, N)):
+            t0, t1 = int(sum(lengths[:s_])), int(sum(lengths[:s_ + 1]))
+            ref = linear_backward(g["q"][t0:t1], g["k"][t0:t1], g["v"][t0:t1], g["theta"][t0:t1],
+                                  g["eta"][t0:t1], g["alpha"][t0:t1], dzn[t0:t1], None, None, None, None, b=b)
+            got = [x[h, t0:t1] for x in outs[:6]] + [outs[6][s_, h], outs[7][s_, h]]
+            for x, r in zip(got, ref):
+                xg = x.double().cpu().numpy()
+                errs.append(float(np.max(np.abs(xg - r)) / np.sqrt(np.mean(r ** 2))))
+    parity = max(errs)
+    log(f"sampled parity (documents 0-1, heads 0 and {H - 1}, every gradient): max|d|/rms = {parity:.3e}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_varlen_train(inp, dz_h, lengths, H, b)
+        log(f"cpu baseline: {cpu}")
+    result = {
+        "metric": "packed-document training tokens/s (forward + backward) at H=16,d=128,b=64",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "titans-linear-varlen-train", "documents": N, "tokens_per_head": T, "H": H,
+                   "d": d, "b": b, "lengths": "lognormal(sigma 1) around 1024, clipped to [1, 8192], seed 3001",
+                   "inputs": "bf16 q,k,v; f32 gates; f32 dz (seeded N(0,1))", "accumulate": "f32",
+                   "gradients": "f32", "checkpoints": "fp16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
+                   "checkpoint_bytes": ckpt.numel() * ckpt.element_size()},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None, "traffic_unit": "bytes/launch",
+                     "algorithmic_bytes": nbytes, "kernel": "backward pass (carry walk + chunk gradients)"},
+        "cpu_baseline": cpu,
+        "parity_sample_max_rel_err": parity,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_varlen_train(inp, dz, lengths, H, b, docs=8):
+    """Time the float64 oracle (forward, then backward) on the first `docs`
+    documents of every head, in a process pool."""
+    import multiprocessing as mp
+    ncores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    g = {k: to_numpy64(v[0]) for k, v in inp.items() if k in ("q", "k", "v", "theta", "eta", "alpha")}
+    dzn = to_numpy64(dz)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    nd = min(docs, len(lengths))
+    jobs = [([], b) for _ in range(ncores)]
+    for i, (s_, h) in enumerate((s_, h) for s_ in range(nd) for h in range(H)):
+        t0, t1 = cu[s_], cu[s_ + 1]
+        jobs[i % ncores][0].append(tuple(g[x][h, t0:t1] for x in ("q", "k", "v", "theta", "eta", "alpha"))
+                                   + (dzn[h, t0:t1],))
+    jobs = [j for j in jobs if j[0]]
+    ctx = mp.get_context("fork")
+    t0w = time.perf_counter()
+    with ctx.Pool(len(jobs)) as pool:
+        per_job = pool.map(_oracle_train_worker, jobs)
+    wall = time.perf_counter() - t0w
+    tokens = int(cu[nd])
+    return {
+        "value": tokens / wall,   # training tokens/s, each token covering all H heads
+        "unit": "tokens/s",
+        "cores": len(jobs),
+        "kind": "oracle",
+        "sample": f"first {nd} of {len(lengths)} documents ({tokens} tokens) on all {H} heads; float64 per-token "
+                  f"NumPy forward then reverse-mode backward, {len(jobs)} processes x 1 thread; wall {wall:.2f} s, "
+                  f"busiest process {max(per_job):.2f} s; tokens/s = sampled tokens / wall",
+    }
+
+
 def cpu_baseline_varlen(inp, lengths, H, b, docs=12):
     """Time the float64 oracle on the first `docs` documents of every head, in a process pool."""
     import multiprocessing as mp
@@ -624,6 +752,9 @@ def main():
         del src, dst
     if args.decode:
         decode_main(args)
+        return
+    if args.varlen and args.backward:
+        varlen_train_main(args)
         return
     if args.varlen:
         varlen_main(args)

@@ -227,6 +227,34 @@ __device__ __forceinline__ int doc_chunk_prefix(const int* cu, int s, int T, int
     return acc;
 }
 
+// Packed documents: the document of rank r when the N documents are ordered
+// by length, longest first (ties by index, so a permutation); lane is the
+// lane index in a 64-wide wave.  Workgroups
+// dispatched first then take the longest chains (longest processing time
+// first), and the short ones fill in behind them.  Every wave computes it
+// (lanes over candidate documents, the table read with uniform indices);
+// above kLptDocs documents the packing order is kept.
+constexpr int kLptDocs = 128;
+__device__ __forceinline__ int doc_of_rank(const int* cu, int N, int T, int r, int lane) {
+    if (N > kLptDocs) return r;
+    auto len = [&](int i) {
+        const int t0 = min(max(cu[i], 0), T);
+        return min(max(cu[i + 1], t0), T) - t0;
+    };
+    for (int base = 0; base < N; base += 64) {
+        const int i = base + lane;
+        const int li = i < N ? len(i) : -1;
+        int rank = 0;
+        for (int j = 0; j < N; ++j) {
+            const int lj = len(j);
+            rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(i < N && rank == r);
+        if (hit) return base + __ffsll(static_cast<long long>(hit)) - 1;
+    }
+    return r;
+}
+
 }  // namespace
 
 #endif  // TTT_MEM_GFX950_H

@@ -528,21 +528,31 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
     const int nwg = gridDim.x;
     int lin = blockIdx.x;
     if ((p.BH % 8) == 0) lin = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;   // row blocks of a sequence on one XCD
-    const int bh = lin / Gm::NRB;
-    const int rb = lin % Gm::NRB;
-    const int row_wg = rb * Gm::RB;
+    int bh = lin / Gm::NRB;
+    int rb = lin % Gm::NRB;
     int nch = p.nch, seqlen = p.T;
     size_t seq_tok = static_cast<size_t>(bh) * p.T;
     size_t w_chunk0 = static_cast<size_t>(bh) * p.nch;   // work-buffer slot of chunk 0
     if (p.cu) {
-        // Packed documents: sequence bh = document s of head h (state slot s * H + h).
-        const int s = bh / p.H, h = bh % p.H;
+        // Packed documents: units u = (rank, head), documents ranked longest
+        // first and dealt round-robin to the XCDs (the row blocks of a unit on
+        // one XCD), so the longest walks start first; sequence bh = document s
+        // of head h (state slot s * H + h).
+        int u = bh;
+        if ((p.BH % 8) == 0) {
+            const int x = blockIdx.x % 8, m = blockIdx.x / 8;
+            rb = m % Gm::NRB;
+            u = (m / Gm::NRB) * 8 + x;
+        }
+        const int s = doc_of_rank(p.cu, p.BH / p.H, p.T, u / p.H, lane), h = u % p.H;
+        bh = s * p.H + h;
         int t0;
         seqlen = doc_len(p.cu, s, p.T, t0);
         seq_tok = static_cast<size_t>(h) * p.T + t0;
         nch = (seqlen + p.b - 1) / p.b;
         w_chunk0 = static_cast<size_t>(h) * p.tcmax + doc_chunk_prefix(p.cu, s, p.T, p.b);
     }
+    const int row_wg = rb * Gm::RB;
     auto chunk_of = [&](int u) { return nch - 1 - u; };
     auto chunk_n = [&](int c) { return min(p.b, seqlen - c * p.b); };
     // Gate entry of token 0 of chunk c, and the step between tokens.
@@ -842,20 +852,34 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
     if (p.cu) {
         // Packed documents: workgroup = (head h, chunk slot); the slots past
         // the head's last chunk have no work (the whole workgroup leaves).
+        // The slot's document is found by the wave's lanes, 64 documents at a
+        // time: each lane takes one document's chunk count, an inclusive
+        // prefix sum over the lanes gives each document's slot range, and a
+        // ballot picks the one holding the slot (empty documents own none).
         const int h = blockIdx.x / p.tcmax, cidx = blockIdx.x % p.tcmax;
         const int ndoc = p.BH / p.H;
         int s = -1, acc = 0, t0 = 0, len = 0;
-        for (int j = 0; j < ndoc; ++j) {
-            int tj;
-            const int lj = doc_len(p.cu, j, p.T, tj);
+        for (int base = 0, before = 0; base < ndoc; base += kW) {
+            const int j = base + lane;
+            int tj = 0, lj = 0;
+            if (j < ndoc) lj = doc_len(p.cu, j, p.T, tj);
             const int nj = (lj + p.b - 1) / p.b;
-            if (cidx < acc + nj) {
-                s = j;
-                t0 = tj;
-                len = lj;
+            int incl = nj;
+            for (int o = 1; o < kW; o <<= 1) {
+                const int y = __shfl_up(incl, o, kW);
+                incl += lane >= o ? y : 0;
+            }
+            const int first = before + incl - nj;
+            const unsigned long long hit = __ballot(j < ndoc && cidx >= first && cidx < first + nj);
+            if (hit) {
+                const int l = __ffsll(static_cast<long long>(hit)) - 1;
+                s = base + l;
+                acc = __builtin_amdgcn_readfirstlane(__shfl(first, l, kW));
+                t0 = __builtin_amdgcn_readfirstlane(__shfl(tj, l, kW));
+                len = __builtin_amdgcn_readfirstlane(__shfl(lj, l, kW));
                 break;
             }
-            acc += nj;
+            before += __shfl(incl, kW - 1, kW);
         }
         if (s < 0) return;
         c = cidx - acc;
