@@ -108,6 +108,9 @@ def measured_traffic(w, kind="forward"):
     if kind == "decode":
         path = os.path.join(ROOT, "profiles", "linear_memory_decode_titans_d128_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_decode.hip")
+    elif kind == "varlen":
+        path = os.path.join(ROOT, "profiles", "linear_memory_fwd_varlen_titans_d128_traffic.json")
+        src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear.hip")
     elif kind == "backward":
         path = os.path.join(ROOT, "profiles", "linear_memory_train_titans_d128_b64_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear_bwd.hip")
@@ -504,8 +507,8 @@ def varlen_main(args):
                    "b": wv.b, "lengths": "lognormal(sigma 1) around 1024, clipped to [1, 8192], seed 3001",
                    "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "state": "f32", "z": "f32"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None, "traffic_unit": "bytes/launch",
-                     "algorithmic_bytes": nbytes},
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wv, "varlen"),
+                     "traffic_unit": "bytes/launch", "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
         "parity_sample_max_rel_err": parity,
     }
