@@ -78,6 +78,8 @@ CASES = [
     ("titans-d64-b16", 3, 2, [50, 16, 7, 100], 16, 64),
     ("ttt-b16", 2, 2, [31, 90, 16, 3], 16, None),
     ("tiny-d16", 1, 2, [9, 1, 24, 8], 8, None),
+    # 150 documents: above 128 the dispatch keeps the packing order.
+    ("many-docs", 3, 1, [int(x) for x in np.random.default_rng(5).integers(0, 41, 150)], 16, 32),
 ]
 
 
@@ -85,7 +87,7 @@ CASES = [
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_varlen_parity(label, wid, H, lengths, b, d, dtype):
     w, g, cu = _packed(wid, H, lengths, dtype, d=d)
-    _say(f"case {label} {dtype} H={H} lengths={lengths} b={b} d={w.d}")
+    _say(f"case {label} {dtype} H={H} N={len(lengths)} lengths={lengths[:8]} b={b} d={w.d}")
     _check(g, cu, b, TOL[dtype])
 
 

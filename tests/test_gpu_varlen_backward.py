@@ -85,6 +85,9 @@ CASES = [
     ("titans-d64-b16", 3, 2, [50, 16, 7, 100], 16, 64),
     ("ttt-b16", 2, 2, [31, 90, 16, 3], 16, None),
     ("tiny-d16", 1, 2, [9, 1, 24, 8], 8, None),
+    # 150 documents: the gradient kernel's document search takes three 64-lane
+    # steps, and above 128 documents the carry walk keeps the packing order.
+    ("many-docs", 3, 1, [int(x) for x in np.random.default_rng(5).integers(0, 41, 150)], 16, 32),
 ]
 
 
@@ -92,7 +95,7 @@ CASES = [
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_varlen_backward_parity(label, wid, H, lengths, b, d, dtype):
     w, g, cot, cu = _packed(wid, H, lengths, dtype, d=d)
-    _say(f"case {label} {dtype} H={H} lengths={lengths} b={b} d={w.d}")
+    _say(f"case {label} {dtype} H={H} N={len(lengths)} lengths={lengths[:8]} b={b} d={w.d}")
     _check(g, cot, cu, b, TOL[dtype])
 
 
