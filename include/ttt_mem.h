@@ -321,7 +321,10 @@ int ttt_mem_backward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_
  *     the f32 entry points and fp16 on the bf16 ones, of
  *     ttt_mem_ckpt_bytes_varlen / ttt_mem_ckpt_bytes_varlen_bf16 bytes, caller
  *     owned.  Document s of head h uses the slots from h * (ceil(T/b) + N) +
- *     (the chunks of documents 0..s-1) on; the rest are not written.
+ *     (the chunks of documents 0..s-1) on; the rest are not written.  A
+ *     table that is not non-decreasing can make documents overlap; results
+ *     are then undefined, and a document whose chunks would pass the head's
+ *     last slot is cut there, so no access leaves the caller's buffers.
  *   Layouts: q, k, v, dz, dq, dk, dv [H, T, d]; theta, eta, alpha and their
  *     gradients [H, T]; M0, S0, dM_T, dS_T, dM0, dS0 [N, H, d, d]; cu_seqlens as
  *     for ttt_mem_forward_varlen_*.  The gradients of tokens outside every

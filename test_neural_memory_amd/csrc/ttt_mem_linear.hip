@@ -1185,12 +1185,19 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
         }
         const int s = doc_of_rank(p.cu, p.BH / p.H, p.T, u / p.H, lane), h = u % p.H;
         bh = s * p.H + h;
-        if (p.ckpt) ck_chunk0 = static_cast<size_t>(h) * p.tcmax + doc_chunk_prefix(p.cu, s, p.T, p.b);
         // Offsets clamped into [0, T]: a malformed table cannot send any
         // access outside the packed arrays.
         const int t0 = min(max(p.cu[s], 0), p.T);
         seqlen = min(max(p.cu[s + 1], t0), p.T) - t0;
         seq_tok = static_cast<size_t>(h) * p.T + t0;
+        if (p.ckpt) {
+            // Non-overlapping documents fill at most the head's tcmax slots;
+            // overlapping ones (a table that is not non-decreasing) are cut
+            // at the head's last slot.
+            const int pre = doc_chunk_prefix(p.cu, s, p.T, p.b);
+            ck_chunk0 = static_cast<size_t>(h) * p.tcmax + pre;
+            seqlen = min(seqlen, max(p.tcmax - pre, 0) * p.b);
+        }
     }
     const int b = p.b;
     const int row_wg = rb * RB;

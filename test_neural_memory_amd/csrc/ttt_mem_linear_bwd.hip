@@ -549,8 +549,12 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         int t0;
         seqlen = doc_len(p.cu, s, p.T, t0);
         seq_tok = static_cast<size_t>(h) * p.T + t0;
+        // Cut at the head's last slot, as the forward that wrote the
+        // checkpoints does (only a table that is not non-decreasing gets there).
+        const int pre = doc_chunk_prefix(p.cu, s, p.T, p.b);
+        seqlen = min(seqlen, max(p.tcmax - pre, 0) * p.b);
         nch = (seqlen + p.b - 1) / p.b;
-        w_chunk0 = static_cast<size_t>(h) * p.tcmax + doc_chunk_prefix(p.cu, s, p.T, p.b);
+        w_chunk0 = static_cast<size_t>(h) * p.tcmax + pre;
     }
     const int row_wg = rb * Gm::RB;
     auto chunk_of = [&](int u) { return nch - 1 - u; };

@@ -155,3 +155,23 @@ def test_varlen_backward_argument_errors():
     with pytest.raises(TTTError) as e:
         tm.backward_varlen(*args, cu.cuda(), tm.new_ckpt_varlen(dev["q"], cu, 65), cot["dz"].cuda(), b=65)
     assert e.value.status == -2
+
+
+def test_varlen_training_overlapping_offsets_stay_in_slots():
+    # Offsets that are not non-decreasing make documents overlap, so their
+    # chunks can outnumber the ceil(T/b) + N slots of a head.  The values are
+    # then undefined, but every checkpoint and work-buffer write stays within
+    # the caller's slots: a canary head placed behind both buffers is untouched.
+    w, g, cot, _ = _packed(3, 2, [100, 100], "bf16", d=64)
+    dev = {k: v.cuda() for k, v in g.items() if k not in ("M0", "S0")}
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    cu = torch.tensor([0, 200, 0, 200, 200], dtype=torch.int32, device="cuda")
+    H = dev["q"].shape[0]
+    shape = tm.new_ckpt_varlen(dev["q"], cu, 16).shape
+    ck_big = torch.full((H + 1,) + tuple(shape[1:]), 7.0, dtype=torch.float16, device="cuda")
+    wk_big = torch.full_like(ck_big, 7.0)
+    _say(f"case overlapping offsets {cu.tolist()} b=16 slots={shape[1]}")
+    tm.forward_varlen(*args, cu, b=16, ckpt=ck_big[:H])
+    tm.backward_varlen(*args, cu, ck_big[:H], cot["dz"].cuda(), b=16, work=wk_big[:H])
+    torch.cuda.synchronize()
+    assert (ck_big[H] == 7.0).all() and (wk_big[H] == 7.0).all()
