@@ -14,13 +14,14 @@ from its own state); with ``--backward`` as well, one training step over
 those documents.  ``--backward`` times one training step of the Titans
 linear memory: the forward that saves the chunk-start states plus the
 backward pass (gradients for q, k, v, the three gates and the initial state),
-with a seeded synthetic outer-loss derivative dz.  ``--chunk-gates`` times
+with a seeded synthetic outer-loss derivative dz (with ``--chunk-gates`` as
+well, that step with chunk-shared gates).  ``--chunk-gates`` times
 the Titans forward with gates shared by each chunk's tokens (one theta, eta,
 alpha per 64-token chunk, drawn from the same distributions).  Prints ONE
 JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload {2,3,4,5} | --decode | --varlen [--backward] | --backward | --chunk-gates]
+                    [--workload {2,3,4,5} | --decode | --varlen [--backward] | [--chunk-gates] [--backward]]
                     [--no-cpu-baseline]
 """
 
@@ -264,7 +265,19 @@ def decode_main(args):
     print(json.dumps(result), flush=True)
 
 
-def algorithmic_work_backward(w, in_bytes=2):
+def set_chunk_gates(w, inp):
+    """Replace the per-token gates of `inp` by one gate triple per (batch, head,
+    chunk), drawn from the same Titans distributions (seed 4003)."""
+    nc = (w.T + w.b - 1) // w.b
+    rng = np.random.default_rng(4003)
+    sig = lambda x: 1.0 / (1.0 + np.exp(-x))  # noqa: E731
+    gsh = (w.B, w.H, nc)
+    inp["theta"] = torch.from_numpy((0.1 * sig(rng.standard_normal(gsh))).astype(np.float32))
+    inp["eta"] = torch.from_numpy(sig(rng.normal(2.0, np.sqrt(0.5), gsh)).astype(np.float32))
+    inp["alpha"] = torch.from_numpy((0.05 * sig(rng.normal(-1.0, 1.0, gsh))).astype(np.float32))
+
+
+def algorithmic_work_backward(w, in_bytes=2, chunk_gates=False):
     """Bytes and flops the method must move / do for one backward pass.
 
     Per (batch, head, token): read q, k, v, three gates and dz; write dq, dk,
@@ -274,29 +287,35 @@ def algorithmic_work_backward(w, in_bytes=2):
     K dS^T, Q^T (A.dZ), Q^T (c.dZ), K^T dE) and the chunk gradients (6: K M0^T,
     dZ M0, dZ S0, dE M0, E dM, E dS) are 22 d^2; the intra-chunk products
     (P^T dZ, Q K^T twice, dZ E^T, DL K, DL^T Q) add 12 b d.  The checkpointed
-    states the implementation writes and reads are not counted.
+    states the implementation writes and reads are not counted.  With chunk
+    gates, the gates and their gradients are one triple per chunk.
     """
     ht = w.B * w.H * w.T
-    per_tok = 3 * w.d * in_bytes + 3 * 4 + w.d * 4 + 3 * w.d * 4 + 3 * 4
+    gate_tok = 0 if chunk_gates else 3 * 4 + 3 * 4
+    per_tok = 3 * w.d * in_bytes + w.d * 4 + 3 * w.d * 4 + gate_tok
+    gates = w.B * w.H * ((w.T + w.b - 1) // w.b) * (3 * 4 + 3 * 4) if chunk_gates else 0
     state = w.B * w.H * w.d * w.d * 4 * 2
     flops = ht * (22 * w.d * w.d + 12 * w.b * w.d)
-    return ht * per_tok + state, flops, per_tok
+    return ht * per_tok + gates + state, flops, per_tok
 
 
 def _oracle_train_worker(args):
     # One BLAS thread; the oracle's forward and backward, one sequence at a time.
-    seqs, b = args
+    seqs, b = args[:2]
+    chunk_gates = len(args) > 2 and args[2]
     from threadpoolctl import threadpool_limits
-    from oracle import linear_backward, linear_forward
+    from oracle import linear_backward, linear_backward_chunk_gates, linear_forward, linear_forward_chunk_gates
+    fwd = linear_forward_chunk_gates if chunk_gates else linear_forward
+    bwd = linear_backward_chunk_gates if chunk_gates else linear_backward
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         for q, k, v, th, et, al, dz in seqs:
-            linear_forward(q, k, v, th, et, al, None, None, b=b)
-            linear_backward(q, k, v, th, et, al, dz, None, None, None, None, b=b)
+            fwd(q, k, v, th, et, al, None, None, b=b)
+            bwd(q, k, v, th, et, al, dz, None, None, None, None, b=b)
         return time.perf_counter() - t0
 
 
-def cpu_baseline_backward(w, inp, cot, pairs=64, tokens=2048):
+def cpu_baseline_backward(w, inp, cot, pairs=64, tokens=2048, chunk_gates=False):
     """Time the float64 oracle (forward, then backward) on `pairs` (batch, head)
     sequences cut to their first `tokens` tokens, in a process pool."""
     import multiprocessing as mp
@@ -305,9 +324,11 @@ def cpu_baseline_backward(w, inp, cot, pairs=64, tokens=2048):
     dz = to_numpy64(cot["dz"])
     B, H = w.B, w.H
     sel = [(i // H, i % H) for i in range(B * H)][:pairs]
-    jobs = [([], w.b) for _ in range(ncores)]
+    jobs = [([], w.b, chunk_gates) for _ in range(ncores)]
+    gt = (tokens + w.b - 1) // w.b if chunk_gates else tokens
     for i, (bi, hi) in enumerate(sel):
-        jobs[i % ncores][0].append(tuple(g[x][bi, hi, :tokens] for x in ("q", "k", "v", "theta", "eta", "alpha"))
+        jobs[i % ncores][0].append(tuple(g[x][bi, hi, :tokens] for x in ("q", "k", "v"))
+                                   + tuple(g[x][bi, hi, :gt] for x in ("theta", "eta", "alpha"))
                                    + (dz[bi, hi, :tokens],))
     jobs = [j for j in jobs if j[0]]
     ctx = mp.get_context("fork")
@@ -322,18 +343,23 @@ def cpu_baseline_backward(w, inp, cot, pairs=64, tokens=2048):
         "cores": len(jobs),
         "kind": "oracle",
         "sample": f"{len(sel)} of {B * H} (batch, head) sequences, first {tokens} of T={w.T} tokens, all "
-                  f"d={w.d} rows; float64 per-token NumPy forward then reverse-mode backward, "
+                  f"d={w.d} rows; float64 per-token NumPy forward then reverse-mode backward"
+                  f"{' (chunk-shared gates)' if chunk_gates else ''}, "
                   f"{len(jobs)} processes x 1 thread; wall {wall:.2f} s, busiest process {max(per_job):.2f} s; "
                   f"tokens/s = sampled head-tokens / H / wall",
     }
 
 
 def backward_main(args):
-    """One training step of the Titans linear memory: forward with checkpoints + backward."""
+    """One training step of the Titans linear memory: forward with checkpoints +
+    backward; with ``--chunk-gates``, gates shared by each chunk's tokens."""
     w = WORKLOADS[3]
+    cg = args.chunk_gates
     B, H, T, d = w.B, w.H, w.T, w.d
-    log(f"training step workload {w}")
+    log(f"training step workload {w}{' with chunk-shared gates' if cg else ''}")
     inp = make_inputs(w)
+    if cg:
+        set_chunk_gates(w, inp)
     cot = make_cotangents(w, states=False)
     dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     dz = cot["dz"].cuda()
@@ -344,11 +370,15 @@ def backward_main(args):
     nch = (T + w.b - 1) // w.b
     ckpt = tm.new_ckpt(dev["q"], w.b)
     work = torch.empty_like(ckpt)
+    gl = nch if cg else T
     outs = [torch.empty(B, H, T, d, dtype=torch.float32, device="cuda") for _ in range(3)] + \
-           [torch.empty(B, H, T, dtype=torch.float32, device="cuda") for _ in range(3)] + \
+           [torch.empty(B, H, gl, dtype=torch.float32, device="cuda") for _ in range(3)] + \
            [torch.empty(B, H, d, d, dtype=torch.float32, device="cuda") for _ in range(2)]
-    fwd = lambda: tm.forward_train(*args_, b=w.b, out=(z, MT, ST), ckpt=ckpt)  # noqa: E731
-    bwd = lambda: tm.backward(*args_, ckpt, dz, b=w.b, work=work, out=outs)  # noqa: E731
+    if cg:
+        fwd = lambda: tm.forward_chunk_gates(*args_, b=w.b, out=(z, MT, ST), ckpt=ckpt)  # noqa: E731
+    else:
+        fwd = lambda: tm.forward_train(*args_, b=w.b, out=(z, MT, ST), ckpt=ckpt)  # noqa: E731
+    bwd = lambda: tm.backward(*args_, ckpt, dz, b=w.b, work=work, out=outs, chunk_gates=cg)  # noqa: E731
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -368,7 +398,7 @@ def backward_main(args):
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_per_step = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
-    nbytes, flops, _ = algorithmic_work_backward(w)
+    nbytes, flops, _ = algorithmic_work_backward(w, chunk_gates=cg)
     fbytes, _, _ = algorithmic_work(w)
     achieved_gbs = nbytes / (bwd_ms * 1e-3) / 1e9
     achieved_tflops = flops / (bwd_ms * 1e-3) / 1e12
@@ -382,26 +412,29 @@ def backward_main(args):
     # Sampled parity: the last two chunks of sequences (0, 0) and (B-1, H-1).
     # No loss reaches past them, so their gradients are the oracle's on that
     # window started from the oracle's own state after the chunks before it.
-    from oracle import linear_backward, linear_forward
+    from oracle import linear_backward, linear_backward_chunk_gates, linear_forward, linear_forward_chunk_gates
+    lf = linear_forward_chunk_gates if cg else linear_forward
+    lb = linear_backward_chunk_gates if cg else linear_backward
     t0 = (nch - 2) * w.b
+    g0 = nch - 2 if cg else t0   # first gate entry of the window
     errs = []
     for (bi, hi) in ((0, 0), (B - 1, H - 1)):
         g = {k: to_numpy64(v[bi, hi]) for k, v in inp.items() if v is not None}
-        _, Ms, Ss = linear_forward(g["q"][:t0], g["k"][:t0], g["v"][:t0], g["theta"][:t0], g["eta"][:t0],
-                                   g["alpha"][:t0], None, None, b=w.b)
-        ref = linear_backward(g["q"][t0:], g["k"][t0:], g["v"][t0:], g["theta"][t0:], g["eta"][t0:],
-                              g["alpha"][t0:], to_numpy64(cot["dz"][bi, hi, t0:]), None, None, Ms, Ss, b=w.b)
-        for x, r in zip(outs[:6], ref[:6]):
-            xg = x[bi, hi, t0:].double().cpu().numpy()
+        _, Ms, Ss = lf(g["q"][:t0], g["k"][:t0], g["v"][:t0], g["theta"][:g0], g["eta"][:g0],
+                       g["alpha"][:g0], None, None, b=w.b)
+        ref = lb(g["q"][t0:], g["k"][t0:], g["v"][t0:], g["theta"][g0:], g["eta"][g0:],
+                 g["alpha"][g0:], to_numpy64(cot["dz"][bi, hi, t0:]), None, None, Ms, Ss, b=w.b)
+        for i, (x, r) in enumerate(zip(outs[:6], ref[:6])):
+            xg = x[bi, hi, (t0 if i < 3 else g0):].double().cpu().numpy()
             errs.append(float(np.max(np.abs(xg - r)) / np.sqrt(np.mean(r ** 2))))
     parity = max(errs)
     log(f"sampled parity (last two chunks of two sequences, every gradient): max|d|/rms = {parity:.3e}")
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_backward(w, inp, cot)
+        cpu = cpu_baseline_backward(w, inp, cot, chunk_gates=cg)
         log(f"cpu baseline: {cpu}")
     result = {
-        "metric": "training tokens/s (forward + backward) at H=16,d=128,b=64",
+        "metric": "training tokens/s (forward + backward) at H=16,d=128,b=64" + (" (chunk-shared gates)" if cg else ""),
         "value": B * T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -413,12 +446,14 @@ def backward_main(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "titans-linear-train", "B": B, "H": H, "T": T, "d": d, "b": w.b,
-                   "inputs": "bf16 q,k,v; f32 gates; f32 dz (seeded N(0,1))", "accumulate": "f32",
+        "config": {"workload": "titans-linear-train" + ("-chunk-gates" if cg else ""), "B": B, "H": H, "T": T,
+                   "d": d, "b": w.b,
+                   "inputs": f"bf16 q,k,v; f32 gates{' per chunk' if cg else ''}; f32 dz (seeded N(0,1))",
+                   "accumulate": "f32",
                    "gradients": "f32", "checkpoints": "fp16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                    "checkpoint_bytes": ck_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w, "backward"),
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None if cg else measured_traffic(w, "backward"),
                      "traffic_unit": "bytes/launch",
                      "algorithmic_bytes": nbytes, "kernel": "backward pass (carry walk + chunk gradients)",
                      "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS},
@@ -773,14 +808,7 @@ def main():
     log(f"workload {w}{' with chunk-shared gates' if args.chunk_gates else ''}")
     inp = make_inputs(w)
     if args.chunk_gates:
-        # One gate triple per (batch, head, chunk), the Titans distributions.
-        nc = (w.T + w.b - 1) // w.b
-        rng = np.random.default_rng(4003)
-        sig = lambda x: 1.0 / (1.0 + np.exp(-x))  # noqa: E731
-        gsh = (w.B, w.H, nc)
-        inp["theta"] = torch.from_numpy((0.1 * sig(rng.standard_normal(gsh))).astype(np.float32))
-        inp["eta"] = torch.from_numpy(sig(rng.normal(2.0, np.sqrt(0.5), gsh)).astype(np.float32))
-        inp["alpha"] = torch.from_numpy((0.05 * sig(rng.normal(-1.0, 1.0, gsh))).astype(np.float32))
+        set_chunk_gates(w, inp)
     dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     B, H, T, d = w.B, w.H, w.T, w.d
     z = torch.empty(B, H, T, d, dtype=torch.float32, device="cuda")

@@ -138,8 +138,9 @@ def forward_chunk_gates(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=
 
     ``theta, eta, alpha`` are ``[B, H, ceil(T/b)]``: every token of chunk c uses
     entry c.  Returns ``(z, M_T, S_T)``, or ``(z, M_T, S_T, ckpt)`` when a
-    ``ckpt`` tensor (``[B, H, ceil(T/b), 2, d, d]`` float32) is given to keep
-    the chunk-start states for ``backward(..., chunk_gates=True)``.
+    ``ckpt`` tensor (``[B, H, ceil(T/b), 2, d, d]`` of ``ckpt_dtype(q.dtype)``,
+    as from ``new_ckpt``) is given to keep the chunk-start states for
+    ``backward(..., chunk_gates=True)``.
     """
     if q.dtype == torch.float32:
         name = "ttt_mem_forward_cg_f32"
