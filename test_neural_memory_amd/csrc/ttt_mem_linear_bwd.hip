@@ -1521,8 +1521,10 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
     const long long nch = (static_cast<long long>(Tlen) + b - 1) / b;
     const long long tcmax = packed ? varlen_chunk_slots(B, Tlen, b) : 0;
     const long long seqs = packed ? H : BH;   // rows of Tlen tokens
-    if (seqs * static_cast<long long>(Tlen) > 0x7fffffffLL || BH * nch > 0x7fffffffLL ||
-        BH * (d / 16) > 0x7fffffffLL || static_cast<long long>(H) * tcmax > 0x7fffffffLL)
+    // Grids and int indices: the carry walk has BH * (d / 16) workgroups at
+    // most; the gradient kernel BH * nch (dense) or H * tcmax (packed).
+    if (seqs * static_cast<long long>(Tlen) > 0x7fffffffLL || BH * (d / 16) > 0x7fffffffLL ||
+        (packed ? static_cast<long long>(H) * tcmax : BH * nch) > 0x7fffffffLL)
         return TTT_ERR_UNSUPPORTED;
     if (packed && !aligned(cu, 4)) return TTT_ERR_INVALID_ARG;
     const size_t tok = static_cast<size_t>(seqs) * static_cast<size_t>(Tlen);

@@ -98,3 +98,13 @@ def test_varlen_training_forward_requires_ckpt(lib, name):
 def test_varlen_backward_requires_offsets(lib, name):
     # 19 arrays, then cu_seqlens (NULL); N H T d b; stream
     assert getattr(lib, name)(*([None] * 20), 2, 1, 8, 16, 4, None) == -1
+
+
+@pytest.mark.parametrize("name", ["ttt_mem_backward_varlen_f32", "ttt_mem_backward_varlen_bf16"])
+def test_varlen_backward_large_document_count_is_checked_not_refused(lib, name):
+    # 100000 documents of a 4M-token packed row on 32 heads: the gradient grid
+    # is H * (ceil(T/b) + N) workgroups, well inside int, so the size check
+    # passes and the NULL arrays are what is rejected (no array is touched:
+    # the offsets pointer is a never-read stand-in).
+    fake_cu = ctypes.c_void_p(1 << 20)
+    assert getattr(lib, name)(*([None] * 19), fake_cu, 100000, 32, 1 << 22, 128, 64, None) == -1
