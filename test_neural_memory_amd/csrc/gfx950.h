@@ -217,14 +217,23 @@ __device__ __forceinline__ int doc_len(const int* cu, int s, int T, int& t0) {
     t0 = min(max(cu[s], 0), T);
     return min(max(cu[s + 1], t0), T) - t0;
 }
-// Chunks of documents 0 .. s-1 (the first chunk slot of document s).
-__device__ __forceinline__ int doc_chunk_prefix(const int* cu, int s, int T, int b) {
+// Chunks of documents 0 .. s-1 (the first chunk slot of document s).  Called
+// by a whole 64-wide wave (lane = its lane index, s uniform): the lanes take
+// 64 documents at a time and the wave sums their chunk counts.
+__device__ __forceinline__ int doc_chunk_prefix(const int* cu, int s, int T, int b, int lane) {
     int acc = 0;
-    for (int j = 0; j < s; ++j) {
-        int t0;
-        acc += (doc_len(cu, j, T, t0) + b - 1) / b;
+    for (int base = 0; base < s; base += 64) {
+        const int j = base + lane;
+        int nj = 0;
+        if (j < s) {
+            int t0;
+            nj = (doc_len(cu, j, T, t0) + b - 1) / b;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) nj += __shfl_xor(nj, o, 64);
+        acc += nj;
     }
-    return acc;
+    return __builtin_amdgcn_readfirstlane(acc);
 }
 
 // Packed documents: the document of rank r when the N documents are ordered
@@ -236,21 +245,33 @@ __device__ __forceinline__ int doc_chunk_prefix(const int* cu, int s, int T, int
 // above kLptDocs documents the packing order is kept.
 constexpr int kLptDocs = 128;
 __device__ __forceinline__ int doc_of_rank(const int* cu, int N, int T, int r, int lane) {
+    static_assert(kLptDocs <= 128, "two lengths per lane");
     if (N > kLptDocs) return r;
-    auto len = [&](int i) {
-        const int t0 = min(max(cu[i], 0), T);
-        return min(max(cu[i + 1], t0), T) - t0;
-    };
-    for (int base = 0; base < N; base += 64) {
-        const int i = base + lane;
-        const int li = i < N ? len(i) : -1;
+    // Lane l holds the lengths of documents l and 64 + l (-1 past N); the
+    // rank loop reads them back with uniform lane reads, not memory loads.
+    int len[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int i = 64 * g + lane;
+        int t0;
+        len[g] = i < N ? doc_len(cu, i, T, t0) : -1;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        if (64 * g >= N) break;
+        const int i = 64 * g + lane;
+        const int li = len[g];
         int rank = 0;
-        for (int j = 0; j < N; ++j) {
-            const int lj = len(j);
+        for (int j = 0; j < min(N, 64); ++j) {
+            const int lj = __builtin_amdgcn_readlane(len[0], j);
+            rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+        for (int j = 64; j < N; ++j) {
+            const int lj = __builtin_amdgcn_readlane(len[1], j - 64);
             rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
         }
         const unsigned long long hit = __ballot(i < N && rank == r);
-        if (hit) return base + __ffsll(static_cast<long long>(hit)) - 1;
+        if (hit) return 64 * g + __ffsll(static_cast<long long>(hit)) - 1;
     }
     return r;
 }

@@ -1194,7 +1194,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
             // Non-overlapping documents fill at most the head's tcmax slots;
             // overlapping ones (a table that is not non-decreasing) are cut
             // at the head's last slot.
-            const int pre = doc_chunk_prefix(p.cu, s, p.T, p.b);
+            const int pre = doc_chunk_prefix(p.cu, s, p.T, p.b, lane);
             ck_chunk0 = static_cast<size_t>(h) * p.tcmax + pre;
             seqlen = min(seqlen, max(p.tcmax - pre, 0) * p.b);
         }

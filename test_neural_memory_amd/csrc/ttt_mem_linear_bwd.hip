@@ -551,7 +551,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         seq_tok = static_cast<size_t>(h) * p.T + t0;
         // Cut at the head's last slot, as the forward that wrote the
         // checkpoints does (only a table that is not non-decreasing gets there).
-        const int pre = doc_chunk_prefix(p.cu, s, p.T, p.b);
+        const int pre = doc_chunk_prefix(p.cu, s, p.T, p.b, lane);
         seqlen = min(seqlen, max(p.tcmax - pre, 0) * p.b);
         nch = (seqlen + p.b - 1) / p.b;
         w_chunk0 = static_cast<size_t>(h) * p.tcmax + pre;

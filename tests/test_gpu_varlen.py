@@ -79,6 +79,8 @@ CASES = [
     ("ttt-b16", 2, 2, [31, 90, 16, 3], 16, None),
     ("tiny-d16", 1, 2, [9, 1, 24, 8], 8, None),
     # 150 documents: above 128 the dispatch keeps the packing order.
+    # 100 documents: the longest-first ranking uses both of its 64-lane groups.
+    ("hundred-docs", 3, 1, [int(x) for x in np.random.default_rng(6).integers(0, 41, 100)], 16, 32),
     ("many-docs", 3, 1, [int(x) for x in np.random.default_rng(5).integers(0, 41, 150)], 16, 32),
 ]
 
