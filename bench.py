@@ -112,8 +112,11 @@ def measured_traffic(w, kind="forward"):
     elif kind == "varlen":
         path = os.path.join(ROOT, "profiles", "linear_memory_fwd_varlen_titans_d128_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear.hip")
-    elif kind == "backward":
-        path = os.path.join(ROOT, "profiles", "linear_memory_train_titans_d128_b64_traffic.json")
+    elif kind in ("backward", "varlen_backward", "cg_backward"):
+        name = {"backward": "linear_memory_train_titans_d128_b64",
+                "varlen_backward": "linear_memory_train_varlen_titans_d128",
+                "cg_backward": "linear_memory_train_chunk_gates_titans_d128_b64"}[kind]
+        path = os.path.join(ROOT, "profiles", name + "_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear_bwd.hip")
     else:
         path = os.path.join(ROOT, "profiles", "linear_memory_fwd_titans_d128_b64_traffic.json")
@@ -453,7 +456,7 @@ def backward_main(args):
                    "gradients": "f32", "checkpoints": "fp16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                    "checkpoint_bytes": ck_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None if cg else measured_traffic(w, "backward"),
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w, "cg_backward" if cg else "backward"),
                      "traffic_unit": "bytes/launch",
                      "algorithmic_bytes": nbytes, "kernel": "backward pass (carry walk + chunk gradients)",
                      "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS},
@@ -637,8 +640,9 @@ def varlen_train_main(args):
                    "gradients": "f32", "checkpoints": "fp16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                    "checkpoint_bytes": ckpt.numel() * ckpt.element_size()},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None, "traffic_unit": "bytes/launch",
-                     "algorithmic_bytes": nbytes, "kernel": "backward pass (carry walk + chunk gradients)"},
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wv, "varlen_backward"),
+                     "traffic_unit": "bytes/launch", "algorithmic_bytes": nbytes,
+                     "kernel": "backward pass (carry walk + chunk gradients)"},
         "cpu_baseline": cpu,
         "parity_sample_max_rel_err": parity,
     }
