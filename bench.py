@@ -109,6 +109,9 @@ def measured_traffic(w, kind="forward"):
     if kind == "decode":
         path = os.path.join(ROOT, "profiles", "linear_memory_decode_titans_d128_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_decode.hip")
+    elif kind == "cg_forward":
+        path = os.path.join(ROOT, "profiles", "linear_memory_fwd_chunk_gates_titans_d128_b64_traffic.json")
+        src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear.hip")
     elif kind == "varlen":
         path = os.path.join(ROOT, "profiles", "linear_memory_fwd_varlen_titans_d128_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_linear.hip")
@@ -857,7 +860,7 @@ def main():
         if args.chunk_gates:
             # Three gate floats per chunk instead of per token.
             nbytes -= w.B * w.H * (w.T - (w.T + w.b - 1) // w.b) * 12
-            traffic = None
+            traffic = measured_traffic(w, "cg_forward")
     achieved_gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
     achieved_tflops = flops / (avg_launch_ms * 1e-3) / 1e12
     tokens_per_s = B * T / (ms_per_step * 1e-3)
