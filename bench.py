@@ -104,9 +104,12 @@ def measured_traffic(w, kind="forward"):
     longer describes this kernel and None is returned.
     """
     import hashlib
-    if w.id != 3:
+    if w.id != (5 if kind == "mlp" else 3):
         return None
-    if kind == "decode":
+    if kind == "mlp":
+        path = os.path.join(ROOT, "profiles", "mlp_memory_fwd_deep_d64_h256_b16_traffic.json")
+        src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_mlp.hip")
+    elif kind == "decode":
         path = os.path.join(ROOT, "profiles", "linear_memory_decode_titans_d128_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_decode.hip")
     elif kind == "cg_forward":
@@ -853,7 +856,7 @@ def main():
 
     if deep:
         nbytes, flops, per_tok = algorithmic_work_mlp(w)
-        traffic = None
+        traffic = measured_traffic(w, "mlp")
     else:
         nbytes, flops, per_tok = algorithmic_work(w, reads_state=dev.get("M0") is not None)
         traffic = measured_traffic(w)
