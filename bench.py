@@ -41,7 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from test_neural_memory_amd import memory as tm  # noqa: E402
-from test_neural_memory_amd.workloads import WORKLOADS, make_cotangents, make_inputs, to_numpy64  # noqa: E402
+from test_neural_memory_amd.workloads import WORKLOADS, make_cotangents, make_inputs, to_numpy64, varlen_lengths  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
@@ -470,19 +470,6 @@ def backward_main(args):
         "parity_sample_max_rel_err": parity,
     }
     print(json.dumps(result), flush=True)
-
-
-def varlen_lengths(total, seed=3001, mean=1024):
-    """Seeded document lengths for a packed batch: lognormal (sigma 1) around `mean`,
-    clipped to [1, 8192], the last one trimmed so that they sum to `total`."""
-    rng = np.random.default_rng(seed)
-    out, acc = [], 0
-    while acc < total:
-        n = int(np.clip(rng.lognormal(np.log(mean) - 0.5, 1.0), 1, 8192))
-        n = min(n, total - acc)
-        out.append(n)
-        acc += n
-    return out
 
 
 def varlen_main(args):

@@ -169,3 +169,16 @@ def make_cotangents(w: Workload, seed: int | None = None, states: bool = True, c
 def to_numpy64(t):
     """A CPU tensor (any float dtype) as a float64 numpy array; None stays None."""
     return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+
+def varlen_lengths(total, seed=3001, mean=1024):
+    """Seeded document lengths for a packed batch: lognormal (sigma 1) around `mean`,
+    clipped to [1, 8192], the last one trimmed so that they sum to `total`."""
+    rng = np.random.default_rng(seed)
+    out, acc = [], 0
+    while acc < total:
+        n = int(np.clip(rng.lognormal(np.log(mean) - 0.5, 1.0), 1, 8192))
+        n = min(n, total - acc)
+        out.append(n)
+        acc += n
+    return out

@@ -143,3 +143,30 @@ def test_varlen_argument_errors():
     assert e.value.status == -1
     with pytest.raises(ValueError):
         tm.forward_varlen(*args, cu, b=16)   # offsets must be on the device
+
+
+def test_varlen_full_size_sampled():
+    # The packed workload in the launch configuration of the bench: 32768
+    # tokens per head in 31 documents of seeded lognormal lengths, H=16,
+    # d=128, b=64, bf16.  Checked on documents 0 and 1 and the longest, on
+    # heads 0 and 15, every row of z and both final states.
+    from test_neural_memory_amd.workloads import varlen_lengths
+    w = WORKLOADS[3].replace(B=1, T=4 * 8192)
+    L = varlen_lengths(w.T)
+    inp = make_inputs(w)
+    dev = {k: v[0].cuda() for k, v in inp.items() if v is not None}
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    _say(f"case full-size packed forward: {len(L)} documents, T={w.T}")
+    z, M, S = tm.forward_varlen(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"],
+                                torch.from_numpy(cu).cuda(), b=w.b)
+    torch.cuda.synchronize()
+    for h in (0, w.H - 1):
+        n = {k: to_numpy64(v[0, h]) for k, v in inp.items() if v is not None}
+        for s in (0, 1, int(np.argmax(L))):
+            t0, t1 = int(cu[s]), int(cu[s + 1])
+            zo, Mo, So = linear_forward(n["q"][t0:t1], n["k"][t0:t1], n["v"][t0:t1], n["theta"][t0:t1],
+                                        n["eta"][t0:t1], n["alpha"][t0:t1], None, None, b=w.b)
+            errs = [rel_err(to_numpy64(z[h, t0:t1].cpu()), zo), rel_err(to_numpy64(M[s, h].cpu()), Mo),
+                    rel_err(to_numpy64(S[s, h].cpu()), So)]
+            _say(f"  head {h} document {s} ({t1 - t0} tokens): z={errs[0]:.2e} M_T={errs[1]:.2e} S_T={errs[2]:.2e}")
+            assert max(errs) <= TOL["bf16"], errs

@@ -177,3 +177,37 @@ def test_varlen_training_overlapping_offsets_stay_in_slots():
     tm.backward_varlen(*args, cu, ck_big[:H], cot["dz"].cuda(), b=16, work=wk_big[:H])
     torch.cuda.synchronize()
     assert (ck_big[H] == 7.0).all() and (wk_big[H] == 7.0).all()
+
+
+def test_varlen_training_full_size_sampled():
+    # Training over the packed workload in the launch configuration of the
+    # bench (32768 tokens per head in 31 documents of seeded lognormal
+    # lengths, H=16, d=128, b=64, bf16, seeded N(0,1) dz).  Every gradient of
+    # documents 0 and 1 and of the longest one, on heads 0 and 15, against the
+    # oracle's backward of each document alone.
+    from test_neural_memory_amd.workloads import make_cotangents, varlen_lengths
+    w = WORKLOADS[3].replace(B=1, T=4 * 8192)
+    L = varlen_lengths(w.T)
+    inp = make_inputs(w)
+    dev = {k: v[0].cuda() for k, v in inp.items() if v is not None}
+    dz = make_cotangents(w, states=False)["dz"][0]
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    cud = torch.from_numpy(cu).cuda()
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    _say(f"case full-size packed training: {len(L)} documents, T={w.T}")
+    ckpt = tm.new_ckpt_varlen(dev["q"], cud, w.b)
+    tm.forward_varlen(*args, cud, b=w.b, ckpt=ckpt)
+    g = tm.backward_varlen(*args, cud, ckpt, dz.cuda(), b=w.b)
+    torch.cuda.synchronize()
+    for h in (0, w.H - 1):
+        n = {k: to_numpy64(v[0, h]) for k, v in inp.items() if v is not None}
+        dzn = to_numpy64(dz[h])
+        for s in (0, 1, int(np.argmax(L))):
+            t0, t1 = int(cu[s]), int(cu[s + 1])
+            ref = linear_backward(n["q"][t0:t1], n["k"][t0:t1], n["v"][t0:t1], n["theta"][t0:t1],
+                                  n["eta"][t0:t1], n["alpha"][t0:t1], dzn[t0:t1], None, None, None, None, b=w.b)
+            got = [to_numpy64(x[h, t0:t1].cpu()) for x in g[:6]] + [to_numpy64(g[6][s, h].cpu()),
+                                                                      to_numpy64(g[7][s, h].cpu())]
+            errs = {nm: rel_err(x, r) for nm, x, r in zip(NAMES, got, ref)}
+            _say(f"  head {h} document {s} ({t1 - t0} tokens): max error {max(errs.values()):.2e}")
+            assert max(errs.values()) <= TOL["bf16"], errs
