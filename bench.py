@@ -41,7 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from test_neural_memory_amd import memory as tm  # noqa: E402
-from test_neural_memory_amd.workloads import WORKLOADS, make_cotangents, make_inputs, to_numpy64, varlen_lengths  # noqa: E402
+from test_neural_memory_amd.workloads import WORKLOADS, make_cotangents, make_inputs, to_numpy64, varlen_lengths, set_chunk_gates  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
@@ -272,18 +272,6 @@ def decode_main(args):
         "parity_sample_max_rel_err": parity,
     }
     print(json.dumps(result), flush=True)
-
-
-def set_chunk_gates(w, inp):
-    """Replace the per-token gates of `inp` by one gate triple per (batch, head,
-    chunk), drawn from the same Titans distributions (seed 4003)."""
-    nc = (w.T + w.b - 1) // w.b
-    rng = np.random.default_rng(4003)
-    sig = lambda x: 1.0 / (1.0 + np.exp(-x))  # noqa: E731
-    gsh = (w.B, w.H, nc)
-    inp["theta"] = torch.from_numpy((0.1 * sig(rng.standard_normal(gsh))).astype(np.float32))
-    inp["eta"] = torch.from_numpy(sig(rng.normal(2.0, np.sqrt(0.5), gsh)).astype(np.float32))
-    inp["alpha"] = torch.from_numpy((0.05 * sig(rng.normal(-1.0, 1.0, gsh))).astype(np.float32))
 
 
 def algorithmic_work_backward(w, in_bytes=2, chunk_gates=False):

@@ -182,3 +182,15 @@ def varlen_lengths(total, seed=3001, mean=1024):
         out.append(n)
         acc += n
     return out
+
+
+def set_chunk_gates(w, inp):
+    """Replace the per-token gates of `inp` by one gate triple per (batch, head,
+    chunk), drawn from the same Titans distributions (seed 4003)."""
+    nc = (w.T + w.b - 1) // w.b
+    rng = np.random.default_rng(4003)
+    sig = lambda x: 1.0 / (1.0 + np.exp(-x))  # noqa: E731
+    gsh = (w.B, w.H, nc)
+    inp["theta"] = torch.from_numpy((0.1 * sig(rng.standard_normal(gsh))).astype(np.float32))
+    inp["eta"] = torch.from_numpy(sig(rng.normal(2.0, np.sqrt(0.5), gsh)).astype(np.float32))
+    inp["alpha"] = torch.from_numpy((0.05 * sig(rng.normal(-1.0, 1.0, gsh))).astype(np.float32))

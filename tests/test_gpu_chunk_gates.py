@@ -81,3 +81,40 @@ def test_backward_parity(label, wid, kw, dtype):
     errs = {nm: rel_err(to_numpy64(x.cpu()), r) for nm, x, r in zip(names, g, ref)}
     _say("  errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert max(errs.values()) <= TOL[dtype], errs
+
+
+def test_full_size_training_window():
+    # The full-size Titans workload with the bench's chunk-shared gates (B=4,
+    # H=16, T=8192, d=128, b=64, bf16), in its launch configuration, with the
+    # outer loss on chunks 60-61 only: their z and gradients are the oracle's
+    # on that window, started from the oracle's state after 60 chunks, and no
+    # gradient reaches the gates of later chunks.
+    from test_neural_memory_amd.workloads import set_chunk_gates
+    w = WORKLOADS[3]
+    c0, c1 = 60, 62
+    inp = make_inputs(w)
+    set_chunk_gates(w, inp)
+    cot = make_cotangents(w, states=False, chunks=(c0, c1))
+    dev, cd = to_dev(inp), to_dev(cot)
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
+    _say("case full size chunk gates: forward with checkpoints")
+    ckpt = tm.new_ckpt(dev["q"], w.b)
+    z, _, _, _ = tm.forward_chunk_gates(*args, b=w.b, ckpt=ckpt)
+    _say("case full size chunk gates: backward")
+    g = tm.backward(*args, ckpt, cd["dz"], b=w.b, chunk_gates=True)
+    torch.cuda.synchronize()
+    t0, t1 = c0 * w.b, c1 * w.b
+    for x in g[3:6]:
+        assert not torch.any(x[:, :, c1:]), "gate gradient after the window"
+    for (bi, hi) in ((0, 0), (3, 15)):
+        n = {k: to_numpy64(v[bi, hi]) for k, v in inp.items() if v is not None}
+        _, Ms, Ss = linear_forward_chunk_gates(n["q"][:t0], n["k"][:t0], n["v"][:t0], n["theta"][:c0],
+                                               n["eta"][:c0], n["alpha"][:c0], None, None, b=w.b)
+        win = (n["q"][t0:t1], n["k"][t0:t1], n["v"][t0:t1], n["theta"][c0:c1], n["eta"][c0:c1], n["alpha"][c0:c1])
+        zo = linear_forward_chunk_gates(*win, Ms, Ss, b=w.b)[0]
+        ref = linear_backward_chunk_gates(*win, to_numpy64(cot["dz"][bi, hi, t0:t1]), None, None, Ms, Ss, b=w.b)
+        got = [to_numpy64(x[bi, hi, t0:t1].cpu()) for x in g[:3]] + [to_numpy64(x[bi, hi, c0:c1].cpu()) for x in g[3:6]]
+        errs = {nm: rel_err(x, r) for nm, x, r in zip(("dq", "dk", "dv", "dtheta", "deta", "dalpha"), got, ref[:6])}
+        errs["z"] = rel_err(to_numpy64(z[bi, hi, t0:t1].cpu()), zo)
+        _say(f"  ({bi},{hi}) errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        assert max(errs.values()) <= TOL["bf16"], errs
