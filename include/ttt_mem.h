@@ -34,7 +34,9 @@
  *       theta, eta, alpha [B, H, T]      float32
  *       M0, S0, M_T, S_T  [B, H, d, d]   float32, M[i*d + j] carries key
  *                                        coordinate j into value coordinate i
- *       z                 [B, H, T, d]   float32
+ *       z                 [B, H, T, d]   bf16 on ttt_mem_forward_bf16 and
+ *                                        ttt_mem_mlp_forward_bf16 (rounded to
+ *                                        nearest even), float32 everywhere else
  *   - M0 or S0 may be NULL, meaning zeros.  M_T or S_T may be NULL, meaning
  *     "do not write".  M_T may be the same pointer as M0 and S_T the same as
  *     S0 (in-place state carry); z must not overlap any input.
@@ -79,24 +81,32 @@ int ttt_mem_forward_f32(const float* q, const float* k, const float* v,
                         int B, int H, int T, int d, int b, void* stream);
 
 /*
- * Linear memory, bfloat16 q, k, v (raw bf16 bit patterns, uint16_t per
- * element), float32 state and z.  Matrix products run on fp16 MFMA operands
- * with float32 accumulation: q and k convert to fp16 exactly (fp16 normal
- * range), the state, the residuals and the intra-chunk weights are rounded
- * to fp16 once per chunk where they enter a product.  Precondition: q, k,
- * the state and the residuals M k - v stay below 65504 in magnitude (beyond
- * it the result is Inf/NaN).  z is float32 because the bf16 rounding of the
- * output alone would use most of a 2e-2 max-error/RMS budget.
+ * Linear memory, bfloat16 q, k, v and z (raw bf16 bit patterns, uint16_t per
+ * element), float32 gates and state.  Matrix products run on fp16 MFMA
+ * operands with float32 accumulation: q and k convert to fp16 exactly (fp16
+ * normal range), the state, the residuals and the intra-chunk weights are
+ * rounded to fp16 once per chunk where they enter a product.  z is computed in
+ * float32 and rounded to bf16 (nearest even) when it is stored, so its error
+ * includes up to half a bf16 ulp of each element.  Precondition: q, k, the
+ * state and the residuals M k - v stay below 65504 in magnitude (beyond it
+ * the result is Inf/NaN).
  */
 int ttt_mem_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const float* theta, const float* eta, const float* alpha,
                          const float* M0, const float* S0,
-                         float* z, float* M_T, float* S_T,
+                         uint16_t* z, float* M_T, float* S_T,
                          int B, int H, int T, int d, int b, void* stream);
 
+/* The same computation with z stored as float32 (no output rounding). */
+int ttt_mem_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const float* theta, const float* eta, const float* alpha,
+                              const float* M0, const float* S0,
+                              float* z, float* M_T, float* S_T,
+                              int B, int H, int T, int d, int b, void* stream);
+
 /*
- * Deep (two-layer MLP) memory, bfloat16 q, k, v; float32 gates, weights,
- * momenta and z.  The memory is f(u) = u + SiLU(u W1) W2 in row-vector form
+ * Deep (two-layer MLP) memory, bfloat16 q, k, v and z (rounded to nearest
+ * even from float32); float32 gates, weights and momenta.  The memory is f(u) = u + SiLU(u W1) W2 in row-vector form
  * (W1: d x hidden, W2: hidden x d, no biases), written by gradient steps on
  * 1/2 ||f(k_t) - v_t||^2 taken by explicit backprop at the chunk-start
  * weights; each tensor has its own momentum (S1, S2) and both use the token's
@@ -121,8 +131,16 @@ int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_
                              const float* theta, const float* eta, const float* alpha,
                              const float* W1_0, const float* W2_0,
                              const float* S1_0, const float* S2_0,
-                             float* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T,
+                             uint16_t* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T,
                              int B, int H, int T, int d, int hidden, int b, void* stream);
+
+/* The same computation with z stored as float32. */
+int ttt_mem_mlp_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const float* theta, const float* eta, const float* alpha,
+                                  const float* W1_0, const float* W2_0,
+                                  const float* S1_0, const float* S2_0,
+                                  float* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T,
+                                  int B, int H, int T, int d, int hidden, int b, void* stream);
 
 /*
  * Linear memory over packed variable-length documents: every document starts
@@ -371,7 +389,7 @@ const char* ttt_mem_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ttt_mem_abi_version(void);
 
-#define TTT_MEM_ABI_VERSION ((1 << 16) | 4)
+#define TTT_MEM_ABI_VERSION ((2 << 16) | 0)
 
 #ifdef __cplusplus
 }

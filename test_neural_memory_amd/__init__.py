@@ -7,10 +7,12 @@ binding and the seeded synthetic workloads used by the tests and the bench.
 
 from .memory import (LinearMemoryFunction, backward, backward_varlen, decode, forward, forward_chunk_gates,
                      forward_train, forward_varlen, linear_memory, new_ckpt_varlen,
-                     ttt_mem_decode_bf16, ttt_mem_decode_f32, ttt_mem_forward_bf16, ttt_mem_forward_f32,
+                     ttt_mem_decode_bf16, ttt_mem_decode_f32, ttt_mem_forward_bf16, ttt_mem_forward_bf16_zf32,
+                     ttt_mem_forward_f32,
                      ttt_mem_mlp_forward_bf16)
 
 __all__ = ["LinearMemoryFunction", "backward", "backward_varlen", "decode", "forward", "forward_chunk_gates",
            "forward_train", "forward_varlen", "linear_memory", "new_ckpt_varlen",
-           "ttt_mem_decode_bf16", "ttt_mem_decode_f32", "ttt_mem_forward_bf16", "ttt_mem_forward_f32",
+           "ttt_mem_decode_bf16", "ttt_mem_decode_f32", "ttt_mem_forward_bf16", "ttt_mem_forward_bf16_zf32",
+           "ttt_mem_forward_f32",
            "ttt_mem_mlp_forward_bf16"]

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libttt_mem.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "ttt_mem.h")
 
 _lib = None
+ABI_MAJOR = 2
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -23,7 +24,9 @@ _SIGNATURES = {
     # name: (restype, argtypes) -- mirrors include/ttt_mem.h
     "ttt_mem_forward_f32": (_I, [_P] * 11 + [_I] * 5 + [_P]),
     "ttt_mem_forward_bf16": (_I, [_P] * 11 + [_I] * 5 + [_P]),
+    "ttt_mem_forward_bf16_zf32": (_I, [_P] * 11 + [_I] * 5 + [_P]),
     "ttt_mem_mlp_forward_bf16": (_I, [_P] * 15 + [_I] * 6 + [_P]),
+    "ttt_mem_mlp_forward_bf16_zf32": (_I, [_P] * 15 + [_I] * 6 + [_P]),
     "ttt_mem_forward_varlen_f32": (_I, [_P] * 12 + [_I] * 5 + [_P]),
     "ttt_mem_forward_varlen_bf16": (_I, [_P] * 12 + [_I] * 5 + [_P]),
     "ttt_mem_decode_f32": (_I, [_P] * 11 + [_I] * 4 + [_P]),
@@ -72,8 +75,8 @@ def load() -> ctypes.CDLL:
         fn.restype = res
         fn.argtypes = args
     abi = lib.ttt_mem_abi_version()
-    if abi >> 16 != 1:
-        raise RuntimeError(f"libttt_mem ABI major version {abi >> 16}, expected 1")
+    if abi >> 16 != ABI_MAJOR:
+        raise RuntimeError(f"libttt_mem ABI major version {abi >> 16}, expected {ABI_MAJOR}")
     _lib = lib
     return lib
 

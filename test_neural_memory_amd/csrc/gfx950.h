@@ -17,12 +17,21 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Two floats to two fp16, round to nearest even (one v_cvt_pk_f16_f32).
 __device__ __forceinline__ f16x2 cvt2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, f16x2); }
 __device__ __forceinline__ f16x4 cvt4(f32x4 v) {
     const f16x2 lo = cvt2(v[0], v[1]), hi = cvt2(v[2], v[3]);
     return f16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Four floats to four bf16, round to nearest even (two v_cvt_pk_bf16_f32),
+// packed in two dwords in element order.
+__device__ __forceinline__ u32x2 pack_bf16x4(f32x4 v) {
+    const bf16x2 lo = __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -73,6 +82,17 @@ __device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t of
 __device__ __forceinline__ void buf_store16(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+// Four consecutive elements of an output row: float32 (16 bytes) or, with bf,
+// bf16 rounded to nearest even (8 bytes); off counts elements.  Stores at or
+// past the descriptor's range are dropped.
+__device__ __forceinline__ void store_out4(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off, bool bf) {
+    if (bf) buf_store8(pack_bf16x4(v), r, off * 2);
+    else buf_store16(v, r, off * 4);
 }
 
 __device__ __forceinline__ float readlane(float x, int lane) {

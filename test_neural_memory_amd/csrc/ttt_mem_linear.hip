@@ -156,7 +156,7 @@ struct Params {
     const float* alpha;
     const float* M0;
     const float* S0;
-    float* z;
+    void* z;             // float32, or bf16 bits when z_bf16 (rounded to nearest even)
     float* MT;
     float* ST;
     int BH;
@@ -177,6 +177,7 @@ struct Params {
     // eta, alpha are [B*H][ceil(T/b)] and every token of chunk c uses entry c.
     int chunk_gates;
     int tcmax;   // packed documents: chunk slots per head
+    int z_bf16;  // z element type: 0 float32, 1 bf16
 };
 
 // Compile-time geometry of one kernel instance: NS 16-row tiles per
@@ -784,7 +785,7 @@ struct Kernel {
     // the update of the own columns of M and S.
     __device__ static void phaseB(const StateCtx& x, const Buf& B, const ReadGates& rg, S& sm, f32x4* Macc,
                                   f32x4* Sacc, F* MB, F* SB,
-                                  const f32x4* E, f32x4* Zp, __amdgpu_buffer_rsrc_t rz, uint32_t zcol) {
+                                  const f32x4* E, f32x4* Zp, __amdgpu_buffer_rsrc_t rz, uint32_t zcol, bool zb) {
         // (MB, SB: the own key k-groups, refreshed from the updated state at the end.)
         F EB[NKT];
         if constexpr (CS > 1) {
@@ -805,7 +806,7 @@ struct Kernel {
 #pragma unroll
             for (int s = 0; s < NKT; ++s)
                 if (s <= tt / TPB) Zp[tw] = O::mma(Zp[tw], EB[s], frag_p(B.p, t, s, x.lg));
-            buf_store16(Zp[tw], rz, (static_cast<uint32_t>(t) * D + zcol) * 4);   // rows >= n dropped
+            store_out4(Zp[tw], rz, static_cast<uint32_t>(t) * D + zcol, zb);   // rows >= n dropped
         }
         F WMB[NKT], WSB[NKT];
 #pragma unroll
@@ -965,7 +966,7 @@ struct Kernel {
     // above its diagonal are never written and stay zero.
     template <int BI>
     __device__ static void phaseB2(const Lanes& a, f32x4* Macc, f32x4* Sacc, F* MB, F* SB, f32x4* Zp,
-                                   __amdgpu_buffer_rsrc_t rz, uint32_t zoff) {
+                                   __amdgpu_buffer_rsrc_t rz, uint32_t zoff, bool zb) {
         constexpr uint32_t BO = BI * kBufB;
         f16x4 eb[NT];
 #pragma unroll
@@ -1012,7 +1013,7 @@ struct Kernel {
             WSB[s] = EB[s] * wsf[s];
         }
 #pragma unroll
-        for (int tw = 0; tw < NTW; ++tw) buf_store16(Zp[tw], rz, zoff + 4 * rowoff(tw) * D);   // rows >= n dropped
+        for (int tw = 0; tw < NTW; ++tw) store_out4(Zp[tw], rz, zoff + rowoff(tw) * D, zb);   // rows >= n dropped
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int cw = 0; cw < NCW; ++cw) {
@@ -1252,34 +1253,39 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
         f32x4 E[Gm::NTW], Zp[Gm::NTW];
         K::own_frags(x, sm, Macc, Sacc, MB, SB);
         const uint32_t zcol = row + 4 * lg;
+        // z of chunk c: its n rows of float32 or bf16 (stores past them are dropped).
+        const bool zb = p.z_bf16 != 0;
+        const uint32_t zsz = zb ? 2u : 4u;
+        auto zchunk = [&](int c) {
+            return make_rsrc(static_cast<char*>(p.z) + (seq_tok + static_cast<size_t>(c) * b) * D * zsz,
+                             static_cast<uint32_t>(chunk_n(c)) * D * zsz);
+        };
         if constexpr (NBUF == 2 && Gm::F16 && CS == 2) {
             __syncthreads();   // chunk 0 staged
             __syncthreads();   // chunk 0 decay matrix
             __syncthreads();   // chunk 0 P tiles
             const typename K::Lanes a = K::lanes(x, sm);
-            const uint32_t zoff = opaque((O::tmap(x.chi * Gm::NTW, lr) * D + zcol) * 4);
+            const uint32_t zoff = opaque(O::tmap(x.chi * Gm::NTW, lr) * D + zcol);   // elements
             // Chunk c reads buffer c & 1 and gate slot c & 3.
             for (int c = 0; c < nch; c += 2) {
                 {
-                    const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
-                                              static_cast<uint32_t>(chunk_n(c)) * D * 4);
+                    const auto rz = zchunk(c);
                     const uint32_t gs = a.g + static_cast<uint32_t>(c & 3) * K::kGateB;
                     const uint32_t gsc = lds_addr(&sm.rg[c & 3].scal[0]);
                     save(c);
                     K::template phaseA2<0>(a, gs, gsc, MB, SB, E, Zp, Macc, Sacc);
                     __syncthreads();
-                    K::template phaseB2<0>(a, Macc, Sacc, MB, SB, Zp, rz, zoff);
+                    K::template phaseB2<0>(a, Macc, Sacc, MB, SB, Zp, rz, zoff, zb);
                     __syncthreads();
                 }
                 if (c + 1 < nch) {
-                    const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c + 1) * b) * D,
-                                              static_cast<uint32_t>(chunk_n(c + 1)) * D * 4);
+                    const auto rz = zchunk(c + 1);
                     const uint32_t gs = a.g + static_cast<uint32_t>((c + 1) & 3) * K::kGateB;
                     const uint32_t gsc = lds_addr(&sm.rg[(c + 1) & 3].scal[0]);
                     save(c + 1);
                     K::template phaseA2<1>(a, gs, gsc, MB, SB, E, Zp, Macc, Sacc);
                     __syncthreads();
-                    K::template phaseB2<1>(a, Macc, Sacc, MB, SB, Zp, rz, zoff);
+                    K::template phaseB2<1>(a, Macc, Sacc, MB, SB, Zp, rz, zoff, zb);
                     __syncthreads();
                 }
             }
@@ -1290,13 +1296,12 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
             // Chunk c reads buffer c & 1; the loop is unrolled by two so that
             // every LDS address is a compile-time offset from lane constants.
             auto chunk = [&](int c, const typename K::Buf& B) {
-                const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
-                                          static_cast<uint32_t>(chunk_n(c)) * D * 4);
+                const auto rz = zchunk(c);
                 const typename K::ReadGates& rg = sm.rg[c & 3];
                 save(c);
                 K::phaseA(x, B, rg, sm, MB, SB, E, Zp);
                 __syncthreads();
-                K::phaseB(x, B, rg, sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
+                K::phaseB(x, B, rg, sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol, zb);
                 __syncthreads();
             };
             for (int c = 0; c < nch; c += 2) {
@@ -1308,12 +1313,11 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
                 __syncthreads();   // chunk c staged
                 __syncthreads();   // chunk c decay matrix
                 __syncthreads();   // chunk c P tiles
-                const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * D,
-                                          static_cast<uint32_t>(chunk_n(c)) * D * 4);
+                const auto rz = zchunk(c);
                 save(c);
                 K::phaseA(x, sm.buf[0], sm.rg[c & 3], sm, MB, SB, E, Zp);
                 __syncthreads();
-                K::phaseB(x, sm.buf[0], sm.rg[c & 3], sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol);
+                K::phaseB(x, sm.buf[0], sm.rg[c & 3], sm, Macc, Sacc, MB, SB, E, Zp, rz, zcol, zb);
                 __syncthreads();   // chunk c consumed
             }
         }
@@ -1393,8 +1397,9 @@ hipError_t dispatch(const Params& p, int d, hipStream_t stream) {
 
 template <typename T>
 int forward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
-                 const float* alpha, const float* M0, const float* S0, float* z, float* M_T, float* S_T,
-                 void* ckpt, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false) {
+                 const float* alpha, const float* M0, const float* S0, void* z, float* M_T, float* S_T,
+                 void* ckpt, int B, int H, int Tlen, int d, int b, void* stream, bool chunk_gates = false,
+                 bool z_bf16 = false) {
     using G = typename GlobalOf<T>::type;
     if (B < 0 || H < 0 || Tlen < 0) return TTT_ERR_INVALID_ARG;
     if (b < 1) return TTT_ERR_INVALID_ARG;
@@ -1406,7 +1411,7 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
     if (BH * static_cast<long long>(Tlen) > 0x7fffffffLL) return TTT_ERR_UNSUPPORTED;
     const size_t tok = static_cast<size_t>(BH) * static_cast<size_t>(Tlen);
     const size_t in_bytes = tok * d * sizeof(G);
-    const size_t z_bytes = tok * d * sizeof(float);
+    const size_t z_bytes = tok * d * (z_bf16 ? 2 : sizeof(float));
     const size_t st_bytes = static_cast<size_t>(BH) * d * d * sizeof(float);
     // Gate entries: one per token, or one per chunk.
     const size_t g_count = chunk_gates ? static_cast<size_t>(BH) * ((static_cast<size_t>(Tlen) + b - 1) / b) : tok;
@@ -1449,7 +1454,7 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
     }
 
     Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, nullptr, H, ckpt,
-             chunk_gates ? 1 : 0, 0};
+             chunk_gates ? 1 : 0, 0, z_bf16 ? 1 : 0};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1513,7 +1518,7 @@ int forward_varlen_impl(const void* q, const void* k, const void* v, const float
     }
 
     Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H, ckpt, 0,
-             static_cast<int>(tcmax)};
+             static_cast<int>(tcmax), 0};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1529,8 +1534,15 @@ int ttt_mem_forward_f32(const float* q, const float* k, const float* v, const fl
 }
 
 int ttt_mem_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
-                         const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
+                         const float* eta, const float* alpha, const float* M0, const float* S0, uint16_t* z,
                          float* M_T, float* S_T, int B, int H, int T, int d, int b, void* stream) {
+    return forward_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, nullptr, B, H, T, d, b, stream,
+                                  false, true);
+}
+
+int ttt_mem_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                              const float* eta, const float* alpha, const float* M0, const float* S0, float* z,
+                              float* M_T, float* S_T, int B, int H, int T, int d, int b, void* stream) {
     return forward_impl<_Float16>(q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, nullptr, B, H, T, d, b, stream);
 }
 

@@ -161,13 +161,14 @@ struct MlpParams {
     const float* W2;
     const float* S1;
     const float* S2;
-    float* z;
+    void* z;      // float32, or bf16 bits (rounded to nearest even) when z_bf16
     float* W1T;
     float* W2T;
     float* S1T;
     float* S2T;
     int T;
     int b;
+    int z_bf16;
 };
 
 // One chunk of staged inputs and its gate quantities (double-buffered).
@@ -521,7 +522,10 @@ __global__ __launch_bounds__(kThreads) void mlp_memory_fwd(const MlpParams p) {
         __syncthreads();
 
         // ================= phase 4 =================
-        const auto rz = make_rsrc(p.z + (seq_tok + static_cast<size_t>(c) * b) * kD, static_cast<uint32_t>(n) * kD * 4);
+        const bool zb = p.z_bf16 != 0;
+        const uint32_t zsz = zb ? 2u : 4u;
+        const auto rz = make_rsrc(static_cast<char*>(p.z) + (seq_tok + static_cast<size_t>(c) * b) * kD * zsz,
+                                  static_cast<uint32_t>(n) * kD * zsz);
         if (w < kDT) {
             // z^T tile dt = w [d x t] = Q^T + sum of partial Z^T + R^T (-(L .* Aq Ak^T))^T.
             const int dt = w;
@@ -541,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void mlp_memory_fwd(const MlpParams p) {
             const int t = lr, d0 = 16 * dt + 4 * lg;
             const f16x4 q4 = *reinterpret_cast<const f16x4*>(B.qh + t * kLK + d0);
             zt += to_f32(q4);
-            buf_store16(zt, rz, static_cast<uint32_t>(t * kD + d0) * 4);
+            store_out4(zt, rz, static_cast<uint32_t>(t * kD + d0), zb);
         }
         if (c + 1 < nch) {
             ChunkBuf& Bn = sm.buf[(c + 1) & 1];
@@ -578,8 +582,8 @@ __global__ __launch_bounds__(kThreads) void mlp_memory_fwd(const MlpParams p) {
 
 int mlp_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta, const float* eta,
                      const float* alpha, const float* W1_0, const float* W2_0, const float* S1_0, const float* S2_0,
-                     float* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T, int B, int H, int Tlen, int d,
-                     int hidden, int b, void* stream) {
+                     void* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T, int B, int H, int Tlen, int d,
+                     int hidden, int b, void* stream, bool z_bf16) {
     if (B < 0 || H < 0 || Tlen < 0 || b < 1) return TTT_ERR_INVALID_ARG;
     if (d != kD || hidden != kHid || b > kNP) return TTT_ERR_UNSUPPORTED;
     const long long BH = static_cast<long long>(B) * H;
@@ -587,7 +591,7 @@ int mlp_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
     if (BH > 0x7fffffffLL || BH * static_cast<long long>(Tlen) > 0x7fffffffLL) return TTT_ERR_UNSUPPORTED;
     if (!W1_0 || !W2_0) return TTT_ERR_INVALID_ARG;
     const size_t tok = static_cast<size_t>(BH) * static_cast<size_t>(Tlen);
-    const size_t in_bytes = tok * kD * 2, z_bytes = tok * kD * 4;
+    const size_t in_bytes = tok * kD * 2, z_bytes = tok * kD * (z_bf16 ? 2 : 4);
     const size_t w_bytes = static_cast<size_t>(BH) * kD * kHid * 4;
     if (Tlen > 0) {
         if (!q || !k || !v || !theta || !eta || !alpha || !z) return TTT_ERR_INVALID_ARG;
@@ -618,7 +622,7 @@ int mlp_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
                 return TTT_ERR_INVALID_ARG;
         }
     }
-    MlpParams p{q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0, S2_0, z, W1_T, W2_T, S1_T, S2_T, Tlen, b};
+    MlpParams p{q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0, S2_0, z, W1_T, W2_T, S1_T, S2_T, Tlen, b, z_bf16 ? 1 : 0};
     hipLaunchKernelGGL(mlp_memory_fwd, dim3(static_cast<unsigned>(BH)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), p);
     return hipGetLastError() == hipSuccess ? TTT_OK : TTT_ERR_HIP;
@@ -628,9 +632,19 @@ int mlp_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
 
 extern "C" int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
                                         const float* eta, const float* alpha, const float* W1_0, const float* W2_0,
-                                        const float* S1_0, const float* S2_0, float* z, float* W1_T, float* W2_T,
+                                        const float* S1_0, const float* S2_0, uint16_t* z, float* W1_T, float* W2_T,
                                         float* S1_T, float* S2_T, int B, int H, int T, int d, int hidden, int b,
                                         void* stream) {
     return mlp_forward_impl(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0, S2_0, z, W1_T, W2_T, S1_T, S2_T, B, H, T, d,
-                            hidden, b, stream);
+                            hidden, b, stream, true);
+}
+
+extern "C" int ttt_mem_mlp_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                             const float* theta, const float* eta, const float* alpha,
+                                             const float* W1_0, const float* W2_0, const float* S1_0,
+                                             const float* S2_0, float* z, float* W1_T, float* W2_T, float* S1_T,
+                                             float* S2_T, int B, int H, int T, int d, int hidden, int b,
+                                             void* stream) {
+    return mlp_forward_impl(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0, S2_0, z, W1_T, W2_T, S1_T, S2_T, B, H, T, d,
+                            hidden, b, stream, false);
 }

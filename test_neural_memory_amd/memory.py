@@ -31,7 +31,7 @@ def _as_dev(t, name, dtype, shape, device):
 
 
 def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=True, extra=None,
-             gate_len=None, pass_extra=False):
+             gate_len=None, pass_extra=False, z_dtype=torch.float32):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
     B, H, T, d = q.shape
@@ -48,15 +48,16 @@ def _forward(name, in_dtype, q, k, v, theta, eta, alpha, M0, S0, b, out, with_b=
     M0 = _as_dev(M0, "M0", torch.float32, (B, H, d, d), dev)
     S0 = _as_dev(S0, "S0", torch.float32, (B, H, d, d), dev)
     if out is None:
-        z = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+        z = torch.empty((B, H, T, d), dtype=z_dtype, device=dev)
         M_T = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
         S_T = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     else:
         z, M_T, S_T = out
-        for t, nm, shp in ((z, "z", (B, H, T, d)), (M_T, "M_T", (B, H, d, d)), (S_T, "S_T", (B, H, d, d))):
-            if t is not None and (not t.is_contiguous() or t.dtype != torch.float32
+        for t, nm, shp, dt in ((z, "z", (B, H, T, d), z_dtype), (M_T, "M_T", (B, H, d, d), torch.float32),
+                               (S_T, "S_T", (B, H, d, d), torch.float32)):
+            if t is not None and (not t.is_contiguous() or t.dtype != dt
                                   or tuple(t.shape) != shp or t.device != dev):
-                raise ValueError(f"out tensor {nm} must be contiguous float32 {shp} on {dev}")
+                raise ValueError(f"out tensor {nm} must be contiguous {dt} {shp} on {dev}")
     lib = _lib.load()
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
@@ -76,16 +77,32 @@ def ttt_mem_forward_f32(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=
 
 
 def ttt_mem_forward_bf16(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
-    """bf16-input linear memory (float32 state and z); returns ``(z, M_T, S_T)``."""
-    return _forward("ttt_mem_forward_bf16", torch.bfloat16, q, k, v, theta, eta, alpha, M0, S0, b, out)
+    """bf16-input linear memory: bf16 z, float32 state; returns ``(z, M_T, S_T)``."""
+    return _forward("ttt_mem_forward_bf16", torch.bfloat16, q, k, v, theta, eta, alpha, M0, S0, b, out,
+                    z_dtype=torch.bfloat16)
 
 
-def forward(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
-    """Dispatch on the input dtype (float32 or bfloat16)."""
+def ttt_mem_forward_bf16_zf32(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None):
+    """bf16-input linear memory with float32 z (and state); returns ``(z, M_T, S_T)``."""
+    return _forward("ttt_mem_forward_bf16_zf32", torch.bfloat16, q, k, v, theta, eta, alpha, M0, S0, b, out)
+
+
+def forward(q, k, v, theta, eta, alpha, M0=None, S0=None, *, b, out=None, z_dtype=None):
+    """Dispatch on the input dtype (float32 or bfloat16).
+
+    z has the input dtype unless ``z_dtype=torch.float32`` asks for float32 z
+    from bf16 inputs.
+    """
     if q.dtype == torch.float32:
+        if z_dtype not in (None, torch.float32):
+            raise TypeError("float32 inputs give float32 z")
         return ttt_mem_forward_f32(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
     if q.dtype == torch.bfloat16:
-        return ttt_mem_forward_bf16(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
+        if z_dtype in (None, torch.bfloat16):
+            return ttt_mem_forward_bf16(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
+        if z_dtype == torch.float32:
+            return ttt_mem_forward_bf16_zf32(q, k, v, theta, eta, alpha, M0, S0, b=b, out=out)
+        raise TypeError(f"unsupported z dtype {z_dtype}")
     raise TypeError(f"unsupported input dtype {q.dtype}")
 
 
@@ -413,13 +430,20 @@ def decode(q, k, v, theta, eta, alpha, M0=None, S0=None, *, out=None):
     raise TypeError(f"unsupported input dtype {q.dtype}")
 
 
-def ttt_mem_mlp_forward_bf16(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0=None, S2_0=None, *, b, out=None):
+def ttt_mem_mlp_forward_bf16(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0=None, S2_0=None, *, b, out=None,
+                             z_dtype=torch.bfloat16):
     """bf16-input deep (2-layer MLP) memory; returns ``(z, W1_T, W2_T, S1_T, S2_T)``.
 
     ``W1_0, S1_0`` are ``[B, H, d, hidden]`` and ``W2_0, S2_0`` ``[B, H, hidden, d]``
-    float32; ``out`` may pass preallocated ``(z, W1_T, W2_T, S1_T, S2_T)``.
+    float32; z is bf16 (``z_dtype=torch.float32`` for float32 z); ``out`` may
+    pass preallocated ``(z, W1_T, W2_T, S1_T, S2_T)``.
     """
-    name = "ttt_mem_mlp_forward_bf16"
+    if z_dtype == torch.bfloat16:
+        name = "ttt_mem_mlp_forward_bf16"
+    elif z_dtype == torch.float32:
+        name = "ttt_mem_mlp_forward_bf16_zf32"
+    else:
+        raise TypeError(f"unsupported z dtype {z_dtype}")
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
     B, H, T, d = q.shape
@@ -440,18 +464,19 @@ def ttt_mem_mlp_forward_bf16(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0=None, 
     S1_0 = _as_dev(S1_0, "S1_0", torch.float32, (B, H, d, hid), dev)
     S2_0 = _as_dev(S2_0, "S2_0", torch.float32, (B, H, hid, d), dev)
     shapes = ((B, H, T, d), (B, H, d, hid), (B, H, hid, d), (B, H, d, hid), (B, H, hid, d))
+    dts = (z_dtype,) + (torch.float32,) * 4
     if out is None:
-        out = tuple(torch.empty(s, dtype=torch.float32, device=dev) for s in shapes)
+        out = tuple(torch.empty(s, dtype=dt, device=dev) for s, dt in zip(shapes, dts))
     else:
-        for t, nm, shp in zip(out, ("z", "W1_T", "W2_T", "S1_T", "S2_T"), shapes):
-            if t is not None and (not t.is_contiguous() or t.dtype != torch.float32
+        for t, nm, shp, dt in zip(out, ("z", "W1_T", "W2_T", "S1_T", "S2_T"), shapes, dts):
+            if t is not None and (not t.is_contiguous() or t.dtype != dt
                                   or tuple(t.shape) != shp or t.device != dev):
-                raise ValueError(f"out tensor {nm} must be contiguous float32 {shp} on {dev}")
+                raise ValueError(f"out tensor {nm} must be contiguous {dt} {shp} on {dev}")
     z, W1_T, W2_T, S1_T, S2_T = out
     lib = _lib.load()
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
-        status = lib.ttt_mem_mlp_forward_bf16(
+        status = getattr(lib, name)(
             _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(W1_0), _ptr(W2_0),
             _ptr(S1_0), _ptr(S2_0), _ptr(z), _ptr(W1_T), _ptr(W2_T), _ptr(S1_T), _ptr(S2_T),
             B, H, T, d, int(hid), int(b), stream)

@@ -27,12 +27,16 @@ def to_dev(inp, device="cuda"):
     return {k: (None if v is None else v.to(device)) for k, v in inp.items()}
 
 
-def run_gpu(inp, b, **kw):
-    """Linear memory on the GPU; returns float64 numpy (z, M_T, S_T)."""
+def run_gpu(inp, b, raw=False, **kw):
+    """Linear memory on the GPU; returns float64 numpy (z, M_T, S_T), or the
+    device tensors themselves with ``raw``.  z is bf16 for bf16 inputs unless
+    ``z_dtype=torch.float32`` is passed."""
     dev = to_dev(inp)
     z, M, S = tm.forward(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"],
                          dev.get("M0"), dev.get("S0"), b=b, **kw)
     torch.cuda.synchronize()
+    if raw:
+        return z, M, S
     return to_numpy64(z.cpu()), to_numpy64(M.cpu()), to_numpy64(S.cpu())
 
 

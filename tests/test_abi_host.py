@@ -14,14 +14,15 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
-    assert {"ttt_mem_forward_f32", "ttt_mem_forward_bf16", "ttt_mem_status_string",
-            "ttt_mem_abi_version"} <= set(names)
+    assert {"ttt_mem_forward_f32", "ttt_mem_forward_bf16", "ttt_mem_forward_bf16_zf32", "ttt_mem_mlp_forward_bf16",
+            "ttt_mem_mlp_forward_bf16_zf32", "ttt_mem_status_string", "ttt_mem_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ttt_mem_abi_version() == (1 << 16) | 4
+    assert lib.ttt_mem_abi_version() == (2 << 16) | 0
+    assert lib.ttt_mem_abi_version() >> 16 == _lib.ABI_MAJOR
     assert lib.ttt_mem_status_string(0) == b"ok"
     for s in (-1, -2, -3, 12345):
         assert lib.ttt_mem_status_string(s)
@@ -32,7 +33,7 @@ def _call(lib, name, ptrs=None, B=1, H=1, T=8, d=16, b=4):
     return getattr(lib, name)(*p, B, H, T, d, b, None)
 
 
-@pytest.mark.parametrize("name", ["ttt_mem_forward_f32", "ttt_mem_forward_bf16"])
+@pytest.mark.parametrize("name", ["ttt_mem_forward_f32", "ttt_mem_forward_bf16", "ttt_mem_forward_bf16_zf32"])
 def test_rejections_happen_before_any_launch(lib, name):
     # NULL required pointers, bad sizes: every one returns before touching HIP.
     assert _call(lib, name) == -1                    # NULL q, k, v, ...
@@ -49,10 +50,21 @@ def test_rejections_happen_before_any_launch(lib, name):
     assert _call(lib, name, ptrs=fake) == -1
 
 
-@pytest.mark.parametrize("name", ["ttt_mem_forward_f32", "ttt_mem_forward_bf16"])
+@pytest.mark.parametrize("name", ["ttt_mem_forward_f32", "ttt_mem_forward_bf16", "ttt_mem_forward_bf16_zf32"])
 def test_empty_batch_returns_ok_without_pointers(lib, name):
     assert _call(lib, name, B=0) == 0
     assert _call(lib, name, H=0) == 0
+
+
+def test_mlp_rejections_happen_before_any_launch(lib):
+    for name in ("ttt_mem_mlp_forward_bf16", "ttt_mem_mlp_forward_bf16_zf32"):
+        def call(B=1, H=1, T=8, d=64, hid=256, b=4):
+            return getattr(lib, name)(*([None] * 15), B, H, T, d, hid, b, None)
+        assert call() == -1                 # NULL weights
+        assert call(d=32) == -2
+        assert call(hid=128) == -2
+        assert call(b=17) == -2
+        assert call(B=0) == 0
 
 
 def test_ckpt_bytes(lib):

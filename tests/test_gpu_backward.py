@@ -127,9 +127,12 @@ def test_checkpoints_are_the_chunk_start_states(dtype):
     args = (inp["q"], inp["k"], inp["v"], inp["theta"], inp["eta"], inp["alpha"])
     b = 64
     z, M, S, ckpt = tm.forward_train(*args, inp["M0"], inp["S0"], b=b)
-    z0, M0, S0 = tm.forward(*args, inp["M0"], inp["S0"], b=b)
+    z0, M0, S0 = tm.forward(*args, inp["M0"], inp["S0"], b=b, z_dtype=torch.float32)
+    zb, _, _ = tm.forward(*args, inp["M0"], inp["S0"], b=b)
     torch.cuda.synchronize()
     assert torch.equal(z, z0) and torch.equal(M, M0) and torch.equal(S, S0)
+    # bf16 inputs: the default z is the same float32 z rounded to nearest even.
+    assert torch.equal(zb, z0.to(zb.dtype))
     # float32 inputs: the states; bf16 inputs: the states rounded to fp16 (nearest even).
     cast = (lambda x: x) if dtype == "f32" else (lambda x: x.half())  # noqa: E731
     assert torch.equal(ckpt[:, :, 0, 0], cast(inp["M0"])) and torch.equal(ckpt[:, :, 0, 1], cast(inp["S0"]))

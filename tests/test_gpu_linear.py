@@ -21,9 +21,9 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _check_all(inp, b, tol, heads=None, rows=None):
-    z, M, S = run_gpu(inp, b)
-    zo, Mo, So = run_oracle(inp, b, heads, rows)
+def _check_all(inp, b, tol, heads=None, rows=None, ref=None, **kw):
+    z, M, S = run_gpu(inp, b, **kw)
+    zo, Mo, So = run_oracle(inp, b, heads, rows) if ref is None else ref
     d = inp["q"].shape[-1]
     if heads is None:
         B, H = inp["q"].shape[:2]
@@ -70,11 +70,28 @@ FULL = [
 @pytest.mark.parametrize("wid,heads,rows", FULL, ids=[f"workload{f[0]}" for f in FULL])
 def test_full_size_sampled(wid, heads, rows):
     # Full shapes in the bench's launch configuration; the oracle checks sampled
-    # (batch, head) pairs and value rows (rows are independent problems).
+    # (batch, head) pairs and value rows (rows are independent problems).  Both
+    # z forms: bf16 z (the entry point the bench times) and float32 z.
     w = WORKLOADS[wid]
-    _say(f"case full {w.name}")
+    _say(f"case full {w.name} (bf16 z, then float32 z)")
     inp = make_inputs(w)
-    _check_all(inp, w.b, TOL[w.dtype], heads=heads, rows=rows)
+    ref = run_oracle(inp, w.b, heads, rows)
+    _check_all(inp, w.b, TOL[w.dtype], heads=heads, rows=rows, ref=ref)
+    _check_all(inp, w.b, TOL[w.dtype], heads=heads, rows=rows, ref=ref, z_dtype=torch.float32)
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4])
+def test_full_size_bf16_z_is_rounded_f32_z(wid):
+    # Over the whole output: the bf16 z is the float32 z rounded to nearest
+    # even, element for element, and the final states are the same floats.
+    w = WORKLOADS[wid]
+    _say(f"case full {w.name}: bf16 z == RNE(float32 z)")
+    inp = make_inputs(w)
+    zb, Mb, Sb = run_gpu(inp, w.b, raw=True)
+    zf, Mf, Sf = run_gpu(inp, w.b, raw=True, z_dtype=torch.float32)
+    assert zb.dtype == torch.bfloat16 and zf.dtype == torch.float32
+    assert torch.equal(zb, zf.to(torch.bfloat16))
+    assert torch.equal(Mb, Mf) and torch.equal(Sb, Sf)
 
 
 EDGE = [

@@ -43,9 +43,9 @@ def run_oracle(inp, b, heads=None):
                        g.get("S1"), g.get("S2"), b=b)
 
 
-def _check(inp, b, heads=None, tol=TOL_MLP):
-    got = run_gpu(inp, b)
-    ref = run_oracle(inp, b, heads)
+def _check(inp, b, heads=None, tol=TOL_MLP, ref=None, **kw):
+    got = run_gpu(inp, b, **kw)
+    ref = run_oracle(inp, b, heads) if ref is None else ref
     if heads is None:
         got = [x.reshape((-1,) + x.shape[2:]) for x in got]   # (batch, head) pairs in row-major order
     else:
@@ -134,11 +134,22 @@ def test_theta0_is_plain_read():
 
 
 def test_full_size_sampled():
-    # The deep-memory workload at full size; the oracle checks two sequences.
+    # The deep-memory workload at full size; the oracle checks two sequences,
+    # for bf16 z and for float32 z; over the whole output the bf16 z is the
+    # float32 z rounded to nearest even.
     w = WORKLOADS[5]
     _say(f"case full size {w}")
     inp = make_inputs(w)
-    _check(inp, w.b, heads=[(0, 0), (w.B - 1, w.H - 1)])
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    ref = run_oracle(inp, w.b, heads)
+    _check(inp, w.b, heads=heads, ref=ref)
+    _check(inp, w.b, heads=heads, ref=ref, z_dtype=torch.float32)
+    dev = to_dev(inp)
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"], dev["W1"], dev["W2"])
+    zb = tm.ttt_mem_mlp_forward_bf16(*args, b=w.b)[0]
+    zf = tm.ttt_mem_mlp_forward_bf16(*args, b=w.b, z_dtype=torch.float32)[0]
+    torch.cuda.synchronize()
+    assert zb.dtype == torch.bfloat16 and torch.equal(zb, zf.to(torch.bfloat16))
 
 
 def test_empty_sequence_copies_weights():

@@ -104,7 +104,8 @@ def test_varlen_equals_dense_bitwise():
     w = WORKLOADS[3].replace(B=3, H=2, T=150)
     inp = make_inputs(w)
     dense = {k: v.cuda() for k, v in inp.items() if v is not None}
-    zd, Md, Sd = tm.forward(dense["q"], dense["k"], dense["v"], dense["theta"], dense["eta"], dense["alpha"], b=64)
+    zd, Md, Sd = tm.forward(dense["q"], dense["k"], dense["v"], dense["theta"], dense["eta"], dense["alpha"], b=64,
+                            z_dtype=torch.float32)
     pack = {k: v.transpose(0, 1).reshape(w.H, w.B * w.T, *v.shape[3:]).contiguous() for k, v in dense.items()}
     cu = torch.arange(0, (w.B + 1) * w.T, w.T, dtype=torch.int32, device="cuda")
     zp, Mp, Sp = tm.forward_varlen(pack["q"], pack["k"], pack["v"], pack["theta"], pack["eta"], pack["alpha"], cu,
