@@ -27,13 +27,19 @@ What it computes, in the pages' own order (a per-token loop, float64):
   torch.autograd (a library routine), finite differences, and by agreement of
   an autograd-driven generic loop whose linear instance is pinned by the
   worked examples.
+* ``deep_forward`` -- the same schedule for a deep memory of any depth
+  L >= 2, ``f(u) = u + SiLU(...SiLU(u W_1)...) W_L``, with its own explicit
+  backprop (``deep_chunk_grads``).  Pinned by torch.autograd and finite
+  differences at depths 2-4, by the generic autograd loop at depths 2-4, by
+  agreement with ``mlp_forward`` at depth 2, and by the plain read (no
+  update) at theta = eta = alpha = 0.
 
 Every function here is pinned by tests in ``tests/test_oracle_*.py``; none is
 "parity unpinned".
 """
 
-from .memory import (linear_backward, linear_backward_chunk_gates, linear_forward, linear_forward_chunk_gates,
-                     mlp_forward, silu, silu_grad, mlp_chunk_grads)
+from .memory import (deep_chunk_grads, deep_forward, linear_backward, linear_backward_chunk_gates, linear_forward,
+                     linear_forward_chunk_gates, mlp_chunk_grads, mlp_forward, silu, silu_grad)
 
 __all__ = ["linear_forward", "linear_backward", "linear_forward_chunk_gates", "linear_backward_chunk_gates",
-           "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]
+           "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads", "deep_forward", "deep_chunk_grads"]

@@ -34,7 +34,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["linear_forward", "linear_backward", "linear_forward_chunk_gates", "linear_backward_chunk_gates",
-           "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads"]
+           "mlp_forward", "silu", "silu_grad", "mlp_chunk_grads", "deep_forward", "deep_chunk_grads"]
 
 
 def _f64(x):
@@ -305,3 +305,80 @@ def mlp_forward(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0=None, S2_0=None, b=
             W2 = (1.0 - al) * W2 + S2
             z[..., t, :] = _mlp_apply(q[..., t, :], W1, W2)
     return z, W1, W2, S1, S2
+
+
+def _deep_apply(u, Ws):
+    """Deep memory read with L = len(Ws) >= 2 layers, row-vector form:
+    ``f(u) = u + SiLU(...SiLU(SiLU(u W_1) W_2)...) W_L``."""
+    x = u
+    for W in Ws[:-1]:
+        x = silu(np.matmul(x[..., None, :], W)[..., 0, :])
+    return u + np.matmul(x[..., None, :], Ws[-1])[..., 0, :]
+
+
+def deep_chunk_grads(k, v, Ws):
+    """Gradients of ``1/2 ||f(k) - v||^2`` w.r.t. every layer of the L-layer memory.
+
+    Explicit backprop through ``f(u) = u + SiLU(...SiLU(u W_1)...) W_L`` for one
+    key/value pair per leading index.  Forward: ``x_0 = k``, ``h_l = x_{l-1} W_l``
+    and ``x_l = SiLU(h_l)`` for l < L, ``r = k + x_{L-1} W_L - v``.  Backward:
+    ``delta_L = r``, ``dL/dW_L = x_{L-1}^T r``, and for l = L-1 .. 1
+    ``delta_l = (delta_{l+1} W_{l+1}^T) * SiLU'(h_l)``, ``dL/dW_l = x_{l-1}^T delta_l``.
+    """
+    L = len(Ws)
+    xs, hs = [k], []
+    for W in Ws[:-1]:
+        h = np.matmul(xs[-1][..., None, :], W)[..., 0, :]
+        hs.append(h)
+        xs.append(silu(h))
+    r = k + np.matmul(xs[-1][..., None, :], Ws[-1])[..., 0, :] - v
+    grads = [None] * L
+    delta = r
+    grads[L - 1] = _outer(xs[L - 1], delta)
+    for l in range(L - 2, -1, -1):
+        back = np.matmul(delta[..., None, :], np.swapaxes(Ws[l + 1], -1, -2))[..., 0, :]
+        delta = back * silu_grad(hs[l])
+        grads[l] = _outer(xs[l], delta)
+    return grads
+
+
+def deep_forward(q, k, v, theta, eta, alpha, Ws0, Ss0=None, b=1):
+    """Deep memory of depth L = len(Ws0) >= 2 with the chunked schedule of ``linear_forward``.
+
+    "论文速览 | Titans" section 3.9: a deep memory is a stack of L linear maps
+    with a nonlinearity between them; section 8.5 compares depths 1 to 4.
+    Here, in row-vector form with the residual and no biases of the 2-layer
+    memory (``mlp_forward``): ``f(u) = u + SiLU(...SiLU(u W_1)...) W_L`` with
+    ``W_1 [d, hid]``, ``W_l [hid, hid]`` for 1 < l < L, ``W_L [hid, d]``.
+    Every layer has its own momentum; all use the token's ``theta, eta, alpha``;
+    every gradient of a chunk is taken at the chunk-start weights and the read
+    ``z_t = f(q_t)`` uses the weights after token t's own write.
+
+    ``Ws0``, ``Ss0``: lists of L arrays (leading dimensions broadcast);
+    ``Ss0=None`` means zero momenta.  Returns ``(z, Ws_T, Ss_T)``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    theta, eta, alpha = _f64(theta), _f64(eta), _f64(alpha)
+    if b < 1:
+        raise ValueError("chunk size b must be >= 1")
+    if len(Ws0) < 2:
+        raise ValueError("a deep memory has at least two layers")
+    lead, T, d = q.shape[:-2], q.shape[-2], q.shape[-1]
+    Ws = [np.array(np.broadcast_to(_f64(W), lead + np.shape(W)[-2:])) for W in Ws0]
+    if Ss0 is None:
+        Ss = [np.zeros_like(W) for W in Ws]
+    else:
+        Ss = [np.zeros_like(W) if S is None else np.array(np.broadcast_to(_f64(S), W.shape))
+              for S, W in zip(Ss0, Ws)]
+    z = np.zeros(lead + (T, d))
+    for c0 in range(0, T, b):
+        Wc = [W.copy() for W in Ws]                 # chunk-start weights
+        for t in range(c0, min(c0 + b, T)):
+            Gs = deep_chunk_grads(k[..., t, :], v[..., t, :], Wc)
+            th = theta[..., t][..., None, None]
+            et = eta[..., t][..., None, None]
+            al = alpha[..., t][..., None, None]
+            Ss = [et * S - th * G for S, G in zip(Ss, Gs)]
+            Ws = [(1.0 - al) * W + S for W, S in zip(Ws, Ss)]
+            z[..., t, :] = _deep_apply(q[..., t, :], Ws)
+    return z, Ws, Ss
