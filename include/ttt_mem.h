@@ -26,9 +26,11 @@
  * Conventions shared by every entry point:
  *
  *   - All data pointers are DEVICE pointers on the current HIP device, owned
- *     by the caller.  The library allocates nothing and keeps no state, so
- *     calls are re-entrant; they are enqueued asynchronously on `stream`
- *     (a hipStream_t passed as void*, NULL = the default stream).
+ *     by the caller.  The library keeps no state, so calls are re-entrant;
+ *     they are enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*, NULL = the default stream).  It allocates nothing, except the
+ *     deep-memory entry points when they are given no workspace (they then
+ *     take one from the stream-ordered allocator on `stream`).
  *   - Layouts are dense row-major:
  *       q, k, v           [B, H, T, d]   (token rows, d contiguous)
  *       theta, eta, alpha [B, H, T]      float32
@@ -67,7 +69,8 @@ enum ttt_status {
     TTT_OK = 0,
     TTT_ERR_INVALID_ARG = -1, /* bad size, NULL required pointer, misalignment, aliasing */
     TTT_ERR_UNSUPPORTED = -2, /* valid request outside what the kernels implement (d, b, hidden) */
-    TTT_ERR_HIP = -3          /* the HIP runtime rejected a launch */
+    TTT_ERR_HIP = -3,         /* the HIP runtime rejected a launch */
+    TTT_ERR_DEVICE = -4       /* a deep-memory launch reported a failure on the device (ttt_mem_deep_status) */
 };
 
 /*
@@ -106,14 +109,15 @@ int ttt_mem_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const uint16
 
 /*
  * Deep (two-layer MLP) memory, bfloat16 q, k, v and z (rounded to nearest
- * even from float32); float32 gates, weights and momenta.  The memory is f(u) = u + SiLU(u W1) W2 in row-vector form
- * (W1: d x hidden, W2: hidden x d, no biases), written by gradient steps on
- * 1/2 ||f(k_t) - v_t||^2 taken by explicit backprop at the chunk-start
- * weights; each tensor has its own momentum (S1, S2) and both use the token's
- * theta, eta, alpha with the same recurrences as the linear memory
- * ("论文速览 | Titans", sections 3.4, 3.7, 3.9 and 4.2; "Continual Learning:
- * From Attention to Neural Memory", sections 4.2 and 5.1-5.2).  The read is
- * z_t = f(q_t) with the weights after token t's own write.
+ * even from float32); float32 gates, weights and momenta.  The memory is
+ * f(u) = u + SiLU(u W1) W2 in row-vector form (W1: d x hidden, W2: hidden x d,
+ * no biases), written by gradient steps on 1/2 ||f(k_t) - v_t||^2 taken by
+ * explicit backprop at the chunk-start weights; each tensor has its own
+ * momentum (S1, S2) and both use the token's theta, eta, alpha with the same
+ * recurrences as the linear memory ("论文速览 | Titans", sections 3.4, 3.7,
+ * 3.9 and 4.2; "Continual Learning: From Attention to Neural Memory",
+ * sections 4.2 and 5.1-5.2).  The read is z_t = f(q_t) with the weights after
+ * token t's own write.
  *
  *   Layouts: q, k, v, z [B, H, T, d] as above; W1_0, S1_0, W1_T, S1_T
  *   [B, H, d, hidden] and W2_0, S2_0, W2_T, S2_T [B, H, hidden, d], float32
@@ -123,9 +127,16 @@ int ttt_mem_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const uint16
  *   tensor (in-place carry).  Pointers to the weights must be 4-byte aligned;
  *   q, k, v, z 16-byte aligned.
  *   Sizes: d = 64 and hidden = 256, 1 <= b <= 16 (other sizes return
- *   TTT_ERR_UNSUPPORTED).  Matrix products use fp16 operands with float32
- *   accumulation (same precondition as ttt_mem_forward_bf16); SiLU uses the
- *   hardware exp2 and reciprocal.
+ *   TTT_ERR_UNSUPPORTED).
+ *   Precision: matrix products on bf16 operands with float32 accumulation;
+ *   every float32 operand is split into two bf16 parts (about 16 significant
+ *   bits); SiLU uses the hardware exp2 and reciprocal.
+ *   Execution: the hidden units are split over a group of 8 workgroups per
+ *   (batch, head), which exchange partial products once per chunk through a
+ *   workspace in device memory (see ttt_mem_deep_forward_bf16).  This entry
+ *   point takes that workspace from the stream-ordered allocator of the
+ *   call's device (hipMallocAsync / hipFreeAsync on `stream`); use
+ *   ttt_mem_deep_forward_bf16 to pass one and to read the device status.
  */
 int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const float* theta, const float* eta, const float* alpha,
@@ -141,6 +152,40 @@ int ttt_mem_mlp_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const ui
                                   const float* S1_0, const float* S2_0,
                                   float* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T,
                                   int B, int H, int T, int d, int hidden, int b, void* stream);
+
+/*
+ * Deep memory of depth L = `depth` ("论文速览 | Titans", section 3.9: L linear
+ * maps with a nonlinearity between them; section 8.5 compares depths 1-4):
+ * f(u) = u + SiLU(...SiLU(u W_1)...) W_L in row-vector form, W_1: d x hidden,
+ * W_l: hidden x hidden (1 < l < L), W_L: hidden x d, every layer with its own
+ * momentum, trained exactly as the two-layer memory above (which is depth 2).
+ *
+ *   Parameters are packed per (batch, head): W0, S0, W_T, S_T are
+ *   [B, H, P] float32 with P = ttt_mem_deep_param_count(d, hidden, depth);
+ *   layer 1 starts at 0, layer l (1 < l <= L) at d*hidden + (l-2)*hidden*hidden,
+ *   each row-major as above.  W0 is required; S0 may be NULL (zeros); W_T and
+ *   S_T may be NULL or equal W0 / S0 (in-place carry).
+ *   work: a caller-owned workspace of at least
+ *   ttt_mem_deep_work_bytes(B, H, d, hidden, depth) bytes, 256-byte aligned
+ *   (NULL: taken from the stream-ordered allocator as above).  Calls that
+ *   share a workspace must not overlap in time.  The workgroups of a group
+ *   exchange through it and wait for each other with bounded waits: a wait
+ *   that runs out, or a workgroup that finds no place in a group of its XCD,
+ *   records a failure in the workspace instead of hanging; the results are
+ *   then undefined.  ttt_mem_deep_status(work, stream) synchronizes `stream`
+ *   and returns TTT_OK, or TTT_ERR_DEVICE if the last launch on `work`
+ *   recorded a failure.
+ *   Sizes: d = 64, hidden = 256, depth in {2, 3, 4}, 1 <= b <= 16.
+ */
+size_t ttt_mem_deep_param_count(int d, int hidden, int depth);
+size_t ttt_mem_deep_work_bytes(int B, int H, int d, int hidden, int depth);
+int ttt_mem_deep_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const float* theta, const float* eta, const float* alpha,
+                              const float* W0, const float* S0,
+                              uint16_t* z, float* W_T, float* S_T,
+                              int B, int H, int T, int d, int hidden, int depth, int b,
+                              void* work, size_t work_bytes, void* stream);
+int ttt_mem_deep_status(const void* work, void* stream);
 
 /*
  * Linear memory over packed variable-length documents: every document starts

@@ -14,7 +14,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", name) for name in ("ttt_mem_linear.hip", "ttt_mem_mlp.hip", "ttt_mem_decode.hip", "ttt_mem_linear_bwd.hip")]
+SOURCES = [os.path.join(PKG, "csrc", name) for name in ("ttt_mem_linear.hip", "ttt_mem_deep.hip", "ttt_mem_decode.hip", "ttt_mem_linear_bwd.hip")]
 LIB = os.path.join(PKG, "libttt_mem.so")
 
 HIPCC_FLAGS = [

@@ -1,0 +1,871 @@
+// Chunked TTT deep memory (L = 2, 3 or 4 layers) forward for gfx950
+// (MI355X): the hidden units of every layer are split over the workgroups of
+// a group, and the groups exchange partial products through the L2 of their
+// XCD once or a few times per chunk.
+//
+// The memory is f(u) = u + SiLU(...SiLU(u W_1)...) W_L in row-vector form
+// (W_1: d x hid, W_l: hid x hid for 1 < l < L, W_L: hid x d, no biases),
+// written by gradient steps on 1/2 ||f(k_t) - v_t||^2 with every gradient of
+// a chunk taken at the chunk-start weights, one momentum per layer and the
+// token's theta, eta, alpha for all of them ("论文速览 | Titans", sections
+// 3.4, 3.7, 3.9 and 4.2; "Continual Learning: From Attention to Neural
+// Memory", sections 4.2 and 5.2).  The chunk is unrolled in its dual form
+// ("5.1.1 · TTT layers 与 fast weights", section 1.1, eqs. (7)-(9), carried
+// through a nonlinear inner model): with keys K, values V, queries Q of the
+// chunk (rows are tokens), the decay matrix L_ij = theta_j gamma_ij (j <= i),
+// the gate products A_i, c_i, E_i and the chunk-end weights w^M, w^S,
+//
+//   keys     X_0 = K, H_l = X_{l-1} W_l, X_l = SiLU(H_l) (l < L),
+//            R = K + X_{L-1} W_L - V
+//   deltas   D_L = R, D_l = (D_{l+1} W_{l+1}^T) .* SiLU'(H_l)
+//   reads    Y_0 = Q, Hq_l = diag(A) Y_{l-1} W_l + diag(c) Y_{l-1} S_l
+//                          - (L .* Y_{l-1} X_{l-1}^T) D_l,  Y_l = SiLU(Hq_l),
+//            Z = Q + Hq_L
+//   carry    W_l <- A_n W_l + c_n S_l - X_{l-1}^T diag(w^M) D_l,
+//            S_l <- E_n S_l - X_{l-1}^T diag(w^S) D_l
+//
+// Work split.  A group of G = 8 workgroups owns one (batch, head) sequence at
+// a time; each workgroup has two waves and each wave owns 16 hidden units of
+// every hidden layer: the columns of W_l (l < L) and the rows of W_L, with
+// their momenta, in fp32 MFMA accumulators for the whole sequence.  What
+// crosses waves is exchanged per chunk: R (a sum of per-wave partials of
+// X_{L-1} W_L), the z partials, and for deeper memories the activations X_l,
+// Y_l (gathered) and the partial products of D_l (summed).  The sixteen
+// waves of a group exchange through a workspace in global memory: every
+// workgroup writes its (two-wave) contribution, adds one to the group's
+// counter, and waits until the counter shows all G contributions; the counter
+// and the data live in the L2 of the XCD all G workgroups run on (workgroup
+// ids congruent mod 8; checked at run time against the hardware XCC id), so
+// the counter is polled with an atomic that executes in that L2 and the data
+// is read with plain loads from slots that rotate through a ring, with the
+// CU's vector L1 invalidated every few steps so that no slot is ever read
+// from a stale L1 line (a slot's previous read is a full ring ago, and an
+// invalidation lies between).  Every wait is bounded: a
+// wait that runs out sets a status bit and the kernel finishes (with wrong
+// results) instead of hanging.
+//
+// Precision.  MFMA operands are bf16 (v_mfma_f32_16x16x16_bf16): k, q and v
+// are exact; every float32 operand (weights, momenta, activations, residuals,
+// deltas) is split into bf16 hi + lo, and a product takes hi*hi + hi*lo +
+// lo*hi (about 16 significant bits), accumulating in float32.  bf16 keeps
+// float32's exponent range, so weights that decay far below the fp16 range
+// need no scaling.
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ttt_mem.h"
+#include "gfx950.h"
+
+namespace {
+
+constexpr int kD = 64;          // model width d
+constexpr int kHid = 256;       // hidden width
+constexpr int kNP = 16;         // padded chunk length (b <= 16)
+constexpr int kG = 8;           // workgroups per group (one sequence at a time)
+constexpr int kWaves = 2;       // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDT = kD / 16;    // 16-wide tiles of d
+constexpr int kHT = kHid / 16;  // 16-wide tiles of the hidden width (one per wave of a group)
+constexpr int kKS = kD + 8;     // LDS row stride (bf16) of K, Q, V rows
+constexpr int kRS = kD + 4;     // LDS row stride (floats) of R rows [t][d]
+constexpr int kRTS = kNP + 4;   // LDS row stride (floats) of R^T rows [d][t]
+constexpr int kLS = kNP + 4;    // LDS row stride (floats) of the decay matrix rows
+constexpr int kWS = 16 + 4;     // LDS row stride (bf16) of a wave's staged W_L^T rows [d][h]
+constexpr int kSlot = 2 * kNP * kD;   // floats per workgroup slot and exchange step: R and z partials
+// Exchange slots form a ring of kRing steps per group; every kInvEvery steps
+// the CU's vector L1 is invalidated, so a slot read again kRing steps later
+// cannot be served from a line the L1 kept since its previous read.
+constexpr int kRing = 32, kInvEvery = 16;
+static_assert(kRing >= 2 * kInvEvery, "an invalidation between any two reads of one slot");
+constexpr int kCtrStride = 64;        // ints between group counters (256 bytes)
+constexpr int kHdrInts = 1024;        // status word, XCD ticket counters and padding before the group counters
+constexpr int kTicketInts = 64;       // first XCD ticket counter (one per XCD, kCtrStride apart)
+constexpr uint32_t kStatusTimeout = 1u, kStatusPlacement = 2u;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// x = hi + lo, both bf16 (round to nearest even); together about 16 bits.
+struct Sp {
+    s16x4 hi, lo;
+};
+__device__ __forceinline__ s16x4 pack4(f32x4 v) { return __builtin_bit_cast(s16x4, pack_bf16x4(v)); }
+__device__ __forceinline__ f32x4 unpack4(s16x4 h) {
+    const u32x2 w = __builtin_bit_cast(u32x2, h);
+    return f32x4{bf16lo(w[0]), bf16hi(w[0]), bf16lo(w[1]), bf16hi(w[1])};
+}
+__device__ __forceinline__ Sp split(f32x4 x) {
+    const s16x4 hi = pack4(x);
+    return Sp{hi, pack4(x - unpack4(hi))};
+}
+// Products of split operands, dropping lo * lo; with an exact bf16 operand.
+__device__ __forceinline__ f32x4 mma3(const Sp& a, const Sp& b, f32x4 c) {
+    c = mma(a.hi, b.hi, c);
+    c = mma(a.hi, b.lo, c);
+    return mma(a.lo, b.hi, c);
+}
+__device__ __forceinline__ f32x4 mma2(s16x4 a, const Sp& b, f32x4 c) { return mma(a, b.lo, mma(a, b.hi, c)); }
+__device__ __forceinline__ f32x4 mma2(const Sp& a, s16x4 b, f32x4 c) { return mma(a.lo, b, mma(a.hi, b, c)); }
+
+// SiLU and its derivative through the hardware exp2 and reciprocal.
+__device__ __forceinline__ float sigm(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * x));
+}
+__device__ __forceinline__ f32x4 silu4(f32x4 x) {
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = x[e] * sigm(x[e]);
+    return r;
+}
+__device__ __forceinline__ void silu_d4(f32x4 x, f32x4& y, f32x4& dy) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float s = sigm(x[e]);
+        y[e] = x[e] * s;
+        dy[e] = s * (1.f + x[e] * (1.f - s));
+    }
+}
+
+__device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf; }
+
+// Poll the group counter with an atomic add of 0 that returns the value; the
+// atomic executes in the L2, where the other workgroups' increments are.  The
+// wait for the result is in the same asm block.
+__device__ __forceinline__ int l2_counter(int* p) {
+    int c, zero = 0;
+    asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(c) : "v"(p), "v"(zero) : "memory");
+    return c;
+}
+// Drop the CU's vector L1 lines (so that the loads after it read the L2).
+__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc1\n\ts_waitcnt vmcnt(0)" ::: "memory"); }
+
+struct DeepParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* theta;
+    const float* eta;
+    const float* alpha;
+    // Layer l (0-based) of sequence s: W0[l] + s * wstride[l] (row-major).
+    const float* W0[4];
+    const float* S0[4];
+    float* WT[4];
+    float* ST[4];
+    long long wstride[4];
+    void* z;         // float32, or bf16 bits (rounded to nearest even) when z_bf16
+    int z_bf16;
+    int BH;
+    int T;
+    int b;
+    int ngroups;
+    int nxcc;        // XCCs of the device (workgroup b is expected on XCC b % nxcc)
+    int spin_limit;  // polls before a wait gives up
+    int* work;       // [kHdrInts status][ngroups counters][exchange slots]
+};
+
+// One chunk of staged inputs and its gate quantities (double-buffered).
+struct ChunkBuf {
+    alignas(16) uint16_t kb[kNP * kKS];   // K rows [t][d], bf16
+    alignas(16) uint16_t qb[kNP * kKS];   // Q rows
+    alignas(16) uint16_t vb[kNP * kKS];   // V rows
+    alignas(16) float L[kNP * kLS];       // theta_j gamma_ij, row i, column j (0 above the diagonal)
+    alignas(16) float A[kNP];
+    alignas(16) float C[kNP];
+    alignas(16) float wm[kNP];            // -theta_j gamma_{n-1,j}
+    alignas(16) float ws[kNP];            // -theta_j p_{n-1,j}
+    alignas(16) float scal[4];            // A_n, c_n, E_n
+};
+
+struct Stash {
+    s16x4 w1[kDT][2][64];
+    s16x4 s1[kDT][2][64];
+    s16x4 w2[kDT][2][64];
+    s16x4 s2[kDT][2][64];
+};
+
+struct DeepSmem {
+    ChunkBuf buf[2];
+    alignas(16) float R[kNP * kRS];              // R rows [t][d]
+    alignas(16) float RT[kD * kRTS];             // R^T rows [d][t]
+    alignas(16) uint16_t wst[kWaves][2][kD * kWS];   // per wave: its W_L rows staged as [d][h], hi and lo
+    alignas(16) f32x4 xpart[kWaves][2][64];      // partner tiles for the two-wave pre-reduction
+    // Partials of one exchange step copied from the workspace straight into
+    // LDS (global-to-LDS loads, all in flight at once): per wave its two R
+    // tiles from the G workgroups; the z tile of the reducing workgroups.
+    alignas(16) f32x4 dma[kWaves][2 * kG][64];
+    alignas(16) f32x4 dmaz[kG][64];
+    // Chunk-start weights and momenta (bf16 hi / lo fragments) of the last two
+    // chunks, per wave, for the reads of a chunk one step later.
+    Stash stash[kWaves][2];
+    // Ak^T (by chunk parity) and dH fragments (hi / lo), per wave, for the same.
+    struct {
+        s16x4 akt[2][2][64];
+        s16x4 dh[2][64];
+    } act[kWaves];
+    int bail, gid, part;
+};
+
+// Registers of one prefetched chunk: thread u (0..127) holds one 16-byte unit
+// of K, Q and V each (token u / 8, columns 8 (u % 8)..+7); lanes < 16 of wave
+// 1 the chunk's gates.
+struct Prefetch {
+    uint4 k, q, v;
+    float th, et, al;
+};
+
+__device__ void prefetch(Prefetch& pf, const DeepParams& p, size_t seq_tok, int c, int tid) {
+    const int c0 = c * p.b;
+    const int n = max(0, min(p.b, p.T - c0));
+    const uint32_t nbytes = static_cast<uint32_t>(n) * kD * 2;
+    const size_t off = (seq_tok + static_cast<size_t>(c0)) * kD;
+    const uint32_t boff = static_cast<uint32_t>((tid >> 3) * kD + 8 * (tid & 7)) * 2;
+    pf.k = buf_load16(make_rsrc(p.k + off, nbytes), boff);
+    pf.q = buf_load16(make_rsrc(p.q + off, nbytes), boff);
+    pf.v = buf_load16(make_rsrc(p.v + off, nbytes), boff);
+    if (tid >= 64) {
+        const int lane = tid - 64;
+        const uint32_t gbytes = static_cast<uint32_t>(n) * 4;
+        const size_t gi = seq_tok + static_cast<size_t>(c0);
+        pf.th = buf_load4(make_rsrc(p.theta + gi, gbytes), lane * 4);
+        pf.al = buf_load4(make_rsrc(p.alpha + gi, gbytes), lane * 4);
+        pf.et = buf_load4(make_rsrc(p.eta + gi, gbytes), lane * 4);
+    }
+}
+
+__device__ void stage(const Prefetch& pf, ChunkBuf& B, int tid) {
+    const int t = tid >> 3, col = 8 * (tid & 7);
+    *reinterpret_cast<uint4*>(B.kb + t * kKS + col) = pf.k;
+    *reinterpret_cast<uint4*>(B.qb + t * kKS + col) = pf.q;
+    *reinterpret_cast<uint4*>(B.vb + t * kKS + col) = pf.v;
+}
+
+// row_newbcast:N -- every lane of a 16-lane row receives lane N of that row.
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+}
+
+// Gate quantities of one chunk, lanes j < 16 of one wave (token j): A_j, c_j
+// by a DPP scan of the 2x2 maps [[a, eta], [0, eta]] (a = 1 - alpha), column j
+// of the decay matrix by its recurrence p <- eta_i p + [i = j], gamma <- a_i
+// gamma + p (zero above the diagonal; a_i, eta_i broadcast from lane i), and
+// the chunk-end weights.  Padding tokens read theta = alpha = 0 and take
+// eta = 1.  Only products and sums: eta = 0 and alpha = 1 are exact.
+__device__ void gates(const Prefetch& pf, ChunkBuf& B, int n, int lane) {
+    const int j = lane & 15;
+    const float a = 1.f - pf.al, e = lane < n ? pf.et : 1.f, th = pf.th;
+    float X = a, Y = e, W = e;   // -> A_j, c_j, E_j
+    tri_step<kRowShr1>(X, Y, W);
+    tri_step<kRowShr2>(X, Y, W);
+    tri_step<kRowShr4>(X, Y, W);
+    tri_step<kRowShr8>(X, Y, W);
+    float ai[kNP], ei[kNP];
+    ai[0] = row_bcast<0>(a); ei[0] = row_bcast<0>(e);
+    ai[1] = row_bcast<1>(a); ei[1] = row_bcast<1>(e);
+    ai[2] = row_bcast<2>(a); ei[2] = row_bcast<2>(e);
+    ai[3] = row_bcast<3>(a); ei[3] = row_bcast<3>(e);
+    ai[4] = row_bcast<4>(a); ei[4] = row_bcast<4>(e);
+    ai[5] = row_bcast<5>(a); ei[5] = row_bcast<5>(e);
+    ai[6] = row_bcast<6>(a); ei[6] = row_bcast<6>(e);
+    ai[7] = row_bcast<7>(a); ei[7] = row_bcast<7>(e);
+    ai[8] = row_bcast<8>(a); ei[8] = row_bcast<8>(e);
+    ai[9] = row_bcast<9>(a); ei[9] = row_bcast<9>(e);
+    ai[10] = row_bcast<10>(a); ei[10] = row_bcast<10>(e);
+    ai[11] = row_bcast<11>(a); ei[11] = row_bcast<11>(e);
+    ai[12] = row_bcast<12>(a); ei[12] = row_bcast<12>(e);
+    ai[13] = row_bcast<13>(a); ei[13] = row_bcast<13>(e);
+    ai[14] = row_bcast<14>(a); ei[14] = row_bcast<14>(e);
+    ai[15] = row_bcast<15>(a); ei[15] = row_bcast<15>(e);
+    float g = 0.f, pe = 0.f, wm = 0.f, ws = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNP; ++i) {
+        pe = i == j ? 1.f : ei[i] * pe;
+        g = ai[i] * g + pe;
+        if (lane < kNP) B.L[i * kLS + j] = th * g;
+        if (i == n - 1) {
+            wm = th * g;
+            ws = th * pe;
+        }
+    }
+    if (lane < kNP) {
+        B.A[j] = X;
+        B.C[j] = Y;
+        B.wm[j] = -wm;
+        B.ws[j] = -ws;
+        if (lane == n - 1) {
+            B.scal[0] = X;
+            B.scal[1] = Y;
+            B.scal[2] = W;
+        }
+    }
+}
+
+// 4 bf16 of an LDS row (8 bytes).
+__device__ __forceinline__ s16x4 lds4(const uint16_t* p) { return *reinterpret_cast<const s16x4*>(p); }
+// Transpose load: with row pointer base (row stride rs elements), lane L of
+// 16-lane group g reads row 4g + L/4 at columns 4 (L % 4)..+3; lane i then
+// holds column i of rows 4g..4g+3.
+__device__ __forceinline__ s16x4 lds_tr4(const uint16_t* base, int rs, int lr, int lg) {
+    return ds_read_tr16(base + (4 * lg + (lr >> 2)) * rs + 4 * (lr & 3));
+}
+
+__global__ __launch_bounds__(kThreads, 1) void deep_fwd2(const DeepParams p) {
+    __shared__ DeepSmem sm;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    int* const status = p.work;
+
+    // Group and part from the XCD the workgroup actually runs on: a ticket
+    // from that XCD's counter (an atomic in its L2) numbers the workgroups
+    // of the XCD; G consecutive tickets form a group.  The grid is a
+    // multiple of 8 G, so round-robin dispatch gives every XCD whole groups;
+    // a workgroup past its XCD's share flags the status and leaves.
+    if (tid == 0) {
+        const int x = xcc_id() % p.nxcc;
+        const int t = __hip_atomic_fetch_add(p.work + kTicketInts + x * kCtrStride, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        const int per_xcd = p.ngroups / p.nxcc;
+        sm.bail = t >= per_xcd * kG ? 1 : 0;
+        if (sm.bail)
+            __hip_atomic_fetch_or(status, static_cast<int>(kStatusPlacement), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_SYSTEM);
+        sm.gid = x + p.nxcc * (t / kG);
+        sm.part = t % kG;
+    }
+    __syncthreads();
+    if (sm.bail) return;
+    const int gi = __builtin_amdgcn_readfirstlane(sm.gid);
+    const int part = __builtin_amdgcn_readfirstlane(sm.part);
+    int* const ctr = p.work + kHdrInts + gi * kCtrStride;
+    float* const xbase = reinterpret_cast<float*>(p.work + kHdrInts + p.ngroups * kCtrStride) +
+                         static_cast<size_t>(gi) * kRing * kG * kSlot;
+    const int hu = 32 * part + 16 * w;   // first hidden unit of this wave
+    int epoch = 0;                       // exchanges of this group so far
+
+    // Group exchange in two halves: signal() after this workgroup's
+    // contribution is written; wait() until all G have signalled.  Work that
+    // needs none of this step's data goes in between.
+    auto signal = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto wait = [&]() -> bool {
+        if (tid == 0) {
+            const int target = kG * (epoch + 1);
+            int spins = 0;
+            while (l2_counter(ctr) < target) {
+                if (++spins > p.spin_limit) {
+                    sm.bail = 1;
+                    __hip_atomic_fetch_or(status, static_cast<int>(kStatusTimeout), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_SYSTEM);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __syncthreads();
+        ++epoch;
+        if (sm.bail) return false;
+        if ((epoch - 1) % kInvEvery == 0) l1_invalidate();
+        return true;
+    };
+
+    for (int s = gi; s < p.BH; s += p.ngroups) {
+        const size_t seq_tok = static_cast<size_t>(s) * p.T;
+        const int nch = (p.T + p.b - 1) / p.b;
+        auto chunk_n = [&](int c) { return min(p.b, p.T - c * p.b); };
+
+        // ---- resident weights: W1[dt] = W_1[16dt.., hu..] as [d][h]; W2[dt] = W_L[hu.., 16dt..] as [h][d] ----
+        f32x4 W1[kDT], S1[kDT], W2[kDT], S2[kDT];
+        {
+            const float* w1 = p.W0[0] + s * p.wstride[0];
+            const float* s1 = p.S0[0] ? p.S0[0] + s * p.wstride[0] : nullptr;
+            const float* w2 = p.W0[1] + s * p.wstride[1];
+            const float* s2 = p.S0[1] ? p.S0[1] + s * p.wstride[1] : nullptr;
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i1 = (16 * dt + 4 * lg + e) * kHid + hu + lr;
+                    const int i2 = (hu + 4 * lg + e) * kD + 16 * dt + lr;
+                    W1[dt][e] = w1[i1];
+                    S1[dt][e] = s1 ? s1[i1] : 0.f;
+                    W2[dt][e] = w2[i2];
+                    S2[dt][e] = s2 ? s2[i2] : 0.f;
+                }
+        }
+        // W_L rows of this wave split into bf16 hi / lo (W2s, reused by the
+        // products of the next chunk) and staged as [d][h] (for the
+        // transposed operand of R W_L^T).
+        Sp W2s[kDT];
+        auto stage_w2 = [&]() {
+            uint16_t* hi = sm.wst[w][0];
+            uint16_t* lo = sm.wst[w][1];
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt) {
+                W2s[dt] = split(W2[dt]);
+                *reinterpret_cast<s16x4*>(hi + (16 * dt + lr) * kWS + 4 * lg) = W2s[dt].hi;
+                *reinterpret_cast<s16x4*>(lo + (16 * dt + lr) * kWS + 4 * lg) = W2s[dt].lo;
+            }
+        };
+        stage_w2();
+
+        Prefetch pf;
+        prefetch(pf, p, seq_tok, 0, tid);
+        __syncthreads();   // the previous sequence's last use of the chunk buffers
+        if (nch > 0) {
+            stage(pf, sm.buf[0], tid);
+            if (w == 1) gates(pf, sm.buf[0], chunk_n(0), lane);
+        }
+        __syncthreads();
+
+        // Iteration c: the keys of chunk c and its exchange; in the exchange's
+        // wait, the reads (z) of chunk c - 1; after it, the z of chunk c - 2,
+        // and the deltas and carry of chunk c.  Two more iterations finish
+        // the z of the last chunks.
+        f32x4 Zp[2] = {};   // this workgroup's z partial of chunk c - 1 (own two d tiles), pre-reduced
+        bool ok = true;
+        const int iters = nch > 0 ? nch + 2 : 0;
+        for (int c = 0; c < iters; ++c) {
+            const bool keys = c < nch;
+            const bool reads = c >= 1 && c <= nch;   // reads of chunk c - 1 in this step's wait
+            const bool zout = c >= 2;                // z of chunk c - 2 leaves with this step
+            const ChunkBuf& B = sm.buf[c & 1];
+            const int n = keys ? chunk_n(c) : 0;
+            if (keys && c + 1 < nch) prefetch(pf, p, seq_tok, c + 1, tid);
+            float* slot = xbase + static_cast<size_t>((epoch % kRing) * kG + part) * kSlot;
+
+            // ================= keys forward at the chunk-start weights =================
+            f32x4 Ak = {0.f, 0.f, 0.f, 0.f}, dAk = Ak;
+            if (keys) {
+                Stash& st = sm.stash[w][c & 1];
+                f32x4 hk = {0.f, 0.f, 0.f, 0.f}, hkt = hk;
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) {
+                    const s16x4 kf = lds4(B.kb + lr * kKS + 16 * dt + 4 * lg);
+                    const Sp w1s = split(W1[dt]);
+                    hk = mma2(kf, w1s, hk);      // (K W_1)[t][h]
+                    hkt = mma2(w1s, kf, hkt);    // (K W_1)^T[h][t]
+                    // Chunk-start weights and momenta for this chunk's reads.
+                    st.w1[dt][0][lane] = w1s.hi;
+                    st.w1[dt][1][lane] = w1s.lo;
+                    st.w2[dt][0][lane] = W2s[dt].hi;
+                    st.w2[dt][1][lane] = W2s[dt].lo;
+                    const Sp s1s = split(S1[dt]), s2s = split(S2[dt]);
+                    st.s1[dt][0][lane] = s1s.hi;
+                    st.s1[dt][1][lane] = s1s.lo;
+                    st.s2[dt][0][lane] = s2s.hi;
+                    st.s2[dt][1][lane] = s2s.lo;
+                }
+                silu_d4(hk, Ak, dAk);
+                // Partial R^T[d][t] over this wave's hidden units, d tile dt.
+                const Sp akt = split(silu4(hkt));             // Ak^T[h][t]
+                sm.act[w].akt[c & 1][0][lane] = akt.hi;
+                sm.act[w].akt[c & 1][1][lane] = akt.lo;
+                f32x4 rp[kDT];
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) rp[dt] = mma3(W2s[dt], akt, f32x4{0.f, 0.f, 0.f, 0.f});
+                // Two-wave pre-reduction: wave w keeps d tiles 2w, 2w+1.
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = rp[2 * (1 - w) + k2];
+                __syncthreads();
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    const int dt = 2 * w + k2;
+                    const f32x4 r = rp[dt] + sm.xpart[w][k2][lane];
+                    // lane (t = lr, lg) holds R^T[16dt + 4lg + e][t] = R[t][16dt + 4lg + e]
+                    *reinterpret_cast<f32x4*>(slot + lr * kD + 16 * dt + 4 * lg) = r;
+                }
+            }
+            if (zout) {
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2)
+                    *reinterpret_cast<f32x4*>(slot + kNP * kD + lr * kD + 16 * (2 * w + k2) + 4 * lg) = Zp[k2];
+            }
+            signal();
+
+            // ================= reads of chunk c - 1 (in the wait) =================
+            if (reads) {
+                const ChunkBuf& Bp = sm.buf[(c - 1) & 1];
+                const Stash& st = sm.stash[w][(c - 1) & 1];
+                const float At = Bp.A[lr], Ct = Bp.C[lr];
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(Bp.L + lr * kLS + 4 * lg);   // L[t][4lg..]
+                f32x4 kq = {0.f, 0.f, 0.f, 0.f}, za = kq, zc = kq;
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) {
+                    const s16x4 kf = lds4(Bp.kb + lr * kKS + 16 * dt + 4 * lg);
+                    const s16x4 qf = lds4(Bp.qb + lr * kKS + 16 * dt + 4 * lg);
+                    kq = mma(kf, qf, kq);                                            // (K Q^T)[j][t]
+                    za = mma2(Sp{st.w1[dt][0][lane], st.w1[dt][1][lane]}, qf, za);   // (W_1^T Q^T)[h][t]
+                    zc = mma2(Sp{st.s1[dt][0][lane], st.s1[dt][1][lane]}, qf, zc);
+                }
+                const Sp pt = split(kq * l4);             // P^T[j][t] = (L .* Q K^T)[t][j]
+                const Sp dHs{sm.act[w].dh[0][lane], sm.act[w].dh[1][lane]};
+                const Sp akt{sm.act[w].akt[(c - 1) & 1][0][lane], sm.act[w].akt[(c - 1) & 1][1][lane]};
+                f32x4 hq = mma3(dHs, pt, f32x4{0.f, 0.f, 0.f, 0.f});   // (dH^T P^T)[h][t]
+                hq = At * za + Ct * zc - hq;
+                const Sp aq = split(silu4(hq));           // Aq^T[h][t]
+                // (Ak Aq^T)[j][t] over this wave's hidden units, times L.
+                const Sp lg4 = split(mma3(akt, aq, f32x4{0.f, 0.f, 0.f, 0.f}) * l4);
+                f32x4 zp[kDT];
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) {
+                    const f32x4 a2 = mma3(Sp{st.w2[dt][0][lane], st.w2[dt][1][lane]}, aq, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 c2 = mma3(Sp{st.s2[dt][0][lane], st.s2[dt][1][lane]}, aq, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const Sp rs = split(*reinterpret_cast<const f32x4*>(sm.RT + (16 * dt + lr) * kRTS + 4 * lg));
+                    const f32x4 in = mma3(rs, lg4, f32x4{0.f, 0.f, 0.f, 0.f});   // (R^T (L .* G)^T)[d][t]
+                    zp[dt] = At * a2 + Ct * c2 - in;
+                }
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = zp[2 * (1 - w) + k2];
+                __syncthreads();
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    const int dt = 2 * w + k2;
+                    Zp[k2] = zp[dt] + sm.xpart[w][k2][lane];
+                    // z = q + the sum of the partials: workgroup 0 adds q.
+                    if (part == 0) Zp[k2] += unpack4(lds4(Bp.qb + lr * kKS + 16 * dt + 4 * lg));
+                }
+            } else {
+                __syncthreads();
+            }
+            // Gate quantities of chunk c + 1 (their buffer held chunk c - 1's, read above).
+            if (w == 1 && keys && c + 1 < nch) gates(pf, sm.buf[(c + 1) & 1], chunk_n(c + 1), lane);
+            if (!wait()) {
+                ok = false;
+                break;
+            }
+            const float* rslot = xbase + static_cast<size_t>(((epoch - 1) % kRing) * kG) * kSlot;
+
+            // Copy this step's partials into LDS: every load in flight at once,
+            // none through registers.
+            const bool zred = zout && part < kDT && w == 0;
+            if (keys) {
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                    for (int g2 = 0; g2 < kG; ++g2)
+                        __builtin_amdgcn_global_load_lds(rslot + g2 * kSlot + lr * kD + 16 * (2 * w + k2) + 4 * lg,
+                                                         &sm.dma[w][k2 * kG + g2][0], 16, 0, 0);
+            }
+            if (zred) {
+#pragma unroll
+                for (int g2 = 0; g2 < kG; ++g2)
+                    __builtin_amdgcn_global_load_lds(rslot + g2 * kSlot + kNP * kD + lr * kD + 16 * part + 4 * lg,
+                                                     &sm.dmaz[g2][0], 16, 0, 0);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+            // ================= z of chunk c - 2: four workgroups, one d tile each =================
+            if (zred) {
+                const int np = chunk_n(c - 2);
+                f32x4 zt = sm.dmaz[0][lane];
+#pragma unroll
+                for (int g2 = 1; g2 < kG; ++g2) zt += sm.dmaz[g2][lane];
+                const bool zb = p.z_bf16 != 0;
+                const uint32_t zsz = zb ? 2u : 4u;
+                const auto rz = make_rsrc(static_cast<char*>(p.z) + (seq_tok + static_cast<size_t>(c - 2) * p.b) * kD * zsz,
+                                          static_cast<uint32_t>(np) * kD * zsz);
+                store_out4(zt, rz, static_cast<uint32_t>(lr * kD + 16 * part + 4 * lg), zb);
+            }
+            if (!keys) continue;
+
+            // ================= R = K - V + sum of partials =================
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int dt = 2 * w + k2;
+                f32x4 r = unpack4(lds4(B.kb + lr * kKS + 16 * dt + 4 * lg)) - unpack4(lds4(B.vb + lr * kKS + 16 * dt + 4 * lg));
+#pragma unroll
+                for (int g2 = 0; g2 < kG; ++g2) r += sm.dma[w][k2 * kG + g2][lane];
+                if (lr >= n) r = f32x4{0.f, 0.f, 0.f, 0.f};   // padding tokens carry no residual
+                *reinterpret_cast<f32x4*>(sm.R + lr * kRS + 16 * dt + 4 * lg) = r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.RT[(16 * dt + 4 * lg + e) * kRTS + lr] = r[e];
+            }
+            __syncthreads();
+
+            // ================= dH = (R W_L^T) .* SiLU'(Hk) =================
+            f32x4 dH = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt) {
+                const Sp rf = split(*reinterpret_cast<const f32x4*>(sm.R + lr * kRS + 16 * dt + 4 * lg));
+                const Sp wt{lds_tr4(sm.wst[w][0] + 16 * dt * kWS, kWS, lr, lg), lds_tr4(sm.wst[w][1] + 16 * dt * kWS, kWS, lr, lg)};
+                dH = mma3(rf, wt, dH);   // [t][h]
+            }
+            dH *= dAk;
+            {
+                const Sp dHs = split(dH);   // for this chunk's reads, in the next step's wait
+                sm.act[w].dh[0][lane] = dHs.hi;
+                sm.act[w].dh[1][lane] = dHs.lo;
+            }
+
+            // ================= carry =================
+            {
+                const float An = B.scal[0], Cn = B.scal[1], En = B.scal[2];
+                const f32x4 wm4 = *reinterpret_cast<const f32x4*>(B.wm + 4 * lg);
+                const f32x4 ws4 = *reinterpret_cast<const f32x4*>(B.ws + 4 * lg);
+                const Sp dm = split(dH * wm4), dsv = split(dH * ws4);   // B = (w .* dH)[t][h]
+                // A = (Ak diag(w))^T[h][t]: the token weights ride on Ak.
+                const Sp akm = split(Ak * wm4), aks = split(Ak * ws4);
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) {
+                    const s16x4 kt = lds_tr4(B.kb + 16 * dt, kKS, lr, lg);   // A = K^T[d][t]
+                    const f32x4 w1 = An * W1[dt] + Cn * S1[dt];
+                    S1[dt] = mma2(kt, dsv, En * S1[dt]);
+                    W1[dt] = mma2(kt, dm, w1);
+                    // R[4lg..4lg+3][16dt + lr]: B = R[t][d] of the W_L carry.
+                    const Sp rs = split(*reinterpret_cast<const f32x4*>(sm.RT + (16 * dt + lr) * kRTS + 4 * lg));
+                    const f32x4 w2 = An * W2[dt] + Cn * S2[dt];
+                    S2[dt] = mma3(aks, rs, En * S2[dt]);
+                    W2[dt] = mma3(akm, rs, w2);
+                }
+                stage_w2();
+            }
+            // ================= next chunk's inputs =================
+            if (c + 1 < nch) stage(pf, sm.buf[(c + 1) & 1], tid);
+            __syncthreads();
+        }
+        if (!ok) break;
+
+        // ---- final weights ----
+        {
+            float* w1 = p.WT[0] ? p.WT[0] + s * p.wstride[0] : nullptr;
+            float* s1 = p.ST[0] ? p.ST[0] + s * p.wstride[0] : nullptr;
+            float* w2 = p.WT[1] ? p.WT[1] + s * p.wstride[1] : nullptr;
+            float* s2 = p.ST[1] ? p.ST[1] + s * p.wstride[1] : nullptr;
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i1 = (16 * dt + 4 * lg + e) * kHid + hu + lr;
+                    const int i2 = (hu + 4 * lg + e) * kD + 16 * dt + lr;
+                    if (w1) w1[i1] = W1[dt][e];
+                    if (s1) s1[i1] = S1[dt][e];
+                    if (w2) w2[i2] = W2[dt][e];
+                    if (s2) s2[i2] = S2[dt][e];
+                }
+        }
+    }
+}
+
+// Zero the status word and the group counters before a launch.
+__global__ void deep_init(int* work, int nints) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nints; i += gridDim.x * blockDim.x) work[i] = 0;
+}
+
+}  // namespace
+
+namespace {
+
+size_t deep_work_bytes_for(long long ngroups) {
+    return (static_cast<size_t>(kHdrInts) + static_cast<size_t>(ngroups) * kCtrStride) * 4 +
+           static_cast<size_t>(ngroups) * kRing * kG * kSlot * 4;
+}
+
+// Groups for BH sequences: a multiple of 8 (one XCD each), at most BH rounded
+// up, and at most what can be resident at once.
+long long deep_groups(long long BH, int max_groups) {
+    long long g = (BH + 7) / 8 * 8;
+    return g < max_groups ? g : max_groups;
+}
+
+struct TensorSet {   // a weight tensor, its momentum and their outputs, as passed by the caller
+    const void* W0;
+    const void* S0;
+    const void* WT;
+    const void* ST;
+    size_t bytes;
+};
+
+struct Layers {
+    const float* W0[4];
+    const float* S0[4];
+    float* WT[4];
+    float* ST[4];
+    long long stride[4];
+    TensorSet tensors[4];
+    int ntensors;
+};
+
+int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta, const float* eta,
+                      const float* alpha, const Layers& ly, int depth, void* z, bool z_bf16, int B, int H, int Tlen,
+                      int d, int hidden, int b, void* work, size_t work_bytes, void* stream_) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (B < 0 || H < 0 || Tlen < 0 || b < 1) return TTT_ERR_INVALID_ARG;
+    if (d != kD || hidden != kHid || b > kNP || depth != 2) return TTT_ERR_UNSUPPORTED;
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0) return TTT_OK;
+    if (BH > 0x7fffffffLL || BH * static_cast<long long>(Tlen) > 0x7fffffffLL) return TTT_ERR_UNSUPPORTED;
+    for (int l = 0; l < depth; ++l)
+        if (!ly.W0[l]) return TTT_ERR_INVALID_ARG;
+    const size_t tok = static_cast<size_t>(BH) * static_cast<size_t>(Tlen);
+    const size_t in_bytes = tok * kD * 2, z_bytes = tok * kD * (z_bf16 ? 2 : 4);
+    if (Tlen > 0) {
+        if (!q || !k || !v || !theta || !eta || !alpha || !z) return TTT_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(z, 16)) return TTT_ERR_INVALID_ARG;
+        if (!aligned(theta, 4) || !aligned(eta, 4) || !aligned(alpha, 4)) return TTT_ERR_INVALID_ARG;
+        const void* ins[] = {q, k, v};
+        for (const void* in : ins)
+            if (overlaps(z, z_bytes, in, in_bytes)) return TTT_ERR_INVALID_ARG;
+        const void* gs[] = {theta, eta, alpha};
+        for (const void* g : gs)
+            if (overlaps(z, z_bytes, g, tok * 4)) return TTT_ERR_INVALID_ARG;
+    }
+    // Weight tensors (as the caller passes them: one per layer, or one
+    // packed tensor for all layers): 4-byte aligned; an output may be its own
+    // initial tensor (in-place carry) and overlaps nothing else; z overlaps
+    // none of them.
+    for (int i = 0; i < ly.ntensors; ++i) {
+        const TensorSet& t = ly.tensors[i];
+        const void* all[] = {t.W0, t.S0, t.WT, t.ST};
+        for (const void* x : all) {
+            if (x && !aligned(x, 4)) return TTT_ERR_INVALID_ARG;
+            if (x && Tlen > 0 && overlaps(z, z_bytes, x, t.bytes)) return TTT_ERR_INVALID_ARG;
+        }
+        const void* outs[] = {t.WT, t.ST};
+        const void* own[] = {t.W0, t.S0};
+        for (int o = 0; o < 2; ++o) {
+            if (!outs[o]) continue;
+            for (int j = 0; j < ly.ntensors; ++j) {
+                const TensorSet& u = ly.tensors[j];
+                const void* others[] = {u.W0, u.S0, u.WT, u.ST};
+                for (int k2 = 0; k2 < 4; ++k2) {
+                    if (!others[k2]) continue;
+                    if (j == i && k2 == 2 + o) continue;                     // itself
+                    if (j == i && k2 == o && own[o] == outs[o]) continue;    // in-place carry
+                    if (overlaps(outs[o], t.bytes, others[k2], u.bytes)) return TTT_ERR_INVALID_ARG;
+                }
+            }
+        }
+    }
+
+    int dev = 0, ncu = 0, nxcc = 1, occ = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return TTT_ERR_HIP;
+    if (hipDeviceGetAttribute(&nxcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || nxcc < 1) nxcc = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, deep_fwd2, kThreads, 0) != hipSuccess) return TTT_ERR_HIP;
+    const int max_groups = (ncu * occ / kG) / 8 * 8;
+    if (max_groups < 8) return TTT_ERR_UNSUPPORTED;
+    const long long ngroups = deep_groups(BH, max_groups);
+    const size_t need = deep_work_bytes_for(ngroups);
+    bool own_work = false;
+    if (work) {
+        if (!aligned(work, 256) || work_bytes < need) return TTT_ERR_INVALID_ARG;
+    } else {
+        if (hipMallocAsync(&work, need, stream) != hipSuccess) return TTT_ERR_HIP;
+        own_work = true;
+    }
+
+    DeepParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.theta = theta;
+    p.eta = eta;
+    p.alpha = alpha;
+    for (int l = 0; l < 4; ++l) {
+        p.W0[l] = l < depth ? ly.W0[l] : nullptr;
+        p.S0[l] = l < depth ? ly.S0[l] : nullptr;
+        p.WT[l] = l < depth ? ly.WT[l] : nullptr;
+        p.ST[l] = l < depth ? ly.ST[l] : nullptr;
+        p.wstride[l] = l < depth ? ly.stride[l] : 0;
+    }
+    p.z = z;
+    p.z_bf16 = z_bf16 ? 1 : 0;
+    p.BH = static_cast<int>(BH);
+    p.T = Tlen;
+    p.b = b;
+    p.ngroups = static_cast<int>(ngroups);
+    p.nxcc = nxcc;
+    p.spin_limit = 2000000;
+    p.work = static_cast<int*>(work);
+    const int hdr = kHdrInts + static_cast<int>(ngroups) * kCtrStride;
+    hipLaunchKernelGGL(deep_init, dim3(8), dim3(256), 0, stream, p.work, hdr);
+    hipError_t err = hipGetLastError();
+    if (err == hipSuccess) {
+        void* args[] = {&p};
+        err = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(deep_fwd2), dim3(static_cast<unsigned>(ngroups * kG)),
+                                         dim3(kThreads), args, 0, stream);
+    }
+    if (own_work) hipFreeAsync(work, stream);
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ttt_mem_deep_param_count(int d, int hidden, int depth) {
+    if (d < 1 || hidden < 1 || depth < 2) return 0;
+    return static_cast<size_t>(d) * hidden * 2 + static_cast<size_t>(depth - 2) * hidden * hidden;
+}
+
+size_t ttt_mem_deep_work_bytes(int B, int H, int d, int hidden, int depth) {
+    if (B < 0 || H < 0 || d != kD || hidden != kHid || depth < 2 || depth > 2) return 0;
+    const long long BH = static_cast<long long>(B) * H;
+    return deep_work_bytes_for(deep_groups(BH, 1 << 30));
+}
+
+int ttt_mem_deep_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                              const float* eta, const float* alpha, const float* W0, const float* S0, uint16_t* z,
+                              float* W_T, float* S_T, int B, int H, int T, int d, int hidden, int depth, int b,
+                              void* work, size_t work_bytes, void* stream) {
+    if (depth < 2 || depth > 4) return TTT_ERR_UNSUPPORTED;
+    const long long P = static_cast<long long>(ttt_mem_deep_param_count(d, hidden, depth));
+    Layers ly{};
+    for (int l = 0; l < depth; ++l) {
+        const long long off = l == 0 ? 0 : static_cast<long long>(d) * hidden + static_cast<long long>(l - 1) * hidden * hidden;
+        ly.W0[l] = W0 ? W0 + off : nullptr;
+        ly.S0[l] = S0 ? S0 + off : nullptr;
+        ly.WT[l] = W_T ? W_T + off : nullptr;
+        ly.ST[l] = S_T ? S_T + off : nullptr;
+        ly.stride[l] = P;
+    }
+    const size_t tb = static_cast<size_t>(B > 0 && H > 0 ? static_cast<long long>(B) * H : 0) * P * 4;
+    ly.tensors[0] = TensorSet{W0, S0, W_T, S_T, tb};
+    ly.ntensors = 1;
+    if (!W0) return TTT_ERR_INVALID_ARG;
+    return deep_forward_impl(q, k, v, theta, eta, alpha, ly, depth, z, true, B, H, T, d, hidden, b, work, work_bytes,
+                             stream);
+}
+
+int ttt_mem_deep_status(const void* work, void* stream) {
+    if (!work) return TTT_ERR_INVALID_ARG;
+    int st = 0;
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return TTT_ERR_HIP;
+    if (hipMemcpy(&st, work, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return TTT_ERR_HIP;
+    return st == 0 ? TTT_OK : TTT_ERR_DEVICE;
+}
+
+int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                             const float* eta, const float* alpha, const float* W1_0, const float* W2_0,
+                             const float* S1_0, const float* S2_0, uint16_t* z, float* W1_T, float* W2_T, float* S1_T,
+                             float* S2_T, int B, int H, int T, int d, int hidden, int b, void* stream) {
+    const long long s1 = static_cast<long long>(d) * hidden;
+    const size_t tb = static_cast<size_t>(B > 0 && H > 0 ? static_cast<long long>(B) * H : 0) * s1 * 4;
+    const Layers ly{{W1_0, W2_0}, {S1_0, S2_0}, {W1_T, W2_T}, {S1_T, S2_T}, {s1, s1},
+                    {{W1_0, S1_0, W1_T, S1_T, tb}, {W2_0, S2_0, W2_T, S2_T, tb}}, 2};
+    return deep_forward_impl(q, k, v, theta, eta, alpha, ly, 2, z, true, B, H, T, d, hidden, b, nullptr, 0, stream);
+}
+
+int ttt_mem_mlp_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                                  const float* eta, const float* alpha, const float* W1_0, const float* W2_0,
+                                  const float* S1_0, const float* S2_0, float* z, float* W1_T, float* W2_T,
+                                  float* S1_T, float* S2_T, int B, int H, int T, int d, int hidden, int b,
+                                  void* stream) {
+    const long long s1 = static_cast<long long>(d) * hidden;
+    const size_t tb = static_cast<size_t>(B > 0 && H > 0 ? static_cast<long long>(B) * H : 0) * s1 * 4;
+    const Layers ly{{W1_0, W2_0}, {S1_0, S2_0}, {W1_T, W2_T}, {S1_T, S2_T}, {s1, s1},
+                    {{W1_0, S1_0, W1_T, S1_T, tb}, {W2_0, S2_0, W2_T, S2_T, tb}}, 2};
+    return deep_forward_impl(q, k, v, theta, eta, alpha, ly, 2, z, false, B, H, T, d, hidden, b, nullptr, 0, stream);
+}
+
+}  // extern "C"

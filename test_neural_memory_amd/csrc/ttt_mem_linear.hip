@@ -1624,6 +1624,7 @@ const char* ttt_mem_status_string(int status) {
         case TTT_ERR_INVALID_ARG: return "invalid argument";
         case TTT_ERR_UNSUPPORTED: return "unsupported size";
         case TTT_ERR_HIP: return "HIP launch failed";
+        case TTT_ERR_DEVICE: return "device-side failure (deep-memory group exchange)";
         default: return "unknown status";
     }
 }

@@ -482,3 +482,99 @@ def ttt_mem_mlp_forward_bf16(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0=None, 
             B, H, T, d, int(hid), int(b), stream)
     _lib.check(name, status)
     return z, W1_T, W2_T, S1_T, S2_T
+
+
+def deep_param_count(d, hidden, depth):
+    """Floats per (batch, head) of the packed deep-memory parameters."""
+    return int(_lib.load().ttt_mem_deep_param_count(int(d), int(hidden), int(depth)))
+
+
+def deep_layer_shapes(d, hidden, depth):
+    """Shapes of the layers of a deep memory: [d, hid], [hid, hid] * (depth - 2), [hid, d]."""
+    return [(d, hidden)] + [(hidden, hidden)] * (depth - 2) + [(hidden, d)]
+
+
+def deep_pack(layers):
+    """[B, H, *shape_l] float32 layers -> one contiguous [B, H, P] tensor (layer-major per sequence)."""
+    B, H = layers[0].shape[:2]
+    return torch.cat([x.reshape(B, H, -1) for x in layers], dim=-1).contiguous()
+
+
+def deep_unpack(packed, d, hidden, depth):
+    """The inverse of ``deep_pack``: views of the layers of a [B, H, P] tensor."""
+    B, H = packed.shape[:2]
+    out, off = [], 0
+    for shp in deep_layer_shapes(d, hidden, depth):
+        n = shp[0] * shp[1]
+        out.append(packed[..., off:off + n].reshape(B, H, *shp))
+        off += n
+    return out
+
+
+def new_deep_work(B, H, d, hidden, depth, device):
+    """A workspace for ``deep_forward`` (uninitialised; the launch clears what it needs)."""
+    n = int(_lib.load().ttt_mem_deep_work_bytes(int(B), int(H), int(d), int(hidden), int(depth)))
+    if n == 0:
+        raise ValueError("unsupported deep-memory sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def deep_forward(q, k, v, theta, eta, alpha, W0, S0=None, *, hidden, depth, b, work=None, out=None):
+    """bf16-input deep memory of depth 2-4 with packed parameters.
+
+    ``W0, S0`` are ``[B, H, P]`` float32 (``deep_pack``), P =
+    ``deep_param_count(d, hidden, depth)``.  Returns
+    ``(z, W_T, S_T)`` with bf16 z.  ``work`` (``new_deep_work``) is the
+    exchange workspace; if None, the call takes one from the stream-ordered
+    allocator.  ``out`` may pass ``(z, W_T, S_T)``.
+    """
+    name = "ttt_mem_deep_forward_bf16"
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be HIP device tensors (torch 'cuda' device)")
+    if W0 is None:
+        raise ValueError("W0 is required")
+    P = deep_param_count(d, hidden, depth)
+    q = _as_dev(q, "q", torch.bfloat16, (B, H, T, d), dev)
+    k = _as_dev(k, "k", torch.bfloat16, (B, H, T, d), dev)
+    v = _as_dev(v, "v", torch.bfloat16, (B, H, T, d), dev)
+    theta = _as_dev(theta, "theta", torch.float32, (B, H, T), dev)
+    eta = _as_dev(eta, "eta", torch.float32, (B, H, T), dev)
+    alpha = _as_dev(alpha, "alpha", torch.float32, (B, H, T), dev)
+    W0 = _as_dev(W0, "W0", torch.float32, (B, H, P), dev)
+    S0 = _as_dev(S0, "S0", torch.float32, (B, H, P), dev)
+    if out is None:
+        z = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+        W_T = torch.empty((B, H, P), dtype=torch.float32, device=dev)
+        S_T = torch.empty((B, H, P), dtype=torch.float32, device=dev)
+    else:
+        z, W_T, S_T = out
+        for t, nm, shp, dt in ((z, "z", (B, H, T, d), torch.bfloat16), (W_T, "W_T", (B, H, P), torch.float32),
+                               (S_T, "S_T", (B, H, P), torch.float32)):
+            if t is not None and (not t.is_contiguous() or t.dtype != dt or tuple(t.shape) != shp or t.device != dev):
+                raise ValueError(f"out tensor {nm} must be contiguous {dt} {shp} on {dev}")
+    nbytes = 0
+    if work is not None:
+        if work.device != dev or not work.is_contiguous():
+            raise ValueError("work must be a contiguous tensor on the inputs' device")
+        nbytes = work.numel() * work.element_size()
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        status = lib.ttt_mem_deep_forward_bf16(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(W0), _ptr(S0),
+            _ptr(z), _ptr(W_T), _ptr(S_T), B, H, T, d, int(hidden), int(depth),
+            int(b), _ptr(work), nbytes, stream)
+    _lib.check(name, status)
+    return z, W_T, S_T
+
+
+def deep_status(work):
+    """Synchronize torch's current stream and check the deep-memory status in ``work``."""
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(work.device).cuda_stream
+    with torch.cuda.device(work.device):
+        _lib.check("ttt_mem_deep_status", lib.ttt_mem_deep_status(_ptr(work), stream))

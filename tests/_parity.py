@@ -23,6 +23,27 @@ def rel_err(x, ref):
     return err / rms if rms > 0 else err
 
 
+def bf16_half_ulp(x):
+    """Half a bf16 ulp at each |x| (the most that rounding a float to bf16 moves it)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, np.finfo(np.float64).tiny)))
+    return np.where(a > 0, np.exp2(e - 8), 0.0)
+
+
+def rel_err_bf16_out(x, ref):
+    """``rel_err`` of an output stored in bf16, not counting the rounding of
+    the output itself: each element's error is first reduced by half a bf16
+    ulp of the reference value (never below zero).  The bound then applies to
+    the computation; the storage format adds at most that half ulp."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.maximum(np.abs(x - ref) - bf16_half_ulp(ref), 0.0)))
+    return err / rms if rms > 0 else err
+
+
 def to_dev(inp, device="cuda"):
     return {k: (None if v is None else v.to(device)) for k, v in inp.items()}
 

@@ -120,3 +120,23 @@ def test_varlen_backward_large_document_count_is_checked_not_refused(lib, name):
     # the offsets pointer is a never-read stand-in).
     fake_cu = ctypes.c_void_p(1 << 20)
     assert getattr(lib, name)(*([None] * 19), fake_cu, 100000, 32, 1 << 22, 128, 64, None) == -1
+
+
+def test_deep_sizes(lib):
+    d, h = 64, 256
+    assert lib.ttt_mem_deep_param_count(d, h, 2) == 2 * d * h
+    assert lib.ttt_mem_deep_param_count(d, h, 4) == 2 * d * h + 2 * h * h
+    assert lib.ttt_mem_deep_param_count(d, h, 1) == 0
+    assert lib.ttt_mem_deep_work_bytes(4, 8, d, h, 2) > 0
+    assert lib.ttt_mem_deep_work_bytes(4, 8, 32, h, 2) == 0      # unsupported width
+
+
+def test_deep_rejections_happen_before_any_launch(lib):
+    # q k v theta eta alpha W0 S0 z W_T S_T; B H T d hidden depth b; work, work_bytes, stream
+    def call(B=1, H=1, T=8, d=64, hid=256, depth=2, b=4):
+        return lib.ttt_mem_deep_forward_bf16(*([None] * 11), B, H, T, d, hid, depth, b, None, 0, None)
+    assert call() == -1                 # NULL W0
+    assert call(depth=5) == -2
+    assert call(d=32) == -1             # no parameters to size either way: NULL W0 first
+    assert call(B=0) == -1
+    assert lib.ttt_mem_deep_status(None, None) == -1

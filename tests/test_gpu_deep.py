@@ -1,0 +1,124 @@
+"""GPU parity of the deep-memory entry point with packed parameters (depths 2-4)
+against the float64 oracle ``deep_forward``, and its workspace/status contract.
+
+Every comparison is element by element, per output tensor, as
+max|gpu - oracle| / rms(oracle) <= 2e-2 (bf16 inputs and z, float32
+accumulation and weights).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import deep_forward as oracle_deep
+from tests._parity import TOL, rel_err, rel_err_bf16_out, to_dev
+from test_neural_memory_amd import memory as tm
+from test_neural_memory_amd._lib import TTTError
+from test_neural_memory_amd.workloads import WORKLOADS, make_inputs, to_numpy64
+
+pytestmark = pytest.mark.gpu
+TOL_DEEP = TOL["bf16"]
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _layers(w, depth, seed=5):
+    """Initial layers N(0, 1/fan_in) per head, shared by the batch (the deep-memory recipe)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for (fi, fo) in tm.deep_layer_shapes(w.d, w.hidden, depth):
+        x = rng.standard_normal((w.H, fi, fo)) / np.sqrt(fi)
+        out.append(torch.from_numpy(np.ascontiguousarray(np.broadcast_to(x, (w.B, w.H, fi, fo)), dtype=np.float32)))
+    return out
+
+
+def _run(inp, layers, w, depth, work=None, momenta=None):
+    dev = to_dev(inp)
+    W0 = tm.deep_pack([x.cuda() for x in layers])
+    S0 = None if momenta is None else tm.deep_pack([x.cuda() for x in momenta])
+    z, WT, ST = tm.deep_forward(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"], W0, S0,
+                                hidden=w.hidden, depth=depth, b=w.b, work=work)
+    if work is not None:
+        tm.deep_status(work)
+    torch.cuda.synchronize()
+    return z, tm.deep_unpack(WT, w.d, w.hidden, depth), tm.deep_unpack(ST, w.d, w.hidden, depth)
+
+
+def _check(inp, layers, w, depth, heads, momenta=None, work=None):
+    z, WT, ST = _run(inp, layers, w, depth, work=work, momenta=momenta)
+    bi = np.array([h[0] for h in heads])
+    hi = np.array([h[1] for h in heads])
+    g = {k: (None if v is None else to_numpy64(v)[bi, hi]) for k, v in inp.items() if k in ("q", "k", "v", "theta", "eta", "alpha")}
+    Ws = [to_numpy64(x)[bi, hi] for x in layers]
+    Ss = None if momenta is None else [to_numpy64(x)[bi, hi] for x in momenta]
+    zo, Wo, So = oracle_deep(g["q"], g["k"], g["v"], g["theta"], g["eta"], g["alpha"], Ws, Ss, b=w.b)
+    zg = to_numpy64(z.cpu())[bi, hi]
+    # z is stored in bf16: its own rounding (half an ulp per element) is not
+    # counted against the bound; the plain figure is printed beside it.
+    errs = {"z": rel_err_bf16_out(zg, zo)}
+    _say(f"  z max|err|/rms with the bf16 rounding of z: {rel_err(zg, zo):.2e}")
+    for l in range(depth):
+        errs[f"W{l + 1}_T"] = rel_err(to_numpy64(WT[l].cpu())[bi, hi], Wo[l])
+        errs[f"S{l + 1}_T"] = rel_err(to_numpy64(ST[l].cpu())[bi, hi], So[l])
+    _say("  errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" (tol {TOL_DEEP})")
+    assert max(errs.values()) <= TOL_DEEP, errs
+    return errs
+
+
+def _small(**kw):
+    return WORKLOADS[5].replace(**kw)
+
+
+@pytest.mark.parametrize("depth", [2])
+@pytest.mark.parametrize("label,kw", [("small", dict(B=2, H=3, T=100)), ("ragged-b5", dict(B=1, H=2, T=47, b=5)),
+                                      ("b1", dict(B=1, H=1, T=20, b=1))], ids=lambda x: x if isinstance(x, str) else "")
+def test_small_cases(depth, label, kw):
+    w = _small(**kw)
+    _say(f"case deep depth {depth} {label} {w}")
+    inp = make_inputs(w)
+    layers = _layers(w, depth)
+    work = tm.new_deep_work(w.B, w.H, w.d, w.hidden, depth, "cuda")
+    _check(inp, layers, w, depth, [(i, j) for i in range(w.B) for j in range(w.H)], work=work)
+
+
+@pytest.mark.parametrize("depth", [2])
+def test_titans_gates_and_momenta(depth):
+    w = _small(B=1, H=2, T=160).replace(gates="titans")
+    _say(f"case deep depth {depth} titans gates, nonzero momenta")
+    inp = make_inputs(w, seed=9)
+    layers = _layers(w, depth)
+    rng = np.random.default_rng(11)
+    momenta = [torch.from_numpy((rng.standard_normal(x.shape) * 0.003).astype(np.float32)) for x in layers]
+    _check(inp, layers, w, depth, [(0, 0), (0, 1)], momenta=momenta)
+
+
+def test_depth2_equals_two_layer_entry_point_bitwise():
+    w = _small(B=2, H=2, T=90)
+    inp = make_inputs(w)
+    dev = to_dev(inp)
+    layers = [inp["W1"], inp["W2"]]
+    z, WT, ST = _run(inp, layers, w, 2, work=tm.new_deep_work(w.B, w.H, w.d, w.hidden, 2, "cuda"))
+    z2, W1, W2, S1, S2 = tm.ttt_mem_mlp_forward_bf16(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"],
+                                                     dev["alpha"], dev["W1"], dev["W2"], b=w.b)
+    torch.cuda.synchronize()
+    assert torch.equal(z, z2)
+    for a, b_ in zip(WT + ST, (W1, W2, S1, S2)):
+        assert torch.equal(a, b_)
+
+
+def test_status_and_workspace_errors():
+    w = _small(B=1, H=2, T=32)
+    inp = make_inputs(w)
+    dev = to_dev(inp)
+    layers = _layers(w, 2)
+    W0 = tm.deep_pack([x.cuda() for x in layers])
+    work = tm.new_deep_work(w.B, w.H, w.d, w.hidden, 2, "cuda")
+    args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"], W0)
+    tm.deep_forward(*args, hidden=w.hidden, depth=2, b=w.b, work=work)
+    tm.deep_status(work)
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(TTTError) as e:
+        tm.deep_forward(*args, hidden=w.hidden, depth=2, b=w.b, work=small)
+    assert e.value.status == -1

@@ -164,3 +164,19 @@ def test_chunking_changes_the_result():
     z4 = deep_forward(q, k, v, th, et, al, Ws, b=4)[0]
     np.testing.assert_allclose(z1[0], z4[0], atol=1e-15)      # the first token sees the same state
     assert np.max(np.abs(z1 - z4)) > 1e-6
+
+
+def test_bf16_output_allowance_is_half_an_ulp():
+    # The parity helper that discounts the bf16 rounding of a stored output
+    # subtracts exactly half an ulp: RNE-rounded values score 0, anything a
+    # full ulp off does not.
+    import torch
+    from tests._parity import bf16_half_ulp, rel_err_bf16_out
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(10000) * 3.0
+    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert rel_err_bf16_out(xb, x) == 0.0
+    assert np.all(np.abs(xb - x) <= bf16_half_ulp(x))
+    off = xb + 2 * bf16_half_ulp(x) * np.sign(x)
+    assert rel_err_bf16_out(off, x) > 0.0
+    assert bf16_half_ulp(np.array([1.0, 1.5, 2.0, 0.0])).tolist() == [2.0 ** -8, 2.0 ** -8, 2.0 ** -7, 0.0]
