@@ -145,6 +145,28 @@ int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_
                              uint16_t* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T,
                              int B, int H, int T, int d, int hidden, int b, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and arguments as ttt_mem_mlp_forward_bf16, with the exchange
+ * workspace in a file-scope device array of the library (16.8 MB per GPU,
+ * reserved when the library is loaded and held until the process ends)
+ * instead of an allocation.  It runs at most 8 (batch, head) sequences at a
+ * time (the array holds 8 groups), so larger batches take proportionally
+ * longer; a call whose workspace would not fit the array returns
+ * TTT_ERR_UNSUPPORTED.  Every call on one GPU uses the same array: calls that
+ * overlap in time on one GPU (different streams, other threads) race and
+ * give undefined results; calls in stream order are fine (each launch clears
+ * the counters it needs).  No hipMalloc, hipFree or allocating library
+ * routine is called.
+ */
+int ttt_mem_mlp_forward_bf16_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const float* theta, const float* eta, const float* alpha,
+                                     const float* W1_0, const float* W2_0,
+                                     const float* S1_0, const float* S2_0,
+                                     uint16_t* z, float* W1_T, float* W2_T, float* S1_T, float* S2_T,
+                                     int B, int H, int T, int d, int hidden, int b, void* stream);
+
 /* The same computation with z stored as float32. */
 int ttt_mem_mlp_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   const float* theta, const float* eta, const float* alpha,

@@ -27,6 +27,7 @@ _SIGNATURES = {
     "ttt_mem_forward_bf16_zf32": (_I, [_P] * 11 + [_I] * 5 + [_P]),
     "ttt_mem_mlp_forward_bf16": (_I, [_P] * 15 + [_I] * 6 + [_P]),
     "ttt_mem_mlp_forward_bf16_zf32": (_I, [_P] * 15 + [_I] * 6 + [_P]),
+    "ttt_mem_mlp_forward_bf16_noalloc": (_I, [_P] * 15 + [_I] * 6 + [_P]),
     "ttt_mem_deep_param_count": (ctypes.c_size_t, [_I] * 3),
     "ttt_mem_deep_work_bytes": (ctypes.c_size_t, [_I] * 5),
     "ttt_mem_deep_forward_bf16": (_I, [_P] * 11 + [_I] * 7 + [_P, ctypes.c_size_t, _P]),

@@ -55,6 +55,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ttt_mem.h"
 #include "gfx950.h"
 
@@ -665,6 +667,34 @@ __global__ void deep_init(int* work, int nints) {
 
 namespace {
 
+// Exchange workspace of the entry point that allocates nothing: a file-scope
+// device array (one copy per GPU, held until the process ends).  It holds the
+// header and kScratchGroups groups; larger batches run kScratchGroups groups
+// at a time.  Host code never passes the array's name to a kernel: it takes
+// the array's device address on each GPU once (scratch_ptr) and uses that.
+constexpr int kScratchGroups = 8;
+constexpr size_t kScratchBytes = (static_cast<size_t>(kHdrInts) + kScratchGroups * kCtrStride) * 4 +
+                                 static_cast<size_t>(kScratchGroups) * kRing * kG * kSlot * 4;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the current device (hipGetSymbolAddress
+// once per device, with that device current); NULL on failure.
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch[dev] = ptr;
+    }
+    return g_scratch[dev];
+}
+
 size_t deep_work_bytes_for(long long ngroups) {
     return (static_cast<size_t>(kHdrInts) + static_cast<size_t>(ngroups) * kCtrStride) * 4 +
            static_cast<size_t>(ngroups) * kRing * kG * kSlot * 4;
@@ -697,7 +727,8 @@ struct Layers {
 
 int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta, const float* eta,
                       const float* alpha, const Layers& ly, int depth, void* z, bool z_bf16, int B, int H, int Tlen,
-                      int d, int hidden, int b, void* work, size_t work_bytes, void* stream_) {
+                      int d, int hidden, int b, void* work, size_t work_bytes, void* stream_,
+                      bool use_scratch = false) {
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (B < 0 || H < 0 || Tlen < 0 || b < 1) return TTT_ERR_INVALID_ARG;
     if (d != kD || hidden != kHid || b > kNP || depth != 2) return TTT_ERR_UNSUPPORTED;
@@ -752,12 +783,18 @@ int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return TTT_ERR_HIP;
     if (hipDeviceGetAttribute(&nxcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || nxcc < 1) nxcc = 1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, deep_fwd2, kThreads, 0) != hipSuccess) return TTT_ERR_HIP;
-    const int max_groups = (ncu * occ / kG) / 8 * 8;
+    int max_groups = (ncu * occ / kG) / 8 * 8;
+    if (use_scratch && max_groups > kScratchGroups) max_groups = kScratchGroups;
     if (max_groups < 8) return TTT_ERR_UNSUPPORTED;
     const long long ngroups = deep_groups(BH, max_groups);
     const size_t need = deep_work_bytes_for(ngroups);
     bool own_work = false;
-    if (work) {
+    if (use_scratch) {
+        // The file-scope scratch: no allocation; sizes past it are refused.
+        if (need > kScratchBytes) return TTT_ERR_UNSUPPORTED;
+        work = scratch_ptr();
+        if (!work) return TTT_ERR_HIP;
+    } else if (work) {
         if (!aligned(work, 256) || work_bytes < need) return TTT_ERR_INVALID_ARG;
     } else {
         if (hipMallocAsync(&work, need, stream) != hipSuccess) return TTT_ERR_HIP;
@@ -854,6 +891,19 @@ int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_
     const Layers ly{{W1_0, W2_0}, {S1_0, S2_0}, {W1_T, W2_T}, {S1_T, S2_T}, {s1, s1},
                     {{W1_0, S1_0, W1_T, S1_T, tb}, {W2_0, S2_0, W2_T, S2_T, tb}}, 2};
     return deep_forward_impl(q, k, v, theta, eta, alpha, ly, 2, z, true, B, H, T, d, hidden, b, nullptr, 0, stream);
+}
+
+int ttt_mem_mlp_forward_bf16_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,
+                                     const float* eta, const float* alpha, const float* W1_0, const float* W2_0,
+                                     const float* S1_0, const float* S2_0, uint16_t* z, float* W1_T, float* W2_T,
+                                     float* S1_T, float* S2_T, int B, int H, int T, int d, int hidden, int b,
+                                     void* stream) {
+    const long long s1 = static_cast<long long>(d) * hidden;
+    const size_t tb = static_cast<size_t>(B > 0 && H > 0 ? static_cast<long long>(B) * H : 0) * s1 * 4;
+    const Layers ly{{W1_0, W2_0}, {S1_0, S2_0}, {W1_T, W2_T}, {S1_T, S2_T}, {s1, s1},
+                    {{W1_0, S1_0, W1_T, S1_T, tb}, {W2_0, S2_0, W2_T, S2_T, tb}}, 2};
+    return deep_forward_impl(q, k, v, theta, eta, alpha, ly, 2, z, true, B, H, T, d, hidden, b, nullptr, 0, stream,
+                             true);
 }
 
 int ttt_mem_mlp_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,

@@ -444,6 +444,22 @@ def ttt_mem_mlp_forward_bf16(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0=None, 
         name = "ttt_mem_mlp_forward_bf16_zf32"
     else:
         raise TypeError(f"unsupported z dtype {z_dtype}")
+    return _mlp_forward(name, z_dtype, q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0, S2_0, b, out)
+
+
+def ttt_mem_mlp_forward_bf16_noalloc(q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0=None, S2_0=None, *, b, out):
+    """As :func:`ttt_mem_mlp_forward_bf16` (bf16 z), with the library allocating
+    no device memory: ``out`` (preallocated ``(z, W1_T, W2_T, S1_T, S2_T)``) is
+    required and the exchange workspace is the library's fixed per-GPU array, so
+    calls that overlap in time on one GPU race.  At most 8 sequences run at a time.
+    """
+    if out is None or any(t is None for t in out):
+        raise ValueError("the no-allocation entry point needs every output preallocated")
+    return _mlp_forward("ttt_mem_mlp_forward_bf16_noalloc", torch.bfloat16, q, k, v, theta, eta, alpha, W1_0, W2_0,
+                        S1_0, S2_0, b, out)
+
+
+def _mlp_forward(name, z_dtype, q, k, v, theta, eta, alpha, W1_0, W2_0, S1_0, S2_0, b, out):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
     B, H, T, d = q.shape

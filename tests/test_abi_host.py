@@ -15,7 +15,8 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
     assert {"ttt_mem_forward_f32", "ttt_mem_forward_bf16", "ttt_mem_forward_bf16_zf32", "ttt_mem_mlp_forward_bf16",
-            "ttt_mem_mlp_forward_bf16_zf32", "ttt_mem_status_string", "ttt_mem_abi_version"} <= set(names)
+            "ttt_mem_mlp_forward_bf16_zf32", "ttt_mem_mlp_forward_bf16_noalloc", "ttt_mem_status_string",
+            "ttt_mem_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -57,7 +58,7 @@ def test_empty_batch_returns_ok_without_pointers(lib, name):
 
 
 def test_mlp_rejections_happen_before_any_launch(lib):
-    for name in ("ttt_mem_mlp_forward_bf16", "ttt_mem_mlp_forward_bf16_zf32"):
+    for name in ("ttt_mem_mlp_forward_bf16", "ttt_mem_mlp_forward_bf16_zf32", "ttt_mem_mlp_forward_bf16_noalloc"):
         def call(B=1, H=1, T=8, d=64, hid=256, b=4):
             return getattr(lib, name)(*([None] * 15), B, H, T, d, hid, b, None)
         assert call() == -1                 # NULL weights
