@@ -388,7 +388,7 @@ def backward_main(args):
     ST = torch.empty_like(MT)
     nch = (T + w.b - 1) // w.b
     ckpt = tm.new_ckpt(dev["q"], w.b)
-    work = torch.empty_like(ckpt)
+    work = torch.empty(tm.backward_work_bytes(dev["q"], w.b), dtype=torch.uint8, device="cuda")
     gl = nch if cg else T
     outs = [torch.empty(B, H, T, d, dtype=torch.float32, device="cuda") for _ in range(3)] + \
            [torch.empty(B, H, gl, dtype=torch.float32, device="cuda") for _ in range(3)] + \
@@ -575,7 +575,7 @@ def varlen_train_main(args):
     MT = torch.empty(N, H, d, d, dtype=torch.float32, device="cuda")
     ST = torch.empty_like(MT)
     ckpt = tm.new_ckpt_varlen(dev["q"], cu, b)
-    work = torch.empty_like(ckpt)
+    work = torch.empty(tm.backward_work_bytes(dev["q"], b, cu), dtype=torch.uint8, device="cuda")
     outs = [torch.empty(H, T, d, dtype=torch.float32, device="cuda") for _ in range(3)] + \
            [torch.empty(H, T, dtype=torch.float32, device="cuda") for _ in range(3)] + \
            [torch.empty(N, H, d, d, dtype=torch.float32, device="cuda") for _ in range(2)]

@@ -307,12 +307,23 @@ int ttt_mem_decode_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *     dq, dk, dv                 [B, H, T, d] float32 (both entry points),
  *     dtheta, deta, dalpha       [B, H, T]    float32,
  *     dM0, dS0                   [B, H, d, d] float32 (NULL: not written).
- * work is a caller-owned scratch buffer of the checkpoints' type and size
- * (the derivatives with respect to the state leaving every chunk); its
- * contents on entry do not matter and on return are unspecified.
+ * work is a caller-owned scratch buffer (the derivatives with respect to the
+ * state leaving every chunk): for the _f32 entry points of the checkpoints'
+ * type and size (ttt_mem_ckpt_bytes), for the _bf16 ones of
+ * ttt_mem_backward_work_bytes_bf16 bytes (the fp16 checkpoints' size plus a
+ * few floats per sequence); its contents on entry do not matter and on return
+ * are unspecified.
  * The bf16 entry point takes q, k, v in bf16 and computes its matrix products
  * with fp16 operands and float32 accumulation, as the bf16 forward does; the
  * float32 one uses float32 products.
+ * Cotangent range (bf16 entry points): dz, dM_T and dS_T may have any finite
+ * float32 magnitude.  Each sequence's cotangents are multiplied by one power
+ * of two that brings their largest magnitude into [1, 2) before they are
+ * rounded to fp16, and every gradient is divided by it again (both exact), so
+ * the small values of a mean-reduced loss (1e-6 .. 1e-9) keep fp16's relative
+ * precision.  Entries below about 2^-14 of their sequence's largest magnitude
+ * fall into fp16's subnormal range (absolute error up to 2^-25 of that
+ * magnitude).  Non-finite cotangents propagate (no scaling is applied).
  * Argument rules as for the forward: sizes, alignment (16 bytes for every
  * array except the gate arrays and their gradients, 4 bytes), no overlap
  * between any output and any other argument (dM0 may not alias dM_T).
@@ -331,10 +342,14 @@ int ttt_mem_forward_ckpt_bf16(const uint16_t* q, const uint16_t* k, const uint16
                               float* z, float* M_T, float* S_T, uint16_t* ckpt,
                               int B, int H, int T, int d, int b, void* stream);
 
-/* Bytes of ckpt (and of the backward's work buffer) for the _f32 and the
- * _bf16 entry points; 0 for negative sizes. */
+/* Bytes of ckpt for the _f32 and the _bf16 entry points (and of the _f32
+ * backward's work buffer); 0 for negative sizes. */
 size_t ttt_mem_ckpt_bytes(int B, int H, int T, int d, int b);
 size_t ttt_mem_ckpt_bytes_bf16(int B, int H, int T, int d, int b);
+
+/* Bytes of the work buffer of ttt_mem_backward_bf16 and ttt_mem_backward_cg_bf16
+ * (16-byte aligned, as every array); 0 for negative sizes. */
+size_t ttt_mem_backward_work_bytes_bf16(int B, int H, int T, int d, int b);
 
 int ttt_mem_backward_f32(const float* q, const float* k, const float* v,
                          const float* theta, const float* eta, const float* alpha,
@@ -405,7 +420,9 @@ int ttt_mem_backward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_
  *   Checkpoints and work buffer: [H][ceil(T/b) + N][M | S][d][d], float32 on
  *     the f32 entry points and fp16 on the bf16 ones, of
  *     ttt_mem_ckpt_bytes_varlen / ttt_mem_ckpt_bytes_varlen_bf16 bytes, caller
- *     owned.  Document s of head h uses the slots from h * (ceil(T/b) + N) +
+ *     owned; the bf16 backward's work buffer takes
+ *     ttt_mem_backward_work_bytes_varlen_bf16 bytes (the cotangent scaling is
+ *     per document and head).  Document s of head h uses the slots from h * (ceil(T/b) + N) +
  *     (the chunks of documents 0..s-1) on; the rest are not written.  A
  *     table that is not non-decreasing can make documents overlap; results
  *     are then undefined, and a document whose chunks would pass the head's
@@ -421,6 +438,7 @@ int ttt_mem_backward_cg_bf16(const uint16_t* q, const uint16_t* k, const uint16_
  */
 size_t ttt_mem_ckpt_bytes_varlen(int N, int H, int T, int d, int b);
 size_t ttt_mem_ckpt_bytes_varlen_bf16(int N, int H, int T, int d, int b);
+size_t ttt_mem_backward_work_bytes_varlen_bf16(int N, int H, int T, int d, int b);
 
 int ttt_mem_forward_varlen_ckpt_f32(const float* q, const float* k, const float* v,
                                     const float* theta, const float* eta, const float* alpha,
@@ -456,7 +474,7 @@ const char* ttt_mem_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ttt_mem_abi_version(void);
 
-#define TTT_MEM_ABI_VERSION ((2 << 16) | 0)
+#define TTT_MEM_ABI_VERSION ((3 << 16) | 0)
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libttt_mem.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "ttt_mem.h")
 
 _lib = None
-ABI_MAJOR = 2
+ABI_MAJOR = 3
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -40,6 +40,7 @@ _SIGNATURES = {
     "ttt_mem_forward_ckpt_bf16": (_I, [_P] * 12 + [_I] * 5 + [_P]),
     "ttt_mem_ckpt_bytes": (ctypes.c_size_t, [_I] * 5),
     "ttt_mem_ckpt_bytes_bf16": (ctypes.c_size_t, [_I] * 5),
+    "ttt_mem_backward_work_bytes_bf16": (ctypes.c_size_t, [_I] * 5),
     "ttt_mem_backward_f32": (_I, [_P] * 19 + [_I] * 5 + [_P]),
     "ttt_mem_backward_bf16": (_I, [_P] * 19 + [_I] * 5 + [_P]),
     "ttt_mem_forward_cg_f32": (_I, [_P] * 12 + [_I] * 5 + [_P]),
@@ -48,6 +49,7 @@ _SIGNATURES = {
     "ttt_mem_backward_cg_bf16": (_I, [_P] * 19 + [_I] * 5 + [_P]),
     "ttt_mem_ckpt_bytes_varlen": (ctypes.c_size_t, [_I] * 5),
     "ttt_mem_ckpt_bytes_varlen_bf16": (ctypes.c_size_t, [_I] * 5),
+    "ttt_mem_backward_work_bytes_varlen_bf16": (ctypes.c_size_t, [_I] * 5),
     "ttt_mem_forward_varlen_ckpt_f32": (_I, [_P] * 13 + [_I] * 5 + [_P]),
     "ttt_mem_forward_varlen_ckpt_bf16": (_I, [_P] * 13 + [_I] * 5 + [_P]),
     "ttt_mem_backward_varlen_f32": (_I, [_P] * 20 + [_I] * 5 + [_P]),

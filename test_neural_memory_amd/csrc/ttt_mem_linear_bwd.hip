@@ -50,6 +50,13 @@
 // range; states, cotangents and P are rounded to fp16 where they enter a
 // product) with float32 accumulation, float32 carried cotangents and float32
 // gate arithmetic.
+//
+// The backward is linear in the cotangents (dz, dM', dS').  On the bf16 path a
+// first kernel takes the largest magnitude of each sequence's cotangents, and
+// both kernels multiply every cotangent they round to fp16 by a power of two
+// that brings that magnitude into [1, 2), then divide every gradient they
+// write by it: exact in float32, and small cotangents (a mean-reduced loss
+// gives 1e-6 .. 1e-9) stay in fp16's normal range instead of its subnormals.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -64,6 +71,59 @@ namespace {
 
 constexpr int kW = 64;
 constexpr int kLdsMax = 160 * 1024;
+// Partial maxima of the cotangents' magnitude per sequence.
+constexpr int kScaleParts = 16;
+
+// Power of two that brings the largest cotangent magnitude of sequence g into
+// [1, 2): the maximum over its kScaleParts partial maxima.  1 when
+// there are none (NULL), when all are zero, or when one is not finite.
+__device__ __forceinline__ float cot_scale(const float* smax, int g) {
+    if (!smax) return 1.f;
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < kScaleParts; ++i) m = fmaxf(m, smax[static_cast<size_t>(g) * kScaleParts + i]);
+    if (!(m > 0.f) || !(m <= 3.0e38f)) return 1.f;
+    const int e = min(max(ilogbf(m), -126), 126);
+    return ldexpf(1.f, -e);
+}
+
+// Partial maxima of |dz|, |dM_T|, |dS_T| per sequence g (dense: sequence bh,
+// tokens g*T .. g*T+T-1; packed documents: document g / H of head g % H, its
+// tokens of row h): workgroup (g, part) covers every kScaleParts-th 256-unit
+// stretch of the sequence's dz and, for part 0, its d x d state cotangents,
+// and writes one value.
+__global__ __launch_bounds__(256) void cot_absmax(const float* __restrict__ dz, const float* __restrict__ dMT,
+                                                  const float* __restrict__ dST, float* __restrict__ out, int T,
+                                                  int d, const int* __restrict__ cu, int H) {
+    const int g = blockIdx.x / kScaleParts, part = blockIdx.x % kScaleParts;
+    size_t tok0 = static_cast<size_t>(g) * T;
+    int len = T;
+    if (cu) {
+        int t0;
+        len = doc_len(cu, g / H, T, t0);
+        tok0 = static_cast<size_t>(g % H) * T + t0;
+    }
+    const float4* z4 = reinterpret_cast<const float4*>(dz + tok0 * d);
+    const size_t nz4 = static_cast<size_t>(len) * d / 4;
+    auto amax4 = [](float m, const float4 v) {
+        return fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    };
+    float m = 0.f;
+    for (size_t u = static_cast<size_t>(part) * 256 + threadIdx.x; u < nz4; u += static_cast<size_t>(kScaleParts) * 256)
+        m = amax4(m, z4[u]);
+    if (part == 0) {
+        const size_t dd4 = static_cast<size_t>(d) * d / 4, base = static_cast<size_t>(g) * d * d;
+        for (size_t e = threadIdx.x; e < dd4; e += 256) {
+            if (dMT) m = amax4(m, reinterpret_cast<const float4*>(dMT + base)[e]);
+            if (dST) m = amax4(m, reinterpret_cast<const float4*>(dST + base)[e]);
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    __shared__ float wm[4];
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+}
 
 __host__ __device__ constexpr int bmax(int a, int b) { return a > b ? a : b; }
 
@@ -286,6 +346,8 @@ struct CarryParams {
     const int* cu;
     int H;
     int tcmax;
+    // Partial maxima of the cotangents per sequence bh; NULL: no scaling.
+    const float* smax;
 };
 
 template <typename T, int D, int NS, int NP>
@@ -395,7 +457,7 @@ struct Carry {
     }
     // n: the chunk's token count (positions at or past it are written as zero
     // and as the identity gates).
-    __device__ static void commit(const Regs& r, typename Sm::QSlot& s, int n, int lane, int lw) {
+    __device__ static void commit(const Regs& r, typename Sm::QSlot& s, int n, int lane, int lw, float sc) {
 #pragma unroll
         for (int i = 0; i < NQU; ++i) {
             const int u = lane + (lw + i * NLW) * kW;
@@ -411,7 +473,7 @@ struct Carry {
             const int u = lane + (lw + i * NLW) * kW;
             if (u < NP * UZ) {
                 const int t = u / UZ, col = (u % UZ) * 4;
-                st4<T>(s.dz + t * LZ + col, t < n ? r.z[i] : f32x4{0.f, 0.f, 0.f, 0.f});
+                st4<T>(s.dz + t * LZ + col, t < n ? sc * r.z[i] : f32x4{0.f, 0.f, 0.f, 0.f});
             }
         }
         if (lw == 0 && lane < NP) {
@@ -424,7 +486,7 @@ struct Carry {
 
     // Serial schedule (one slot): load and stage directly.
     __device__ static void load_direct(const CarryParams& p, typename Sm::QSlot& s, size_t tok0, int n, int row0,
-                                       int lane, size_t g0, int gs) {
+                                       int lane, size_t g0, int gs, float sc) {
         const G* q = static_cast<const G*>(p.q);
         const G* k = static_cast<const G*>(p.k);
         for (int u = lane; u < NP * UR; u += kW) {
@@ -438,7 +500,7 @@ struct Carry {
             const int t = u / UZ, col = (u % UZ) * 4;
             const f32x4 v = t < n ? *reinterpret_cast<const f32x4*>(p.dz + (tok0 + t) * D + row0 + col)
                                   : f32x4{0.f, 0.f, 0.f, 0.f};
-            st4<T>(s.dz + t * LZ + col, v);
+            st4<T>(s.dz + t * LZ + col, sc * v);
         }
         for (int l = lane; l < NP; l += kW) {
             const bool ok = l < n;
@@ -557,6 +619,10 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         w_chunk0 = static_cast<size_t>(h) * p.tcmax + pre;
     }
     const int row_wg = rb * Gm::RB;
+    // Every cotangent enters scaled by sc; dv, dM0, dS0 leave divided by it
+    // (the work buffer keeps the scaled cotangents for the gradient kernel).
+    const float sc = cot_scale(p.smax, bh);
+    const float isc = 1.f / sc;
     auto chunk_of = [&](int u) { return nch - 1 - u; };
     auto chunk_n = [&](int c) { return min(p.b, seqlen - c * p.b); };
     // Gate entry of token 0 of chunk c, and the step between tokens.
@@ -576,7 +642,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         C::issue(p, lr_regs, seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane, lw, gate0(c),
                  gstride);
     };
-    auto do_commit = [&](int u) { C::commit(lr_regs, sm.qs[u % Gm::NQ], chunk_n(chunk_of(u)), lane, lw); };
+    auto do_commit = [&](int u) { C::commit(lr_regs, sm.qs[u % Gm::NQ], chunk_n(chunk_of(u)), lane, lw, sc); };
     auto do_build = [&](int u) {
         const int c = chunk_of(u);
         C::build(sm.qs[u % Gm::NQ], sm.ps[u % Gm::NPR], sm.ls, chunk_n(c), lane);
@@ -593,8 +659,10 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         for (int jt = 0; jt < NCT; ++jt) {
             const int col = O::tmap(jt, 4 * lg);
             const bool ok = col < D;
-            dM[jt] = (p.dMT && ok) ? *reinterpret_cast<const f32x4*>(p.dMT + st_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-            dS[jt] = (p.dST && ok) ? *reinterpret_cast<const f32x4*>(p.dST + st_off + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+            dM[jt] = (p.dMT && ok) ? sc * *reinterpret_cast<const f32x4*>(p.dMT + st_off + col)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+            dS[jt] = (p.dST && ok) ? sc * *reinterpret_cast<const f32x4*>(p.dST + st_off + col)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
     auto state_final = [&]() {
@@ -602,8 +670,8 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         for (int jt = 0; jt < NCT; ++jt) {
             const int col = O::tmap(jt, 4 * lg);
             if (col < D) {
-                if (p.dM0) *reinterpret_cast<f32x4*>(p.dM0 + st_off + col) = dM[jt];
-                if (p.dS0) *reinterpret_cast<f32x4*>(p.dS0 + st_off + col) = dS[jt];
+                if (p.dM0) *reinterpret_cast<f32x4*>(p.dM0 + st_off + col) = isc * dM[jt];
+                if (p.dS0) *reinterpret_cast<f32x4*>(p.dS0 + st_off + col) = isc * dS[jt];
             }
         }
     };
@@ -653,7 +721,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
             for (int e = 0; e < 4; ++e) {
                 const int t = O::tmap(tt, 4 * lg + e);
                 dE[tt][e] = -(ps.wm[t] * x1[e] + ps.ws[t] * x2[e] + x3[e]);
-                if (t < n) p.dv[(tok0 + t) * D + r0 + lr] = -dE[tt][e];
+                if (t < n) p.dv[(tok0 + t) * D + r0 + lr] = -isc * dE[tt][e];
             }
         }
         // Carry: dM <- A dM + Q^T diag(A) dZ + K^T dE, dS <- c dM + E dS + Q^T diag(c) dZ.
@@ -731,7 +799,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
             if (w == NS) {
                 const int c = chunk_of(u);
                 C::load_direct(p, sm.qs[0], seq_tok + static_cast<size_t>(c) * p.b, chunk_n(c), row_wg, lane,
-                               gate0(c), gstride);
+                               gate0(c), gstride, sc);
             }
             __syncthreads();
             if (is_builder) do_build(u);
@@ -773,6 +841,7 @@ struct GradParams {
     const int* cu;
     int H;
     int tcmax;
+    const float* smax;   // as for the carry
 };
 
 template <typename T, int D, int NP>
@@ -898,6 +967,10 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         tok0 = static_cast<size_t>(bh) * p.T + static_cast<size_t>(c) * p.b;
         slot = static_cast<size_t>(bh) * p.nch + c;
     }
+    // Cotangents enter scaled by sc (the work buffer already is); every
+    // gradient leaves divided by it.
+    const float sc = cot_scale(p.smax, bh);
+    const float isc = 1.f / sc;
     const T* Mc = static_cast<const T*>(p.ckpt) + slot * (2 * D * D);
     const T* Sc = Mc + D * D;
     const T* dMe = static_cast<const T*>(p.work) + slot * (2 * D * D);
@@ -937,8 +1010,8 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 const size_t g = ok ? (tok0 + t) * D + col : 0;
                 const f32x4 z4 = *reinterpret_cast<const f32x4*>(p.dz + g);
                 const f32x4 v4 = *reinterpret_cast<const f32x4*>(p.dv + g);
-                za[i] = ok ? z4 : f32x4{0.f, 0.f, 0.f, 0.f};
-                va[i] = ok ? -v4 : f32x4{0.f, 0.f, 0.f, 0.f};
+                za[i] = ok ? sc * z4 : f32x4{0.f, 0.f, 0.f, 0.f};
+                va[i] = ok ? -sc * v4 : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
 #pragma unroll
@@ -979,6 +1052,7 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         if constexpr (Gm::DZ_LDS) {
             return R::rm(lds, LQ, t, k0, lg);
         } else {
+            sign *= sc;
             float x[KS];
             const int col = k0 + KS * lg;
             const bool ok = t < n && col < D;
@@ -1211,14 +1285,14 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
             const float sa2 = wave_sum(l < n ? da : 0.f);
             if (l == 0) {
                 const size_t gi = static_cast<size_t>(bh) * p.nch + c;
-                p.dth[gi] = st;
-                p.deta[gi] = se2;
-                p.dal[gi] = -sa2;
+                p.dth[gi] = isc * st;
+                p.deta[gi] = isc * se2;
+                p.dal[gi] = -isc * sa2;
             }
         } else if (l < n) {
-            p.dth[tok0 + l] = dth;
-            p.deta[tok0 + l] = de;
-            p.dal[tok0 + l] = -da;
+            p.dth[tok0 + l] = isc * dth;
+            p.deta[tok0 + l] = isc * de;
+            p.dal[tok0 + l] = -isc * da;
         }
     } else {
         // ===================== feature wave =====================
@@ -1450,8 +1524,8 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 }
                 const int t = 16 * tt + lr;
                 if (t < n) {
-                    *reinterpret_cast<f32x4*>(p.dq + (tok0 + t) * D + f0 + 4 * lg) = dQ[ft][tt];
-                    *reinterpret_cast<f32x4*>(p.dk + (tok0 + t) * D + f0 + 4 * lg) = dK[ft][tt];
+                    *reinterpret_cast<f32x4*>(p.dq + (tok0 + t) * D + f0 + 4 * lg) = isc * dQ[ft][tt];
+                    *reinterpret_cast<f32x4*>(p.dk + (tok0 + t) * D + f0 + 4 * lg) = isc * dK[ft][tt];
                 }
             }
         }
@@ -1500,6 +1574,14 @@ hipError_t launch_bwd_np(const CarryParams& cp, const GradParams& gp, int b, hip
 }
 
 
+// The bf16 entry points' work buffer: the cotangent slots (the checkpoints'
+// size), then at the next 256-byte boundary kScaleParts floats per sequence
+// (per document and head for packed documents).
+size_t scale_offset(size_t ck_b) { return (ck_b + 255) / 256 * 256; }
+size_t bwd_work_bytes_bf16(size_t ck_b, long long groups) {
+    return scale_offset(ck_b) + static_cast<size_t>(groups) * kScaleParts * sizeof(float);
+}
+
 template <typename T>
 int backward_impl(const void* q, const void* k, const void* v, const float* theta, const float* eta,
                   const float* alpha, const void* ckpt, const float* dz, const float* dMT, const float* dST,
@@ -1533,6 +1615,10 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
     const size_t st_b = static_cast<size_t>(BH) * d * d * 4;
     const size_t ck_b = packed ? ckpt_bytes_varlen(B, H, Tlen, d, b, sizeof(T)) : ckpt_bytes(B, H, Tlen, d, b, sizeof(T));
     const size_t cu_b = packed ? (static_cast<size_t>(B) + 1) * sizeof(int) : 0;
+    // fp16 operands: per-group power-of-two scaling of the cotangents.
+    constexpr bool kScaled = !std::is_same<T, float>::value;
+    const long long groups = BH;
+    const size_t work_b = kScaled ? bwd_work_bytes_bf16(ck_b, groups) : ck_b;
     if (Tlen > 0) {
         const void* req[] = {q, k, v, theta, eta, alpha, ckpt, dz, dq, dk, dv, dth, deta, dal, work};
         for (const void* r : req)
@@ -1551,7 +1637,7 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
     const Span ins[] = {{q, in_b}, {k, in_b}, {v, in_b}, {theta, g_b}, {eta, g_b}, {alpha, g_b},
                         {ckpt, ck_b}, {dz, f_b}, {dMT, st_b}, {dST, st_b}, {cu, cu_b}};
     const Span outs[] = {{dq, f_b}, {dk, f_b}, {dv, f_b}, {dth, g_b}, {deta, g_b}, {dal, g_b},
-                         {dM0, st_b}, {dS0, st_b}, {work, ck_b}};
+                         {dM0, st_b}, {dS0, st_b}, {work, work_b}};
     const int n_outs = static_cast<int>(sizeof(outs) / sizeof(outs[0]));
     for (int i = 0; i < n_outs; ++i) {
         if (outs[i].n == 0) continue;
@@ -1562,11 +1648,19 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
     }
 
     const int cg = chunk_gates ? 1 : 0;
-    const CarryParams cp{q, k, dz, theta, eta, alpha, dMT, dST, work, dv, dM0, dS0,
-                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax)};
-    const GradParams gp{q, k, v, theta, eta, alpha, ckpt, work, dz, dv, dq, dk, dth, deta, dal,
-                        static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax)};
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    float* smax = nullptr;
+    if (kScaled && Tlen > 0) {
+        smax = reinterpret_cast<float*>(static_cast<char*>(work) + scale_offset(ck_b));
+        hipLaunchKernelGGL(cot_absmax, dim3(static_cast<unsigned>(groups * kScaleParts)), dim3(256), 0, s, dz, dMT,
+                           dST, smax, Tlen, d, cu, H);
+        const hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return TTT_ERR_HIP;
+    }
+    const CarryParams cp{q, k, dz, theta, eta, alpha, dMT, dST, work, dv, dM0, dS0,
+                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax), smax};
+    const GradParams gp{q, k, v, theta, eta, alpha, ckpt, work, dz, dv, dq, dk, dth, deta, dal,
+                        static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax), smax};
     hipError_t err;
     switch (d) {
         case 16: err = launch_bwd_np<T, 16>(cp, gp, b, s); break;
@@ -1597,6 +1691,16 @@ int ttt_mem_backward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           int d, int b, void* stream) {
     return backward_impl<_Float16>(q, k, v, theta, eta, alpha, ckpt, dz, dM_T, dS_T, dq, dk, dv, dtheta, deta,
                                    dalpha, dM0, dS0, work, B, H, T, d, b, stream);
+}
+
+size_t ttt_mem_backward_work_bytes_bf16(int B, int H, int T, int d, int b) {
+    if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1) return 0;
+    return bwd_work_bytes_bf16(ckpt_bytes(B, H, T, d, b, 2), static_cast<long long>(B) * H);
+}
+
+size_t ttt_mem_backward_work_bytes_varlen_bf16(int N, int H, int T, int d, int b) {
+    if (N < 0 || H < 0 || T < 0 || d < 1 || b < 1) return 0;
+    return bwd_work_bytes_bf16(ckpt_bytes_varlen(N, H, T, d, b, 2), static_cast<long long>(N) * H);
 }
 
 int ttt_mem_backward_cg_f32(const float* q, const float* k, const float* v, const float* theta, const float* eta,

@@ -189,8 +189,8 @@ def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, w
     the derivatives of the outer loss with respect to ``z, M_T, S_T``.
     Returns ``(dq, dk, dv, dtheta, deta, dalpha, dM0, dS0)``, all float32
     (``dM0, dS0`` are None when ``want_state_grads`` is False).  ``work`` may
-    pass a scratch tensor shaped and typed like ``ckpt``; ``out`` preallocated
-    outputs in the same order.
+    pass a contiguous scratch tensor of at least ``backward_work_bytes(q, b)``
+    bytes; ``out`` preallocated outputs in the same order.
     """
     suffix = "_cg" if chunk_gates else ""
     if q.dtype == torch.float32:
@@ -220,10 +220,7 @@ def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, w
     dz = _as_dev(dz, "dz", torch.float32, (B, H, T, d), dev)
     dM_T = _as_dev(dM_T, "dM_T", torch.float32, (B, H, d, d), dev)
     dS_T = _as_dev(dS_T, "dS_T", torch.float32, (B, H, d, d), dev)
-    if work is None:
-        work = torch.empty(ck_shape, dtype=cdt, device=dev)
-    else:
-        work = _as_dev(work, "work", cdt, ck_shape, dev)
+    work = _work_buffer(work, backward_work_bytes(q, b), dev)
     shapes = [(B, H, T, d)] * 3 + [(B, H, gl)] * 3 + [(B, H, d, d)] * 2
     if out is None:
         out = [torch.empty(s_, dtype=torch.float32, device=dev) for s_ in shapes]
@@ -243,6 +240,29 @@ def backward(q, k, v, theta, eta, alpha, ckpt, dz, dM_T=None, dS_T=None, *, b, w
             _ptr(dM_T), _ptr(dS_T), *[_ptr(t) for t in out], _ptr(work), B, H, T, d, b, stream)
     _lib.check(name, status)
     return tuple(out)
+
+
+def backward_work_bytes(q, b, cu_seqlens=None):
+    """Bytes of the backward's work buffer for inputs like ``q`` (``[B, H, T, d]``,
+    or ``[H, T, d]`` with ``cu_seqlens`` for packed documents) and chunk size ``b``."""
+    lib = _lib.load()
+    bf = q.dtype == torch.bfloat16
+    if cu_seqlens is None:
+        B, H, T, d = q.shape
+        fn = lib.ttt_mem_backward_work_bytes_bf16 if bf else lib.ttt_mem_ckpt_bytes
+        return int(fn(B, H, T, d, int(b)))
+    H, T, d = q.shape
+    N = cu_seqlens.numel() - 1
+    fn = lib.ttt_mem_backward_work_bytes_varlen_bf16 if bf else lib.ttt_mem_ckpt_bytes_varlen
+    return int(fn(N, H, T, d, int(b)))
+
+
+def _work_buffer(work, nbytes, dev):
+    if work is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if not work.is_contiguous() or work.device != dev or work.numel() * work.element_size() < nbytes:
+        raise ValueError(f"work must be a contiguous tensor of at least {nbytes} bytes on {dev}")
+    return work
 
 
 class LinearMemoryFunction(torch.autograd.Function):
@@ -388,7 +408,7 @@ def backward_varlen(q, k, v, theta, eta, alpha, cu_seqlens, ckpt, dz, dM_T=None,
     dz = _as_dev(dz, "dz", torch.float32, (H, T, d), dev)
     dM_T = _as_dev(dM_T, "dM_T", torch.float32, (N, H, d, d), dev)
     dS_T = _as_dev(dS_T, "dS_T", torch.float32, (N, H, d, d), dev)
-    work = torch.empty(ck_shape, dtype=cdt, device=dev) if work is None else _as_dev(work, "work", cdt, ck_shape, dev)
+    work = _work_buffer(work, backward_work_bytes(q, b, cu), dev)
     shapes = [(H, T, d)] * 3 + [(H, T)] * 3 + [(N, H, d, d)] * 2
     if out is None:
         out = [torch.empty(s_, dtype=torch.float32, device=dev) for s_ in shapes]

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ttt_mem_abi_version() == (2 << 16) | 0
+    assert lib.ttt_mem_abi_version() == (3 << 16) | 0
     assert lib.ttt_mem_abi_version() >> 16 == _lib.ABI_MAJOR
     assert lib.ttt_mem_status_string(0) == b"ok"
     for s in (-1, -2, -3, 12345):
@@ -92,6 +92,19 @@ def test_backward_rejections_happen_before_any_launch(lib, name):
     assert call(b=65) == -2
     assert call(T=-1) == -1
     assert call(B=0) == 0                    # nothing to do: no pointer is touched
+
+
+def test_backward_work_bytes(lib):
+    # bf16 backward: the fp16 cotangent slots, then 16 floats per sequence (per
+    # document and head for packed documents) at the next 256-byte boundary.
+    ck = lib.ttt_mem_ckpt_bytes_bf16(2, 3, 130, 64, 64)
+    assert lib.ttt_mem_backward_work_bytes_bf16(2, 3, 130, 64, 64) == (ck + 255) // 256 * 256 + 2 * 3 * 16 * 4
+    ck = lib.ttt_mem_ckpt_bytes_bf16(1, 1, 5, 16, 4)
+    assert lib.ttt_mem_backward_work_bytes_bf16(1, 1, 5, 16, 4) == (ck + 255) // 256 * 256 + 16 * 4
+    ck = lib.ttt_mem_ckpt_bytes_varlen_bf16(3, 2, 100, 16, 8)
+    assert lib.ttt_mem_backward_work_bytes_varlen_bf16(3, 2, 100, 16, 8) == (ck + 255) // 256 * 256 + 3 * 2 * 16 * 4
+    assert lib.ttt_mem_backward_work_bytes_bf16(-1, 1, 8, 16, 8) == 0
+    assert lib.ttt_mem_backward_work_bytes_varlen_bf16(1, 1, 8, 16, 0) == 0
 
 
 def test_ckpt_bytes_varlen(lib):

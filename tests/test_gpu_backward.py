@@ -160,43 +160,86 @@ def test_autograd_function_matches_direct_call():
         assert torch.equal(leaves[key].grad, ref), nm
 
 
+def _prefix_errors(got, ref, t0, t1, b):
+    """Errors of full-size gradients over tokens [0, t1) whose loss sits on
+    tokens [t0, t1).  Backward of the window the gradients shrink about tenfold
+    per chunk (the forget gate), down to ~1e-27 of the window's at token 0.
+    fp16 operands resolve a value relative to its sequence's largest cotangent,
+    not relative to itself, so: the window and the 4 chunks before it are
+    bounded by each output's own rms there; every earlier token by the
+    window's rms of that output (an absolute bound at the loss's scale)."""
+    errs = {}
+    near = slice(max(t0 - 4 * b, 0), t0)
+    for nm, x, r in zip(NAMES[:6], got, ref):
+        errs[nm] = rel_err(x[t0:t1], r[t0:t1])
+        if t0 > 0:
+            errs[nm + "-near"] = rel_err(x[near], r[near])
+            scale = np.sqrt(np.mean(r[t0:t1] ** 2))
+            errs[nm + "-early"] = float(np.max(np.abs(x[:t0] - r[:t0]))) / scale
+    return errs
+
+
 def test_full_size_titans_window():
     # The full-size Titans workload (B=4, H=16, T=8192, d=128, b=64) in the
-    # bench's launch configuration, with the outer loss on chunks 60-61 only
-    # and no state cotangent: nothing flows into those chunks from later, so
-    # their gradients are the oracle's on that 2-chunk window started from the
-    # oracle's own state after 60 chunks.  Tokens after the window get exactly
-    # zero gradient, dq is zero wherever dz is, and the cotangent leaving chunk
-    # 59 (the work buffer) is the window's dM0, dS0.
+    # bench's launch configuration, no state cotangent, and the outer loss on
+    # two 8-chunk windows in turn: chunks 56-63, and chunks 0-7.  Every
+    # gradient of the first 64 chunks (the window, and through the reverse
+    # carry every chunk before it) is the oracle's backward over tokens
+    # 0 .. 4095 with that dz; on the window at chunk 0, dM0 and dS0 too.
+    # Tokens after a window get exactly zero gradient and dq is zero wherever
+    # dz is.
     w = WORKLOADS[3]
-    c0, c1 = 60, 62
     inp = make_inputs(w)
-    cot = make_cotangents(w, states=False, chunks=(c0, c1))
     dev = to_dev(inp)
-    cd = to_dev(cot)
     args = (dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"])
     _say("case full size: training forward")
     z, M, S, ckpt = tm.forward_train(*args, b=w.b)
-    work = torch.empty_like(ckpt)
-    _say("case full size: backward")
-    g = tm.backward(*args, ckpt, cd["dz"], b=w.b, work=work)
-    torch.cuda.synchronize()
-    t0, t1 = c0 * w.b, c1 * w.b
-    for x in g[:6]:
-        assert not torch.any(x[:, :, t1:]), "gradient after the window"
-    assert not torch.any(g[0][:, :, :t0])
-    for (bi, hi) in ((0, 0), (3, 15)):
-        n = {k: to_numpy64(v[bi, hi]) for k, v in inp.items() if v is not None}
-        _, Ms, Ss = linear_forward(n["q"][:t0], n["k"][:t0], n["v"][:t0], n["theta"][:t0], n["eta"][:t0],
-                                   n["alpha"][:t0], None, None, b=w.b)
-        sl = slice(t0, t1)
-        ref = linear_backward(n["q"][sl], n["k"][sl], n["v"][sl], n["theta"][sl], n["eta"][sl], n["alpha"][sl],
-                              to_numpy64(cot["dz"][bi, hi, sl]), None, None, Ms, Ss, b=w.b)
-        got = [to_numpy64(x[bi, hi, sl].cpu()) for x in g[:6]]
-        got += [to_numpy64(work[bi, hi, c0 - 1, 0].cpu()), to_numpy64(work[bi, hi, c0 - 1, 1].cpu())]
-        errs = {nm: rel_err(x, r) for nm, x, r in zip(NAMES, got, ref)}
-        _say(f"  ({bi},{hi}) errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-        assert max(errs.values()) <= TOL["bf16"], errs
+    for c0, c1 in ((56, 64), (0, 8)):
+        cot = make_cotangents(w, states=False, chunks=(c0, c1))
+        _say(f"case full size: backward, loss on chunks {c0}-{c1 - 1}")
+        g = tm.backward(*args, ckpt, cot["dz"].cuda(), b=w.b)
+        torch.cuda.synchronize()
+        t0, t1 = c0 * w.b, c1 * w.b
+        for x in g[:6]:
+            assert not torch.any(x[:, :, t1:]), "gradient after the window"
+        assert not torch.any(g[0][:, :, :t0])
+        for (bi, hi) in ((0, 0), (3, 15)):
+            n = {k: to_numpy64(v[bi, hi]) for k, v in inp.items() if v is not None}
+            sl = slice(0, t1)
+            ref = linear_backward(n["q"][sl], n["k"][sl], n["v"][sl], n["theta"][sl], n["eta"][sl],
+                                  n["alpha"][sl], to_numpy64(cot["dz"][bi, hi, sl]), None, None, None, None, b=w.b)
+            got = [to_numpy64(x[bi, hi, sl].cpu()) for x in g[:6]]
+            errs = _prefix_errors(got, ref, t0, t1, w.b)
+            if t0 == 0:
+                errs["dM0"] = rel_err(to_numpy64(g[6][bi, hi].cpu()), ref[6])
+                errs["dS0"] = rel_err(to_numpy64(g[7][bi, hi].cpu()), ref[7])
+            _say(f"  ({bi},{hi}) errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+            assert max(errs.values()) <= TOL["bf16"], errs
+
+
+@pytest.mark.parametrize("mag", [1e-7, 1e-9, 3e4])
+def test_bf16_backward_small_and_large_cotangents(mag):
+    # A mean-reduced loss gives cotangents of 1e-6 .. 1e-9, below fp16's normal
+    # range; large ones would pass its maximum.  The gradients still meet the
+    # bf16 bound against the oracle (which is exact at any magnitude).
+    w = WORKLOADS[3].replace(B=2, H=2, T=300, d=64, b=16, dtype="bf16")
+    _say(f"case cotangents scaled by {mag}")
+    inp = _with_state(make_inputs(w))
+    cot = {k: (None if v is None else v * mag) for k, v in make_cotangents(w).items()}
+    _check(inp, cot, w.b, TOL["bf16"])
+
+
+def test_bf16_backward_is_exact_under_power_of_two_cotangent_scaling():
+    # The kernels scale each sequence's cotangents by a power of two taken from
+    # their largest magnitude, so multiplying dz, dM_T, dS_T by 2^-30 (still
+    # normal in float32) multiplies every gradient by exactly 2^-30.
+    w = WORKLOADS[3].replace(B=2, H=3, T=200, d=128, b=64, dtype="bf16")
+    inp = _with_state(make_inputs(w))
+    cot = make_cotangents(w)
+    _, g1 = _gpu(inp, cot, w.b)
+    _, g2 = _gpu(inp, {k: v * 2.0 ** -30 for k, v in cot.items()}, w.b)
+    for nm, a, b_ in zip(NAMES, g1, g2):
+        assert torch.equal(a * 2.0 ** -30, b_), nm
 
 
 def test_backward_argument_errors():

@@ -171,12 +171,13 @@ def test_varlen_training_overlapping_offsets_stay_in_slots():
     H = dev["q"].shape[0]
     shape = tm.new_ckpt_varlen(dev["q"], cu, 16).shape
     ck_big = torch.full((H + 1,) + tuple(shape[1:]), 7.0, dtype=torch.float16, device="cuda")
-    wk_big = torch.full_like(ck_big, 7.0)
+    need = tm.backward_work_bytes(dev["q"], 16, cu)
+    wk_big = torch.full((need + 4096,), 7, dtype=torch.uint8, device="cuda")
     _say(f"case overlapping offsets {cu.tolist()} b=16 slots={shape[1]}")
     tm.forward_varlen(*args, cu, b=16, ckpt=ck_big[:H])
-    tm.backward_varlen(*args, cu, ck_big[:H], cot["dz"].cuda(), b=16, work=wk_big[:H])
+    tm.backward_varlen(*args, cu, ck_big[:H], cot["dz"].cuda(), b=16, work=wk_big[:need])
     torch.cuda.synchronize()
-    assert (ck_big[H] == 7.0).all() and (wk_big[H] == 7.0).all()
+    assert (ck_big[H] == 7.0).all() and (wk_big[need:] == 7).all()
 
 
 def test_varlen_training_full_size_sampled():
