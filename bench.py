@@ -43,7 +43,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from test_neural_memory_amd import memory as tm  # noqa: E402
-from test_neural_memory_amd.workloads import WORKLOADS, make_cotangents, make_inputs, to_numpy64, varlen_lengths, set_chunk_gates  # noqa: E402
+from test_neural_memory_amd.workloads import (WORKLOADS, make_cotangents, make_deep_layers, make_inputs,  # noqa: E402
+                                              set_chunk_gates, to_numpy64, varlen_lengths)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
@@ -77,21 +78,25 @@ def algorithmic_work(w, in_bytes=2, z_bytes=4, reads_state=False):
     return ht * per_tok + state, flops, per_tok
 
 
-def algorithmic_work_mlp(w, in_bytes=2, z_bytes=4):
-    """Bytes and flops of one deep-memory forward (f(u) = u + SiLU(u W1) W2, hidden h).
+def algorithmic_work_mlp(w, in_bytes=2, z_bytes=4, depth=2):
+    """Bytes and flops of one deep-memory forward (f(u) = u + SiLU(...SiLU(u W_1)...) W_L, hidden h).
 
-    Per (batch, head, token), per chunk of b tokens in the dual form: 2dh flops
-    for each of K W1, Ak W2, R W2^T, Q W1, Q S1, Aq W2, Aq S2 and for each of the
-    four weight/momentum carries (22 dh = 88 d^2 at h = 4d), plus 2bd or 2bh
-    for each of Q K^T, (L.QK^T) dH, Aq Ak^T and (L.G) R (4b(d + h) = 20bd).
-    Bytes: q, k, v, three gates and z per token; the four weight tensors read
-    and written once per (batch, head).
+    Per (batch, head, token), per chunk of b tokens in the dual form, for the
+    two outer layers: 2dh flops for each of K W1, X W_L, R W_L^T, Q W1, Q S1,
+    Y W_L, Y S_L and for each of the four weight/momentum carries (22 dh = 88
+    d^2 at h = 4d), plus 2bd or 2bh for each of Q K^T, (L.QK^T) D_1, Y X^T and
+    (L.G) R (4b(d + h) = 20bd).  Each of the depth - 2 hidden-to-hidden layers
+    adds 2h^2 for each of X W, D W^T, Y W, Y S and the two carries (12 h^2)
+    and 2bh for each of Y X^T and (L.G) D (4bh).
+    Bytes: q, k, v, three gates and z per token; every weight and momentum
+    tensor read and written once per (batch, head).
     """
     ht = w.B * w.H * w.T
     d, h = w.d, w.hidden
+    nm = depth - 2
     per_tok = 3 * d * in_bytes + 3 * 4 + d * z_bytes
-    state = w.B * w.H * 8 * d * h * 4
-    flops = ht * (22 * d * h + 4 * w.b * (d + h))
+    state = w.B * w.H * 4 * (2 * d * h + nm * h * h) * 4
+    flops = ht * (22 * d * h + 4 * w.b * (d + h) + nm * (12 * h * h + 4 * w.b * h))
     return ht * per_tok + state, flops, per_tok
 
 
@@ -123,11 +128,13 @@ def measured_traffic(w, kind="forward"):
     if kind == "forward":
         if w.id not in FWD_PROFILES:
             return None
-    elif w.id != (5 if kind == "mlp" else 3):
+    elif w.id != (5 if kind in ("mlp", "deep3", "deep4") else 3):
         return None
-    if kind == "mlp":
-        path = os.path.join(ROOT, "profiles", "mlp_memory_fwd_deep_d64_h256_b16_traffic.json")
-        src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_mlp.hip")
+    if kind in ("mlp", "deep3", "deep4"):
+        name = {"mlp": "mlp_memory_fwd_deep_d64_h256_b16", "deep3": "deep_memory_fwd_depth3_d64_h256_b16",
+                "deep4": "deep_memory_fwd_depth4_d64_h256_b16"}[kind]
+        path = os.path.join(ROOT, "profiles", name + "_traffic.json")
+        src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_deep.hip")
     elif kind == "decode":
         path = os.path.join(ROOT, "profiles", "linear_memory_decode_titans_d128_traffic.json")
         src = os.path.join(ROOT, "test_neural_memory_amd", "csrc", "ttt_mem_decode.hip")
@@ -161,11 +168,14 @@ def _oracle_worker(args):
     q, k, v, th, et, al, b, W1, W2 = args[:9]
     chunk_gates = len(args) > 9 and args[9]
     M0 = args[10] if len(args) > 10 else None
+    layers = args[11] if len(args) > 11 else None
     from threadpoolctl import threadpool_limits
-    from oracle import linear_forward, linear_forward_chunk_gates, mlp_forward
+    from oracle import deep_forward, linear_forward, linear_forward_chunk_gates, mlp_forward
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        if chunk_gates:
+        if layers is not None:
+            deep_forward(q, k, v, th, et, al, layers, None, b=b)
+        elif chunk_gates:
             linear_forward_chunk_gates(q, k, v, th, et, al, M0, None, b=b)
         elif W1 is None:
             linear_forward(q, k, v, th, et, al, M0, None, b=b)
@@ -718,8 +728,9 @@ def cpu_baseline_varlen(inp, lengths, H, b, docs=12):
     }
 
 
-def cpu_baseline(w, inp, heads, chunk_gates=False):
-    """Time the float64 oracle on ``heads`` (batch, head) pairs with full T, in a process pool."""
+def cpu_baseline(w, inp, heads, chunk_gates=False, layers=None):
+    """Time the float64 oracle on ``heads`` (batch, head) pairs with full T, in a process pool
+    (``layers``: the initial layers of a deeper memory, run by the oracle's deep_forward)."""
     import multiprocessing as mp
     ncores = max(1, min(len(os.sched_getaffinity(0)), 16))
     g = {k: to_numpy64(v) for k, v in inp.items()
@@ -735,7 +746,8 @@ def cpu_baseline(w, inp, heads, chunk_gates=False):
         hi = np.array([p[1] for p in grp])
         jobs.append(tuple(g[x][bi, hi] for x in ("q", "k", "v", "theta", "eta", "alpha")) + (w.b,)
                     + ((g["W1"][bi, hi], g["W2"][bi, hi]) if w.hidden else (None, None)) + (chunk_gates,)
-                    + ((g["M0"][bi, hi] if "M0" in g else None),))
+                    + ((g["M0"][bi, hi] if "M0" in g else None),)
+                    + ((None if layers is None else [to_numpy64(x)[bi, hi] for x in layers]),))
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(len(jobs)) as pool:
@@ -765,6 +777,8 @@ def main():
     # default warmup runs past that ramp.
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--depth", type=int, default=2, choices=[2, 3, 4],
+                    help="layers of the deep memory (workload 5); 3 and 4 start from seeded N(0, 1/fan_in) layers")
     ap.add_argument("--decode", action="store_true",
                     help="time token-by-token generation (primal form) on the Titans shapes instead")
     ap.add_argument("--varlen", action="store_true",
@@ -828,7 +842,22 @@ def main():
     dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     B, H, T, d = w.B, w.H, w.T, w.d
     z = torch.empty(B, H, T, d, dtype=zdt, device="cuda")
-    if deep:
+    if args.depth != 2 and not deep:
+        print("--depth applies to the deep-memory workload (5)", file=sys.stderr)
+        sys.exit(2)
+    deep_layers = None
+    if deep and args.depth > 2:
+        if args.z_f32:
+            print("--depth 3 and 4 write bf16 z", file=sys.stderr)
+            sys.exit(2)
+        deep_layers = make_deep_layers(w, args.depth)
+        W0 = tm.deep_pack([x.cuda() for x in deep_layers])
+        WT, ST = torch.empty_like(W0), torch.empty_like(W0)
+        dwork = tm.new_deep_work(B, H, d, w.hidden, args.depth, "cuda")
+        call = lambda: tm.deep_forward(  # noqa: E731
+            dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"], W0, None, hidden=w.hidden,
+            depth=args.depth, b=w.b, work=dwork, out=(z, WT, ST))
+    elif deep:
         outs = (z,) + tuple(torch.empty_like(dev[k]) for k in ("W1", "W2", "W1", "W2"))
         call = lambda: tm.ttt_mem_mlp_forward_bf16(  # noqa: E731
             dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"], dev["W1"], dev["W2"],
@@ -877,8 +906,8 @@ def main():
     med_launch_ms = float(np.median(launch_ms))
 
     if deep:
-        nbytes, flops, per_tok = algorithmic_work_mlp(w, z_bytes=z_bytes)
-        traffic = measured_traffic(w, "mlp") if not args.z_f32 else None
+        nbytes, flops, per_tok = algorithmic_work_mlp(w, z_bytes=z_bytes, depth=args.depth)
+        traffic = measured_traffic(w, "mlp" if args.depth == 2 else f"deep{args.depth}") if not args.z_f32 else None
     else:
         nbytes, flops, per_tok = algorithmic_work(w, z_bytes=z_bytes, reads_state=True)
         traffic = measured_traffic(w) if not args.z_f32 else None
@@ -898,11 +927,16 @@ def main():
     # Sampled parity check of the timed outputs against the oracle: the first
     # and last (batch, head) sequences, and for the linear memory a few value
     # rows of each (rows are independent problems).
-    from oracle import linear_forward, linear_forward_chunk_gates, mlp_forward
+    from oracle import deep_forward, linear_forward, linear_forward_chunk_gates, mlp_forward
     errs = []
     for (bi, hi) in ((0, 0), (B - 1, H - 1)):
         g = {k: to_numpy64(v[bi, hi]) for k, v in inp.items() if v is not None}
-        if deep:
+        if deep_layers is not None:
+            zo = deep_forward(g["q"], g["k"], g["v"], g["theta"], g["eta"], g["alpha"],
+                              [to_numpy64(x[bi, hi]) for x in deep_layers], None, b=w.b)[0]
+            zg = z[bi, hi].double().cpu().numpy()
+            what = "sequences (0,0) and (B-1,H-1), all columns"
+        elif deep:
             zo = mlp_forward(g["q"], g["k"], g["v"], g["theta"], g["eta"], g["alpha"], g["W1"], g["W2"], b=w.b)[0]
             zg = z[bi, hi].double().cpu().numpy()
             what = "sequences (0,0) and (B-1,H-1), all columns"
@@ -921,18 +955,21 @@ def main():
     if not args.no_cpu_baseline:
         heads = args.cpu_heads or (16 if deep else min(64, B * H))
         cw = w if w.T <= 8192 else w.replace(T=8192)   # long sequences: the oracle on their first 8192 tokens
-        cpu = cpu_baseline(cw, inp if cw is w else _head_slice(inp, cw.T), heads, chunk_gates=args.chunk_gates)
+        cpu = cpu_baseline(cw, inp if cw is w else _head_slice(inp, cw.T), heads, chunk_gates=args.chunk_gates,
+                           layers=deep_layers)
         log(f"cpu baseline: {cpu}")
 
     if deep:
-        metric = f"deep-memory tokens/s at H={H},d={d},hidden={w.hidden},b={w.b}"
+        metric = f"deep-memory tokens/s at H={H},d={d},hidden={w.hidden},b={w.b}" + (
+            f",depth={args.depth}" if args.depth != 2 else "")
         roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
                     "traffic_unit": "bytes/launch", "traffic_source": "profiles/ counter summary",
                     "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                     "hbm_frac": achieved_gbs / HBM_PEAK_GBS,
                     "launch_us": {"mean": avg_launch_ms * 1e3, "median": med_launch_ms * 1e3}}
-        cfg = {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "hidden": w.hidden, "b": w.b,
+        cfg = {"workload": w.name + (f"-depth{args.depth}" if args.depth != 2 else ""), "B": B, "H": H, "T": T,
+               "d": d, "hidden": w.hidden, "depth": args.depth, "b": w.b,
                "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "weights": "f32", "z": zname,
                "head_tokens_per_s": B * H * T / (ms_per_step * 1e-3)}
     else:

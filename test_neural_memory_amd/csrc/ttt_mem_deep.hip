@@ -658,6 +658,531 @@ __global__ __launch_bounds__(kThreads, 1) void deep_fwd2(const DeepParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Deeper memories: L = NM + 2 layers, NM hidden-to-hidden layers W_j
+// (2 <= j <= L - 1, hid x hid).  The same group of G workgroups and the same
+// exchange as deep_fwd2, with every crossing of the hidden units of a layer
+// made explicit: each wave owns the columns of W_j for its 16 units of layer
+// j (all hid rows, in registers) and the matching 16 x 16 tiles of its
+// momentum (in the workspace, read and written only by the owning lanes).
+// Per chunk, in order:
+//   keys     X_1[:, U] = SiLU(K W_1[:, U]); for j = 2 .. L-1 gather X_{j-1}
+//            (every wave's 16 columns to every workgroup) and form
+//            X_j[:, U] = SiLU(X_{j-1} W_j[:, U]); the partial products
+//            X_{L-1}[:, U] W_L[U, :] are summed into R (with the z partials
+//            of the previous chunk) as in deep_fwd2.
+//   deltas   D_{L-1}[:, U] = (R W_L[U, :]^T) .* SiLU'(H_{L-1}); for j = L-1
+//            .. 2 the partial products D_j[:, U] W_j[:, U]^T over this
+//            wave's units are summed across the group and every wave keeps
+//            its own columns: D_{j-1}[:, U] = (sum) .* SiLU'(H_{j-1}).
+//   reads    Y_1 as in deep_fwd2 from the chunk-start W_1, S_1; for j = 2 ..
+//            L-1 gather Y_{j-1} and form Y_j[:, U] from W_j, S_j, D_j and
+//            the decayed Gram (L .* Y_{j-1} X_{j-1}^T); the z partial from
+//            Y_{L-1}[:, U], W_L[U, :], S_L[U, :], R.
+//   carry    every layer at once, from the chunk-start weights.
+// That is 3 L - 5 exchanges per chunk (the reads are not moved into a wait
+// as in deep_fwd2: a stash of chunk-start hidden-to-hidden weights would not
+// fit in LDS).
+constexpr int kSlotM = kHT * 256;   // floats per workgroup slot: 16 delta partial tiles
+constexpr int kBlk = 256;           // bf16 per plane of a 16 x 16 activation block
+
+template <int NM>
+struct MidSmem {
+    ChunkBuf buf[2];
+    alignas(16) float R[kNP * kRS];
+    alignas(16) float RT[kD * kRTS];
+    alignas(16) uint16_t wst[kWaves][2][kD * kWS];
+    alignas(16) f32x4 xpart[kWaves][2][64];
+    union {
+        f32x4 dma[kWaves][2 * kG][64];   // R partials; a wave's delta partials (first kG)
+        f32x4 pred[kWaves][8][64];       // two-wave pre-reduction of delta partials
+    } u;
+    alignas(16) f32x4 dmaz[kG][64];
+    // Gathered activations: block kt (units 16 kt .. 16 kt + 15) as
+    // [hi | lo][token][unit] bf16.
+    alignas(16) uint16_t xg[NM][kHT][2][kBlk];   // X_1 .. X_NM of the keys
+    alignas(16) uint16_t yg[kHT][2][kBlk];       // Y_{j-1} of the queries, one layer at a time
+    alignas(16) float scr[kWaves][16 * 17];       // per-wave 16 x 16 transposes
+    alignas(16) uint16_t wtr[kWaves][2][16 * kWS];
+    int bail, gid, part;
+};
+
+__device__ __forceinline__ void wave_lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// 16 x 16 tile between the two accumulator layouts: lane (lr, lg) holds
+// x[e] = M[4 lg + e][lr] and receives M[lr][4 lg + e] (wave-local scratch).
+__device__ __forceinline__ f32x4 tr16(f32x4 x, float* scr, int lr, int lg) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) scr[(4 * lg + e) * 17 + lr] = x[e];
+    wave_lds_wait();
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = scr[lr * 17 + 4 * lg + e];
+    wave_lds_wait();
+    return y;
+}
+
+// bf16 hi / lo split of a weight tile (lane (lr, lg): W[4 lg + e][lr]) read
+// back transposed: lane (lr, lg) receives W[lr][4 lg + j], j < 4.
+__device__ __forceinline__ Sp tr_split(f32x4 x, uint16_t (*t)[16 * kWS], int lr, int lg) {
+    const Sp s = split(x);
+    *reinterpret_cast<s16x4*>(t[0] + lr * kWS + 4 * lg) = s.hi;
+    *reinterpret_cast<s16x4*>(t[1] + lr * kWS + 4 * lg) = s.lo;
+    wave_lds_wait();
+    const Sp r{lds_tr4(t[0], kWS, lr, lg), lds_tr4(t[1], kWS, lr, lg)};
+    wave_lds_wait();
+    return r;
+}
+
+template <int NM>
+__device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
+    constexpr int L = NM + 2;
+    __shared__ MidSmem<NM> sm;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    int* const status = p.work;
+
+    // Group and part from the XCD the workgroup runs on (as deep_fwd2).
+    if (tid == 0) {
+        const int x = xcc_id() % p.nxcc;
+        const int t = __hip_atomic_fetch_add(p.work + kTicketInts + x * kCtrStride, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        const int per_xcd = p.ngroups / p.nxcc;
+        sm.bail = t >= per_xcd * kG ? 1 : 0;
+        if (sm.bail)
+            __hip_atomic_fetch_or(status, static_cast<int>(kStatusPlacement), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_SYSTEM);
+        sm.gid = x + p.nxcc * (t / kG);
+        sm.part = t % kG;
+    }
+    __syncthreads();
+    if (sm.bail) return;
+    const int gi = __builtin_amdgcn_readfirstlane(sm.gid);
+    const int part = __builtin_amdgcn_readfirstlane(sm.part);
+    int* const ctr = p.work + kHdrInts + gi * kCtrStride;
+    float* const xall = reinterpret_cast<float*>(p.work + kHdrInts + p.ngroups * kCtrStride);
+    float* const xbase = xall + static_cast<size_t>(gi) * kRing * kG * kSlotM;
+    // Momenta of the hidden-to-hidden layers, [group][layer][wave of the group][tile][lane].
+    f32x4* const sbase = reinterpret_cast<f32x4*>(xall + static_cast<size_t>(p.ngroups) * kRing * kG * kSlotM) +
+                         (static_cast<size_t>(gi) * NM * (kG * kWaves) + (2 * part + w)) * kHT * 64 + lane;
+    auto smom = [&](int m, int kt) -> f32x4* { return sbase + (static_cast<size_t>(m) * (kG * kWaves) * kHT + kt) * 64; };
+    const int hu = 32 * part + 16 * w;   // first hidden unit of this wave (every hidden layer)
+    const int own = 2 * part + w;        // its 16-unit block
+    int epoch = 0;
+
+    auto signal = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto wait = [&]() -> bool {
+        if (tid == 0) {
+            const int target = kG * (epoch + 1);
+            int spins = 0;
+            while (l2_counter(ctr) < target) {
+                if (++spins > p.spin_limit) {
+                    sm.bail = 1;
+                    __hip_atomic_fetch_or(status, static_cast<int>(kStatusTimeout), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_SYSTEM);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __syncthreads();
+        ++epoch;
+        if (sm.bail) return false;
+        if ((epoch - 1) % kInvEvery == 0) l1_invalidate();
+        return true;
+    };
+    auto my_slot = [&]() { return xbase + static_cast<size_t>((epoch % kRing) * kG + part) * kSlotM; };
+    auto step_slots = [&]() { return xbase + static_cast<size_t>(((epoch - 1) % kRing) * kG) * kSlotM; };
+    // Gather: this wave's block of an activation (T layout: lane (lr, lg) =
+    // X[token lr][unit hu + 4 lg + j], split) into dst[kt] of every workgroup.
+    auto gather = [&](const Sp& xt, uint16_t (*dst)[2][kBlk]) -> bool {
+        uint16_t* s = reinterpret_cast<uint16_t*>(my_slot());
+        *reinterpret_cast<s16x4*>(s + (2 * w) * kBlk + lr * 16 + 4 * lg) = xt.hi;
+        *reinterpret_cast<s16x4*>(s + (2 * w + 1) * kBlk + lr * 16 + 4 * lg) = xt.lo;
+        signal();
+        if (!wait()) return false;
+        const char* r = reinterpret_cast<const char*>(step_slots());
+#pragma unroll
+        for (int g2 = 0; g2 < kG; ++g2)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(r + static_cast<size_t>(g2) * kSlotM * 4 +
+                                                                            w * 1024 + lane * 16),
+                                             reinterpret_cast<float*>(reinterpret_cast<char*>(&dst[2 * g2][0][0]) + w * 1024),
+                                             16, 0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        return true;
+    };
+    // T-layout fragment of gathered block kt (A with m = token, or B with n = token).
+    auto gfrag = [&](const uint16_t (*src)[2][kBlk], int kt) -> Sp {
+        return Sp{lds4(&src[kt][0][lr * 16 + 4 * lg]), lds4(&src[kt][1][lr * 16 + 4 * lg])};
+    };
+
+    for (int s = gi; s < p.BH; s += p.ngroups) {
+        const size_t seq_tok = static_cast<size_t>(s) * p.T;
+        const int nch = (p.T + p.b - 1) / p.b;
+        auto chunk_n = [&](int c) { return min(p.b, p.T - c * p.b); };
+
+        // ---- resident weights ----
+        f32x4 W1[kDT], S1[kDT], WL[kDT], SL[kDT];
+        f32x4 Wm[NM][kHT];
+        {
+            const float* w1 = p.W0[0] + s * p.wstride[0];
+            const float* s1 = p.S0[0] ? p.S0[0] + s * p.wstride[0] : nullptr;
+            const float* wl = p.W0[L - 1] + s * p.wstride[L - 1];
+            const float* sl = p.S0[L - 1] ? p.S0[L - 1] + s * p.wstride[L - 1] : nullptr;
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i1 = (16 * dt + 4 * lg + e) * kHid + hu + lr;
+                    const int i2 = (hu + 4 * lg + e) * kD + 16 * dt + lr;
+                    W1[dt][e] = w1[i1];
+                    S1[dt][e] = s1 ? s1[i1] : 0.f;
+                    WL[dt][e] = wl[i2];
+                    SL[dt][e] = sl ? sl[i2] : 0.f;
+                }
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const float* wm = p.W0[1 + m] + s * p.wstride[1 + m];
+                const float* sm0 = p.S0[1 + m] ? p.S0[1 + m] + s * p.wstride[1 + m] : nullptr;
+#pragma unroll
+                for (int kt = 0; kt < kHT; ++kt) {
+                    f32x4 sv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int ij = (16 * kt + 4 * lg + e) * kHid + hu + lr;
+                        Wm[m][kt][e] = wm[ij];
+                        sv[e] = sm0 ? sm0[ij] : 0.f;
+                    }
+                    *smom(m, kt) = sv;
+                }
+            }
+        }
+        Sp WLs[kDT];
+        auto stage_wl = [&]() {
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt) {
+                WLs[dt] = split(WL[dt]);
+                *reinterpret_cast<s16x4*>(sm.wst[w][0] + (16 * dt + lr) * kWS + 4 * lg) = WLs[dt].hi;
+                *reinterpret_cast<s16x4*>(sm.wst[w][1] + (16 * dt + lr) * kWS + 4 * lg) = WLs[dt].lo;
+            }
+        };
+        stage_wl();
+
+        Prefetch pf;
+        prefetch(pf, p, seq_tok, 0, tid);
+        __syncthreads();
+        if (nch > 0) {
+            stage(pf, sm.buf[0], tid);
+            if (w == 1) gates(pf, sm.buf[0], chunk_n(0), lane);
+        }
+        __syncthreads();
+
+        f32x4 Zp[2] = {};   // this workgroup's z partial of the previous chunk (own two d tiles)
+        bool ok = true;
+        const int iters = nch > 0 ? nch + 1 : 0;
+        for (int c = 0; c < iters && ok; ++c) {
+            const bool keys = c < nch;
+            const bool zout = c >= 1;
+            const ChunkBuf& B = sm.buf[c & 1];
+            const int n = keys ? chunk_n(c) : 0;
+            if (keys && c + 1 < nch) prefetch(pf, p, seq_tok, c + 1, tid);
+
+            // ================= keys forward =================
+            f32x4 dX[L - 1], Dk[L - 1];   // SiLU'(H_j), D_j (K layout: lane (lr, lg) = [token 4lg+e][unit lr])
+            f32x4 XLk = {0.f, 0.f, 0.f, 0.f};
+            Sp xlt{};                      // X_{L-1} (T layout), split
+            if (keys) {
+                f32x4 hk = {0.f, 0.f, 0.f, 0.f}, hkt = hk;
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) {
+                    const s16x4 kf = lds4(B.kb + lr * kKS + 16 * dt + 4 * lg);
+                    const Sp w1s = split(W1[dt]);
+                    hk = mma2(kf, w1s, hk);
+                    hkt = mma2(w1s, kf, hkt);
+                }
+                f32x4 xk;
+                silu_d4(hk, xk, dX[0]);
+                f32x4 xt = silu4(hkt);
+#pragma unroll
+                for (int j = 2; j <= L - 1; ++j) {
+                    if (!gather(split(xt), sm.xg[j - 2])) {
+                        ok = false;
+                        break;
+                    }
+                    f32x4 ht = {0.f, 0.f, 0.f, 0.f};   // H_j^T[unit][token]
+#pragma unroll
+                    for (int kt = 0; kt < kHT; ++kt) ht = mma3(split(Wm[j - 2][kt]), gfrag(sm.xg[j - 2], kt), ht);
+                    silu_d4(tr16(ht, sm.scr[w], lr, lg), xk, dX[j - 1]);
+                    xt = silu4(ht);
+                }
+                if (!ok) break;
+                XLk = xk;
+                xlt = split(xt);
+                f32x4 rp[kDT];
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) rp[dt] = mma3(WLs[dt], xlt, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = rp[2 * (1 - w) + k2];
+                __syncthreads();
+                float* slot = my_slot();
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    const int dt = 2 * w + k2;
+                    const f32x4 r = rp[dt] + sm.xpart[w][k2][lane];
+                    *reinterpret_cast<f32x4*>(slot + lr * kD + 16 * dt + 4 * lg) = r;
+                }
+            }
+            // ================= R (and the z of chunk c - 1) across the group =================
+            {
+                float* slot = my_slot();
+                if (zout) {
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2)
+                        *reinterpret_cast<f32x4*>(slot + kNP * kD + lr * kD + 16 * (2 * w + k2) + 4 * lg) = Zp[k2];
+                }
+                signal();
+                if (w == 1 && keys && c + 1 < nch) gates(pf, sm.buf[(c + 1) & 1], chunk_n(c + 1), lane);
+                if (!wait()) {
+                    ok = false;
+                    break;
+                }
+                const float* rslot = step_slots();
+                const bool zred = zout && part < kDT && w == 0;
+                if (keys) {
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                        for (int g2 = 0; g2 < kG; ++g2)
+                            __builtin_amdgcn_global_load_lds(rslot + g2 * kSlotM + lr * kD + 16 * (2 * w + k2) + 4 * lg,
+                                                             &sm.u.dma[w][k2 * kG + g2][0], 16, 0, 0);
+                }
+                if (zred) {
+#pragma unroll
+                    for (int g2 = 0; g2 < kG; ++g2)
+                        __builtin_amdgcn_global_load_lds(rslot + g2 * kSlotM + kNP * kD + lr * kD + 16 * part + 4 * lg,
+                                                         &sm.dmaz[g2][0], 16, 0, 0);
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (zred) {
+                    const int np = chunk_n(c - 1);
+                    f32x4 zt = sm.dmaz[0][lane];
+#pragma unroll
+                    for (int g2 = 1; g2 < kG; ++g2) zt += sm.dmaz[g2][lane];
+                    const bool zb = p.z_bf16 != 0;
+                    const uint32_t zsz = zb ? 2u : 4u;
+                    const auto rz = make_rsrc(static_cast<char*>(p.z) + (seq_tok + static_cast<size_t>(c - 1) * p.b) * kD * zsz,
+                                              static_cast<uint32_t>(np) * kD * zsz);
+                    store_out4(zt, rz, static_cast<uint32_t>(lr * kD + 16 * part + 4 * lg), zb);
+                }
+            }
+            if (!keys) continue;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int dt = 2 * w + k2;
+                f32x4 r = unpack4(lds4(B.kb + lr * kKS + 16 * dt + 4 * lg)) - unpack4(lds4(B.vb + lr * kKS + 16 * dt + 4 * lg));
+#pragma unroll
+                for (int g2 = 0; g2 < kG; ++g2) r += sm.u.dma[w][k2 * kG + g2][lane];
+                if (lr >= n) r = f32x4{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<f32x4*>(sm.R + lr * kRS + 16 * dt + 4 * lg) = r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.RT[(16 * dt + 4 * lg + e) * kRTS + lr] = r[e];
+            }
+            __syncthreads();
+
+            // ================= deltas =================
+            {
+                f32x4 dH = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) {
+                    const Sp rf = split(*reinterpret_cast<const f32x4*>(sm.R + lr * kRS + 16 * dt + 4 * lg));
+                    const Sp wt{lds_tr4(sm.wst[w][0] + 16 * dt * kWS, kWS, lr, lg),
+                                lds_tr4(sm.wst[w][1] + 16 * dt * kWS, kWS, lr, lg)};
+                    dH = mma3(rf, wt, dH);
+                }
+                Dk[L - 2] = dH * dX[L - 2];
+            }
+#pragma unroll
+            for (int j = L - 1; j >= 2; --j) {
+                // Partials of D_{j-1} over this wave's units: tile kt = D_j[:, U] W_j[16kt.., U]^T (K layout).
+                const Sp dT = split(tr16(Dk[j - 1], sm.scr[w], lr, lg));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int kt = (1 - w) * 8 + i;
+                    sm.u.pred[w][i][lane] = mma3(dT, tr_split(Wm[j - 2][kt], sm.wtr[w], lr, lg), f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+                __syncthreads();
+                float* slot = my_slot();
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int kt = w * 8 + i;
+                    const f32x4 t = mma3(dT, tr_split(Wm[j - 2][kt], sm.wtr[w], lr, lg), f32x4{0.f, 0.f, 0.f, 0.f}) +
+                                    sm.u.pred[1 - w][i][lane];
+                    *reinterpret_cast<f32x4*>(slot + kt * 256 + lane * 4) = t;
+                }
+                signal();
+                if (!wait()) {
+                    ok = false;
+                    break;
+                }
+                const float* rslot = step_slots();
+#pragma unroll
+                for (int g2 = 0; g2 < kG; ++g2)
+                    __builtin_amdgcn_global_load_lds(rslot + g2 * kSlotM + own * 256 + lane * 4, &sm.u.dma[w][g2][0], 16, 0, 0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                f32x4 sum = sm.u.dma[w][0][lane];
+#pragma unroll
+                for (int g2 = 1; g2 < kG; ++g2) sum += sm.u.dma[w][g2][lane];
+                Dk[j - 2] = sum * dX[j - 2];
+            }
+            if (!ok) break;
+
+            // ================= reads of chunk c =================
+            {
+                const float At = B.A[lr], Ct = B.C[lr];
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(B.L + lr * kLS + 4 * lg);   // L[t][4lg..]
+                f32x4 kq = {0.f, 0.f, 0.f, 0.f}, za = kq, zc = kq;
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) {
+                    const s16x4 kf = lds4(B.kb + lr * kKS + 16 * dt + 4 * lg);
+                    const s16x4 qf = lds4(B.qb + lr * kKS + 16 * dt + 4 * lg);
+                    kq = mma(kf, qf, kq);
+                    za = mma2(split(W1[dt]), qf, za);
+                    zc = mma2(split(S1[dt]), qf, zc);
+                }
+                f32x4 hq = mma3(split(Dk[0]), split(kq * l4), f32x4{0.f, 0.f, 0.f, 0.f});
+                hq = At * za + Ct * zc - hq;   // Hq_1^T[unit][token]
+#pragma unroll
+                for (int j = 2; j <= L - 1; ++j) {
+                    if (!gather(split(silu4(hq)), sm.yg)) {
+                        ok = false;
+                        break;
+                    }
+                    f32x4 yw = {0.f, 0.f, 0.f, 0.f}, ys = yw, gt = yw;
+#pragma unroll
+                    for (int kt = 0; kt < kHT; ++kt) {
+                        const Sp yf = gfrag(sm.yg, kt);
+                        yw = mma3(split(Wm[j - 2][kt]), yf, yw);
+                        ys = mma3(split(*smom(j - 2, kt)), yf, ys);
+                        gt = mma3(gfrag(sm.xg[j - 2], kt), yf, gt);   // (X_{j-1} Y_{j-1}^T)[j'][t]
+                    }
+                    hq = At * yw + Ct * ys - mma3(split(Dk[j - 1]), split(gt * l4), f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+                if (!ok) break;
+                // z partial: Y_{L-1}[:, U] through W_L, S_L and the decayed Gram with R.
+                const Sp aq = split(silu4(hq));
+                const Sp lgm = split(mma3(xlt, aq, f32x4{0.f, 0.f, 0.f, 0.f}) * l4);
+                f32x4 zp[kDT];
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) {
+                    const f32x4 a2 = mma3(WLs[dt], aq, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 c2 = mma3(split(SL[dt]), aq, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const Sp rs = split(*reinterpret_cast<const f32x4*>(sm.RT + (16 * dt + lr) * kRTS + 4 * lg));
+                    const f32x4 in = mma3(rs, lgm, f32x4{0.f, 0.f, 0.f, 0.f});
+                    zp[dt] = At * a2 + Ct * c2 - in;
+                }
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = zp[2 * (1 - w) + k2];
+                __syncthreads();
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    const int dt = 2 * w + k2;
+                    Zp[k2] = zp[dt] + sm.xpart[w][k2][lane];
+                    if (part == 0) Zp[k2] += unpack4(lds4(B.qb + lr * kKS + 16 * dt + 4 * lg));
+                }
+            }
+
+            // ================= carry =================
+            {
+                const float An = B.scal[0], Cn = B.scal[1], En = B.scal[2];
+                const f32x4 wm4 = *reinterpret_cast<const f32x4*>(B.wm + 4 * lg);
+                const f32x4 ws4 = *reinterpret_cast<const f32x4*>(B.ws + 4 * lg);
+                {
+                    const Sp dm = split(Dk[0] * wm4), dsv = split(Dk[0] * ws4);
+#pragma unroll
+                    for (int dt = 0; dt < kDT; ++dt) {
+                        const s16x4 kt = lds_tr4(B.kb + 16 * dt, kKS, lr, lg);
+                        const f32x4 w1 = An * W1[dt] + Cn * S1[dt];
+                        S1[dt] = mma2(kt, dsv, En * S1[dt]);
+                        W1[dt] = mma2(kt, dm, w1);
+                    }
+                }
+#pragma unroll
+                for (int j = 2; j <= L - 1; ++j) {
+                    const Sp dm = split(Dk[j - 1] * wm4), dsv = split(Dk[j - 1] * ws4);
+#pragma unroll
+                    for (int kt = 0; kt < kHT; ++kt) {
+                        // X_{j-1}^T rows 16kt.. (A = X_{j-1}[token][unit] read transposed).
+                        const Sp xk{lds_tr4(&sm.xg[j - 2][kt][0][0], 16, lr, lg), lds_tr4(&sm.xg[j - 2][kt][1][0], 16, lr, lg)};
+                        f32x4 sv = *smom(j - 2, kt);
+                        const f32x4 wn = An * Wm[j - 2][kt] + Cn * sv;
+                        sv = mma3(xk, dsv, En * sv);
+                        Wm[j - 2][kt] = mma3(xk, dm, wn);
+                        *smom(j - 2, kt) = sv;
+                    }
+                }
+                {
+                    const Sp akm = split(XLk * wm4), aks = split(XLk * ws4);
+#pragma unroll
+                    for (int dt = 0; dt < kDT; ++dt) {
+                        const Sp rs = split(*reinterpret_cast<const f32x4*>(sm.RT + (16 * dt + lr) * kRTS + 4 * lg));
+                        const f32x4 w2 = An * WL[dt] + Cn * SL[dt];
+                        SL[dt] = mma3(aks, rs, En * SL[dt]);
+                        WL[dt] = mma3(akm, rs, w2);
+                    }
+                }
+                stage_wl();
+            }
+            if (c + 1 < nch) stage(pf, sm.buf[(c + 1) & 1], tid);
+            __syncthreads();
+        }
+        if (!ok) break;
+
+        // ---- final weights ----
+        {
+            float* w1 = p.WT[0] ? p.WT[0] + s * p.wstride[0] : nullptr;
+            float* s1 = p.ST[0] ? p.ST[0] + s * p.wstride[0] : nullptr;
+            float* wl = p.WT[L - 1] ? p.WT[L - 1] + s * p.wstride[L - 1] : nullptr;
+            float* sl = p.ST[L - 1] ? p.ST[L - 1] + s * p.wstride[L - 1] : nullptr;
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i1 = (16 * dt + 4 * lg + e) * kHid + hu + lr;
+                    const int i2 = (hu + 4 * lg + e) * kD + 16 * dt + lr;
+                    if (w1) w1[i1] = W1[dt][e];
+                    if (s1) s1[i1] = S1[dt][e];
+                    if (wl) wl[i2] = WL[dt][e];
+                    if (sl) sl[i2] = SL[dt][e];
+                }
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                float* wm = p.WT[1 + m] ? p.WT[1 + m] + s * p.wstride[1 + m] : nullptr;
+                float* smt = p.ST[1 + m] ? p.ST[1 + m] + s * p.wstride[1 + m] : nullptr;
+#pragma unroll
+                for (int kt = 0; kt < kHT; ++kt) {
+                    const f32x4 sv = *smom(m, kt);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int ij = (16 * kt + 4 * lg + e) * kHid + hu + lr;
+                        if (wm) wm[ij] = Wm[m][kt][e];
+                        if (smt) smt[ij] = sv[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void deep_fwd3(const DeepParams p) { deep_fwd_mid<1>(p); }
+__global__ __launch_bounds__(kThreads, 1) void deep_fwd4(const DeepParams p) { deep_fwd_mid<2>(p); }
+
 // Zero the status word and the group counters before a launch.
 __global__ void deep_init(int* work, int nints) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nints; i += gridDim.x * blockDim.x) work[i] = 0;
@@ -695,9 +1220,14 @@ void* scratch_ptr() {
     return g_scratch[dev];
 }
 
-size_t deep_work_bytes_for(long long ngroups) {
-    return (static_cast<size_t>(kHdrInts) + static_cast<size_t>(ngroups) * kCtrStride) * 4 +
-           static_cast<size_t>(ngroups) * kRing * kG * kSlot * 4;
+// Workspace of a launch with ngroups groups: the header and group counters,
+// the exchange slots and, for depth > 2, the momenta of the hidden-to-hidden
+// layers (16 tiles of 64 x 4 floats per wave and layer).
+size_t deep_work_bytes_for(long long ngroups, int depth = 2) {
+    const size_t hdr = (static_cast<size_t>(kHdrInts) + static_cast<size_t>(ngroups) * kCtrStride) * 4;
+    if (depth <= 2) return hdr + static_cast<size_t>(ngroups) * kRing * kG * kSlot * 4;
+    return hdr + static_cast<size_t>(ngroups) * kRing * kG * kSlotM * 4 +
+           static_cast<size_t>(ngroups) * (depth - 2) * (kG * kWaves) * kHT * 64 * 16;
 }
 
 // Groups for BH sequences: a multiple of 8 (one XCD each), at most BH rounded
@@ -731,7 +1261,8 @@ int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       bool use_scratch = false) {
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (B < 0 || H < 0 || Tlen < 0 || b < 1) return TTT_ERR_INVALID_ARG;
-    if (d != kD || hidden != kHid || b > kNP || depth != 2) return TTT_ERR_UNSUPPORTED;
+    if (d != kD || hidden != kHid || b > kNP || depth < 2 || depth > 4) return TTT_ERR_UNSUPPORTED;
+    if (use_scratch && depth != 2) return TTT_ERR_UNSUPPORTED;
     const long long BH = static_cast<long long>(B) * H;
     if (BH == 0) return TTT_OK;
     if (BH > 0x7fffffffLL || BH * static_cast<long long>(Tlen) > 0x7fffffffLL) return TTT_ERR_UNSUPPORTED;
@@ -782,12 +1313,14 @@ int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
     if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return TTT_ERR_HIP;
     if (hipDeviceGetAttribute(&nxcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || nxcc < 1) nxcc = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, deep_fwd2, kThreads, 0) != hipSuccess) return TTT_ERR_HIP;
+    void (*const kfn)(const DeepParams) = depth == 2 ? deep_fwd2 : depth == 3 ? deep_fwd3 : deep_fwd4;
+    const void* kern = reinterpret_cast<const void*>(kfn);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess) return TTT_ERR_HIP;
     int max_groups = (ncu * occ / kG) / 8 * 8;
     if (use_scratch && max_groups > kScratchGroups) max_groups = kScratchGroups;
     if (max_groups < 8) return TTT_ERR_UNSUPPORTED;
     const long long ngroups = deep_groups(BH, max_groups);
-    const size_t need = deep_work_bytes_for(ngroups);
+    const size_t need = deep_work_bytes_for(ngroups, depth);
     bool own_work = false;
     if (use_scratch) {
         // The file-scope scratch: no allocation; sizes past it are refused.
@@ -829,8 +1362,8 @@ int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
     hipError_t err = hipGetLastError();
     if (err == hipSuccess) {
         void* args[] = {&p};
-        err = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(deep_fwd2), dim3(static_cast<unsigned>(ngroups * kG)),
-                                         dim3(kThreads), args, 0, stream);
+        err = hipLaunchCooperativeKernel(kern, dim3(static_cast<unsigned>(ngroups * kG)), dim3(kThreads), args, 0,
+                                         stream);
     }
     if (own_work) hipFreeAsync(work, stream);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
@@ -846,9 +1379,9 @@ size_t ttt_mem_deep_param_count(int d, int hidden, int depth) {
 }
 
 size_t ttt_mem_deep_work_bytes(int B, int H, int d, int hidden, int depth) {
-    if (B < 0 || H < 0 || d != kD || hidden != kHid || depth < 2 || depth > 2) return 0;
+    if (B < 0 || H < 0 || d != kD || hidden != kHid || depth < 2 || depth > 4) return 0;
     const long long BH = static_cast<long long>(B) * H;
-    return deep_work_bytes_for(deep_groups(BH, 1 << 30));
+    return deep_work_bytes_for(deep_groups(BH, 1 << 30), depth);
 }
 
 int ttt_mem_deep_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* theta,

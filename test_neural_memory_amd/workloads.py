@@ -194,3 +194,21 @@ def set_chunk_gates(w, inp):
     inp["theta"] = torch.from_numpy((0.1 * sig(rng.standard_normal(gsh))).astype(np.float32))
     inp["eta"] = torch.from_numpy(sig(rng.normal(2.0, np.sqrt(0.5), gsh)).astype(np.float32))
     inp["alpha"] = torch.from_numpy((0.05 * sig(rng.normal(-1.0, 1.0, gsh))).astype(np.float32))
+
+
+def deep_layer_shapes(d: int, hidden: int, depth: int):
+    """(fan_in, fan_out) of each layer of a depth-L deep memory: d -> hidden,
+    (depth - 2) x hidden -> hidden, hidden -> d."""
+    return [(d, hidden)] + [(hidden, hidden)] * (depth - 2) + [(hidden, d)]
+
+
+def make_deep_layers(w: Workload, depth: int, seed: int = 5) -> list:
+    """Initial layers of a depth-L deep memory for workload ``w``: each layer
+    N(0, 1 / fan_in) float32, drawn per head and shared by the batch
+    ([B, H, fan_in, fan_out] CPU tensors).  Seed: ``default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for (fi, fo) in deep_layer_shapes(w.d, w.hidden, depth):
+        x = rng.standard_normal((w.H, fi, fo)) / np.sqrt(fi)
+        out.append(torch.from_numpy(np.ascontiguousarray(np.broadcast_to(x, (w.B, w.H, fi, fo)), dtype=np.float32)))
+    return out

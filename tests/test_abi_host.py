@@ -142,6 +142,9 @@ def test_deep_sizes(lib):
     assert lib.ttt_mem_deep_param_count(d, h, 4) == 2 * d * h + 2 * h * h
     assert lib.ttt_mem_deep_param_count(d, h, 1) == 0
     assert lib.ttt_mem_deep_work_bytes(4, 8, d, h, 2) > 0
+    # Deeper memories also keep their hidden-to-hidden momenta in the workspace.
+    assert lib.ttt_mem_deep_work_bytes(4, 8, d, h, 4) > lib.ttt_mem_deep_work_bytes(4, 8, d, h, 3) > 0
+    assert lib.ttt_mem_deep_work_bytes(4, 8, d, h, 5) == 0
     assert lib.ttt_mem_deep_work_bytes(4, 8, 32, h, 2) == 0      # unsupported width
 
 

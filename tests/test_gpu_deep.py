@@ -14,7 +14,7 @@ from oracle import deep_forward as oracle_deep
 from tests._parity import TOL, rel_err, rel_err_bf16_out, to_dev
 from test_neural_memory_amd import memory as tm
 from test_neural_memory_amd._lib import TTTError
-from test_neural_memory_amd.workloads import WORKLOADS, make_inputs, to_numpy64
+from test_neural_memory_amd.workloads import WORKLOADS, make_deep_layers, make_inputs, to_numpy64
 
 pytestmark = pytest.mark.gpu
 TOL_DEEP = TOL["bf16"]
@@ -26,12 +26,7 @@ def _say(msg):
 
 def _layers(w, depth, seed=5):
     """Initial layers N(0, 1/fan_in) per head, shared by the batch (the deep-memory recipe)."""
-    rng = np.random.default_rng(seed)
-    out = []
-    for (fi, fo) in tm.deep_layer_shapes(w.d, w.hidden, depth):
-        x = rng.standard_normal((w.H, fi, fo)) / np.sqrt(fi)
-        out.append(torch.from_numpy(np.ascontiguousarray(np.broadcast_to(x, (w.B, w.H, fi, fo)), dtype=np.float32)))
-    return out
+    return make_deep_layers(w, depth, seed)
 
 
 def _run(inp, layers, w, depth, work=None, momenta=None):
@@ -44,6 +39,16 @@ def _run(inp, layers, w, depth, work=None, momenta=None):
         tm.deep_status(work)
     torch.cuda.synchronize()
     return z, tm.deep_unpack(WT, w.d, w.hidden, depth), tm.deep_unpack(ST, w.d, w.hidden, depth)
+
+
+def _rel_err_state(x, ref, floor=1e-30):
+    """max|x - ref| / max(rms(ref), floor): a state whose rms has decayed below
+    float32's normal range (about 1e-38; the momenta of 3- and 4-layer
+    memories do so over the full-size workload, where the keys' hidden
+    pre-activations saturate) is compared at the floor's scale, not its own."""
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = max(float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0, floor)
+    return float(np.max(np.abs(np.asarray(x, dtype=np.float64) - ref))) / scale if ref.size else 0.0
 
 
 def _check(inp, layers, w, depth, heads, momenta=None, work=None):
@@ -61,7 +66,7 @@ def _check(inp, layers, w, depth, heads, momenta=None, work=None):
     _say(f"  z max|err|/rms with the bf16 rounding of z: {rel_err(zg, zo):.2e}")
     for l in range(depth):
         errs[f"W{l + 1}_T"] = rel_err(to_numpy64(WT[l].cpu())[bi, hi], Wo[l])
-        errs[f"S{l + 1}_T"] = rel_err(to_numpy64(ST[l].cpu())[bi, hi], So[l])
+        errs[f"S{l + 1}_T"] = _rel_err_state(to_numpy64(ST[l].cpu())[bi, hi], So[l])
     _say("  errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" (tol {TOL_DEEP})")
     assert max(errs.values()) <= TOL_DEEP, errs
     return errs
@@ -71,7 +76,7 @@ def _small(**kw):
     return WORKLOADS[5].replace(**kw)
 
 
-@pytest.mark.parametrize("depth", [2])
+@pytest.mark.parametrize("depth", [2, 3, 4])
 @pytest.mark.parametrize("label,kw", [("small", dict(B=2, H=3, T=100)), ("ragged-b5", dict(B=1, H=2, T=47, b=5)),
                                       ("b1", dict(B=1, H=1, T=20, b=1))], ids=lambda x: x if isinstance(x, str) else "")
 def test_small_cases(depth, label, kw):
@@ -83,7 +88,7 @@ def test_small_cases(depth, label, kw):
     _check(inp, layers, w, depth, [(i, j) for i in range(w.B) for j in range(w.H)], work=work)
 
 
-@pytest.mark.parametrize("depth", [2])
+@pytest.mark.parametrize("depth", [2, 3, 4])
 def test_titans_gates_and_momenta(depth):
     w = _small(B=1, H=2, T=160).replace(gates="titans")
     _say(f"case deep depth {depth} titans gates, nonzero momenta")
@@ -92,6 +97,19 @@ def test_titans_gates_and_momenta(depth):
     rng = np.random.default_rng(11)
     momenta = [torch.from_numpy((rng.standard_normal(x.shape) * 0.003).astype(np.float32)) for x in layers]
     _check(inp, layers, w, depth, [(0, 0), (0, 1)], momenta=momenta)
+
+
+@pytest.mark.parametrize("depth", [3, 4])
+def test_full_size_sampled(depth):
+    # The deep-memory workload at full size (B=4, H=8, T=4096, d=64, hidden=256,
+    # b=16) with 3 or 4 layers, in the bench's launch configuration: every
+    # sequence runs; sequences (0, 0) and (3, 7) against the oracle.
+    w = WORKLOADS[5]
+    _say(f"case deep depth {depth} full size {w}")
+    inp = make_inputs(w)
+    layers = _layers(w, depth)
+    work = tm.new_deep_work(w.B, w.H, w.d, w.hidden, depth, "cuda")
+    _check(inp, layers, w, depth, [(0, 0), (w.B - 1, w.H - 1)], work=work)
 
 
 def test_depth2_equals_two_layer_entry_point_bitwise():
