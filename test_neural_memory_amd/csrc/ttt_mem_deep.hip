@@ -56,6 +56,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "ttt_mem.h"
 #include "gfx950.h"
@@ -688,6 +689,13 @@ constexpr int kBlk = 256;           // bf16 per plane of a 16 x 16 activation bl
 
 template <int NM>
 struct MidSmem {
+    // Gathered activations first (the unrolled tile loops address them with
+    // immediate offsets from one base): block kt (units 16 kt .. 16 kt + 15)
+    // as [hi | lo][token][unit] bf16.
+    alignas(16) uint16_t xg[NM][kHT][2][kBlk];   // X_1 .. X_NM of the keys
+    alignas(16) uint16_t yg[kHT][2][kBlk];       // Y_{j-1} of the queries, one layer at a time
+    alignas(16) float scr[kWaves][16 * 17];       // per-wave 16 x 16 transposes
+    alignas(16) uint16_t wtr[kWaves][2][16 * kWS];
     ChunkBuf buf[2];
     alignas(16) float R[kNP * kRS];
     alignas(16) float RT[kD * kRTS];
@@ -698,16 +706,29 @@ struct MidSmem {
         f32x4 pred[kWaves][8][64];       // two-wave pre-reduction of delta partials
     } u;
     alignas(16) f32x4 dmaz[kG][64];
-    // Gathered activations: block kt (units 16 kt .. 16 kt + 15) as
-    // [hi | lo][token][unit] bf16.
-    alignas(16) uint16_t xg[NM][kHT][2][kBlk];   // X_1 .. X_NM of the keys
-    alignas(16) uint16_t yg[kHT][2][kBlk];       // Y_{j-1} of the queries, one layer at a time
-    alignas(16) float scr[kWaves][16 * 17];       // per-wave 16 x 16 transposes
-    alignas(16) uint16_t wtr[kWaves][2][16 * kWS];
     int bail, gid, part;
 };
 
 __device__ __forceinline__ void wave_lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// f(std::integral_constant<int, I>{}) for I = B, B + S, ... while I != E:
+// loops over layers whose index must be a compile-time constant (the
+// resident weight arrays are indexed by it).
+template <int B, int E, int S, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B != E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + S, E, S>(f);
+    }
+}
+
+// The value itself, opaque to the compiler: a split of a resident weight tile
+// is then recomputed where it is used instead of being kept live from an
+// earlier use (which costs 4 registers per tile across the whole chunk).
+__device__ __forceinline__ f32x4 fresh(f32x4 x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // 16 x 16 tile between the two accumulator layouts: lane (lr, lg) holds
 // x[e] = M[4 lg + e][lr] and receives M[lr][4 lg + e] (wave-local scratch).
@@ -764,10 +785,22 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
     int* const ctr = p.work + kHdrInts + gi * kCtrStride;
     float* const xall = reinterpret_cast<float*>(p.work + kHdrInts + p.ngroups * kCtrStride);
     float* const xbase = xall + static_cast<size_t>(gi) * kRing * kG * kSlotM;
-    // Momenta of the hidden-to-hidden layers, [group][layer][wave of the group][tile][lane].
+    // Weights and momenta of the hidden-to-hidden layers, [group][layer][W | S][wave of the group][tile][lane]
+    // (this wave's 16 columns as accumulator tiles; only the owning lanes touch them).
     f32x4* const sbase = reinterpret_cast<f32x4*>(xall + static_cast<size_t>(p.ngroups) * kRing * kG * kSlotM) +
-                         (static_cast<size_t>(gi) * NM * (kG * kWaves) + (2 * part + w)) * kHT * 64 + lane;
-    auto smom = [&](int m, int kt) -> f32x4* { return sbase + (static_cast<size_t>(m) * (kG * kWaves) * kHT + kt) * 64; };
+                         (static_cast<size_t>(gi) * NM * 2 * (kG * kWaves) + (2 * part + w)) * kHT * 64 + lane;
+    // Tile addresses come from a base made opaque where they are used, so that
+    // the compiler forms them there instead of keeping all of them live across
+    // the chunk loop (two registers each).
+    auto tbase = [&]() -> f32x4* {
+        f32x4* b = sbase;
+        asm volatile("" : "+v"(b));
+        return b;
+    };
+    auto wmid_at = [](f32x4* b, int m, int kt) -> f32x4* { return b + (static_cast<size_t>(2 * m) * (kG * kWaves) * kHT + kt) * 64; };
+    auto smom_at = [](f32x4* b, int m, int kt) -> f32x4* {
+        return b + (static_cast<size_t>(2 * m + 1) * (kG * kWaves) * kHT + kt) * 64;
+    };
     const int hu = 32 * part + 16 * w;   // first hidden unit of this wave (every hidden layer)
     const int own = 2 * part + w;        // its 16-unit block
     int epoch = 0;
@@ -830,7 +863,6 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
 
         // ---- resident weights ----
         f32x4 W1[kDT], S1[kDT], WL[kDT], SL[kDT];
-        f32x4 Wm[NM][kHT];
         {
             const float* w1 = p.W0[0] + s * p.wstride[0];
             const float* s1 = p.S0[0] ? p.S0[0] + s * p.wstride[0] : nullptr;
@@ -851,26 +883,27 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
             for (int m = 0; m < NM; ++m) {
                 const float* wm = p.W0[1 + m] + s * p.wstride[1 + m];
                 const float* sm0 = p.S0[1 + m] ? p.S0[1 + m] + s * p.wstride[1 + m] : nullptr;
+                f32x4* const tb = tbase();
 #pragma unroll
                 for (int kt = 0; kt < kHT; ++kt) {
-                    f32x4 sv;
+                    f32x4 wv, sv;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int ij = (16 * kt + 4 * lg + e) * kHid + hu + lr;
-                        Wm[m][kt][e] = wm[ij];
+                        wv[e] = wm[ij];
                         sv[e] = sm0 ? sm0[ij] : 0.f;
                     }
-                    *smom(m, kt) = sv;
+                    *wmid_at(tb, m, kt) = wv;
+                    *smom_at(tb, m, kt) = sv;
                 }
             }
         }
-        Sp WLs[kDT];
         auto stage_wl = [&]() {
 #pragma unroll
             for (int dt = 0; dt < kDT; ++dt) {
-                WLs[dt] = split(WL[dt]);
-                *reinterpret_cast<s16x4*>(sm.wst[w][0] + (16 * dt + lr) * kWS + 4 * lg) = WLs[dt].hi;
-                *reinterpret_cast<s16x4*>(sm.wst[w][1] + (16 * dt + lr) * kWS + 4 * lg) = WLs[dt].lo;
+                const Sp ws = split(WL[dt]);
+                *reinterpret_cast<s16x4*>(sm.wst[w][0] + (16 * dt + lr) * kWS + 4 * lg) = ws.hi;
+                *reinterpret_cast<s16x4*>(sm.wst[w][1] + (16 * dt + lr) * kWS + 4 * lg) = ws.lo;
             }
         };
         stage_wl();
@@ -903,39 +936,44 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
 #pragma unroll
                 for (int dt = 0; dt < kDT; ++dt) {
                     const s16x4 kf = lds4(B.kb + lr * kKS + 16 * dt + 4 * lg);
-                    const Sp w1s = split(W1[dt]);
+                    const Sp w1s = split(fresh(W1[dt]));
                     hk = mma2(kf, w1s, hk);
                     hkt = mma2(w1s, kf, hkt);
                 }
                 f32x4 xk;
                 silu_d4(hk, xk, dX[0]);
                 f32x4 xt = silu4(hkt);
-#pragma unroll
-                for (int j = 2; j <= L - 1; ++j) {
+                static_for<2, L, 1>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    if (!ok) return;
                     if (!gather(split(xt), sm.xg[j - 2])) {
                         ok = false;
-                        break;
+                        return;
                     }
                     f32x4 ht = {0.f, 0.f, 0.f, 0.f};   // H_j^T[unit][token]
+                    f32x4* const tb = tbase();
 #pragma unroll
-                    for (int kt = 0; kt < kHT; ++kt) ht = mma3(split(Wm[j - 2][kt]), gfrag(sm.xg[j - 2], kt), ht);
+                    for (int kt = 0; kt < kHT; ++kt) {
+                        ht = mma3(split(*wmid_at(tb, j - 2, kt)), gfrag(sm.xg[j - 2], kt), ht);
+                        if ((kt & 3) == 3) asm volatile("" ::: "memory");   // at most 4 tiles of loads in flight (registers)
+                    }
                     silu_d4(tr16(ht, sm.scr[w], lr, lg), xk, dX[j - 1]);
                     xt = silu4(ht);
-                }
+                });
                 if (!ok) break;
                 XLk = xk;
                 xlt = split(xt);
                 f32x4 rp[kDT];
 #pragma unroll
-                for (int dt = 0; dt < kDT; ++dt) rp[dt] = mma3(WLs[dt], xlt, f32x4{0.f, 0.f, 0.f, 0.f});
+                for (int dt = 0; dt < kDT; ++dt) rp[dt] = mma3(split(fresh(WL[dt])), xlt, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = rp[2 * (1 - w) + k2];
+                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = w == 0 ? rp[2 + k2] : rp[k2];   // no run-time index into a register array
                 __syncthreads();
                 float* slot = my_slot();
 #pragma unroll
                 for (int k2 = 0; k2 < 2; ++k2) {
                     const int dt = 2 * w + k2;
-                    const f32x4 r = rp[dt] + sm.xpart[w][k2][lane];
+                    const f32x4 r = (w == 0 ? rp[k2] : rp[2 + k2]) + sm.xpart[w][k2][lane];
                     *reinterpret_cast<f32x4*>(slot + lr * kD + 16 * dt + 4 * lg) = r;
                 }
             }
@@ -1008,28 +1046,30 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
                 }
                 Dk[L - 2] = dH * dX[L - 2];
             }
-#pragma unroll
-            for (int j = L - 1; j >= 2; --j) {
+            static_for<L - 1, 1, -1>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                if (!ok) return;
                 // Partials of D_{j-1} over this wave's units: tile kt = D_j[:, U] W_j[16kt.., U]^T (K layout).
                 const Sp dT = split(tr16(Dk[j - 1], sm.scr[w], lr, lg));
+                f32x4* const tb = tbase();
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int kt = (1 - w) * 8 + i;
-                    sm.u.pred[w][i][lane] = mma3(dT, tr_split(Wm[j - 2][kt], sm.wtr[w], lr, lg), f32x4{0.f, 0.f, 0.f, 0.f});
+                    sm.u.pred[w][i][lane] = mma3(dT, tr_split(*wmid_at(tb, j - 2, kt), sm.wtr[w], lr, lg), f32x4{0.f, 0.f, 0.f, 0.f});
                 }
                 __syncthreads();
                 float* slot = my_slot();
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int kt = w * 8 + i;
-                    const f32x4 t = mma3(dT, tr_split(Wm[j - 2][kt], sm.wtr[w], lr, lg), f32x4{0.f, 0.f, 0.f, 0.f}) +
+                    const f32x4 t = mma3(dT, tr_split(*wmid_at(tb, j - 2, kt), sm.wtr[w], lr, lg), f32x4{0.f, 0.f, 0.f, 0.f}) +
                                     sm.u.pred[1 - w][i][lane];
                     *reinterpret_cast<f32x4*>(slot + kt * 256 + lane * 4) = t;
                 }
                 signal();
                 if (!wait()) {
                     ok = false;
-                    break;
+                    return;
                 }
                 const float* rslot = step_slots();
 #pragma unroll
@@ -1040,7 +1080,7 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
 #pragma unroll
                 for (int g2 = 1; g2 < kG; ++g2) sum += sm.u.dma[w][g2][lane];
                 Dk[j - 2] = sum * dX[j - 2];
-            }
+            });
             if (!ok) break;
 
             // ================= reads of chunk c =================
@@ -1053,27 +1093,30 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
                     const s16x4 kf = lds4(B.kb + lr * kKS + 16 * dt + 4 * lg);
                     const s16x4 qf = lds4(B.qb + lr * kKS + 16 * dt + 4 * lg);
                     kq = mma(kf, qf, kq);
-                    za = mma2(split(W1[dt]), qf, za);
-                    zc = mma2(split(S1[dt]), qf, zc);
+                    za = mma2(split(fresh(W1[dt])), qf, za);
+                    zc = mma2(split(fresh(S1[dt])), qf, zc);
                 }
                 f32x4 hq = mma3(split(Dk[0]), split(kq * l4), f32x4{0.f, 0.f, 0.f, 0.f});
                 hq = At * za + Ct * zc - hq;   // Hq_1^T[unit][token]
-#pragma unroll
-                for (int j = 2; j <= L - 1; ++j) {
+                static_for<2, L, 1>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    if (!ok) return;
                     if (!gather(split(silu4(hq)), sm.yg)) {
                         ok = false;
-                        break;
+                        return;
                     }
                     f32x4 yw = {0.f, 0.f, 0.f, 0.f}, ys = yw, gt = yw;
+                    f32x4* const tb = tbase();
 #pragma unroll
                     for (int kt = 0; kt < kHT; ++kt) {
                         const Sp yf = gfrag(sm.yg, kt);
-                        yw = mma3(split(Wm[j - 2][kt]), yf, yw);
-                        ys = mma3(split(*smom(j - 2, kt)), yf, ys);
+                        yw = mma3(split(*wmid_at(tb, j - 2, kt)), yf, yw);
+                        ys = mma3(split(*smom_at(tb, j - 2, kt)), yf, ys);
                         gt = mma3(gfrag(sm.xg[j - 2], kt), yf, gt);   // (X_{j-1} Y_{j-1}^T)[j'][t]
+                        if ((kt & 3) == 3) asm volatile("" ::: "memory");
                     }
                     hq = At * yw + Ct * ys - mma3(split(Dk[j - 1]), split(gt * l4), f32x4{0.f, 0.f, 0.f, 0.f});
-                }
+                });
                 if (!ok) break;
                 // z partial: Y_{L-1}[:, U] through W_L, S_L and the decayed Gram with R.
                 const Sp aq = split(silu4(hq));
@@ -1081,19 +1124,19 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
                 f32x4 zp[kDT];
 #pragma unroll
                 for (int dt = 0; dt < kDT; ++dt) {
-                    const f32x4 a2 = mma3(WLs[dt], aq, f32x4{0.f, 0.f, 0.f, 0.f});
-                    const f32x4 c2 = mma3(split(SL[dt]), aq, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 a2 = mma3(split(fresh(WL[dt])), aq, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 c2 = mma3(split(fresh(SL[dt])), aq, f32x4{0.f, 0.f, 0.f, 0.f});
                     const Sp rs = split(*reinterpret_cast<const f32x4*>(sm.RT + (16 * dt + lr) * kRTS + 4 * lg));
                     const f32x4 in = mma3(rs, lgm, f32x4{0.f, 0.f, 0.f, 0.f});
                     zp[dt] = At * a2 + Ct * c2 - in;
                 }
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = zp[2 * (1 - w) + k2];
+                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = w == 0 ? zp[2 + k2] : zp[k2];
                 __syncthreads();
 #pragma unroll
                 for (int k2 = 0; k2 < 2; ++k2) {
                     const int dt = 2 * w + k2;
-                    Zp[k2] = zp[dt] + sm.xpart[w][k2][lane];
+                    Zp[k2] = (w == 0 ? zp[k2] : zp[2 + k2]) + sm.xpart[w][k2][lane];
                     if (part == 0) Zp[k2] += unpack4(lds4(B.qb + lr * kKS + 16 * dt + 4 * lg));
                 }
             }
@@ -1113,20 +1156,22 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
                         W1[dt] = mma2(kt, dm, w1);
                     }
                 }
-#pragma unroll
-                for (int j = 2; j <= L - 1; ++j) {
+                static_for<2, L, 1>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
                     const Sp dm = split(Dk[j - 1] * wm4), dsv = split(Dk[j - 1] * ws4);
+                    f32x4* const tb = tbase();
 #pragma unroll
                     for (int kt = 0; kt < kHT; ++kt) {
                         // X_{j-1}^T rows 16kt.. (A = X_{j-1}[token][unit] read transposed).
                         const Sp xk{lds_tr4(&sm.xg[j - 2][kt][0][0], 16, lr, lg), lds_tr4(&sm.xg[j - 2][kt][1][0], 16, lr, lg)};
-                        f32x4 sv = *smom(j - 2, kt);
-                        const f32x4 wn = An * Wm[j - 2][kt] + Cn * sv;
+                        f32x4 sv = *smom_at(tb, j - 2, kt);
+                        const f32x4 wn = An * *wmid_at(tb, j - 2, kt) + Cn * sv;
                         sv = mma3(xk, dsv, En * sv);
-                        Wm[j - 2][kt] = mma3(xk, dm, wn);
-                        *smom(j - 2, kt) = sv;
+                        *wmid_at(tb, j - 2, kt) = mma3(xk, dm, wn);
+                        *smom_at(tb, j - 2, kt) = sv;
+                        if ((kt & 3) == 3) asm volatile("" ::: "memory");
                     }
-                }
+                });
                 {
                     const Sp akm = split(XLk * wm4), aks = split(XLk * ws4);
 #pragma unroll
@@ -1146,6 +1191,10 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
 
         // ---- final weights ----
         {
+            // Lane coordinates recomputed here (opaque), not kept live from the initial loads.
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int lr = ln & 15, lg = ln >> 4;
             float* w1 = p.WT[0] ? p.WT[0] + s * p.wstride[0] : nullptr;
             float* s1 = p.ST[0] ? p.ST[0] + s * p.wstride[0] : nullptr;
             float* wl = p.WT[L - 1] ? p.WT[L - 1] + s * p.wstride[L - 1] : nullptr;
@@ -1165,13 +1214,14 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
             for (int m = 0; m < NM; ++m) {
                 float* wm = p.WT[1 + m] ? p.WT[1 + m] + s * p.wstride[1 + m] : nullptr;
                 float* smt = p.ST[1 + m] ? p.ST[1 + m] + s * p.wstride[1 + m] : nullptr;
+                f32x4* const tb = tbase();
 #pragma unroll
                 for (int kt = 0; kt < kHT; ++kt) {
-                    const f32x4 sv = *smom(m, kt);
+                    const f32x4 wv = *wmid_at(tb, m, kt), sv = *smom_at(tb, m, kt);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int ij = (16 * kt + 4 * lg + e) * kHid + hu + lr;
-                        if (wm) wm[ij] = Wm[m][kt][e];
+                        if (wm) wm[ij] = wv[e];
                         if (smt) smt[ij] = sv[e];
                     }
                 }
@@ -1227,7 +1277,7 @@ size_t deep_work_bytes_for(long long ngroups, int depth = 2) {
     const size_t hdr = (static_cast<size_t>(kHdrInts) + static_cast<size_t>(ngroups) * kCtrStride) * 4;
     if (depth <= 2) return hdr + static_cast<size_t>(ngroups) * kRing * kG * kSlot * 4;
     return hdr + static_cast<size_t>(ngroups) * kRing * kG * kSlotM * 4 +
-           static_cast<size_t>(ngroups) * (depth - 2) * (kG * kWaves) * kHT * 64 * 16;
+           static_cast<size_t>(ngroups) * (depth - 2) * 2 * (kG * kWaves) * kHT * 64 * 16;
 }
 
 // Groups for BH sequences: a multiple of 8 (one XCD each), at most BH rounded
