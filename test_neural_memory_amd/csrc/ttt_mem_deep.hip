@@ -695,7 +695,7 @@ struct MidSmem {
     alignas(16) uint16_t xg[NM][kHT][2][kBlk];   // X_1 .. X_NM of the keys
     alignas(16) uint16_t yg[kHT][2][kBlk];       // Y_{j-1} of the queries, one layer at a time
     alignas(16) float scr[kWaves][16 * 17];       // per-wave 16 x 16 transposes
-    alignas(16) uint16_t wtr[kWaves][2][16 * kWS];
+    alignas(16) uint16_t wtr[kWaves][8][2][16 * kWS];   // per-wave transposes of 8 weight tiles (hi, lo)
     ChunkBuf buf[2];
     alignas(16) float R[kNP * kRS];
     alignas(16) float RT[kD * kRTS];
@@ -741,18 +741,6 @@ __device__ __forceinline__ f32x4 tr16(f32x4 x, float* scr, int lr, int lg) {
     for (int e = 0; e < 4; ++e) y[e] = scr[lr * 17 + 4 * lg + e];
     wave_lds_wait();
     return y;
-}
-
-// bf16 hi / lo split of a weight tile (lane (lr, lg): W[4 lg + e][lr]) read
-// back transposed: lane (lr, lg) receives W[lr][4 lg + j], j < 4.
-__device__ __forceinline__ Sp tr_split(f32x4 x, uint16_t (*t)[16 * kWS], int lr, int lg) {
-    const Sp s = split(x);
-    *reinterpret_cast<s16x4*>(t[0] + lr * kWS + 4 * lg) = s.hi;
-    *reinterpret_cast<s16x4*>(t[1] + lr * kWS + 4 * lg) = s.lo;
-    wave_lds_wait();
-    const Sp r{lds_tr4(t[0], kWS, lr, lg), lds_tr4(t[1], kWS, lr, lg)};
-    wave_lds_wait();
-    return r;
 }
 
 template <int NM>
@@ -955,7 +943,7 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
 #pragma unroll
                     for (int kt = 0; kt < kHT; ++kt) {
                         ht = mma3(split(*wmid_at(tb, j - 2, kt)), gfrag(sm.xg[j - 2], kt), ht);
-                        if ((kt & 3) == 3) asm volatile("" ::: "memory");   // at most 4 tiles of loads in flight (registers)
+                        if ((kt & 7) == 7) asm volatile("" ::: "memory");   // at most 8 tiles of loads in flight (registers)
                     }
                     silu_d4(tr16(ht, sm.scr[w], lr, lg), xk, dX[j - 1]);
                     xt = silu4(ht);
@@ -1049,23 +1037,35 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
             static_for<L - 1, 1, -1>([&](auto J) {
                 constexpr int j = decltype(J)::value;
                 if (!ok) return;
-                // Partials of D_{j-1} over this wave's units: tile kt = D_j[:, U] W_j[16kt.., U]^T (K layout).
-                const Sp dT = split(tr16(Dk[j - 1], sm.scr[w], lr, lg));
+                const Sp dT = split(tr16(Dk[j - 1], sm.scr[w], lr, lg));   // D_j[:, U] (T layout)
                 f32x4* const tb = tbase();
+                // Eight tiles kt = 8 h + i at a time: loads in flight together,
+                // then the transposes through LDS with one wait.
+                auto half = [&](int h, auto&& use) {
+                    f32x4 wv[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int kt = (1 - w) * 8 + i;
-                    sm.u.pred[w][i][lane] = mma3(dT, tr_split(*wmid_at(tb, j - 2, kt), sm.wtr[w], lr, lg), f32x4{0.f, 0.f, 0.f, 0.f});
-                }
+                    for (int i = 0; i < 8; ++i) wv[i] = *wmid_at(tb, j - 2, 8 * h + i);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const Sp sp = split(wv[i]);
+                        *reinterpret_cast<s16x4*>(sm.wtr[w][i][0] + lr * kWS + 4 * lg) = sp.hi;
+                        *reinterpret_cast<s16x4*>(sm.wtr[w][i][1] + lr * kWS + 4 * lg) = sp.lo;
+                    }
+                    wave_lds_wait();
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const Sp t{lds_tr4(sm.wtr[w][i][0], kWS, lr, lg), lds_tr4(sm.wtr[w][i][1], kWS, lr, lg)};
+                        use(i, mma3(dT, t, f32x4{0.f, 0.f, 0.f, 0.f}));
+                    }
+                    wave_lds_wait();
+                };
+                // Partials of D_{j-1} over this wave's units: tile kt = D_j[:, U] W_j[16kt.., U]^T (K layout).
+                half(1 - w, [&](int i, f32x4 t) { sm.u.pred[w][i][lane] = t; });
                 __syncthreads();
                 float* slot = my_slot();
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int kt = w * 8 + i;
-                    const f32x4 t = mma3(dT, tr_split(*wmid_at(tb, j - 2, kt), sm.wtr[w], lr, lg), f32x4{0.f, 0.f, 0.f, 0.f}) +
-                                    sm.u.pred[1 - w][i][lane];
-                    *reinterpret_cast<f32x4*>(slot + kt * 256 + lane * 4) = t;
-                }
+                half(w, [&](int i, f32x4 t) {
+                    *reinterpret_cast<f32x4*>(slot + (8 * w + i) * 256 + lane * 4) = t + sm.u.pred[1 - w][i][lane];
+                });
                 signal();
                 if (!wait()) {
                     ok = false;
@@ -1113,7 +1113,7 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
                         yw = mma3(split(*wmid_at(tb, j - 2, kt)), yf, yw);
                         ys = mma3(split(*smom_at(tb, j - 2, kt)), yf, ys);
                         gt = mma3(gfrag(sm.xg[j - 2], kt), yf, gt);   // (X_{j-1} Y_{j-1}^T)[j'][t]
-                        if ((kt & 3) == 3) asm volatile("" ::: "memory");
+                        if ((kt & 7) == 7) asm volatile("" ::: "memory");
                     }
                     hq = At * yw + Ct * ys - mma3(split(Dk[j - 1]), split(gt * l4), f32x4{0.f, 0.f, 0.f, 0.f});
                 });
@@ -1169,7 +1169,7 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
                         sv = mma3(xk, dsv, En * sv);
                         *wmid_at(tb, j - 2, kt) = mma3(xk, dm, wn);
                         *smom_at(tb, j - 2, kt) = sv;
-                        if ((kt & 3) == 3) asm volatile("" ::: "memory");
+                        if ((kt & 7) == 7) asm volatile("" ::: "memory");
                     }
                 });
                 {
