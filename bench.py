@@ -777,8 +777,9 @@ def main():
     # default warmup runs past that ramp.
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
-    ap.add_argument("--depth", type=int, default=2, choices=[2, 3, 4],
-                    help="layers of the deep memory (workload 5); 3 and 4 start from seeded N(0, 1/fan_in) layers")
+    ap.add_argument("--depth", type=int, default=2, choices=[1, 2, 3, 4],
+                    help="layers of the deep memory (workload 5); 3 and 4 start from seeded N(0, 1/fan_in) layers, "
+                         "1 is the linear memory on the same inputs (the depth sweep's first point)")
     ap.add_argument("--decode", action="store_true",
                     help="time token-by-token generation (primal form) on the Titans shapes instead")
     ap.add_argument("--varlen", action="store_true",
@@ -829,6 +830,9 @@ def main():
         backward_main(args)
         return
     w = WORKLOADS[args.workload]
+    if args.depth == 1 and w.hidden:
+        # Memory depth 1: the linear memory (d x d state) on the deep workload's inputs.
+        w = w.replace(hidden=0)
     if args.chunk_gates and args.workload != 3:
         print("--chunk-gates runs on the Titans workload (3)", file=sys.stderr)
         sys.exit(2)
@@ -842,7 +846,7 @@ def main():
     dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     B, H, T, d = w.B, w.H, w.T, w.d
     z = torch.empty(B, H, T, d, dtype=zdt, device="cuda")
-    if args.depth != 2 and not deep:
+    if args.depth != 2 and args.workload != 5:
         print("--depth applies to the deep-memory workload (5)", file=sys.stderr)
         sys.exit(2)
     deep_layers = None
@@ -974,7 +978,8 @@ def main():
                "head_tokens_per_s": B * H * T / (ms_per_step * 1e-3)}
     else:
         metric = (f"memory-layer tokens/s at H={H},d={d},b={w.b}"
-                  + (" (chunk-shared gates)" if args.chunk_gates else ""))
+                  + (" (chunk-shared gates)" if args.chunk_gates else "")
+                  + (" (memory depth 1 on the deep-memory inputs)" if args.depth == 1 else ""))
         roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved_gbs / HBM_PEAK_GBS,
                     "traffic": traffic, "traffic_unit": "bytes/launch",
@@ -983,7 +988,8 @@ def main():
                     "frac_of_step": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS,
                     "launch_us": {"mean": avg_launch_ms * 1e3, "median": med_launch_ms * 1e3}}
-        cfg = {"workload": w.name + ("-chunk-gates" if args.chunk_gates else ""), "B": B, "H": H, "T": T, "d": d,
+        cfg = {"workload": w.name + ("-chunk-gates" if args.chunk_gates else "") + ("-depth1" if args.depth == 1 else ""),
+               "B": B, "H": H, "T": T, "d": d,
                "b": w.b, "inputs": "bf16 q,k,v; f32 gates" + (" per chunk" if args.chunk_gates else ""),
                "accumulate": "f32", "state": "f32 (M0, S0 read)", "z": zname,
                "head_tokens_per_s": B * H * T / (ms_per_step * 1e-3)}
