@@ -37,10 +37,9 @@
 // and the data live in the L2 of the XCD all G workgroups run on (workgroup
 // ids congruent mod 8; checked at run time against the hardware XCC id), so
 // the counter is polled with an atomic that executes in that L2 and the data
-// is read with plain loads from slots that rotate through a ring, with the
-// CU's vector L1 invalidated every few steps so that no slot is ever read
-// from a stale L1 line (a slot's previous read is a full ring ago, and an
-// invalidation lies between).  Every wait is bounded: a
+// is copied into LDS with device-scope loads (served coherently at device
+// scope, never from a line the CU's vector L1 kept) from slots that rotate
+// through a short ring.  Every wait is bounded: a
 // wait that runs out sets a status bit and the kernel finishes (with wrong
 // results) instead of hanging.
 //
@@ -77,11 +76,16 @@ constexpr int kRTS = kNP + 4;   // LDS row stride (floats) of R^T rows [d][t]
 constexpr int kLS = kNP + 4;    // LDS row stride (floats) of the decay matrix rows
 constexpr int kWS = 16 + 4;     // LDS row stride (bf16) of a wave's staged W_L^T rows [d][h]
 constexpr int kSlot = 2 * kNP * kD;   // floats per workgroup slot and exchange step: R and z partials
-// Exchange slots form a ring of kRing steps per group; every kInvEvery steps
-// the CU's vector L1 is invalidated, so a slot read again kRing steps later
-// cannot be served from a line the L1 kept since its previous read.
-constexpr int kRing = 32, kInvEvery = 16;
-static_assert(kRing >= 2 * kInvEvery, "an invalidation between any two reads of one slot");
+// Exchange slots form a ring of kRing steps per group.  A workgroup writes
+// the slot of step e + kRing only after every workgroup of its group has
+// signalled step e + kRing - 1, i.e. has finished reading step e, so two steps
+// would do; four leave margin.  The ring is small enough to stay in the XCD's
+// L2 (no write-back to HBM).
+constexpr int kRing = 4;
+// Cache policy of the slot copies: SC1 (device scope), so a copy is served
+// coherently at device scope -- never from a line the CU's vector L1 kept from
+// an earlier step -- and no L1 invalidation is needed.
+constexpr int kSlotLoadPolicy = 16;
 constexpr int kCtrStride = 64;        // ints between group counters (256 bytes)
 constexpr int kHdrInts = 1024;        // status word, XCD ticket counters and padding before the group counters
 constexpr int kTicketInts = 64;       // first XCD ticket counter (one per XCD, kCtrStride apart)
@@ -144,8 +148,6 @@ __device__ __forceinline__ int l2_counter(int* p) {
     asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(c) : "v"(p), "v"(zero) : "memory");
     return c;
 }
-// Drop the CU's vector L1 lines (so that the loads after it read the L2).
-__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc1\n\ts_waitcnt vmcnt(0)" ::: "memory"); }
 
 struct DeepParams {
     const uint16_t* q;
@@ -376,9 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void deep_fwd2(const DeepParams p) {
         }
         __syncthreads();
         ++epoch;
-        if (sm.bail) return false;
-        if ((epoch - 1) % kInvEvery == 0) l1_invalidate();
-        return true;
+        return sm.bail == 0;
     };
 
     for (int s = gi; s < p.BH; s += p.ngroups) {
@@ -557,13 +557,13 @@ __global__ __launch_bounds__(kThreads, 1) void deep_fwd2(const DeepParams p) {
 #pragma unroll
                     for (int g2 = 0; g2 < kG; ++g2)
                         __builtin_amdgcn_global_load_lds(rslot + g2 * kSlot + lr * kD + 16 * (2 * w + k2) + 4 * lg,
-                                                         &sm.dma[w][k2 * kG + g2][0], 16, 0, 0);
+                                                         &sm.dma[w][k2 * kG + g2][0], 16, 0, kSlotLoadPolicy);
             }
             if (zred) {
 #pragma unroll
                 for (int g2 = 0; g2 < kG; ++g2)
                     __builtin_amdgcn_global_load_lds(rslot + g2 * kSlot + kNP * kD + lr * kD + 16 * part + 4 * lg,
-                                                     &sm.dmaz[g2][0], 16, 0, 0);
+                                                     &sm.dmaz[g2][0], 16, 0, kSlotLoadPolicy);
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -814,9 +814,7 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
         }
         __syncthreads();
         ++epoch;
-        if (sm.bail) return false;
-        if ((epoch - 1) % kInvEvery == 0) l1_invalidate();
-        return true;
+        return sm.bail == 0;
     };
     auto my_slot = [&]() { return xbase + static_cast<size_t>((epoch % kRing) * kG + part) * kSlotM; };
     auto step_slots = [&]() { return xbase + static_cast<size_t>(((epoch - 1) % kRing) * kG) * kSlotM; };
@@ -987,13 +985,13 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
 #pragma unroll
                         for (int g2 = 0; g2 < kG; ++g2)
                             __builtin_amdgcn_global_load_lds(rslot + g2 * kSlotM + lr * kD + 16 * (2 * w + k2) + 4 * lg,
-                                                             &sm.u.dma[w][k2 * kG + g2][0], 16, 0, 0);
+                                                             &sm.u.dma[w][k2 * kG + g2][0], 16, 0, kSlotLoadPolicy);
                 }
                 if (zred) {
 #pragma unroll
                     for (int g2 = 0; g2 < kG; ++g2)
                         __builtin_amdgcn_global_load_lds(rslot + g2 * kSlotM + kNP * kD + lr * kD + 16 * part + 4 * lg,
-                                                         &sm.dmaz[g2][0], 16, 0, 0);
+                                                         &sm.dmaz[g2][0], 16, 0, kSlotLoadPolicy);
                 }
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 if (zred) {
@@ -1074,7 +1072,7 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
                 const float* rslot = step_slots();
 #pragma unroll
                 for (int g2 = 0; g2 < kG; ++g2)
-                    __builtin_amdgcn_global_load_lds(rslot + g2 * kSlotM + own * 256 + lane * 4, &sm.u.dma[w][g2][0], 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(rslot + g2 * kSlotM + own * 256 + lane * 4, &sm.u.dma[w][g2][0], 16, 0, kSlotLoadPolicy);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 f32x4 sum = sm.u.dma[w][0][lane];
 #pragma unroll
