@@ -75,7 +75,8 @@ constexpr int kRS = kD + 4;     // LDS row stride (floats) of R rows [t][d]
 constexpr int kRTS = kNP + 4;   // LDS row stride (floats) of R^T rows [d][t]
 constexpr int kLS = kNP + 4;    // LDS row stride (floats) of the decay matrix rows
 constexpr int kWS = 16 + 4;     // LDS row stride (bf16) of a wave's staged W_L^T rows [d][h]
-constexpr int kSlot = 2 * kNP * kD;   // floats per workgroup slot and exchange step: R and z partials
+constexpr int kThreads2 = 256;         // deep_fwd2: two chain waves and two read waves
+constexpr int kSlot = 3 * kNP * kD;   // floats per workgroup slot and exchange step: R, then the two read waves' z partials
 // Exchange slots form a ring of kRing steps per group.  A workgroup writes
 // the slot of step e + kRing only after every workgroup of its group has
 // signalled step e + kRing - 1, i.e. has finished reading step e, so two steps
@@ -184,33 +185,30 @@ struct ChunkBuf {
     alignas(16) float wm[kNP];            // -theta_j gamma_{n-1,j}
     alignas(16) float ws[kNP];            // -theta_j p_{n-1,j}
     alignas(16) float scal[4];            // A_n, c_n, E_n
-};
-
-struct Stash {
-    s16x4 w1[kDT][2][64];
-    s16x4 s1[kDT][2][64];
-    s16x4 w2[kDT][2][64];
-    s16x4 s2[kDT][2][64];
+    alignas(16) float rth[kNP];           // the chunk's raw gates (theta, eta, alpha), for a later gate pass
+    alignas(16) float ret[kNP];
+    alignas(16) float ral[kNP];
 };
 
 struct DeepSmem {
     ChunkBuf buf[2];
     alignas(16) float R[kNP * kRS];              // R rows [t][d]
-    alignas(16) float RT[kD * kRTS];             // R^T rows [d][t]
-    alignas(16) uint16_t wst[kWaves][2][kD * kWS];   // per wave: its W_L rows staged as [d][h], hi and lo
-    alignas(16) f32x4 xpart[kWaves][2][64];      // partner tiles for the two-wave pre-reduction
+    alignas(16) float RT[2][kD * kRTS];          // R^T rows [d][t], by chunk parity (the read waves lag a chunk)
+    alignas(16) uint16_t wst[kWaves][2][kD * kWS];   // per chain wave: its W_L rows staged as [d][h], hi and lo
+    alignas(16) f32x4 xpart[kWaves][2][64];      // partner tiles for the two-wave pre-reduction of R
     // Partials of one exchange step copied from the workspace straight into
-    // LDS (global-to-LDS loads, all in flight at once): per wave its two R
-    // tiles from the G workgroups; the z tile of the reducing workgroups.
+    // LDS (global-to-LDS loads, all in flight at once): per chain wave its two
+    // R tiles from the G workgroups; the z tiles (two per workgroup) of the
+    // reducing workgroups.
     alignas(16) f32x4 dma[kWaves][2 * kG][64];
-    alignas(16) f32x4 dmaz[kG][64];
-    // Chunk-start weights and momenta (bf16 hi / lo fragments) of the last two
-    // chunks, per wave, for the reads of a chunk one step later.
-    Stash stash[kWaves][2];
-    // Ak^T (by chunk parity) and dH fragments (hi / lo), per wave, for the same.
+    alignas(16) f32x4 dmaz[2 * kG][64];
+    // Per chain wave, for the read wave of the same units: SiLU(Hk)^T (bf16
+    // hi / lo) and SiLU(Hk) (float32, K layout) by chunk parity, and dH
+    // (float32, K layout) of the last chunk.
     struct {
         s16x4 akt[2][2][64];
-        s16x4 dh[2][64];
+        f32x4 ak[2][64];
+        f32x4 dh[64];
     } act[kWaves];
     int bail, gid, part;
 };
@@ -319,10 +317,21 @@ __device__ __forceinline__ s16x4 lds_tr4(const uint16_t* base, int rs, int lr, i
     return ds_read_tr16(base + (4 * lg + (lr >> 2)) * rs + 4 * (lr & 3));
 }
 
-__global__ __launch_bounds__(kThreads, 1) void deep_fwd2(const DeepParams p) {
+// Two-layer deep memory.  Waves 0 and 1 (the chain waves) carry the
+// dependent work of a chunk: keys, the R exchange, dH and the carry of the
+// weights.  Waves 2 and 3 (the read waves, units of waves 0 and 1) read the
+// previous chunk -- Hq, Aq and the z partial -- from their own copy of the
+// weights one chunk behind, which they keep by applying the same carry to the
+// same float32 inputs (so both copies hold identical values), and compute the
+// gate quantities of the chunk the chain waves carry next.  Per chunk step the
+// five barriers below are shared by all four waves; the read waves' work fills
+// the chain's segments instead of lengthening them.
+__global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
     __shared__ DeepSmem sm;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool chain = w < 2;
+    const int wp = w & 1;            // the chain wave whose units this wave holds
     const int lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     int* const status = p.work;
@@ -351,12 +360,11 @@ __global__ __launch_bounds__(kThreads, 1) void deep_fwd2(const DeepParams p) {
     int* const ctr = p.work + kHdrInts + gi * kCtrStride;
     float* const xbase = reinterpret_cast<float*>(p.work + kHdrInts + p.ngroups * kCtrStride) +
                          static_cast<size_t>(gi) * kRing * kG * kSlot;
-    const int hu = 32 * part + 16 * w;   // first hidden unit of this wave
-    int epoch = 0;                       // exchanges of this group so far
+    const int hu = 32 * part + 16 * wp;   // first hidden unit of this wave
+    int epoch = 0;                        // exchanges of this group so far
 
     // Group exchange in two halves: signal() after this workgroup's
-    // contribution is written; wait() until all G have signalled.  Work that
-    // needs none of this step's data goes in between.
+    // contribution is written; wait() until all G have signalled.
     auto signal = [&]() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
@@ -386,7 +394,8 @@ __global__ __launch_bounds__(kThreads, 1) void deep_fwd2(const DeepParams p) {
         const int nch = (p.T + p.b - 1) / p.b;
         auto chunk_n = [&](int c) { return min(p.b, p.T - c * p.b); };
 
-        // ---- resident weights: W1[dt] = W_1[16dt.., hu..] as [d][h]; W2[dt] = W_L[hu.., 16dt..] as [h][d] ----
+        // ---- weights: W1[dt] = W_1[16dt.., hu..] as [d][h]; W2[dt] = W_L[hu.., 16dt..] as [h][d] ----
+        // (every wave: the chain waves' copy is current, the read waves' one chunk behind)
         f32x4 W1[kDT], S1[kDT], W2[kDT], S2[kDT];
         {
             const float* w1 = p.W0[0] + s * p.wstride[0];
@@ -405,13 +414,13 @@ __global__ __launch_bounds__(kThreads, 1) void deep_fwd2(const DeepParams p) {
                     S2[dt][e] = s2 ? s2[i2] : 0.f;
                 }
         }
-        // W_L rows of this wave split into bf16 hi / lo (W2s, reused by the
+        // Chain waves: W_L rows split into bf16 hi / lo (W2s, reused by the
         // products of the next chunk) and staged as [d][h] (for the
         // transposed operand of R W_L^T).
         Sp W2s[kDT];
         auto stage_w2 = [&]() {
-            uint16_t* hi = sm.wst[w][0];
-            uint16_t* lo = sm.wst[w][1];
+            uint16_t* hi = sm.wst[wp][0];
+            uint16_t* lo = sm.wst[wp][1];
 #pragma unroll
             for (int dt = 0; dt < kDT; ++dt) {
                 W2s[dt] = split(W2[dt]);
@@ -419,227 +428,231 @@ __global__ __launch_bounds__(kThreads, 1) void deep_fwd2(const DeepParams p) {
                 *reinterpret_cast<s16x4*>(lo + (16 * dt + lr) * kWS + 4 * lg) = W2s[dt].lo;
             }
         };
-        stage_w2();
+        // The carry of one chunk (buffer Bc) from dH, SiLU(Hk) (K layout) and
+        // R^T: the chain waves apply it to their weights, the read waves (a
+        // chunk later) to theirs, from the same float32 values.
+        auto carry = [&](const ChunkBuf& Bc, f32x4 dH, f32x4 Ak, const float* RTc) {
+            const float An = Bc.scal[0], Cn = Bc.scal[1], En = Bc.scal[2];
+            const f32x4 wm4 = *reinterpret_cast<const f32x4*>(Bc.wm + 4 * lg);
+            const f32x4 ws4 = *reinterpret_cast<const f32x4*>(Bc.ws + 4 * lg);
+            const Sp dm = split(dH * wm4), dsv = split(dH * ws4);   // B = (w .* dH)[t][h]
+            // A = (Ak diag(w))^T[h][t]: the token weights ride on Ak.
+            const Sp akm = split(Ak * wm4), aks = split(Ak * ws4);
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt) {
+                const s16x4 kt = lds_tr4(Bc.kb + 16 * dt, kKS, lr, lg);   // A = K^T[d][t]
+                const f32x4 w1 = An * W1[dt] + Cn * S1[dt];
+                S1[dt] = mma2(kt, dsv, En * S1[dt]);
+                W1[dt] = mma2(kt, dm, w1);
+                // R[4lg..4lg+3][16dt + lr]: B = R[t][d] of the W_L carry.
+                const Sp rs = split(*reinterpret_cast<const f32x4*>(RTc + (16 * dt + lr) * kRTS + 4 * lg));
+                const f32x4 w2 = An * W2[dt] + Cn * S2[dt];
+                S2[dt] = mma3(aks, rs, En * S2[dt]);
+                W2[dt] = mma3(akm, rs, w2);
+            }
+        };
+        if (chain) stage_w2();
 
         Prefetch pf;
-        prefetch(pf, p, seq_tok, 0, tid);
+        if (chain) prefetch(pf, p, seq_tok, 0, tid);
         __syncthreads();   // the previous sequence's last use of the chunk buffers
-        if (nch > 0) {
+        if (chain && nch > 0) {
             stage(pf, sm.buf[0], tid);
             if (w == 1) gates(pf, sm.buf[0], chunk_n(0), lane);
         }
         __syncthreads();
 
-        // Iteration c: the keys of chunk c and its exchange; in the exchange's
-        // wait, the reads (z) of chunk c - 1; after it, the z of chunk c - 2,
-        // and the deltas and carry of chunk c.  Two more iterations finish
-        // the z of the last chunks.
-        f32x4 Zp[2] = {};   // this workgroup's z partial of chunk c - 1 (own two d tiles), pre-reduced
+        // Step c: the chain waves run chunk c (keys, exchange, dH, carry); the
+        // read waves read chunk c - 1 and put its z partial in the slot of the
+        // next step; after this step's exchange the z of chunk c - 2 is summed.
+        // Two more steps finish the z of the last chunks.
         bool ok = true;
         const int iters = nch > 0 ? nch + 2 : 0;
         for (int c = 0; c < iters; ++c) {
             const bool keys = c < nch;
-            const bool reads = c >= 1 && c <= nch;   // reads of chunk c - 1 in this step's wait
-            const bool zout = c >= 2;                // z of chunk c - 2 leaves with this step
-            const ChunkBuf& B = sm.buf[c & 1];
+            const bool reads = c >= 1 && c <= nch;    // read waves: chunk c - 1
+            const bool zout = c >= 2;                 // the z of chunk c - 2 leaves with this step
+            ChunkBuf& B = sm.buf[c & 1];
+            const ChunkBuf& Bp = sm.buf[(c + 1) & 1];  // chunk c - 1
+            const float* RTp = sm.RT[(c + 1) & 1];
             const int n = keys ? chunk_n(c) : 0;
-            if (keys && c + 1 < nch) prefetch(pf, p, seq_tok, c + 1, tid);
             float* slot = xbase + static_cast<size_t>((epoch % kRing) * kG + part) * kSlot;
+            float* nslot = xbase + static_cast<size_t>(((epoch + 1) % kRing) * kG + part) * kSlot;
 
-            // ================= keys forward at the chunk-start weights =================
-            f32x4 Ak = {0.f, 0.f, 0.f, 0.f}, dAk = Ak;
-            if (keys) {
-                Stash& st = sm.stash[w][c & 1];
-                f32x4 hk = {0.f, 0.f, 0.f, 0.f}, hkt = hk;
+            // ================= segment 1: keys of chunk c | reads of chunk c - 1 =================
+            f32x4 Ak = {0.f, 0.f, 0.f, 0.f}, dAk = Ak, rp[kDT];
+            Sp aq{}, lgm{};
+            float At = 0.f, Ct = 0.f;
+            if (chain) {
+                if (keys && c + 1 < nch) prefetch(pf, p, seq_tok, c + 1, tid);
+                if (keys) {
+                    f32x4 hk = {0.f, 0.f, 0.f, 0.f}, hkt = hk;
 #pragma unroll
-                for (int dt = 0; dt < kDT; ++dt) {
-                    const s16x4 kf = lds4(B.kb + lr * kKS + 16 * dt + 4 * lg);
-                    const Sp w1s = split(W1[dt]);
-                    hk = mma2(kf, w1s, hk);      // (K W_1)[t][h]
-                    hkt = mma2(w1s, kf, hkt);    // (K W_1)^T[h][t]
-                    // Chunk-start weights and momenta for this chunk's reads.
-                    st.w1[dt][0][lane] = w1s.hi;
-                    st.w1[dt][1][lane] = w1s.lo;
-                    st.w2[dt][0][lane] = W2s[dt].hi;
-                    st.w2[dt][1][lane] = W2s[dt].lo;
-                    const Sp s1s = split(S1[dt]), s2s = split(S2[dt]);
-                    st.s1[dt][0][lane] = s1s.hi;
-                    st.s1[dt][1][lane] = s1s.lo;
-                    st.s2[dt][0][lane] = s2s.hi;
-                    st.s2[dt][1][lane] = s2s.lo;
+                    for (int dt = 0; dt < kDT; ++dt) {
+                        const s16x4 kf = lds4(B.kb + lr * kKS + 16 * dt + 4 * lg);
+                        const Sp w1s = split(W1[dt]);
+                        hk = mma2(kf, w1s, hk);      // (K W_1)[t][h]
+                        hkt = mma2(w1s, kf, hkt);    // (K W_1)^T[h][t]
+                    }
+                    silu_d4(hk, Ak, dAk);
+                    const Sp akt = split(silu4(hkt));   // Ak^T[h][t]
+                    sm.act[w].akt[c & 1][0][lane] = akt.hi;
+                    sm.act[w].akt[c & 1][1][lane] = akt.lo;
+                    sm.act[w].ak[c & 1][lane] = Ak;
+                    // Partial R^T[d][t] over this wave's hidden units; two-wave pre-reduction.
+#pragma unroll
+                    for (int dt = 0; dt < kDT; ++dt) rp[dt] = mma3(W2s[dt], akt, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = w == 0 ? rp[2 + k2] : rp[k2];
                 }
-                silu_d4(hk, Ak, dAk);
-                // Partial R^T[d][t] over this wave's hidden units, d tile dt.
-                const Sp akt = split(silu4(hkt));             // Ak^T[h][t]
-                sm.act[w].akt[c & 1][0][lane] = akt.hi;
-                sm.act[w].akt[c & 1][1][lane] = akt.lo;
-                f32x4 rp[kDT];
-#pragma unroll
-                for (int dt = 0; dt < kDT; ++dt) rp[dt] = mma3(W2s[dt], akt, f32x4{0.f, 0.f, 0.f, 0.f});
-                // Two-wave pre-reduction: wave w keeps d tiles 2w, 2w+1.
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = rp[2 * (1 - w) + k2];
-                __syncthreads();
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    const int dt = 2 * w + k2;
-                    const f32x4 r = rp[dt] + sm.xpart[w][k2][lane];
-                    // lane (t = lr, lg) holds R^T[16dt + 4lg + e][t] = R[t][16dt + 4lg + e]
-                    *reinterpret_cast<f32x4*>(slot + lr * kD + 16 * dt + 4 * lg) = r;
-                }
-            }
-            if (zout) {
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
-                    *reinterpret_cast<f32x4*>(slot + kNP * kD + lr * kD + 16 * (2 * w + k2) + 4 * lg) = Zp[k2];
-            }
-            signal();
-
-            // ================= reads of chunk c - 1 (in the wait) =================
-            if (reads) {
-                const ChunkBuf& Bp = sm.buf[(c - 1) & 1];
-                const Stash& st = sm.stash[w][(c - 1) & 1];
-                const float At = Bp.A[lr], Ct = Bp.C[lr];
+            } else if (reads) {
+                At = Bp.A[lr];
+                Ct = Bp.C[lr];
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(Bp.L + lr * kLS + 4 * lg);   // L[t][4lg..]
                 f32x4 kq = {0.f, 0.f, 0.f, 0.f}, za = kq, zc = kq;
 #pragma unroll
                 for (int dt = 0; dt < kDT; ++dt) {
                     const s16x4 kf = lds4(Bp.kb + lr * kKS + 16 * dt + 4 * lg);
                     const s16x4 qf = lds4(Bp.qb + lr * kKS + 16 * dt + 4 * lg);
-                    kq = mma(kf, qf, kq);                                            // (K Q^T)[j][t]
-                    za = mma2(Sp{st.w1[dt][0][lane], st.w1[dt][1][lane]}, qf, za);   // (W_1^T Q^T)[h][t]
-                    zc = mma2(Sp{st.s1[dt][0][lane], st.s1[dt][1][lane]}, qf, zc);
+                    kq = mma(kf, qf, kq);                  // (K Q^T)[j][t]
+                    za = mma2(split(W1[dt]), qf, za);     // (W_1^T Q^T)[h][t]
+                    zc = mma2(split(S1[dt]), qf, zc);
                 }
                 const Sp pt = split(kq * l4);             // P^T[j][t] = (L .* Q K^T)[t][j]
-                const Sp dHs{sm.act[w].dh[0][lane], sm.act[w].dh[1][lane]};
-                const Sp akt{sm.act[w].akt[(c - 1) & 1][0][lane], sm.act[w].akt[(c - 1) & 1][1][lane]};
-                f32x4 hq = mma3(dHs, pt, f32x4{0.f, 0.f, 0.f, 0.f});   // (dH^T P^T)[h][t]
+                f32x4 hq = mma3(split(sm.act[wp].dh[lane]), pt, f32x4{0.f, 0.f, 0.f, 0.f});   // (dH^T P^T)[h][t]
                 hq = At * za + Ct * zc - hq;
-                const Sp aq = split(silu4(hq));           // Aq^T[h][t]
+                aq = split(silu4(hq));                   // Aq^T[h][t]
+                const Sp akt{sm.act[wp].akt[(c + 1) & 1][0][lane], sm.act[wp].akt[(c + 1) & 1][1][lane]};
                 // (Ak Aq^T)[j][t] over this wave's hidden units, times L.
-                const Sp lg4 = split(mma3(akt, aq, f32x4{0.f, 0.f, 0.f, 0.f}) * l4);
-                f32x4 zp[kDT];
-#pragma unroll
-                for (int dt = 0; dt < kDT; ++dt) {
-                    const f32x4 a2 = mma3(Sp{st.w2[dt][0][lane], st.w2[dt][1][lane]}, aq, f32x4{0.f, 0.f, 0.f, 0.f});
-                    const f32x4 c2 = mma3(Sp{st.s2[dt][0][lane], st.s2[dt][1][lane]}, aq, f32x4{0.f, 0.f, 0.f, 0.f});
-                    const Sp rs = split(*reinterpret_cast<const f32x4*>(sm.RT + (16 * dt + lr) * kRTS + 4 * lg));
-                    const f32x4 in = mma3(rs, lg4, f32x4{0.f, 0.f, 0.f, 0.f});   // (R^T (L .* G)^T)[d][t]
-                    zp[dt] = At * a2 + Ct * c2 - in;
-                }
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) sm.xpart[1 - w][k2][lane] = zp[2 * (1 - w) + k2];
-                __syncthreads();
+                lgm = split(mma3(akt, aq, f32x4{0.f, 0.f, 0.f, 0.f}) * l4);
+            }
+            __syncthreads();
+
+            // ================= segment 2: R partial to the slot; signal =================
+            if (chain && keys) {
 #pragma unroll
                 for (int k2 = 0; k2 < 2; ++k2) {
                     const int dt = 2 * w + k2;
-                    Zp[k2] = zp[dt] + sm.xpart[w][k2][lane];
-                    // z = q + the sum of the partials: workgroup 0 adds q.
-                    if (part == 0) Zp[k2] += unpack4(lds4(Bp.qb + lr * kKS + 16 * dt + 4 * lg));
+                    const f32x4 r = (w == 0 ? rp[k2] : rp[2 + k2]) + sm.xpart[w][k2][lane];
+                    // lane (t = lr, lg) holds R^T[16dt + 4lg + e][t] = R[t][16dt + 4lg + e]
+                    *reinterpret_cast<f32x4*>(slot + lr * kD + 16 * dt + 4 * lg) = r;
                 }
-            } else {
-                __syncthreads();
             }
-            // Gate quantities of chunk c + 1 (their buffer held chunk c - 1's, read above).
-            if (w == 1 && keys && c + 1 < nch) gates(pf, sm.buf[(c + 1) & 1], chunk_n(c + 1), lane);
+            signal();
+
+            // ================= segment 3 (the wait): z partial of chunk c - 1 =================
+            if (!chain && reads) {
+                // z = q + the sum of the partials: read wave 0 of workgroup 0 adds q.
+                float* zs = nslot + kNP * kD * (1 + wp) + lr * kD + 4 * lg;
+#pragma unroll
+                for (int dt = 0; dt < kDT; ++dt) {
+                    const f32x4 a2 = mma3(split(W2[dt]), aq, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 c2 = mma3(split(S2[dt]), aq, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const Sp rs = split(*reinterpret_cast<const f32x4*>(RTp + (16 * dt + lr) * kRTS + 4 * lg));
+                    const f32x4 in = mma3(rs, lgm, f32x4{0.f, 0.f, 0.f, 0.f});   // (R^T (L .* G)^T)[d][t]
+                    f32x4 zp = At * a2 + Ct * c2 - in;
+                    if (part == 0 && wp == 0) zp += unpack4(lds4(Bp.qb + lr * kKS + 16 * dt + 4 * lg));
+                    *reinterpret_cast<f32x4*>(zs + 16 * dt) = zp;
+                }
+            }
             if (!wait()) {
                 ok = false;
                 break;
             }
             const float* rslot = xbase + static_cast<size_t>(((epoch - 1) % kRing) * kG) * kSlot;
 
-            // Copy this step's partials into LDS: every load in flight at once,
-            // none through registers.
+            // ================= segment 4: partials in; z out | the read waves' carry, next gates =================
             const bool zred = zout && part < kDT && w == 0;
-            if (keys) {
+            if (chain) {
+                if (keys) {
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
+                    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                        for (int g2 = 0; g2 < kG; ++g2)
+                            __builtin_amdgcn_global_load_lds(rslot + g2 * kSlot + lr * kD + 16 * (2 * w + k2) + 4 * lg,
+                                                             &sm.dma[w][k2 * kG + g2][0], 16, 0, kSlotLoadPolicy);
+                }
+                if (zred) {
 #pragma unroll
                     for (int g2 = 0; g2 < kG; ++g2)
-                        __builtin_amdgcn_global_load_lds(rslot + g2 * kSlot + lr * kD + 16 * (2 * w + k2) + 4 * lg,
-                                                         &sm.dma[w][k2 * kG + g2][0], 16, 0, kSlotLoadPolicy);
-            }
-            if (zred) {
 #pragma unroll
-                for (int g2 = 0; g2 < kG; ++g2)
-                    __builtin_amdgcn_global_load_lds(rslot + g2 * kSlot + kNP * kD + lr * kD + 16 * part + 4 * lg,
-                                                     &sm.dmaz[g2][0], 16, 0, kSlotLoadPolicy);
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-            // ================= z of chunk c - 2: four workgroups, one d tile each =================
-            if (zred) {
-                const int np = chunk_n(c - 2);
-                f32x4 zt = sm.dmaz[0][lane];
+                        for (int r2 = 0; r2 < 2; ++r2)
+                            __builtin_amdgcn_global_load_lds(rslot + g2 * kSlot + kNP * kD * (1 + r2) + lr * kD + 16 * part + 4 * lg,
+                                                             &sm.dmaz[2 * g2 + r2][0], 16, 0, kSlotLoadPolicy);
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                // z of chunk c - 2: four workgroups, one d tile each.
+                if (zred) {
+                    const int np = chunk_n(c - 2);
+                    f32x4 zt = sm.dmaz[0][lane];
 #pragma unroll
-                for (int g2 = 1; g2 < kG; ++g2) zt += sm.dmaz[g2][lane];
-                const bool zb = p.z_bf16 != 0;
-                const uint32_t zsz = zb ? 2u : 4u;
-                const auto rz = make_rsrc(static_cast<char*>(p.z) + (seq_tok + static_cast<size_t>(c - 2) * p.b) * kD * zsz,
-                                          static_cast<uint32_t>(np) * kD * zsz);
-                store_out4(zt, rz, static_cast<uint32_t>(lr * kD + 16 * part + 4 * lg), zb);
-            }
-            if (!keys) continue;
-
-            // ================= R = K - V + sum of partials =================
+                    for (int g2 = 1; g2 < 2 * kG; ++g2) zt += sm.dmaz[g2][lane];
+                    const bool zb = p.z_bf16 != 0;
+                    const uint32_t zsz = zb ? 2u : 4u;
+                    const auto rz = make_rsrc(static_cast<char*>(p.z) + (seq_tok + static_cast<size_t>(c - 2) * p.b) * kD * zsz,
+                                              static_cast<uint32_t>(np) * kD * zsz);
+                    store_out4(zt, rz, static_cast<uint32_t>(lr * kD + 16 * part + 4 * lg), zb);
+                }
+                // R = K - V + sum of partials (rows [t][d] and R^T [d][t] of this chunk's parity).
+                if (keys) {
+                    float* RTc = sm.RT[c & 1];
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const int dt = 2 * w + k2;
-                f32x4 r = unpack4(lds4(B.kb + lr * kKS + 16 * dt + 4 * lg)) - unpack4(lds4(B.vb + lr * kKS + 16 * dt + 4 * lg));
+                    for (int k2 = 0; k2 < 2; ++k2) {
+                        const int dt = 2 * w + k2;
+                        f32x4 r = unpack4(lds4(B.kb + lr * kKS + 16 * dt + 4 * lg)) - unpack4(lds4(B.vb + lr * kKS + 16 * dt + 4 * lg));
 #pragma unroll
-                for (int g2 = 0; g2 < kG; ++g2) r += sm.dma[w][k2 * kG + g2][lane];
-                if (lr >= n) r = f32x4{0.f, 0.f, 0.f, 0.f};   // padding tokens carry no residual
-                *reinterpret_cast<f32x4*>(sm.R + lr * kRS + 16 * dt + 4 * lg) = r;
+                        for (int g2 = 0; g2 < kG; ++g2) r += sm.dma[w][k2 * kG + g2][lane];
+                        if (lr >= n) r = f32x4{0.f, 0.f, 0.f, 0.f};   // padding tokens carry no residual
+                        *reinterpret_cast<f32x4*>(sm.R + lr * kRS + 16 * dt + 4 * lg) = r;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm.RT[(16 * dt + 4 * lg + e) * kRTS + lr] = r[e];
+                        for (int e = 0; e < 4; ++e) RTc[(16 * dt + 4 * lg + e) * kRTS + lr] = r[e];
+                    }
+                }
+            } else {
+                // The carry of chunk c - 1 on the read waves' weights (needed
+                // only while a later chunk remains to be read).
+                if (reads && c < nch) carry(Bp, sm.act[wp].dh[lane], sm.act[wp].ak[(c + 1) & 1][lane], RTp);
+                // Gate quantities of chunk c (from its raw gates), for the chain's carry below.
+                if (w == 2 && keys && c >= 1) {
+                    Prefetch g;
+                    g.th = lane < kNP ? B.rth[lane] : 0.f;
+                    g.et = lane < kNP ? B.ret[lane] : 0.f;
+                    g.al = lane < kNP ? B.ral[lane] : 0.f;
+                    gates(g, B, n, lane);
+                }
             }
             __syncthreads();
+            if (!keys) continue;
 
-            // ================= dH = (R W_L^T) .* SiLU'(Hk) =================
-            f32x4 dH = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int dt = 0; dt < kDT; ++dt) {
-                const Sp rf = split(*reinterpret_cast<const f32x4*>(sm.R + lr * kRS + 16 * dt + 4 * lg));
-                const Sp wt{lds_tr4(sm.wst[w][0] + 16 * dt * kWS, kWS, lr, lg), lds_tr4(sm.wst[w][1] + 16 * dt * kWS, kWS, lr, lg)};
-                dH = mma3(rf, wt, dH);   // [t][h]
-            }
-            dH *= dAk;
-            {
-                const Sp dHs = split(dH);   // for this chunk's reads, in the next step's wait
-                sm.act[w].dh[0][lane] = dHs.hi;
-                sm.act[w].dh[1][lane] = dHs.lo;
-            }
-
-            // ================= carry =================
-            {
-                const float An = B.scal[0], Cn = B.scal[1], En = B.scal[2];
-                const f32x4 wm4 = *reinterpret_cast<const f32x4*>(B.wm + 4 * lg);
-                const f32x4 ws4 = *reinterpret_cast<const f32x4*>(B.ws + 4 * lg);
-                const Sp dm = split(dH * wm4), dsv = split(dH * ws4);   // B = (w .* dH)[t][h]
-                // A = (Ak diag(w))^T[h][t]: the token weights ride on Ak.
-                const Sp akm = split(Ak * wm4), aks = split(Ak * ws4);
+            // ================= segment 5: dH and the carry of chunk c =================
+            if (chain) {
+                f32x4 dH = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int dt = 0; dt < kDT; ++dt) {
-                    const s16x4 kt = lds_tr4(B.kb + 16 * dt, kKS, lr, lg);   // A = K^T[d][t]
-                    const f32x4 w1 = An * W1[dt] + Cn * S1[dt];
-                    S1[dt] = mma2(kt, dsv, En * S1[dt]);
-                    W1[dt] = mma2(kt, dm, w1);
-                    // R[4lg..4lg+3][16dt + lr]: B = R[t][d] of the W_L carry.
-                    const Sp rs = split(*reinterpret_cast<const f32x4*>(sm.RT + (16 * dt + lr) * kRTS + 4 * lg));
-                    const f32x4 w2 = An * W2[dt] + Cn * S2[dt];
-                    S2[dt] = mma3(aks, rs, En * S2[dt]);
-                    W2[dt] = mma3(akm, rs, w2);
+                    const Sp rf = split(*reinterpret_cast<const f32x4*>(sm.R + lr * kRS + 16 * dt + 4 * lg));
+                    const Sp wt{lds_tr4(sm.wst[w][0] + 16 * dt * kWS, kWS, lr, lg), lds_tr4(sm.wst[w][1] + 16 * dt * kWS, kWS, lr, lg)};
+                    dH = mma3(rf, wt, dH);   // [t][h]
                 }
+                dH *= dAk;
+                sm.act[w].dh[lane] = dH;
+                carry(B, dH, Ak, sm.RT[c & 1]);
                 stage_w2();
+                if (c + 1 < nch) {
+                    ChunkBuf& Bn = sm.buf[(c + 1) & 1];
+                    stage(pf, Bn, tid);
+                    if (w == 1 && lane < kNP) {   // the next chunk's raw gates (padding tokens read 0)
+                        Bn.rth[lane] = pf.th;
+                        Bn.ret[lane] = pf.et;
+                        Bn.ral[lane] = pf.al;
+                    }
+                }
             }
-            // ================= next chunk's inputs =================
-            if (c + 1 < nch) stage(pf, sm.buf[(c + 1) & 1], tid);
             __syncthreads();
         }
         if (!ok) break;
 
-        // ---- final weights ----
-        {
+        // ---- final weights (the chain waves' copy) ----
+        if (chain) {
             float* w1 = p.WT[0] ? p.WT[0] + s * p.wstride[0] : nullptr;
             float* s1 = p.ST[0] ? p.ST[0] + s * p.wstride[0] : nullptr;
             float* w2 = p.WT[1] ? p.WT[1] + s * p.wstride[1] : nullptr;
@@ -1363,7 +1376,8 @@ int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
     if (hipDeviceGetAttribute(&nxcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || nxcc < 1) nxcc = 1;
     void (*const kfn)(const DeepParams) = depth == 2 ? deep_fwd2 : depth == 3 ? deep_fwd3 : deep_fwd4;
     const void* kern = reinterpret_cast<const void*>(kfn);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess) return TTT_ERR_HIP;
+    const int threads = depth == 2 ? kThreads2 : kThreads;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess) return TTT_ERR_HIP;
     int max_groups = (ncu * occ / kG) / 8 * 8;
     if (use_scratch && max_groups > kScratchGroups) max_groups = kScratchGroups;
     if (max_groups < 8) return TTT_ERR_UNSUPPORTED;
@@ -1410,7 +1424,7 @@ int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
     hipError_t err = hipGetLastError();
     if (err == hipSuccess) {
         void* args[] = {&p};
-        err = hipLaunchCooperativeKernel(kern, dim3(static_cast<unsigned>(ngroups * kG)), dim3(kThreads), args, 0,
+        err = hipLaunchCooperativeKernel(kern, dim3(static_cast<unsigned>(ngroups * kG)), dim3(threads), args, 0,
                                          stream);
     }
     if (own_work) hipFreeAsync(work, stream);
