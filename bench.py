@@ -496,7 +496,7 @@ def varlen_main(args):
     """Packed variable-length documents with the Titans recipe: H=16, d=128, b=64,
     B*T = 32768 tokens per head split into documents of seeded lengths."""
     wv = WORKLOADS[3].replace(B=1, T=4 * 8192)
-    lengths = varlen_lengths(wv.T)
+    lengths = varlen_lengths(wv.T, mean=args.doc_mean)
     N, H, T, d = len(lengths), wv.H, wv.T, wv.d
     log(f"varlen workload: {N} documents, lengths min {min(lengths)} median {int(np.median(lengths))} "
         f"max {max(lengths)}, {T} tokens per head, H={H} d={d} b={wv.b}")
@@ -555,7 +555,7 @@ def varlen_main(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "titans-linear-varlen", "documents": N, "tokens_per_head": T, "H": H, "d": d,
-                   "b": wv.b, "lengths": "lognormal(sigma 1) around 1024, clipped to [1, 8192], seed 3001",
+                   "b": wv.b, "lengths": f"lognormal(sigma 1) around {args.doc_mean}, clipped to [1, 8192], seed 3001",
                    "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "state": "f32", "z": "f32"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wv, "varlen"),
@@ -571,7 +571,7 @@ def varlen_train_main(args):
     ``--varlen`` workload): the forward that keeps every document's chunk-start
     states, then the backward pass over the same documents."""
     wv = WORKLOADS[3].replace(B=1, T=4 * 8192)
-    lengths = varlen_lengths(wv.T)
+    lengths = varlen_lengths(wv.T, mean=args.doc_mean)
     N, H, T, d, b = len(lengths), wv.H, wv.T, wv.d, wv.b
     log(f"varlen training workload: {N} documents, lengths min {min(lengths)} median {int(np.median(lengths))} "
         f"max {max(lengths)}, {T} tokens per head, H={H} d={d} b={b}")
@@ -648,7 +648,7 @@ def varlen_train_main(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "titans-linear-varlen-train", "documents": N, "tokens_per_head": T, "H": H,
-                   "d": d, "b": b, "lengths": "lognormal(sigma 1) around 1024, clipped to [1, 8192], seed 3001",
+                   "d": d, "b": b, "lengths": f"lognormal(sigma 1) around {args.doc_mean}, clipped to [1, 8192], seed 3001",
                    "inputs": "bf16 q,k,v; f32 gates; f32 dz (seeded N(0,1))", "accumulate": "f32",
                    "gradients": "f32", "checkpoints": "fp16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                    "checkpoint_bytes": ckpt.numel() * ckpt.element_size()},
@@ -786,6 +786,8 @@ def main():
                     help="time packed variable-length documents with the Titans recipe instead")
     ap.add_argument("--backward", action="store_true",
                     help="time one training step (forward with checkpoints + backward) on the Titans workload")
+    ap.add_argument("--doc-mean", type=int, default=1024,
+                    help="--varlen: mean document length (lognormal lengths; 1024 packs 31 documents per head)")
     ap.add_argument("--chunk-gates", action="store_true",
                     help="time the Titans forward with gates shared by each chunk's tokens instead")
     ap.add_argument("--z-f32", action="store_true",

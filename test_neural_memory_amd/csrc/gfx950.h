@@ -258,15 +258,16 @@ __device__ __forceinline__ int doc_chunk_prefix(const int* cu, int s, int T, int
 
 // Packed documents: the document of rank r when the N documents are ordered
 // by length, longest first (ties by index, so a permutation); lane is the
-// lane index in a 64-wide wave.  Workgroups
-// dispatched first then take the longest chains (longest processing time
-// first), and the short ones fill in behind them.  Every wave computes it
-// (lanes over candidate documents, the table read with uniform indices);
-// above kLptDocs documents the packing order is kept.
+// lane index in a 64-wide wave.  Workgroups dispatched first then take the
+// longest chains (longest processing time first), and the short ones fill in
+// behind them.  Up to kLptDocs documents every wave computes it (lanes over
+// candidate documents, the table read with uniform indices); above that the
+// order comes from doc_rank_order (perm[r], written by a pass before the
+// launch), or, with no such table, the packing order is kept.
 constexpr int kLptDocs = 128;
-__device__ __forceinline__ int doc_of_rank(const int* cu, int N, int T, int r, int lane) {
+__device__ __forceinline__ int doc_of_rank(const int* cu, int N, int T, int r, int lane, const int* perm = nullptr) {
     static_assert(kLptDocs <= 128, "two lengths per lane");
-    if (N > kLptDocs) return r;
+    if (N > kLptDocs) return perm ? perm[r] : r;
     // Lane l holds the lengths of documents l and 64 + l (-1 past N); the
     // rank loop reads them back with uniform lane reads, not memory loads.
     int len[2];
@@ -294,6 +295,52 @@ __device__ __forceinline__ int doc_of_rank(const int* cu, int N, int T, int r, i
         if (hit) return 64 * g + __ffsll(static_cast<long long>(hit)) - 1;
     }
     return r;
+}
+
+// perm[rank(i)] = i for the same order (length descending, index ascending),
+// any N: thread i counts the documents that come before document i, reading
+// the lengths through LDS 256 at a time.  The ranks are distinct, so perm is
+// a permutation of 0 .. N-1.  Launch: ceil(N / 256) workgroups of 256.
+__global__ __launch_bounds__(256) void doc_rank_order(const int* __restrict__ cu, int N, int T, int* __restrict__ perm) {
+    __shared__ int lens[256];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    int t0;
+    const int li = i < N ? doc_len(cu, i, T, t0) : -1;
+    int rank = 0;
+    for (int base = 0; base < N; base += 256) {
+        __syncthreads();
+        const int j = base + threadIdx.x;
+        lens[threadIdx.x] = j < N ? doc_len(cu, j, T, t0) : -1;
+        __syncthreads();
+        const int cnt = min(256, N - base);
+        for (int jj = 0; jj < cnt; ++jj) {
+            const int lj = lens[jj];
+            rank += (lj > li || (lj == li && base + jj < i)) ? 1 : 0;
+        }
+    }
+    if (i < N) perm[rank] = i;
+}
+
+// Host: the LPT order table for N packed documents when the in-kernel ranking
+// does not cover them (N > kLptDocs): N ints from the stream-ordered
+// allocator, filled by doc_rank_order on `stream`; NULL (and hipSuccess) when
+// not needed.  The caller frees it with hipFreeAsync after its launches.
+hipError_t make_doc_order(const int* cu, int N, int T, hipStream_t stream, int** perm) {
+    *perm = nullptr;
+    if (N <= kLptDocs) return hipSuccess;
+    hipError_t err = hipMallocAsync(reinterpret_cast<void**>(perm), static_cast<size_t>(N) * sizeof(int), stream);
+    if (err != hipSuccess) {
+        *perm = nullptr;
+        return err;
+    }
+    hipLaunchKernelGGL(doc_rank_order, dim3(static_cast<unsigned>((N + 255) / 256)), dim3(256), 0, stream, cu, N, T,
+                       *perm);
+    err = hipGetLastError();
+    if (err != hipSuccess) {
+        (void)hipFreeAsync(*perm, stream);
+        *perm = nullptr;
+    }
+    return err;
 }
 
 }  // namespace

@@ -178,6 +178,7 @@ struct Params {
     int chunk_gates;
     int tcmax;   // packed documents: chunk slots per head
     int z_bf16;  // z element type: 0 float32, 1 bf16
+    const int* perm;   // packed documents above kLptDocs: their longest-first order (NULL: packing order)
 };
 
 // Compile-time geometry of one kernel instance: NS 16-row tiles per
@@ -1184,7 +1185,7 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
             rb = m % Gm::NRB;
             u = (m / Gm::NRB) * 8 + x;
         }
-        const int s = doc_of_rank(p.cu, p.BH / p.H, p.T, u / p.H, lane), h = u % p.H;
+        const int s = doc_of_rank(p.cu, p.BH / p.H, p.T, u / p.H, lane, p.perm), h = u % p.H;
         bh = s * p.H + h;
         // Offsets clamped into [0, T]: a malformed table cannot send any
         // access outside the packed arrays.
@@ -1519,7 +1520,14 @@ int forward_varlen_impl(const void* q, const void* k, const void* v, const float
 
     Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H, ckpt, 0,
              static_cast<int>(tcmax), 0};
-    const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
+    // More documents than the in-kernel ranking covers: a pass before the
+    // launch writes their longest-first order to a stream-ordered table.
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int* perm = nullptr;
+    if (Tlen > 0 && make_doc_order(cu, N, Tlen, s, &perm) != hipSuccess) return TTT_ERR_HIP;
+    p.perm = perm;
+    const hipError_t err = dispatch<T>(p, d, s);
+    if (perm) (void)hipFreeAsync(perm, s);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

@@ -348,6 +348,8 @@ struct CarryParams {
     int tcmax;
     // Partial maxima of the cotangents per sequence bh; NULL: no scaling.
     const float* smax;
+    // Packed documents above kLptDocs: their longest-first order (NULL: packing order).
+    const int* perm;
 };
 
 template <typename T, int D, int NS, int NP>
@@ -606,7 +608,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
             rb = m % Gm::NRB;
             u = (m / Gm::NRB) * 8 + x;
         }
-        const int s = doc_of_rank(p.cu, p.BH / p.H, p.T, u / p.H, lane), h = u % p.H;
+        const int s = doc_of_rank(p.cu, p.BH / p.H, p.T, u / p.H, lane, p.perm), h = u % p.H;
         bh = s * p.H + h;
         int t0;
         seqlen = doc_len(p.cu, s, p.T, t0);
@@ -1657,8 +1659,11 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
         const hipError_t e0 = hipGetLastError();
         if (e0 != hipSuccess) return TTT_ERR_HIP;
     }
+    int* perm = nullptr;
+    if (packed && Tlen > 0 && make_doc_order(cu, B, Tlen, s, &perm) != hipSuccess) return TTT_ERR_HIP;
     const CarryParams cp{q, k, dz, theta, eta, alpha, dMT, dST, work, dv, dM0, dS0,
-                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax), smax};
+                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax), smax,
+                         perm};
     const GradParams gp{q, k, v, theta, eta, alpha, ckpt, work, dz, dv, dq, dk, dth, deta, dal,
                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax), smax};
     hipError_t err;
@@ -1668,6 +1673,7 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
         case 64: err = launch_bwd_np<T, 64>(cp, gp, b, s); break;
         default: err = launch_bwd_np<T, 128>(cp, gp, b, s); break;
     }
+    if (perm) (void)hipFreeAsync(perm, s);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

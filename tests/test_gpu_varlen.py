@@ -78,10 +78,12 @@ CASES = [
     ("titans-d64-b16", 3, 2, [50, 16, 7, 100], 16, 64),
     ("ttt-b16", 2, 2, [31, 90, 16, 3], 16, None),
     ("tiny-d16", 1, 2, [9, 1, 24, 8], 8, None),
-    # 150 documents: above 128 the dispatch keeps the packing order.
-    # 100 documents: the longest-first ranking uses both of its 64-lane groups.
+    # 100 documents: the in-kernel longest-first ranking uses both of its 64-lane groups.
+    # 150 and 600 documents: the order comes from the ranking pass before the launch
+    # (lengths 0 .. 40, so empty documents and many ties).
     ("hundred-docs", 3, 1, [int(x) for x in np.random.default_rng(6).integers(0, 41, 100)], 16, 32),
     ("many-docs", 3, 1, [int(x) for x in np.random.default_rng(5).integers(0, 41, 150)], 16, 32),
+    ("600-docs", 3, 2, [int(x) for x in np.random.default_rng(7).integers(0, 41, 600)], 16, 32),
 ]
 
 

@@ -86,10 +86,12 @@ CASES = [
     ("ttt-b16", 2, 2, [31, 90, 16, 3], 16, None),
     ("tiny-d16", 1, 2, [9, 1, 24, 8], 8, None),
     # 150 documents: the gradient kernel's document search takes three 64-lane
-    # steps, and above 128 documents the carry walk keeps the packing order.
-    # 100 documents: the longest-first ranking uses both of its 64-lane groups.
+    # steps, and above 128 documents the carry walk takes its order from the
+    # ranking pass before the launch (600: ten steps, many ties and empty ones).
+    # 100 documents: the in-kernel longest-first ranking uses both of its 64-lane groups.
     ("hundred-docs", 3, 1, [int(x) for x in np.random.default_rng(6).integers(0, 41, 100)], 16, 32),
     ("many-docs", 3, 1, [int(x) for x in np.random.default_rng(5).integers(0, 41, 150)], 16, 32),
+    ("600-docs", 3, 1, [int(x) for x in np.random.default_rng(7).integers(0, 41, 600)], 16, 32),
 ]
 
 
