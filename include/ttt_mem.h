@@ -226,11 +226,18 @@ int ttt_mem_deep_status(const void* work, void* stream);
  *     cu_seqlens[s+1]-1.  (The host cannot read it; the kernel clamps every
  *     offset into [0, T], so a malformed table gives wrong results, never an
  *     access outside the arrays.)  An empty document copies its initial state.
- *   Order: documents run longest first.  Above 128 documents a ranking pass
- *     on `stream` writes that order to N ints taken from the stream-ordered
- *     allocator (hipMallocAsync) and returned with hipFreeAsync on the same
- *     stream after the launch; TTT_ERR_HIP if that allocation fails.  This
- *     also holds for the training entry points below.
+ *   Order: documents run longest first.  On the bf16 entry points at
+ *     d >= 64, when the ranking fits the workgroup's LDS (up to 2048
+ *     documents at d = 128 and b > 32, at least 680 in every configuration)
+ *     and no workgroup lane takes more than 384 (document, head) pairs, the
+ *     launch is persistent: about one workgroup per CU ranks the documents
+ *     itself and walks its share of them, nothing is allocated.  Otherwise one
+ *     workgroup runs per document, and above 128 documents a ranking pass on
+ *     `stream` writes the order to N ints taken from the stream-ordered
+ *     allocator (hipMallocAsync), returned with hipFreeAsync on the same
+ *     stream after the launch; TTT_ERR_HIP if that allocation fails.  The
+ *     training entry points below use the same forward; their backward pass
+ *     always takes the second form.
  *   Layouts: q, k, v, z [H, T, d]; theta, eta, alpha [H, T]; M0, S0, M_T, S_T
  *     [N, H, d, d] (document-major).  Tokens outside every document are not
  *     read and their z is not written.

@@ -74,6 +74,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <type_traits>
+
 #include "ttt_mem.h"
 #include "gfx950.h"
 
@@ -88,6 +91,7 @@ constexpr int kLdsBytes = 160 * 1024;
 __host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 __host__ __device__ constexpr int cdiv(int x, int m) { return (x + m - 1) / m; }
 __host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
+__host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
 // LDS service on gfx950 (measured with the bank-conflict counter): 64 banks
 // of 4 bytes.  A ds_read_b128 is served in four passes of 16 lanes -- lanes
@@ -220,8 +224,18 @@ struct Geo {
                                      (F16 ? NP * LV * 2 : (DS * LKT + RB * LV) * 4);
     static constexpr int XCH_BYTES = CS > 1 ? NS * (2 * NKC * kWave * 16 + NT * kWave * 8) : 0;
     static constexpr int GATE_BYTES = 2 * (2 * NT * kGB + NT * NP * 3 + 2 * NP) * 4 + 4 * (2 * NP + 4) * 4;
-    static constexpr int HELP_BYTES = GATE_BYTES + XCH_BYTES;
+    // Packed documents on the pipelined instances run persistent workgroups
+    // that walk a table of their (document, head) units, KMAX at most.
+    static constexpr bool PIPE = F16 && CS == 2;
+    static constexpr int KMAX = PIPE ? 384 : 0;
+    static constexpr int UNIT_BYTES = PIPE ? KMAX * 16 + 16 : 0;
+    static constexpr int HELP_BYTES = GATE_BYTES + XCH_BYTES + UNIT_BYTES;
     static constexpr int NBUF = (2 * BUF_BYTES + HELP_BYTES + 1024 <= kLdsBytes) ? 2 : 1;
+    static constexpr bool PERSIST = PIPE && NBUF == 2;
+    // Documents the persistent schedule ranks in LDS: four ints each, and one
+    // per unit of the workgroup, in the second chunk buffer, which the
+    // schedule borrows before the pipeline starts.
+    static constexpr int NMAX_DOCS = cmin(2048, (BUF_BYTES / 4 - KMAX) / 4);
     // The dense decay matrix theta_j gamma_ij of one chunk, when it fits.
     static constexpr int GAM_BYTES = NP * NP * 4;
     static constexpr bool USE_GAM = NBUF * BUF_BYTES + HELP_BYTES + GAM_BYTES + 1024 <= kLdsBytes;
@@ -275,6 +289,15 @@ struct Smem {
     alignas(16) f16x8 xm[CS > 1 ? NS * Gm::NKC * kWave : 1];
     alignas(16) f16x8 xs[CS > 1 ? NS * Gm::NKC * kWave : 1];
     alignas(16) f16x4 xe[CS > 1 ? NS * Gm::NT * kWave : 1];
+    // Persistent packed documents: the workgroup's non-empty units in walk
+    // order (first token in the [H, T] rows, length, checkpoint slot of its
+    // first chunk, state slot s * H + h), their count, their chunks in all,
+    // and the number of empty units.
+    struct Unit {
+        int tok0, len, ck0, bh;
+    };
+    Unit units[Gm::KMAX > 0 ? Gm::KMAX : 1];
+    int nitems, nunits, nempty;
 };
 
 template <typename T, int D, int NS, int CS, int NP>
@@ -965,7 +988,9 @@ struct Kernel {
     // with the transposed k reads of the next column tile in flight.  The
     // intra-chunk products run over every token k-group: the blocks of P
     // above its diagonal are never written and stay zero.
-    template <int BI>
+    // FRAGS: end with the next chunk's fragments (frags2); the persistent walk
+    // calls frags2 itself, after any switch to the next document.
+    template <int BI, bool FRAGS = true>
     __device__ static void phaseB2(const Lanes& a, f32x4* Macc, f32x4* Sacc, F* MB, F* SB, f32x4* Zp,
                                    __amdgpu_buffer_rsrc_t rz, uint32_t zoff, bool zb) {
         constexpr uint32_t BO = BI * kBufB;
@@ -1027,6 +1052,12 @@ struct Kernel {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (FRAGS) frags2(a, Macc, Sacc, MB, SB);
+    }
+
+    // fp16 fragments of the own columns of M, S for the next chunk, and their
+    // copy in the exchange for the partner wave.
+    __device__ static void frags2(const Lanes& a, const f32x4* Macc, const f32x4* Sacc, F* MB, F* SB) {
 #pragma unroll
         for (int sw = 0; sw < NKCW; ++sw) {
             MB[sw] = O::template from_acc<NCW>(Macc, sw);
@@ -1141,6 +1172,513 @@ __device__ __forceinline__ void producer_loop_impl(const Params& p, typename Ker
             __syncthreads();
             __syncthreads();
             __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Packed documents on persistent workgroups.
+//
+// One workgroup launch per (document, head, row block) pays the chunk
+// pipeline's fill (loads, staging, gate scan, decay matrix and P tiles ahead
+// of the first chunk) and its drain every time, several chunk periods for a
+// document of a few chunks.  Here about one workgroup per CU walks many
+// documents as one stream of chunks: the producers keep running ahead across
+// document boundaries, and the state waves store a document's final state and
+// take the next one's initial state between the update of its last chunk and
+// the fragments of the next chunk.  Each document is still computed from its
+// own state and chunked from its own first token ("5.1.1 · TTT layers 与 fast
+// weights", section 1.2, packed documents: the state resets at every document
+// boundary), exactly as one launch per document computes it.
+//
+// Units u = (rank, head), documents ranked longest first (ties by index), go
+// to workgroup lanes: u = x + 8 (v + k V), k = 0, 1, ..., where x is the
+// workgroup id mod 8 (its XCD) and the NRB row blocks of lane (x, v) are NRB
+// workgroups of that XCD, so the row blocks of a unit share one L2.  Longest
+// first and dealt round-robin, every workgroup gets a similar mix of lengths.
+// ---------------------------------------------------------------------------
+// A walk position: unit k of the workgroup's table, the first token of its
+// current chunk in the [H, T] rows, the tokens left from there, the chunk's
+// checkpoint slot and the unit's state slot.  Past the last unit rem = 0.
+struct Cursor {
+    int k, tok, rem, ck, bh;
+};
+
+// s_waitcnt immediate for vmcnt(0) alone (expcnt 7, lgkmcnt 15 left open).
+constexpr int kWaitVm0 = 0x0F70;
+// Minimum and maximum over a 64-wide wave (every lane gets a value; the
+// result is exact in lane 63), with the row-shift / row-broadcast DPP steps
+// of the gate scan.
+__device__ __forceinline__ unsigned wave_min_u32(unsigned x) {
+    auto step = [&](auto ctrl, auto rmask) {
+        const unsigned y = static_cast<unsigned>(__builtin_amdgcn_update_dpp(
+            static_cast<int>(0xffffffffu), static_cast<int>(x), decltype(ctrl)::value, decltype(rmask)::value, 0xf, false));
+        x = min(x, y);
+    };
+    step(std::integral_constant<int, kRowShr1>{}, std::integral_constant<int, 0xf>{});
+    step(std::integral_constant<int, kRowShr2>{}, std::integral_constant<int, 0xf>{});
+    step(std::integral_constant<int, kRowShr4>{}, std::integral_constant<int, 0xf>{});
+    step(std::integral_constant<int, kRowShr8>{}, std::integral_constant<int, 0xf>{});
+    step(std::integral_constant<int, kRowBcast15>{}, std::integral_constant<int, 0xa>{});
+    step(std::integral_constant<int, kRowBcast31>{}, std::integral_constant<int, 0xc>{});
+    return static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+template <typename Sm>
+__device__ __forceinline__ void cursor_at(Cursor& q, const Sm& sm, int k, int nu) {
+    q.k = k;
+    if (k < nu) {
+        const auto u = sm.units[k];
+        q.tok = __builtin_amdgcn_readfirstlane(u.tok0);
+        q.rem = __builtin_amdgcn_readfirstlane(u.len);
+        q.ck = __builtin_amdgcn_readfirstlane(u.ck0);
+        q.bh = __builtin_amdgcn_readfirstlane(u.bh);
+    } else {
+        q.tok = 0;
+        q.rem = 0;
+        q.ck = 0;
+        q.bh = 0;
+    }
+}
+
+// Next chunk: within the unit, or the next unit's first.
+template <typename Sm>
+__device__ __forceinline__ void cursor_next(Cursor& q, const Sm& sm, int nu, int b) {
+    if (q.rem > b) {
+        q.tok += b;
+        q.rem -= b;
+        q.ck += 1;
+    } else {
+        cursor_at(q, sm, q.k + 1, nu);
+    }
+}
+
+// The workgroup's table of non-empty units and its chunk count.  The
+// documents' offsets, lengths, chunk prefixes and ranks live in the second
+// chunk buffer while the table is built (N <= NMAX_DOCS); it is cleared again
+// before the pipeline starts.  The rank of document i counts the documents
+// before it in the order (longer, or as long with a smaller index), so the
+// ranks are a permutation.  Empty documents get their final state (the
+// initial one) here and take no place in the table.
+template <typename T, int D, int NS, int CS, int NP>
+__device__ __forceinline__ int packed_schedule(const Params& p, typename Kernel<T, D, NS, CS, NP>::S& sm, int x8,
+                                               int v, int V, int row_wg, int& nu) {
+    using Gm = Geo<T, D, NS, CS, NP>;
+    constexpr int NTH = kWave * Gm::NWAVE;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+    const int N = p.BH / p.H, Tl = p.T, b = p.b, H = p.H;
+    int* tlen = reinterpret_cast<int*>(&sm.buf[1]);
+    int* tt0 = tlen + N;
+    int* tpre = tt0 + N;
+    int* tperm = tpre + N;
+    int* tempty = tperm + N;   // state slots of the empty units (KMAX at most)
+    for (int i = tid; i < N; i += NTH) {
+        const int a = min(max(p.cu[i], 0), Tl);
+        tt0[i] = a;
+        tlen[i] = min(max(p.cu[i + 1], a), Tl) - a;
+    }
+    __syncthreads();
+    if (w == 0 && p.ckpt) {
+        // Checkpoint slots: chunks of the documents before each one, in document order.
+        int carry = 0;
+        for (int base = 0; base < N; base += kWave) {
+            const int i = base + lane;
+            const int cnt = i < N ? (tlen[i] + b - 1) / b : 0;
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int y = __shfl_up(incl, o, kWave);
+                if (lane >= o) incl += y;
+            }
+            if (i < N) tpre[i] = carry + incl - cnt;
+            carry += __shfl(incl, kWave - 1, kWave);
+        }
+    }
+    for (int i = tid; i < N; i += NTH) {
+        const int li = tlen[i];
+        int r = 0;
+        for (int j = 0; j < N; ++j) {
+            const int lj = tlen[j];
+            r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+        tperm[r] = i;
+    }
+    __syncthreads();
+    // Wave 0 builds this workgroup's table.  Workgroup lanes (one lane = the
+    // NRB row-block workgroups of one XCD slot, me = x8 + 8 v of G2 = 8 V)
+    // take units u = (rank, head) in rank order, longest processing time
+    // first in two steps:
+    // - head: when the lengths are heavy-tailed (the longest unit at least a
+    //   quarter of a lane's average), the units of at least 1/16 of that
+    //   average go one by one to the least-loaded lane (ties by lane), kept
+    //   as one load per wave lane and found by a wave-wide minimum;
+    // - rest: the lanes still below the average take the remaining units in
+    //   boustrophedon order (round q deals one unit to each open lane, in
+    //   lane order for even q and in reverse for odd q), which a lane
+    //   enumerates alone.  Without a head every lane is open.
+    // Empty units take no place in the walk; their owner copies the states.
+    int empties = 0;
+    if (w == 0) {
+        const int me = x8 + 8 * v, G2 = 8 * V, U = p.BH;
+        auto unit_len = [&](int r, int h, int& tok0, int& ck0, int& bh) {
+            const int s = tperm[r];
+            int len = tlen[s];
+            ck0 = 0;
+            if (p.ckpt) {
+                // Overlapping documents (offsets not non-decreasing) are cut at the head's last slot.
+                const int pre = tpre[s];
+                len = min(len, max(p.tcmax - pre, 0) * b);
+                ck0 = h * p.tcmax + pre;
+            }
+            tok0 = h * Tl + tt0[s];
+            bh = s * H + h;
+            return len;
+        };
+        auto chunks_of_rank = [&](int r) {
+            int t0_, c0_, bh_;
+            return (unit_len(r, 0, t0_, c0_, bh_) + b - 1) / b;
+        };
+        // Total chunks over all units (the heads of a rank share its length).
+        long long tot = 0;
+        for (int base = 0; base < N; base += kWave) {
+            int c = base + lane < N ? chunks_of_rank(base + lane) : 0;
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
+            tot += c;
+        }
+        tot *= H;
+        int kept = 0, J = 0;
+        int E = 0;            // units in the head
+        int ld = 0, cnt = 0;  // this wave lane's workgroup lane: chunks and units from the head
+        const bool skew = G2 <= kWave && N > 0 && 4LL * chunks_of_rank(0) * G2 >= tot && (tot << 6) < 0x7fffffffLL;
+        if (skew) {
+            for (int r = 0; r < N; ++r) {
+                const int c = chunks_of_rank(r);
+                if (16LL * c * G2 < tot) break;
+                for (int h = 0; h < H; ++h) {
+                    // key = load * 64 + lane (lanes >= G2 never win)
+                    const unsigned key = lane < G2 ? static_cast<unsigned>(ld) * kWave + lane : 0xffffffffu;
+                    const int win = static_cast<int>(wave_min_u32(key) & (kWave - 1));
+                    if (lane == win) {
+                        ld += c;
+                        cnt += 1;
+                    }
+                    if (win == me) {
+                        int tok0, ck0, bh;
+                        const int len = unit_len(r, h, tok0, ck0, bh);
+                        if (lane == 0 && kept < Gm::KMAX) sm.units[kept] = {tok0, len, ck0, bh};
+                        ++kept;
+                        J += c;
+                    }
+                }
+                E += H;
+            }
+        }
+        // Open lanes: below the average load (tot / G2 chunks).
+        // (When the head holds every chunk and leaves no lane below, all lanes stay open for the empty units.)
+        const unsigned long long below_avg = __ballot(lane < G2 && static_cast<long long>(ld) * G2 < tot);
+        const unsigned long long open = below_avg ? below_avg : __ballot(lane < G2);
+        const int nopen = __popcll(open);
+        const bool me_open = (open >> me) & 1ull;
+        const int myidx = __popcll(open & ((1ull << me) - 1ull));
+        const int rest = U - E;
+        const int rounds = nopen > 0 ? (rest + nopen - 1) / nopen : 0;
+        // Every lane's table must fit: the head counts are known per lane, the rest at most `rounds`.
+        const int maxhead = __builtin_amdgcn_readfirstlane(wave_max_i32(lane < G2 ? cnt : 0));
+        if (maxhead + rounds <= Gm::KMAX && me_open) {
+            for (int base = 0; base < rounds; base += kWave) {
+                const int q = base + lane;
+                const int u = E + q * nopen + ((q & 1) ? nopen - 1 - myidx : myidx);
+                int tok0 = 0, ck0 = 0, bh = 0, len = 0;
+                const bool live = q < rounds && u < U;
+                if (live) len = unit_len(u / H, u % H, tok0, ck0, bh);
+                const unsigned long long full = __ballot(live && len > 0);
+                const unsigned long long none = __ballot(live && len == 0);
+                const unsigned long long below = (1ull << lane) - 1ull;
+                if (live && len > 0) sm.units[kept + __popcll(full & below)] = {tok0, len, ck0, bh};
+                if (live && len == 0) tempty[empties + __popcll(none & below)] = bh;
+                kept += __popcll(full);
+                empties += __popcll(none);
+                int c = len > 0 ? (len + b - 1) / b : 0;
+#pragma unroll
+                for (int o = kWave / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
+                J += c;
+            }
+        } else if (maxhead + rounds > Gm::KMAX) {
+            // Some lane's table would overflow: plain boustrophedon order over all lanes
+            // (at most ceil(U / G2) units each, which the launch checked).
+            kept = 0;
+            J = 0;
+            const int rr = (U + G2 - 1) / G2;
+            for (int base = 0; base < rr; base += kWave) {
+                const int q = base + lane;
+                const int u = q * G2 + ((q & 1) ? G2 - 1 - me : me);
+                int tok0 = 0, ck0 = 0, bh = 0, len = 0;
+                const bool live = q < rr && u < U;
+                if (live) len = unit_len(u / H, u % H, tok0, ck0, bh);
+                const unsigned long long full = __ballot(live && len > 0);
+                const unsigned long long none = __ballot(live && len == 0);
+                const unsigned long long below = (1ull << lane) - 1ull;
+                if (live && len > 0) sm.units[kept + __popcll(full & below)] = {tok0, len, ck0, bh};
+                if (live && len == 0) tempty[empties + __popcll(none & below)] = bh;
+                kept += __popcll(full);
+                empties += __popcll(none);
+                int c = len > 0 ? (len + b - 1) / b : 0;
+#pragma unroll
+                for (int o = kWave / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
+                J += c;
+            }
+        }
+        if (lane == 0) {
+            sm.nitems = J;
+            sm.nunits = kept;
+            sm.nempty = empties;
+        }
+    }
+    __syncthreads();
+    empties = sm.nempty;
+    // The final state of an empty document is its initial state (rows of this row block).
+    if (empties > 0 && (p.MT || p.ST)) {
+        constexpr int Q = D / 4;   // float4 per row
+        for (int e = 0; e < empties; ++e) {
+            const size_t base = static_cast<size_t>(tempty[e]) * D * D + static_cast<size_t>(row_wg) * D;
+            for (int i = tid; i < Gm::RB * Q; i += NTH) {
+                const size_t off = base + static_cast<size_t>(i / Q) * D + 4 * (i % Q);
+                const f32x4 zero{0.f, 0.f, 0.f, 0.f};
+                if (p.MT) *reinterpret_cast<f32x4*>(p.MT + off) = p.M0 ? *reinterpret_cast<const f32x4*>(p.M0 + off) : zero;
+                if (p.ST) *reinterpret_cast<f32x4*>(p.ST + off) = p.S0 ? *reinterpret_cast<const f32x4*>(p.S0 + off) : zero;
+            }
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < 4 * N + Gm::KMAX; i += NTH) tlen[i] = 0;
+    __syncthreads();
+    nu = __builtin_amdgcn_readfirstlane(sm.nunits);
+    return __builtin_amdgcn_readfirstlane(sm.nitems);
+}
+
+// One producer wave's walk over the workgroup's chunks (role PW): the chunk
+// pipeline of producer_loop_impl with chunk c of a sequence replaced by item j
+// of the stream.  The loads run three items ahead through a cursor; the
+// lengths of the four newest items stay in one register (8 bits each).
+template <typename T, int D, int NS, int CS, int NP, int PW>
+__device__ __forceinline__ void producer_packed_impl(const Params& p, typename Kernel<T, D, NS, CS, NP>::S& sm,
+                                                     int row_wg, int nu, int J, int lane) {
+    using Gm = Geo<T, D, NS, CS, NP>;
+    using K = Kernel<T, D, NS, CS, NP>;
+    using G = typename Gm::G;
+    static_assert(Gm::NBUF == 2, "pipelined instances only");
+    const int lr = lane & 15, lg = lane >> 4;
+    __builtin_amdgcn_s_setprio(PW < 2 ? 3 : 1);
+    const int b = p.b;
+    const G* __restrict__ gq = static_cast<const G*>(p.q);
+    const G* __restrict__ gk = static_cast<const G*>(p.k);
+    const G* __restrict__ gv = static_cast<const G*>(p.v);
+    Cursor ci;
+    cursor_at(ci, sm, 0, nu);
+    uint32_t nring = 0;
+    int ji = 0;
+    // Items past the last one have n = 0: their loads touch no memory.
+    auto issue = [&](typename K::Prefetch& pf) {
+        K::template issue<PW>(pf, p, gq, gk, gv, static_cast<size_t>(ci.tok), ci.rem, row_wg, 0, lane);
+        const uint32_t n = static_cast<uint32_t>(max(0, min(b, ci.rem)));
+        const int sh = 8 * (ji & 3);
+        nring = (nring & ~(0xffu << sh)) | (n << sh);
+        ++ji;
+        cursor_next(ci, sm, nu, b);
+    };
+    auto nof = [&](int j) { return static_cast<int>((nring >> (8 * (j & 3))) & 0xffu); };
+    auto gates = [&](int j, const typename K::Prefetch& pf) {
+        if constexpr (PW == 0) K::gate_scan(pf, sm.gs[j & 1], sm.rg[j & 3], nof(j), lane);
+        if constexpr (PW == 1) K::gate_diag(pf, sm.gs[j & 1], nof(j), lane);
+    };
+    auto build = [&](int j, typename K::Buf& B) {
+        if constexpr (Gm::USE_GAM) {
+            if constexpr (PW == 0) K::template gamma_build<0>(sm.gs[j & 1], sm.gam, lane);
+            if constexpr (PW == 1) K::template gamma_build<1>(sm.gs[j & 1], sm.gam, lane);
+            if constexpr (PW == K::kWrowWave) K::wrow(sm.gs[j & 1], B, nof(j), lane);
+        }
+    };
+    auto finish = [&](int j, typename K::Buf& B) {
+        K::template ptiles<PW>(sm.gs[j & 1], sm.gam, B, lr, lg);
+        if constexpr (!Gm::USE_GAM && PW == K::kWrowWave) K::wrow(sm.gs[j & 1], B, nof(j), lane);
+    };
+    typename K::Prefetch pf0, pf1;
+    issue(pf0);
+    issue(pf1);
+    if (J > 0) {
+        K::template stage<PW>(pf0, sm.buf[0], lane);
+        gates(0, pf0);
+    }
+    issue(pf0);
+    __syncthreads();
+    if (J > 0) build(0, sm.buf[0]);
+    if (J > 1) gates(1, pf1);
+    __syncthreads();
+    if (J > 0) finish(0, sm.buf[0]);
+    __syncthreads();
+    auto step = [&](int j, typename K::Prefetch& cur, const typename K::Prefetch& nxt, typename K::Buf& B) {
+        if (j + 1 < J) {
+            K::template stage<PW>(cur, B, lane);
+            build(j + 1, B);
+        }
+        issue(cur);
+        __syncthreads();
+        if (j + 1 < J) finish(j + 1, B);
+        if (j + 2 < J) gates(j + 2, nxt);
+        __syncthreads();
+    };
+    for (int j = 0; j < J; j += 2) {
+        step(j, pf1, pf0, sm.buf[1]);
+        if (j + 1 < J) step(j + 1, pf0, pf1, sm.buf[0]);
+    }
+}
+
+template <typename T, int D, int NS, int CS, int NP>
+__global__ __launch_bounds__(kWave * (NS * CS + 8)) void linear_memory_fwd_packed(const Params p) {
+    using Gm = Geo<T, D, NS, CS, NP>;
+    using K = Kernel<T, D, NS, CS, NP>;
+    using O = Op<T>;
+    using F = typename O::frag;
+    static_assert(Gm::PERSIST, "persistent walk: pipelined instances only");
+    constexpr int NSW = Gm::NSW;
+
+    __shared__ __attribute__((aligned(16))) typename K::S sm;
+
+    const int tid = threadIdx.x;
+    const int w = tid / kWave;
+    const int lane = tid % kWave;
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+    const int V = gridDim.x / (8 * Gm::NRB);
+    const int x8 = blockIdx.x % 8, m = blockIdx.x / 8;
+    const int rb = m % Gm::NRB, v = m / Gm::NRB;
+    const int b = p.b;
+    const int row_wg = rb * Gm::RB;
+
+    {
+        uint32_t* words = reinterpret_cast<uint32_t*>(&sm);
+        for (int i = tid; i < static_cast<int>(sizeof(sm) / 4); i += kWave * Gm::NWAVE) words[i] = 0u;
+    }
+    __syncthreads();
+    int nu = 0;
+    const int J = packed_schedule<T, D, NS, CS, NP>(p, sm, x8, v, V, row_wg, nu);
+
+    if (w < NSW) {
+        // ===================== state wave =====================
+        typename K::StateCtx x;
+        __builtin_amdgcn_s_setprio(2);
+        x.rho = w / CS;
+        x.chi = w % CS;
+        x.r0 = 16 * x.rho;
+        x.lr = lr;
+        x.lg = lg;
+        const int row = row_wg + x.r0;
+        f32x4 Macc[Gm::NCW], Sacc[Gm::NCW];
+        Cursor cs;
+        cursor_at(cs, sm, 0, nu);
+        auto state_off = [&]() { return static_cast<size_t>(cs.bh) * D * D + static_cast<size_t>(row + lr) * D; };
+        // The initial state of unit cs (zeros past the last unit).  The loads
+        // are waited for here: a wait left for the fragments after the switch
+        // would sit on every chunk's path and also wait for its z stores (the
+        // vector-memory counter counts stores too).
+        auto load_state = [&]() {
+            const f32x4 zero{0.f, 0.f, 0.f, 0.f};
+            if (cs.k < nu && (p.M0 || p.S0)) {
+                const size_t so = state_off();
+#pragma unroll
+                for (int cw = 0; cw < Gm::NCW; ++cw) {
+                    const int col = O::tmap(x.chi * Gm::NCW + cw, 4 * lg);
+                    const bool ok = col < D;
+                    Macc[cw] = (p.M0 && ok) ? *reinterpret_cast<const f32x4*>(p.M0 + so + col) : zero;
+                    Sacc[cw] = (p.S0 && ok) ? *reinterpret_cast<const f32x4*>(p.S0 + so + col) : zero;
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            } else {
+#pragma unroll
+                for (int cw = 0; cw < Gm::NCW; ++cw) {
+                    Macc[cw] = zero;
+                    Sacc[cw] = zero;
+                }
+            }
+        };
+        auto store_state = [&]() {
+            const size_t so = state_off();
+#pragma unroll
+            for (int cw = 0; cw < Gm::NCW; ++cw) {
+                const int col = O::tmap(x.chi * Gm::NCW + cw, 4 * lg);
+                if (col < D) {
+                    if (p.MT) *reinterpret_cast<f32x4*>(p.MT + so + col) = Macc[cw];
+                    if (p.ST) *reinterpret_cast<f32x4*>(p.ST + so + col) = Sacc[cw];
+                }
+            }
+        };
+        load_state();
+        F MB[Gm::NKCW], SB[Gm::NKCW];
+        f32x4 E[Gm::NTW], Zp[Gm::NTW];
+        K::own_frags(x, sm, Macc, Sacc, MB, SB);
+        const uint32_t zcol = row + 4 * lg;
+        const bool zb = p.z_bf16 != 0;
+        const uint32_t zsz = zb ? 2u : 4u;
+        __syncthreads();   // item 0 staged
+        __syncthreads();   // item 0 decay matrix
+        __syncthreads();   // item 0 P tiles
+        const typename K::Lanes a = K::lanes(x, sm);
+        const uint32_t zoff = opaque(O::tmap(x.chi * Gm::NTW, lr) * D + zcol);
+        auto item = [&](int j, auto bi) {
+            constexpr int BI = decltype(bi)::value;
+            const auto rz = make_rsrc(static_cast<char*>(p.z) + static_cast<size_t>(cs.tok) * D * zsz,
+                                      static_cast<uint32_t>(min(b, cs.rem)) * D * zsz);
+            if (p.ckpt) {
+                T* base = static_cast<T*>(p.ckpt) + static_cast<size_t>(cs.ck) * (2 * D * D) +
+                          static_cast<size_t>(row + lr) * D;
+#pragma unroll
+                for (int cw = 0; cw < Gm::NCW; ++cw) {
+                    const int col = O::tmap(x.chi * Gm::NCW + cw, 4 * lg);
+                    if (col < D) {
+                        st4<T>(base + col, Macc[cw]);
+                        st4<T>(base + D * D + col, Sacc[cw]);
+                    }
+                }
+            }
+            const uint32_t gs = a.g + static_cast<uint32_t>(j & 3) * K::kGateB;
+            const uint32_t gsc = lds_addr(&sm.rg[j & 3].scal[0]);
+            K::template phaseA2<BI>(a, gs, gsc, MB, SB, E, Zp, Macc, Sacc);
+            __syncthreads();
+            K::template phaseB2<BI, false>(a, Macc, Sacc, MB, SB, Zp, rz, zoff, zb);
+            if (cs.rem > b) {
+                cs.tok += b;
+                cs.rem -= b;
+                cs.ck += 1;
+            } else {
+                // Last chunk of the document: its final state out, the next one's initial state in.
+                store_state();
+                cursor_at(cs, sm, cs.k + 1, nu);
+                load_state();
+            }
+            K::frags2(a, Macc, Sacc, MB, SB);
+            __syncthreads();
+        };
+        for (int j = 0; j < J; j += 2) {
+            item(j, std::integral_constant<int, 0>{});
+            if (j + 1 < J) item(j + 1, std::integral_constant<int, 1>{});
+        }
+    } else {
+        // ===================== producer wave =====================
+        switch (w - NSW) {
+            case 0: producer_packed_impl<T, D, NS, CS, NP, 0>(p, sm, row_wg, nu, J, lane); break;
+            case 1: producer_packed_impl<T, D, NS, CS, NP, 1>(p, sm, row_wg, nu, J, lane); break;
+            case 2: producer_packed_impl<T, D, NS, CS, NP, 2>(p, sm, row_wg, nu, J, lane); break;
+            case 3: producer_packed_impl<T, D, NS, CS, NP, 3>(p, sm, row_wg, nu, J, lane); break;
+            case 4: producer_packed_impl<T, D, NS, CS, NP, 4>(p, sm, row_wg, nu, J, lane); break;
+            case 5: producer_packed_impl<T, D, NS, CS, NP, 5>(p, sm, row_wg, nu, J, lane); break;
+            case 6: producer_packed_impl<T, D, NS, CS, NP, 6>(p, sm, row_wg, nu, J, lane); break;
+            default: producer_packed_impl<T, D, NS, CS, NP, 7>(p, sm, row_wg, nu, J, lane); break;
         }
     }
 }
@@ -1351,13 +1889,61 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
 // ---------------------------------------------------------------------------
 // Host side: validation, instance selection, launch.
 // ---------------------------------------------------------------------------
+// Workgroup lanes V of the persistent packed walk on the current device:
+// resident workgroups (CUs x occupancy) / (8 XCD lanes x NRB row blocks),
+// queried once per device and instance.
+template <typename T, int D, int NS, int CS, int NP>
+int packed_lanes() {
+    using Gm = Geo<T, D, NS, CS, NP>;
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::atomic<int>& slot = cached[dev & 63];
+    int v = slot.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, linear_memory_fwd_packed<T, D, NS, CS, NP>,
+                                                     kWave * Gm::NWAVE, 0) != hipSuccess || per_cu <= 0)
+        per_cu = 1;
+    v = cmax(1, cus * per_cu / (8 * Gm::NRB));
+    slot.store(v, std::memory_order_relaxed);
+    return v;
+}
+
 template <typename T, int D, int NS, int CS, int NP>
 hipError_t launch(const Params& p, hipStream_t stream) {
     using Gm = Geo<T, D, NS, CS, NP>;
+    if constexpr (Gm::PERSIST) {
+        if (p.cu) {
+            // Packed documents: persistent workgroups when the documents fit the
+            // in-LDS ranking and every workgroup's units fit its table.
+            const int N = p.BH / p.H;
+            const int V = cmax(1, cmin(packed_lanes<T, D, NS, CS, NP>(), (p.BH + 7) / 8));
+            const long long kmax = (static_cast<long long>(p.BH) + 8LL * V - 1) / (8LL * V);
+            if (N <= Gm::NMAX_DOCS && kmax <= Gm::KMAX) {
+                hipLaunchKernelGGL((linear_memory_fwd_packed<T, D, NS, CS, NP>), dim3(8 * Gm::NRB * V),
+                                   dim3(kWave * Gm::NWAVE), 0, stream, p);
+                return hipGetLastError();
+            }
+        }
+    }
+    // One workgroup per (sequence or document, row block).  Packed documents
+    // above the in-wave ranking's limit take their order from a pass before
+    // the launch.
+    Params q = p;
+    int* perm = nullptr;
+    if (p.cu && p.T > 0) {
+        const hipError_t e = make_doc_order(p.cu, p.BH / p.H, p.T, stream, &perm);
+        if (e != hipSuccess) return e;
+    }
+    q.perm = perm;
     const long long nwg = static_cast<long long>(p.BH) * Gm::NRB;
     hipLaunchKernelGGL((linear_memory_fwd<T, D, NS, CS, NP>), dim3(static_cast<unsigned>(nwg)),
-                       dim3(kWave * Gm::NWAVE), 0, stream, p);
-    return hipGetLastError();
+                       dim3(kWave * Gm::NWAVE), 0, stream, q);
+    const hipError_t err = hipGetLastError();
+    if (perm) (void)hipFreeAsync(perm, stream);
+    return err;
 }
 
 template <typename T, int D, int NS>
@@ -1522,12 +2108,7 @@ int forward_varlen_impl(const void* q, const void* k, const void* v, const float
              static_cast<int>(tcmax), 0};
     // More documents than the in-kernel ranking covers: a pass before the
     // launch writes their longest-first order to a stream-ordered table.
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    int* perm = nullptr;
-    if (Tlen > 0 && make_doc_order(cu, N, Tlen, s, &perm) != hipSuccess) return TTT_ERR_HIP;
-    p.perm = perm;
-    const hipError_t err = dispatch<T>(p, d, s);
-    if (perm) (void)hipFreeAsync(perm, s);
+    const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

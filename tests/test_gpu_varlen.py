@@ -84,6 +84,15 @@ CASES = [
     ("hundred-docs", 3, 1, [int(x) for x in np.random.default_rng(6).integers(0, 41, 100)], 16, 32),
     ("many-docs", 3, 1, [int(x) for x in np.random.default_rng(5).integers(0, 41, 150)], 16, 32),
     ("600-docs", 3, 2, [int(x) for x in np.random.default_rng(7).integers(0, 41, 600)], 16, 32),
+    # bf16 at d >= 64 runs persistent workgroups that walk a table of documents:
+    # 600 documents dealt in boustrophedon order; one 8000-token document among
+    # 400 short ones (longest-processing-time head, then the lanes below the
+    # average); 700 documents, past the in-LDS ranking's limit at d = 64, b = 16
+    # (one workgroup per document, ordered by the pass before the launch).
+    ("600-docs-d64", 3, 2, [int(x) for x in np.random.default_rng(8).integers(0, 41, 600)], 16, 64),
+    ("skewed-d128", 3, 4, [int(x) for x in np.random.default_rng(9).integers(20, 61, 150)] + [8000]
+     + [int(x) for x in np.random.default_rng(10).integers(0, 61, 250)], 64, None),
+    ("700-docs-d64", 3, 1, [int(x) for x in np.random.default_rng(11).integers(0, 11, 700)], 16, 64),
 ]
 
 

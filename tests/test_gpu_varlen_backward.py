@@ -92,6 +92,9 @@ CASES = [
     ("hundred-docs", 3, 1, [int(x) for x in np.random.default_rng(6).integers(0, 41, 100)], 16, 32),
     ("many-docs", 3, 1, [int(x) for x in np.random.default_rng(5).integers(0, 41, 150)], 16, 32),
     ("600-docs", 3, 1, [int(x) for x in np.random.default_rng(7).integers(0, 41, 600)], 16, 32),
+    # bf16 at d = 64: the forward with checkpoints runs the persistent document walk
+    # (checkpoint slots from the in-kernel chunk prefix, 300 documents, empty ones among them).
+    ("300-docs-d64", 3, 1, [int(x) for x in np.random.default_rng(12).integers(0, 41, 300)], 16, 64),
 ]
 
 
