@@ -1386,8 +1386,10 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                 st4<T>(sm.ec + t * LQ + f0 + 4 * lg, acc - vv);
             }
         }
+        // The first state in flight is M0, whose rows the residual pass above
+        // has just brought into the L2: its column slices are read from there.
         R2 raw[NRAW];
-        colload(Sc, 16 * fw * FPW, raw);
+        colload(Mc, 16 * fw * FPW, raw);
         __syncthreads();   // (1)
         tiles();
         __syncthreads();   // (1b)
@@ -1428,48 +1430,9 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
         for (int ft = 0; ft < FPW; ++ft) {
             const int f0 = 16 * (fw * FPW + ft);
             F fs[NKD], fo[NKD], fm[NKD];
-            colcvt(raw, fs);                       // S0
-            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
-            colload(dSe, f0, raw);
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int t = 16 * tt + lr;
-                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < NKD; ++kk) Y = O::mma(Y, fs[kk], zfrag(sm.dz, p.dz, 1.f, t, kk * KG));
-                keep(pc, ft, tt, 1, rdot(ld4<T>(sm.q + t * LQ + f0 + 4 * lg), Y));
-                dQ[ft][tt] = sm.c[t] * Y;
-            }
-            colcvt(raw, fo);                       // dS'
-            d3 += fdot(fo, fs);
+            colcvt(raw, fm);                       // M0
             __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
             colload(dMe, f0, raw);
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int t = 16 * tt + lr;
-                f32x4 W = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < NKD; ++kk) W = O::mma(W, fo[kk], R::rm(sm.ec, LQ, t, kk * KG, lg));
-                keep(pws, ft, tt, 3, -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), W));
-                dK[ft][tt] = -sm.ws[t] * W;
-            }
-            colcvt(raw, fo);                       // dM'
-            d2 += fdot(fo, fs);
-            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
-            colload(Mc, f0, raw);
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int t = 16 * tt + lr;
-                f32x4 U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < NKD; ++kk) U = O::mma(U, fo[kk], R::rm(sm.ec, LQ, t, kk * KG, lg));
-                keep(pwm, ft, tt, 2, -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), U));
-                dK[ft][tt] -= sm.wm[t] * U;
-            }
-            colcvt(raw, fm);                       // M0
-            d1 += fdot(fo, fm);
-            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
-            if (ft + 1 < FPW) colload(Sc, f0 + 16, raw);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 const int t = 16 * tt + lr;
@@ -1480,8 +1443,47 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
                     H = O::mma(H, fm[kk], zfrag(sm.de, p.dv, -1.f, t, kk * KG));
                 }
                 keep(pa, ft, tt, 0, rdot(ld4<T>(sm.q + t * LQ + f0 + 4 * lg), X));
-                dQ[ft][tt] += sm.A[t] * X;
-                dK[ft][tt] += H;
+                dQ[ft][tt] = sm.A[t] * X;
+                dK[ft][tt] = H;
+            }
+            colcvt(raw, fo);                       // dM'
+            d1 += fdot(fo, fm);
+            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
+            colload(Sc, f0, raw);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = 16 * tt + lr;
+                f32x4 U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) U = O::mma(U, fo[kk], R::rm(sm.ec, LQ, t, kk * KG, lg));
+                keep(pwm, ft, tt, 2, -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), U));
+                dK[ft][tt] -= sm.wm[t] * U;
+            }
+            colcvt(raw, fs);                       // S0
+            d2 += fdot(fo, fs);
+            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
+            colload(dSe, f0, raw);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = 16 * tt + lr;
+                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) Y = O::mma(Y, fs[kk], zfrag(sm.dz, p.dz, 1.f, t, kk * KG));
+                keep(pc, ft, tt, 1, rdot(ld4<T>(sm.q + t * LQ + f0 + 4 * lg), Y));
+                dQ[ft][tt] += sm.c[t] * Y;
+            }
+            colcvt(raw, fo);                       // dS'
+            d3 += fdot(fo, fs);
+            __builtin_amdgcn_sched_barrier(0);   // the next state's loads stay behind this point
+            if (ft + 1 < FPW) colload(Mc, f0 + 16, raw);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = 16 * tt + lr;
+                f32x4 W = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk) W = O::mma(W, fo[kk], R::rm(sm.ec, LQ, t, kk * KG, lg));
+                keep(pws, ft, tt, 3, -rdot(ld4<T>(sm.k + t * LQ + f0 + 4 * lg), W));
+                dK[ft][tt] -= sm.ws[t] * W;
             }
         }
         d1 = wave_sum(d1);
