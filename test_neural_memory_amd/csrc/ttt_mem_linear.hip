@@ -293,11 +293,8 @@ struct Smem {
     // order (first token in the [H, T] rows, length, checkpoint slot of its
     // first chunk, state slot s * H + h), their count, their chunks in all,
     // and the number of empty units.
-    struct Unit {
-        int tok0, len, ck0, bh;
-    };
-    Unit units[Gm::KMAX > 0 ? Gm::KMAX : 1];
-    int nitems, nunits, nempty;
+    WalkUnit units[Gm::KMAX > 0 ? Gm::KMAX : 1];
+    int nitems, nunits, nempty;   // build_walk_table's counts, in this order
 };
 
 template <typename T, int D, int NS, int CS, int NP>
@@ -1204,31 +1201,6 @@ struct Cursor {
     int k, tok, rem, ck, bh;
 };
 
-// s_waitcnt immediate for vmcnt(0) alone (expcnt 7, lgkmcnt 15 left open).
-constexpr int kWaitVm0 = 0x0F70;
-// Minimum and maximum over a 64-wide wave (every lane gets a value; the
-// result is exact in lane 63), with the row-shift / row-broadcast DPP steps
-// of the gate scan.
-__device__ __forceinline__ unsigned wave_min_u32(unsigned x) {
-    auto step = [&](auto ctrl, auto rmask) {
-        const unsigned y = static_cast<unsigned>(__builtin_amdgcn_update_dpp(
-            static_cast<int>(0xffffffffu), static_cast<int>(x), decltype(ctrl)::value, decltype(rmask)::value, 0xf, false));
-        x = min(x, y);
-    };
-    step(std::integral_constant<int, kRowShr1>{}, std::integral_constant<int, 0xf>{});
-    step(std::integral_constant<int, kRowShr2>{}, std::integral_constant<int, 0xf>{});
-    step(std::integral_constant<int, kRowShr4>{}, std::integral_constant<int, 0xf>{});
-    step(std::integral_constant<int, kRowShr8>{}, std::integral_constant<int, 0xf>{});
-    step(std::integral_constant<int, kRowBcast15>{}, std::integral_constant<int, 0xa>{});
-    step(std::integral_constant<int, kRowBcast31>{}, std::integral_constant<int, 0xc>{});
-    return static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
-}
-__device__ __forceinline__ int wave_max_i32(int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
-    return x;
-}
-
 template <typename Sm>
 __device__ __forceinline__ void cursor_at(Cursor& q, const Sm& sm, int k, int nu) {
     q.k = k;
@@ -1258,190 +1230,22 @@ __device__ __forceinline__ void cursor_next(Cursor& q, const Sm& sm, int nu, int
     }
 }
 
-// The workgroup's table of non-empty units and its chunk count.  The
-// documents' offsets, lengths, chunk prefixes and ranks live in the second
-// chunk buffer while the table is built (N <= NMAX_DOCS); it is cleared again
-// before the pipeline starts.  The rank of document i counts the documents
-// before it in the order (longer, or as long with a smaller index), so the
-// ranks are a permutation.  Empty documents get their final state (the
-// initial one) here and take no place in the table.
+// The workgroup's table of non-empty units (build_walk_table, with the second
+// chunk buffer as its scratch) and its chunk count.  Empty documents get their
+// final state (the initial one) here; the buffer is cleared again before the
+// pipeline starts.
 template <typename T, int D, int NS, int CS, int NP>
 __device__ __forceinline__ int packed_schedule(const Params& p, typename Kernel<T, D, NS, CS, NP>::S& sm, int x8,
                                                int v, int V, int row_wg, int& nu) {
     using Gm = Geo<T, D, NS, CS, NP>;
     constexpr int NTH = kWave * Gm::NWAVE;
-    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
-    const int N = p.BH / p.H, Tl = p.T, b = p.b, H = p.H;
-    int* tlen = reinterpret_cast<int*>(&sm.buf[1]);
-    int* tt0 = tlen + N;
-    int* tpre = tt0 + N;
-    int* tperm = tpre + N;
-    int* tempty = tperm + N;   // state slots of the empty units (KMAX at most)
-    for (int i = tid; i < N; i += NTH) {
-        const int a = min(max(p.cu[i], 0), Tl);
-        tt0[i] = a;
-        tlen[i] = min(max(p.cu[i + 1], a), Tl) - a;
-    }
-    __syncthreads();
-    if (w == 0 && p.ckpt) {
-        // Checkpoint slots: chunks of the documents before each one, in document order.
-        int carry = 0;
-        for (int base = 0; base < N; base += kWave) {
-            const int i = base + lane;
-            const int cnt = i < N ? (tlen[i] + b - 1) / b : 0;
-            int incl = cnt;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int y = __shfl_up(incl, o, kWave);
-                if (lane >= o) incl += y;
-            }
-            if (i < N) tpre[i] = carry + incl - cnt;
-            carry += __shfl(incl, kWave - 1, kWave);
-        }
-    }
-    for (int i = tid; i < N; i += NTH) {
-        const int li = tlen[i];
-        int r = 0;
-        for (int j = 0; j < N; ++j) {
-            const int lj = tlen[j];
-            r += (lj > li || (lj == li && j < i)) ? 1 : 0;
-        }
-        tperm[r] = i;
-    }
-    __syncthreads();
-    // Wave 0 builds this workgroup's table.  Workgroup lanes (one lane = the
-    // NRB row-block workgroups of one XCD slot, me = x8 + 8 v of G2 = 8 V)
-    // take units u = (rank, head) in rank order, longest processing time
-    // first in two steps:
-    // - head: when the lengths are heavy-tailed (the longest unit at least a
-    //   quarter of a lane's average), the units of at least 1/16 of that
-    //   average go one by one to the least-loaded lane (ties by lane), kept
-    //   as one load per wave lane and found by a wave-wide minimum;
-    // - rest: the lanes still below the average take the remaining units in
-    //   boustrophedon order (round q deals one unit to each open lane, in
-    //   lane order for even q and in reverse for odd q), which a lane
-    //   enumerates alone.  Without a head every lane is open.
-    // Empty units take no place in the walk; their owner copies the states.
-    int empties = 0;
-    if (w == 0) {
-        const int me = x8 + 8 * v, G2 = 8 * V, U = p.BH;
-        auto unit_len = [&](int r, int h, int& tok0, int& ck0, int& bh) {
-            const int s = tperm[r];
-            int len = tlen[s];
-            ck0 = 0;
-            if (p.ckpt) {
-                // Overlapping documents (offsets not non-decreasing) are cut at the head's last slot.
-                const int pre = tpre[s];
-                len = min(len, max(p.tcmax - pre, 0) * b);
-                ck0 = h * p.tcmax + pre;
-            }
-            tok0 = h * Tl + tt0[s];
-            bh = s * H + h;
-            return len;
-        };
-        auto chunks_of_rank = [&](int r) {
-            int t0_, c0_, bh_;
-            return (unit_len(r, 0, t0_, c0_, bh_) + b - 1) / b;
-        };
-        // Total chunks over all units (the heads of a rank share its length).
-        long long tot = 0;
-        for (int base = 0; base < N; base += kWave) {
-            int c = base + lane < N ? chunks_of_rank(base + lane) : 0;
-#pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
-            tot += c;
-        }
-        tot *= H;
-        int kept = 0, J = 0;
-        int E = 0;            // units in the head
-        int ld = 0, cnt = 0;  // this wave lane's workgroup lane: chunks and units from the head
-        const bool skew = G2 <= kWave && N > 0 && 4LL * chunks_of_rank(0) * G2 >= tot && (tot << 6) < 0x7fffffffLL;
-        if (skew) {
-            for (int r = 0; r < N; ++r) {
-                const int c = chunks_of_rank(r);
-                if (16LL * c * G2 < tot) break;
-                for (int h = 0; h < H; ++h) {
-                    // key = load * 64 + lane (lanes >= G2 never win)
-                    const unsigned key = lane < G2 ? static_cast<unsigned>(ld) * kWave + lane : 0xffffffffu;
-                    const int win = static_cast<int>(wave_min_u32(key) & (kWave - 1));
-                    if (lane == win) {
-                        ld += c;
-                        cnt += 1;
-                    }
-                    if (win == me) {
-                        int tok0, ck0, bh;
-                        const int len = unit_len(r, h, tok0, ck0, bh);
-                        if (lane == 0 && kept < Gm::KMAX) sm.units[kept] = {tok0, len, ck0, bh};
-                        ++kept;
-                        J += c;
-                    }
-                }
-                E += H;
-            }
-        }
-        // Open lanes: below the average load (tot / G2 chunks).
-        // (When the head holds every chunk and leaves no lane below, all lanes stay open for the empty units.)
-        const unsigned long long below_avg = __ballot(lane < G2 && static_cast<long long>(ld) * G2 < tot);
-        const unsigned long long open = below_avg ? below_avg : __ballot(lane < G2);
-        const int nopen = __popcll(open);
-        const bool me_open = (open >> me) & 1ull;
-        const int myidx = __popcll(open & ((1ull << me) - 1ull));
-        const int rest = U - E;
-        const int rounds = nopen > 0 ? (rest + nopen - 1) / nopen : 0;
-        // Every lane's table must fit: the head counts are known per lane, the rest at most `rounds`.
-        const int maxhead = __builtin_amdgcn_readfirstlane(wave_max_i32(lane < G2 ? cnt : 0));
-        if (maxhead + rounds <= Gm::KMAX && me_open) {
-            for (int base = 0; base < rounds; base += kWave) {
-                const int q = base + lane;
-                const int u = E + q * nopen + ((q & 1) ? nopen - 1 - myidx : myidx);
-                int tok0 = 0, ck0 = 0, bh = 0, len = 0;
-                const bool live = q < rounds && u < U;
-                if (live) len = unit_len(u / H, u % H, tok0, ck0, bh);
-                const unsigned long long full = __ballot(live && len > 0);
-                const unsigned long long none = __ballot(live && len == 0);
-                const unsigned long long below = (1ull << lane) - 1ull;
-                if (live && len > 0) sm.units[kept + __popcll(full & below)] = {tok0, len, ck0, bh};
-                if (live && len == 0) tempty[empties + __popcll(none & below)] = bh;
-                kept += __popcll(full);
-                empties += __popcll(none);
-                int c = len > 0 ? (len + b - 1) / b : 0;
-#pragma unroll
-                for (int o = kWave / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
-                J += c;
-            }
-        } else if (maxhead + rounds > Gm::KMAX) {
-            // Some lane's table would overflow: plain boustrophedon order over all lanes
-            // (at most ceil(U / G2) units each, which the launch checked).
-            kept = 0;
-            J = 0;
-            const int rr = (U + G2 - 1) / G2;
-            for (int base = 0; base < rr; base += kWave) {
-                const int q = base + lane;
-                const int u = q * G2 + ((q & 1) ? G2 - 1 - me : me);
-                int tok0 = 0, ck0 = 0, bh = 0, len = 0;
-                const bool live = q < rr && u < U;
-                if (live) len = unit_len(u / H, u % H, tok0, ck0, bh);
-                const unsigned long long full = __ballot(live && len > 0);
-                const unsigned long long none = __ballot(live && len == 0);
-                const unsigned long long below = (1ull << lane) - 1ull;
-                if (live && len > 0) sm.units[kept + __popcll(full & below)] = {tok0, len, ck0, bh};
-                if (live && len == 0) tempty[empties + __popcll(none & below)] = bh;
-                kept += __popcll(full);
-                empties += __popcll(none);
-                int c = len > 0 ? (len + b - 1) / b : 0;
-#pragma unroll
-                for (int o = kWave / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
-                J += c;
-            }
-        }
-        if (lane == 0) {
-            sm.nitems = J;
-            sm.nunits = kept;
-            sm.nempty = empties;
-        }
-    }
-    __syncthreads();
-    empties = sm.nempty;
+    const int tid = threadIdx.x;
+    const int N = p.BH / p.H;
+    int* temp = reinterpret_cast<int*>(&sm.buf[1]);
+    build_walk_table<NTH, Gm::KMAX>(p.cu, N, p.H, p.T, p.b, p.ckpt != nullptr, p.tcmax, temp,
+                                    sm.units, &sm.nitems, x8, v, V);
+    const int empties = sm.nempty;
+    const int* tempty = temp + 4 * N;
     // The final state of an empty document is its initial state (rows of this row block).
     if (empties > 0 && (p.MT || p.ST)) {
         constexpr int Q = D / 4;   // float4 per row
@@ -1456,7 +1260,7 @@ __device__ __forceinline__ int packed_schedule(const Params& p, typename Kernel<
         }
         __syncthreads();
     }
-    for (int i = tid; i < 4 * N + Gm::KMAX; i += NTH) tlen[i] = 0;
+    for (int i = tid; i < 4 * N + Gm::KMAX; i += NTH) temp[i] = 0;
     __syncthreads();
     nu = __builtin_amdgcn_readfirstlane(sm.nunits);
     return __builtin_amdgcn_readfirstlane(sm.nitems);

@@ -62,6 +62,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "ttt_mem.h"
@@ -126,6 +127,7 @@ __global__ __launch_bounds__(256) void cot_absmax(const float* __restrict__ dz, 
 }
 
 __host__ __device__ constexpr int bmax(int a, int b) { return a > b ? a : b; }
+__host__ __device__ constexpr int bmin(int a, int b) { return a < b ? a : b; }
 
 // Earlier LDS accesses of this wave have completed (same-wave hand-over of
 // LDS data between lanes).
@@ -371,13 +373,21 @@ struct CarryGeo {
     static constexpr int QSLOT = (2 * NP * LQ + NP * LZ) * (int)sizeof(T) + 3 * NP * 4;
     static constexpr int PSLOT = NP * LP * (int)sizeof(T) + 4 * NP * 4 + 16;
     static constexpr int LS = NP * LF * 4;
+    // Packed documents on persistent workgroups: a table of up to KMAX units
+    // (plus their cotangent scales) per workgroup.
+    static constexpr int KMAX = 128;
+    static constexpr int UNIT_BYTES = KMAX * (16 + 4) + 16;
     // Three staging slots (state waves, P builder and loader each on their
     // own chunk, one barrier per chunk) when they fit; else one slot and a
     // serial schedule.
-    static constexpr int NQ = (3 * QSLOT + 2 * PSLOT + LS + 1024 <= kLdsMax) ? 3 : 1;
+    static constexpr int NQ = (3 * QSLOT + 2 * PSLOT + LS + UNIT_BYTES + 1024 <= kLdsMax) ? 3 : 1;
+    // The persistent walk (three slots): documents it ranks in LDS, four ints
+    // each plus KMAX in the last staging slot, borrowed before the walk.
+    static constexpr bool PERSIST = NQ == 3;
+    static constexpr int NMAX_DOCS = bmin(2048, (QSLOT / 4 - KMAX) / 4);
     static constexpr int NPR = NQ == 3 ? 2 : 1;
     static constexpr int NWAVE = NS + 3;            // state waves, two loaders, one builder
-    static_assert(NQ * QSLOT + NPR * PSLOT + LS + 1024 <= kLdsMax, "LDS budget");
+    static_assert(NQ * QSLOT + NPR * PSLOT + LS + UNIT_BYTES + 1024 <= kLdsMax, "LDS budget");
     static_assert(D % RB == 0 && NP % KG == 0, "tiling");
 };
 
@@ -403,6 +413,11 @@ struct CarrySmem {
     QSlot qs[Gm::NQ];
     PSlot ps[Gm::NPR];
     alignas(16) float ls[NP * Gm::LF];     // L_ij = theta_j gamma_ij (builder only)
+    // Persistent walk over packed documents: the workgroup's units, their
+    // cotangent scales, and build_walk_table's counts (in this order).
+    WalkUnit units[Gm::KMAX];
+    float usc[Gm::KMAX];
+    int nitems, nunits, nempty;
 };
 
 template <typename T, int D, int NS, int NP>
@@ -432,7 +447,7 @@ struct Carry {
         float th, et, al;
     };
     // Loader wave lw (0 or 1) handles units lw*kW + lane + i*NLW*kW; wave 0 also the gates.
-    __device__ static void issue(const CarryParams& p, Regs& r, size_t tok0, int n, int row0, int lane, int lw,
+    __device__ __forceinline__ static void issue(const CarryParams& p, Regs& r, size_t tok0, int n, int row0, int lane, int lw,
                                  size_t g0, int gs) {
         const G* q = static_cast<const G*>(p.q);
         const G* k = static_cast<const G*>(p.k);
@@ -459,7 +474,7 @@ struct Carry {
     }
     // n: the chunk's token count (positions at or past it are written as zero
     // and as the identity gates).
-    __device__ static void commit(const Regs& r, typename Sm::QSlot& s, int n, int lane, int lw, float sc) {
+    __device__ __forceinline__ static void commit(const Regs& r, typename Sm::QSlot& s, int n, int lane, int lw, float sc) {
 #pragma unroll
         for (int i = 0; i < NQU; ++i) {
             const int u = lane + (lw + i * NLW) * kW;
@@ -487,7 +502,7 @@ struct Carry {
     }
 
     // Serial schedule (one slot): load and stage directly.
-    __device__ static void load_direct(const CarryParams& p, typename Sm::QSlot& s, size_t tok0, int n, int row0,
+    __device__ __forceinline__ static void load_direct(const CarryParams& p, typename Sm::QSlot& s, size_t tok0, int n, int row0,
                                        int lane, size_t g0, int gs, float sc) {
         const G* q = static_cast<const G*>(p.q);
         const G* k = static_cast<const G*>(p.k);
@@ -514,7 +529,7 @@ struct Carry {
     }
 
     // Gates, decay matrix and P^T of one staged chunk.
-    __device__ static void build(const typename Sm::QSlot& s, typename Sm::PSlot& ps, float* ls, int n, int lane) {
+    __device__ __forceinline__ static void build(const typename Sm::QSlot& s, typename Sm::PSlot& ps, float* ls, int n, int lane) {
         const int lr = lane & 15, lg = lane >> 4;
         const float my_th = s.th[lane % NP], my_et = s.et[lane % NP], my_a = s.av[lane % NP];
         float A, E, c;
@@ -574,6 +589,96 @@ struct Carry {
         }
     }
 };
+
+// One chunk step of a carry walk's state wave (rows r0 .. r0+15 of the
+// cotangents dM, dS, as accumulator tiles of dM^T): store the cotangent
+// leaving the chunk into work slot `slot`, write dv of the chunk's n tokens
+// from token tok0, and carry dM, dS back to the chunk's start.  s and ps hold
+// the chunk's staged inputs and gate quantities; isc undoes the cotangent
+// scaling on dv.
+template <typename T, int D, int NS, int NP>
+__device__ __forceinline__ void carry_state_step(const CarryParams& p,
+                                                 const typename CarrySmem<T, D, NS, NP>::QSlot& s,
+                                                 const typename CarrySmem<T, D, NS, NP>::PSlot& ps, f32x4* dM,
+                                                 f32x4* dS, int n, size_t tok0, size_t slot, int r0, int r0l, int lr,
+                                                 int lg, float isc) {
+    using Gm = CarryGeo<T, D, NS, NP>;
+    using O = Op<T>;
+    using R = Fr<T>;
+    using F = typename O::frag;
+    constexpr int KG = Gm::KG, KS = R::KS, NT = Gm::NT, NKD = Gm::NKD, NKT = Gm::NKT, NCT = Gm::NCT;
+    // Cotangent of the state leaving chunk c.
+    {
+        T* base = static_cast<T*>(p.work) + slot * (2 * D * D) + static_cast<size_t>(r0 + lr) * D;
+#pragma unroll
+        for (int jt = 0; jt < NCT; ++jt) {
+            const int col = O::tmap(jt, 4 * lg);
+            if (col < D) {
+                st4<T>(base + col, dM[jt]);
+                st4<T>(base + D * D + col, dS[jt]);
+            }
+        }
+    }
+    F MB[NKD], SB[NKD], ZC[NKT];
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk) {
+        MB[kk] = O::template from_acc<NCT>(dM, kk);
+        SB[kk] = O::template from_acc<NCT>(dS, kk);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKT; ++kk) ZC[kk] = R::cm(s.dz, Gm::LZ, kk * KG, r0l, lr, lg);
+    // dE (tokens x own rows): -w^M K dM^T - w^S K dS^T - P^T dZ.
+    f32x4 dE[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+        const int trow = O::tmap(tt, lr);
+        f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = x1, x3 = x1;
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) {
+            const F kf = R::rm(s.k, Gm::LQ, trow, kk * KG, lg);
+            x1 = O::mma(x1, kf, MB[kk]);
+            x2 = O::mma(x2, kf, SB[kk]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKT; ++kk) x3 = O::mma(x3, R::rm(ps.pt, Gm::LP, trow, kk * KG, lg), ZC[kk]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = O::tmap(tt, 4 * lg + e);
+            dE[tt][e] = -(ps.wm[t] * x1[e] + ps.ws[t] * x2[e] + x3[e]);
+            if (t < n) p.dv[(tok0 + t) * D + r0 + lr] = -isc * dE[tt][e];
+        }
+    }
+    // Carry: dM <- A dM + Q^T diag(A) dZ + K^T dE, dS <- c dM + E dS + Q^T diag(c) dZ.
+    F DE[NKT], ZA[NKT], ZK[NKT];
+#pragma unroll
+    for (int kk = 0; kk < NKT; ++kk) {
+        DE[kk] = O::template from_acc<NT>(dE, kk);
+        float av[KS], cv[KS];
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+            av[s2] = ps.A[kk * KG + KS * lg + s2];
+            cv[s2] = ps.c[kk * KG + KS * lg + s2];
+        }
+        ZA[kk] = R::scale(ZC[kk], av);
+        ZK[kk] = R::scale(ZC[kk], cv);
+    }
+    const float An = ps.scal[0], cn = ps.scal[1], En = ps.scal[2];
+#pragma unroll
+    for (int jt = 0; jt < NCT; ++jt) {
+        f32x4 nM = An * dM[jt];
+        f32x4 nS = cn * dM[jt] + En * dS[jt];
+#pragma unroll
+        for (int kk = 0; kk < NKT; ++kk) {
+            const F qf = R::cm_t(s.q, Gm::LQ, kk * KG, jt, lr, lg);
+            const F kf = R::cm_t(s.k, Gm::LQ, kk * KG, jt, lr, lg);
+            nM = O::mma(nM, qf, ZA[kk]);
+            nM = O::mma(nM, kf, DE[kk]);
+            nS = O::mma(nS, qf, ZK[kk]);
+        }
+        dM[jt] = nM;
+        dS[jt] = nS;
+    }
+}
 
 template <typename T, int D, int NS, int NP>
 __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_memory_bwd_carry(const CarryParams p) {
@@ -680,82 +785,8 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
 
     auto do_state = [&](int u) {
         const int c = chunk_of(u);
-        const int n = chunk_n(c);
-        const size_t tok0 = seq_tok + static_cast<size_t>(c) * p.b;
-        const typename C::Sm::QSlot& s = sm.qs[u % Gm::NQ];
-        const typename C::Sm::PSlot& ps = sm.ps[u % Gm::NPR];
-        // Cotangent of the state leaving chunk c.
-        {
-            T* base = static_cast<T*>(p.work) + (w_chunk0 + c) * (2 * D * D) +
-                      static_cast<size_t>(r0 + lr) * D;
-#pragma unroll
-            for (int jt = 0; jt < NCT; ++jt) {
-                const int col = O::tmap(jt, 4 * lg);
-                if (col < D) {
-                    st4<T>(base + col, dM[jt]);
-                    st4<T>(base + D * D + col, dS[jt]);
-                }
-            }
-        }
-        F MB[NKD], SB[NKD], ZC[NKT];
-#pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) {
-            MB[kk] = O::template from_acc<NCT>(dM, kk);
-            SB[kk] = O::template from_acc<NCT>(dS, kk);
-        }
-#pragma unroll
-        for (int kk = 0; kk < NKT; ++kk) ZC[kk] = R::cm(s.dz, Gm::LZ, kk * KG, r0l, lr, lg);
-        // dE (tokens x own rows): -w^M K dM^T - w^S K dS^T - P^T dZ.
-        f32x4 dE[NT];
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            const int trow = O::tmap(tt, lr);
-            f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = x1, x3 = x1;
-#pragma unroll
-            for (int kk = 0; kk < NKD; ++kk) {
-                const F kf = R::rm(s.k, Gm::LQ, trow, kk * KG, lg);
-                x1 = O::mma(x1, kf, MB[kk]);
-                x2 = O::mma(x2, kf, SB[kk]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < NKT; ++kk) x3 = O::mma(x3, R::rm(ps.pt, Gm::LP, trow, kk * KG, lg), ZC[kk]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = O::tmap(tt, 4 * lg + e);
-                dE[tt][e] = -(ps.wm[t] * x1[e] + ps.ws[t] * x2[e] + x3[e]);
-                if (t < n) p.dv[(tok0 + t) * D + r0 + lr] = -isc * dE[tt][e];
-            }
-        }
-        // Carry: dM <- A dM + Q^T diag(A) dZ + K^T dE, dS <- c dM + E dS + Q^T diag(c) dZ.
-        F DE[NKT], ZA[NKT], ZK[NKT];
-#pragma unroll
-        for (int kk = 0; kk < NKT; ++kk) {
-            DE[kk] = O::template from_acc<NT>(dE, kk);
-            float av[KS], cv[KS];
-#pragma unroll
-            for (int s2 = 0; s2 < KS; ++s2) {
-                av[s2] = ps.A[kk * KG + KS * lg + s2];
-                cv[s2] = ps.c[kk * KG + KS * lg + s2];
-            }
-            ZA[kk] = R::scale(ZC[kk], av);
-            ZK[kk] = R::scale(ZC[kk], cv);
-        }
-        const float An = ps.scal[0], cn = ps.scal[1], En = ps.scal[2];
-#pragma unroll
-        for (int jt = 0; jt < NCT; ++jt) {
-            f32x4 nM = An * dM[jt];
-            f32x4 nS = cn * dM[jt] + En * dS[jt];
-#pragma unroll
-            for (int kk = 0; kk < NKT; ++kk) {
-                const F qf = R::cm_t(s.q, Gm::LQ, kk * KG, jt, lr, lg);
-                const F kf = R::cm_t(s.k, Gm::LQ, kk * KG, jt, lr, lg);
-                nM = O::mma(nM, qf, ZA[kk]);
-                nM = O::mma(nM, kf, DE[kk]);
-                nS = O::mma(nS, qf, ZK[kk]);
-            }
-            dM[jt] = nM;
-            dS[jt] = nS;
-        }
+        carry_state_step<T, D, NS, NP>(p, sm.qs[u % Gm::NQ], sm.ps[u % Gm::NPR], dM, dS, chunk_n(c),
+                                       seq_tok + static_cast<size_t>(c) * p.b, w_chunk0 + c, r0, r0l, lr, lg, isc);
     };
 
     // Each role runs its own loop; the loops execute the same barriers.
@@ -812,6 +843,213 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         if (is_state) state_final();
     }
 
+}
+
+// Packed documents on persistent workgroups: about one workgroup per CU walks
+// its table of (document, head) units (build_walk_table: longest first,
+// balanced over the workgroup lanes) as one stream of chunks, each document's
+// chunks from its last to its first.  The loaders and the builder run ahead
+// across document boundaries; the state waves write a document's dM0, dS0
+// after its first chunk and take the next document's dM_T, dS_T before that
+// document's last chunk.  Each document's gradients are those of a walk of its
+// own (the classic kernel's per-chunk step on the same staged inputs).
+template <typename T, int D, int NS, int NP>
+__global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_memory_bwd_carry_packed(
+    const CarryParams p) {
+    using Gm = CarryGeo<T, D, NS, NP>;
+    using C = Carry<T, D, NS, NP>;
+    using O = Op<T>;
+    constexpr int NCT = Gm::NCT;
+    constexpr int NTH = kW * Gm::NWAVE;
+    static_assert(Gm::PERSIST, "persistent walk: three staging slots");
+
+    __shared__ __attribute__((aligned(16))) typename C::Sm sm;
+
+    const int tid = threadIdx.x;
+    const int w = tid / kW;
+    const int lane = tid % kW;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int V = gridDim.x / (8 * Gm::NRB);
+    const int x8 = blockIdx.x % 8, m = blockIdx.x / 8;
+    const int rb = m % Gm::NRB, v = m / Gm::NRB;
+    const int row_wg = rb * Gm::RB;
+    const int N = p.BH / p.H, b = p.b;
+
+    // The table (its scratch in the last staging slot), the units' cotangent
+    // scales, and the empty documents: dM0 = dM_T, dS0 = dS_T on this row block.
+    int* temp = reinterpret_cast<int*>(&sm.qs[Gm::NQ - 1]);
+    build_walk_table<NTH, Gm::KMAX>(p.cu, N, p.H, p.T, b, true, p.tcmax, temp, sm.units, &sm.nitems, x8, v, V);
+    {
+        const int nu0 = sm.nunits;
+        for (int kk = tid; kk < nu0; kk += NTH) sm.usc[kk] = cot_scale(p.smax, sm.units[kk].bh);
+        const int empties = sm.nempty;
+        const int* tempty = temp + 4 * N;
+        if (p.dM0 || p.dS0) {
+            constexpr int Q = D / 4;
+            for (int e = 0; e < empties; ++e) {
+                const size_t base = static_cast<size_t>(tempty[e]) * D * D + static_cast<size_t>(row_wg) * D;
+                for (int i = tid; i < Gm::RB * Q; i += NTH) {
+                    const size_t off = base + static_cast<size_t>(i / Q) * D + 4 * (i % Q);
+                    const f32x4 zero{0.f, 0.f, 0.f, 0.f};
+                    if (p.dM0) *reinterpret_cast<f32x4*>(p.dM0 + off) = p.dMT ? *reinterpret_cast<const f32x4*>(p.dMT + off) : zero;
+                    if (p.dS0) *reinterpret_cast<f32x4*>(p.dS0 + off) = p.dST ? *reinterpret_cast<const f32x4*>(p.dST + off) : zero;
+                }
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < 4 * N + Gm::KMAX; i += NTH) temp[i] = 0;
+        __syncthreads();
+    }
+    const int nu = __builtin_amdgcn_readfirstlane(sm.nunits);
+    const int J = __builtin_amdgcn_readfirstlane(sm.nitems);
+
+    // Walk position: unit k, its chunk c (counting down from nch - 1); past the
+    // last unit every chunk has no tokens.
+    struct Walk {
+        int k, c, len, tok0, ck0, bh;
+        float sc;
+    };
+    auto at = [&](Walk& q, int k) {
+        q.k = k;
+        if (k < nu) {
+            const WalkUnit u = sm.units[k];
+            q.tok0 = __builtin_amdgcn_readfirstlane(u.tok0);
+            q.len = __builtin_amdgcn_readfirstlane(u.len);
+            q.ck0 = __builtin_amdgcn_readfirstlane(u.ck0);
+            q.bh = __builtin_amdgcn_readfirstlane(u.bh);
+            q.sc = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sm.usc[k])));
+            q.c = (q.len + b - 1) / b - 1;
+        } else {
+            q.tok0 = q.len = q.ck0 = q.bh = q.c = 0;
+            q.sc = 1.f;
+        }
+    };
+    auto next = [&](Walk& q) {
+        if (q.c > 0) --q.c;
+        else at(q, q.k + 1);
+    };
+    auto n_of = [&](const Walk& q) { return max(0, min(b, q.len - q.c * b)); };
+    auto tok_of = [&](const Walk& q) { return static_cast<size_t>(q.tok0) + static_cast<size_t>(q.c) * b; };
+
+    if (w < NS) {
+        // ===================== state waves =====================
+        const int r0l = 16 * w;
+        const int r0 = row_wg + r0l;
+        f32x4 dM[NCT], dS[NCT];
+        Walk q;
+        at(q, 0);
+        auto off_of = [&]() { return static_cast<size_t>(q.bh) * D * D + static_cast<size_t>(r0 + lr) * D; };
+        // The document's dM_T, dS_T (scaled); the loads are waited for here, so
+        // that the common path of the walk carries no wait on its own stores.
+        auto init = [&]() {
+            const f32x4 zero{0.f, 0.f, 0.f, 0.f};
+            if (q.k < nu && (p.dMT || p.dST)) {
+                const size_t so = off_of();
+#pragma unroll
+                for (int jt = 0; jt < NCT; ++jt) {
+                    const int col = O::tmap(jt, 4 * lg);
+                    const bool ok = col < D;
+                    dM[jt] = (p.dMT && ok) ? q.sc * *reinterpret_cast<const f32x4*>(p.dMT + so + col) : zero;
+                    dS[jt] = (p.dST && ok) ? q.sc * *reinterpret_cast<const f32x4*>(p.dST + so + col) : zero;
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            } else {
+#pragma unroll
+                for (int jt = 0; jt < NCT; ++jt) {
+                    dM[jt] = zero;
+                    dS[jt] = zero;
+                }
+            }
+        };
+        auto final_ = [&]() {
+            const size_t so = off_of();
+            const float isc = 1.f / q.sc;
+#pragma unroll
+            for (int jt = 0; jt < NCT; ++jt) {
+                const int col = O::tmap(jt, 4 * lg);
+                if (col < D) {
+                    if (p.dM0) *reinterpret_cast<f32x4*>(p.dM0 + so + col) = isc * dM[jt];
+                    if (p.dS0) *reinterpret_cast<f32x4*>(p.dS0 + so + col) = isc * dS[jt];
+                }
+            }
+        };
+        init();
+        __syncthreads();
+        __syncthreads();
+        for (int u = 0; u < J; ++u) {
+            carry_state_step<T, D, NS, NP>(p, sm.qs[u % Gm::NQ], sm.ps[u % Gm::NPR], dM, dS, n_of(q), tok_of(q),
+                                           static_cast<size_t>(q.ck0) + q.c, r0, r0l, lr, lg, 1.f / q.sc);
+            if (q.c == 0) {
+                final_();
+                at(q, q.k + 1);
+                init();
+            } else {
+                --q.c;
+            }
+            __syncthreads();
+        }
+    } else if (w == NS + 2) {
+        // ===================== builder =====================
+        Walk q;
+        at(q, 0);
+        auto build = [&](int u) { C::build(sm.qs[u % Gm::NQ], sm.ps[u % Gm::NPR], sm.ls, n_of(q), lane); };
+        __syncthreads();
+        if (J > 0) {
+            build(0);
+            next(q);
+        }
+        __syncthreads();
+        for (int u = 0; u < J; ++u) {
+            if (u + 1 < J) {
+                build(u + 1);
+                next(q);
+            }
+            __syncthreads();
+        }
+    } else {
+        // ===================== loaders =====================
+        // Items are requested in order (three steps ahead) and staged one step
+        // later; the length and scale of the two not yet staged are kept by parity.
+        const int lw = w - NS;
+        typename C::Regs regs;
+        Walk q;
+        at(q, 0);
+        int rn[2] = {0, 0};
+        float rsc[2] = {1.f, 1.f};
+        int ji = 0;
+        auto issue = [&]() {
+            const size_t t0 = tok_of(q);
+            const int n = n_of(q);
+            C::issue(p, regs, t0, n, row_wg, lane, lw, t0, 1);
+            if (ji & 1) {
+                rn[1] = n;
+                rsc[1] = q.sc;
+            } else {
+                rn[0] = n;
+                rsc[0] = q.sc;
+            }
+            ++ji;
+            next(q);
+        };
+        auto commit = [&](int u) {
+            const bool odd = u & 1;
+            C::commit(regs, sm.qs[u % Gm::NQ], odd ? rn[1] : rn[0], lane, lw, odd ? rsc[1] : rsc[0]);
+        };
+        if (J > 0) {
+            issue();
+            commit(0);
+        }
+        if (J > 1) issue();
+        __syncthreads();
+        if (J > 1) commit(1);
+        if (J > 2) issue();
+        __syncthreads();
+        for (int u = 0; u < J; ++u) {
+            if (u + 2 < J) commit(u + 2);
+            if (u + 3 < J) issue();
+            __syncthreads();
+        }
+    }
 }
 
 // ===========================================================================
@@ -1539,13 +1777,61 @@ __global__ __launch_bounds__((kW * GradGeo<T, D, NP>::NWAVE)) void linear_memory
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
+// Workgroup lanes V of the persistent carry walk on the current device:
+// resident workgroups (CUs x occupancy) / (8 XCD lanes x NRB row blocks),
+// queried once per device and instance.
+template <typename T, int D, int NS, int NP>
+int carry_lanes() {
+    using Gm = CarryGeo<T, D, NS, NP>;
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::atomic<int>& slot = cached[dev & 63];
+    int v = slot.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, linear_memory_bwd_carry_packed<T, D, NS, NP>,
+                                                     kW * Gm::NWAVE, 0) != hipSuccess || per_cu <= 0)
+        per_cu = 1;
+    v = bmax(1, cus * per_cu / (8 * Gm::NRB));
+    slot.store(v, std::memory_order_relaxed);
+    return v;
+}
+
 template <typename T, int D, int NS, int NP>
 hipError_t launch_carry(const CarryParams& cp, hipStream_t s) {
     using Gm = CarryGeo<T, D, NS, NP>;
+    if constexpr (Gm::PERSIST) {
+        if (cp.cu) {
+            // Packed documents: persistent workgroups when the documents fit the
+            // in-LDS ranking and every workgroup's units fit its table.
+            const int N = cp.BH / cp.H;
+            const int V = bmax(1, bmin(carry_lanes<T, D, NS, NP>(), (cp.BH + 7) / 8));
+            const long long kmax = (static_cast<long long>(cp.BH) + 8LL * V - 1) / (8LL * V);
+            if (N <= Gm::NMAX_DOCS && kmax <= Gm::KMAX) {
+                hipLaunchKernelGGL((linear_memory_bwd_carry_packed<T, D, NS, NP>), dim3(8 * Gm::NRB * V),
+                                   dim3(kW * Gm::NWAVE), 0, s, cp);
+                return hipGetLastError();
+            }
+        }
+    }
+    // One workgroup per (sequence or document, row block); packed documents
+    // above the in-wave ranking's limit take their order from a pass before
+    // the launch.
+    CarryParams q = cp;
+    int* perm = nullptr;
+    if (cp.cu && cp.T > 0) {
+        const hipError_t e = make_doc_order(cp.cu, cp.BH / cp.H, cp.T, s, &perm);
+        if (e != hipSuccess) return e;
+    }
+    q.perm = perm;
     const long long nwg = static_cast<long long>(cp.BH) * Gm::NRB;
     hipLaunchKernelGGL((linear_memory_bwd_carry<T, D, NS, NP>), dim3(static_cast<unsigned>(nwg)),
-                       dim3(kW * Gm::NWAVE), 0, s, cp);
-    return hipGetLastError();
+                       dim3(kW * Gm::NWAVE), 0, s, q);
+    const hipError_t err = hipGetLastError();
+    if (perm) (void)hipFreeAsync(perm, s);
+    return err;
 }
 
 template <typename T, int D, int NP>
@@ -1661,11 +1947,9 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
         const hipError_t e0 = hipGetLastError();
         if (e0 != hipSuccess) return TTT_ERR_HIP;
     }
-    int* perm = nullptr;
-    if (packed && Tlen > 0 && make_doc_order(cu, B, Tlen, s, &perm) != hipSuccess) return TTT_ERR_HIP;
     const CarryParams cp{q, k, dz, theta, eta, alpha, dMT, dST, work, dv, dM0, dS0,
                          static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax), smax,
-                         perm};
+                         nullptr};
     const GradParams gp{q, k, v, theta, eta, alpha, ckpt, work, dz, dv, dq, dk, dth, deta, dal,
                         static_cast<int>(BH), Tlen, b, static_cast<int>(nch), cg, cu, H, static_cast<int>(tcmax), smax};
     hipError_t err;
@@ -1675,7 +1959,6 @@ int backward_impl(const void* q, const void* k, const void* v, const float* thet
         case 64: err = launch_bwd_np<T, 64>(cp, gp, b, s); break;
         default: err = launch_bwd_np<T, 128>(cp, gp, b, s); break;
     }
-    if (perm) (void)hipFreeAsync(perm, s);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

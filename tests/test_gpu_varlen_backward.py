@@ -92,9 +92,14 @@ CASES = [
     ("hundred-docs", 3, 1, [int(x) for x in np.random.default_rng(6).integers(0, 41, 100)], 16, 32),
     ("many-docs", 3, 1, [int(x) for x in np.random.default_rng(5).integers(0, 41, 150)], 16, 32),
     ("600-docs", 3, 1, [int(x) for x in np.random.default_rng(7).integers(0, 41, 600)], 16, 32),
-    # bf16 at d = 64: the forward with checkpoints runs the persistent document walk
-    # (checkpoint slots from the in-kernel chunk prefix, 300 documents, empty ones among them).
+    # bf16 at d = 64: the forward with checkpoints and the carry walk run the
+    # persistent document walks (checkpoint slots from the in-kernel chunk
+    # prefix, 300 documents, empty ones among them).
     ("300-docs-d64", 3, 1, [int(x) for x in np.random.default_rng(12).integers(0, 41, 300)], 16, 64),
+    # One long document among short ones at d = 128: the persistent carry walk's
+    # longest-processing-time head (and the forward's) take the long one alone.
+    ("skewed-d128", 3, 2, [int(x) for x in np.random.default_rng(13).integers(5, 41, 40)] + [1500]
+     + [int(x) for x in np.random.default_rng(14).integers(0, 41, 60)], 64, None),
 ]
 
 
