@@ -1764,12 +1764,27 @@ hipError_t launch_np(const Params& p, int np, hipStream_t stream) {
     }
 }
 
+// Compute units of the current device, queried once per device.
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::atomic<int>& slot = cached[dev & 63];
+    int v = slot.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    slot.store(v, std::memory_order_relaxed);
+    return v;
+}
+
 template <typename T, int D>
 hipError_t launch_ns(const Params& p, int np, hipStream_t stream) {
     if constexpr (D >= 32) {
-        // Two 16-row tiles per workgroup when that still leaves >= 256 workgroups.
+        // Two 16-row tiles per workgroup when there are more row tiles than
+        // CUs: one-tile workgroups would then share CUs or run in a second
+        // round, which costs more than the fewer, larger workgroups.
         const long long row_tiles = static_cast<long long>(p.BH) * (D / 16);
-        if (row_tiles >= 512) return launch_np<T, D, 2>(p, np, stream);
+        if (row_tiles > device_cus()) return launch_np<T, D, 2>(p, np, stream);
     }
     return launch_np<T, D, 1>(p, np, stream);
 }
