@@ -511,20 +511,21 @@ def varlen_main(args):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for i in range(args.steps):
-        starts[i].record()
+    # Timed region: K back-to-back launches between two HIP events on the
+    # library's stream (no event between launches).
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
         call()
-        ends[i].record()
+    e1.record()
     torch.cuda.synchronize()
-    launch_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
-    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
-    avg_launch_ms = float(np.mean(launch_ms))
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    avg_launch_ms = ms_per_step
     per_tok = 3 * d * 2 + 3 * 4 + d * 4
     nbytes = H * T * per_tok + N * H * d * d * 4 * 2
     achieved_gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
-    log(f"avg launch {avg_launch_ms * 1e3:.1f} us, min {min(launch_ms) * 1e3:.1f} us; "
+    log(f"launch average {avg_launch_ms * 1e3:.1f} us; "
         f"algorithmic bytes/launch {nbytes / 1e6:.1f} MB -> {achieved_gbs:.0f} GB/s")
     # Parity: the first two documents of head 0, every row.
     from oracle import linear_forward
@@ -897,22 +898,22 @@ def main():
         call()
     torch.cuda.synchronize()
 
-    # Timed region: K steps, one kernel launch each, on torch's current stream
-    # (the stream the library launches on), bracketed by HIP events.
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: K steps, one kernel launch each, back to back on torch's
+    # current stream (the stream the library launches on), between two HIP
+    # events; no event sits between launches, so the launch average is the
+    # events' interval over K (launch gaps included).
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record()
+    e0.record()
+    for _ in range(args.steps):
         call()
-        ends[i].record()
+    e1.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    launch_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
-    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
-    avg_launch_ms = float(np.mean(launch_ms))
-    med_launch_ms = float(np.median(launch_ms))
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    avg_launch_ms = ms_per_step
 
     if deep:
         nbytes, flops, per_tok = algorithmic_work_mlp(w, z_bytes=z_bytes, depth=args.depth)
@@ -927,9 +928,7 @@ def main():
     achieved_gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
     achieved_tflops = flops / (avg_launch_ms * 1e-3) / 1e12
     tokens_per_s = B * T / (ms_per_step * 1e-3)
-    log(f"avg launch {avg_launch_ms * 1e3:.1f} us, median {med_launch_ms * 1e3:.1f} us, "
-        f"min {min(launch_ms) * 1e3:.1f} us, max {max(launch_ms) * 1e3:.1f} us; "
-        f"step {ms_per_step * 1e3:.1f} us; wall/step {t_wall / args.steps * 1e3:.3f} ms")
+    log(f"launch average {avg_launch_ms * 1e3:.1f} us; wall/step {t_wall / args.steps * 1e3:.3f} ms")
     log(f"algorithmic bytes/launch {nbytes / 1e6:.1f} MB ({per_tok} B per head-token + state) -> "
         f"{achieved_gbs:.0f} GB/s; flops/launch {flops / 1e9:.1f} GFLOP -> {achieved_tflops:.1f} TFLOP/s")
 
@@ -976,7 +975,7 @@ def main():
                     "traffic_unit": "bytes/launch", "traffic_source": "profiles/ counter summary",
                     "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                     "hbm_frac": achieved_gbs / HBM_PEAK_GBS,
-                    "launch_us": {"mean": avg_launch_ms * 1e3, "median": med_launch_ms * 1e3}}
+                    "launch_us": avg_launch_ms * 1e3}
         cfg = {"workload": w.name + (f"-depth{args.depth}" if args.depth != 2 else ""), "B": B, "H": H, "T": T,
                "d": d, "hidden": w.hidden, "depth": args.depth, "b": w.b,
                "inputs": "bf16 q,k,v; f32 gates", "accumulate": "f32", "weights": "f32", "z": zname,
@@ -992,7 +991,7 @@ def main():
                     "algorithmic_flops": flops,
                     "frac_of_step": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS,
-                    "launch_us": {"mean": avg_launch_ms * 1e3, "median": med_launch_ms * 1e3}}
+                    "launch_us": avg_launch_ms * 1e3}
         cfg = {"workload": w.name + ("-chunk-gates" if args.chunk_gates else "") + ("-depth1" if args.depth == 1 else ""),
                "B": B, "H": H, "T": T, "d": d,
                "b": w.b, "inputs": "bf16 q,k,v; f32 gates" + (" per chunk" if args.chunk_gates else ""),
