@@ -217,6 +217,24 @@ def test_run_to_run_determinism():
             assert torch.equal(p_, q_)
 
 
+@pytest.mark.parametrize("d,b,T,H_small,H_big", [(64, 16, 200, 12, 24), (128, 64, 300, 4, 12)])
+def test_row_tile_layouts_agree_bitwise(d, b, T, H_small, H_big):
+    # Rows are independent, so the workgroup layout must not change any output
+    # bit.  A batch with fewer 16-row tiles than CUs runs one tile per
+    # workgroup; embedded in a batch with more (on a 256-CU MI355X: 4 x 24 x 4
+    # = 384 and 4 x 12 x 8 = 384 tiles against 192 and 128), the same
+    # sequences run two tiles per workgroup.
+    w, big = _dev_inputs(B=4, H=H_big, T=T, d=d, b=b)
+    small = {k: v[:, :H_small].contiguous() for k, v in big.items()}
+    args = ("q", "k", "v", "theta", "eta", "alpha", "M0", "S0")
+    _say(f"case d={d} b={b} T={T}: heads {H_small} and {H_big}")
+    a = tm.forward(*(small[k] for k in args), b=b)
+    c = tm.forward(*(big[k] for k in args), b=b)
+    torch.cuda.synchronize()
+    for p_, q_ in zip(a, c):
+        assert torch.equal(p_, q_[:, :H_small])
+
+
 def test_argument_errors_are_reported():
     w, x = _dev_inputs(B=1, H=1, T=64, d=64, b=16)
     args = (x["q"], x["k"], x["v"], x["theta"], x["eta"], x["alpha"])
