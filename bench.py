@@ -116,9 +116,9 @@ FWD_PROFILES = {2: "linear_memory_fwd_ttt_linear_d64_b16", 3: "linear_memory_fwd
 
 
 def measured_traffic(w, kind="forward"):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
-    summary under profiles/ (a separate rocprofv3 run; see the summary for its
-    command), not measured in this run.
+    """HBM bytes per launch from the committed counter summary under profiles/
+    (TCC read and write requests by size, from separate rocprofv3 runs; see the
+    summary for the commands), not measured in this run.
 
     The summary records the sha256 of the kernel source it was measured on; if
     the source has changed since (or the workload differs), the figure no

@@ -210,7 +210,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // Bytes of the chunk-start state checkpoints of a dense [B, H, T] problem:
 // [B*H][ceil(T/b)][M | S][d][d] elements of elem bytes (0 for sizes no entry
 // point accepts).
-size_t ckpt_bytes(int B, int H, int T, int d, int b, size_t elem = sizeof(float)) {
+[[maybe_unused]] size_t ckpt_bytes(int B, int H, int T, int d, int b, size_t elem = sizeof(float)) {
     if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1) return 0;
     const size_t nch = (static_cast<size_t>(T) + b - 1) / b;
     return static_cast<size_t>(B) * H * nch * 2 * d * d * elem;
@@ -229,7 +229,7 @@ struct Span {
 inline long long varlen_chunk_slots(int N, int T, int b) {
     return (static_cast<long long>(T) + b - 1) / b + N;
 }
-size_t ckpt_bytes_varlen(int N, int H, int T, int d, int b, size_t elem = sizeof(float)) {
+[[maybe_unused]] size_t ckpt_bytes_varlen(int N, int H, int T, int d, int b, size_t elem = sizeof(float)) {
     if (N < 0 || H < 0 || T < 0 || d < 1 || b < 1) return 0;
     return static_cast<size_t>(H) * static_cast<size_t>(varlen_chunk_slots(N, T, b)) * 2 * d * d * elem;
 }
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256) void doc_rank_order(const int* __restrict__ cu
 // does not cover them (N > kLptDocs): N ints from the stream-ordered
 // allocator, filled by doc_rank_order on `stream`; NULL (and hipSuccess) when
 // not needed.  The caller frees it with hipFreeAsync after its launches.
-hipError_t make_doc_order(const int* cu, int N, int T, hipStream_t stream, int** perm) {
+[[maybe_unused]] hipError_t make_doc_order(const int* cu, int N, int T, hipStream_t stream, int** perm) {
     *perm = nullptr;
     if (N <= kLptDocs) return hipSuccess;
     hipError_t err = hipMallocAsync(reinterpret_cast<void**>(perm), static_cast<size_t>(N) * sizeof(int), stream);

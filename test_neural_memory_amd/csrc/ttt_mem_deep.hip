@@ -1427,7 +1427,7 @@ int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
         err = hipLaunchCooperativeKernel(kern, dim3(static_cast<unsigned>(ngroups * kG)), dim3(threads), args, 0,
                                          stream);
     }
-    if (own_work) hipFreeAsync(work, stream);
+    if (own_work) (void)hipFreeAsync(work, stream);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

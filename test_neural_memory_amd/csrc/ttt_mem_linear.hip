@@ -1492,7 +1492,6 @@ __global__ __launch_bounds__(kWave * (NS * CS + (CS == 2 ? 8 : 2))) void linear_
     using Gm = Geo<T, D, NS, CS, NP>;
     using K = Kernel<T, D, NS, CS, NP>;
     using O = Op<T>;
-    using G = typename Gm::G;
     using F = typename O::frag;
     constexpr int NBUF = Gm::NBUF;
     constexpr int RB = Gm::RB;
@@ -1860,7 +1859,7 @@ int forward_impl(const void* q, const void* k, const void* v, const float* theta
     }
 
     Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, nullptr, H, ckpt,
-             chunk_gates ? 1 : 0, 0, z_bf16 ? 1 : 0};
+             chunk_gates ? 1 : 0, 0, z_bf16 ? 1 : 0, nullptr};
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -1924,7 +1923,7 @@ int forward_varlen_impl(const void* q, const void* k, const void* v, const float
     }
 
     Params p{q, k, v, theta, eta, alpha, M0, S0, z, M_T, S_T, static_cast<int>(BH), Tlen, b, cu, H, ckpt, 0,
-             static_cast<int>(tcmax), 0};
+             static_cast<int>(tcmax), 0, nullptr};
     // More documents than the in-kernel ranking covers: a pass before the
     // launch writes their longest-first order to a stream-ordered table.
     const hipError_t err = dispatch<T>(p, d, static_cast<hipStream_t>(stream));

@@ -685,9 +685,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
     using Gm = CarryGeo<T, D, NS, NP>;
     using C = Carry<T, D, NS, NP>;
     using O = Op<T>;
-    using R = Fr<T>;
-    using F = typename O::frag;
-    constexpr int KG = Gm::KG, KS = R::KS, NT = Gm::NT, NKD = Gm::NKD, NKT = Gm::NKT, NCT = Gm::NCT;
+    constexpr int NCT = Gm::NCT;
 
     __shared__ __attribute__((aligned(16))) typename C::Sm sm;
 
@@ -738,8 +736,7 @@ __global__ __launch_bounds__((kW * CarryGeo<T, D, NS, NP>::NWAVE)) void linear_m
         return p.chunk_gates ? static_cast<size_t>(bh) * nch + c : seq_tok + static_cast<size_t>(c) * p.b;
     };
 
-    const bool is_state = w < NS;
-    const bool is_loader = w == NS || w == NS + 1;
+    const bool is_state = w < NS;   // the two waves after them load, the last one builds
     const bool is_builder = w == NS + 2;
     const int lw = w - NS;   // loader index
 
