@@ -364,8 +364,13 @@ __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
     int epoch = 0;                        // exchanges of this group so far
 
     // Group exchange in two halves: signal() after this workgroup's
-    // contribution is written; wait() until all G have signalled.
+    // contribution is written; wait() until all G have signalled.  Every
+    // wave first waits until its own stores have completed (a completed store
+    // sits in the L2 that the whole group shares), so the counter can only
+    // show this workgroup once its slot data is there for the other
+    // workgroups' device-scope copies.
     auto signal = [&]() {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
         if (tid == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -806,7 +811,9 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
     const int own = 2 * part + w;        // its 16-unit block
     int epoch = 0;
 
+    // As in deep_fwd2: each wave's stores complete before the counter moves.
     auto signal = [&]() {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
         if (tid == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
