@@ -189,9 +189,6 @@ struct ChunkBuf {
     alignas(16) float wm[kNP];            // -theta_j gamma_{n-1,j}
     alignas(16) float ws[kNP];            // -theta_j p_{n-1,j}
     alignas(16) float scal[4];            // A_n, c_n, E_n
-    alignas(16) float rth[kNP];           // the chunk's raw gates (theta, eta, alpha), for a later gate pass
-    alignas(16) float ret[kNP];
-    alignas(16) float ral[kNP];
 };
 
 struct DeepSmem {
@@ -320,10 +317,11 @@ __device__ __forceinline__ s16x4 lds_tr4(const uint16_t* base, int rs, int lr, i
 // weights.  Waves 2 and 3 (the read waves, units of waves 0 and 1) read the
 // previous chunk -- Hq, Aq and the z partial -- from their own copy of the
 // weights one chunk behind, which they keep by applying the same carry to the
-// same float32 inputs (so both copies hold identical values), and compute the
-// gate quantities of the chunk the chain waves carry next.  Per chunk step the
-// five barriers below are shared by all four waves; the read waves' work fills
-// the chain's segments instead of lengthening them.
+// same float32 inputs (so both copies hold identical values), sum the z of the
+// chunk before and compute the gate quantities of the chunk the chain waves
+// carry next.  Per chunk step the five barriers below are shared by all four
+// waves; the read waves' work fills the chain's segments instead of
+// lengthening them.
 __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
     __shared__ DeepSmem sm;
     const int tid = threadIdx.x;
@@ -479,6 +477,7 @@ __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
             const ChunkBuf& Bp = sm.buf[(c + 1) & 1];  // chunk c - 1
             const float* RTp = sm.RT[(c + 1) & 1];
             const int n = keys ? chunk_n(c) : 0;
+            Prefetch graw;   // read wave 0: raw gates of chunk c + 1
             float* slot = xbase + static_cast<size_t>((epoch % kRing) * kG + part) * kSlot;
             float* nslot = xbase + static_cast<size_t>(((epoch + 1) % kRing) * kG + part) * kSlot;
 
@@ -564,40 +563,21 @@ __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
             }
             const float* rslot = xbase + static_cast<size_t>(((epoch - 1) % kRing) * kG) * kSlot;
 
-            // ================= segment 4: partials in; z out | the read waves' carry, next gates =================
-            const bool zred = zout && part < kDT && w == 0;
+            // ================= segment 4: partials in, R | the read waves' carry =================
+            const bool zred = zout && part < kDT && w == 3;
             if (chain) {
                 // The partials straight into registers (device-scope loads, all
                 // in flight at once), summed in slot order.  Global-to-LDS
                 // copies of the same tiles measured 1.84 against 1.60 ms per
                 // launch: each lane needs only its own 16 bytes back.
                 const auto rsl = make_rsrc(rslot, static_cast<uint32_t>(kG * kSlot * 4));
-                f32x4 rpart[2][kG], zpart[2 * kG];
+                f32x4 rpart[2][kG];
                 if (keys) {
 #pragma unroll
                     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
                         for (int g2 = 0; g2 < kG; ++g2)
                             rpart[k2][g2] = slot_load(rsl, g2 * kSlot + lr * kD + 16 * (2 * w + k2) + 4 * lg);
-                }
-                if (zred) {
-#pragma unroll
-                    for (int g2 = 0; g2 < kG; ++g2)
-#pragma unroll
-                        for (int r2 = 0; r2 < 2; ++r2)
-                            zpart[2 * g2 + r2] = slot_load(rsl, g2 * kSlot + kNP * kD * (1 + r2) + lr * kD + 16 * part + 4 * lg);
-                }
-                // z of chunk c - 2: four workgroups, one d tile each.
-                if (zred) {
-                    const int np = chunk_n(c - 2);
-                    f32x4 zt = zpart[0];
-#pragma unroll
-                    for (int g2 = 1; g2 < 2 * kG; ++g2) zt += zpart[g2];
-                    const bool zb = p.z_bf16 != 0;
-                    const uint32_t zsz = zb ? 2u : 4u;
-                    const auto rz = make_rsrc(static_cast<char*>(p.z) + (seq_tok + static_cast<size_t>(c - 2) * p.b) * kD * zsz,
-                                              static_cast<uint32_t>(np) * kD * zsz);
-                    store_out4(zt, rz, static_cast<uint32_t>(lr * kD + 16 * part + 4 * lg), zb);
                 }
                 // R = K - V + sum of partials (rows [t][d] and R^T [d][t] of this chunk's parity).
                 if (keys) {
@@ -615,22 +595,46 @@ __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
                     }
                 }
             } else {
+                // Raw gates of chunk c + 1 into registers, for the gate pass of
+                // read wave 0 in segment 5.
+                if (w == 2 && keys && c + 1 < nch) {
+                    const int n1 = chunk_n(c + 1);
+                    const size_t gi = seq_tok + static_cast<size_t>(c + 1) * p.b;
+                    const uint32_t gbytes = static_cast<uint32_t>(n1) * 4;
+                    graw.th = buf_load4(make_rsrc(p.theta + gi, gbytes), lane * 4);
+                    graw.al = buf_load4(make_rsrc(p.alpha + gi, gbytes), lane * 4);
+                    graw.et = buf_load4(make_rsrc(p.eta + gi, gbytes), lane * 4);
+                }
                 // The carry of chunk c - 1 on the read waves' weights (needed
                 // only while a later chunk remains to be read).
                 if (reads && c < nch) carry(Bp, sm.act[wp].dh[lane], sm.act[wp].ak[(c + 1) & 1][lane], RTp);
-                // Gate quantities of chunk c (from its raw gates), for the chain's carry below.
-                if (w == 2 && keys && c >= 1) {
-                    Prefetch g;
-                    g.th = lane < kNP ? B.rth[lane] : 0.f;
-                    g.et = lane < kNP ? B.ret[lane] : 0.f;
-                    g.al = lane < kNP ? B.ral[lane] : 0.f;
-                    gates(g, B, n, lane);
-                }
             }
             __syncthreads();
+            // z of chunk c - 2 on read wave 1 (four workgroups, one d tile
+            // each), while the chain waves run segment 5: the sum of the two
+            // read waves' partials of every workgroup, in slot order (on chain
+            // wave 0 it lengthened segment 4).
+            if (zred) {
+                const auto rsl = make_rsrc(rslot, static_cast<uint32_t>(kG * kSlot * 4));
+                f32x4 zpart[2 * kG];
+#pragma unroll
+                for (int g2 = 0; g2 < kG; ++g2)
+#pragma unroll
+                    for (int r2 = 0; r2 < 2; ++r2)
+                        zpart[2 * g2 + r2] = slot_load(rsl, g2 * kSlot + kNP * kD * (1 + r2) + lr * kD + 16 * part + 4 * lg);
+                const int np = chunk_n(c - 2);
+                f32x4 zt = zpart[0];
+#pragma unroll
+                for (int g2 = 1; g2 < 2 * kG; ++g2) zt += zpart[g2];
+                const bool zb = p.z_bf16 != 0;
+                const uint32_t zsz = zb ? 2u : 4u;
+                const auto rz = make_rsrc(static_cast<char*>(p.z) + (seq_tok + static_cast<size_t>(c - 2) * p.b) * kD * zsz,
+                                          static_cast<uint32_t>(np) * kD * zsz);
+                store_out4(zt, rz, static_cast<uint32_t>(lr * kD + 16 * part + 4 * lg), zb);
+            }
             if (!keys) continue;
 
-            // ================= segment 5: dH and the carry of chunk c =================
+            // ================= segment 5: dH and the carry of chunk c | z of chunk c - 2, gates of chunk c + 1 =================
             if (chain) {
                 f32x4 dH = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -646,12 +650,13 @@ __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
                 if (c + 1 < nch) {
                     ChunkBuf& Bn = sm.buf[(c + 1) & 1];
                     stage(pf, Bn, tid);
-                    if (w == 1 && lane < kNP) {   // the next chunk's raw gates (padding tokens read 0)
-                        Bn.rth[lane] = pf.th;
-                        Bn.ret[lane] = pf.et;
-                        Bn.ral[lane] = pf.al;
-                    }
                 }
+            } else if (w == 2 && c + 1 < nch) {
+                // Gate quantities of chunk c + 1, for the chain's carry in the
+                // next step.  In segment 4 this pass made read wave 0 the
+                // longest wave there; with it and the z sum moved here a launch
+                // of 32 sequences x 4096 tokens takes 1.47-1.48 ms, not 1.58.
+                gates(graw, sm.buf[(c + 1) & 1], chunk_n(c + 1), lane);
             }
             __syncthreads();
         }
