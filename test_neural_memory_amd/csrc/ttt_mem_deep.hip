@@ -77,12 +77,17 @@ constexpr int kLS = kNP + 4;    // LDS row stride (floats) of the decay matrix r
 constexpr int kWS = 16 + 4;     // LDS row stride (bf16) of a wave's staged W_L^T rows [d][h]
 constexpr int kThreads2 = 256;         // deep_fwd2: two chain waves and two read waves
 constexpr int kSlot = 3 * kNP * kD;   // floats per workgroup slot and exchange step: R, then the two read waves' z partials
-// Exchange slots form a ring of kRing steps per group.  A workgroup writes
-// the slot of step e + kRing only after every workgroup of its group has
-// signalled step e + kRing - 1, i.e. has finished reading step e, so two steps
-// would do; four leave margin.  The ring is small enough to stay in the XCD's
-// L2 (no write-back to HBM).
-constexpr int kRing = 4;
+// Exchange slots form a ring of steps per group.  A workgroup reads the
+// slots of step e after the group counter shows every workgroup's signal of
+// e, and its own signal of e + 1 follows the completion of those reads.  So
+// once the counter shows step e + 1, nobody reads step e - 1 any more:
+// deep_fwd3/4, which write the slot of step e + 1 only after that, need two
+// steps; deep_fwd2 writes a z partial into the slot of step e + 2 before its
+// wait for e + 1 and needs three.  The smaller the ring, the less of the XCD's
+// L2 it takes from the hidden layers' weights and from the data streamed
+// through it (lines evicted dirty are written back to HBM).
+constexpr int kRing = 3;    // deep_fwd2
+constexpr int kRingM = 2;   // deep_fwd3, deep_fwd4
 // Cache policy of the slot copies: SC1 (device scope), so a copy is served
 // coherently at device scope -- never from a line the CU's vector L1 kept from
 // an earlier step -- and no L1 invalidation is needed.
@@ -799,10 +804,10 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
     const int part = __builtin_amdgcn_readfirstlane(sm.part);
     int* const ctr = p.work + kHdrInts + gi * kCtrStride;
     float* const xall = reinterpret_cast<float*>(p.work + kHdrInts + p.ngroups * kCtrStride);
-    float* const xbase = xall + static_cast<size_t>(gi) * kRing * kG * kSlotM;
+    float* const xbase = xall + static_cast<size_t>(gi) * kRingM * kG * kSlotM;
     // Weights and momenta of the hidden-to-hidden layers, [group][layer][W | S][wave of the group][tile][lane]
     // (this wave's 16 columns as accumulator tiles; only the owning lanes touch them).
-    f32x4* const sbase = reinterpret_cast<f32x4*>(xall + static_cast<size_t>(p.ngroups) * kRing * kG * kSlotM) +
+    f32x4* const sbase = reinterpret_cast<f32x4*>(xall + static_cast<size_t>(p.ngroups) * kRingM * kG * kSlotM) +
                          (static_cast<size_t>(gi) * NM * 2 * (kG * kWaves) + (2 * part + w)) * kHT * 64 + lane;
     // Tile addresses come from a base made opaque where they are used, so that
     // the compiler forms them there instead of keeping all of them live across
@@ -845,8 +850,8 @@ __device__ __forceinline__ void deep_fwd_mid(const DeepParams& p) {
         ++epoch;
         return sm.bail == 0;
     };
-    auto my_slot = [&]() { return xbase + static_cast<size_t>((epoch % kRing) * kG + part) * kSlotM; };
-    auto step_slots = [&]() { return xbase + static_cast<size_t>(((epoch - 1) % kRing) * kG) * kSlotM; };
+    auto my_slot = [&]() { return xbase + static_cast<size_t>((epoch % kRingM) * kG + part) * kSlotM; };
+    auto step_slots = [&]() { return xbase + static_cast<size_t>(((epoch - 1) % kRingM) * kG) * kSlotM; };
     // Gather: this wave's block of an activation (T layout: lane (lr, lg) =
     // X[token lr][unit hu + 4 lg + j], split) into dst[kt] of every workgroup.
     auto gather = [&](const Sp& xt, uint16_t (*dst)[2][kBlk]) -> bool {
@@ -1334,7 +1339,7 @@ void* scratch_ptr() {
 size_t deep_work_bytes_for(long long ngroups, int depth = 2) {
     const size_t hdr = (static_cast<size_t>(kHdrInts) + static_cast<size_t>(ngroups) * kCtrStride) * 4;
     if (depth <= 2) return hdr + static_cast<size_t>(ngroups) * kRing * kG * kSlot * 4;
-    return hdr + static_cast<size_t>(ngroups) * kRing * kG * kSlotM * 4 +
+    return hdr + static_cast<size_t>(ngroups) * kRingM * kG * kSlotM * 4 +
            static_cast<size_t>(ngroups) * (depth - 2) * 2 * (kG * kWaves) * kHT * 64 * 16;
 }
 
