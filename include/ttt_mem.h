@@ -149,7 +149,7 @@ int ttt_mem_mlp_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * computation and arguments as ttt_mem_mlp_forward_bf16, with the exchange
- * workspace in a file-scope device array of the library (2.1 MB per GPU,
+ * workspace in a file-scope device array of the library (2.4 MB per GPU,
  * reserved when the library is loaded and held until the process ends)
  * instead of an allocation.  It runs at most 8 (batch, head) sequences at a
  * time (the array holds 8 groups), so larger batches take proportionally
