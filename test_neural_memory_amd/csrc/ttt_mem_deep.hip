@@ -376,8 +376,14 @@ __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
         __syncthreads();
         if (tid == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    auto wait = [&]() -> bool {
-        if (tid == 0) {
+    // Only the chain waves, which read the slots, wait: lane 0 of each polls,
+    // and the wave goes on when it returns (3.5 % faster than one poller and
+    // a workgroup barrier; the deeper kernels, whose waves all read slots,
+    // gain nothing from it).  The read waves' next work does not depend on
+    // the exchange; a timeout is seen by every wave after the next workgroup
+    // barrier (sm.bail).
+    auto wait = [&]() {
+        if (chain && lane == 0) {
             const int target = kG * (epoch + 1);
             int spins = 0;
             while (l2_counter(ctr) < target) {
@@ -390,9 +396,7 @@ __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
                 __builtin_amdgcn_s_sleep(1);
             }
         }
-        __syncthreads();
         ++epoch;
-        return sm.bail == 0;
     };
 
     for (int s = gi; s < p.BH; s += p.ngroups) {
@@ -562,10 +566,7 @@ __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
                     *reinterpret_cast<f32x4*>(zs + 16 * dt) = zp;
                 }
             }
-            if (!wait()) {
-                ok = false;
-                break;
-            }
+            wait();
             const float* rslot = xbase + static_cast<size_t>(((epoch - 1) % kRing) * kG) * kSlot;
 
             // ================= segment 4: partials in, R | the read waves' carry =================
@@ -615,6 +616,10 @@ __global__ __launch_bounds__(kThreads2, 1) void deep_fwd2(const DeepParams p) {
                 if (reads && c < nch) carry(Bp, sm.act[wp].dh[lane], sm.act[wp].ak[(c + 1) & 1][lane], RTp);
             }
             __syncthreads();
+            if (sm.bail) {
+                ok = false;
+                break;
+            }
             // z of chunk c - 2 on read wave 1 (four workgroups, one d tile
             // each), while the chain waves run segment 5: the sum of the two
             // read waves' partials of every workgroup, in slot order (on chain
