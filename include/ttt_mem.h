@@ -196,7 +196,11 @@ int ttt_mem_mlp_forward_bf16_zf32(const uint16_t* q, const uint16_t* k, const ui
  *   records a failure in the workspace instead of hanging; the results are
  *   then undefined.  ttt_mem_deep_status(work, stream) synchronizes `stream`
  *   and returns TTT_OK, or TTT_ERR_DEVICE if the last launch on `work`
- *   recorded a failure.
+ *   recorded a failure.  A wait gives up after 2,000,000 polls of its
+ *   counter; the environment variable TTT_MEM_DEEP_SPIN_LIMIT (read at each
+ *   call of the deep-memory entry points) sets another limit, so that a test
+ *   can drive that path (0: a wait gives up as soon as a poll finds the
+ *   group incomplete).
  *   Sizes: d = 64, hidden = 256, depth in {2, 3, 4}, 1 <= b <= 16.
  */
 size_t ttt_mem_deep_param_count(int d, int hidden, int depth);

@@ -50,6 +50,7 @@
 // float32's exponent range, so weights that decay far below the fp16 range
 // need no scaling.
 
+#include <cstdlib>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -1338,6 +1339,17 @@ void* scratch_ptr() {
     return g_scratch[dev];
 }
 
+// Polls before a wait gives up: 2,000,000 (seconds, far beyond any healthy
+// exchange), or TTT_MEM_DEEP_SPIN_LIMIT from the environment (read at every
+// call), with which a test drives the timeout path from the host.
+int spin_limit() {
+    const char* e = std::getenv("TTT_MEM_DEEP_SPIN_LIMIT");
+    if (!e || !*e) return 2000000;
+    char* end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    return (*end == '\0' && v >= 0 && v <= 2000000000L) ? static_cast<int>(v) : 2000000;
+}
+
 // Workspace of a launch with ngroups groups: the header and group counters,
 // the exchange slots and, for depth > 2, the momenta of the hidden-to-hidden
 // layers (16 tiles of 64 x 4 floats per wave and layer).
@@ -1474,7 +1486,7 @@ int deep_forward_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
     p.b = b;
     p.ngroups = static_cast<int>(ngroups);
     p.nxcc = nxcc;
-    p.spin_limit = 2000000;
+    p.spin_limit = spin_limit();
     p.work = static_cast<int*>(work);
     const int hdr = kHdrInts + static_cast<int>(ngroups) * kCtrStride;
     hipLaunchKernelGGL(deep_init, dim3(8), dim3(256), 0, stream, p.work, hdr);

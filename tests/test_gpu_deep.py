@@ -140,3 +140,32 @@ def test_status_and_workspace_errors():
     with pytest.raises(TTTError) as e:
         tm.deep_forward(*args, hidden=w.hidden, depth=2, b=w.b, work=small)
     assert e.value.status == -1
+
+
+def test_forced_timeout_reports_and_recovers(monkeypatch):
+    # With a spin limit of 0 a wait gives up as soon as one poll finds its group
+    # incomplete: the launch must still finish, report TTT_ERR_DEVICE through
+    # the workspace status (if any wait gave up), and the next launch on the
+    # same workspace must give the results of an undisturbed one.
+    w = _small(B=2, H=8, T=4096)
+    inp = make_inputs(w)
+    layers = _layers(w, 2)
+    work = tm.new_deep_work(w.B, w.H, w.d, w.hidden, 2, "cuda")
+    ref = _run(inp, layers, w, 2, work=work)
+    monkeypatch.setenv("TTT_MEM_DEEP_SPIN_LIMIT", "0")
+    dev = to_dev(inp)
+    W0 = tm.deep_pack([x.cuda() for x in layers])
+    tm.deep_forward(dev["q"], dev["k"], dev["v"], dev["theta"], dev["eta"], dev["alpha"], W0,
+                    hidden=w.hidden, depth=2, b=w.b, work=work)
+    try:
+        tm.deep_status(work)
+        timed_out = False
+    except TTTError as e:
+        assert e.status == -4
+        timed_out = True
+    print(f"forced spin limit 0: a wait gave up = {timed_out}", flush=True)
+    monkeypatch.delenv("TTT_MEM_DEEP_SPIN_LIMIT")
+    again = _run(inp, layers, w, 2, work=work)
+    torch.cuda.synchronize()
+    for a, b_ in zip((ref[0],) + tuple(ref[1]) + tuple(ref[2]), (again[0],) + tuple(again[1]) + tuple(again[2])):
+        assert torch.equal(a, b_)
