@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._parity import TOL, rel_err, run_gpu, run_oracle, select, to_dev
+from tests._parity import TOL, rel_err, rel_err_bf16_out, run_gpu, run_oracle, select, to_dev
 from test_neural_memory_amd import memory as tm
 from test_neural_memory_amd._lib import TTTError
 from test_neural_memory_amd.workloads import WORKLOADS, make_inputs
@@ -29,10 +29,16 @@ def _check_all(inp, b, tol, heads=None, rows=None, ref=None, **kw):
         B, H = inp["q"].shape[:2]
         heads = [(i, j) for i in range(B) for j in range(H)]
     rows = np.arange(d) if rows is None else np.asarray(rows)
-    errs = (rel_err(select(z, heads, rows), zo),
+    # A z stored in bf16 is measured without its own rounding to bf16 (half an
+    # ulp per element), which alone can pass 2e-2 of the RMS where the largest
+    # |z| is more than about 5 times the RMS; the plain figure is printed too.
+    z_bf16 = inp["q"].dtype == torch.bfloat16 and kw.get("z_dtype") in (None, torch.bfloat16)
+    zs = select(z, heads, rows)
+    errs = (rel_err_bf16_out(zs, zo) if z_bf16 else rel_err(zs, zo),
             rel_err(select(M, heads, rows, state=True), Mo),
             rel_err(select(S, heads, rows, state=True), So))
-    _say(f"  errors z={errs[0]:.3e} M_T={errs[1]:.3e} S_T={errs[2]:.3e} (tol {tol})")
+    plain = f" (plain {rel_err(zs, zo):.3e})" if z_bf16 else ""
+    _say(f"  errors z={errs[0]:.3e}{plain} M_T={errs[1]:.3e} S_T={errs[2]:.3e} (tol {tol})")
     assert max(errs) <= tol, errs
     return errs
 
@@ -113,8 +119,9 @@ def test_edge_shapes(label, kw, dtype):
     w = WORKLOADS[3].replace(dtype=dtype, **kw)
     _say(f"case edge {label} {dtype}")
     inp = make_inputs(w, seed=7)
-    inp["S0"] = torch.randn(w.B, w.H, w.d, w.d) * 0.05
-    inp["M0"] = torch.randn(w.B, w.H, w.d, w.d) * 0.1
+    g = torch.Generator().manual_seed(7)
+    inp["S0"] = torch.randn(w.B, w.H, w.d, w.d, generator=g) * 0.05
+    inp["M0"] = torch.randn(w.B, w.H, w.d, w.d, generator=g) * 0.1
     _check_all(inp, w.b, TOL[dtype])
 
 
@@ -126,7 +133,7 @@ def test_degenerate_gates(dtype):
     inp["eta"][:, :, ::7] = 0.0
     inp["alpha"][:, :, 5::31] = 1.0
     inp["theta"][:, :, 3::11] = 0.0
-    inp["M0"] = torch.randn(1, 2, 64, 64) * 0.1
+    inp["M0"] = torch.randn(1, 2, 64, 64, generator=torch.Generator().manual_seed(11)) * 0.1
     _say(f"case degenerate gates {dtype}")
     _check_all(inp, w.b, TOL[dtype])
 
@@ -139,8 +146,9 @@ def test_zero_momentum_everywhere():
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_empty_sequence_copies_state(dtype):
-    M0 = torch.randn(2, 3, 32, 32, device="cuda")
-    S0 = torch.randn(2, 3, 32, 32, device="cuda")
+    gen = torch.Generator().manual_seed(2)
+    M0 = torch.randn(2, 3, 32, 32, generator=gen).cuda()
+    S0 = torch.randn(2, 3, 32, 32, generator=gen).cuda()
     e = torch.empty(2, 3, 0, 32, device="cuda", dtype=dtype)
     g = torch.empty(2, 3, 0, device="cuda")
     z, M, S = tm.forward(e, e, e, g, g, g, M0, S0, b=8)
@@ -163,8 +171,9 @@ def test_empty_batch_is_a_noop():
 def _dev_inputs(seed=3, **kw):
     w = WORKLOADS[3].replace(**kw)
     inp = make_inputs(w, seed=seed)
-    inp["M0"] = torch.randn(w.B, w.H, w.d, w.d) * 0.1
-    inp["S0"] = torch.randn(w.B, w.H, w.d, w.d) * 0.02
+    gen = torch.Generator().manual_seed(seed)
+    inp["M0"] = torch.randn(w.B, w.H, w.d, w.d, generator=gen) * 0.1
+    inp["S0"] = torch.randn(w.B, w.H, w.d, w.d, generator=gen) * 0.02
     return w, to_dev(inp)
 
 
@@ -268,5 +277,5 @@ def test_random_shapes(seed):
     w = WORKLOADS[3].replace(B=B, H=H, T=T, d=d, b=b, dtype=dtype)
     _say(f"case random {w}")
     inp = make_inputs(w, seed=seed)
-    inp["M0"] = torch.randn(B, H, d, d) * 0.1
+    inp["M0"] = torch.randn(B, H, d, d, generator=torch.Generator().manual_seed(seed)) * 0.1
     _check_all(inp, b, TOL[dtype])
